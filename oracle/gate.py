@@ -1,0 +1,117 @@
+"""BSFA tile-maximum gating (float64, CPU).  Test infrastructure only.
+
+Definition followed: "Block Sparse Flash Attention", Abstract and Figure 2
+(mechanism).  Inside the FlashAttention tile loop the exact per-tile maximum
+score s_max^(i,j) of query block i against key block j is compared with a
+calibrated threshold T(h, i) (one value per query block of a head; -inf keeps
+every tile).  Off-diagonal tiles are kept when s_max >= T; the diagonal tile
+always runs; a skipped tile contributes neither the V_j load nor the P V_j
+product.
+
+Readings (the page leaves these open):
+* Causal self-attention only (Sq == Sk), square tiles; tiles j > i are never
+  visited.
+* A skipped tile's scores are excluded from the softmax entirely (from the
+  running maximum, from the normaliser and from P V), so the gated result is
+  exactly block-sparse attention over the kept tiles.  Parity unpinned: the
+  page does not say, and this is the reading under which "skip computation"
+  holds.  Pinned only through that equivalence.
+* The scores are the scaled dot products scale*<q, k>; the comparison is taken
+  in float32, the precision of the kernel: the exact float64 tile maximum is
+  rounded to float32 and compared with the float32 threshold.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .core import _attend, _kv_head, as_f64, default_scale
+
+
+def _check(Sq: int, Sk: int, BM: int, BN: int) -> None:
+    if Sq != Sk or BM != BN or Sq % BM:
+        raise ValueError("gating needs Sq == Sk, square tiles and Sq divisible by the tile")
+
+
+def tile_max_row(q, k, b: int, h: int, i: int, BM: int, BN: int, scale: float | None = None):
+    """Scaled tile maxima t(i, j) for j = 0..i of head h (float64).
+
+    t(i, i) is taken over the causally visible entries of the diagonal tile.
+    """
+    q, k = np.asarray(q), np.asarray(k)
+    Hq, D = q.shape[2], q.shape[3]
+    Hkv = k.shape[2]
+    scale = default_scale(D) if scale is None else scale
+    hk = _kv_head(h, Hq, Hkv)
+    qi = as_f64(q[b, i * BM:(i + 1) * BM, h])                 # [BM, D]
+    kk = as_f64(k[b, :(i + 1) * BN, hk])                       # [(i+1)BN, D]
+    s = scale * (qi @ kk.T)                                    # [BM, (i+1)BN]
+    r = np.arange(BM)[:, None] + i * BM
+    c = np.arange((i + 1) * BN)[None, :]
+    s = np.where(c <= r, s, -np.inf)
+    return s.reshape(BM, i + 1, BN).max(axis=(0, 2))
+
+
+def _keep_row(t: np.ndarray, T: float, i: int) -> np.ndarray:
+    """Keep decisions for query block i: float32(t) >= float32(T); diagonal always kept."""
+    keep = (t.astype(np.float32) >= np.float32(T)).astype(np.uint8)
+    keep[i] = 1
+    return keep
+
+
+def gated(q, k, v, T, BM: int = 128, BN: int = 128, scale: float | None = None):
+    """Gated causal attention for small inputs.
+
+    q [B,S,Hq,D], k/v [B,S,Hkv,D], T [B,Hq,nQB] (float32 thresholds).
+    Returns O [B,S,Hq,D], LSE [B,Hq,S], keep [B,Hq,nQB,nKB] (uint8, 0 above the
+    diagonal) and tmax [B,Hq,nQB,nKB] (float64, NaN above the diagonal).
+    """
+    B, S, Hq, D = np.asarray(q).shape
+    Hkv = np.asarray(k).shape[2]
+    _check(S, np.asarray(k).shape[1], BM, BN)
+    scale = default_scale(D) if scale is None else scale
+    nqb = S // BM
+    o = np.zeros((B, S, Hq, D))
+    lse = np.zeros((B, Hq, S))
+    keep = np.zeros((B, Hq, nqb, nqb), np.uint8)
+    tmax = np.full((B, Hq, nqb, nqb), np.nan)
+    vv = as_f64(v)
+    qq = as_f64(q)
+    kk = as_f64(k)
+    for b in range(B):
+        for h in range(Hq):
+            hk = _kv_head(h, Hq, Hkv)
+            mask = np.zeros((S, S), bool)
+            for i in range(nqb):
+                t = tile_max_row(q, k, b, h, i, BM, BN, scale)
+                tmax[b, h, i, :i + 1] = t
+                kr = _keep_row(t, T[b, h, i], i)
+                keep[b, h, i, :i + 1] = kr
+                for j in np.nonzero(kr)[0]:
+                    mask[i * BM:(i + 1) * BM, j * BN:(j + 1) * BN] = True
+            mask &= np.arange(S)[None, :] <= np.arange(S)[:, None]
+            o[b, :, h], lse[b, h] = _attend(qq[b, :, h], kk[b, :, hk], vv[b, :, hk], mask, scale)
+    return o, lse, keep, tmax
+
+
+def gated_rows(q, k, v, T: float, b: int, h: int, i: int, rows, BM: int = 128, BN: int = 128,
+               scale: float | None = None):
+    """Gated attention for selected rows of query block i of head h (full-size spot checks).
+
+    Returns (O [R, D], LSE [R], keep row [i+1], t row [i+1]).
+    """
+    q, k = np.asarray(q), np.asarray(k)
+    Hq, D = q.shape[2], q.shape[3]
+    Hkv = k.shape[2]
+    scale = default_scale(D) if scale is None else scale
+    hk = _kv_head(h, Hq, Hkv)
+    t = tile_max_row(q, k, b, h, i, BM, BN, scale)
+    kr = _keep_row(t, T, i)
+    kept = np.nonzero(kr)[0]
+    cols = np.concatenate([np.arange(j * BN, (j + 1) * BN) for j in kept])
+    kv = as_f64(k[b, cols, hk])
+    vv = as_f64(v[b, cols, hk])
+    rows = np.asarray(rows)
+    qr = as_f64(q[b, rows, h])
+    mask = cols[None, :] <= rows[:, None]
+    o, lse = _attend(qr, kv, vv, mask, scale)
+    return o, lse, kr, t
