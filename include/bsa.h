@@ -1,0 +1,219 @@
+/*
+ * bsa.h — block-sparse attention forward for AMD Instinct MI355X (gfx950).
+ *
+ * A C ABI over hand-written HIP kernels.  Every entry point takes plain
+ * device pointers and sizes, validates its arguments on the host, enqueues
+ * its kernels on the caller's stream and returns without synchronising.
+ * The library keeps no state and allocates no memory: every buffer,
+ * including scratch ("workspace"), belongs to the caller.  Errors are
+ * reported through the returned status; nothing is launched when
+ * validation fails.  No exception crosses this interface.
+ *
+ * Sources of the operations (cited by page title and section):
+ *   [IR]   "Sparse FlashAttention with Incremental Repair" (README):
+ *          What's in this fork; Usage sections 1 (sparse-only forward),
+ *          2 (speculative + sparse decoding with exact combine) and
+ *          3 (per-block partials).
+ *   [BSFA] "Block Sparse Flash Attention": Abstract; Figure 2 (mechanism).
+ *   [SGL]  "Implementation: Sgl project Sglang Sparse Flash Attention":
+ *          Description; Signature; I/O Contract.
+ *
+ * Conventions shared by the attention entry points
+ * -------------------------------------------------
+ * Layouts (element strides, head dim contiguous), as in [IR] Usage 1 and
+ * the [SGL] I/O Contract:
+ *   q     [B, Sq, Hq, D]       k, v  [B, Sk, Hkv, D]
+ *   o     [B, Sq, Hq, D]       lse   [B, Hq, Sq] float32, contiguous
+ *   varlen (cu_seqlens given): q [total_q, Hq, D], k/v [total_k, Hkv, D],
+ *         o like q, lse [Hq, total_q]; the batch stride is then ignored.
+ * Query head h reads key/value head h / (Hq / Hkv).
+ * Scores are scale * <q, k> with scale = 1/sqrt(D) unless given
+ * ([SGL] I/O Contract, softmax_scale); LSE is the natural-log
+ * log-sum-exp of the attended scores.  A row with no attended key gives
+ * O = 0 and LSE = -inf, the neutral partial of the combine ([IR] Usage 1).
+ * Causal masking is bottom-right aligned: key c is visible to row r iff
+ * c <= r + (Sk - Sq) (per sequence in varlen).
+ * Inputs q/k/v are bfloat16; o may be bfloat16 or float32.
+ * D must be 64 or 128.
+ */
+#ifndef BSA_H
+#define BSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* The caller's HIP stream (hipStream_t); NULL is the null stream. */
+typedef void* bsa_stream;
+
+typedef enum {
+  BSA_OK = 0,
+  BSA_ERR_INVALID_ARG = 1, /* malformed shape, stride, pointer or size      */
+  BSA_ERR_UNSUPPORTED = 2, /* well formed but outside what the kernels cover */
+  BSA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required    */
+  BSA_ERR_HIP = 4          /* a HIP launch failed                           */
+} bsa_status;
+
+typedef enum { BSA_BF16 = 0, BSA_F32 = 1 } bsa_dtype;
+
+/* A strided 4-D (or varlen 3-D) tensor view.  Strides are in elements; the
+ * last (head-dim) axis is contiguous.  For varlen tensors stride_b is
+ * ignored and the token axis is indexed by cu_seqlens[b] + s. */
+typedef struct {
+  void* ptr;
+  int32_t dtype; /* bsa_dtype */
+  int64_t stride_b, stride_s, stride_h;
+} bsa_tensor;
+
+/* Problem shape.  cu_seqlens_q/k are device int32 arrays of B+1 prefix sums
+ * (NULL for fixed length); max_seqlen_q/k bound the per-sequence lengths
+ * and must be given for varlen.  softmax_scale <= 0 selects 1/sqrt(D). */
+typedef struct {
+  int32_t B, Hq, Hkv, Sq, Sk, D;
+  const int32_t* cu_seqlens_q;
+  const int32_t* cu_seqlens_k;
+  int32_t max_seqlen_q, max_seqlen_k;
+  float softmax_scale;
+  int32_t causal;
+} bsa_problem;
+
+typedef enum {
+  BSA_PAT_DENSE = 0, /* every key (subject to the causal mask)                */
+  BSA_PAT_BLOCK = 1, /* per-query-block lists of key-block ids                */
+  BSA_PAT_VS = 2     /* per-query-block key windows plus gathered columns    */
+} bsa_pattern_kind;
+
+/* Which keys each query block attends to.
+ *
+ * BLOCK ([IR] Usage 1): entry j of the list for (b, h_t, query block m) is
+ *   the key block [j*block_N, (j+1)*block_N).  Lists are sets (no repeats)
+ *   of in-range ids; order does not matter.
+ * VS ([SGL] I/O Contract): index holds block_offset — key positions w whose
+ *   windows [w, w+block_N) are attended (clipped to the sequence) — and
+ *   col_index holds column_index, single key positions; col_count is
+ *   column_count.  Windows are disjoint; columns lie outside them.
+ *
+ * Storage: the list of (b, h_t, m) has count[b*s_b + h_t*s_h + m*s_q]
+ * entries at index[(b*s_b + h_t*s_h + m*s_q) * cap + e] (and likewise
+ * col_index with col_cap).  Strides of 0 broadcast: s_b = s_h = s_q = 0
+ * is the single 1-D table of [IR] Usage 1 shared by every row and head.
+ * Ht is the number of list heads: Hq (a list per query head) or Hkv (one
+ * list per key/value head, shared by its Hq/Hkv query heads).
+ * All arrays are device int32. */
+typedef struct {
+  int32_t kind; /* bsa_pattern_kind */
+  int32_t Ht;
+  int32_t block_M, block_N;
+  int32_t cap, col_cap;
+  const int32_t* count;
+  const int32_t* index;
+  const int32_t* col_count;
+  const int32_t* col_index;
+  int64_t s_b, s_h, s_q;
+} bsa_pattern;
+
+/* Human-readable name of a status code (static storage). */
+const char* bsa_status_string(bsa_status s);
+
+/* Bytes of workspace bsa_fwd needs for this problem and pattern (0 when the
+ * chosen kernel needs none).  Returns 0 on invalid arguments as well; the
+ * subsequent bsa_fwd call reports them. */
+size_t bsa_workspace_size(const bsa_problem* prob, const bsa_pattern* pat);
+
+/* Attention restricted to a key pattern, returning (O, LSE).
+ * [IR] Usage 1 (sparse-only forward; pattern NULL or DENSE gives ordinary
+ * attention, as the speculative pass of [IR] Usage 2 needs).
+ *   q, k, v  bf16 inputs (layouts above); k/v may be strided views.
+ *   pat      NULL or a pattern; BLOCK needs Sk % block_N == 0 and
+ *            block_N in {64, 128}; block_M in {64, 128} (ignored when the
+ *            query rows fit one block).  VS needs causal and varlen or
+ *            fixed length, block_M <= block_N, both 64.
+ *   o        output, bf16 or f32; lse float32 output (may be NULL).
+ *   ws       device scratch of at least bsa_workspace_size() bytes (may be
+ *            NULL when that is 0).  Overwritten; the caller keeps it alive
+ *            until the stream has passed this call.
+ * Errors: BSA_ERR_INVALID_ARG for NULL tensors, non-positive sizes,
+ * Hq % Hkv != 0, pattern heads other than Hq/Hkv, Sk % block_N != 0;
+ * BSA_ERR_UNSUPPORTED for D or block sizes outside the list above;
+ * BSA_ERR_WORKSPACE for a short workspace; BSA_ERR_HIP on launch failure. */
+bsa_status bsa_fwd(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, bsa_tensor v,
+                   const bsa_pattern* pat, bsa_tensor o, float* lse, void* ws, size_t ws_bytes,
+                   bsa_stream stream);
+
+/* One (o, lse) partial per list entry.  [IR] Usage 3 (per-block partials).
+ *   pat       a BLOCK pattern (fixed length only).
+ *   o_part    float32 [cap, B, Sq, Hq, D] contiguous; entry e of a list with
+ *             at most e entries is written as (0, -inf).
+ *   lse_part  float32 [cap, B, Hq, Sq] contiguous.
+ * The partials merge back with bsa_combine into bsa_fwd's result.
+ * Errors as for bsa_fwd. */
+bsa_status bsa_fwd_partials(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, bsa_tensor v,
+                            const bsa_pattern* pat, float* o_part, float* lse_part, bsa_stream stream);
+
+/* Log-sum-exp combine of P partials.  [IR] What's in this fork (combine
+ * identity FA(A u B) == Combine(FA(A), FA(B))) and Usage 2.
+ * For each (b, h, s): m = max_p lse_p; if m = -inf the result is (0, -inf);
+ * else w_p = exp(lse_p - m), O = sum w_p o_p / sum w_p, LSE = m + ln sum w_p.
+ *   o_part    float32 [P, B, Sq, Hq, D] contiguous.
+ *   lse_part  float32 [P, B, Hq, Sq] contiguous.
+ *   o         output view [B, Sq, Hq, D] (bf16 or f32); lse float32
+ *             [B, Hq, Sq] (may be NULL).  o may alias partial 0 only when
+ *             it is float32 and contiguous.
+ * Errors: BSA_ERR_INVALID_ARG for P < 1 or bad shapes; BSA_ERR_HIP. */
+bsa_status bsa_combine(int32_t P, int32_t B, int32_t Hq, int32_t Sq, int32_t D, const float* o_part,
+                       const float* lse_part, bsa_tensor o, float* lse, bsa_stream stream);
+
+/* BSFA gated causal attention.  [BSFA] Abstract and Figure 2: for query
+ * block i and key block j < i the exact tile maximum
+ * t(i,j) = max over the tile of scale*<q, k> is computed inside the tile loop
+ * and the tile is kept iff t(i,j) >= T[b, h, i] (compared in float32);
+ * the diagonal tile always runs; a skipped tile loads no V and does no P V
+ * product, and its scores are left out of the softmax altogether.
+ *   T          float32 [B, Hq, nQB] thresholds (-inf keeps every tile).
+ *   block_M/N  tile sizes; both 128.  Needs Sq == Sk, causal, fixed length,
+ *              Sq % 128 == 0.
+ *   keep_mask  optional uint8 [B, Hq, nQB, nKB]: 1 kept, 0 skipped, for
+ *              j <= i (entries j > i are not written).
+ *   tile_max   optional float32 [B, Hq, nQB, nKB]: t(i, j) for j <= i
+ *              (the diagonal tile's maximum over its causal entries).
+ * Errors as for bsa_fwd; BSA_ERR_UNSUPPORTED outside the cases above. */
+bsa_status bsa_fwd_gated(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, bsa_tensor v, const float* T,
+                         int32_t block_M, int32_t block_N, bsa_tensor o, float* lse, uint8_t* keep_mask,
+                         float* tile_max, bsa_stream stream);
+
+/* Vertical-slash index conversion.  [SGL] Description and I/O Contract
+ * (convert_vertical_slash_indexes); the conversion rule is this library's
+ * own, since the page defers it to a paper that is not among the sources:
+ * for query block m of sequence b (rows r0 = m*block_M .. r1-1, d =
+ * kv_len - q_len), slash offsets s (key = row + d - s) are walked in the
+ * given descending order; each covers keys [max(0, r0+d-s), r1-1+d-s];
+ * a frontier f starts at -inf; a range [a, e] opens a window at a when
+ * a >= f (f = a + block_N), at f when a < f <= e (f += block_N), and
+ * nothing otherwise.  Windows go to block_offset (key positions).  Then
+ * the vertical indices v <= r1-1+d, in the given ascending order, that
+ * no window contains go to column_index.
+ *   q_seqlens, kv_seqlens  device int32 [B].
+ *   vertical   device int32 [B, H, nnz_v], ascending, unique.
+ *   slash      device int32 [B, H, nnz_s], descending, unique, >= 0.
+ *   context_size  rows = cdiv(context_size, block_M) per (b, h); rows past
+ *              a sequence's end get counts 0.
+ *   outputs    block_count [B,H,rows], block_offset [B,H,rows,nnz_s],
+ *              column_count [B,H,rows], column_index [B,H,rows,nnz_v],
+ *              device int32; entries past a count are not written.
+ * Needs causal != 0 and block_M <= block_N ([SGL] Signature default).
+ * Errors: BSA_ERR_INVALID_ARG (NULL, sizes); BSA_ERR_UNSUPPORTED
+ * (causal == 0, block_M > block_N); BSA_ERR_HIP. */
+bsa_status vs_convert_indexes(const int32_t* q_seqlens, const int32_t* kv_seqlens, const int32_t* vertical,
+                              const int32_t* slash, int32_t B, int32_t H, int32_t nnz_v, int32_t nnz_s,
+                              int32_t context_size, int32_t block_M, int32_t block_N, int32_t causal,
+                              int32_t* block_count, int32_t* block_offset, int32_t* column_count,
+                              int32_t* column_index, bsa_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSA_H */

@@ -1,0 +1,20 @@
+"""Block-sparse FlashAttention forward for AMD MI355X (gfx950).
+
+Python face of libbsa.so; every entry point has the name of its C function in
+include/bsa.h and only marshals arguments — the kernels do all the work:
+
+  bsa_fwd             attention restricted to a key pattern (dense, block
+                      lists or vertical-slash metadata), returning (O, LSE)
+  bsa_fwd_partials    one (o, lse) partial per list entry
+  bsa_combine         log-sum-exp combine of partials
+  bsa_fwd_gated       BSFA gated causal attention (tile max vs threshold)
+  vs_convert_indexes  vertical-slash index conversion
+  speculative_sparse  dense speculative pass + sparse repair pass + combine
+"""
+from ._binding import (EXPORTS, LIB_PATH, BlockPattern, BSAError, VSPattern, bsa_combine, bsa_fwd, bsa_fwd_gated,
+                       bsa_fwd_partials, bsa_workspace_size, load, speculative_buffers, speculative_sparse,
+                       vs_convert_indexes)
+
+__all__ = ["EXPORTS", "LIB_PATH", "BlockPattern", "BSAError", "VSPattern", "bsa_combine", "bsa_fwd", "bsa_fwd_gated",
+           "bsa_fwd_partials", "bsa_workspace_size", "load", "speculative_buffers", "speculative_sparse",
+           "vs_convert_indexes"]

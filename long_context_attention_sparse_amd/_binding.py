@@ -1,0 +1,345 @@
+"""ctypes binding of libbsa.so (C ABI in include/bsa.h).
+
+Argument marshalling only: tensors are described by pointer, dtype and
+strides, outputs are allocated with torch on the caller's device, and every
+computation happens in the HIP kernels behind the C entry points.  Importing
+this module does not need a GPU; calling an entry point without the built
+library raises immediately.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libbsa.so")
+
+BSA_OK, BSA_ERR_INVALID_ARG, BSA_ERR_UNSUPPORTED, BSA_ERR_WORKSPACE, BSA_ERR_HIP = range(5)
+BSA_BF16, BSA_F32 = 0, 1
+BSA_PAT_DENSE, BSA_PAT_BLOCK, BSA_PAT_VS = 0, 1, 2
+
+EXPORTS = ("bsa_status_string", "bsa_workspace_size", "bsa_fwd", "bsa_fwd_partials", "bsa_combine",
+           "bsa_fwd_gated", "vs_convert_indexes")
+
+
+class BSAError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: {msg} (status {status})")
+        self.status = status
+
+
+class _Tensor(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("stride_b", ctypes.c_int64),
+                ("stride_s", ctypes.c_int64), ("stride_h", ctypes.c_int64)]
+
+
+class _Problem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("Sq", ctypes.c_int32),
+                ("Sk", ctypes.c_int32), ("D", ctypes.c_int32), ("cu_seqlens_q", ctypes.c_void_p),
+                ("cu_seqlens_k", ctypes.c_void_p), ("max_seqlen_q", ctypes.c_int32),
+                ("max_seqlen_k", ctypes.c_int32), ("softmax_scale", ctypes.c_float), ("causal", ctypes.c_int32)]
+
+
+class _Pattern(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("Ht", ctypes.c_int32), ("block_M", ctypes.c_int32),
+                ("block_N", ctypes.c_int32), ("cap", ctypes.c_int32), ("col_cap", ctypes.c_int32),
+                ("count", ctypes.c_void_p), ("index", ctypes.c_void_p), ("col_count", ctypes.c_void_p),
+                ("col_index", ctypes.c_void_p), ("s_b", ctypes.c_int64), ("s_h", ctypes.c_int64),
+                ("s_q", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libbsa.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m long_context_attention_sparse_amd.build`")
+    lib = ctypes.CDLL(path)
+    lib.bsa_status_string.restype = ctypes.c_char_p
+    lib.bsa_status_string.argtypes = [ctypes.c_int]
+    lib.bsa_workspace_size.restype = ctypes.c_size_t
+    lib.bsa_workspace_size.argtypes = [ctypes.POINTER(_Problem), ctypes.POINTER(_Pattern)]
+    lib.bsa_fwd.restype = ctypes.c_int
+    lib.bsa_fwd.argtypes = [ctypes.POINTER(_Problem), _Tensor, _Tensor, _Tensor, ctypes.POINTER(_Pattern), _Tensor,
+                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.bsa_fwd_partials.restype = ctypes.c_int
+    lib.bsa_fwd_partials.argtypes = [ctypes.POINTER(_Problem), _Tensor, _Tensor, _Tensor, ctypes.POINTER(_Pattern),
+                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.bsa_combine.restype = ctypes.c_int
+    lib.bsa_combine.argtypes = [ctypes.c_int32] * 5 + [ctypes.c_void_p, ctypes.c_void_p, _Tensor, ctypes.c_void_p,
+                                                      ctypes.c_void_p]
+    lib.bsa_fwd_gated.restype = ctypes.c_int
+    lib.bsa_fwd_gated.argtypes = [ctypes.POINTER(_Problem), _Tensor, _Tensor, _Tensor, ctypes.c_void_p,
+                                  ctypes.c_int32, ctypes.c_int32, _Tensor, ctypes.c_void_p, ctypes.c_void_p,
+                                  ctypes.c_void_p, ctypes.c_void_p]
+    lib.vs_convert_indexes.restype = ctypes.c_int
+    lib.vs_convert_indexes.argtypes = ([ctypes.c_void_p] * 4 + [ctypes.c_int32] * 8 + [ctypes.c_void_p] * 5)
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != BSA_OK:
+        raise BSAError(fn, status, load().bsa_status_string(status).decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BSA_BF16
+    if t.dtype == torch.float32:
+        return BSA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _tensor(t: torch.Tensor, varlen: bool = False) -> _Tensor:
+    """[B, S, H, D] (or varlen [T, H, D]) view with a contiguous last axis."""
+    if t.stride(-1) != 1:
+        raise ValueError("the head-dim axis must be contiguous")
+    if varlen:
+        if t.dim() != 3:
+            raise ValueError("varlen tensors are [total, heads, head_dim]")
+        return _Tensor(t.data_ptr(), _dtype_code(t), 0, t.stride(0), t.stride(1))
+    if t.dim() != 4:
+        raise ValueError("tensors are [batch, seq, heads, head_dim]")
+    return _Tensor(t.data_ptr(), _dtype_code(t), t.stride(0), t.stride(1), t.stride(2))
+
+
+def _i32(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dtype != torch.int32 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int32 device tensor")
+    return t
+
+
+@dataclass
+class BlockPattern:
+    """Per-query-block lists of key-block ids.
+
+    count [B, Ht, nQB] and index [B, Ht, nQB, cap] (int32, device).  Ht is Hq
+    or Hkv.  A 1-D table of N ids shared by every row and head (the form of the
+    sparse block-table forward) is ``BlockPattern.table(ids, block_size)``.
+    """
+    count: torch.Tensor
+    index: torch.Tensor
+    block_M: int
+    block_N: int
+    broadcast: bool = False
+
+    @staticmethod
+    def table(ids: torch.Tensor, block_size: int, block_M: int = 128) -> "BlockPattern":
+        ids = _i32(ids.reshape(-1), "table")
+        count = torch.tensor([ids.numel()], dtype=torch.int32, device=ids.device)
+        return BlockPattern(count, ids, block_M, block_size, broadcast=True)
+
+    def struct(self, Hq: int) -> _Pattern:
+        _i32(self.count, "count")
+        _i32(self.index, "index")
+        if self.broadcast:
+            return _Pattern(BSA_PAT_BLOCK, Hq, self.block_M, self.block_N, self.index.numel(), 0,
+                            self.count.data_ptr(), self.index.data_ptr(), None, None, 0, 0, 0)
+        B, Ht, nqb = self.count.shape
+        cap = self.index.shape[-1]
+        if tuple(self.index.shape[:3]) != (B, Ht, nqb):
+            raise ValueError("index must be [B, Ht, nQB, cap] matching count")
+        return _Pattern(BSA_PAT_BLOCK, Ht, self.block_M, self.block_N, cap, 0, self.count.data_ptr(),
+                        self.index.data_ptr(), None, None, Ht * nqb, nqb, 1)
+
+
+@dataclass
+class VSPattern:
+    """Converted vertical-slash metadata: block_count [B,H,R], block_offset [B,H,R,NNZ_S],
+    column_count [B,H,R], column_index [B,H,R,NNZ_V] (int32, device)."""
+    block_count: torch.Tensor
+    block_offset: torch.Tensor
+    column_count: torch.Tensor
+    column_index: torch.Tensor
+    block_M: int = 64
+    block_N: int = 64
+
+    def struct(self, Hq: int) -> _Pattern:
+        B, H, R = self.block_count.shape
+        for n, t in (("block_count", self.block_count), ("block_offset", self.block_offset),
+                     ("column_count", self.column_count), ("column_index", self.column_index)):
+            _i32(t, n)
+        return _Pattern(BSA_PAT_VS, H, self.block_M, self.block_N, self.block_offset.shape[-1],
+                        self.column_index.shape[-1], self.block_count.data_ptr(), self.block_offset.data_ptr(),
+                        self.column_count.data_ptr(), self.column_index.data_ptr(), H * R, R, 1)
+
+
+def _problem(q, k, causal, softmax_scale, cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=0, max_seqlen_k=0):
+    if cu_seqlens_q is not None:
+        B = cu_seqlens_q.numel() - 1
+        _, Hq, D = q.shape
+        Hkv = k.shape[1]
+        return _Problem(B, Hq, Hkv, int(max_seqlen_q), int(max_seqlen_k), D,
+                        _i32(cu_seqlens_q, "cu_seqlens_q").data_ptr(), _i32(cu_seqlens_k, "cu_seqlens_k").data_ptr(),
+                        int(max_seqlen_q), int(max_seqlen_k), float(softmax_scale or 0.0), int(bool(causal)))
+    B, Sq, Hq, D = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    return _Problem(B, Hq, Hkv, Sq, Sk, D, None, None, 0, 0, float(softmax_scale or 0.0), int(bool(causal)))
+
+
+def bsa_workspace_size(q, k, pattern=None, causal=False, **varlen) -> int:
+    prob = _problem(q, k, causal, None, **varlen)
+    pat = pattern.struct(prob.Hq) if pattern is not None else None
+    return int(load().bsa_workspace_size(ctypes.byref(prob), ctypes.byref(pat) if pat is not None else None))
+
+
+def bsa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pattern=None, *, causal: bool = False,
+            softmax_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+            out_dtype: torch.dtype = torch.bfloat16, lse: Optional[torch.Tensor] = None,
+            workspace: Optional[torch.Tensor] = None, cu_seqlens_q=None, cu_seqlens_k=None,
+            max_seqlen_q: int = 0, max_seqlen_k: int = 0, stream=None):
+    """Attention over a key pattern (None = dense).  Returns (out, lse).
+
+    q [B, Sq, Hq, D], k/v [B, Sk, Hkv, D] bf16 (or varlen [total, H, D] with
+    cu_seqlens).  out defaults to a new ``out_dtype`` tensor shaped like q;
+    lse is float32 [B, Hq, Sq] (varlen: [Hq, total_q]).
+    """
+    lib = load()
+    varlen = cu_seqlens_q is not None
+    prob = _problem(q, k, causal, softmax_scale, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse_shape = (q.shape[1], q.shape[0]) if varlen else (q.shape[0], q.shape[2], q.shape[1])
+        lse = torch.empty(lse_shape, dtype=torch.float32, device=q.device)
+    pat = pattern.struct(prob.Hq) if pattern is not None else None
+    pat_p = ctypes.byref(pat) if pat is not None else None
+    need = int(lib.bsa_workspace_size(ctypes.byref(prob), pat_p))
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.bsa_fwd(ctypes.byref(prob), _tensor(q, varlen), _tensor(k, varlen), _tensor(v, varlen), pat_p,
+                     _tensor(out, varlen), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream))
+    _check("bsa_fwd", st)
+    return out, lse
+
+
+def bsa_fwd_partials(q, k, v, pattern: BlockPattern, *, causal: bool = False, softmax_scale=None, stream=None):
+    """One (o, lse) per list entry: o_part [cap, B, Sq, Hq, D], lse_part [cap, B, Hq, Sq] (float32)."""
+    lib = load()
+    prob = _problem(q, k, causal, softmax_scale)
+    pat = pattern.struct(prob.Hq)
+    cap = pat.cap
+    B, Sq, Hq, D = q.shape
+    o_part = torch.empty((cap, B, Sq, Hq, D), dtype=torch.float32, device=q.device)
+    lse_part = torch.empty((cap, B, Hq, Sq), dtype=torch.float32, device=q.device)
+    st = lib.bsa_fwd_partials(ctypes.byref(prob), _tensor(q), _tensor(k), _tensor(v), ctypes.byref(pat),
+                              _ptr(o_part), _ptr(lse_part), _stream(stream))
+    _check("bsa_fwd_partials", st)
+    return o_part, lse_part
+
+
+def bsa_combine(o_part: torch.Tensor, lse_part: torch.Tensor, *, out: Optional[torch.Tensor] = None,
+                out_dtype: torch.dtype = torch.bfloat16, lse: Optional[torch.Tensor] = None, stream=None):
+    """Log-sum-exp combine of partials o_part [P, B, Sq, Hq, D], lse_part [P, B, Hq, Sq] (float32)."""
+    lib = load()
+    P, B, Sq, Hq, D = o_part.shape
+    if not (o_part.is_contiguous() and lse_part.is_contiguous()) or o_part.dtype != torch.float32:
+        raise ValueError("partials must be contiguous float32")
+    if tuple(lse_part.shape) != (P, B, Hq, Sq):
+        raise ValueError("lse_part must be [P, B, Hq, Sq]")
+    if out is None:
+        out = torch.empty((B, Sq, Hq, D), dtype=out_dtype, device=o_part.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=o_part.device)
+    st = lib.bsa_combine(P, B, Hq, Sq, D, _ptr(o_part), _ptr(lse_part), _tensor(out), _ptr(lse), _stream(stream))
+    _check("bsa_combine", st)
+    return out, lse
+
+
+def bsa_fwd_gated(q, k, v, T: torch.Tensor, *, block_M: int = 128, block_N: int = 128, softmax_scale=None,
+                  out: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.bfloat16,
+                  return_mask: bool = True, return_tile_max: bool = False, stream=None):
+    """BSFA gated causal attention.  Returns (out, lse, keep_mask or None, tile_max or None)."""
+    lib = load()
+    prob = _problem(q, k, True, softmax_scale)
+    B, S, Hq, D = q.shape
+    nqb = S // block_M
+    nkb = k.shape[1] // block_N
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    keep = torch.zeros((B, Hq, nqb, nkb), dtype=torch.uint8, device=q.device) if return_mask else None
+    tmax = torch.full((B, Hq, nqb, nkb), float("nan"), dtype=torch.float32, device=q.device) \
+        if return_tile_max else None
+    if T.dtype != torch.float32 or not T.is_contiguous():
+        raise ValueError("T must be contiguous float32 [B, Hq, nQB]")
+    st = lib.bsa_fwd_gated(ctypes.byref(prob), _tensor(q), _tensor(k), _tensor(v), _ptr(T), block_M, block_N,
+                           _tensor(out), _ptr(lse), _ptr(keep), _ptr(tmax), _stream(stream))
+    _check("bsa_fwd_gated", st)
+    return out, lse, keep, tmax
+
+
+def vs_convert_indexes(q_seqlens, kv_seqlens, vertical_indexes, slash_indexes, context_size: int,
+                       block_size_M: int = 64, block_size_N: int = 64, causal: bool = True, stream=None):
+    """Vertical-slash conversion.  Returns (block_count, block_offset, column_count, column_index)."""
+    lib = load()
+    B, H, nnz_v = vertical_indexes.shape
+    nnz_s = slash_indexes.shape[-1]
+    rows = (context_size + block_size_M - 1) // block_size_M
+    dev = vertical_indexes.device
+    bc = torch.empty((B, H, rows), dtype=torch.int32, device=dev)
+    bo = torch.empty((B, H, rows, nnz_s), dtype=torch.int32, device=dev)
+    cc = torch.empty((B, H, rows), dtype=torch.int32, device=dev)
+    ci = torch.empty((B, H, rows, nnz_v), dtype=torch.int32, device=dev)
+    st = lib.vs_convert_indexes(_ptr(_i32(q_seqlens, "q_seqlens")), _ptr(_i32(kv_seqlens, "kv_seqlens")),
+                                _ptr(_i32(vertical_indexes, "vertical_indexes")),
+                                _ptr(_i32(slash_indexes, "slash_indexes")), B, H, nnz_v, nnz_s, int(context_size),
+                                int(block_size_M), int(block_size_N), int(bool(causal)), _ptr(bc), _ptr(bo),
+                                _ptr(cc), _ptr(ci), _stream(stream))
+    _check("vs_convert_indexes", st)
+    return bc, bo, cc, ci
+
+
+def speculative_sparse(q, k_spec, v_spec, k, v, missed: BlockPattern, *, causal_spec: bool = True,
+                       softmax_scale=None, out_dtype: torch.dtype = torch.bfloat16, stream=None, buffers=None):
+    """Speculative + sparse decoding with exact combine ("Sparse FlashAttention with
+    Incremental Repair", Usage 2): dense attention over (k_spec, v_spec) with the causal
+    flag, sparse attention over the missed blocks of (k, v) without a mask, and the
+    log-sum-exp combine of the two partials.  Returns (out, lse)."""
+    B, Sq, Hq, D = q.shape
+    if buffers is None:
+        buffers = speculative_buffers(q, k_spec, k, missed, causal_spec)
+    o_part, lse_part, ws1, ws2 = buffers
+    bsa_fwd(q, k_spec, v_spec, None, causal=causal_spec, softmax_scale=softmax_scale, out=o_part[0],
+            lse=lse_part[0], workspace=ws1, stream=stream)
+    bsa_fwd(q, k, v, missed, causal=False, softmax_scale=softmax_scale, out=o_part[1], lse=lse_part[1],
+            workspace=ws2, stream=stream)
+    return bsa_combine(o_part, lse_part, out_dtype=out_dtype, stream=stream)
+
+
+def speculative_buffers(q, k_spec, k, missed: BlockPattern, causal_spec: bool = True):
+    """Preallocated partials and workspaces for ``speculative_sparse`` (reusable across calls)."""
+    B, Sq, Hq, D = q.shape
+    dev = q.device
+    o_part = torch.empty((2, B, Sq, Hq, D), dtype=torch.float32, device=dev)
+    lse_part = torch.empty((2, B, Hq, Sq), dtype=torch.float32, device=dev)
+    n1 = bsa_workspace_size(q, k_spec, None, causal_spec)
+    n2 = bsa_workspace_size(q, k, missed, False)
+    ws1 = torch.empty(max(n1, 1), dtype=torch.uint8, device=dev)
+    ws2 = torch.empty(max(n2, 1), dtype=torch.uint8, device=dev)
+    return o_part, lse_part, ws1, ws2
+
+
+def default_scale(D: int) -> float:
+    return 1.0 / math.sqrt(D)

@@ -1,0 +1,58 @@
+// Log-sum-exp combine of attention partials ("Sparse FlashAttention with
+// Incremental Repair", What's in this fork and Usage 2: FA(A u B) equals
+// Combine(FA(A), FA(B))).  For each (b, s, h): m = max_p lse_p; when m is
+// -inf the row has no keys and the result is (0, -inf); otherwise
+// w_p = exp(lse_p - m), O = sum w_p o_p / sum w_p, LSE = m + ln sum w_p.
+//
+// Memory bound: each thread owns four consecutive head-dim values of one row
+// (D/4 threads per row, all in one wavefront), reads every partial's LSE for
+// its row and streams the partial outputs with 16-byte loads.
+#pragma once
+#include "common.cuh"
+
+namespace bsa {
+
+struct CombineArgs {
+  int P, B, Hq, Sq, D;
+  const float* o_part;    // [P, B, Sq, Hq, D]
+  const float* lse_part;  // [P, B, Hq, Sq]
+  OutArg o;               // [B, Sq, Hq, D] view
+  float* lse;             // [B, Hq, Sq] or nullptr
+};
+
+__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+  const int tpr = a.D / 4;
+  const int rows_per_block = 256 / tpr;
+  const int64_t row = (int64_t)blockIdx.x * rows_per_block + threadIdx.x / tpr;
+  const int d = (threadIdx.x % tpr) * 4;
+  const int64_t nrows = (int64_t)a.B * a.Sq * a.Hq;
+  if (row >= nrows) return;
+  const int h = (int)(row % a.Hq);
+  const int s = (int)((row / a.Hq) % a.Sq);
+  const int b = (int)(row / ((int64_t)a.Hq * a.Sq));
+  const int64_t lse_stride = (int64_t)a.B * a.Hq * a.Sq;
+  const int64_t lse0 = ((int64_t)b * a.Hq + h) * a.Sq + s;
+  const int64_t o_stride = (int64_t)a.B * a.Sq * a.Hq * a.D;
+  const int64_t o0 = row * a.D + d;  // row = (b*Sq + s)*Hq + h
+
+  float m = kNegInf;
+  for (int p = 0; p < a.P; ++p) m = fmaxf(m, a.lse_part[lse0 + p * lse_stride]);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+  if (m != kNegInf) {
+    for (int p = 0; p < a.P; ++p) {
+      const float wgt = expf(a.lse_part[lse0 + p * lse_stride] - m);
+      if (wgt == 0.f) continue;  // empty partials may hold anything finite; skip them
+      const f32x4 v = *reinterpret_cast<const f32x4*>(a.o_part + o0 + p * o_stride);
+      acc += wgt * v;
+      wsum += wgt;
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  acc *= inv;
+  const int64_t off = (int64_t)b * a.o.sb + (int64_t)s * a.o.ss + (int64_t)h * a.o.sh + d;
+  store4(a.o, off, acc[0], acc[1], acc[2], acc[3]);
+  if (a.lse && d == 0) a.lse[lse0] = wsum > 0.f ? m + logf(wsum) : kNegInf;
+}
+
+}  // namespace bsa

@@ -1,0 +1,102 @@
+// Shared device helpers for the gfx950 attention kernels: vector types, the
+// bf16 MFMA builtins, bf16 packing, shuffles and the argument structs the
+// host passes to every kernel.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.69314718055994531f;
+constexpr float kNegInf = -__builtin_inff();
+
+// ---------------------------------------------------------------------------
+// Kernel argument blocks (plain data; built on the host by the C ABI layer)
+// ---------------------------------------------------------------------------
+
+struct TensorArg {
+  const void* ptr;
+  int64_t sb, ss, sh;  // element strides (batch, token, head); head dim contiguous
+};
+
+struct OutArg {
+  void* ptr;
+  int64_t sb, ss, sh;
+  int f32;  // 1: float32 output, 0: bf16
+};
+
+struct PatternArg {
+  int kind;  // 0 dense, 1 block lists, 2 vertical-slash
+  int block_M, block_N, cap, col_cap;
+  const int32_t* count;
+  const int32_t* index;
+  const int32_t* col_count;
+  const int32_t* col_index;
+  int64_t s_b, s_h, s_q;
+};
+
+// ---------------------------------------------------------------------------
+// Small helpers
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Round two floats to bf16 (nearest-even) and pack: lo in bits 0..15.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  __bf16 a = (__bf16)lo;
+  __bf16 b = (__bf16)hi;
+  uint16_t ua = __builtin_bit_cast(uint16_t, a);
+  uint16_t ub = __builtin_bit_cast(uint16_t, b);
+  return (uint32_t)ua | ((uint32_t)ub << 16);
+}
+
+__device__ __forceinline__ uint16_t to_bf16_bits(float x) {
+  __bf16 a = (__bf16)x;
+  return __builtin_bit_cast(uint16_t, a);
+}
+
+// 16-bit halves of two dwords: (a.lo, b.lo) and (a.hi, b.hi).
+__device__ __forceinline__ uint32_t lo_halves(uint32_t a, uint32_t b) { return (a & 0xFFFFu) | (b << 16); }
+__device__ __forceinline__ uint32_t hi_halves(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xFFFF0000u); }
+
+__device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, 64); }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ bf16x4 as_bf16x4(u32x2 v) { return __builtin_bit_cast(bf16x4, v); }
+
+__device__ __forceinline__ u32x4 ldg128(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16x16x16(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// Store 4 consecutive head-dim values of one output row.
+__device__ __forceinline__ void store4(const OutArg& o, int64_t off, float a, float b, float c, float d) {
+  if (o.f32) {
+    f32x4 v = {a, b, c, d};
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(o.ptr) + off) = v;
+  } else {
+    u32x2 v = {pack_bf16x2(a, b), pack_bf16x2(c, d)};
+    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(o.ptr) + off) = v;
+  }
+}
+
+}  // namespace bsa

@@ -1,0 +1,241 @@
+// Split-KV decode kernel: few query rows per key/value head, many keys.
+//
+// Computes attention restricted to listed key blocks ("Sparse FlashAttention
+// with Incremental Repair", Usage 1) for problems whose query rows per
+// key/value head fit one 16-wide MFMA tile: the G query heads that share a
+// key/value head (and share its block list) are packed together with the Sq
+// query positions into at most 16 rows, so every K/V byte is read once per
+// group.  The list of a group is cut into splits; each workgroup streams its
+// split's 64-key chunks through LDS and writes either the final (O, LSE) or a
+// float32 partial that the combine kernel merges (log-sum-exp combine, same
+// page, What's in this fork).
+//
+// Work decomposition: grid (splits, head groups, B), 256 threads = 4 waves.
+// Per 64-key chunk every thread loads D/32 16-byte pieces of K and of V
+// (coalesced: 16 or 8 lanes per 256/128-byte key row), K goes to LDS row-major,
+// V is transposed in registers and stored key-contiguous per head-dim row.
+// Wave w owns keys 16w..16w+15 of the chunk and keeps its own running
+// (max, sum, O^T); the four waves merge once at the end.
+//   S^T = K Q^T  : v_mfma_f32_16x16x32_bf16, D/32 per chunk (lane = query col)
+//   O^T += V^T P^T : v_mfma_f32_16x16x16_bf16, D/16 per chunk
+// so softmax statistics stay in one lane per query (plus one 4-lane reduce).
+// The next chunk's loads are issued before the current chunk's MFMAs.
+#pragma once
+#include "common.cuh"
+
+namespace bsa {
+
+struct DecodeArgs {
+  TensorArg q, k, v;
+  OutArg o;        // final output (direct mode)
+  float* lse;      // final LSE [B, Hq, Sq] or nullptr (direct mode)
+  float* part_o;   // partials [splits, B, Sq, Hq, D] (split mode)
+  float* part_lse; // partials [splits, B, Hq, Sq] (split mode)
+  PatternArg pat;
+  int B, Hq, Hkv, Sq, Sk, G, Gp, R;
+  int n_entries;          // dense: number of 64-key chunks; lists: entries per list (cap)
+  int entries_per_split;
+  int causal;
+  int direct;
+  float scale_log2;       // softmax_scale * log2(e)
+};
+
+template <int D, int CPE>  // CPE: 64-key chunks per list entry (block_N / 64); 1 for dense
+__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
+  constexpr int PIECES = D / 8;                // 16-byte pieces per key row
+  constexpr int KEYS_PER_PASS = 256 / PIECES;  // key rows one pass of 256 threads covers
+  constexpr int L = 64 / KEYS_PER_PASS;        // consecutive keys per thread (4 or 2)
+  constexpr int KS = D + 8;                    // Ks row stride in bf16 (pad: conflict-free b128 reads)
+  constexpr int VSTR = 64 + 8;                 // Vt row stride in bf16
+  constexpr int LDS_KV = (64 * KS + D * VSTR) * 2;
+  constexpr int LDS_MERGE = (4 * 16 * D + 2 * 64) * 4;
+  constexpr int LDS_BYTES = LDS_KV > LDS_MERGE ? LDS_KV : LDS_MERGE;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[LDS_BYTES];
+  uint16_t* Ks = reinterpret_cast<uint16_t*>(smem);
+  uint16_t* Vt = Ks + 64 * KS;
+
+  const int t = threadIdx.x;
+  const int w = t >> 6, l = t & 63;
+  const int lr = l & 15, kg = l >> 4;
+  const int sp = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
+
+  // ---- query rows of this lane (MFMA column lr) ----
+  const int rho = lr;
+  const bool row_ok = rho < a.R;
+  const int s_row = row_ok ? rho / a.Gp : 0;
+  const int hq_row = hg * a.Gp + (row_ok ? rho % a.Gp : 0);
+  const int hkv = (hg * a.Gp) / a.G;
+  const int lim = a.causal ? s_row + (a.Sk - a.Sq) : 0x7fffffff;
+
+  bf16x8 qreg[D / 32];
+  {
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q.ptr) + b * a.q.sb + (int64_t)s_row * a.q.ss +
+                         (int64_t)hq_row * a.q.sh + kg * 8;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+      u32x4 v = row_ok ? ldg128(qp + ks * 32) : u32x4{0, 0, 0, 0};
+      qreg[ks] = as_bf16x8(v);
+    }
+  }
+
+  // ---- this split's entries ----
+  int n_list;
+  const int32_t* list = nullptr;
+  if (a.pat.kind == 0) {
+    n_list = a.n_entries;
+  } else {
+    const int64_t lb = b * a.pat.s_b + hg * a.pat.s_h;
+    n_list = a.pat.count[lb];
+    list = a.pat.index + lb * a.pat.cap;
+  }
+  const int e0 = sp * a.entries_per_split;
+  const int e1 = min(n_list, e0 + a.entries_per_split);
+  const int nchunks = e1 > e0 ? (e1 - e0) * CPE : 0;
+
+  const int c = t % PIECES, kk = t / PIECES;
+  const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.k.ptr) + b * a.k.sb + (int64_t)hkv * a.k.sh + c * 8;
+  const uint16_t* vbase = reinterpret_cast<const uint16_t*>(a.v.ptr) + b * a.v.sb + (int64_t)hkv * a.v.sh + c * 8;
+
+  auto chunk_key0 = [&](int ci) -> int {
+    const int e = e0 + ci / CPE;
+    if (a.pat.kind == 0) return e * 64;
+    return list[e] * (64 * CPE) + (ci % CPE) * 64;
+  };
+
+  u32x4 kr[L], vr[L];
+  auto load_chunk = [&](int key0) {
+#pragma unroll
+    for (int j = 0; j < L; ++j) {
+      const int key = key0 + kk * L + j;
+      const bool ok = (unsigned)key < (unsigned)a.Sk;
+      kr[j] = ok ? ldg128(kbase + (int64_t)key * a.k.ss) : u32x4{0, 0, 0, 0};
+      vr[j] = ok ? ldg128(vbase + (int64_t)key * a.v.ss) : u32x4{0, 0, 0, 0};
+    }
+  };
+
+  float m_run = kNegInf, l_run = 0.f;
+  f32x4 oacc[D / 16];
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  int key0_next = nchunks > 0 ? chunk_key0(0) : 0;
+  if (nchunks > 0) load_chunk(key0_next);
+
+  for (int ci = 0; ci < nchunks; ++ci) {
+    const int key0 = key0_next;
+    __syncthreads();
+    // K row-major; V transposed to [d][key]
+#pragma unroll
+    for (int j = 0; j < L; ++j) *reinterpret_cast<u32x4*>(Ks + (kk * L + j) * KS + c * 8) = kr[j];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      uint16_t* dst0 = Vt + (c * 8 + 2 * p) * VSTR + kk * L;
+      uint16_t* dst1 = dst0 + VSTR;
+      if constexpr (L == 4) {
+        u32x2 ev = {lo_halves(vr[0][p], vr[1][p]), lo_halves(vr[2][p], vr[3][p])};
+        u32x2 od = {hi_halves(vr[0][p], vr[1][p]), hi_halves(vr[2][p], vr[3][p])};
+        *reinterpret_cast<u32x2*>(dst0) = ev;
+        *reinterpret_cast<u32x2*>(dst1) = od;
+      } else {
+        *reinterpret_cast<uint32_t*>(dst0) = lo_halves(vr[0][p], vr[1][p]);
+        *reinterpret_cast<uint32_t*>(dst1) = hi_halves(vr[0][p], vr[1][p]);
+      }
+    }
+    __syncthreads();
+    if (ci + 1 < nchunks) {
+      key0_next = chunk_key0(ci + 1);
+      load_chunk(key0_next);
+    }
+
+    // S^T for this wave's 16 keys
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+      const u32x4 kv = *reinterpret_cast<const u32x4*>(Ks + (w * 16 + lr) * KS + ks * 32 + kg * 8);
+      s = mfma16x16x32(as_bf16x8(kv), qreg[ks], s);
+    }
+    float sc[4];
+    float cmax = kNegInf;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int key = key0 + w * 16 + kg * 4 + r;
+      const bool ok = (unsigned)key < (unsigned)a.Sk && key <= lim;
+      sc[r] = ok ? s[r] * a.scale_log2 : kNegInf;
+      cmax = fmaxf(cmax, sc[r]);
+    }
+    cmax = fmaxf(cmax, shfl_xor_f(cmax, 16));
+    cmax = fmaxf(cmax, shfl_xor_f(cmax, 32));
+    const float m_new = fmaxf(m_run, cmax);
+    const float m_use = m_new == kNegInf ? 0.f : m_new;
+    const float alpha = exp2_fast(m_run - m_use);
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p[r] = exp2_fast(sc[r] - m_use);
+    l_run = l_run * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+    m_run = m_new;
+    const u32x2 pb = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+      oacc[db] *= alpha;
+      const u32x2 vv = *reinterpret_cast<const u32x2*>(Vt + (db * 16 + lr) * VSTR + w * 16 + kg * 4);
+      oacc[db] = mfma16x16x16(as_bf16x4(vv), as_bf16x4(pb), oacc[db]);
+    }
+  }
+
+  // ---- merge the four waves ----
+  l_run += shfl_xor_f(l_run, 16);
+  l_run += shfl_xor_f(l_run, 32);
+  __syncthreads();
+  float* mo = reinterpret_cast<float*>(smem);  // [4][16][D]
+  float* mm = mo + 4 * 16 * D;                 // [4][16]
+  float* ml = mm + 64;
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) mo[(w * 16 + lr) * D + db * 16 + kg * 4 + r] = oacc[db][r];
+  if (kg == 0) {
+    mm[w * 16 + lr] = m_run;
+    ml[w * 16 + lr] = l_run;
+  }
+  __syncthreads();
+
+  constexpr int DPT = D / 16;  // head-dim values per thread in the merge
+  const int row = t >> 4, dp = t & 15;
+  if (row >= a.R) return;
+  float M = kNegInf;
+#pragma unroll
+  for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, mm[ww * 16 + row]);
+  float wt[4], Lt = 0.f;
+  const float Mu = M == kNegInf ? 0.f : M;
+#pragma unroll
+  for (int ww = 0; ww < 4; ++ww) {
+    wt[ww] = exp2_fast(mm[ww * 16 + row] - Mu);
+    Lt += wt[ww] * ml[ww * 16 + row];
+  }
+  const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
+  const float lse_val = Lt > 0.f ? (M + __log2f(Lt)) * kLn2 : kNegInf;
+  float out[DPT];
+#pragma unroll
+  for (int i = 0; i < DPT; ++i) {
+    const int d = dp * DPT + i;
+    float acc = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) acc += wt[ww] * mo[(ww * 16 + row) * D + d];
+    out[i] = acc * inv;
+  }
+  const int s_o = row / a.Gp;
+  const int hq_o = hg * a.Gp + row % a.Gp;
+  if (a.direct) {
+    const int64_t off = b * a.o.sb + (int64_t)s_o * a.o.ss + (int64_t)hq_o * a.o.sh + dp * DPT;
+#pragma unroll
+    for (int i = 0; i < DPT; i += 4) store4(a.o, off + i, out[i], out[i + 1], out[i + 2], out[i + 3]);
+    if (dp == 0 && a.lse) a.lse[((int64_t)b * a.Hq + hq_o) * a.Sq + s_o] = lse_val;
+  } else {
+    float* po = a.part_o + ((((int64_t)sp * a.B + b) * a.Sq + s_o) * a.Hq + hq_o) * D + dp * DPT;
+#pragma unroll
+    for (int i = 0; i < DPT; i += 4) *reinterpret_cast<f32x4*>(po + i) = f32x4{out[i], out[i + 1], out[i + 2], out[i + 3]};
+    if (dp == 0) a.part_lse[(((int64_t)sp * a.B + b) * a.Hq + hq_o) * a.Sq + s_o] = lse_val;
+  }
+}
+
+}  // namespace bsa

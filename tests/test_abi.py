@@ -1,0 +1,101 @@
+"""Host-side checks of the C ABI: the library loads, exports every function include/bsa.h
+declares, and validates arguments before launching anything (no GPU needed: every call here
+returns an error status before any HIP work)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import long_context_attention_sparse_amd as bsa
+from long_context_attention_sparse_amd import _binding as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "bsa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bsa_\w+|vs_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bd.LIB_PATH):
+        pytest.fail("libbsa.so is not built (run __graft_entry__.build())")
+    return bd.load()
+
+
+def test_exports_match_header(lib):
+    declared = _header_functions()
+    assert set(declared) == set(bd.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        assert lib.bsa_status_string(code)
+    assert lib.bsa_status_string(99) == b"unknown status"
+
+
+def _prob(**kw):
+    base = dict(B=1, Hq=4, Hkv=2, Sq=1, Sk=256, D=128, cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=0,
+                max_seqlen_k=0, softmax_scale=0.0, causal=0)
+    base.update(kw)
+    return bd._Problem(**base)
+
+
+def _t(ptr=16, dtype=0, sb=256 * 2 * 128, ss=2 * 128, sh=128):
+    return bd._Tensor(ptr, dtype, sb, ss, sh)
+
+
+def _fwd(lib, prob, q=None, k=None, v=None, o=None, pat=None, ws=None, ws_bytes=0):
+    q = q or _t(sb=4 * 128, ss=4 * 128)
+    k = k or _t()
+    v = v or _t()
+    o = o or _t(sb=4 * 128, ss=4 * 128)
+    return lib.bsa_fwd(ctypes.byref(prob), q, k, v, ctypes.byref(pat) if pat else None, o, None, ws, ws_bytes, None)
+
+
+def test_fwd_argument_errors(lib):
+    assert lib.bsa_fwd(None, _t(), _t(), _t(), None, _t(), None, None, 0, None) == bd.BSA_ERR_INVALID_ARG
+    assert _fwd(lib, _prob(Hq=3, Hkv=2)) == bd.BSA_ERR_INVALID_ARG                # Hq % Hkv
+    assert _fwd(lib, _prob(B=0)) == bd.BSA_ERR_INVALID_ARG
+    assert _fwd(lib, _prob(D=96)) == bd.BSA_ERR_UNSUPPORTED                       # head dim
+    assert _fwd(lib, _prob(), q=_t(ptr=0)) == bd.BSA_ERR_INVALID_ARG              # null tensor
+    assert _fwd(lib, _prob(), k=_t(dtype=1)) == bd.BSA_ERR_UNSUPPORTED            # f32 inputs
+    assert _fwd(lib, _prob(), q=_t(ptr=18)) == bd.BSA_ERR_INVALID_ARG             # misaligned rows
+    assert _fwd(lib, _prob(), o=_t(dtype=7)) == bd.BSA_ERR_INVALID_ARG            # output dtype
+
+
+def test_pattern_errors(lib):
+    cnt = ctypes.c_int32(0)
+    idx = (ctypes.c_int32 * 4)()
+    addr = ctypes.addressof
+    pat = bd._Pattern(1, 2, 128, 96, 4, 0, addr(cnt), addr(idx), None, None, 0, 0, 0)
+    assert _fwd(lib, _prob(), pat=pat) == bd.BSA_ERR_UNSUPPORTED                  # block_N
+    pat = bd._Pattern(1, 3, 128, 64, 4, 0, addr(cnt), addr(idx), None, None, 0, 0, 0)
+    assert _fwd(lib, _prob(), pat=pat) == bd.BSA_ERR_INVALID_ARG                  # list heads
+    pat = bd._Pattern(1, 2, 128, 128, 4, 0, addr(cnt), addr(idx), None, None, 0, 0, 0)
+    assert _fwd(lib, _prob(Sk=320), pat=pat) == bd.BSA_ERR_INVALID_ARG            # Sk % block_N
+    pat = bd._Pattern(2, 4, 64, 64, 4, 4, addr(cnt), addr(idx), addr(cnt), addr(idx), 0, 0, 0)
+    assert _fwd(lib, _prob(causal=0), pat=pat) == bd.BSA_ERR_UNSUPPORTED          # VS needs causal
+    pat = bd._Pattern(9, 2, 64, 64, 4, 0, addr(cnt), addr(idx), None, None, 0, 0, 0)
+    assert _fwd(lib, _prob(), pat=pat) == bd.BSA_ERR_INVALID_ARG                  # kind
+
+
+def test_workspace_errors(lib):
+    prob = _prob(B=4, Hq=8, Hkv=2, Sk=4096)
+    need = lib.bsa_workspace_size(ctypes.byref(prob), None)
+    assert need > 0                                                               # split-KV decode needs scratch
+    assert _fwd(lib, prob) == bd.BSA_ERR_WORKSPACE
+    assert _fwd(lib, prob, ws=16, ws_bytes=need - 1) == bd.BSA_ERR_WORKSPACE
+
+
+def test_combine_and_partials_errors(lib):
+    assert lib.bsa_combine(0, 1, 1, 1, 128, 16, 16, _t(), None, None) == bd.BSA_ERR_INVALID_ARG
+    assert lib.bsa_combine(2, 1, 1, 1, 80, 16, 16, _t(), None, None) == bd.BSA_ERR_UNSUPPORTED
+    prob = _prob()
+    assert lib.bsa_fwd_partials(ctypes.byref(prob), _t(), _t(), _t(), None, 16, 16, None) == bd.BSA_ERR_UNSUPPORTED
+    assert lib.bsa_fwd_partials(ctypes.byref(prob), _t(), _t(), _t(), None, None, 16, None) == bd.BSA_ERR_INVALID_ARG
