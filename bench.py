@@ -1,0 +1,408 @@
+"""Benchmark of the block-sparse attention hot path on one MI355X.
+
+Default: the speculative + sparse decode workload (B=32, Hq=32, Hkv=8, D=128, Sk=32768;
+speculative pass over the last 2048 keys, repair pass over 25% of the earlier 64-key
+blocks, one combine).  A step is one full pass: both attention passes plus the combine.
+``--config N`` selects another workload (1 tiny decode, 3 block-sparse prefill, 4 gated
+prefill, 5 vertical-slash conversion + varlen prefill).
+
+Prints one JSON line: whole-step throughput (HBM GB/s of algorithmic bytes for decode,
+effective TFLOP/s over visited tiles for prefill), the dominant kernel's roofline figures
+measured with HIP events on the stream the kernels run on, and the float64 CPU oracle's
+rate on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+METRIC = "sparse-attn fwd: effective TFLOP/s (prefill), HBM GB/s (decode), ms/call"
+
+
+def _args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def _log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+class Timer:
+    """HIP events around named launches on torch's current stream (where the library enqueues)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.spans = {}
+
+    def span(self, name):
+        torch = self.torch
+        timer = self
+
+        class _S:
+            def __enter__(self):
+                self.a = torch.cuda.Event(enable_timing=True)
+                self.b = torch.cuda.Event(enable_timing=True)
+                self.a.record()
+
+            def __exit__(self, *exc):
+                self.b.record()
+                timer.spans.setdefault(name, []).append((self.a, self.b))
+        return _S()
+
+    def mean_ms(self, name):
+        return float(np.mean([a.elapsed_time(b) for a, b in self.spans[name]]))
+
+    def reset(self):
+        self.spans = {}
+
+
+def run_steps(torch, step, timer, steps, warmup):
+    for _ in range(warmup):
+        step(timer)
+    torch.cuda.synchronize()
+    timer.reset()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(timer)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def cpu_rate(fn, units, budget_s):
+    """Run fn(unit) over units, BLAS limited to one thread, until the budget is spent;
+    returns (units done, seconds)."""
+    from threadpoolctl import threadpool_limits
+
+    done, t0 = 0, time.perf_counter()
+    with threadpool_limits(limits=1):
+        for u in units:
+            fn(u)
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+    return done, time.perf_counter() - t0
+
+
+# ---------------------------------------------------------------------------
+# Workload 2: speculative + sparse decode (default)
+# ---------------------------------------------------------------------------
+
+def bench_spec_decode(torch, bsa, args):
+    from synth import to_torch_bf16
+    from synth.workloads import spec_sparse_decode
+
+    _log("generating speculative+sparse decode inputs")
+    w = spec_sparse_decode()
+    dev = torch.device("cuda:0")
+    q, k, v = (to_torch_bf16(w[n]).to(dev) for n in ("q", "k", "v"))
+    B, Hq, Hkv, D, Sk, bs = w["B"], w["Hq"], w["Hkv"], w["D"], w["Sk"], w["block_size"]
+    s0 = w["spec_start"]
+    n_missed = w["missed"].shape[-1]
+    count = torch.full((B, Hkv, 1), n_missed, dtype=torch.int32, device=dev)
+    index = torch.from_numpy(np.ascontiguousarray(w["missed"][:, :, None, :])).to(dev)
+    missed = bsa.BlockPattern(count, index, 128, bs)
+    k_spec, v_spec = k[:, s0:], v[:, s0:]
+    o_part, lse_part, p1 = bsa.speculative_buffers(q, k_spec, k, missed, True)
+    out = torch.empty((B, 1, Hq, D), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, Hq, 1), dtype=torch.float32, device=dev)
+
+    def step(timer):
+        with timer.span("speculative pass"):
+            bsa.bsa_fwd_partials(q, k_spec, v_spec, None, 0, causal=True, o_part=o_part[:p1], lse_part=lse_part[:p1])
+        with timer.span("repair pass"):
+            bsa.bsa_fwd_partials(q, k, v, missed, 0, causal=False, o_part=o_part[p1:], lse_part=lse_part[p1:])
+        with timer.span("combine"):
+            bsa.bsa_combine(o_part, lse_part, out=out, lse=lse)
+
+    timer = Timer(torch)
+    ms = run_steps(torch, step, timer, args.steps, args.warmup)
+    groups = B * Hkv
+    blk_bytes = bs * D * 2 * 2
+    kv_bytes = groups * (n_missed + (Sk - s0) // bs) * blk_bytes
+    io_bytes = q.numel() * 2 + out.numel() * 2 + lse.numel() * 4 + index.numel() * 4 + count.numel() * 4
+    step_bytes = kv_bytes + io_bytes
+    repair_bytes = groups * n_missed * blk_bytes + q.numel() * 2 + index.numel() * 4 + count.numel() * 4
+    repair_ms = timer.mean_ms("repair pass")
+    achieved = repair_bytes / (repair_ms * 1e-3) / 1e9
+    spans = {n: round(timer.mean_ms(n) * 1e3, 2) for n in timer.spans}
+    _log("per-launch us:", spans)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        G = Hq // Hkv
+        order = [(b, h) for b in range(B) for h in range(Hkv)]
+
+        def one(bh):
+            b, h = bh
+            hs = slice(h * G, (h + 1) * G)
+            oracle.speculative_sparse(w["q"][b:b + 1, :, hs], w["k"][b:b + 1, s0:, h:h + 1],
+                                      w["v"][b:b + 1, s0:, h:h + 1], w["k"][b:b + 1, :, h:h + 1],
+                                      w["v"][b:b + 1, :, h:h + 1], np.full((1, 1, 1), n_missed, np.int32),
+                                      w["missed"][b:b + 1, h:h + 1, None, :], bs, causal_spec=True)
+        done, secs = cpu_rate(one, order, args.cpu_seconds)
+        per_group = step_bytes / groups
+        cpu = {"value": round(done * per_group / secs / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"{done} of {groups} (batch, kv-head) groups of the same workload, float64 NumPy, "
+                         f"{secs:.1f} s, BLAS limited to 1 thread"}
+    value = step_bytes / (ms * 1e-3) / 1e9
+    return dict(
+        metric=METRIC, value=round(value, 2), unit="GB/s", ms_per_step=round(ms, 4), dtype="bf16",
+        config={"workload": "speculative+sparse decode", "B": B, "Hq": Hq, "Hkv": Hkv, "D": D, "Sk": Sk,
+                "block": bs, "spec_tokens": Sk - s0, "missed_blocks_per_group": n_missed,
+                "partials": int(o_part.shape[0]), "algorithmic_bytes_per_step": step_bytes,
+                "launch_us": spans},
+        roofline={"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                  "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                  "kernel": "decode_kernel<128,1> (repair pass)", "algorithmic_bytes": repair_bytes,
+                  "avg_ms": round(repair_ms, 5)},
+        cpu_baseline=cpu)
+
+
+# ---------------------------------------------------------------------------
+# Workload 1: tiny sparse decode (latency)
+# ---------------------------------------------------------------------------
+
+def bench_tiny(torch, bsa, args):
+    from synth import to_torch_bf16
+    from synth.workloads import tiny_decode
+
+    w = tiny_decode()
+    dev = torch.device("cuda:0")
+    q, k, v = (to_torch_bf16(w[n]).to(dev) for n in ("q", "k", "v"))
+    B, H = w["B"], w["Hq"]
+    pats = {}
+    for name in ("set_a", "set_b"):
+        lists = w[name]
+        pats[name] = bsa.BlockPattern(torch.full((B, H, 1), lists.shape[-1], dtype=torch.int32, device=dev),
+                                      torch.from_numpy(np.ascontiguousarray(lists[:, :, None, :])).to(dev), 128, 64)
+    o_part = torch.empty((2, B, 1, H, w["D"]), dtype=torch.float32, device=dev)
+    lse_part = torch.empty((2, B, H, 1), dtype=torch.float32, device=dev)
+    out = torch.empty((B, 1, H, w["D"]), dtype=torch.bfloat16, device=dev)
+
+    def step(timer):
+        with timer.span("set A"):
+            bsa.bsa_fwd(q, k, v, pats["set_a"], out=o_part[0], lse=lse_part[0])
+        with timer.span("set B"):
+            bsa.bsa_fwd(q, k, v, pats["set_b"], out=o_part[1], lse=lse_part[1])
+        with timer.span("combine"):
+            bsa.bsa_combine(o_part, lse_part, out=out)
+
+    timer = Timer(torch)
+    ms = run_steps(torch, step, timer, args.steps, args.warmup)
+    spans = {n: round(timer.mean_ms(n) * 1e3, 2) for n in timer.spans}
+    kv = B * H * 16 * 64 * w["D"] * 2 * 2
+    a_ms = timer.mean_ms("set A")
+    a_bytes = B * H * 6 * 64 * w["D"] * 4
+    return dict(metric=METRIC, value=round(ms, 4), unit="ms/call", higher_is_better=False, ms_per_step=round(ms, 4),
+                dtype="bf16",
+                config={"workload": "tiny sparse decode (A, B, combine)", "B": B, "H": H, "D": w["D"], "Sk": w["Sk"],
+                        "block": 64, "kv_bytes": kv, "launch_us": spans},
+                roofline={"bound": "hbm", "achieved": round(a_bytes / (a_ms * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS,
+                          "unit": "GB/s", "frac": round(a_bytes / (a_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 6),
+                          "traffic": None, "kernel": "decode_kernel<64,1> (set A)"},
+                cpu_baseline=None)
+
+
+# ---------------------------------------------------------------------------
+# Workload 3: block-sparse causal prefill
+# ---------------------------------------------------------------------------
+
+def bench_block_prefill(torch, bsa, args):
+    from synth import to_torch_bf16
+    from synth.workloads import block_sparse_prefill
+
+    _log("generating block-sparse prefill inputs")
+    w = block_sparse_prefill()
+    dev = torch.device("cuda:0")
+    q, k, v = (to_torch_bf16(w[n]).to(dev) for n in ("q", "k", "v"))
+    pat = bsa.BlockPattern(torch.from_numpy(w["count"]).to(dev), torch.from_numpy(w["index"]).to(dev), 128, 128)
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((1, w["Hq"], w["Sq"]), dtype=torch.float32, device=dev)
+
+    def step(timer):
+        with timer.span("prefill"):
+            bsa.bsa_fwd(q, k, v, pat, causal=True, out=out, lse=lse)
+
+    timer = Timer(torch)
+    ms = run_steps(torch, step, timer, args.steps, args.warmup)
+    tiles = int(w["count"].sum())
+    flops = tiles * 4 * 128 ** 3
+    kms = timer.mean_ms("prefill")
+    tf = flops / (kms * 1e-3) / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        scale = 1.0 / np.sqrt(128)
+        g = np.random.default_rng(0)
+        units = [(int(h), int(i)) for h, i in zip(g.integers(0, 32, 4096), g.integers(0, 256, 4096))]
+        fl = [0]
+
+        def one(hi):
+            h, i = hi
+            ents = w["index"][0, h, i, :w["count"][0, h, i]]
+            keys = np.concatenate([np.arange(j * 128, (j + 1) * 128) for j in ents])
+            rows = np.arange(i * 128, (i + 1) * 128)
+            oracle.attend_rows(w["q"][0, rows, h], w["k"][0, :, h // 4], w["v"][0, :, h // 4],
+                               [keys[keys <= r] for r in rows], scale)
+            fl[0] += len(ents) * 4 * 128 ** 3
+        done, secs = cpu_rate(one, units, args.cpu_seconds)
+        cpu = {"value": round(fl[0] / secs / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+               "sample": f"{done} random (head, query block) tiles rows of the same workload, float64, {secs:.1f} s"}
+    return dict(metric=METRIC, value=round(flops / (ms * 1e-3) / 1e12, 2), unit="TFLOP/s", ms_per_step=round(ms, 4),
+                dtype="bf16",
+                config={"workload": "block-sparse causal prefill", "B": 1, "Hq": 32, "Hkv": 8, "S": w["Sq"], "D": 128,
+                        "tile": 128, "visited_tiles": tiles, "flops": flops},
+                roofline={"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                          "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                          "kernel": "prefill_kernel<4,1>", "avg_ms": round(kms, 4)},
+                cpu_baseline=cpu)
+
+
+# ---------------------------------------------------------------------------
+# Workload 4: gated prefill
+# ---------------------------------------------------------------------------
+
+def bench_gated(torch, bsa, args):
+    from synth import to_torch_bf16
+    from synth.workloads import gated_prefill, thresholds_from_tile_max
+
+    _log("generating gated prefill inputs")
+    w = gated_prefill()
+    dev = torch.device("cuda:0")
+    q, k, v = (to_torch_bf16(w[n]).to(dev) for n in ("q", "k", "v"))
+    Hq, S = w["Hq"], w["Sq"]
+    nqb = S // 128
+    # Threshold calibration (the one-time step the gating method describes): exact tile maxima
+    # of this input from the kernel with every tile kept, then per query block the gap
+    # midpoint nearest half of the off-diagonal tiles.  Not used by any parity check.
+    T_all = torch.full((1, Hq, nqb), float("-inf"), dtype=torch.float32, device=dev)
+    _, _, _, tmax = bsa.bsa_fwd_gated(q, k, v, T_all, return_mask=False, return_tile_max=True)
+    tm = tmax.cpu().numpy()
+    T = np.array([[[thresholds_from_tile_max(tm[0, h, i], i) for i in range(nqb)] for h in range(Hq)]], np.float32)
+    Td = torch.from_numpy(T).to(dev)
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    keep = [None]
+
+    def step(timer):
+        with timer.span("gated"):
+            o, l, kmask, _ = bsa.bsa_fwd_gated(q, k, v, Td, out=out)
+        keep[0] = kmask
+
+    def step_dense(timer):
+        with timer.span("ungated"):
+            bsa.bsa_fwd_gated(q, k, v, T_all, out=out, return_mask=False)
+
+    timer = Timer(torch)
+    ms = run_steps(torch, step, timer, args.steps, args.warmup)
+    kms = timer.mean_ms("gated")
+    km = keep[0].cpu().numpy()
+    lower = np.tril(np.ones((nqb, nqb), bool))
+    kept = int(km[..., lower].sum())
+    causal_tiles = Hq * int(lower.sum())
+    flops = causal_tiles * 2 * 128 ** 3 + kept * 2 * 128 ** 3
+    timer2 = Timer(torch)
+    ms_dense = run_steps(torch, step_dense, timer2, max(3, args.steps // 4), 2)
+    tf = flops / (kms * 1e-3) / 1e12
+    off = lower & ~np.eye(nqb, dtype=bool)
+    skip = 1.0 - float(km[..., off].mean())
+    return dict(metric=METRIC, value=round(flops / (ms * 1e-3) / 1e12, 2), unit="TFLOP/s", ms_per_step=round(ms, 4),
+                dtype="bf16",
+                config={"workload": "BSFA gated causal prefill", "B": 1, "Hq": Hq, "Hkv": 8, "S": S, "D": 128,
+                        "tile": 128, "skip_fraction_offdiag": round(skip, 4), "flops": flops,
+                        "ungated_ms": round(ms_dense, 4), "gated_speedup": round(ms_dense / ms, 3)},
+                roofline={"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                          "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None, "kernel": "gated_kernel",
+                          "avg_ms": round(kms, 4)},
+                cpu_baseline=None)
+
+
+# ---------------------------------------------------------------------------
+# Workload 5: vertical-slash conversion + varlen prefill
+# ---------------------------------------------------------------------------
+
+def bench_vs(torch, bsa, args):
+    from synth import to_torch_bf16
+    from synth.workloads import vs_varlen_prefill
+
+    _log("generating vertical-slash inputs")
+    w = vs_varlen_prefill()
+    dev = torch.device("cuda:0")
+    q, k, v = (to_torch_bf16(w[n]).to(dev) for n in ("q", "k", "v"))
+    sl = torch.from_numpy(w["seqlens"]).to(dev)
+    vert = torch.from_numpy(w["vertical"]).to(dev)
+    slash = torch.from_numpy(w["slash"]).to(dev)
+    cu = torch.from_numpy(w["cu_seqlens"]).to(dev)
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w["H"], q.shape[0]), dtype=torch.float32, device=dev)
+    res = {}
+
+    def step(timer):
+        with timer.span("convert"):
+            bc, bo, cc, ci = bsa.vs_convert_indexes(sl, sl, vert, slash, w["context_size"], 64, 64)
+        with timer.span("attention"):
+            bsa.bsa_fwd(q, k, v, bsa.VSPattern(bc, bo, cc, ci, 64, 64), causal=True, out=out, lse=lse,
+                        cu_seqlens_q=cu, cu_seqlens_k=cu, max_seqlen_q=w["max_seqlen"], max_seqlen_k=w["max_seqlen"])
+        res["m"] = (bc, cc)
+
+    timer = Timer(torch)
+    ms = run_steps(torch, step, timer, args.steps, args.warmup)
+    bc, cc = (x.cpu().numpy().astype(np.int64) for x in res["m"])
+    flops = int((4 * 64 * 128 * (64 * bc + cc)).sum())
+    ams = timer.mean_ms("attention")
+    cms = timer.mean_ms("convert")
+    conv_bytes = int(4 * (bc.sum() + cc.sum() + bc.size + cc.size))
+    tf = flops / (ams * 1e-3) / 1e12
+    return dict(metric=METRIC, value=round(flops / (ms * 1e-3) / 1e12, 2), unit="TFLOP/s", ms_per_step=round(ms, 4),
+                dtype="bf16",
+                config={"workload": "vertical-slash conversion + varlen causal prefill", "seqlens": [65536, 32768],
+                        "H": 32, "D": 128, "block": 64, "nnz_v": 1000, "nnz_s": 2000, "flops": flops,
+                        "convert_ms": round(cms, 4), "convert_output_bytes": conv_bytes},
+                roofline={"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                          "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None, "kernel": "prefill_kernel<2,2>",
+                          "avg_ms": round(ams, 4)},
+                cpu_baseline=None)
+
+
+def main():
+    args = _args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the kernels are single-GPU and "
+              "the multi-GPU sharding is a design note, not part of this build.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import long_context_attention_sparse_amd as bsa
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    bsa.load()
+    fn = {1: bench_tiny, 2: bench_spec_decode, 3: bench_block_prefill, 4: bench_gated, 5: bench_vs}[args.config]
+    res = fn(torch, bsa, args)
+    line = {"metric": res["metric"], "value": res["value"], "unit": res["unit"], "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": res["ms_per_step"],
+            "higher_is_better": res.get("higher_is_better", True), "scaling": "weak", "vs_baseline": None,
+            "dtype": res["dtype"], "data": "synthetic", "config": res["config"], "roofline": res["roofline"],
+            "cpu_baseline": res["cpu_baseline"]}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -143,15 +143,25 @@ bsa_status bsa_fwd(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, bsa_tens
                    const bsa_pattern* pat, bsa_tensor o, float* lse, void* ws, size_t ws_bytes,
                    bsa_stream stream);
 
-/* One (o, lse) partial per list entry.  [IR] Usage 3 (per-block partials).
- *   pat       a BLOCK pattern (fixed length only).
- *   o_part    float32 [cap, B, Sq, Hq, D] contiguous; entry e of a list with
- *             at most e entries is written as (0, -inf).
- *   lse_part  float32 [cap, B, Hq, Sq] contiguous.
- * The partials merge back with bsa_combine into bsa_fwd's result.
- * Errors as for bsa_fwd. */
+/* (o, lse) partials over consecutive groups of pattern entries.  [IR] Usage 3
+ * (per-block partials: entries_per_partial = 1 gives one partial per table
+ * entry) and What's in this fork (partials merge exactly with the combine).
+ * Entries are the list entries of a BLOCK pattern, or the 64-key blocks
+ * [64e, 64e + 64) of a DENSE pattern (pat NULL).  Partial p covers entries
+ * [p*E, (p+1)*E) of each list, E = entries_per_partial (E <= 0 lets the
+ * library choose, as it does for its own split-KV decode); a partial with no
+ * entries is (0, -inf).  The partials of two passes written into one buffer
+ * merge with a single bsa_combine.
+ *   o_part    float32 [P, B, Sq, Hq, D] contiguous.
+ *   lse_part  float32 [P, B, Hq, Sq] contiguous.
+ *   P = bsa_num_partials(prob, pat, entries_per_partial).
+ * Fixed length only; VS patterns are not accepted.  Errors as for bsa_fwd. */
 bsa_status bsa_fwd_partials(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, bsa_tensor v,
-                            const bsa_pattern* pat, float* o_part, float* lse_part, bsa_stream stream);
+                            const bsa_pattern* pat, int32_t entries_per_partial, float* o_part, float* lse_part,
+                            bsa_stream stream);
+
+/* Number of partials bsa_fwd_partials writes for these arguments (-1 if invalid). */
+int32_t bsa_num_partials(const bsa_problem* prob, const bsa_pattern* pat, int32_t entries_per_partial);
 
 /* Log-sum-exp combine of P partials.  [IR] What's in this fork (combine
  * identity FA(A u B) == Combine(FA(A), FA(B))) and Usage 2.

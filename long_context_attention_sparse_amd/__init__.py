@@ -12,9 +12,9 @@ include/bsa.h and only marshals arguments — the kernels do all the work:
   speculative_sparse  dense speculative pass + sparse repair pass + combine
 """
 from ._binding import (EXPORTS, LIB_PATH, BlockPattern, BSAError, VSPattern, bsa_combine, bsa_fwd, bsa_fwd_gated,
-                       bsa_fwd_partials, bsa_workspace_size, load, speculative_buffers, speculative_sparse,
+                       bsa_fwd_partials, bsa_num_partials, bsa_workspace_size, load, speculative_buffers, speculative_sparse,
                        vs_convert_indexes)
 
 __all__ = ["EXPORTS", "LIB_PATH", "BlockPattern", "BSAError", "VSPattern", "bsa_combine", "bsa_fwd", "bsa_fwd_gated",
-           "bsa_fwd_partials", "bsa_workspace_size", "load", "speculative_buffers", "speculative_sparse",
+           "bsa_fwd_partials", "bsa_num_partials", "bsa_workspace_size", "load", "speculative_buffers", "speculative_sparse",
            "vs_convert_indexes"]

@@ -9,7 +9,6 @@ library raises immediately.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 from dataclasses import dataclass
 from typing import Optional
@@ -23,8 +22,8 @@ BSA_OK, BSA_ERR_INVALID_ARG, BSA_ERR_UNSUPPORTED, BSA_ERR_WORKSPACE, BSA_ERR_HIP
 BSA_BF16, BSA_F32 = 0, 1
 BSA_PAT_DENSE, BSA_PAT_BLOCK, BSA_PAT_VS = 0, 1, 2
 
-EXPORTS = ("bsa_status_string", "bsa_workspace_size", "bsa_fwd", "bsa_fwd_partials", "bsa_combine",
-           "bsa_fwd_gated", "vs_convert_indexes")
+EXPORTS = ("bsa_status_string", "bsa_workspace_size", "bsa_fwd", "bsa_fwd_partials", "bsa_num_partials",
+           "bsa_combine", "bsa_fwd_gated", "vs_convert_indexes")
 
 
 class BSAError(RuntimeError):
@@ -73,7 +72,9 @@ def load(path: str = LIB_PATH):
                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.bsa_fwd_partials.restype = ctypes.c_int
     lib.bsa_fwd_partials.argtypes = [ctypes.POINTER(_Problem), _Tensor, _Tensor, _Tensor, ctypes.POINTER(_Pattern),
-                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+                                     ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.bsa_num_partials.restype = ctypes.c_int32
+    lib.bsa_num_partials.argtypes = [ctypes.POINTER(_Problem), ctypes.POINTER(_Pattern), ctypes.c_int32]
     lib.bsa_combine.restype = ctypes.c_int
     lib.bsa_combine.argtypes = [ctypes.c_int32] * 5 + [ctypes.c_void_p, ctypes.c_void_p, _Tensor, ctypes.c_void_p,
                                                       ctypes.c_void_p]
@@ -234,17 +235,41 @@ def bsa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pattern=None, *, 
     return out, lse
 
 
-def bsa_fwd_partials(q, k, v, pattern: BlockPattern, *, causal: bool = False, softmax_scale=None, stream=None):
-    """One (o, lse) per list entry: o_part [cap, B, Sq, Hq, D], lse_part [cap, B, Hq, Sq] (float32)."""
+def bsa_num_partials(q, k, pattern=None, entries_per_partial: int = 1, causal: bool = False) -> int:
+    prob = _problem(q, k, causal, None)
+    pat = pattern.struct(prob.Hq) if pattern is not None else None
+    n = int(load().bsa_num_partials(ctypes.byref(prob), ctypes.byref(pat) if pat is not None else None,
+                                    int(entries_per_partial)))
+    if n < 0:
+        raise BSAError("bsa_num_partials", BSA_ERR_INVALID_ARG, "invalid arguments")
+    return n
+
+
+def bsa_fwd_partials(q, k, v, pattern=None, entries_per_partial: int = 1, *, causal: bool = False,
+                     softmax_scale=None, o_part: Optional[torch.Tensor] = None,
+                     lse_part: Optional[torch.Tensor] = None, stream=None):
+    """(o, lse) partials over groups of ``entries_per_partial`` pattern entries (1 = one per
+    list entry; a dense pattern's entries are 64-key blocks).  Returns
+    o_part [P, B, Sq, Hq, D] and lse_part [P, B, Hq, Sq] (float32); given buffers (views into a
+    larger partial buffer, for instance) are filled in place."""
     lib = load()
     prob = _problem(q, k, causal, softmax_scale)
-    pat = pattern.struct(prob.Hq)
-    cap = pat.cap
+    pat = pattern.struct(prob.Hq) if pattern is not None else None
+    pat_p = ctypes.byref(pat) if pat is not None else None
+    P = int(lib.bsa_num_partials(ctypes.byref(prob), pat_p, int(entries_per_partial)))
+    if P < 0:
+        raise BSAError("bsa_fwd_partials", BSA_ERR_INVALID_ARG, "invalid arguments")
     B, Sq, Hq, D = q.shape
-    o_part = torch.empty((cap, B, Sq, Hq, D), dtype=torch.float32, device=q.device)
-    lse_part = torch.empty((cap, B, Hq, Sq), dtype=torch.float32, device=q.device)
-    st = lib.bsa_fwd_partials(ctypes.byref(prob), _tensor(q), _tensor(k), _tensor(v), ctypes.byref(pat),
-                              _ptr(o_part), _ptr(lse_part), _stream(stream))
+    if o_part is None:
+        o_part = torch.empty((P, B, Sq, Hq, D), dtype=torch.float32, device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty((P, B, Hq, Sq), dtype=torch.float32, device=q.device)
+    if tuple(o_part.shape) != (P, B, Sq, Hq, D) or tuple(lse_part.shape) != (P, B, Hq, Sq):
+        raise ValueError(f"partial buffers must be [{P}, B, Sq, Hq, D] and [{P}, B, Hq, Sq]")
+    if not (o_part.is_contiguous() and lse_part.is_contiguous()):
+        raise ValueError("partial buffers must be contiguous")
+    st = lib.bsa_fwd_partials(ctypes.byref(prob), _tensor(q), _tensor(k), _tensor(v), pat_p,
+                              int(entries_per_partial), _ptr(o_part), _ptr(lse_part), _stream(stream))
     _check("bsa_fwd_partials", st)
     return o_part, lse_part
 
@@ -312,34 +337,29 @@ def vs_convert_indexes(q_seqlens, kv_seqlens, vertical_indexes, slash_indexes, c
 
 
 def speculative_sparse(q, k_spec, v_spec, k, v, missed: BlockPattern, *, causal_spec: bool = True,
-                       softmax_scale=None, out_dtype: torch.dtype = torch.bfloat16, stream=None, buffers=None):
+                       softmax_scale=None, out_dtype: torch.dtype = torch.bfloat16, out=None, stream=None,
+                       buffers=None):
     """Speculative + sparse decoding with exact combine ("Sparse FlashAttention with
-    Incremental Repair", Usage 2): dense attention over (k_spec, v_spec) with the causal
-    flag, sparse attention over the missed blocks of (k, v) without a mask, and the
-    log-sum-exp combine of the two partials.  Returns (out, lse)."""
-    B, Sq, Hq, D = q.shape
+    Incremental Repair", Usage 2): attention over (k_spec, v_spec) with the causal flag
+    (the speculative pass), attention over the missed blocks of (k, v) without a mask (the
+    repair pass), and the log-sum-exp combine.  Both passes write split partials into one
+    buffer and a single combine merges them all.  Returns (out, lse)."""
     if buffers is None:
         buffers = speculative_buffers(q, k_spec, k, missed, causal_spec)
-    o_part, lse_part, ws1, ws2 = buffers
-    bsa_fwd(q, k_spec, v_spec, None, causal=causal_spec, softmax_scale=softmax_scale, out=o_part[0],
-            lse=lse_part[0], workspace=ws1, stream=stream)
-    bsa_fwd(q, k, v, missed, causal=False, softmax_scale=softmax_scale, out=o_part[1], lse=lse_part[1],
-            workspace=ws2, stream=stream)
-    return bsa_combine(o_part, lse_part, out_dtype=out_dtype, stream=stream)
+    o_part, lse_part, p1 = buffers
+    bsa_fwd_partials(q, k_spec, v_spec, None, 0, causal=causal_spec, softmax_scale=softmax_scale,
+                     o_part=o_part[:p1], lse_part=lse_part[:p1], stream=stream)
+    bsa_fwd_partials(q, k, v, missed, 0, causal=False, softmax_scale=softmax_scale, o_part=o_part[p1:],
+                     lse_part=lse_part[p1:], stream=stream)
+    return bsa_combine(o_part, lse_part, out=out, out_dtype=out_dtype, stream=stream)
 
 
 def speculative_buffers(q, k_spec, k, missed: BlockPattern, causal_spec: bool = True):
-    """Preallocated partials and workspaces for ``speculative_sparse`` (reusable across calls)."""
+    """Partial buffers for ``speculative_sparse`` (reusable across calls): (o_part, lse_part, P1)."""
     B, Sq, Hq, D = q.shape
-    dev = q.device
-    o_part = torch.empty((2, B, Sq, Hq, D), dtype=torch.float32, device=dev)
-    lse_part = torch.empty((2, B, Hq, Sq), dtype=torch.float32, device=dev)
-    n1 = bsa_workspace_size(q, k_spec, None, causal_spec)
-    n2 = bsa_workspace_size(q, k, missed, False)
-    ws1 = torch.empty(max(n1, 1), dtype=torch.uint8, device=dev)
-    ws2 = torch.empty(max(n2, 1), dtype=torch.uint8, device=dev)
-    return o_part, lse_part, ws1, ws2
+    p1 = bsa_num_partials(q, k_spec, None, 0, causal_spec)
+    p2 = bsa_num_partials(q, k, missed, 0, False)
+    o_part = torch.empty((p1 + p2, B, Sq, Hq, D), dtype=torch.float32, device=q.device)
+    lse_part = torch.empty((p1 + p2, B, Hq, Sq), dtype=torch.float32, device=q.device)
+    return o_part, lse_part, p1
 
-
-def default_scale(D: int) -> float:
-    return 1.0 / math.sqrt(D)

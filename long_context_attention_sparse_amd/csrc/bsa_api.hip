@@ -14,6 +14,9 @@
 #include "bsa.h"
 #include "combine.cuh"
 #include "decode.cuh"
+#include "gated.cuh"
+#include "prefill.cuh"
+#include "vs_convert.cuh"
 
 using namespace bsa;
 
@@ -193,6 +196,72 @@ bsa_status run_decode(const bsa_problem& p, const DecodePlan& d, const bsa_tenso
   return launch_status();
 }
 
+
+// ---------------------------------------------------------------------------
+// Prefill path
+// ---------------------------------------------------------------------------
+
+template <int NW, int KIND>
+void launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((prefill_kernel<NW, KIND>), dim3(a.n_items), dim3(NW * 64), 0, st, a);
+}
+
+bsa_status run_prefill(const bsa_problem& p, const bsa_tensor& q, const bsa_tensor& k, const bsa_tensor& v,
+                       const bsa_pattern* pat, const bsa_tensor* o, float* lse, int epp, int n_part, float* part_o,
+                       float* part_lse, hipStream_t st) {
+  if (p.D != 128) return BSA_ERR_UNSUPPORTED;
+  const int kind = pat ? pat->kind : BSA_PAT_DENSE;
+  const int BM = kind == BSA_PAT_DENSE ? 128 : pat->block_M;
+  const int Sq = p.cu_seqlens_q ? p.max_seqlen_q : p.Sq;
+  PrefillArgs a{};
+  a.q = targ(q);
+  a.k = targ(k);
+  a.v = targ(v);
+  a.pat = parg(pat);
+  a.cu_q = p.cu_seqlens_q;
+  a.cu_k = p.cu_seqlens_k;
+  a.B = p.B;
+  a.Hq = p.Hq;
+  a.Hkv = p.Hkv;
+  a.G = p.Hq / p.Hkv;
+  a.Sq = Sq;
+  a.Sk = p.cu_seqlens_q ? p.max_seqlen_k : p.Sk;
+  a.nqb = (Sq + BM - 1) / BM;
+  a.list_by_kv = pat && kind != BSA_PAT_DENSE && pat->Ht == p.Hkv && p.Hkv != p.Hq;
+  a.causal = p.causal != 0;
+  a.scale_log2 = scale_of(p) * kLog2e;
+  const int64_t items = (int64_t)p.B * p.Hq * a.nqb;
+  if (items > INT_MAX) return BSA_ERR_UNSUPPORTED;
+  a.n_items = (int)items;
+  if (o) {
+    a.o = oarg(*o);
+    a.lse = lse;
+  } else {
+    a.partial = 1;
+    a.epp = epp;
+    a.n_part = n_part;
+    a.part_o = part_o;
+    a.part_lse = part_lse;
+  }
+  if (BM == 128) {
+    if (kind == BSA_PAT_DENSE) launch_prefill_t<4, 0>(a, st);
+    else if (kind == BSA_PAT_BLOCK) launch_prefill_t<4, 1>(a, st);
+    else launch_prefill_t<4, 2>(a, st);
+  } else {
+    if (kind == BSA_PAT_DENSE) launch_prefill_t<2, 0>(a, st);
+    else if (kind == BSA_PAT_BLOCK) launch_prefill_t<2, 1>(a, st);
+    else launch_prefill_t<2, 2>(a, st);
+  }
+  return launch_status();
+}
+
+// Entries (list entries, or 64-key chunks for a dense pattern) and the number of
+// partials bsa_fwd_partials writes for a given grouping.
+int partial_entries(const bsa_problem& p, const bsa_pattern* pat) {
+  if (!pat || pat->kind == BSA_PAT_DENSE) return (p.Sk + 63) / 64;
+  return pat->cap;
+}
+
 }  // namespace
 
 extern "C" {
@@ -225,42 +294,56 @@ bsa_status bsa_fwd(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, bsa_tens
   if (st != BSA_OK) return st;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   const DecodePlan d = plan_decode(p, pat);
-  if (d.use) {
-    if (d.splits == 1) return run_decode(p, d, q, k, v, pat, nullptr, nullptr, &o, lse, hs);
-    const size_t need = decode_ws_bytes(p, d);
-    if (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 15)) return BSA_ERR_WORKSPACE;
-    const size_t rows = (size_t)p.B * p.Sq * p.Hq;
-    float* part_o = reinterpret_cast<float*>(ws);
-    float* part_lse = part_o + (size_t)d.splits * rows * p.D;
-    st = run_decode(p, d, q, k, v, pat, part_o, part_lse, nullptr, nullptr, hs);
-    if (st != BSA_OK) return st;
-    CombineArgs c{d.splits, p.B, p.Hq, p.Sq, p.D, part_o, part_lse, oarg(o), lse};
-    launch_combine(c, hs);
-    return launch_status();
+  if (!d.use) return run_prefill(p, q, k, v, pat, &o, lse, 0, 0, nullptr, nullptr, hs);
+  if (d.splits == 1) return run_decode(p, d, q, k, v, pat, nullptr, nullptr, &o, lse, hs);
+  const size_t need = decode_ws_bytes(p, d);
+  if (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 15)) return BSA_ERR_WORKSPACE;
+  const size_t rows = (size_t)p.B * p.Sq * p.Hq;
+  float* part_o = reinterpret_cast<float*>(ws);
+  float* part_lse = part_o + (size_t)d.splits * rows * p.D;
+  st = run_decode(p, d, q, k, v, pat, part_o, part_lse, nullptr, nullptr, hs);
+  if (st != BSA_OK) return st;
+  CombineArgs c{d.splits, p.B, p.Hq, p.Sq, p.D, part_o, part_lse, oarg(o), lse};
+  launch_combine(c, hs);
+  return launch_status();
+}
+
+int32_t bsa_num_partials(const bsa_problem* prob, const bsa_pattern* pat, int32_t entries_per_partial) {
+  if (!prob || prob->B <= 0 || prob->Hkv <= 0 || prob->Sk <= 0 || prob->Hq % prob->Hkv) return -1;
+  if (check_pattern(*prob, pat) != BSA_OK || (pat && pat->kind == BSA_PAT_VS)) return -1;
+  const int n = partial_entries(*prob, pat);
+  int e = entries_per_partial;
+  if (e <= 0) {
+    const DecodePlan d = plan_decode(*prob, pat);
+    e = d.use ? d.entries_per_split : 1;
   }
-  return BSA_ERR_UNSUPPORTED;
+  return n > 0 ? (n + e - 1) / e : 0;
 }
 
 bsa_status bsa_fwd_partials(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, bsa_tensor v,
-                            const bsa_pattern* pat, float* o_part, float* lse_part, bsa_stream stream) {
+                            const bsa_pattern* pat, int32_t entries_per_partial, float* o_part, float* lse_part,
+                            bsa_stream stream) {
   if (!o_part || !lse_part) return BSA_ERR_INVALID_ARG;
   bsa_tensor o_dummy{o_part, BSA_F32, 0, 0, 0};
   bsa_status st = check_problem(prob, q, k, v, o_dummy);
   if (st != BSA_OK) return st;
   const bsa_problem& p = *prob;
-  if (!pat || pat->kind != BSA_PAT_BLOCK || p.cu_seqlens_q) return BSA_ERR_UNSUPPORTED;
+  if (p.cu_seqlens_q || (pat && pat->kind == BSA_PAT_VS)) return BSA_ERR_UNSUPPORTED;
   st = check_pattern(p, pat);
   if (st != BSA_OK) return st;
-  if ((reinterpret_cast<uintptr_t>(o_part) & 15)) return BSA_ERR_INVALID_ARG;
-  if (pat->cap == 0) return BSA_OK;
-  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (reinterpret_cast<uintptr_t>(o_part) & 15) return BSA_ERR_INVALID_ARG;
+  const int n = partial_entries(p, pat);
   DecodePlan d = plan_decode(p, pat);
+  const int epp = entries_per_partial > 0 ? entries_per_partial : (d.use ? d.entries_per_split : 1);
+  const int n_part = n > 0 ? (n + epp - 1) / epp : 0;
+  if (n_part == 0) return BSA_OK;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   if (d.use) {
-    d.entries_per_split = 1;
-    d.splits = pat->cap;
+    d.entries_per_split = epp;
+    d.splits = n_part;
     return run_decode(p, d, q, k, v, pat, o_part, lse_part, nullptr, nullptr, hs);
   }
-  return BSA_ERR_UNSUPPORTED;
+  return run_prefill(p, q, k, v, pat, nullptr, nullptr, epp, n_part, o_part, lse_part, hs);
 }
 
 bsa_status bsa_combine(int32_t P, int32_t B, int32_t Hq, int32_t Sq, int32_t D, const float* o_part,
@@ -277,9 +360,34 @@ bsa_status bsa_combine(int32_t P, int32_t B, int32_t Hq, int32_t Sq, int32_t D, 
 bsa_status bsa_fwd_gated(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, bsa_tensor v, const float* T,
                          int32_t block_M, int32_t block_N, bsa_tensor o, float* lse, uint8_t* keep_mask,
                          float* tile_max, bsa_stream stream) {
-  (void)prob; (void)q; (void)k; (void)v; (void)T; (void)block_M; (void)block_N; (void)o; (void)lse;
-  (void)keep_mask; (void)tile_max; (void)stream;
-  return BSA_ERR_UNSUPPORTED;
+  bsa_status st = check_problem(prob, q, k, v, o);
+  if (st != BSA_OK) return st;
+  const bsa_problem& p = *prob;
+  if (!T) return BSA_ERR_INVALID_ARG;
+  if (block_M != 128 || block_N != 128 || p.D != 128) return BSA_ERR_UNSUPPORTED;
+  if (!p.causal || p.cu_seqlens_q || p.Sq != p.Sk || p.Sq % 128) return BSA_ERR_UNSUPPORTED;
+  GatedArgs a{};
+  a.q = targ(q);
+  a.k = targ(k);
+  a.v = targ(v);
+  a.o = oarg(o);
+  a.lse = lse;
+  a.T = T;
+  a.keep = keep_mask;
+  a.tmax = tile_max;
+  a.B = p.B;
+  a.Hq = p.Hq;
+  a.Hkv = p.Hkv;
+  a.G = p.Hq / p.Hkv;
+  a.S = p.Sq;
+  a.nqb = p.Sq / 128;
+  a.scale = scale_of(p);
+  a.scale_log2 = a.scale * kLog2e;
+  const int64_t items = (int64_t)p.B * p.Hq * a.nqb;
+  if (items > INT_MAX) return BSA_ERR_UNSUPPORTED;
+  a.n_items = (int)items;
+  hipLaunchKernelGGL(gated_kernel, dim3(a.n_items), dim3(256), 0, reinterpret_cast<hipStream_t>(stream), a);
+  return launch_status();
 }
 
 bsa_status vs_convert_indexes(const int32_t* q_seqlens, const int32_t* kv_seqlens, const int32_t* vertical,
@@ -287,10 +395,20 @@ bsa_status vs_convert_indexes(const int32_t* q_seqlens, const int32_t* kv_seqlen
                               int32_t context_size, int32_t block_M, int32_t block_N, int32_t causal,
                               int32_t* block_count, int32_t* block_offset, int32_t* column_count,
                               int32_t* column_index, bsa_stream stream) {
-  (void)q_seqlens; (void)kv_seqlens; (void)vertical; (void)slash; (void)B; (void)H; (void)nnz_v; (void)nnz_s;
-  (void)context_size; (void)block_M; (void)block_N; (void)causal; (void)block_count; (void)block_offset;
-  (void)column_count; (void)column_index; (void)stream;
-  return BSA_ERR_UNSUPPORTED;
+  if (!q_seqlens || !kv_seqlens || !block_count || !column_count) return BSA_ERR_INVALID_ARG;
+  if (B <= 0 || H <= 0 || nnz_v < 0 || nnz_s < 0 || context_size <= 0 || block_M <= 0 || block_N <= 0)
+    return BSA_ERR_INVALID_ARG;
+  if ((nnz_v > 0 && (!vertical || !column_index)) || (nnz_s > 0 && (!slash || !block_offset)))
+    return BSA_ERR_INVALID_ARG;
+  if (!causal || block_M > block_N) return BSA_ERR_UNSUPPORTED;
+  VSConvArgs a{q_seqlens, kv_seqlens, vertical, slash, B, H, nnz_v, nnz_s, 0, block_M, block_N,
+               block_count, block_offset, column_count, column_index};
+  a.rows = (context_size + block_M - 1) / block_M;
+  const int lds_ints = nnz_s + nnz_v <= kVSConvLdsInts ? nnz_s + nnz_v : 0;
+  dim3 grid((a.rows + kVSConvThreads - 1) / kVSConvThreads, B * H);
+  hipLaunchKernelGGL(vs_convert_kernel, grid, dim3(kVSConvThreads), lds_ints * sizeof(int32_t),
+                     reinterpret_cast<hipStream_t>(stream), a);
+  return launch_status();
 }
 
 }  // extern "C"

@@ -67,6 +67,11 @@ __device__ __forceinline__ uint16_t to_bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, a);
 }
 
+// Sum of the two bf16 values packed in a dword (exact widening, one fp32 add).
+__device__ __forceinline__ float bf16x2_sum(uint32_t u) {
+  return __uint_as_float(u << 16) + __uint_as_float(u & 0xFFFF0000u);
+}
+
 // 16-bit halves of two dwords: (a.lo, b.lo) and (a.hi, b.hi).
 __device__ __forceinline__ uint32_t lo_halves(uint32_t a, uint32_t b) { return (a & 0xFFFFu) | (b << 16); }
 __device__ __forceinline__ uint32_t hi_halves(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xFFFF0000u); }

@@ -171,9 +171,11 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     float p[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) p[r] = exp2_fast(sc[r] - m_use);
-    l_run = l_run * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-    m_run = m_new;
     const u32x2 pb = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+    // normaliser from the rounded weights the PV product uses: O is then an exact
+    // convex combination of V rows and the dominant key's rounding cancels
+    l_run = l_run * alpha + (bf16x2_sum(pb[0]) + bf16x2_sum(pb[1]));
+    m_run = m_new;
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) {
       oacc[db] *= alpha;

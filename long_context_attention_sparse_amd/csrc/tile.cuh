@@ -1,0 +1,131 @@
+// MFMA tile steps shared by the prefill and gated kernels (head dim 128,
+// 32 query rows per wave, v_mfma_f32_32x32x16_bf16).
+//
+// Layout conventions (lane l of a wave, lq = l % 32, hh = l / 32):
+//   Q^T operand  qreg[ks] = Q[row lq][16ks + 8hh .. +8]      (8 registers x 4 dwords)
+//   K in LDS     Ks[key][d], row stride KS (D + 8) bf16
+//   S^T block    lane holds query lq, keys 8(r/4) + 4hh + r%4 of the 32-key block (r = 0..15)
+//   V^T in LDS   Vt[d][pos], row stride VSTR; within each 16-key group the
+//                positions hold keys (0-3, 8-11, 4-7, 12-15) so that S^T
+//                registers 8hb..8hb+7 of a block are the P^T operand of the
+//                16-key MFMA step (block, hb) without any data movement
+//   O^T          oacc[db]: lane holds query lq, dims 32db + 8(r/4) + 4hh + r%4
+#pragma once
+#include "common.cuh"
+
+namespace bsa {
+
+constexpr int TD = 128;           // head dim of the tile kernels
+constexpr int TKS = TD + 8;       // K row stride in LDS (bf16)
+constexpr float kSlack = 8.0f;    // lazy rescale threshold (log2 units)
+
+// Position of the first key of a 4-key group inside the V^T row.
+__device__ __forceinline__ int vt_pos(int key4) {
+  const int grp = (key4 >> 2) & 3;
+  return (key4 & ~15) | ((((grp & 1) << 1) | (grp >> 1)) << 2);
+}
+
+// Store V rows (L consecutive keys starting at key kfirst, head dims 8c..8c+7) transposed.
+template <int L, int VSTR>
+__device__ __forceinline__ void store_vt(uint16_t* Vt, const u32x4* vr, int kfirst, int c) {
+#pragma unroll
+  for (int g4 = 0; g4 < L / 4; ++g4) {
+    const int pos = vt_pos(kfirst + g4 * 4);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const u32x4& v0 = vr[g4 * 4 + 0];
+      const u32x4& v1 = vr[g4 * 4 + 1];
+      const u32x4& v2 = vr[g4 * 4 + 2];
+      const u32x4& v3 = vr[g4 * 4 + 3];
+      uint16_t* dst = Vt + (c * 8 + 2 * p) * VSTR + pos;
+      *reinterpret_cast<u32x2*>(dst) = u32x2{lo_halves(v0[p], v1[p]), lo_halves(v2[p], v3[p])};
+      *reinterpret_cast<u32x2*>(dst + VSTR) = u32x2{hi_halves(v0[p], v1[p]), hi_halves(v2[p], v3[p])};
+    }
+  }
+}
+
+// S^T for the 32 keys in LDS rows krow0 .. krow0+31.
+__device__ __forceinline__ f32x16 st_block(const uint16_t* Ks, int krow0, const bf16x8* qreg, int lq, int hh) {
+  f32x16 s = {};
+#pragma unroll
+  for (int ks = 0; ks < TD / 16; ++ks) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(Ks + (krow0 + lq) * TKS + ks * 16 + hh * 8);
+    s = mfma32x32x16(as_bf16x8(a), qreg[ks], s);
+  }
+  return s;
+}
+
+// Online softmax over 64 keys (s0: keys 0-31, s1: keys 32-63 of V^T columns vcol0..vcol0+63)
+// and O^T += V^T P^T.  Masked scores are -inf.  m_run is in scaled log2 units.
+template <int VSTR>
+__device__ __forceinline__ void softmax_pv64(const f32x16& s0, const f32x16& s1, const uint16_t* Vt, int vcol0,
+                                             float scale_log2, float& m_run, float& l_run, f32x16* oacc, int lq,
+                                             int hh) {
+  float mx = kNegInf;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+  mx = fmaxf(mx, shfl_xor_f(mx, 32)) * scale_log2;
+  const float m_new = fmaxf(m_run, mx);
+  const bool need = m_new > m_run + kSlack;
+  if (__any(need)) {
+    const float alpha = need ? exp2_fast(m_run - m_new) : 1.f;
+    if (need) m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < TD / 32; ++db) oacc[db] *= alpha;
+  }
+  const float m_use = m_run == kNegInf ? 0.f : m_run;
+  uint32_t pk[2][8];
+  float psum = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; r += 2) {
+    const float p0 = exp2_fast(fmaf(s0[r], scale_log2, -m_use));
+    const float p1 = exp2_fast(fmaf(s0[r + 1], scale_log2, -m_use));
+    const float p2 = exp2_fast(fmaf(s1[r], scale_log2, -m_use));
+    const float p3 = exp2_fast(fmaf(s1[r + 1], scale_log2, -m_use));
+    pk[0][r / 2] = pack_bf16x2(p0, p1);
+    pk[1][r / 2] = pack_bf16x2(p2, p3);
+    // normaliser from the rounded weights the PV product uses (exact convex combination)
+    psum += bf16x2_sum(pk[0][r / 2]) + bf16x2_sum(pk[1][r / 2]);
+  }
+  l_run += psum;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const u32x4 pb = {pk[kb][hb * 4], pk[kb][hb * 4 + 1], pk[kb][hb * 4 + 2], pk[kb][hb * 4 + 3]};
+      const int ks = kb * 2 + hb;
+#pragma unroll
+      for (int db = 0; db < TD / 32; ++db) {
+        const u32x4 av = *reinterpret_cast<const u32x4*>(Vt + (db * 32 + lq) * VSTR + vcol0 + ks * 16 + hh * 8);
+        oacc[db] = mfma32x32x16(as_bf16x8(av), as_bf16x8(pb), oacc[db]);
+      }
+    }
+}
+
+// Normalise and store one query row's O (32 rows per wave, 64 dims per lane) and its LSE.
+// o_off: element offset of the row start (head dim 0) in the output.
+__device__ __forceinline__ void write_row(const OutArg& o, int64_t o_off, float* lse_ptr, const f32x16* oacc,
+                                          float m_run, float l_run, int hh) {
+  const float lt = l_run + shfl_xor_f(l_run, 32);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+#pragma unroll
+  for (int db = 0; db < TD / 32; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int d = db * 32 + g4 * 8 + hh * 4;
+      store4(o, o_off + d, oacc[db][g4 * 4] * inv, oacc[db][g4 * 4 + 1] * inv, oacc[db][g4 * 4 + 2] * inv,
+             oacc[db][g4 * 4 + 3] * inv);
+    }
+  if (hh == 0 && lse_ptr) *lse_ptr = lt > 0.f ? (m_run + log2f(lt)) * kLn2 : kNegInf;
+}
+
+// Work item for an XCD-aware, heavy-first launch: workgroup lid of n_items ->
+// item index such that XCD x (= lid % 8) runs the contiguous item range x.
+__device__ __forceinline__ int xcd_item(int lid, int n_items) {
+  const int xcd = lid & 7, j8 = lid >> 3;
+  const int per = n_items >> 3, rem = n_items & 7;
+  return xcd * per + min(xcd, rem) + j8;
+}
+
+}  // namespace bsa

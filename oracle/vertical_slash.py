@@ -63,11 +63,14 @@ def vs_convert_item(q_len: int, kv_len: int, vertical, slash, m: int, block_M: i
             windows.append(frontier)
             frontier += block_N
     last_visible = r1 - 1 + d
+    covered = set()
+    for w in windows:
+        covered.update(range(w, w + block_N))
     columns = []
     for v in sorted(int(x) for x in vertical):
         if v > last_visible:
             break
-        if any(w <= v < w + block_N for w in windows):
+        if v in covered:
             continue
         columns.append(v)
     return windows, columns

@@ -185,8 +185,12 @@ def vs_varlen_prefill(seed: int = 1005, seqlens=(65536, 32768), H: int = 32, D: 
         for h in range(H):
             gv = rng(seed, f"vertical.{b}.{h}")
             gs = rng(seed, f"slash.{b}.{h}")
-            vert[b, h] = np.sort(power_law_unique(gv, L, nnz_v))
-            slash[b, h] = np.sort(power_law_unique(gs, L, nnz_s))[::-1]
+            # a sequence shorter than the index count is padded with positions >= L, which no
+            # row of that sequence can reach (keeps the lists unique and sorted)
+            vv = np.sort(power_law_unique(gv, L, nnz_v))
+            vert[b, h] = np.concatenate([vv, L + np.arange(nnz_v - vv.size)])
+            ss = np.sort(power_law_unique(gs, L, nnz_s))[::-1]
+            slash[b, h] = np.concatenate([L + np.arange(nnz_s - ss.size)[::-1], ss])
     if context_size is None:
         context_size = max(seqlens)
     return dict(q=q, k=k, v=v, cu_seqlens=cu, seqlens=np.array(seqlens, np.int32), vertical=vert,

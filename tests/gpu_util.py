@@ -39,6 +39,7 @@ def check_o(o_gpu: np.ndarray, o_ref: np.ndarray, what: str, bf16_out: bool = Fa
         tol = O_TOL + 2.0 ** (np.floor(np.log2(mag)) - 8)
     bad = err > tol
     assert not bad.any(), f"{what}: max |dO| = {err.max():.3e} at {np.unravel_index(err.argmax(), err.shape)}"
+    print(f"[parity] {what}: max |dO| = {err.max():.3e}", flush=True)
     return float(err.max())
 
 
@@ -50,5 +51,6 @@ def check_lse(lse_gpu: np.ndarray, lse_ref: np.ndarray, what: str):
     if fin.any():
         err = np.abs(lse_gpu[fin] - lse_ref[fin])
         assert err.max() <= LSE_TOL, f"{what}: max |dLSE| = {err.max():.3e}"
+        print(f"[parity] {what}: max |dLSE| = {err.max():.3e}", flush=True)
         return float(err.max())
     return 0.0

@@ -97,5 +97,29 @@ def test_combine_and_partials_errors(lib):
     assert lib.bsa_combine(0, 1, 1, 1, 128, 16, 16, _t(), None, None) == bd.BSA_ERR_INVALID_ARG
     assert lib.bsa_combine(2, 1, 1, 1, 80, 16, 16, _t(), None, None) == bd.BSA_ERR_UNSUPPORTED
     prob = _prob()
-    assert lib.bsa_fwd_partials(ctypes.byref(prob), _t(), _t(), _t(), None, 16, 16, None) == bd.BSA_ERR_UNSUPPORTED
-    assert lib.bsa_fwd_partials(ctypes.byref(prob), _t(), _t(), _t(), None, None, 16, None) == bd.BSA_ERR_INVALID_ARG
+    assert lib.bsa_fwd_partials(ctypes.byref(prob), _t(), _t(), _t(), None, 1, None, 16, None) == bd.BSA_ERR_INVALID_ARG
+    cu = ctypes.c_int32(0)
+    varlen = _prob(cu_seqlens_q=ctypes.addressof(cu), cu_seqlens_k=ctypes.addressof(cu), max_seqlen_q=4, max_seqlen_k=4)
+    assert lib.bsa_fwd_partials(ctypes.byref(varlen), _t(), _t(), _t(), None, 1, 16, 16, None) == bd.BSA_ERR_UNSUPPORTED
+    # partial counts: dense entries are 64-key blocks; E <= 0 picks the split size
+    assert lib.bsa_num_partials(ctypes.byref(prob), None, 1) == 4
+    assert lib.bsa_num_partials(ctypes.byref(prob), None, 3) == 2
+    assert lib.bsa_num_partials(ctypes.byref(_prob(Hq=3)), None, 1) == -1
+
+
+def test_gated_and_vs_convert_errors(lib):
+    prob = _prob(Hq=2, Hkv=2, Sq=256, Sk=256, causal=1)
+    T = 16
+    q = _t(sb=256 * 2 * 128, ss=2 * 128)
+    assert lib.bsa_fwd_gated(ctypes.byref(prob), q, _t(), _t(), None, 128, 128, q, None, None, None, None) \
+        == bd.BSA_ERR_INVALID_ARG
+    assert lib.bsa_fwd_gated(ctypes.byref(prob), q, _t(), _t(), T, 64, 64, q, None, None, None, None) \
+        == bd.BSA_ERR_UNSUPPORTED
+    nc = _prob(Hq=2, Hkv=2, Sq=256, Sk=256, causal=0)
+    assert lib.bsa_fwd_gated(ctypes.byref(nc), q, _t(), _t(), T, 128, 128, q, None, None, None, None) \
+        == bd.BSA_ERR_UNSUPPORTED
+    x = 16
+    assert lib.vs_convert_indexes(x, x, x, x, 1, 1, 4, 4, 256, 64, 64, 0, x, x, x, x, None) == bd.BSA_ERR_UNSUPPORTED
+    assert lib.vs_convert_indexes(x, x, x, x, 1, 1, 4, 4, 256, 128, 64, 1, x, x, x, x, None) == bd.BSA_ERR_UNSUPPORTED
+    assert lib.vs_convert_indexes(None, x, x, x, 1, 1, 4, 4, 256, 64, 64, 1, x, x, x, x, None) == bd.BSA_ERR_INVALID_ARG
+    assert lib.vs_convert_indexes(x, x, x, x, 0, 1, 4, 4, 256, 64, 64, 1, x, x, x, x, None) == bd.BSA_ERR_INVALID_ARG

@@ -1,0 +1,107 @@
+"""GPU parity for BSFA gated prefill: keep masks bit-exact, tile maxima, O and LSE, at small
+size (every row) and at full size (sampled query blocks, thresholds from the oracle's exact
+tile maxima with a margin of at least 1e-2 to every tile maximum)."""
+import numpy as np
+import pytest
+import torch
+
+import long_context_attention_sparse_amd as bsa
+import oracle
+from synth import rng
+from synth.workloads import gated_prefill, thresholds_from_tile_max
+from tests.gpu_util import check_lse, check_o, dev_bf16, host, say
+
+pytestmark = [pytest.mark.gpu, pytest.mark.filterwarnings("ignore::RuntimeWarning")]
+
+
+@pytest.fixture(scope="module")
+def small():
+    w = gated_prefill(seed=41, B=2, Hq=4, Hkv=2, S=1024, D=128, bs=128)
+    w["dq"], w["dk"], w["dv"] = dev_bf16(w["q"]), dev_bf16(w["k"]), dev_bf16(w["v"])
+    nqb = 8
+    T = np.zeros((2, 4, nqb), np.float32)
+    for b in range(2):
+        for h in range(4):
+            for i in range(nqb):
+                T[b, h, i] = thresholds_from_tile_max(oracle.tile_max_row(w["q"], w["k"], b, h, i, 128, 128), i)
+    w["T"] = T
+    return w
+
+
+@pytest.mark.parametrize("mode", ["median", "-inf", "+inf"])
+def test_gated_small(small, mode):
+    w = small
+    say("gated small", mode)
+    T = {"median": w["T"], "-inf": np.full_like(w["T"], -np.inf), "+inf": np.full_like(w["T"], np.inf)}[mode]
+    o, lse, keep, tmax = bsa.bsa_fwd_gated(w["dq"], w["dk"], w["dv"], torch.from_numpy(T).cuda(),
+                                           out_dtype=torch.float32, return_tile_max=True)
+    o_ref, lse_ref, keep_ref, tmax_ref = oracle.gated(w["q"], w["k"], w["v"], T, 128, 128)
+    lower = np.tril(np.ones((8, 8), bool))
+    kg = keep.cpu().numpy()
+    assert np.array_equal(kg[..., lower], keep_ref[..., lower]), "keep mask differs"
+    tg = tmax.cpu().numpy().astype(np.float64)
+    assert np.abs(tg[..., lower] - tmax_ref[..., lower]).max() < 1e-3
+    check_o(host(o), o_ref, f"gated {mode}")
+    check_lse(host(lse), lse_ref, f"gated {mode} lse")
+    if mode == "median":
+        off = lower & ~np.eye(8, dtype=bool)
+        frac = 1.0 - kg[..., off].mean()
+        assert 0.3 < frac < 0.7, frac
+
+
+def test_gated_matches_block_sparse_path(small):
+    """The gated result equals the block-sparse kernel on the kept tiles.  Both are GPU paths,
+    each within the parity tolerance of the oracle (checked above), with independent bf16
+    rounding of P (different tile orders): they agree to twice that tolerance."""
+    w = small
+    say("gated vs block-sparse path")
+    o, lse, keep, _ = bsa.bsa_fwd_gated(w["dq"], w["dk"], w["dv"], torch.from_numpy(w["T"]).cuda(),
+                                        out_dtype=torch.float32)
+    kg = keep.cpu().numpy()
+    count = kg.sum(-1).astype(np.int32)
+    index = np.zeros_like(kg, dtype=np.int32)
+    for b in range(2):
+        for h in range(4):
+            for i in range(8):
+                kept = np.nonzero(kg[b, h, i, :i + 1])[0]
+                index[b, h, i, :kept.size] = kept
+    pat = bsa.BlockPattern(torch.from_numpy(count).cuda(), torch.from_numpy(index).cuda(), 128, 128)
+    ob, lb = bsa.bsa_fwd(w["dq"], w["dk"], w["dv"], pat, causal=True, out_dtype=torch.float32)
+    diff = np.abs(host(o) - host(ob)).max()
+    assert diff <= 2 * 1e-2, diff
+    check_lse(host(lse), host(lb), "gated vs block path lse")
+
+
+@pytest.fixture(scope="module")
+def cfg4():
+    say("generating gated prefill workload (S=65536, Hq=32, Hkv=8)")
+    w = gated_prefill()
+    w["dq"], w["dk"], w["dv"] = dev_bf16(w["q"]), dev_bf16(w["k"]), dev_bf16(w["v"])
+    return w
+
+
+def test_gated_full_size_sampled(cfg4):
+    w = cfg4
+    nqb = 512
+    samples = [(0, 511), (31, 300), (9, 1), (17, 64), (5, 0)]
+    T = np.where(np.arange(nqb)[None, None, :] % 2 == 0, -np.inf, np.inf).astype(np.float32)
+    T = np.broadcast_to(T, (1, 32, nqb)).copy()
+    trows = {}
+    for h, i in samples:
+        say("oracle tile maxima", h, i)
+        t = oracle.tile_max_row(w["q"], w["k"], 0, h, i, 128, 128)
+        trows[(h, i)] = t
+        T[0, h, i] = thresholds_from_tile_max(t, i)
+    say("gated full size")
+    o, lse, keep, tmax = bsa.bsa_fwd_gated(w["dq"], w["dk"], w["dv"], torch.from_numpy(T).cuda(),
+                                           out_dtype=torch.float32, return_tile_max=True)
+    kg = keep.cpu().numpy()
+    tg = tmax.cpu().numpy().astype(np.float64)
+    g = rng(4, "rows")
+    for h, i in samples:
+        rows = np.sort(g.choice(np.arange(i * 128, (i + 1) * 128), 4, replace=False))
+        o_ref, lse_ref, kr, t = oracle.gated_rows(w["q"], w["k"], w["v"], T[0, h, i], 0, h, i, rows, 128, 128)
+        assert np.array_equal(kg[0, h, i, :i + 1], kr), f"keep mask differs h={h} i={i}"
+        assert np.abs(tg[0, h, i, :i + 1] - t).max() < 1e-3
+        check_o(host(o[0, rows, h]), o_ref, f"gated full h={h} i={i}")
+        check_lse(host(lse[0, h, rows]), lse_ref, f"gated full lse h={h} i={i}")

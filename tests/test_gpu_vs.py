@@ -1,0 +1,90 @@
+"""GPU parity for vertical-slash conversion (bit-exact counts and valid prefixes) and varlen
+attention over the converted metadata, at small size (everything) and full size (sampled query
+blocks and rows)."""
+import numpy as np
+import pytest
+import torch
+
+import long_context_attention_sparse_amd as bsa
+import oracle
+from synth import rng
+from synth.workloads import vs_varlen_prefill
+from tests.gpu_util import check_lse, check_o, dev_bf16, dev_i32, host, say
+
+pytestmark = [pytest.mark.gpu, pytest.mark.filterwarnings("ignore::RuntimeWarning")]
+
+
+def _convert(w):
+    sl = dev_i32(w["seqlens"])
+    return bsa.vs_convert_indexes(sl, sl, dev_i32(w["vertical"]), dev_i32(w["slash"]), w["context_size"],
+                                  w["block_M"], w["block_N"])
+
+
+def _check_items(gpu, w, items):
+    bc, bo, cc, ci = (x.cpu().numpy() for x in gpu)
+    for b, h, m in items:
+        L = int(w["seqlens"][b])
+        wins, cols = oracle.vs_convert_item(L, L, w["vertical"][b, h], w["slash"][b, h], m, w["block_M"], w["block_N"])
+        assert bc[b, h, m] == len(wins) and cc[b, h, m] == len(cols), (b, h, m)
+        assert np.array_equal(bo[b, h, m, :len(wins)], wins), (b, h, m)
+        assert np.array_equal(ci[b, h, m, :len(cols)], cols), (b, h, m)
+
+
+@pytest.mark.parametrize("seqlens,ctx", [((300, 170), 320), ((64, 1), 64), ((1000, 999, 5), 1024)])
+def test_convert_small_exact(seqlens, ctx):
+    say("vs convert small", seqlens)
+    w = vs_varlen_prefill(seed=51, seqlens=seqlens, H=3, D=128, nnz_v=20, nnz_s=30, block=64, context_size=ctx)
+    gpu = _convert(w)
+    R = -(-ctx // 64)
+    _check_items(gpu, w, [(b, h, m) for b in range(len(seqlens)) for h in range(3) for m in range(R)])
+
+
+def test_attention_small_varlen():
+    w = vs_varlen_prefill(seed=52, seqlens=(700, 300, 64), H=4, D=128, nnz_v=40, nnz_s=60, block=64,
+                          context_size=704)
+    say("vs attention small varlen")
+    bc, bo, cc, ci = _convert(w)
+    pat = bsa.VSPattern(bc, bo, cc, ci, 64, 64)
+    cu = dev_i32(w["cu_seqlens"])
+    o, lse = bsa.bsa_fwd(dev_bf16(w["q"]), dev_bf16(w["k"]), dev_bf16(w["v"]), pat, causal=True,
+                         out_dtype=torch.float32, cu_seqlens_q=cu, cu_seqlens_k=cu, max_seqlen_q=700,
+                         max_seqlen_k=700)
+    rb, rbo, rcc, rci = oracle.vs_convert(w["seqlens"], w["seqlens"], w["vertical"], w["slash"], 704, 64, 64)
+    o_ref, lse_ref = oracle.vs_attention(w["q"], w["k"], w["v"], rb, rbo, rcc, rci, w["cu_seqlens"],
+                                         w["cu_seqlens"], 64, 64)
+    check_o(host(o), o_ref, "vs attention")
+    check_lse(host(lse), lse_ref, "vs attention lse")
+
+
+@pytest.fixture(scope="module")
+def cfg5():
+    say("generating vertical-slash varlen workload (seqlens 65536 + 32768, H=32)")
+    w = vs_varlen_prefill()
+    w["dq"], w["dk"], w["dv"] = dev_bf16(w["q"]), dev_bf16(w["k"]), dev_bf16(w["v"])
+    return w
+
+
+def test_full_size_convert_and_attention_sampled(cfg5):
+    w = cfg5
+    say("vs convert full size")
+    gpu = _convert(w)
+    g = rng(5, "items")
+    items = [(int(g.integers(0, 2)), int(g.integers(0, 32)), int(g.integers(0, 1024))) for _ in range(300)]
+    items += [(0, 0, 1023), (1, 31, 511), (1, 5, 512), (1, 5, 1023), (0, 17, 0)]
+    _check_items(gpu, w, items)
+    say("vs attention full size")
+    bc, bo, cc, ci = gpu
+    pat = bsa.VSPattern(bc, bo, cc, ci, 64, 64)
+    cu = dev_i32(w["cu_seqlens"])
+    o, lse = bsa.bsa_fwd(w["dq"], w["dk"], w["dv"], pat, causal=True, out_dtype=torch.float32, cu_seqlens_q=cu,
+                         cu_seqlens_k=cu, max_seqlen_q=65536, max_seqlen_k=65536)
+    oh, lh = host(o), host(lse)
+    for b, h, m in [(0, 3, 1023), (1, 30, 511), (0, 11, 400), (1, 0, 0), (0, 20, 7)]:
+        L = int(w["seqlens"][b])
+        rows = np.sort(g.choice(np.arange(m * 64, min(L, m * 64 + 64)), 4, replace=False))
+        wins, cols = oracle.vs_convert_item(L, L, w["vertical"][b, h], w["slash"][b, h], m, 64, 64)
+        o_ref, lse_ref = oracle.vs_attention_rows(w["q"], w["k"], w["v"], b, h, rows, wins, cols, w["cu_seqlens"],
+                                                  w["cu_seqlens"], 64)
+        a = int(w["cu_seqlens"][b])
+        check_o(oh[a + rows, h], o_ref, f"vs full b={b} h={h} m={m}")
+        check_lse(lh[h, a + rows], lse_ref, f"vs full lse b={b} h={h} m={m}")
