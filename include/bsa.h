@@ -163,6 +163,39 @@ bsa_status bsa_fwd_partials(const bsa_problem* prob, bsa_tensor q, bsa_tensor k,
 /* Number of partials bsa_fwd_partials writes for these arguments (-1 if invalid). */
 int32_t bsa_num_partials(const bsa_problem* prob, const bsa_pattern* pat, int32_t entries_per_partial);
 
+/* Speculative + sparse decoding with exact combine.  [IR] Usage 2: attention
+ * over a speculative key/value subset (k_spec, v_spec; Sk_spec keys, causal
+ * when causal_spec != 0, bottom-right aligned), attention over the *missed*
+ * blocks of the full cache (k, v) listed in `missed` — never masked — and
+ * the log-sum-exp combine of the two, so the result equals attention over the
+ * union when the sets are disjoint (the caller's precondition).
+ *   prob      shapes of q and of the full cache (Sk); prob->causal is ignored.
+ *   missed    a BLOCK pattern over (k, v) (Ht = Hq or Hkv).
+ *   o, lse    outputs as for bsa_fwd.
+ *   ws        at least bsa_speculative_workspace_size() bytes of device
+ *             scratch (the float32 partials of both passes).
+ * Equivalent to bsa_speculative_partials into ws followed by bsa_combine.
+ * Fixed length only.  Errors as for bsa_fwd. */
+bsa_status bsa_speculative_sparse(const bsa_problem* prob, bsa_tensor q, bsa_tensor k_spec, bsa_tensor v_spec,
+                                  int32_t Sk_spec, int32_t causal_spec, bsa_tensor k, bsa_tensor v,
+                                  const bsa_pattern* missed, bsa_tensor o, float* lse, void* ws, size_t ws_bytes,
+                                  bsa_stream stream);
+
+/* The two passes of bsa_speculative_sparse without the combine: P float32
+ * partials (o_part [P, B, Sq, Hq, D], lse_part [P, B, Hq, Sq], contiguous),
+ * P = bsa_speculative_num_partials().  When the query rows of a kv head fit one
+ * decode tile, both passes run in a single launch whose workgroups each take a
+ * similar number of 64-key chunks.  [IR] Usage 2 and Usage 3. */
+bsa_status bsa_speculative_partials(const bsa_problem* prob, bsa_tensor q, bsa_tensor k_spec, bsa_tensor v_spec,
+                                    int32_t Sk_spec, int32_t causal_spec, bsa_tensor k, bsa_tensor v,
+                                    const bsa_pattern* missed, float* o_part, float* lse_part, bsa_stream stream);
+
+/* Partial count of bsa_speculative_partials (-1 on invalid arguments). */
+int32_t bsa_speculative_num_partials(const bsa_problem* prob, int32_t Sk_spec, const bsa_pattern* missed);
+
+/* Bytes of workspace bsa_speculative_sparse needs (0 on invalid arguments). */
+size_t bsa_speculative_workspace_size(const bsa_problem* prob, int32_t Sk_spec, const bsa_pattern* missed);
+
 /* Log-sum-exp combine of P partials.  [IR] What's in this fork (combine
  * identity FA(A u B) == Combine(FA(A), FA(B))) and Usage 2.
  * For each (b, h, s): m = max_p lse_p; if m = -inf the result is (0, -inf);

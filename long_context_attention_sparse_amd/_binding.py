@@ -23,7 +23,8 @@ BSA_BF16, BSA_F32 = 0, 1
 BSA_PAT_DENSE, BSA_PAT_BLOCK, BSA_PAT_VS = 0, 1, 2
 
 EXPORTS = ("bsa_status_string", "bsa_workspace_size", "bsa_fwd", "bsa_fwd_partials", "bsa_num_partials",
-           "bsa_combine", "bsa_fwd_gated", "vs_convert_indexes")
+           "bsa_speculative_sparse", "bsa_speculative_partials", "bsa_speculative_num_partials",
+           "bsa_speculative_workspace_size", "bsa_combine", "bsa_fwd_gated", "vs_convert_indexes")
 
 
 class BSAError(RuntimeError):
@@ -75,6 +76,18 @@ def load(path: str = LIB_PATH):
                                      ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     lib.bsa_num_partials.restype = ctypes.c_int32
     lib.bsa_num_partials.argtypes = [ctypes.POINTER(_Problem), ctypes.POINTER(_Pattern), ctypes.c_int32]
+    spec_args = [ctypes.POINTER(_Problem), _Tensor, _Tensor, _Tensor, ctypes.c_int32, ctypes.c_int32, _Tensor,
+                 _Tensor, ctypes.POINTER(_Pattern)]
+    lib.bsa_speculative_sparse.restype = ctypes.c_int
+    lib.bsa_speculative_sparse.argtypes = spec_args + [_Tensor, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                                       ctypes.c_void_p]
+    lib.bsa_speculative_partials.restype = ctypes.c_int
+    lib.bsa_speculative_partials.argtypes = spec_args + [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.bsa_speculative_num_partials.restype = ctypes.c_int32
+    lib.bsa_speculative_num_partials.argtypes = [ctypes.POINTER(_Problem), ctypes.c_int32, ctypes.POINTER(_Pattern)]
+    lib.bsa_speculative_workspace_size.restype = ctypes.c_size_t
+    lib.bsa_speculative_workspace_size.argtypes = [ctypes.POINTER(_Problem), ctypes.c_int32,
+                                                   ctypes.POINTER(_Pattern)]
     lib.bsa_combine.restype = ctypes.c_int
     lib.bsa_combine.argtypes = [ctypes.c_int32] * 5 + [ctypes.c_void_p, ctypes.c_void_p, _Tensor, ctypes.c_void_p,
                                                       ctypes.c_void_p]
@@ -336,30 +349,54 @@ def vs_convert_indexes(q_seqlens, kv_seqlens, vertical_indexes, slash_indexes, c
     return bc, bo, cc, ci
 
 
+def bsa_speculative_partials(q, k_spec, v_spec, k, v, missed: BlockPattern, *, causal_spec: bool = True,
+                             softmax_scale=None, o_part: Optional[torch.Tensor] = None,
+                             lse_part: Optional[torch.Tensor] = None, stream=None):
+    """Partials of both passes of speculative + sparse decoding (one launch on the decode path).
+    Returns o_part [P, B, Sq, Hq, D], lse_part [P, B, Hq, Sq] (float32)."""
+    lib = load()
+    prob = _problem(q, k, False, softmax_scale)
+    pat = missed.struct(prob.Hq)
+    Sk_spec = k_spec.shape[1]
+    P = int(lib.bsa_speculative_num_partials(ctypes.byref(prob), Sk_spec, ctypes.byref(pat)))
+    if P < 0:
+        raise BSAError("bsa_speculative_partials", BSA_ERR_INVALID_ARG, "invalid arguments")
+    B, Sq, Hq, D = q.shape
+    if o_part is None:
+        o_part = torch.empty((P, B, Sq, Hq, D), dtype=torch.float32, device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty((P, B, Hq, Sq), dtype=torch.float32, device=q.device)
+    if tuple(o_part.shape) != (P, B, Sq, Hq, D) or tuple(lse_part.shape) != (P, B, Hq, Sq):
+        raise ValueError(f"partial buffers must be [{P}, B, Sq, Hq, D] and [{P}, B, Hq, Sq]")
+    st = lib.bsa_speculative_partials(ctypes.byref(prob), _tensor(q), _tensor(k_spec), _tensor(v_spec), Sk_spec,
+                                      int(bool(causal_spec)), _tensor(k), _tensor(v), ctypes.byref(pat),
+                                      _ptr(o_part), _ptr(lse_part), _stream(stream))
+    _check("bsa_speculative_partials", st)
+    return o_part, lse_part
+
+
 def speculative_sparse(q, k_spec, v_spec, k, v, missed: BlockPattern, *, causal_spec: bool = True,
-                       softmax_scale=None, out_dtype: torch.dtype = torch.bfloat16, out=None, stream=None,
-                       buffers=None):
+                       softmax_scale=None, out_dtype: torch.dtype = torch.bfloat16, out=None, lse=None,
+                       workspace=None, stream=None):
     """Speculative + sparse decoding with exact combine ("Sparse FlashAttention with
     Incremental Repair", Usage 2): attention over (k_spec, v_spec) with the causal flag
     (the speculative pass), attention over the missed blocks of (k, v) without a mask (the
-    repair pass), and the log-sum-exp combine.  Both passes write split partials into one
-    buffer and a single combine merges them all.  Returns (out, lse)."""
-    if buffers is None:
-        buffers = speculative_buffers(q, k_spec, k, missed, causal_spec)
-    o_part, lse_part, p1 = buffers
-    bsa_fwd_partials(q, k_spec, v_spec, None, 0, causal=causal_spec, softmax_scale=softmax_scale,
-                     o_part=o_part[:p1], lse_part=lse_part[:p1], stream=stream)
-    bsa_fwd_partials(q, k, v, missed, 0, causal=False, softmax_scale=softmax_scale, o_part=o_part[p1:],
-                     lse_part=lse_part[p1:], stream=stream)
-    return bsa_combine(o_part, lse_part, out=out, out_dtype=out_dtype, stream=stream)
-
-
-def speculative_buffers(q, k_spec, k, missed: BlockPattern, causal_spec: bool = True):
-    """Partial buffers for ``speculative_sparse`` (reusable across calls): (o_part, lse_part, P1)."""
+    repair pass), and the log-sum-exp combine.  Returns (out, lse)."""
+    lib = load()
+    prob = _problem(q, k, False, softmax_scale)
+    pat = missed.struct(prob.Hq)
+    Sk_spec = k_spec.shape[1]
     B, Sq, Hq, D = q.shape
-    p1 = bsa_num_partials(q, k_spec, None, 0, causal_spec)
-    p2 = bsa_num_partials(q, k, missed, 0, False)
-    o_part = torch.empty((p1 + p2, B, Sq, Hq, D), dtype=torch.float32, device=q.device)
-    lse_part = torch.empty((p1 + p2, B, Hq, Sq), dtype=torch.float32, device=q.device)
-    return o_part, lse_part, p1
-
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    need = int(lib.bsa_speculative_workspace_size(ctypes.byref(prob), Sk_spec, ctypes.byref(pat)))
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = lib.bsa_speculative_sparse(ctypes.byref(prob), _tensor(q), _tensor(k_spec), _tensor(v_spec), Sk_spec,
+                                    int(bool(causal_spec)), _tensor(k), _tensor(v), ctypes.byref(pat), _tensor(out),
+                                    _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                    _stream(stream))
+    _check("bsa_speculative_sparse", st)
+    return out, lse

@@ -102,13 +102,17 @@ bsa_status check_pattern(const bsa_problem& p, const bsa_pattern* pat) {
 // Decode path selection and split heuristic
 // ---------------------------------------------------------------------------
 
+struct SegPlan {
+  int n_entries = 0, cpe = 1, eps = 1, splits = 0;
+};
+
 struct DecodePlan {
   bool use = false;
   int Gp = 1, R = 0;
-  int n_entries = 0, entries_per_split = 0, splits = 0;
-  int cpe = 1;
 };
 
+// Packing rule: the G query heads of a kv head share one workgroup when they share
+// its key set; with the query positions they must fit one 16-column MFMA tile.
 DecodePlan plan_decode(const bsa_problem& p, const bsa_pattern* pat) {
   DecodePlan d;
   const int kind = pat ? pat->kind : BSA_PAT_DENSE;
@@ -119,69 +123,110 @@ DecodePlan plan_decode(const bsa_problem& p, const bsa_pattern* pat) {
   d.R = d.Gp * p.Sq;
   if (d.R > 16) return d;
   if (kind == BSA_PAT_BLOCK && p.Sq > pat->block_M) return d;
-  if (kind == BSA_PAT_DENSE) {
-    d.n_entries = (p.Sk + 63) / 64;
-    d.cpe = 1;
-  } else {
-    d.n_entries = pat->cap;
-    d.cpe = pat->block_N / 64;
-  }
-  const int groups = p.B * (p.Hq / d.Gp);
-  int splits = (kTargetWorkgroups + groups - 1) / groups;
-  splits = std::max(1, std::min(splits, std::max(1, d.n_entries)));
-  d.entries_per_split = std::max(1, (d.n_entries + splits - 1) / splits);
-  d.splits = std::max(1, (d.n_entries + d.entries_per_split - 1) / d.entries_per_split);
   d.use = true;
   return d;
 }
 
-size_t decode_ws_bytes(const bsa_problem& p, const DecodePlan& d) {
-  if (d.splits <= 1) return 0;
-  const size_t rows = (size_t)p.B * p.Sq * p.Hq;
-  return (size_t)d.splits * rows * (p.D + 1) * sizeof(float) + 256;
-}
-
-template <int D, int CPE>
-void launch_decode_t(const DecodeArgs& a, int splits, int groups, int B, hipStream_t st) {
-  hipLaunchKernelGGL((decode_kernel<D, CPE>), dim3(splits, groups, B), dim3(256), 0, st, a);
-}
-
-void launch_decode(const DecodeArgs& a, int D, int cpe, int splits, int groups, int B, hipStream_t st) {
-  if (D == 128) {
-    if (cpe == 2) launch_decode_t<128, 2>(a, splits, groups, B, st);
-    else launch_decode_t<128, 1>(a, splits, groups, B, st);
+SegPlan seg_entries(int Sk, const bsa_pattern* pat) {
+  SegPlan s;
+  if (!pat || pat->kind == BSA_PAT_DENSE) {
+    s.n_entries = (Sk + 63) / 64;
+    s.cpe = 1;
   } else {
-    if (cpe == 2) launch_decode_t<64, 2>(a, splits, groups, B, st);
-    else launch_decode_t<64, 1>(a, splits, groups, B, st);
+    s.n_entries = pat->cap;
+    s.cpe = pat->block_N / 64;
+  }
+  return s;
+}
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+constexpr int kDecodeWgPerCu = 4;      // resident decode workgroups per CU (120 VGPRs, 36 KB LDS)
+constexpr int kDecodeRounds = 2;       // whole rounds of resident workgroups per launch
+constexpr int kMaxChunksPerSplit = 96; // more rounds when splits would get longer than this
+
+// Split the segments of one decode launch: the splits of a group are a whole number of
+// rounds of resident workgroups (no quarter-full last round), shared between segments in
+// proportion to their chunk counts, so every workgroup streams a similar number of chunks.
+void split_segments(SegPlan* segs, int nseg, int groups) {
+  long total = 0;
+  for (int i = 0; i < nseg; ++i) total += (long)std::max(0, segs[i].n_entries) * segs[i].cpe;
+  const long capacity = (long)device_cus() * kDecodeWgPerCu;
+  long rounds = kDecodeRounds;
+  while (total * groups > rounds * capacity * kMaxChunksPerSplit) ++rounds;
+  long per_group = std::max<long>(1, (rounds * capacity + groups / 2) / groups);
+  per_group = std::max<long>(per_group, nseg);
+  long assigned = 0;
+  for (int i = 0; i < nseg; ++i) {
+    SegPlan& s = segs[i];
+    if (s.n_entries <= 0) {
+      s.eps = 1;
+      s.splits = 1;
+      ++assigned;
+      continue;
+    }
+    const long chunks = (long)s.n_entries * s.cpe;
+    long want = i == nseg - 1 ? per_group - assigned : (per_group * chunks + total / 2) / std::max<long>(total, 1);
+    want = std::max<long>(1, std::min<long>(want, s.n_entries));
+    s.eps = (int)((s.n_entries + want - 1) / want);
+    s.splits = (s.n_entries + s.eps - 1) / s.eps;
+    assigned += s.splits;
   }
 }
 
-void launch_combine(const CombineArgs& c, hipStream_t st) {
-  const int64_t rows = (int64_t)c.B * c.Sq * c.Hq;
-  const int rows_per_block = 256 / (c.D / 4);
-  const int64_t blocks = (rows + rows_per_block - 1) / rows_per_block;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(256), 0, st, c);
+size_t partial_bytes(const bsa_problem& p, int slots) {
+  const size_t rows = (size_t)p.B * p.Sq * p.Hq;
+  return (size_t)slots * rows * (p.D + 1) * sizeof(float) + 256;
 }
 
-bsa_status run_decode(const bsa_problem& p, const DecodePlan& d, const bsa_tensor& q, const bsa_tensor& k,
-                      const bsa_tensor& v, const bsa_pattern* pat, float* part_o, float* part_lse,
-                      const bsa_tensor* o, float* lse, hipStream_t st) {
+template <int D>
+void launch_decode_t(const DecodeArgs& a, int gx, int groups, int B, hipStream_t st) {
+  hipLaunchKernelGGL((decode_kernel<D>), dim3(gx, groups, B), dim3(256), 0, st, a);
+}
+
+DecodeSeg make_seg(const bsa_tensor& k, const bsa_tensor& v, const bsa_pattern* pat, int Sk, int causal,
+                   const SegPlan& sp, int slot0) {
+  DecodeSeg s{};
+  s.k = targ(k);
+  s.v = targ(v);
+  s.pat = parg(pat);
+  s.Sk = Sk;
+  s.causal = causal != 0;
+  s.n_entries = sp.n_entries;
+  s.cpe = sp.cpe;
+  s.eps = sp.eps;
+  s.splits = sp.splits;
+  s.slot0 = slot0;
+  return s;
+}
+
+// One decode launch over one or two segments; writes (O, LSE) directly when o is given
+// (single segment, single split), partial slots otherwise.
+bsa_status run_decode(const bsa_problem& p, const DecodePlan& d, const bsa_tensor& q, const DecodeSeg* segs, int nseg,
+                      float* part_o, float* part_lse, const bsa_tensor* o, float* lse, hipStream_t st) {
   DecodeArgs a{};
   a.q = targ(q);
-  a.k = targ(k);
-  a.v = targ(v);
-  a.pat = parg(pat);
+  a.nseg = nseg;
+  a.seg[0] = segs[0];
+  if (nseg > 1) a.seg[1] = segs[1];
   a.B = p.B;
   a.Hq = p.Hq;
   a.Hkv = p.Hkv;
   a.Sq = p.Sq;
-  a.Sk = p.Sk;
   a.G = p.Hq / p.Hkv;
   a.Gp = d.Gp;
   a.R = d.R;
-  a.n_entries = d.n_entries;
-  a.entries_per_split = d.entries_per_split;
-  a.causal = p.causal != 0;
   a.scale_log2 = scale_of(p) * kLog2e;
   if (o) {
     a.direct = 1;
@@ -192,10 +237,26 @@ bsa_status run_decode(const bsa_problem& p, const DecodePlan& d, const bsa_tenso
     a.part_o = part_o;
     a.part_lse = part_lse;
   }
-  launch_decode(a, p.D, d.cpe, d.splits, p.Hq / d.Gp, p.B, st);
+  int gx = 0;
+  for (int i = 0; i < nseg; ++i) gx += segs[i].splits;
+  if (p.D == 128) launch_decode_t<128>(a, gx, p.Hq / d.Gp, p.B, st);
+  else launch_decode_t<64>(a, gx, p.Hq / d.Gp, p.B, st);
   return launch_status();
 }
 
+void launch_combine(const CombineArgs& c, hipStream_t st) {
+  const int64_t rows = (int64_t)c.B * c.Sq * c.Hq;
+  const int rows_per_block = 256 / (c.D / 4);
+  const int64_t blocks = (rows + rows_per_block - 1) / rows_per_block;
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(256), 0, st, c);
+}
+
+// Split plan of bsa_fwd on the decode path (one segment).
+SegPlan fwd_decode_plan(const bsa_problem& p, const bsa_pattern* pat, const DecodePlan& d) {
+  SegPlan sp = seg_entries(p.Sk, pat);
+  split_segments(&sp, 1, p.B * (p.Hq / d.Gp));
+  return sp;
+}
 
 // ---------------------------------------------------------------------------
 // Prefill path
@@ -278,11 +339,12 @@ const char* bsa_status_string(bsa_status s) {
 }
 
 size_t bsa_workspace_size(const bsa_problem* prob, const bsa_pattern* pat) {
-  if (!prob || prob->B <= 0 || prob->Hkv <= 0 || prob->Hq % prob->Hkv) return 0;
+  if (!prob || prob->B <= 0 || prob->Hkv <= 0 || prob->Hq <= 0 || prob->Hq % prob->Hkv) return 0;
   if (check_pattern(*prob, pat) != BSA_OK) return 0;
   const DecodePlan d = plan_decode(*prob, pat);
-  if (d.use) return decode_ws_bytes(*prob, d);
-  return 0;
+  if (!d.use) return 0;
+  const SegPlan sp = fwd_decode_plan(*prob, pat, d);
+  return sp.splits > 1 ? partial_bytes(*prob, sp.splits) : 0;
 }
 
 bsa_status bsa_fwd(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, bsa_tensor v, const bsa_pattern* pat,
@@ -295,29 +357,42 @@ bsa_status bsa_fwd(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, bsa_tens
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   const DecodePlan d = plan_decode(p, pat);
   if (!d.use) return run_prefill(p, q, k, v, pat, &o, lse, 0, 0, nullptr, nullptr, hs);
-  if (d.splits == 1) return run_decode(p, d, q, k, v, pat, nullptr, nullptr, &o, lse, hs);
-  const size_t need = decode_ws_bytes(p, d);
+  const SegPlan sp = fwd_decode_plan(p, pat, d);
+  const DecodeSeg seg = make_seg(k, v, pat, p.Sk, p.causal, sp, 0);
+  if (sp.splits == 1) return run_decode(p, d, q, &seg, 1, nullptr, nullptr, &o, lse, hs);
+  const size_t need = partial_bytes(p, sp.splits);
   if (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 15)) return BSA_ERR_WORKSPACE;
   const size_t rows = (size_t)p.B * p.Sq * p.Hq;
   float* part_o = reinterpret_cast<float*>(ws);
-  float* part_lse = part_o + (size_t)d.splits * rows * p.D;
-  st = run_decode(p, d, q, k, v, pat, part_o, part_lse, nullptr, nullptr, hs);
+  float* part_lse = part_o + (size_t)sp.splits * rows * p.D;
+  st = run_decode(p, d, q, &seg, 1, part_o, part_lse, nullptr, nullptr, hs);
   if (st != BSA_OK) return st;
-  CombineArgs c{d.splits, p.B, p.Hq, p.Sq, p.D, part_o, part_lse, oarg(o), lse};
+  CombineArgs c{sp.splits, p.B, p.Hq, p.Sq, p.D, part_o, part_lse, oarg(o), lse};
   launch_combine(c, hs);
   return launch_status();
 }
 
-int32_t bsa_num_partials(const bsa_problem* prob, const bsa_pattern* pat, int32_t entries_per_partial) {
-  if (!prob || prob->B <= 0 || prob->Hkv <= 0 || prob->Sk <= 0 || prob->Hq % prob->Hkv) return -1;
-  if (check_pattern(*prob, pat) != BSA_OK || (pat && pat->kind == BSA_PAT_VS)) return -1;
-  const int n = partial_entries(*prob, pat);
-  int e = entries_per_partial;
-  if (e <= 0) {
-    const DecodePlan d = plan_decode(*prob, pat);
-    e = d.use ? d.entries_per_split : 1;
+// Entries per partial and partial count of bsa_fwd_partials (E <= 0: the split plan).
+static SegPlan partials_plan(const bsa_problem& p, const bsa_pattern* pat, int E) {
+  const DecodePlan d = plan_decode(p, pat);
+  SegPlan sp = seg_entries(p.Sk, pat);
+  if (E > 0) {
+    sp.eps = E;
+    sp.splits = sp.n_entries > 0 ? (sp.n_entries + E - 1) / E : 0;
+  } else if (d.use) {
+    split_segments(&sp, 1, p.B * (p.Hq / d.Gp));
+  } else {
+    sp.eps = 1;
+    sp.splits = sp.n_entries;
   }
-  return n > 0 ? (n + e - 1) / e : 0;
+  if (sp.n_entries <= 0) sp.splits = 0;
+  return sp;
+}
+
+int32_t bsa_num_partials(const bsa_problem* prob, const bsa_pattern* pat, int32_t entries_per_partial) {
+  if (!prob || prob->B <= 0 || prob->Hkv <= 0 || prob->Hq <= 0 || prob->Sk <= 0 || prob->Hq % prob->Hkv) return -1;
+  if (check_pattern(*prob, pat) != BSA_OK || (pat && pat->kind == BSA_PAT_VS)) return -1;
+  return partials_plan(*prob, pat, entries_per_partial).splits;
 }
 
 bsa_status bsa_fwd_partials(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, bsa_tensor v,
@@ -332,18 +407,104 @@ bsa_status bsa_fwd_partials(const bsa_problem* prob, bsa_tensor q, bsa_tensor k,
   st = check_pattern(p, pat);
   if (st != BSA_OK) return st;
   if (reinterpret_cast<uintptr_t>(o_part) & 15) return BSA_ERR_INVALID_ARG;
-  const int n = partial_entries(p, pat);
-  DecodePlan d = plan_decode(p, pat);
-  const int epp = entries_per_partial > 0 ? entries_per_partial : (d.use ? d.entries_per_split : 1);
-  const int n_part = n > 0 ? (n + epp - 1) / epp : 0;
-  if (n_part == 0) return BSA_OK;
+  const SegPlan sp = partials_plan(p, pat, entries_per_partial);
+  if (sp.splits == 0) return BSA_OK;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  const DecodePlan d = plan_decode(p, pat);
+  if (d.use) {
+    const DecodeSeg seg = make_seg(k, v, pat, p.Sk, p.causal, sp, 0);
+    return run_decode(p, d, q, &seg, 1, o_part, lse_part, nullptr, nullptr, hs);
+  }
+  return run_prefill(p, q, k, v, pat, nullptr, nullptr, sp.eps, sp.splits, o_part, lse_part, hs);
+}
+
+// Partial slots of the fused speculative + repair launch (decode shapes), or 2.
+static void speculative_plan(const bsa_problem& p, int Sk_spec, const bsa_pattern* missed, SegPlan segs[2],
+                             DecodePlan* dp) {
+  *dp = plan_decode(p, missed);
+  segs[0] = seg_entries(Sk_spec, nullptr);
+  segs[1] = seg_entries(p.Sk, missed);
+  if (dp->use) {
+    split_segments(segs, 2, p.B * (p.Hq / dp->Gp));
+  } else {
+    for (int i = 0; i < 2; ++i) {
+      segs[i].eps = std::max(1, segs[i].n_entries);
+      segs[i].splits = 1;
+    }
+  }
+}
+
+int32_t bsa_speculative_num_partials(const bsa_problem* prob, int32_t Sk_spec, const bsa_pattern* missed) {
+  if (!prob || prob->B <= 0 || prob->Hkv <= 0 || prob->Hq <= 0 || prob->Hq % prob->Hkv || Sk_spec <= 0) return -1;
+  if (!missed || missed->kind != BSA_PAT_BLOCK || check_pattern(*prob, missed) != BSA_OK) return -1;
+  SegPlan segs[2];
+  DecodePlan d;
+  speculative_plan(*prob, Sk_spec, missed, segs, &d);
+  return segs[0].splits + segs[1].splits;
+}
+
+size_t bsa_speculative_workspace_size(const bsa_problem* prob, int32_t Sk_spec, const bsa_pattern* missed) {
+  const int32_t n = bsa_speculative_num_partials(prob, Sk_spec, missed);
+  return n > 0 ? partial_bytes(*prob, n) : 0;
+}
+
+bsa_status bsa_speculative_partials(const bsa_problem* prob, bsa_tensor q, bsa_tensor k_spec, bsa_tensor v_spec,
+                                    int32_t Sk_spec, int32_t causal_spec, bsa_tensor k, bsa_tensor v,
+                                    const bsa_pattern* missed, float* o_part, float* lse_part, bsa_stream stream) {
+  if (!o_part || !lse_part || (reinterpret_cast<uintptr_t>(o_part) & 15)) return BSA_ERR_INVALID_ARG;
+  bsa_tensor o_dummy{o_part, BSA_F32, 0, 0, 0};
+  bsa_status st = check_problem(prob, q, k, v, o_dummy);
+  if (st != BSA_OK) return st;
+  const bsa_problem& p = *prob;
+  if (p.cu_seqlens_q) return BSA_ERR_UNSUPPORTED;
+  if (Sk_spec <= 0 || !k_spec.ptr || !v_spec.ptr) return BSA_ERR_INVALID_ARG;
+  if (k_spec.dtype != BSA_BF16 || v_spec.dtype != BSA_BF16) return BSA_ERR_UNSUPPORTED;
+  if (!aligned_rows(k_spec, 2) || !aligned_rows(v_spec, 2)) return BSA_ERR_INVALID_ARG;
+  if (!missed || missed->kind != BSA_PAT_BLOCK) return BSA_ERR_INVALID_ARG;
+  st = check_pattern(p, missed);
+  if (st != BSA_OK) return st;
+  SegPlan segs[2];
+  DecodePlan d;
+  speculative_plan(p, Sk_spec, missed, segs, &d);
+  const size_t rows = (size_t)p.B * p.Sq * p.Hq;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   if (d.use) {
-    d.entries_per_split = epp;
-    d.splits = n_part;
-    return run_decode(p, d, q, k, v, pat, o_part, lse_part, nullptr, nullptr, hs);
+    // both passes in one launch: the speculative keys (dense, causal_spec) and the
+    // missed blocks of the full cache (never masked)
+    const DecodeSeg sg[2] = {make_seg(k_spec, v_spec, nullptr, Sk_spec, causal_spec, segs[0], 0),
+                             make_seg(k, v, missed, p.Sk, 0, segs[1], segs[0].splits)};
+    return run_decode(p, d, q, sg, 2, o_part, lse_part, nullptr, nullptr, hs);
   }
-  return run_prefill(p, q, k, v, pat, nullptr, nullptr, epp, n_part, o_part, lse_part, hs);
+  bsa_problem ps = p;
+  ps.Sk = Sk_spec;
+  ps.causal = causal_spec;
+  st = run_prefill(ps, q, k_spec, v_spec, nullptr, nullptr, nullptr, segs[0].eps, 1, o_part, lse_part, hs);
+  if (st != BSA_OK) return st;
+  bsa_problem pr = p;
+  pr.causal = 0;
+  return run_prefill(pr, q, k, v, missed, nullptr, nullptr, segs[1].eps, 1, o_part + rows * p.D, lse_part + rows, hs);
+}
+
+bsa_status bsa_speculative_sparse(const bsa_problem* prob, bsa_tensor q, bsa_tensor k_spec, bsa_tensor v_spec,
+                                  int32_t Sk_spec, int32_t causal_spec, bsa_tensor k, bsa_tensor v,
+                                  const bsa_pattern* missed, bsa_tensor o, float* lse, void* ws, size_t ws_bytes,
+                                  bsa_stream stream) {
+  bsa_status st = check_problem(prob, q, k, v, o);
+  if (st != BSA_OK) return st;
+  const int32_t slots = bsa_speculative_num_partials(prob, Sk_spec, missed);
+  if (slots <= 0) return BSA_ERR_INVALID_ARG;
+  const bsa_problem& p = *prob;
+  const size_t need = partial_bytes(p, slots);
+  if (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 15)) return BSA_ERR_WORKSPACE;
+  const size_t rows = (size_t)p.B * p.Sq * p.Hq;
+  float* part_o = reinterpret_cast<float*>(ws);
+  float* part_lse = part_o + (size_t)slots * rows * p.D;
+  st = bsa_speculative_partials(prob, q, k_spec, v_spec, Sk_spec, causal_spec, k, v, missed, part_o, part_lse,
+                                stream);
+  if (st != BSA_OK) return st;
+  CombineArgs c{slots, p.B, p.Hq, p.Sq, p.D, part_o, part_lse, oarg(o), lse};
+  launch_combine(c, reinterpret_cast<hipStream_t>(stream));
+  return launch_status();
 }
 
 bsa_status bsa_combine(int32_t P, int32_t B, int32_t Hq, int32_t Sq, int32_t D, const float* o_part,

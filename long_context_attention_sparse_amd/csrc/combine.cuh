@@ -35,17 +35,37 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int64_t o_stride = (int64_t)a.B * a.Sq * a.Hq * a.D;
   const int64_t o0 = row * a.D + d;  // row = (b*Sq + s)*Hq + h
 
+  // batches of 8 partials: all loads of a batch are issued before any is used
+  constexpr int BATCH = 8;
   float m = kNegInf;
-  for (int p = 0; p < a.P; ++p) m = fmaxf(m, a.lse_part[lse0 + p * lse_stride]);
+  for (int p0 = 0; p0 < a.P; p0 += BATCH) {
+    float lv[BATCH];
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) lv[j] = p0 + j < a.P ? a.lse_part[lse0 + (p0 + j) * lse_stride] : kNegInf;
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) m = fmaxf(m, lv[j]);
+  }
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
   if (m != kNegInf) {
-    for (int p = 0; p < a.P; ++p) {
-      const float wgt = expf(a.lse_part[lse0 + p * lse_stride] - m);
-      if (wgt == 0.f) continue;  // empty partials may hold anything finite; skip them
-      const f32x4 v = *reinterpret_cast<const f32x4*>(a.o_part + o0 + p * o_stride);
-      acc += wgt * v;
-      wsum += wgt;
+    for (int p0 = 0; p0 < a.P; p0 += BATCH) {
+      float lv[BATCH];
+      f32x4 ov[BATCH];
+#pragma unroll
+      for (int j = 0; j < BATCH; ++j) {
+        const bool ok = p0 + j < a.P;
+        lv[j] = ok ? a.lse_part[lse0 + (p0 + j) * lse_stride] : kNegInf;
+        ov[j] = ok ? *reinterpret_cast<const f32x4*>(a.o_part + o0 + (p0 + j) * o_stride) : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int j = 0; j < BATCH; ++j) {
+        const float wgt = expf(lv[j] - m);
+        // a partial with no keys contributes nothing (its weight is exactly 0)
+        if (wgt != 0.f) {
+          acc += wgt * ov[j];
+          wsum += wgt;
+        }
+      }
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;

@@ -5,59 +5,77 @@
 // key/value head fit one 16-wide MFMA tile: the G query heads that share a
 // key/value head (and share its block list) are packed together with the Sq
 // query positions into at most 16 rows, so every K/V byte is read once per
-// group.  The list of a group is cut into splits; each workgroup streams its
-// split's 64-key chunks through LDS and writes either the final (O, LSE) or a
-// float32 partial that the combine kernel merges (log-sum-exp combine, same
-// page, What's in this fork).
+// group.  A launch holds one or two segments — key sets over possibly
+// different K/V tensors, e.g. the speculative pass and the repair pass of
+// Usage 2 — and each segment's list is cut into splits.  Each workgroup
+// streams its split's 64-key chunks through LDS and writes either the final
+// (O, LSE) or a float32 partial that the combine kernel merges (log-sum-exp
+// combine, same page, What's in this fork).
 //
-// Work decomposition: grid (splits, head groups, B), 256 threads = 4 waves.
-// Per 64-key chunk every thread loads D/32 16-byte pieces of K and of V
-// (coalesced: 16 or 8 lanes per 256/128-byte key row), K goes to LDS row-major,
-// V is transposed in registers and stored key-contiguous per head-dim row.
-// Wave w owns keys 16w..16w+15 of the chunk and keeps its own running
-// (max, sum, O^T); the four waves merge once at the end.
-//   S^T = K Q^T  : v_mfma_f32_16x16x32_bf16, D/32 per chunk (lane = query col)
+// Work decomposition: grid (splits of all segments, head groups, B), 256
+// threads = 4 waves.  The split's block ids are staged in LDS first, so the
+// address of every chunk is known without a dependent global load.  Per
+// 64-key chunk every thread loads D/32 16-byte pieces of K and of V
+// (coalesced: 16 or 8 lanes per 256/128-byte key row); K goes to LDS
+// row-major, V is transposed in registers and stored key-contiguous per
+// head-dim row.  Wave w owns keys 16w..16w+15 of the chunk and keeps its own
+// running (max, sum, O^T); the four waves merge once at the end.
+//   S^T = K Q^T    : v_mfma_f32_16x16x32_bf16, D/32 per chunk (lane = query col)
 //   O^T += V^T P^T : v_mfma_f32_16x16x16_bf16, D/16 per chunk
-// so softmax statistics stay in one lane per query (plus one 4-lane reduce).
 // The next chunk's loads are issued before the current chunk's MFMAs.
 #pragma once
 #include "common.cuh"
 
 namespace bsa {
 
-struct DecodeArgs {
-  TensorArg q, k, v;
-  OutArg o;        // final output (direct mode)
-  float* lse;      // final LSE [B, Hq, Sq] or nullptr (direct mode)
-  float* part_o;   // partials [splits, B, Sq, Hq, D] (split mode)
-  float* part_lse; // partials [splits, B, Hq, Sq] (split mode)
-  PatternArg pat;
-  int B, Hq, Hkv, Sq, Sk, G, Gp, R;
-  int n_entries;          // dense: number of 64-key chunks; lists: entries per list (cap)
-  int entries_per_split;
-  int causal;
-  int direct;
-  float scale_log2;       // softmax_scale * log2(e)
+struct DecodeSeg {
+  TensorArg k, v;
+  PatternArg pat;       // kind 0: dense over [0, Sk)
+  int Sk, causal;
+  int n_entries;        // dense: number of 64-key chunks; lists: entries per list (cap)
+  int cpe;              // 64-key chunks per entry
+  int eps;              // entries per split
+  int splits;           // splits of this segment (grid x range)
+  int slot0;            // first partial slot written by this segment
 };
 
-template <int D, int CPE>  // CPE: 64-key chunks per list entry (block_N / 64); 1 for dense
-__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
+struct DecodeArgs {
+  TensorArg q;
+  OutArg o;        // final output (direct mode)
+  float* lse;      // final LSE [B, Hq, Sq] or nullptr (direct mode)
+  float* part_o;   // partials [slots, B, Sq, Hq, D] (split mode)
+  float* part_lse; // partials [slots, B, Hq, Sq] (split mode)
+  DecodeSeg seg[2];
+  int nseg;
+  int B, Hq, Hkv, Sq, G, Gp, R;
+  int direct;
+  float scale_log2;  // softmax_scale * log2(e)
+};
+
+constexpr int kDecodeEntsLds = 256;  // block ids of a split staged in LDS (later ones read from global)
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void decode_kernel(DecodeArgs a) {
   constexpr int PIECES = D / 8;                // 16-byte pieces per key row
   constexpr int KEYS_PER_PASS = 256 / PIECES;  // key rows one pass of 256 threads covers
   constexpr int L = 64 / KEYS_PER_PASS;        // consecutive keys per thread (4 or 2)
   constexpr int KS = D + 8;                    // Ks row stride in bf16 (pad: conflict-free b128 reads)
   constexpr int VSTR = 64 + 8;                 // Vt row stride in bf16
   constexpr int LDS_KV = (64 * KS + D * VSTR) * 2;
-  constexpr int LDS_MERGE = (4 * 16 * D + 2 * 64) * 4;
+  constexpr int LDS_MERGE = (4 * 16 * D + 3 * 64) * 4;
   constexpr int LDS_BYTES = LDS_KV > LDS_MERGE ? LDS_KV : LDS_MERGE;
   __shared__ __attribute__((aligned(16))) unsigned char smem[LDS_BYTES];
+  __shared__ int ents[kDecodeEntsLds];
   uint16_t* Ks = reinterpret_cast<uint16_t*>(smem);
   uint16_t* Vt = Ks + 64 * KS;
 
   const int t = threadIdx.x;
   const int w = t >> 6, l = t & 63;
   const int lr = l & 15, kg = l >> 4;
-  const int sp = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
+  const int hg = blockIdx.y, b = blockIdx.z;
+  const int si = (a.nseg > 1 && (int)blockIdx.x >= a.seg[0].splits) ? 1 : 0;
+  const DecodeSeg& sg = a.seg[si];
+  const int sp = blockIdx.x - (si ? a.seg[0].splits : 0);
 
   // ---- query rows of this lane (MFMA column lr) ----
   const int rho = lr;
@@ -65,7 +83,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const int s_row = row_ok ? rho / a.Gp : 0;
   const int hq_row = hg * a.Gp + (row_ok ? rho % a.Gp : 0);
   const int hkv = (hg * a.Gp) / a.G;
-  const int lim = a.causal ? s_row + (a.Sk - a.Sq) : 0x7fffffff;
+  const int lim = sg.causal ? s_row + (sg.Sk - a.Sq) : 0x7fffffff;
 
   bf16x8 qreg[D / 32];
   {
@@ -78,28 +96,32 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     }
   }
 
-  // ---- this split's entries ----
+  // ---- this split's entries, staged in LDS ----
   int n_list;
   const int32_t* list = nullptr;
-  if (a.pat.kind == 0) {
-    n_list = a.n_entries;
+  if (sg.pat.kind == 0) {
+    n_list = sg.n_entries;
   } else {
-    const int64_t lb = b * a.pat.s_b + hg * a.pat.s_h;
-    n_list = a.pat.count[lb];
-    list = a.pat.index + lb * a.pat.cap;
+    const int64_t lb = b * sg.pat.s_b + hg * sg.pat.s_h;
+    n_list = sg.pat.count[lb];
+    list = sg.pat.index + lb * sg.pat.cap;
   }
-  const int e0 = sp * a.entries_per_split;
-  const int e1 = min(n_list, e0 + a.entries_per_split);
-  const int nchunks = e1 > e0 ? (e1 - e0) * CPE : 0;
+  const int e0 = sp * sg.eps;
+  const int e1 = min(n_list, e0 + sg.eps);
+  const int cpe = sg.cpe;
+  const int nchunks = e1 > e0 ? (e1 - e0) * cpe : 0;
+  if (list && t < kDecodeEntsLds && e0 + t < e1) ents[t] = list[e0 + t];
 
   const int c = t % PIECES, kk = t / PIECES;
-  const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.k.ptr) + b * a.k.sb + (int64_t)hkv * a.k.sh + c * 8;
-  const uint16_t* vbase = reinterpret_cast<const uint16_t*>(a.v.ptr) + b * a.v.sb + (int64_t)hkv * a.v.sh + c * 8;
+  const uint16_t* kbase = reinterpret_cast<const uint16_t*>(sg.k.ptr) + b * sg.k.sb + (int64_t)hkv * sg.k.sh + c * 8;
+  const uint16_t* vbase = reinterpret_cast<const uint16_t*>(sg.v.ptr) + b * sg.v.sb + (int64_t)hkv * sg.v.sh + c * 8;
+  const int Sk = sg.Sk;
 
   auto chunk_key0 = [&](int ci) -> int {
-    const int e = e0 + ci / CPE;
-    if (a.pat.kind == 0) return e * 64;
-    return list[e] * (64 * CPE) + (ci % CPE) * 64;
+    const int el = ci / cpe;
+    if (!list) return (e0 + el) * 64;
+    const int id = el < kDecodeEntsLds ? ents[el] : list[e0 + el];
+    return id * (64 * cpe) + (ci - el * cpe) * 64;
   };
 
   u32x4 kr[L], vr[L];
@@ -107,19 +129,22 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int j = 0; j < L; ++j) {
       const int key = key0 + kk * L + j;
-      const bool ok = (unsigned)key < (unsigned)a.Sk;
-      kr[j] = ok ? ldg128(kbase + (int64_t)key * a.k.ss) : u32x4{0, 0, 0, 0};
-      vr[j] = ok ? ldg128(vbase + (int64_t)key * a.v.ss) : u32x4{0, 0, 0, 0};
+      const bool ok = (unsigned)key < (unsigned)Sk;
+      kr[j] = ok ? ldg128(kbase + (int64_t)key * sg.k.ss) : u32x4{0, 0, 0, 0};
+      vr[j] = ok ? ldg128(vbase + (int64_t)key * sg.v.ss) : u32x4{0, 0, 0, 0};
     }
   };
 
-  float m_run = kNegInf, l_run = 0.f;
+  float m_run = kNegInf, l_run = 0.f, le_run = 0.f;
   f32x4 oacc[D / 16];
 #pragma unroll
   for (int i = 0; i < D / 16; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  int key0_next = nchunks > 0 ? chunk_key0(0) : 0;
+  // the first chunk's address comes straight from global memory, so its loads are in
+  // flight while the block ids are being staged
+  int key0_next = nchunks > 0 ? (list ? list[e0] * (64 * cpe) : e0 * 64) : 0;
   if (nchunks > 0) load_chunk(key0_next);
+  __syncthreads();
 
   for (int ci = 0; ci < nchunks; ++ci) {
     const int key0 = key0_next;
@@ -159,7 +184,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int key = key0 + w * 16 + kg * 4 + r;
-      const bool ok = (unsigned)key < (unsigned)a.Sk && key <= lim;
+      const bool ok = (unsigned)key < (unsigned)Sk && key <= lim;
       sc[r] = ok ? s[r] * a.scale_log2 : kNegInf;
       cmax = fmaxf(cmax, sc[r]);
     }
@@ -172,9 +197,11 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) p[r] = exp2_fast(sc[r] - m_use);
     const u32x2 pb = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
-    // normaliser from the rounded weights the PV product uses: O is then an exact
-    // convex combination of V rows and the dominant key's rounding cancels
+    // O is normalised by the rounded weights the PV product uses (an exact convex
+    // combination of V rows, so a dominant key's rounding cancels)
     l_run = l_run * alpha + (bf16x2_sum(pb[0]) + bf16x2_sum(pb[1]));
+    // exact normaliser for LSE
+    le_run = le_run * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
     m_run = m_new;
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) {
@@ -187,10 +214,13 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   // ---- merge the four waves ----
   l_run += shfl_xor_f(l_run, 16);
   l_run += shfl_xor_f(l_run, 32);
+  le_run += shfl_xor_f(le_run, 16);
+  le_run += shfl_xor_f(le_run, 32);
   __syncthreads();
   float* mo = reinterpret_cast<float*>(smem);  // [4][16][D]
   float* mm = mo + 4 * 16 * D;                 // [4][16]
   float* ml = mm + 64;
+  float* mle = ml + 64;
 #pragma unroll
   for (int db = 0; db < D / 16; ++db)
 #pragma unroll
@@ -198,6 +228,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   if (kg == 0) {
     mm[w * 16 + lr] = m_run;
     ml[w * 16 + lr] = l_run;
+    mle[w * 16 + lr] = le_run;
   }
   __syncthreads();
 
@@ -207,15 +238,16 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   float M = kNegInf;
 #pragma unroll
   for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, mm[ww * 16 + row]);
-  float wt[4], Lt = 0.f;
+  float wt[4], Lt = 0.f, Le = 0.f;
   const float Mu = M == kNegInf ? 0.f : M;
 #pragma unroll
   for (int ww = 0; ww < 4; ++ww) {
     wt[ww] = exp2_fast(mm[ww * 16 + row] - Mu);
     Lt += wt[ww] * ml[ww * 16 + row];
+    Le += wt[ww] * mle[ww * 16 + row];
   }
   const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
-  const float lse_val = Lt > 0.f ? (M + __log2f(Lt)) * kLn2 : kNegInf;
+  const float lse_val = Le > 0.f ? (M + log2f(Le)) * kLn2 : kNegInf;
   float out[DPT];
 #pragma unroll
   for (int i = 0; i < DPT; ++i) {
@@ -233,10 +265,11 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     for (int i = 0; i < DPT; i += 4) store4(a.o, off + i, out[i], out[i + 1], out[i + 2], out[i + 3]);
     if (dp == 0 && a.lse) a.lse[((int64_t)b * a.Hq + hq_o) * a.Sq + s_o] = lse_val;
   } else {
-    float* po = a.part_o + ((((int64_t)sp * a.B + b) * a.Sq + s_o) * a.Hq + hq_o) * D + dp * DPT;
+    const int64_t slot = sg.slot0 + sp;
+    float* po = a.part_o + (((slot * a.B + b) * a.Sq + s_o) * a.Hq + hq_o) * D + dp * DPT;
 #pragma unroll
     for (int i = 0; i < DPT; i += 4) *reinterpret_cast<f32x4*>(po + i) = f32x4{out[i], out[i + 1], out[i + 2], out[i + 3]};
-    if (dp == 0) a.part_lse[(((int64_t)sp * a.B + b) * a.Hq + hq_o) * a.Sq + s_o] = lse_val;
+    if (dp == 0) a.part_lse[((slot * a.B + b) * a.Hq + hq_o) * a.Sq + s_o] = lse_val;
   }
 }
 

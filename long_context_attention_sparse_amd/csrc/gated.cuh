@@ -28,7 +28,7 @@ struct GatedArgs {
   int n_items;
 };
 
-__global__ __launch_bounds__(256) void gated_kernel(GatedArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void gated_kernel(GatedArgs a) {
   constexpr int D = TD;
   constexpr int BN = 128;
   constexpr int PIECES = D / 8;
@@ -73,7 +73,7 @@ __global__ __launch_bounds__(256) void gated_kernel(GatedArgs a) {
   };
   auto tile_of = [&](int n) { return n == 0 ? i : n - 1; };  // diagonal first
 
-  float m_run = kNegInf, l_run = 0.f;
+  float m_run = kNegInf, l_run = 0.f, le_run = 0.f;
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int x = 0; x < D / 32; ++x) oacc[x] = f32x16{};
@@ -120,14 +120,14 @@ __global__ __launch_bounds__(256) void gated_kernel(GatedArgs a) {
       store_vt<L, VSTR>(Vt, vr, kk * L, c);
       if (n < i) load_rows(kr, kbp, a.k.ss, tile_of(n + 1) * BN);
       __syncthreads();
-      softmax_pv64<VSTR>(s[0], s[1], Vt, 0, a.scale_log2, m_run, l_run, oacc, lq, hh);
-      softmax_pv64<VSTR>(s[2], s[3], Vt, 64, a.scale_log2, m_run, l_run, oacc, lq, hh);
+      softmax_pv64<VSTR>(s[0], s[1], Vt, 0, a.scale_log2, m_run, l_run, le_run, oacc, lq, hh);
+      softmax_pv64<VSTR>(s[2], s[3], Vt, 64, a.scale_log2, m_run, l_run, le_run, oacc, lq, hh);
     } else {
       if (n < i) load_rows(kr, kbp, a.k.ss, tile_of(n + 1) * BN);
     }
   }
   const int64_t ob = (int64_t)b * a.o.sb + (int64_t)row * a.o.ss + (int64_t)h * a.o.sh;
-  write_row(a.o, ob, a.lse ? a.lse + ((int64_t)b * a.Hq + h) * a.S + row : nullptr, oacc, m_run, l_run, hh);
+  write_row(a.o, ob, a.lse ? a.lse + ((int64_t)b * a.Hq + h) * a.S + row : nullptr, oacc, m_run, l_run, le_run, hh);
 }
 
 }  // namespace bsa

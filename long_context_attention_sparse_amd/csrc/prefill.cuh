@@ -49,7 +49,7 @@ struct PrefillArgs {
 };
 
 template <int NW, int KIND>
-__global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(PrefillArgs a) {
   constexpr int D = TD;
   constexpr int NT = NW * 64;
   constexpr int BM = NW * 32;
@@ -60,6 +60,12 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[64 * TKS];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VSTR];
   __shared__ __attribute__((aligned(16))) int kidx_s[64];
+  // list entries (block ids or window offsets) and gathered column indices staged in LDS,
+  // so a chunk's addresses never wait on a dependent global load
+  constexpr int kEnts = 256;
+  constexpr int kCols = KIND == 2 ? 768 : 1;
+  __shared__ int ents_s[kEnts];
+  __shared__ int cols_s[kCols];
 
   const int item = xcd_item(blockIdx.x, a.n_items);
   const int mrev = item % a.nqb;
@@ -83,8 +89,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   const int delta = kv_len - q_len;
   const int r_last = min(r0 + BM, q_len) - 1;
 
-  const int t = threadIdx.x;
-  const int w = t >> 6, l = t & 63;
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int lq = l & 31, hh = l >> 5;
 
   const int64_t qoff = a.cu_q ? (int64_t)q_start * a.q.ss : (int64_t)b * a.q.sb;
@@ -127,16 +132,32 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
     }
   }
 
-  // chunk ci -> first key (contiguous) or gather base (columns)
-  auto chunk_key0 = [&](int ci, bool& gathered, int& gbase) -> int {
+  const int t = threadIdx.x;
+  if constexpr (KIND != 0) {
+    const int nl = min(KIND == 1 ? n_chunks / cpe : nwin, kEnts);
+    for (int x = t; x < nl; x += NT) ents_s[x] = list[x];
+    if constexpr (KIND == 2) {
+      const int nc = min(ncol, kCols);
+      for (int x = t; x < nc; x += NT) cols_s[x] = cols[x];
+    }
+  }
+  auto entry = [&](int e) -> int { return e < kEnts ? ents_s[e] : list[e]; };
+  auto column = [&](int x) -> int {
+    if constexpr (KIND == 2) return x < kCols ? cols_s[x] : cols[x];
+    return 0;
+  };
+
+  // chunk ci -> first key (contiguous) or gather base (columns); staged=false reads global
+  auto chunk_key0 = [&](int ci, bool& gathered, int& gbase, bool staged) -> int {
     gathered = false;
     gbase = 0;
     if constexpr (KIND == 0) {
       return ci * 64;
     } else if constexpr (KIND == 1) {
-      return list[ci / cpe] * a.pat.block_N + (ci % cpe) * 64;
+      const int e = ci / cpe;
+      return (staged ? entry(e) : list[e]) * a.pat.block_N + (ci - e * cpe) * 64;
     } else {
-      if (ci < nwin) return list[ci];
+      if (ci < nwin) return staged ? entry(ci) : list[ci];
       gathered = true;
       gbase = (ci - nwin) * 64;
       return 0;
@@ -145,7 +166,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
 
   const int c = t % PIECES, kk = t / PIECES;
   u32x4 kr[L], vr[L];
-  auto load_chunk = [&](int key0, bool gathered, int gbase) {
+  auto load_chunk = [&](int key0, bool gathered, int gbase, bool staged) {
 #pragma unroll
     for (int jj = 0; jj < L; ++jj) {
       const int i = kk * L + jj;
@@ -153,7 +174,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
       bool ok;
       if (gathered) {
         ok = gbase + i < ncol;
-        key = ok ? cols[gbase + i] : 0;
+        key = ok ? (staged ? column(gbase + i) : cols[gbase + i]) : 0;
         ok = ok && (unsigned)key < (unsigned)kv_len;
       } else {
         key = key0 + i;
@@ -164,7 +185,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
     }
   };
 
-  float m_run = kNegInf, l_run = 0.f;
+  float m_run = kNegInf, l_run = 0.f, le_run = 0.f;
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
@@ -176,23 +197,26 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
                            (int64_t)h * a.o.sh;
         float* lp = nullptr;
         if (a.lse) lp = a.lse + (a.cu_q ? (int64_t)h * a.cu_q[a.B] + q_start + row : ((int64_t)b * a.Hq + h) * a.Sq + row);
-        write_row(a.o, ob, lp, oacc, m_run, l_run, hh);
+        write_row(a.o, ob, lp, oacc, m_run, l_run, le_run, hh);
       } else {
         const OutArg po{a.part_o, 0, (int64_t)a.Hq * D, D, 1};
         const int64_t ob = (((int64_t)slot * a.B + b) * a.Sq + row) * a.Hq * D + (int64_t)h * D;
-        write_row(po, ob, a.part_lse + (((int64_t)slot * a.B + b) * a.Hq + h) * a.Sq + row, oacc, m_run, l_run, hh);
+        write_row(po, ob, a.part_lse + (((int64_t)slot * a.B + b) * a.Hq + h) * a.Sq + row, oacc, m_run, l_run, le_run, hh);
       }
     }
     m_run = kNegInf;
     l_run = 0.f;
+    le_run = 0.f;
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
   };
 
   bool g_next = false;
   int gb_next = 0;
-  int key0_next = n_chunks > 0 ? chunk_key0(0, g_next, gb_next) : 0;
-  if (n_chunks > 0) load_chunk(key0_next, g_next, gb_next);
+  // the first chunk reads its addresses from global memory, so its loads overlap the staging
+  int key0_next = n_chunks > 0 ? chunk_key0(0, g_next, gb_next, false) : 0;
+  if (n_chunks > 0) load_chunk(key0_next, g_next, gb_next, false);
+  __syncthreads();
 
   const int wrow_min = r0 + w * 32;
   for (int ci = 0; ci < n_chunks; ++ci) {
@@ -204,14 +228,14 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
     for (int jj = 0; jj < L; ++jj) *reinterpret_cast<u32x4*>(Ks + (kk * L + jj) * TKS + c * 8) = kr[jj];
     store_vt<L, VSTR>(Vt, vr, kk * L, c);
     if (t < 64) {
-      int key = gathered ? (gbase + t < ncol ? cols[gbase + t] : -1) : key0 + t;
+      int key = gathered ? (gbase + t < ncol ? column(gbase + t) : -1) : key0 + t;
       if ((unsigned)key >= (unsigned)kv_len) key = 0x7fffffff;
       kidx_s[t] = key;
     }
     __syncthreads();
     if (ci + 1 < n_chunks) {
-      key0_next = chunk_key0(ci + 1, g_next, gb_next);
-      load_chunk(key0_next, g_next, gb_next);
+      key0_next = chunk_key0(ci + 1, g_next, gb_next, true);
+      load_chunk(key0_next, g_next, gb_next, true);
     }
 
     f32x16 s0 = st_block(Ks, 0, qreg, lq, hh);
@@ -240,7 +264,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
         if (k1.w > lim) s1[q4 * 4 + 3] = kNegInf;
       }
     }
-    softmax_pv64<VSTR>(s0, s1, Vt, 0, a.scale_log2, m_run, l_run, oacc, lq, hh);
+    softmax_pv64<VSTR>(s0, s1, Vt, 0, a.scale_log2, m_run, l_run, le_run, oacc, lq, hh);
 
     if constexpr (KIND != 2) {
       if (a.partial && (ci % cpe) == cpe - 1) {

@@ -57,10 +57,13 @@ __device__ __forceinline__ f32x16 st_block(const uint16_t* Ks, int krow0, const 
 
 // Online softmax over 64 keys (s0: keys 0-31, s1: keys 32-63 of V^T columns vcol0..vcol0+63)
 // and O^T += V^T P^T.  Masked scores are -inf.  m_run is in scaled log2 units.
+// Two normalisers are kept: l_run sums the bf16-rounded weights the PV product uses (O is
+// then an exact convex combination of V rows, so a dominant key's rounding cancels) and
+// le_run sums the exact weights (for LSE).
 template <int VSTR>
 __device__ __forceinline__ void softmax_pv64(const f32x16& s0, const f32x16& s1, const uint16_t* Vt, int vcol0,
-                                             float scale_log2, float& m_run, float& l_run, f32x16* oacc, int lq,
-                                             int hh) {
+                                             float scale_log2, float& m_run, float& l_run, float& le_run,
+                                             f32x16* oacc, int lq, int hh) {
   float mx = kNegInf;
 #pragma unroll
   for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
@@ -71,12 +74,13 @@ __device__ __forceinline__ void softmax_pv64(const f32x16& s0, const f32x16& s1,
     const float alpha = need ? exp2_fast(m_run - m_new) : 1.f;
     if (need) m_run = m_new;
     l_run *= alpha;
+    le_run *= alpha;
 #pragma unroll
     for (int db = 0; db < TD / 32; ++db) oacc[db] *= alpha;
   }
   const float m_use = m_run == kNegInf ? 0.f : m_run;
   uint32_t pk[2][8];
-  float psum = 0.f;
+  float psum = 0.f, pesum = 0.f;
 #pragma unroll
   for (int r = 0; r < 16; r += 2) {
     const float p0 = exp2_fast(fmaf(s0[r], scale_log2, -m_use));
@@ -85,10 +89,11 @@ __device__ __forceinline__ void softmax_pv64(const f32x16& s0, const f32x16& s1,
     const float p3 = exp2_fast(fmaf(s1[r + 1], scale_log2, -m_use));
     pk[0][r / 2] = pack_bf16x2(p0, p1);
     pk[1][r / 2] = pack_bf16x2(p2, p3);
-    // normaliser from the rounded weights the PV product uses (exact convex combination)
     psum += bf16x2_sum(pk[0][r / 2]) + bf16x2_sum(pk[1][r / 2]);
+    pesum += (p0 + p1) + (p2 + p3);
   }
   l_run += psum;
+  le_run += pesum;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -106,8 +111,9 @@ __device__ __forceinline__ void softmax_pv64(const f32x16& s0, const f32x16& s1,
 // Normalise and store one query row's O (32 rows per wave, 64 dims per lane) and its LSE.
 // o_off: element offset of the row start (head dim 0) in the output.
 __device__ __forceinline__ void write_row(const OutArg& o, int64_t o_off, float* lse_ptr, const f32x16* oacc,
-                                          float m_run, float l_run, int hh) {
+                                          float m_run, float l_run, float le_run, int hh) {
   const float lt = l_run + shfl_xor_f(l_run, 32);
+  const float le = le_run + shfl_xor_f(le_run, 32);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
 #pragma unroll
   for (int db = 0; db < TD / 32; ++db)
@@ -117,7 +123,7 @@ __device__ __forceinline__ void write_row(const OutArg& o, int64_t o_off, float*
       store4(o, o_off + d, oacc[db][g4 * 4] * inv, oacc[db][g4 * 4 + 1] * inv, oacc[db][g4 * 4 + 2] * inv,
              oacc[db][g4 * 4 + 3] * inv);
     }
-  if (hh == 0 && lse_ptr) *lse_ptr = lt > 0.f ? (m_run + log2f(lt)) * kLn2 : kNegInf;
+  if (hh == 0 && lse_ptr) *lse_ptr = le > 0.f ? (m_run + log2f(le)) * kLn2 : kNegInf;
 }
 
 // Work item for an XCD-aware, heavy-first launch: workgroup lid of n_items ->

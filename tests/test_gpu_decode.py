@@ -169,3 +169,53 @@ def test_speculative_full_size_sampled(spec_full):
             w["missed"][b:b + 1, hkv:hkv + 1, None, :], 64, causal_spec=True)
         check_o(oh[b:b + 1, :, hs], o_ref, f"full b={b} hkv={hkv}")
         check_lse(lh[b:b + 1, hs], lse_ref, f"full lse b={b} hkv={hkv}")
+
+
+@pytest.mark.parametrize("Sq,causal_spec", [(1, True), (8, True), (3, False)])
+def test_speculative_partials_and_fallback(Sq, causal_spec):
+    """bsa_speculative_partials + bsa_combine equal the oracle's two-pass result, on the fused
+    decode launch (Sq*G <= 16) and on the prefill fallback (Sq=8, G=4 gives 32 rows)."""
+    B, Hq, Hkv, D, Sk, bs = 2, 8, 2, 128, 2048, 64
+    say("speculative partials", Sq, causal_spec)
+    q = normal_bf16(9, "q", (B, Sq, Hq, D))
+    k = normal_bf16(9, "k", (B, Sk, Hkv, D))
+    v = normal_bf16(9, "v", (B, Sk, Hkv, D))
+    s0 = Sk - 320                                   # speculative keys: the last 320 (not a 64 multiple)
+    g = rng(9, "missed")
+    n = 7
+    idx = np.stack([np.sort(g.choice(s0 // bs, n, replace=False)) for _ in range(B * Hkv)]).reshape(B, Hkv, 1, n)
+    idx = idx.astype(np.int32)
+    cnt = np.full((B, Hkv, 1), n, np.int32)
+    cnt[1, 0, 0] = 0                                 # one group with nothing missed
+    pat = bsa.BlockPattern(dev_i32(cnt), dev_i32(idx), 128, bs)
+    dq, dk, dv = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    op, lp = bsa.bsa_speculative_partials(dq, dk[:, s0:], dv[:, s0:], dk, dv, pat, causal_spec=causal_spec)
+    o, lse = bsa.bsa_combine(op, lp, out_dtype=torch.float32)
+    o2, lse2 = bsa.speculative_sparse(dq, dk[:, s0:], dv[:, s0:], dk, dv, pat, causal_spec=causal_spec,
+                                      out_dtype=torch.float32)
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    o_ref, lse_ref = oracle.speculative_sparse(q, k[:, s0:], v[:, s0:], k, v, cnt, idx, bs, causal_spec=causal_spec)
+    check_o(host(o), o_ref, "speculative partials")
+    check_lse(host(lse), lse_ref, "speculative partials lse")
+
+
+@pytest.mark.parametrize("E", [0, 1, 5])
+def test_fwd_partials_grouping_decode(E):
+    """Partials of E entries each (E = 0: the library's split) recombine to bsa_fwd's result."""
+    B, Hq, Hkv, D, Sk = 2, 8, 2, 128, 4096
+    say("decode partials E =", E)
+    q = normal_bf16(10, "q", (B, 1, Hq, D))
+    k = normal_bf16(10, "k", (B, Sk, Hkv, D))
+    v = normal_bf16(10, "v", (B, Sk, Hkv, D))
+    g = rng(10, "lists")
+    n = 23
+    idx = np.stack([g.choice(Sk // 64, n, replace=False) for _ in range(B * Hkv)]).reshape(B, Hkv, 1, n)
+    idx = idx.astype(np.int32)
+    cnt = np.full((B, Hkv, 1), n, np.int32)
+    pat = bsa.BlockPattern(dev_i32(cnt), dev_i32(idx), 128, 64)
+    op, lp = bsa.bsa_fwd_partials(dev_bf16(q), dev_bf16(k), dev_bf16(v), pat, E)
+    assert op.shape[0] == bsa.bsa_num_partials(dev_bf16(q), dev_bf16(k), pat, E)
+    o, lse = bsa.bsa_combine(op, lp, out_dtype=torch.float32)
+    o_ref, lse_ref = oracle.block_sparse(q, k, v, cnt, idx, 1, 64)
+    check_o(host(o), o_ref, f"partials E={E}")
+    check_lse(host(lse), lse_ref, f"partials E={E} lse")
