@@ -35,6 +35,8 @@ def _args():
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run 4 device-to-device copies of 1 GiB (reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -392,6 +394,16 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     bsa.load()
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 4}), flush=True)
+        return
     fn = {1: bench_tiny, 2: bench_spec_decode, 3: bench_block_prefill, 4: bench_gated, 5: bench_vs}[args.config]
     res = fn(torch, bsa, args)
     line = {"metric": res["metric"], "value": res["value"], "unit": res["unit"], "n_gpus": 1, "steps": args.steps,

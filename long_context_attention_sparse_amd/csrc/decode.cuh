@@ -124,6 +124,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
     return id * (64 * cpe) + (ci - el * cpe) * 64;
   };
 
+  // V for head dim 128: lanes run over the 16 4-key groups (kv) and each thread owns one
+  // 16-byte head-dim piece (cv), so the transposed LDS stores of a wave write whole
+  // contiguous V^T row segments (no bank conflicts); head dim 64 uses the K mapping
+  constexpr bool kVGroups = D == 128;
+  const int kv = t % 16, cv = t / 16;
+  const uint16_t* vbase2 = reinterpret_cast<const uint16_t*>(sg.v.ptr) + b * sg.v.sb + (int64_t)hkv * sg.v.sh + cv * 8;
   u32x4 kr[L], vr[L];
   auto load_chunk = [&](int key0) {
 #pragma unroll
@@ -131,7 +137,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
       const int key = key0 + kk * L + j;
       const bool ok = (unsigned)key < (unsigned)Sk;
       kr[j] = ok ? ldg128(kbase + (int64_t)key * sg.k.ss) : u32x4{0, 0, 0, 0};
-      vr[j] = ok ? ldg128(vbase + (int64_t)key * sg.v.ss) : u32x4{0, 0, 0, 0};
+      if constexpr (kVGroups) {
+        const int vkey = key0 + kv * 4 + j;
+        vr[j] = (unsigned)vkey < (unsigned)Sk ? ldg128(vbase2 + (int64_t)vkey * sg.v.ss) : u32x4{0, 0, 0, 0};
+      } else {
+        vr[j] = ok ? ldg128(vbase + (int64_t)key * sg.v.ss) : u32x4{0, 0, 0, 0};
+      }
     }
   };
 
@@ -154,7 +165,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
     for (int j = 0; j < L; ++j) *reinterpret_cast<u32x4*>(Ks + (kk * L + j) * KS + c * 8) = kr[j];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      uint16_t* dst0 = Vt + (c * 8 + 2 * p) * VSTR + kk * L;
+      uint16_t* dst0 = kVGroups ? Vt + (cv * 8 + 2 * p) * VSTR + kv * 4 : Vt + (c * 8 + 2 * p) * VSTR + kk * L;
       uint16_t* dst1 = dst0 + VSTR;
       if constexpr (L == 4) {
         u32x2 ev = {lo_halves(vr[0][p], vr[1][p]), lo_halves(vr[2][p], vr[3][p])};

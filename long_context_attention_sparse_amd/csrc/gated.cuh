@@ -65,11 +65,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
   const float T = a.T[th];
   const int64_t mask_row = th * a.nqb;
 
+  // K: 16 lanes per 256-byte row; V: lanes run over the 32 4-key groups of the tile so
+  // the transposed LDS stores are conflict-free (two head-dim pieces per thread)
   const int c = t % PIECES, kk = t / PIECES;
-  u32x4 kr[L], vr[L];
-  auto load_rows = [&](u32x4* dst, const uint16_t* base, int64_t ss, int key0) {
+  const int kv = t % 32, cv0 = t / 32;
+  u32x4 kr[L], vr[2][4];
+  auto load_k = [&](int key0) {
 #pragma unroll
-    for (int jj = 0; jj < L; ++jj) dst[jj] = ldg128(base + (int64_t)(key0 + kk * L + jj) * ss + c * 8);
+    for (int jj = 0; jj < L; ++jj) kr[jj] = ldg128(kbp + (int64_t)(key0 + kk * L + jj) * a.k.ss + c * 8);
+  };
+  auto load_v = [&](int key0) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp)
+        vr[pp][jj] = ldg128(vbp + (int64_t)(key0 + kv * 4 + jj) * a.v.ss + (cv0 + pp * 8) * 8);
   };
   auto tile_of = [&](int n) { return n == 0 ? i : n - 1; };  // diagonal first
 
@@ -78,7 +88,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
 #pragma unroll
   for (int x = 0; x < D / 32; ++x) oacc[x] = f32x16{};
 
-  load_rows(kr, kbp, a.k.ss, tile_of(0) * BN);
+  load_k(tile_of(0) * BN);
   for (int n = 0; n <= i; ++n) {
     const int j = tile_of(n);
     __syncthreads();
@@ -116,14 +126,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
       if (a.tmax) a.tmax[mask_row + j] = tile_max;
     }
     if (keep) {
-      load_rows(vr, vbp, a.v.ss, j * BN);
-      store_vt<L, VSTR>(Vt, vr, kk * L, c);
-      if (n < i) load_rows(kr, kbp, a.k.ss, tile_of(n + 1) * BN);
+      load_v(j * BN);
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) store_vt_group<VSTR>(Vt, vr[pp], kv * 4, cv0 + pp * 8);
+      if (n < i) load_k(tile_of(n + 1) * BN);
       __syncthreads();
       softmax_pv64<VSTR>(s[0], s[1], Vt, 0, a.scale_log2, m_run, l_run, le_run, oacc, lq, hh);
       softmax_pv64<VSTR>(s[2], s[3], Vt, 64, a.scale_log2, m_run, l_run, le_run, oacc, lq, hh);
     } else {
-      if (n < i) load_rows(kr, kbp, a.k.ss, tile_of(n + 1) * BN);
+      if (n < i) load_k(tile_of(n + 1) * BN);
     }
   }
   const int64_t ob = (int64_t)b * a.o.sb + (int64_t)row * a.o.ss + (int64_t)h * a.o.sh;

@@ -164,24 +164,37 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     }
   };
 
+  // K: 16 lanes per 256-byte row (c = 16-byte piece); V: lanes run over 4-key groups
+  // (kv) so the transposed LDS stores are conflict-free; NP (kv, cv) pairs per thread
   const int c = t % PIECES, kk = t / PIECES;
-  u32x4 kr[L], vr[L];
+  constexpr int NP = 16 * PIECES / NT;
+  const int kv = t % 16, cv0 = t / 16;
+  u32x4 kr[L], vr[NP][4];
+  // chunk-local key i -> global key index, or -1 when absent
+  auto key_of = [&](int i, int key0, bool gathered, int gbase, bool staged) -> int {
+    int key;
+    if (gathered) {
+      if (gbase + i >= ncol) return -1;
+      key = staged ? column(gbase + i) : cols[gbase + i];
+    } else {
+      key = key0 + i;
+    }
+    return (unsigned)key < (unsigned)kv_len ? key : -1;
+  };
   auto load_chunk = [&](int key0, bool gathered, int gbase, bool staged) {
 #pragma unroll
     for (int jj = 0; jj < L; ++jj) {
-      const int i = kk * L + jj;
-      int key;
-      bool ok;
-      if (gathered) {
-        ok = gbase + i < ncol;
-        key = ok ? (staged ? column(gbase + i) : cols[gbase + i]) : 0;
-        ok = ok && (unsigned)key < (unsigned)kv_len;
-      } else {
-        key = key0 + i;
-        ok = (unsigned)key < (unsigned)kv_len;
+      const int key = key_of(kk * L + jj, key0, gathered, gbase, staged);
+      kr[jj] = key >= 0 ? ldg128(kbp + (int64_t)key * a.k.ss + c * 8) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int key = key_of(kv * 4 + jj, key0, gathered, gbase, staged);
+#pragma unroll
+      for (int pp = 0; pp < NP; ++pp) {
+        const int cv = cv0 + pp * (NT / 16);
+        vr[pp][jj] = key >= 0 ? ldg128(vbp + (int64_t)key * a.v.ss + cv * 8) : u32x4{0, 0, 0, 0};
       }
-      kr[jj] = ok ? ldg128(kbp + (int64_t)key * a.k.ss + c * 8) : u32x4{0, 0, 0, 0};
-      vr[jj] = ok ? ldg128(vbp + (int64_t)key * a.v.ss + c * 8) : u32x4{0, 0, 0, 0};
     }
   };
 
@@ -226,7 +239,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     __syncthreads();
 #pragma unroll
     for (int jj = 0; jj < L; ++jj) *reinterpret_cast<u32x4*>(Ks + (kk * L + jj) * TKS + c * 8) = kr[jj];
-    store_vt<L, VSTR>(Vt, vr, kk * L, c);
+#pragma unroll
+    for (int pp = 0; pp < NP; ++pp) store_vt_group<VSTR>(Vt, vr[pp], kv * 4, cv0 + pp * (NT / 16));
     if (t < 64) {
       int key = gathered ? (gbase + t < ncol ? column(gbase + t) : -1) : key0 + t;
       if ((unsigned)key >= (unsigned)kv_len) key = 0x7fffffff;

@@ -25,22 +25,18 @@ __device__ __forceinline__ int vt_pos(int key4) {
   return (key4 & ~15) | ((((grp & 1) << 1) | (grp >> 1)) << 2);
 }
 
-// Store V rows (L consecutive keys starting at key kfirst, head dims 8c..8c+7) transposed.
-template <int L, int VSTR>
-__device__ __forceinline__ void store_vt(uint16_t* Vt, const u32x4* vr, int kfirst, int c) {
+// Store 4 V rows (keys key4..key4+3, head dims 8cv..8cv+7) transposed into V^T.  V is
+// loaded with the 4-key group index running fastest across lanes, so the 16 (or 32)
+// lanes of one store instruction write consecutive 8-byte slots of the same V^T row:
+// no LDS bank conflicts.
+template <int VSTR>
+__device__ __forceinline__ void store_vt_group(uint16_t* Vt, const u32x4* v4, int key4, int cv) {
+  const int pos = vt_pos(key4);
 #pragma unroll
-  for (int g4 = 0; g4 < L / 4; ++g4) {
-    const int pos = vt_pos(kfirst + g4 * 4);
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const u32x4& v0 = vr[g4 * 4 + 0];
-      const u32x4& v1 = vr[g4 * 4 + 1];
-      const u32x4& v2 = vr[g4 * 4 + 2];
-      const u32x4& v3 = vr[g4 * 4 + 3];
-      uint16_t* dst = Vt + (c * 8 + 2 * p) * VSTR + pos;
-      *reinterpret_cast<u32x2*>(dst) = u32x2{lo_halves(v0[p], v1[p]), lo_halves(v2[p], v3[p])};
-      *reinterpret_cast<u32x2*>(dst + VSTR) = u32x2{hi_halves(v0[p], v1[p]), hi_halves(v2[p], v3[p])};
-    }
+  for (int p = 0; p < 4; ++p) {
+    uint16_t* dst = Vt + (cv * 8 + 2 * p) * VSTR + pos;
+    *reinterpret_cast<u32x2*>(dst) = u32x2{lo_halves(v4[0][p], v4[1][p]), lo_halves(v4[2][p], v4[3][p])};
+    *reinterpret_cast<u32x2*>(dst + VSTR) = u32x2{hi_halves(v4[0][p], v4[1][p]), hi_halves(v4[2][p], v4[3][p])};
   }
 }
 
