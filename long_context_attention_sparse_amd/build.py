@@ -14,14 +14,20 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libbsa.so")
-SOURCES = ["bsa_api.hip"]
+# translation units and their extra flags
+SOURCES = [
+    ("bsa_api.hip", []),
+    ("kernels_stream.hip", []),
+    # the tile kernels never create NaNs (masked scores are -inf, handled explicitly), so
+    # max needs no NaN-quieting canonicalisation: plain v_max/v_max3 in the softmax
+    ("kernels_tile.hip", ["-fno-honor-nans", "-mno-amdgpu-ieee"]),
+]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     # packed fp32 VALU forms are kept out of generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result",
@@ -35,11 +41,7 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False, extra_flags=None) -> str:
-    """Compile every HIP source into libbsa.so (always recompiles)."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIP_FLAGS, *(extra_flags or []), "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -48,6 +50,20 @@ def build(verbose: bool = False, extra_flags=None) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{out}")
     if verbose and out.strip():
         print(out)
+
+
+def build(verbose: bool = False, extra_flags=None) -> str:
+    """Compile every HIP translation unit and link libbsa.so (always recompiles)."""
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = []
+    for src, flags in SOURCES:
+        obj = os.path.join(objdir, src.replace(".hip", ".o"))
+        _run([hipcc(), *HIP_FLAGS, *flags, *(extra_flags or []), "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+              "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        objs.append(obj)
+    tmp = LIB + ".tmp"
+    _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -1,0 +1,108 @@
+// Plain argument blocks of the kernels, filled on the host by the C ABI layer and
+// passed by value to the launches (launch.h).
+#pragma once
+#include <stdint.h>
+
+namespace bsa {
+
+struct TensorArg {
+  const void* ptr;
+  int64_t sb, ss, sh;  // element strides (batch, token, head); head dim contiguous
+};
+
+struct OutArg {
+  void* ptr;
+  int64_t sb, ss, sh;
+  int f32;  // 1: float32 output, 0: bf16
+};
+
+struct PatternArg {
+  int kind;  // 0 dense, 1 block lists, 2 vertical-slash
+  int block_M, block_N, cap, col_cap;
+  const int32_t* count;
+  const int32_t* index;
+  const int32_t* col_count;
+  const int32_t* col_index;
+  int64_t s_b, s_h, s_q;
+};
+
+constexpr int kDecodeEntsLds = 256;    // block ids of a decode split staged in LDS (later ones read from global)
+constexpr int kVSConvThreads = 64;     // conversion workgroup size (one query block per thread)
+constexpr int kVSConvLdsInts = 16384;  // slash + vertical entries staged in LDS (longer lists stay in global)
+
+struct DecodeSeg {
+  TensorArg k, v;
+  PatternArg pat;       // kind 0: dense over [0, Sk)
+  int Sk, causal;
+  int n_entries;        // dense: number of 64-key chunks; lists: entries per list (cap)
+  int cpe;              // 64-key chunks per entry
+  int eps;              // entries per split
+  int splits;           // splits of this segment (grid x range)
+  int slot0;            // first partial slot written by this segment
+};
+
+struct DecodeArgs {
+  TensorArg q;
+  OutArg o;        // final output (direct mode)
+  float* lse;      // final LSE [B, Hq, Sq] or nullptr (direct mode)
+  float* part_o;   // partials [slots, B, Sq, Hq, D] (split mode)
+  float* part_lse; // partials [slots, B, Hq, Sq] (split mode)
+  DecodeSeg seg[2];
+  int nseg;
+  int B, Hq, Hkv, Sq, G, Gp, R;
+  int direct;
+  float scale_log2;  // softmax_scale * log2(e)
+};
+
+struct PrefillArgs {
+  TensorArg q, k, v;
+  OutArg o;
+  float* lse;
+  PatternArg pat;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int B, Hq, Hkv, G, Sq, Sk;  // Sq/Sk: lengths (varlen: maxima)
+  int nqb;                    // query blocks per (b, h) in the grid
+  int list_by_kv;             // lists indexed by kv head (1) or query head (0)
+  int causal;
+  float scale_log2;
+  int n_items;
+  int partial;                // 1: partials of epp entries each into part_o / part_lse
+  int epp, n_part;
+  float* part_o;              // [n_part, B, Sq, Hq, D]
+  float* part_lse;            // [n_part, B, Hq, Sq]
+};
+
+struct GatedArgs {
+  TensorArg q, k, v;
+  OutArg o;
+  float* lse;
+  const float* T;      // [B, Hq, nqb]
+  uint8_t* keep;       // [B, Hq, nqb, nqb] or nullptr
+  float* tmax;         // [B, Hq, nqb, nqb] or nullptr
+  int B, Hq, Hkv, G, S, nqb;
+  float scale, scale_log2;
+  int n_items;
+};
+
+struct CombineArgs {
+  int P, B, Hq, Sq, D;
+  const float* o_part;    // [P, B, Sq, Hq, D]
+  const float* lse_part;  // [P, B, Hq, Sq]
+  OutArg o;               // [B, Sq, Hq, D] view
+  float* lse;             // [B, Hq, Sq] or nullptr
+};
+
+struct VSConvArgs {
+  const int32_t* q_seqlens;
+  const int32_t* kv_seqlens;
+  const int32_t* vertical;  // [B, H, nnz_v]
+  const int32_t* slash;     // [B, H, nnz_s]
+  int B, H, nnz_v, nnz_s, rows, BM, BN;
+  int32_t* bc;              // [B, H, rows]
+  int32_t* bo;              // [B, H, rows, nnz_s]
+  int32_t* cc;              // [B, H, rows]
+  int32_t* ci;              // [B, H, rows, nnz_v]
+};
+
+}  // namespace bsa

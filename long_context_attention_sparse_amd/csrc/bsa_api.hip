@@ -11,14 +11,13 @@
 #include <cstdint>
 #include <cstring>
 
+#include "args.cuh"
 #include "bsa.h"
-#include "combine.cuh"
-#include "decode.cuh"
-#include "gated.cuh"
-#include "prefill.cuh"
-#include "vs_convert.cuh"
+#include "launch.h"
 
 using namespace bsa;
+
+constexpr float kLog2e = 1.4426950408889634f;
 
 namespace {
 
@@ -190,11 +189,6 @@ size_t partial_bytes(const bsa_problem& p, int slots) {
   return (size_t)slots * rows * (p.D + 1) * sizeof(float) + 256;
 }
 
-template <int D>
-void launch_decode_t(const DecodeArgs& a, int gx, int groups, int B, hipStream_t st) {
-  hipLaunchKernelGGL((decode_kernel<D>), dim3(gx, groups, B), dim3(256), 0, st, a);
-}
-
 DecodeSeg make_seg(const bsa_tensor& k, const bsa_tensor& v, const bsa_pattern* pat, int Sk, int causal,
                    const SegPlan& sp, int slot0) {
   DecodeSeg s{};
@@ -239,16 +233,8 @@ bsa_status run_decode(const bsa_problem& p, const DecodePlan& d, const bsa_tenso
   }
   int gx = 0;
   for (int i = 0; i < nseg; ++i) gx += segs[i].splits;
-  if (p.D == 128) launch_decode_t<128>(a, gx, p.Hq / d.Gp, p.B, st);
-  else launch_decode_t<64>(a, gx, p.Hq / d.Gp, p.B, st);
+  launch_decode(a, p.D, gx, p.Hq / d.Gp, p.B, st);
   return launch_status();
-}
-
-void launch_combine(const CombineArgs& c, hipStream_t st) {
-  const int64_t rows = (int64_t)c.B * c.Sq * c.Hq;
-  const int rows_per_block = 256 / (c.D / 4);
-  const int64_t blocks = (rows + rows_per_block - 1) / rows_per_block;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(256), 0, st, c);
 }
 
 // Split plan of bsa_fwd on the decode path (one segment).
@@ -261,11 +247,6 @@ SegPlan fwd_decode_plan(const bsa_problem& p, const bsa_pattern* pat, const Deco
 // ---------------------------------------------------------------------------
 // Prefill path
 // ---------------------------------------------------------------------------
-
-template <int NW, int KIND>
-void launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((prefill_kernel<NW, KIND>), dim3(a.n_items), dim3(NW * 64), 0, st, a);
-}
 
 bsa_status run_prefill(const bsa_problem& p, const bsa_tensor& q, const bsa_tensor& k, const bsa_tensor& v,
                        const bsa_pattern* pat, const bsa_tensor* o, float* lse, int epp, int n_part, float* part_o,
@@ -304,15 +285,7 @@ bsa_status run_prefill(const bsa_problem& p, const bsa_tensor& q, const bsa_tens
     a.part_o = part_o;
     a.part_lse = part_lse;
   }
-  if (BM == 128) {
-    if (kind == BSA_PAT_DENSE) launch_prefill_t<4, 0>(a, st);
-    else if (kind == BSA_PAT_BLOCK) launch_prefill_t<4, 1>(a, st);
-    else launch_prefill_t<4, 2>(a, st);
-  } else {
-    if (kind == BSA_PAT_DENSE) launch_prefill_t<2, 0>(a, st);
-    else if (kind == BSA_PAT_BLOCK) launch_prefill_t<2, 1>(a, st);
-    else launch_prefill_t<2, 2>(a, st);
-  }
+  launch_prefill(a, BM / 32, kind, st);
   return launch_status();
 }
 
@@ -547,7 +520,7 @@ bsa_status bsa_fwd_gated(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, bs
   const int64_t items = (int64_t)p.B * p.Hq * a.nqb;
   if (items > INT_MAX) return BSA_ERR_UNSUPPORTED;
   a.n_items = (int)items;
-  hipLaunchKernelGGL(gated_kernel, dim3(a.n_items), dim3(256), 0, reinterpret_cast<hipStream_t>(stream), a);
+  launch_gated(a, reinterpret_cast<hipStream_t>(stream));
   return launch_status();
 }
 
@@ -566,9 +539,7 @@ bsa_status vs_convert_indexes(const int32_t* q_seqlens, const int32_t* kv_seqlen
                block_count, block_offset, column_count, column_index};
   a.rows = (context_size + block_M - 1) / block_M;
   const int lds_ints = nnz_s + nnz_v <= kVSConvLdsInts ? nnz_s + nnz_v : 0;
-  dim3 grid((a.rows + kVSConvThreads - 1) / kVSConvThreads, B * H);
-  hipLaunchKernelGGL(vs_convert_kernel, grid, dim3(kVSConvThreads), lds_ints * sizeof(int32_t),
-                     reinterpret_cast<hipStream_t>(stream), a);
+  launch_vs_convert(a, lds_ints * sizeof(int32_t), reinterpret_cast<hipStream_t>(stream));
   return launch_status();
 }
 

@@ -12,13 +12,6 @@
 
 namespace bsa {
 
-struct CombineArgs {
-  int P, B, Hq, Sq, D;
-  const float* o_part;    // [P, B, Sq, Hq, D]
-  const float* lse_part;  // [P, B, Hq, Sq]
-  OutArg o;               // [B, Sq, Hq, D] view
-  float* lse;             // [B, Hq, Sq] or nullptr
-};
 
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int tpr = a.D / 4;

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "args.cuh"
+
 namespace bsa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -19,31 +21,6 @@ constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kNegInf = -__builtin_inff();
 
 // ---------------------------------------------------------------------------
-// Kernel argument blocks (plain data; built on the host by the C ABI layer)
-// ---------------------------------------------------------------------------
-
-struct TensorArg {
-  const void* ptr;
-  int64_t sb, ss, sh;  // element strides (batch, token, head); head dim contiguous
-};
-
-struct OutArg {
-  void* ptr;
-  int64_t sb, ss, sh;
-  int f32;  // 1: float32 output, 0: bf16
-};
-
-struct PatternArg {
-  int kind;  // 0 dense, 1 block lists, 2 vertical-slash
-  int block_M, block_N, cap, col_cap;
-  const int32_t* count;
-  const int32_t* index;
-  const int32_t* col_count;
-  const int32_t* col_index;
-  int64_t s_b, s_h, s_q;
-};
-
-// ---------------------------------------------------------------------------
 // Small helpers
 // ---------------------------------------------------------------------------
 
@@ -53,13 +30,12 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
 
-// Round two floats to bf16 (nearest-even) and pack: lo in bits 0..15.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Round two floats to bf16 (nearest-even) and pack, lo in bits 0..15: one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 a = (__bf16)lo;
-  __bf16 b = (__bf16)hi;
-  uint16_t ua = __builtin_bit_cast(uint16_t, a);
-  uint16_t ub = __builtin_bit_cast(uint16_t, b);
-  return (uint32_t)ua | ((uint32_t)ub << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 __device__ __forceinline__ uint16_t to_bf16_bits(float x) {
@@ -67,14 +43,15 @@ __device__ __forceinline__ uint16_t to_bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, a);
 }
 
-// Sum of the two bf16 values packed in a dword (exact widening, one fp32 add).
-__device__ __forceinline__ float bf16x2_sum(uint32_t u) {
-  return __uint_as_float(u << 16) + __uint_as_float(u & 0xFFFF0000u);
+// acc + (both bf16 values packed in u), as one v_dot2_f32_bf16 against (1, 1).
+__device__ __forceinline__ float bf16x2_sum_acc(uint32_t u, float acc) {
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u), ones, acc, false);
 }
 
-// 16-bit halves of two dwords: (a.lo, b.lo) and (a.hi, b.hi).
-__device__ __forceinline__ uint32_t lo_halves(uint32_t a, uint32_t b) { return (a & 0xFFFFu) | (b << 16); }
-__device__ __forceinline__ uint32_t hi_halves(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xFFFF0000u); }
+// 16-bit halves of two dwords, one v_perm_b32 each: (a.lo, b.lo) and (a.hi, b.hi).
+__device__ __forceinline__ uint32_t lo_halves(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
+__device__ __forceinline__ uint32_t hi_halves(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
 
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, 64); }
 

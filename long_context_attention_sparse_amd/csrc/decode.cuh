@@ -28,31 +28,8 @@
 
 namespace bsa {
 
-struct DecodeSeg {
-  TensorArg k, v;
-  PatternArg pat;       // kind 0: dense over [0, Sk)
-  int Sk, causal;
-  int n_entries;        // dense: number of 64-key chunks; lists: entries per list (cap)
-  int cpe;              // 64-key chunks per entry
-  int eps;              // entries per split
-  int splits;           // splits of this segment (grid x range)
-  int slot0;            // first partial slot written by this segment
-};
 
-struct DecodeArgs {
-  TensorArg q;
-  OutArg o;        // final output (direct mode)
-  float* lse;      // final LSE [B, Hq, Sq] or nullptr (direct mode)
-  float* part_o;   // partials [slots, B, Sq, Hq, D] (split mode)
-  float* part_lse; // partials [slots, B, Hq, Sq] (split mode)
-  DecodeSeg seg[2];
-  int nseg;
-  int B, Hq, Hkv, Sq, G, Gp, R;
-  int direct;
-  float scale_log2;  // softmax_scale * log2(e)
-};
 
-constexpr int kDecodeEntsLds = 256;  // block ids of a split staged in LDS (later ones read from global)
 
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void decode_kernel(DecodeArgs a) {
@@ -210,7 +187,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
     const u32x2 pb = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
     // O is normalised by the rounded weights the PV product uses (an exact convex
     // combination of V rows, so a dominant key's rounding cancels)
-    l_run = l_run * alpha + (bf16x2_sum(pb[0]) + bf16x2_sum(pb[1]));
+    l_run = bf16x2_sum_acc(pb[1], bf16x2_sum_acc(pb[0], l_run * alpha));
     // exact normaliser for LSE
     le_run = le_run * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
     m_run = m_new;

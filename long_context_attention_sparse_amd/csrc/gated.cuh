@@ -16,17 +16,6 @@
 
 namespace bsa {
 
-struct GatedArgs {
-  TensorArg q, k, v;
-  OutArg o;
-  float* lse;
-  const float* T;      // [B, Hq, nqb]
-  uint8_t* keep;       // [B, Hq, nqb, nqb] or nullptr
-  float* tmax;         // [B, Hq, nqb, nqb] or nullptr
-  int B, Hq, Hkv, G, S, nqb;
-  float scale, scale_log2;
-  int n_items;
-};
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void gated_kernel(GatedArgs a) {
   constexpr int D = TD;

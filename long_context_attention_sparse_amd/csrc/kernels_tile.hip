@@ -1,0 +1,31 @@
+// MFMA tile kernels (prefill over patterns, BSFA gating) and their launch wrappers;
+// compiled without IEEE NaN quieting (the kernels never produce NaNs), which keeps the
+// softmax row maxima to plain v_max/v_max3 instructions.
+#include "gated.cuh"
+#include "launch.h"
+#include "prefill.cuh"
+
+namespace bsa {
+
+template <int NW, int KIND>
+static void launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((prefill_kernel<NW, KIND>), dim3(a.n_items), dim3(NW * 64), 0, st, a);
+}
+
+void launch_prefill(const PrefillArgs& a, int NW, int KIND, hipStream_t st) {
+  if (NW == 4) {
+    if (KIND == 0) launch_prefill_t<4, 0>(a, st);
+    else if (KIND == 1) launch_prefill_t<4, 1>(a, st);
+    else launch_prefill_t<4, 2>(a, st);
+  } else {
+    if (KIND == 0) launch_prefill_t<2, 0>(a, st);
+    else if (KIND == 1) launch_prefill_t<2, 1>(a, st);
+    else launch_prefill_t<2, 2>(a, st);
+  }
+}
+
+void launch_gated(const GatedArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(gated_kernel, dim3(a.n_items), dim3(256), 0, st, a);
+}
+
+}  // namespace bsa

@@ -1,0 +1,22 @@
+// Host-side launch wrappers, one per kernel family, defined in the translation unit
+// that instantiates the kernels (kernels_stream.hip, kernels_tile.hip) so that each
+// family is compiled with its own code-generation flags.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "args.cuh"
+
+namespace bsa {
+
+// decode_kernel<D>: grid (gx, groups, B), 256 threads.  D is 64 or 128.
+void launch_decode(const DecodeArgs& a, int D, int gx, int groups, int B, hipStream_t st);
+// combine_kernel over B*Sq*Hq rows.
+void launch_combine(const CombineArgs& a, hipStream_t st);
+// vs_convert_kernel: grid (cdiv(rows, kVSConvThreads), B*H), dynamic LDS lds_bytes.
+void launch_vs_convert(const VSConvArgs& a, unsigned lds_bytes, hipStream_t st);
+// prefill_kernel<NW, KIND>: n_items workgroups of NW*64 threads (NW 2 or 4, KIND 0..2).
+void launch_prefill(const PrefillArgs& a, int NW, int KIND, hipStream_t st);
+// gated_kernel: n_items workgroups of 256 threads.
+void launch_gated(const GatedArgs& a, hipStream_t st);
+
+}  // namespace bsa

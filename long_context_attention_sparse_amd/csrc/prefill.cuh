@@ -29,24 +29,6 @@
 
 namespace bsa {
 
-struct PrefillArgs {
-  TensorArg q, k, v;
-  OutArg o;
-  float* lse;
-  PatternArg pat;
-  const int32_t* cu_q;
-  const int32_t* cu_k;
-  int B, Hq, Hkv, G, Sq, Sk;  // Sq/Sk: lengths (varlen: maxima)
-  int nqb;                    // query blocks per (b, h) in the grid
-  int list_by_kv;             // lists indexed by kv head (1) or query head (0)
-  int causal;
-  float scale_log2;
-  int n_items;
-  int partial;                // 1: partials of epp entries each into part_o / part_lse
-  int epp, n_part;
-  float* part_o;              // [n_part, B, Sq, Hq, D]
-  float* part_lse;            // [n_part, B, Hq, Sq]
-};
 
 template <int NW, int KIND>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(PrefillArgs a) {

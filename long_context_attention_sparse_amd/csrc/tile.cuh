@@ -85,7 +85,8 @@ __device__ __forceinline__ void softmax_pv64(const f32x16& s0, const f32x16& s1,
     const float p3 = exp2_fast(fmaf(s1[r + 1], scale_log2, -m_use));
     pk[0][r / 2] = pack_bf16x2(p0, p1);
     pk[1][r / 2] = pack_bf16x2(p2, p3);
-    psum += bf16x2_sum(pk[0][r / 2]) + bf16x2_sum(pk[1][r / 2]);
+    psum = bf16x2_sum_acc(pk[0][r / 2], psum);
+    psum = bf16x2_sum_acc(pk[1][r / 2], psum);
     pesum += (p0 + p1) + (p2 + p3);
   }
   l_run += psum;

@@ -21,20 +21,7 @@
 
 namespace bsa {
 
-struct VSConvArgs {
-  const int32_t* q_seqlens;
-  const int32_t* kv_seqlens;
-  const int32_t* vertical;  // [B, H, nnz_v]
-  const int32_t* slash;     // [B, H, nnz_s]
-  int B, H, nnz_v, nnz_s, rows, BM, BN;
-  int32_t* bc;              // [B, H, rows]
-  int32_t* bo;              // [B, H, rows, nnz_s]
-  int32_t* cc;              // [B, H, rows]
-  int32_t* ci;              // [B, H, rows, nnz_v]
-};
 
-constexpr int kVSConvThreads = 64;
-constexpr int kVSConvLdsInts = 16384;  // most list entries staged in LDS (dynamic size); longer lists stay in global
 
 __global__ __launch_bounds__(kVSConvThreads) void vs_convert_kernel(VSConvArgs a) {
   extern __shared__ int32_t lists[];
