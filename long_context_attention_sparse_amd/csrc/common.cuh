@@ -9,6 +9,13 @@
 
 namespace bsa {
 
+// Workgroup and thread indices straight from the hardware registers (the builtins stay
+// inline whatever floating-point mode a kernel is compiled in; the library calls behind
+// blockIdx / threadIdx are not inlined into kernels built without IEEE mode, which turns
+// every value derived from them into a per-lane one).
+__device__ __forceinline__ int wg_x() { return (int)__builtin_amdgcn_workgroup_id_x(); }
+__device__ __forceinline__ int tid_x() { return (int)__builtin_amdgcn_workitem_id_x(); }
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));

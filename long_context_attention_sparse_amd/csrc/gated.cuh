@@ -27,7 +27,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
   __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VSTR];
   __shared__ float red[4];
 
-  const int item = xcd_item(blockIdx.x, a.n_items);
+  const int item = xcd_item(wg_x(), a.n_items);
   const int mrev = item % a.nqb;
   int rest = item / a.nqb;
   const int g = rest % a.G;
@@ -37,7 +37,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
   const int h = hkv * a.G + g;
   const int i = a.nqb - 1 - mrev;
 
-  const int t = threadIdx.x;
+  const int t = tid_x();
   const int w = t >> 6, l = t & 63;
   const int lq = l & 31, hh = l >> 5;
 

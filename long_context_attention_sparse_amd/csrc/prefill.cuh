@@ -49,7 +49,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   __shared__ int ents_s[kEnts];
   __shared__ int cols_s[kCols];
 
-  const int item = xcd_item(blockIdx.x, a.n_items);
+  const int item = xcd_item(wg_x(), a.n_items);
   const int mrev = item % a.nqb;
   int rest = item / a.nqb;
   const int g = rest % a.G;
@@ -71,7 +71,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int delta = kv_len - q_len;
   const int r_last = min(r0 + BM, q_len) - 1;
 
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int w = tid_x() >> 6, l = tid_x() & 63;
   const int lq = l & 31, hh = l >> 5;
 
   const int64_t qoff = a.cu_q ? (int64_t)q_start * a.q.ss : (int64_t)b * a.q.sb;
@@ -114,7 +114,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     }
   }
 
-  const int t = threadIdx.x;
+  const int t = tid_x();
   if constexpr (KIND != 0) {
     const int nl = min(KIND == 1 ? n_chunks / cpe : nwin, kEnts);
     for (int x = t; x < nl; x += NT) ents_s[x] = list[x];

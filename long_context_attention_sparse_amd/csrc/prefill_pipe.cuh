@@ -1,0 +1,409 @@
+// Pipelined prefill kernel for 128-row query tiles (four waves of 32 rows).
+//
+// Same operation as prefill_kernel ("Sparse FlashAttention with Incremental
+// Repair", Usage 1 and 3; "Implementation: Sgl project Sglang Sparse Flash
+// Attention", I/O Contract; dense without a pattern), built around two gfx950
+// features:
+//
+//   global_load_lds_dwordx4  K and V rows go straight from global memory into
+//                            LDS (lane L of a wave instruction fills LDS bytes
+//                            16L..16L+15 of a 1 KB slab), no register staging;
+//                            each lane picks the global 16-byte piece that its
+//                            slot holds under an XOR swizzle, which keeps the
+//                            MFMA operand reads free of bank conflicts.
+//   ds_read_b64_tr_b16       V^T operands are read transposed out of the
+//                            row-major V tile: lane r of a 16-lane group points
+//                            at V[k0 + r/4][d0 + 4(r%4)] and receives keys
+//                            k0..k0+3 of column d0 + r.
+//
+// K and V each have two 64-key LDS buffers (64 KB per workgroup, two
+// workgroups per CU).  Iteration ci holds S(ci) in registers and K(ci+1), V(ci)
+// in LDS; it issues the loads of K(ci+2) and V(ci+1), runs chunk ci's softmax
+// and PV product, then computes S(ci+1) and its row max.  One barrier per
+// iteration: each wave waits for its own loads of the previous iteration, the
+// barrier makes every wave's data visible and every wave done with the
+// buffers that the next loads overwrite.  The two waves on each SIMD come
+// from different workgroups and cover each other's LDS and MFMA waits.
+//
+// LDS layout of a buffer: 64 rows of 256 bytes (16 pieces of 8 bf16).  K row R
+// keeps global piece p in slot p ^ (R & 15); V row R in slot p ^ 4(R & 3).
+// Full chunks address K/V from a wave-uniform row pointer plus a fixed per-lane
+// offset; only chunks that run past the sequence end or gather columns resolve
+// keys per lane.
+#pragma once
+#include "tile.cuh"
+
+namespace bsa {
+
+template <int KIND>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_pipe_kernel(PrefillArgs a) {
+  constexpr int D = TD;
+  constexpr int BM = 128;
+  constexpr int RS = D;  // LDS row stride (bf16): rows are packed, the swizzle spreads banks
+  __shared__ __attribute__((aligned(16))) uint16_t K0[64 * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t K1[64 * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t V0[64 * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t V1[64 * RS];
+  __shared__ __attribute__((aligned(16))) int kid0[64];
+  __shared__ __attribute__((aligned(16))) int kid1[64];
+  constexpr int kEnts = 256;
+  constexpr int kCols = KIND == 2 ? 768 : 1;
+  __shared__ int ents_s[kEnts];
+  __shared__ int cols_s[kCols];
+
+  const int item = xcd_item(wg_x(), a.n_items);
+  const int mrev = item % a.nqb;
+  int rest = item / a.nqb;
+  const int g = rest % a.G;
+  rest /= a.G;
+  const int hkv = rest % a.Hkv;
+  const int b = rest / a.Hkv;
+  const int h = hkv * a.G + g;
+  const int m = a.nqb - 1 - mrev;
+
+  int q_start = 0, q_len = a.Sq, k_start = 0, kv_len = a.Sk;
+  if (a.cu_q) {
+    q_start = a.cu_q[b];
+    q_len = a.cu_q[b + 1] - q_start;
+    k_start = a.cu_k[b];
+    kv_len = a.cu_k[b + 1] - k_start;
+  }
+  const int r0 = m * BM;
+  if (r0 >= q_len) return;  // uniform: no barrier has run yet
+  const int delta = kv_len - q_len;
+  const int r_last = min(r0 + BM, q_len) - 1;
+
+  const int t = tid_x();
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63;
+  const int lq = l & 31, hh = l >> 5;
+
+  const uint16_t* qb = reinterpret_cast<const uint16_t*>(a.q.ptr) +
+                       (a.cu_q ? (int64_t)q_start * a.q.ss : (int64_t)b * a.q.sb) + (int64_t)h * a.q.sh;
+  const uint16_t* kbp = reinterpret_cast<const uint16_t*>(a.k.ptr) +
+                        (a.cu_q ? (int64_t)k_start * a.k.ss : (int64_t)b * a.k.sb) + (int64_t)hkv * a.k.sh;
+  const uint16_t* vbp = reinterpret_cast<const uint16_t*>(a.v.ptr) +
+                        (a.cu_q ? (int64_t)k_start * a.v.ss : (int64_t)b * a.v.sb) + (int64_t)hkv * a.v.sh;
+
+  const int row = r0 + w * 32 + lq;
+  const bool row_ok = row < q_len;
+  bf16x8 qreg[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const u32x4 v = row_ok ? ldg128(qb + (int64_t)row * a.q.ss + ks * 16 + hh * 8) : u32x4{0, 0, 0, 0};
+    qreg[ks] = as_bf16x8(v);
+  }
+
+  // ---- chunk list ----
+  int n_chunks = 0, cpe = 1, nwin = 0, ncol = 0;
+  const int32_t* list = nullptr;
+  const int32_t* cols = nullptr;
+  if constexpr (KIND == 0) {
+    int kend = kv_len;
+    if (a.causal) kend = min(kv_len, r_last + delta + 1);
+    n_chunks = kend > 0 ? (kend + 63) / 64 : 0;
+  } else {
+    const int ht = a.list_by_kv ? hkv : h;
+    const int64_t lb = (int64_t)b * a.pat.s_b + (int64_t)ht * a.pat.s_h + (int64_t)m * a.pat.s_q;
+    const int cnt = a.pat.count[lb];
+    list = a.pat.index + lb * a.pat.cap;
+    if constexpr (KIND == 1) {
+      cpe = a.pat.block_N / 64;
+      n_chunks = cnt * cpe;
+    } else {
+      nwin = cnt;
+      ncol = a.pat.col_count[lb];
+      cols = a.pat.col_index + lb * a.pat.col_cap;
+      n_chunks = nwin + (ncol + 63) / 64;
+    }
+  }
+  if (kv_len <= 0) n_chunks = 0;
+  if constexpr (KIND != 0) {
+    const int nl = min(KIND == 1 ? n_chunks / cpe : nwin, kEnts);
+    for (int x = t; x < nl; x += 256) ents_s[x] = list[x];
+    if constexpr (KIND == 2) {
+      const int nc = min(ncol, kCols);
+      for (int x = t; x < nc; x += 256) cols_s[x] = cols[x];
+    }
+  }
+
+  // A chunk is 64 consecutive keys from key0 (possibly running past the sequence end or
+  // starting before 0 for a window) or up to 64 gathered columns from gbase.  key0 and the
+  // flags are wave-uniform and live in scalar registers.
+  struct Chunk {
+    int key0 = 0, gbase = 0;
+    bool gathered = false, full = false;  // full: all 64 keys inside [0, kv_len)
+  };
+  auto chunk_at = [&](int ci, bool staged) -> Chunk {
+    Chunk r;
+    if constexpr (KIND == 0) {
+      r.key0 = ci * 64;
+    } else if constexpr (KIND == 1) {
+      const int e = ci / cpe;
+      const int id = staged && e < kEnts ? lds_int(ents_s, e) : global_int(list, e);
+      r.key0 = __builtin_amdgcn_readfirstlane(id) * a.pat.block_N + (ci - e * cpe) * 64;
+    } else {
+      if (ci < nwin) {
+        const int off = staged && ci < kEnts ? lds_int(ents_s, ci) : global_int(list, ci);
+        r.key0 = __builtin_amdgcn_readfirstlane(off);
+      } else {
+        r.gathered = true;
+        r.gbase = (ci - nwin) * 64;
+      }
+    }
+    r.full = !r.gathered && r.key0 >= 0 && r.key0 <= kv_len - 64;
+    return r;
+  };
+  // chunk-local key i -> key index within the sequence, or -1 when absent
+  auto key_of = [&](int i, const Chunk& r, bool staged) -> int {
+    int key;
+    if (r.gathered) {
+      const int x = r.gbase + i;
+      if (x >= ncol) return -1;
+      key = (staged && x < kCols) ? cols_s[x] : cols[x];
+    } else {
+      key = r.key0 + i;
+    }
+    return (unsigned)key < (unsigned)kv_len ? key : -1;
+  };
+
+  // Wave w fills LDS rows 16w..16w+15 of a tile with four 1 KB instructions: instruction i
+  // covers rows 16w + 4i + l/16, lane l landing in slot l%16.  Row R's slot s holds piece
+  // s ^ (R & 15) (K) or s ^ 4(R & 3) (V); with R & 15 = 4i + l/16 the per-lane byte offset
+  // within the row is kx ^ 64i (K) or a constant (V).  A full chunk adds these to a
+  // wave-uniform row address; otherwise each lane resolves its key, and absent keys load row
+  // 0 (finite data, masked out later) so no slot keeps stale bits.
+  const int lrow = l >> 4, lslot = l & 15;
+  const uint32_t kx = (uint32_t)(lslot ^ lrow) << 4;
+  const uint32_t vx = (uint32_t)(lslot ^ (lrow << 2)) << 4;
+  const uint32_t k_lane = (uint32_t)(lrow * a.k.ss) * 2u, v_lane = (uint32_t)(lrow * a.v.ss) * 2u + vx;
+  auto issue_k = [&](uint16_t* kt, int* kid, const Chunk& r, bool staged) __attribute__((always_inline)) {
+    if (r.full) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const char* rowp = reinterpret_cast<const char*>(kbp + (int64_t)(r.key0 + w * 16 + i * 4) * a.k.ss);
+        __builtin_amdgcn_global_load_lds(rowp + (k_lane + (kx ^ (i << 6))), BSA_LDS(kt + (w * 4 + i) * 4 * RS), 16,
+                                         0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int key = key_of(w * 16 + i * 4 + lrow, r, staged);
+        key = key < 0 ? 0 : key;
+        const char* rowp = reinterpret_cast<const char*>(kbp + (int64_t)key * a.k.ss);
+        __builtin_amdgcn_global_load_lds(rowp + (kx ^ (i << 6)), BSA_LDS(kt + (w * 4 + i) * 4 * RS), 16, 0, 0);
+      }
+      if constexpr (KIND == 2) {
+        if (r.gathered && t < 64) {
+          const int key = key_of(t, r, staged);
+          kid[t] = key >= 0 ? key : 0x7fffffff;
+        }
+      }
+    }
+  };
+  auto issue_v = [&](uint16_t* vt, const Chunk& r, bool staged) __attribute__((always_inline)) {
+    if (r.full) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const char* rowp = reinterpret_cast<const char*>(vbp + (int64_t)(r.key0 + w * 16 + i * 4) * a.v.ss);
+        __builtin_amdgcn_global_load_lds(rowp + v_lane, BSA_LDS(vt + (w * 4 + i) * 4 * RS), 16, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int key = key_of(w * 16 + i * 4 + lrow, r, staged);
+        key = key < 0 ? 0 : key;
+        const char* rowp = reinterpret_cast<const char*>(vbp + (int64_t)key * a.v.ss);
+        __builtin_amdgcn_global_load_lds(rowp + vx, BSA_LDS(vt + (w * 4 + i) * 4 * RS), 16, 0, 0);
+      }
+    }
+  };
+
+  // per-lane LDS offsets of the MFMA operands (loop invariant)
+  int koff[D / 16];  // K: row lq (+32 for the second block), piece 2ks + hh, swizzled
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) koff[ks] = lq * RS + (((ks * 2 + hh) ^ k_swz(lq)) << 3);
+  const int tg = l >> 4, tr = l & 15;  // transpose read: 16-lane group and lane in group
+  // V^T: row (tg/2)*4 + tr/4 (+16ks + 8j), column 32db + 16(tg%2) + 4(tr%4)
+  const int vrow = (tg >> 1) * 4 + (tr >> 2);
+  int voff[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    const int col = db * 32 + (tg & 1) * 16 + (tr & 3) * 4;
+    voff[db] = vrow * RS + ((((col >> 3) ^ v_swz(vrow))) << 3) + (col & 7);
+  }
+
+  auto s_block = [&](const uint16_t* kt, int kb) -> f32x16 {
+    f32x16 s = {};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const u32x4 av = *reinterpret_cast<const u32x4*>(kt + kb * 32 * RS + koff[ks]);
+      s = mfma32x32x16(as_bf16x8(av), qreg[ks], s);
+    }
+    return s;
+  };
+
+  float m_run = kNegInf, l_run = 0.f, le_run = 0.f;
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
+
+  // exponentials of chunk S (s0: keys 0-31, s1: 32-63), both normalisers and O^T += V^T P^T
+  auto exp_pv = [&](const f32x16& s0, const f32x16& s1, const uint16_t* vt) __attribute__((always_inline)) {
+    const float m_use = m_run == kNegInf ? 0.f : m_run;
+    uint32_t pk[2][8];
+    float psum = 0.f, pesum = 0.f;
+    // keys 0-31 first: they feed the first eight PV MFMAs
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const f32x16& sv = kb == 0 ? s0 : s1;
+#pragma unroll
+      for (int r = 0; r < 16; r += 4) {
+        const float p0 = exp2_fast(fmaf(sv[r], a.scale_log2, -m_use));
+        const float p1 = exp2_fast(fmaf(sv[r + 1], a.scale_log2, -m_use));
+        const float p2 = exp2_fast(fmaf(sv[r + 2], a.scale_log2, -m_use));
+        const float p3 = exp2_fast(fmaf(sv[r + 3], a.scale_log2, -m_use));
+        pk[kb][r / 2] = pack_bf16x2(p0, p1);
+        pk[kb][r / 2 + 1] = pack_bf16x2(p2, p3);
+        psum = bf16x2_sum_acc(pk[kb][r / 2], psum);
+        psum = bf16x2_sum_acc(pk[kb][r / 2 + 1], psum);
+        pesum += (p0 + p1) + (p2 + p3);
+      }
+    }
+    l_run += psum;
+    le_run += pesum;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int kb = ks >> 1, hb = ks & 1;
+      const u32x4 pb = {pk[kb][hb * 4], pk[kb][hb * 4 + 1], pk[kb][hb * 4 + 2], pk[kb][hb * 4 + 3]};
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const u32x2 lo = ds_read_tr16(vt + ks * 16 * RS + voff[db]);
+        const u32x2 hi = ds_read_tr16(vt + (ks * 16 + 8) * RS + voff[db]);
+        const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
+        oacc[db] = mfma32x32x16(as_bf16x8(av), as_bf16x8(pb), oacc[db]);
+      }
+    }
+  };
+
+  auto finish = [&](int slot) __attribute__((always_inline)) {
+    if (row_ok) {
+      if (!a.partial) {
+        const int64_t ob = (a.cu_q ? (int64_t)(q_start + row) * a.o.ss : (int64_t)b * a.o.sb + (int64_t)row * a.o.ss) +
+                           (int64_t)h * a.o.sh;
+        float* lp = nullptr;
+        if (a.lse) lp = a.lse + (a.cu_q ? (int64_t)h * a.cu_q[a.B] + q_start + row : ((int64_t)b * a.Hq + h) * a.Sq + row);
+        write_row(a.o, ob, lp, oacc, m_run, l_run, le_run, hh);
+      } else {
+        const OutArg po{a.part_o, 0, (int64_t)a.Hq * D, D, 1};
+        const int64_t ob = (((int64_t)slot * a.B + b) * a.Sq + row) * a.Hq * D + (int64_t)h * D;
+        write_row(po, ob, a.part_lse + (((int64_t)slot * a.B + b) * a.Hq + h) * a.Sq + row, oacc, m_run, l_run,
+                  le_run, hh);
+      }
+    }
+    m_run = kNegInf;
+    l_run = 0.f;
+    le_run = 0.f;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
+  };
+
+  // -inf for absent keys and, when causal, keys after the row's diagonal.  Contiguous
+  // chunks compare key0 + (register's key offset) against a per-row limit; gathered
+  // chunks read the key indices that issue_k stored.
+  const int wrow_min = r0 + w * 32;
+  auto mask_chunk = [&](const int* kid, const Chunk& r, f32x16& s0, f32x16& s1) __attribute__((always_inline)) {
+    const int lim = a.causal ? row + delta : 0x7ffffffe;
+    if (r.gathered) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int4 k0 = *reinterpret_cast<const int4*>(kid + q4 * 8 + hh * 4);
+        const int4 k1 = *reinterpret_cast<const int4*>(kid + 32 + q4 * 8 + hh * 4);
+        if (k0.x > lim) s0[q4 * 4 + 0] = kNegInf;
+        if (k0.y > lim) s0[q4 * 4 + 1] = kNegInf;
+        if (k0.z > lim) s0[q4 * 4 + 2] = kNegInf;
+        if (k0.w > lim) s0[q4 * 4 + 3] = kNegInf;
+        if (k1.x > lim) s1[q4 * 4 + 0] = kNegInf;
+        if (k1.y > lim) s1[q4 * 4 + 1] = kNegInf;
+        if (k1.z > lim) s1[q4 * 4 + 2] = kNegInf;
+        if (k1.w > lim) s1[q4 * 4 + 3] = kNegInf;
+      }
+      return;
+    }
+    const bool need = !r.full || (a.causal && r.key0 + 63 > wrow_min + delta);
+    if (!need) return;
+    // key0 + kl is present and visible iff lo <= kl <= hi
+    const int hi = min(lim, kv_len - 1) - r.key0;
+    const int lo = -r.key0;
+#pragma unroll
+    for (int rg = 0; rg < 16; ++rg) {
+      const int kl = (rg >> 2) * 8 + hh * 4 + (rg & 3);
+      if (kl > hi || kl < lo) s0[rg] = kNegInf;
+      if (kl + 32 > hi || kl + 32 < lo) s1[rg] = kNegInf;
+    }
+  };
+
+  // ---- pipeline ----
+  f32x16 sc0 = {}, sc1 = {};
+  Chunk nxt;
+  if (n_chunks > 0) {
+    // the first chunks read their addresses from global memory, overlapping the staging
+    const Chunk c0 = chunk_at(0, false);
+    issue_k(K0, kid0, c0, false);
+    issue_v(V0, c0, false);
+    if (n_chunks > 1) {
+      nxt = chunk_at(1, false);
+      issue_k(K1, kid1, nxt, false);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    sc0 = s_block(K0, 0);
+    sc1 = s_block(K0, 1);
+    mask_chunk(kid0, c0, sc0, sc1);
+    softmax_max(sc0, sc1, a.scale_log2, m_run, l_run, le_run, oacc);
+  }
+
+  // Chunk ci: S(ci) in (sc0, sc1); K stages kc / kn (this chunk / the next), V stages vc / vn.
+  // The other wave on the SIMD (from the second workgroup on the CU) fills this wave's
+  // LDS and MFMA waits, so S(ci+1) simply follows chunk ci's softmax and PV product.
+  auto step = [&](int ci, uint16_t* kc, int* kidc, uint16_t* kn, const int* kidn, const uint16_t* vc, uint16_t* vn)
+                  __attribute__((always_inline)) {
+    // this wave's loads of the previous step (K(ci+1), V(ci)) are done; after the barrier
+    // every wave's are, and no wave still reads kc or vn
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    const bool has1 = ci + 1 < n_chunks, has2 = ci + 2 < n_chunks;
+    Chunk nn;
+    if (has2) {
+      nn = chunk_at(ci + 2, true);
+      issue_k(kc, kidc, nn, true);
+    }
+    if (has1) issue_v(vn, nxt, true);
+    exp_pv(sc0, sc1, vc);
+    if constexpr (KIND != 2) {
+      if (a.partial && (ci % cpe) == cpe - 1) {
+        const int e = ci / cpe;
+        if ((e + 1) % a.epp == 0 || ci == n_chunks - 1) finish(e / a.epp);
+      }
+    }
+    if (has1) {
+      sc0 = s_block(kn, 0);
+      sc1 = s_block(kn, 1);
+      mask_chunk(kidn, nxt, sc0, sc1);
+      softmax_max(sc0, sc1, a.scale_log2, m_run, l_run, le_run, oacc);
+    }
+    nxt = nn;
+  };
+  for (int ci = 0; ci < n_chunks; ci += 2) {
+    step(ci, K0, kid0, K1, kid1, V0, V1);
+    if (ci + 1 < n_chunks) step(ci + 1, K1, kid1, K0, kid0, V1, V0);
+  }
+
+  if (!a.partial) {
+    finish(0);
+  } else {
+    const int first_empty = n_chunks > 0 ? ((n_chunks - 1) / cpe) / a.epp + 1 : 0;
+    for (int s = first_empty; s < a.n_part; ++s) finish(s);
+  }
+}
+
+}  // namespace bsa

@@ -51,15 +51,17 @@ __device__ __forceinline__ f32x16 st_block(const uint16_t* Ks, int krow0, const 
   return s;
 }
 
-// Online softmax over 64 keys (s0: keys 0-31, s1: keys 32-63 of V^T columns vcol0..vcol0+63)
-// and O^T += V^T P^T.  Masked scores are -inf.  m_run is in scaled log2 units.
-// Two normalisers are kept: l_run sums the bf16-rounded weights the PV product uses (O is
-// then an exact convex combination of V rows, so a dominant key's rounding cancels) and
-// le_run sums the exact weights (for LSE).
-template <int VSTR>
-__device__ __forceinline__ void softmax_pv64(const f32x16& s0, const f32x16& s1, const uint16_t* Vt, int vcol0,
-                                             float scale_log2, float& m_run, float& l_run, float& le_run,
-                                             f32x16* oacc, int lq, int hh) {
+// Online softmax over 64 keys, in two steps so a pipelined loop can place them apart.
+// s0 holds keys 0-31 and s1 keys 32-63 of the chunk (V^T columns vcol0..vcol0+63);
+// masked scores are -inf; m_run is in scaled log2 units.  Two normalisers are kept:
+// l_run sums the bf16-rounded weights the PV product uses (O is then an exact convex
+// combination of V rows, so a dominant key's rounding cancels) and le_run sums the exact
+// weights (for LSE).
+//
+// Step 1: the chunk's row maximum, and the lazy rescale: the reference maximum only
+// moves (rescaling O and the sums) when the new maximum exceeds it by more than 2^8.
+__device__ __forceinline__ void softmax_max(const f32x16& s0, const f32x16& s1, float scale_log2, float& m_run,
+                                            float& l_run, float& le_run, f32x16* oacc) {
   float mx = kNegInf;
 #pragma unroll
   for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
@@ -74,6 +76,13 @@ __device__ __forceinline__ void softmax_pv64(const f32x16& s0, const f32x16& s1,
 #pragma unroll
     for (int db = 0; db < TD / 32; ++db) oacc[db] *= alpha;
   }
+}
+
+// Step 2: weights, both normalisers, and O^T += V^T P^T.
+template <int VSTR>
+__device__ __forceinline__ void softmax_pv(const f32x16& s0, const f32x16& s1, const uint16_t* Vt, int vcol0,
+                                           float scale_log2, float m_run, float& l_run, float& le_run,
+                                           f32x16* oacc, int lq, int hh) {
   const float m_use = m_run == kNegInf ? 0.f : m_run;
   uint32_t pk[2][8];
   float psum = 0.f, pesum = 0.f;
@@ -105,6 +114,15 @@ __device__ __forceinline__ void softmax_pv64(const f32x16& s0, const f32x16& s1,
     }
 }
 
+// Both steps back to back.
+template <int VSTR>
+__device__ __forceinline__ void softmax_pv64(const f32x16& s0, const f32x16& s1, const uint16_t* Vt, int vcol0,
+                                             float scale_log2, float& m_run, float& l_run, float& le_run,
+                                             f32x16* oacc, int lq, int hh) {
+  softmax_max(s0, s1, scale_log2, m_run, l_run, le_run, oacc);
+  softmax_pv<VSTR>(s0, s1, Vt, vcol0, scale_log2, m_run, l_run, le_run, oacc, lq, hh);
+}
+
 // Normalise and store one query row's O (32 rows per wave, 64 dims per lane) and its LSE.
 // o_off: element offset of the row start (head dim 0) in the output.
 __device__ __forceinline__ void write_row(const OutArg& o, int64_t o_off, float* lse_ptr, const f32x16* oacc,
@@ -122,6 +140,30 @@ __device__ __forceinline__ void write_row(const OutArg& o, int64_t o_off, float*
     }
   if (hh == 0 && lse_ptr) *lse_ptr = le > 0.f ? (m_run + log2f(le)) * kLn2 : kNegInf;
 }
+
+// ---- direct global->LDS tiles (global_load_lds_dwordx4) and transposed LDS reads ----
+// A 64-key tile is 64 rows of 256 bytes (16 pieces of 8 bf16).  K row R keeps global piece
+// p in slot p ^ (R & 15), V row R in slot p ^ 4(R & 3): both keep the MFMA operand reads
+// (b128 rows of K, b64 transposed reads of V) free of bank conflicts.
+__device__ __forceinline__ int k_swz(int row) { return row & 15; }
+__device__ __forceinline__ int v_swz(int row) { return (row & 3) << 2; }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+#define BSA_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+// Loads through explicitly typed LDS / global pointers.
+__device__ __forceinline__ int lds_int(const int* p, int i) {
+  return ((const __attribute__((address_space(3))) int*)p)[i];
+}
+__device__ __forceinline__ int global_int(const int* p, int i) {
+  return ((const __attribute__((address_space(1))) int*)p)[i];
+}
+
+__device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
 
 // Work item for an XCD-aware, heavy-first launch: workgroup lid of n_items ->
 // item index such that XCD x (= lid % 8) runs the contiguous item range x.
