@@ -3,17 +3,13 @@
 // softmax row maxima to plain v_max/v_max3 instructions.
 #include "gated.cuh"
 #include "launch.h"
-#include "prefill.cuh"
 #include "prefill_pipe.cuh"
 
 namespace bsa {
 
 template <int NW, int KIND>
 static void launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
-  if constexpr (NW == 4)
-    hipLaunchKernelGGL((prefill_pipe_kernel<KIND>), dim3(a.n_items), dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL((prefill_kernel<NW, KIND>), dim3(a.n_items), dim3(NW * 64), 0, st, a);
+  hipLaunchKernelGGL((prefill_pipe_kernel<KIND, NW>), dim3(a.n_items), dim3(NW * 64), 0, st, a);
 }
 
 void launch_prefill(const PrefillArgs& a, int NW, int KIND, hipStream_t st) {

@@ -14,7 +14,7 @@ void launch_decode(const DecodeArgs& a, int D, int gx, int groups, int B, hipStr
 void launch_combine(const CombineArgs& a, hipStream_t st);
 // vs_convert_kernel: grid (cdiv(rows, kVSConvThreads), B*H), dynamic LDS lds_bytes.
 void launch_vs_convert(const VSConvArgs& a, unsigned lds_bytes, hipStream_t st);
-// prefill_kernel<NW, KIND>: n_items workgroups of NW*64 threads (NW 2 or 4, KIND 0..2).
+// prefill_pipe_kernel<KIND, NW>: n_items workgroups of NW*64 threads (NW 2 or 4, KIND 0..2).
 void launch_prefill(const PrefillArgs& a, int NW, int KIND, hipStream_t st);
 // gated_kernel: n_items workgroups of 256 threads.
 void launch_gated(const GatedArgs& a, hipStream_t st);

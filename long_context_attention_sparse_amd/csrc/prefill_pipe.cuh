@@ -1,10 +1,15 @@
-// Pipelined prefill kernel for 128-row query tiles (four waves of 32 rows).
+// Pipelined prefill kernel: NW waves of 32 query rows (BM = 32 NW rows per
+// workgroup), keys in chunks of CK = 16 NW (64 keys for 128-row tiles, 32 keys
+// for 64-row tiles).
 //
-// Same operation as prefill_kernel ("Sparse FlashAttention with Incremental
-// Repair", Usage 1 and 3; "Implementation: Sgl project Sglang Sparse Flash
-// Attention", I/O Contract; dense without a pattern), built around two gfx950
-// features:
+// Attention restricted to listed keys ("Sparse FlashAttention with Incremental
+// Repair", Usage 1 for block lists and Usage 3 for partials; "Implementation:
+// Sgl project Sglang Sparse Flash Attention", I/O Contract, for vertical-slash
+// block offsets and column indices; dense when no pattern is given).  A chunk
+// is CK consecutive keys (a dense range, part of a listed block or of a
+// vertical-slash window at any offset) or up to CK gathered vertical columns.
 //
+// Built around two gfx950 features:
 //   global_load_lds_dwordx4  K and V rows go straight from global memory into
 //                            LDS (lane L of a wave instruction fills LDS bytes
 //                            16L..16L+15 of a 1 KB slab), no register staging;
@@ -16,36 +21,52 @@
 //                            at V[k0 + r/4][d0 + 4(r%4)] and receives keys
 //                            k0..k0+3 of column d0 + r.
 //
-// K and V each have two 64-key LDS buffers (64 KB per workgroup, two
-// workgroups per CU).  Iteration ci holds S(ci) in registers and K(ci+1), V(ci)
-// in LDS; it issues the loads of K(ci+2) and V(ci+1), runs chunk ci's softmax
-// and PV product, then computes S(ci+1) and its row max.  One barrier per
-// iteration: each wave waits for its own loads of the previous iteration, the
-// barrier makes every wave's data visible and every wave done with the
-// buffers that the next loads overwrite.  The two waves on each SIMD come
-// from different workgroups and cover each other's LDS and MFMA waits.
+// K and V each have two CK-key LDS buffers (64 KB per 128-row workgroup, two per
+// CU; 32 KB per 64-row workgroup, four per CU).  Iteration ci holds S(ci) in
+// registers and K(ci+1), V(ci) in LDS; it issues the loads of K(ci+2) and
+// V(ci+1), runs chunk ci's softmax and PV product, then computes S(ci+1) and its
+// row max.  One barrier per iteration: each wave waits for its own loads of the
+// previous iteration, the barrier makes every wave's data visible and every wave
+// done with the buffers that the next loads overwrite.  The two waves on each
+// SIMD come from different workgroups and cover each other's LDS and MFMA waits.
 //
-// LDS layout of a buffer: 64 rows of 256 bytes (16 pieces of 8 bf16).  K row R
+// Per wave and chunk: S^T = K Q^T (v_mfma_f32_32x32x16_bf16, Q^T in registers),
+// online softmax in base 2 with scale*log2(e) folded into one FMA and a lazy
+// rescale (tile.cuh), O^T += V^T P^T with P rounded to bf16.
+//
+// LDS layout of a buffer: CK rows of 256 bytes (16 pieces of 8 bf16).  K row R
 // keeps global piece p in slot p ^ (R & 15); V row R in slot p ^ 4(R & 3).
 // Full chunks address K/V from a wave-uniform row pointer plus a fixed per-lane
 // offset; only chunks that run past the sequence end or gather columns resolve
 // keys per lane.
+//
+// Grid: one workgroup per (b, h_q, query block), remapped so that each XCD takes
+// a contiguous range ordered (b, h_kv, h_q, query block descending): workgroups
+// sharing a key/value head share an L2, and the longest causal rows start first.
 #pragma once
 #include "tile.cuh"
 
 namespace bsa {
 
-template <int KIND>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_pipe_kernel(PrefillArgs a) {
+template <int KIND, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void prefill_pipe_kernel(PrefillArgs a) {
+  static_assert(NW == 2 || NW == 4, "64- or 128-row tiles");
   constexpr int D = TD;
-  constexpr int BM = 128;
-  constexpr int RS = D;  // LDS row stride (bf16): rows are packed, the swizzle spreads banks
-  __shared__ __attribute__((aligned(16))) uint16_t K0[64 * RS];
-  __shared__ __attribute__((aligned(16))) uint16_t K1[64 * RS];
-  __shared__ __attribute__((aligned(16))) uint16_t V0[64 * RS];
-  __shared__ __attribute__((aligned(16))) uint16_t V1[64 * RS];
-  __shared__ __attribute__((aligned(16))) int kid0[64];
-  __shared__ __attribute__((aligned(16))) int kid1[64];
+  constexpr int NT = NW * 64;
+  constexpr int BM = 32 * NW;
+  constexpr int CK = 16 * NW;   // keys per chunk: every wave loads 16 rows of each tile
+  constexpr int NB = CK / 32;   // 32-key S blocks per chunk
+  constexpr int NKS = CK / 16;  // 16-key PV steps per chunk
+  constexpr int RS = D;         // LDS row stride (bf16): rows are packed, the swizzle spreads banks
+  __shared__ __attribute__((aligned(16))) uint16_t K0[CK * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t K1[CK * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t V0[CK * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t V1[CK * RS];
+  constexpr int kKid = KIND == 2 ? CK : 4;
+  __shared__ __attribute__((aligned(16))) int kid0[kKid];
+  __shared__ __attribute__((aligned(16))) int kid1[kKid];
+  // list entries (block ids or window offsets) and gathered column indices staged in LDS,
+  // so a chunk's addresses never wait on a dependent global load
   constexpr int kEnts = 256;
   constexpr int kCols = KIND == 2 ? 768 : 1;
   __shared__ int ents_s[kEnts];
@@ -94,63 +115,62 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   }
 
   // ---- chunk list ----
-  int n_chunks = 0, cpe = 1, nwin = 0, ncol = 0;
+  // cpe: chunks per list entry (a block, or a window of block_N keys); nwc: window chunks
+  int n_chunks = 0, cpe = 1, nwc = 0, ncol = 0, n_ent = 0;
   const int32_t* list = nullptr;
   const int32_t* cols = nullptr;
   if constexpr (KIND == 0) {
     int kend = kv_len;
     if (a.causal) kend = min(kv_len, r_last + delta + 1);
-    n_chunks = kend > 0 ? (kend + 63) / 64 : 0;
+    n_chunks = kend > 0 ? (kend + CK - 1) / CK : 0;
+    cpe = 64 / CK;  // partial outputs group 64-key entries
   } else {
     const int ht = a.list_by_kv ? hkv : h;
     const int64_t lb = (int64_t)b * a.pat.s_b + (int64_t)ht * a.pat.s_h + (int64_t)m * a.pat.s_q;
-    const int cnt = a.pat.count[lb];
+    n_ent = a.pat.count[lb];
     list = a.pat.index + lb * a.pat.cap;
+    cpe = a.pat.block_N / CK;
     if constexpr (KIND == 1) {
-      cpe = a.pat.block_N / 64;
-      n_chunks = cnt * cpe;
+      n_chunks = n_ent * cpe;
     } else {
-      nwin = cnt;
+      nwc = n_ent * cpe;
       ncol = a.pat.col_count[lb];
       cols = a.pat.col_index + lb * a.pat.col_cap;
-      n_chunks = nwin + (ncol + 63) / 64;
+      n_chunks = nwc + (ncol + CK - 1) / CK;
     }
   }
   if (kv_len <= 0) n_chunks = 0;
   if constexpr (KIND != 0) {
-    const int nl = min(KIND == 1 ? n_chunks / cpe : nwin, kEnts);
-    for (int x = t; x < nl; x += 256) ents_s[x] = list[x];
+    const int nl = min(n_ent, kEnts);
+    for (int x = t; x < nl; x += NT) ents_s[x] = list[x];
     if constexpr (KIND == 2) {
       const int nc = min(ncol, kCols);
-      for (int x = t; x < nc; x += 256) cols_s[x] = cols[x];
+      for (int x = t; x < nc; x += NT) cols_s[x] = cols[x];
     }
   }
 
-  // A chunk is 64 consecutive keys from key0 (possibly running past the sequence end or
-  // starting before 0 for a window) or up to 64 gathered columns from gbase.  key0 and the
+  // A chunk is CK consecutive keys from key0 (possibly running past the sequence end or
+  // starting before 0 for a window) or up to CK gathered columns from gbase.  key0 and the
   // flags are wave-uniform and live in scalar registers.
   struct Chunk {
     int key0 = 0, gbase = 0;
-    bool gathered = false, full = false;  // full: all 64 keys inside [0, kv_len)
+    bool gathered = false, full = false;  // full: all CK keys inside [0, kv_len)
   };
   auto chunk_at = [&](int ci, bool staged) -> Chunk {
     Chunk r;
     if constexpr (KIND == 0) {
-      r.key0 = ci * 64;
-    } else if constexpr (KIND == 1) {
-      const int e = ci / cpe;
-      const int id = staged && e < kEnts ? lds_int(ents_s, e) : global_int(list, e);
-      r.key0 = __builtin_amdgcn_readfirstlane(id) * a.pat.block_N + (ci - e * cpe) * 64;
+      r.key0 = ci * CK;
     } else {
-      if (ci < nwin) {
-        const int off = staged && ci < kEnts ? lds_int(ents_s, ci) : global_int(list, ci);
-        r.key0 = __builtin_amdgcn_readfirstlane(off);
+      if (KIND == 1 || ci < nwc) {
+        const int e = ci / cpe;
+        const int id = __builtin_amdgcn_readfirstlane(staged && e < kEnts ? lds_int(ents_s, e) : global_int(list, e));
+        r.key0 = (KIND == 1 ? id * a.pat.block_N : id) + (ci - e * cpe) * CK;
       } else {
         r.gathered = true;
-        r.gbase = (ci - nwin) * 64;
+        r.gbase = (ci - nwc) * CK;
       }
     }
-    r.full = !r.gathered && r.key0 >= 0 && r.key0 <= kv_len - 64;
+    r.full = !r.gathered && r.key0 >= 0 && r.key0 <= kv_len - CK;
     return r;
   };
   // chunk-local key i -> key index within the sequence, or -1 when absent
@@ -192,8 +212,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         const char* rowp = reinterpret_cast<const char*>(kbp + (int64_t)key * a.k.ss);
         __builtin_amdgcn_global_load_lds(rowp + (kx ^ (i << 6)), BSA_LDS(kt + (w * 4 + i) * 4 * RS), 16, 0, 0);
       }
+      // gathered chunks record their key indices for the mask
       if constexpr (KIND == 2) {
-        if (r.gathered && t < 64) {
+        if (r.gathered && t < CK) {
           const int key = key_of(t, r, staged);
           kid[t] = key >= 0 ? key : 0x7fffffff;
         }
@@ -219,7 +240,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   };
 
   // per-lane LDS offsets of the MFMA operands (loop invariant)
-  int koff[D / 16];  // K: row lq (+32 for the second block), piece 2ks + hh, swizzled
+  int koff[D / 16];  // K: row lq (+32 kb), piece 2ks + hh, swizzled
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) koff[ks] = lq * RS + (((ks * 2 + hh) ^ k_swz(lq)) << 3);
   const int tg = l >> 4, tr = l & 15;  // transpose read: 16-lane group and lane in group
@@ -232,14 +253,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     voff[db] = vrow * RS + ((((col >> 3) ^ v_swz(vrow))) << 3) + (col & 7);
   }
 
-  auto s_block = [&](const uint16_t* kt, int kb) -> f32x16 {
-    f32x16 s = {};
+  // S^T for the chunk in LDS: block kb holds keys 32kb..32kb+31
+  auto s_chunk = [&](const uint16_t* kt, f32x16* s) __attribute__((always_inline)) {
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      const u32x4 av = *reinterpret_cast<const u32x4*>(kt + kb * 32 * RS + koff[ks]);
-      s = mfma32x32x16(as_bf16x8(av), qreg[ks], s);
+    for (int kb = 0; kb < NB; ++kb) {
+      f32x16 acc = {};
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const u32x4 av = *reinterpret_cast<const u32x4*>(kt + kb * 32 * RS + koff[ks]);
+        acc = mfma32x32x16(as_bf16x8(av), qreg[ks], acc);
+      }
+      s[kb] = acc;
     }
-    return s;
   };
 
   float m_run = kNegInf, l_run = 0.f, le_run = 0.f;
@@ -247,21 +272,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
 
-  // exponentials of chunk S (s0: keys 0-31, s1: 32-63), both normalisers and O^T += V^T P^T
-  auto exp_pv = [&](const f32x16& s0, const f32x16& s1, const uint16_t* vt) __attribute__((always_inline)) {
+  // exponentials of the chunk's scores, both normalisers and O^T += V^T P^T
+  auto exp_pv = [&](const f32x16* s, const uint16_t* vt) __attribute__((always_inline)) {
     const float m_use = m_run == kNegInf ? 0.f : m_run;
-    uint32_t pk[2][8];
+    uint32_t pk[NB][8];
     float psum = 0.f, pesum = 0.f;
-    // keys 0-31 first: they feed the first eight PV MFMAs
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const f32x16& sv = kb == 0 ? s0 : s1;
+    for (int kb = 0; kb < NB; ++kb) {
 #pragma unroll
       for (int r = 0; r < 16; r += 4) {
-        const float p0 = exp2_fast(fmaf(sv[r], a.scale_log2, -m_use));
-        const float p1 = exp2_fast(fmaf(sv[r + 1], a.scale_log2, -m_use));
-        const float p2 = exp2_fast(fmaf(sv[r + 2], a.scale_log2, -m_use));
-        const float p3 = exp2_fast(fmaf(sv[r + 3], a.scale_log2, -m_use));
+        const float p0 = exp2_fast(fmaf(s[kb][r], a.scale_log2, -m_use));
+        const float p1 = exp2_fast(fmaf(s[kb][r + 1], a.scale_log2, -m_use));
+        const float p2 = exp2_fast(fmaf(s[kb][r + 2], a.scale_log2, -m_use));
+        const float p3 = exp2_fast(fmaf(s[kb][r + 3], a.scale_log2, -m_use));
         pk[kb][r / 2] = pack_bf16x2(p0, p1);
         pk[kb][r / 2 + 1] = pack_bf16x2(p2, p3);
         psum = bf16x2_sum_acc(pk[kb][r / 2], psum);
@@ -272,7 +295,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     l_run += psum;
     le_run += pesum;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < NKS; ++ks) {
       const int kb = ks >> 1, hb = ks & 1;
       const u32x4 pb = {pk[kb][hb * 4], pk[kb][hb * 4 + 1], pk[kb][hb * 4 + 2], pk[kb][hb * 4 + 3]};
 #pragma unroll
@@ -311,39 +334,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   // chunks compare key0 + (register's key offset) against a per-row limit; gathered
   // chunks read the key indices that issue_k stored.
   const int wrow_min = r0 + w * 32;
-  auto mask_chunk = [&](const int* kid, const Chunk& r, f32x16& s0, f32x16& s1) __attribute__((always_inline)) {
+  auto mask_chunk = [&](const int* kid, const Chunk& r, f32x16* s) __attribute__((always_inline)) {
     const int lim = a.causal ? row + delta : 0x7ffffffe;
     if (r.gathered) {
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int4 k0 = *reinterpret_cast<const int4*>(kid + q4 * 8 + hh * 4);
-        const int4 k1 = *reinterpret_cast<const int4*>(kid + 32 + q4 * 8 + hh * 4);
-        if (k0.x > lim) s0[q4 * 4 + 0] = kNegInf;
-        if (k0.y > lim) s0[q4 * 4 + 1] = kNegInf;
-        if (k0.z > lim) s0[q4 * 4 + 2] = kNegInf;
-        if (k0.w > lim) s0[q4 * 4 + 3] = kNegInf;
-        if (k1.x > lim) s1[q4 * 4 + 0] = kNegInf;
-        if (k1.y > lim) s1[q4 * 4 + 1] = kNegInf;
-        if (k1.z > lim) s1[q4 * 4 + 2] = kNegInf;
-        if (k1.w > lim) s1[q4 * 4 + 3] = kNegInf;
-      }
+      for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int4 k4 = *reinterpret_cast<const int4*>(kid + kb * 32 + q4 * 8 + hh * 4);
+          if (k4.x > lim) s[kb][q4 * 4 + 0] = kNegInf;
+          if (k4.y > lim) s[kb][q4 * 4 + 1] = kNegInf;
+          if (k4.z > lim) s[kb][q4 * 4 + 2] = kNegInf;
+          if (k4.w > lim) s[kb][q4 * 4 + 3] = kNegInf;
+        }
       return;
     }
-    const bool need = !r.full || (a.causal && r.key0 + 63 > wrow_min + delta);
+    const bool need = !r.full || (a.causal && r.key0 + CK - 1 > wrow_min + delta);
     if (!need) return;
     // key0 + kl is present and visible iff lo <= kl <= hi
     const int hi = min(lim, kv_len - 1) - r.key0;
     const int lo = -r.key0;
 #pragma unroll
-    for (int rg = 0; rg < 16; ++rg) {
-      const int kl = (rg >> 2) * 8 + hh * 4 + (rg & 3);
-      if (kl > hi || kl < lo) s0[rg] = kNegInf;
-      if (kl + 32 > hi || kl + 32 < lo) s1[rg] = kNegInf;
-    }
+    for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+      for (int rg = 0; rg < 16; ++rg) {
+        const int kl = kb * 32 + (rg >> 2) * 8 + hh * 4 + (rg & 3);
+        if (kl > hi || kl < lo) s[kb][rg] = kNegInf;
+      }
   };
 
   // ---- pipeline ----
-  f32x16 sc0 = {}, sc1 = {};
+  f32x16 sc[NB];
+#pragma unroll
+  for (int kb = 0; kb < NB; ++kb) sc[kb] = f32x16{};
   Chunk nxt;
   if (n_chunks > 0) {
     // the first chunks read their addresses from global memory, overlapping the staging
@@ -356,15 +379,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    sc0 = s_block(K0, 0);
-    sc1 = s_block(K0, 1);
-    mask_chunk(kid0, c0, sc0, sc1);
-    softmax_max(sc0, sc1, a.scale_log2, m_run, l_run, le_run, oacc);
+    s_chunk(K0, sc);
+    mask_chunk(kid0, c0, sc);
+    softmax_max_n<NB>(sc, a.scale_log2, m_run, l_run, le_run, oacc);
   }
 
-  // Chunk ci: S(ci) in (sc0, sc1); K stages kc / kn (this chunk / the next), V stages vc / vn.
-  // The other wave on the SIMD (from the second workgroup on the CU) fills this wave's
-  // LDS and MFMA waits, so S(ci+1) simply follows chunk ci's softmax and PV product.
+  // Chunk ci: S(ci) in sc; K stages kc / kn (this chunk / the next), V stages vc / vn.
   auto step = [&](int ci, uint16_t* kc, int* kidc, uint16_t* kn, const int* kidn, const uint16_t* vc, uint16_t* vn)
                   __attribute__((always_inline)) {
     // this wave's loads of the previous step (K(ci+1), V(ci)) are done; after the barrier
@@ -378,7 +398,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       issue_k(kc, kidc, nn, true);
     }
     if (has1) issue_v(vn, nxt, true);
-    exp_pv(sc0, sc1, vc);
+    exp_pv(sc, vc);
     if constexpr (KIND != 2) {
       if (a.partial && (ci % cpe) == cpe - 1) {
         const int e = ci / cpe;
@@ -386,10 +406,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       }
     }
     if (has1) {
-      sc0 = s_block(kn, 0);
-      sc1 = s_block(kn, 1);
-      mask_chunk(kidn, nxt, sc0, sc1);
-      softmax_max(sc0, sc1, a.scale_log2, m_run, l_run, le_run, oacc);
+      s_chunk(kn, sc);
+      mask_chunk(kidn, nxt, sc);
+      softmax_max_n<NB>(sc, a.scale_log2, m_run, l_run, le_run, oacc);
     }
     nxt = nn;
   };

@@ -60,11 +60,15 @@ __device__ __forceinline__ f32x16 st_block(const uint16_t* Ks, int krow0, const 
 //
 // Step 1: the chunk's row maximum, and the lazy rescale: the reference maximum only
 // moves (rescaling O and the sums) when the new maximum exceeds it by more than 2^8.
-__device__ __forceinline__ void softmax_max(const f32x16& s0, const f32x16& s1, float scale_log2, float& m_run,
-                                            float& l_run, float& le_run, f32x16* oacc) {
+// s holds NB blocks of 32 keys.
+template <int NB>
+__device__ __forceinline__ void softmax_max_n(const f32x16* s, float scale_log2, float& m_run, float& l_run,
+                                              float& le_run, f32x16* oacc) {
   float mx = kNegInf;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+  for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
   mx = fmaxf(mx, shfl_xor_f(mx, 32)) * scale_log2;
   const float m_new = fmaxf(m_run, mx);
   const bool need = m_new > m_run + kSlack;
@@ -76,6 +80,12 @@ __device__ __forceinline__ void softmax_max(const f32x16& s0, const f32x16& s1, 
 #pragma unroll
     for (int db = 0; db < TD / 32; ++db) oacc[db] *= alpha;
   }
+}
+
+__device__ __forceinline__ void softmax_max(const f32x16& s0, const f32x16& s1, float scale_log2, float& m_run,
+                                            float& l_run, float& le_run, f32x16* oacc) {
+  const f32x16 s[2] = {s0, s1};
+  softmax_max_n<2>(s, scale_log2, m_run, l_run, le_run, oacc);
 }
 
 // Step 2: weights, both normalisers, and O^T += V^T P^T.
