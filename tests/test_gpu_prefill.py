@@ -41,6 +41,7 @@ def _lists(seed, B, H, reach, cap):
     (1000, 1024, 4, 2, "kv", 128, 128),    # ragged query tail, bottom-right causal offset 24
     (512, 512, 4, 4, "q", 64, 64),         # 64-row tiles (two waves), 64-key blocks
     (384, 512, 4, 2, "q", 128, 64),        # 128-row tiles over 64-key blocks
+    (448, 512, 4, 2, "kv", 64, 128),       # 64-row tiles over 128-key blocks (four 32-key chunks each)
 ])
 def test_block_sparse_causal_small(Sq, Sk, Hq, Hkv, Ht, bM, bN):
     B, D = 2, 128
@@ -72,25 +73,28 @@ def test_dense_prefill(Sq, Sk, causal):
     check_lse(host(lse), lse_ref, "dense prefill lse")
 
 
-@pytest.mark.parametrize("E", [1, 3])
-def test_prefill_partials_recombine(E):
-    B, S, Hq, Hkv, D, bs = 1, 512, 4, 2, 128, 128
-    say("prefill partials E =", E)
+@pytest.mark.parametrize("E,bM,bN", [(1, 128, 128), (3, 128, 128), (2, 64, 128)])
+def test_prefill_partials_recombine(E, bM, bN):
+    B, S, Hq, Hkv, D = 1, 512, 4, 2, 128
+    say("prefill partials E =", E, bM, bN)
     q = normal_bf16(13, "q", (B, S, Hq, D))
     k = normal_bf16(13, "k", (B, S, Hkv, D))
     v = normal_bf16(13, "v", (B, S, Hkv, D))
-    count = np.array([[[1, 2, 3, 4]] * Hq], np.int32)
-    index = np.zeros((B, Hq, 4, 4), np.int32)
-    for i in range(4):
-        index[0, :, i, :i + 1] = np.arange(i + 1)[::-1]
-    pat = bsa.BlockPattern(dev_i32(count), dev_i32(index), bs, bs)
+    nqb, nkb = S // bM, S // bN
+    count = np.zeros((B, Hq, nqb), np.int32)
+    index = np.zeros((B, Hq, nqb, nkb), np.int32)
+    for i in range(nqb):
+        reach = ((i + 1) * bM - 1) // bN  # every block up to the diagonal, diagonal first
+        count[0, :, i] = reach + 1
+        index[0, :, i, :reach + 1] = np.arange(reach + 1)[::-1]
+    pat = bsa.BlockPattern(dev_i32(count), dev_i32(index), bM, bN)
     op, lp = bsa.bsa_fwd_partials(dev_bf16(q), dev_bf16(k), dev_bf16(v), pat, E, causal=True)
     if E == 1:
-        op_ref, lp_ref = oracle.block_sparse_partials(q, k, v, count, index, bs, bs, causal=True)
+        op_ref, lp_ref = oracle.block_sparse_partials(q, k, v, count, index, bM, bN, causal=True)
         check_o(host(op), op_ref, "partials")
         check_lse(host(lp), lp_ref, "partials lse")
     o, lse = bsa.bsa_combine(op, lp, out_dtype=torch.float32)
-    o_ref, lse_ref = oracle.block_sparse(q, k, v, count, index, bs, bs, causal=True)
+    o_ref, lse_ref = oracle.block_sparse(q, k, v, count, index, bM, bN, causal=True)
     check_o(host(o), o_ref, "recombined")
     check_lse(host(lse), lse_ref, "recombined lse")
 

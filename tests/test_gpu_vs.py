@@ -39,19 +39,23 @@ def test_convert_small_exact(seqlens, ctx):
     _check_items(gpu, w, [(b, h, m) for b in range(len(seqlens)) for h in range(3) for m in range(R)])
 
 
-def test_attention_small_varlen():
+@pytest.mark.parametrize("bm,bn", [(64, 64), (64, 128), (128, 128)])
+def test_attention_small_varlen(bm, bn):
+    """Both tile sizes of the prefill kernel (64-row tiles with 32-key chunks, 128-row tiles
+    with 64-key chunks) and windows spanning one or two chunks."""
     w = vs_varlen_prefill(seed=52, seqlens=(700, 300, 64), H=4, D=128, nnz_v=40, nnz_s=60, block=64,
-                          context_size=704)
-    say("vs attention small varlen")
-    bc, bo, cc, ci = _convert(w)
-    pat = bsa.VSPattern(bc, bo, cc, ci, 64, 64)
+                          context_size=768)
+    say("vs attention small varlen", bm, bn)
+    sl = dev_i32(w["seqlens"])
+    bc, bo, cc, ci = bsa.vs_convert_indexes(sl, sl, dev_i32(w["vertical"]), dev_i32(w["slash"]), 768, bm, bn)
+    pat = bsa.VSPattern(bc, bo, cc, ci, bm, bn)
     cu = dev_i32(w["cu_seqlens"])
     o, lse = bsa.bsa_fwd(dev_bf16(w["q"]), dev_bf16(w["k"]), dev_bf16(w["v"]), pat, causal=True,
                          out_dtype=torch.float32, cu_seqlens_q=cu, cu_seqlens_k=cu, max_seqlen_q=700,
                          max_seqlen_k=700)
-    rb, rbo, rcc, rci = oracle.vs_convert(w["seqlens"], w["seqlens"], w["vertical"], w["slash"], 704, 64, 64)
+    rb, rbo, rcc, rci = oracle.vs_convert(w["seqlens"], w["seqlens"], w["vertical"], w["slash"], 768, bm, bn)
     o_ref, lse_ref = oracle.vs_attention(w["q"], w["k"], w["v"], rb, rbo, rcc, rci, w["cu_seqlens"],
-                                         w["cu_seqlens"], 64, 64)
+                                         w["cu_seqlens"], bm, bn)
     check_o(host(o), o_ref, "vs attention")
     check_lse(host(lse), lse_ref, "vs attention lse")
 
