@@ -35,6 +35,8 @@ def _args():
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="time decode steps as eager launches instead of HIP graph replays")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 4 device-to-device copies of 1 GiB (reference for HBM byte counters)")
     return ap.parse_args()
@@ -85,6 +87,74 @@ def run_steps(torch, step, timer, steps, warmup):
     return (time.perf_counter() - t0) * 1e3 / steps
 
 
+# HBM bytes per decode launch on the speculative+sparse workload, from two rocprofv3
+# --pmc passes (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) each scaled by what the same
+# counter reads for a 1 GiB device copy (FETCH_SIZE reads half the bytes: x2.0; WRITE_SIZE
+# x1.0).  Valid only for the sources the counters were taken on: the digest covers the
+# kernel, its launch planning and the workload generator, and a mismatch reports null.
+DECODE_TRAFFIC = {"bytes": 1_282_797_568, "fetch_kib": 624_285, "write_kib": 4_162,
+                  "sha256": "679bd0a755e918ecd1b189a17621ca35329fc44fe656976c402323690d78fa34"}
+TRAFFIC_SOURCES = ["long_context_attention_sparse_amd/csrc/decode.cuh", "long_context_attention_sparse_amd/csrc/common.cuh",
+                   "long_context_attention_sparse_amd/csrc/args.cuh", "long_context_attention_sparse_amd/csrc/kernels_stream.hip",
+                   "long_context_attention_sparse_amd/csrc/bsa_api.hip", "synth/workloads.py"]
+
+
+def sources_digest():
+    import hashlib
+
+    h = hashlib.sha256()
+    root = os.path.dirname(os.path.abspath(__file__))
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(root, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def capture(torch, fn):
+    """Capture fn (library launches on torch's current stream) into a HIP graph; the
+    outputs fn writes are preallocated, so replays reuse the same buffers."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def run_graph_steps(torch, g, steps):
+    """Wall-clock ms per replay of g over exactly `steps` replays, synchronized on both sides."""
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def kernel_mean_ms(torch, fn, per_graph=10, replays=5):
+    """Mean device time of the launch fn makes: fn captured per_graph times back to back in
+    one HIP graph, HIP events around each replay (so graph launch overhead is amortised and
+    the figure compares with a profiler's per-dispatch duration)."""
+    g = capture(torch, lambda: [fn() for _ in range(per_graph)])
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    g.replay()
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(replays):
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b) / per_graph)
+    return float(np.mean(ms))
+
+
 def cpu_rate(fn, units, budget_s):
     """Run fn(unit) over units, BLAS limited to one thread, until the budget is spent;
     returns (units done, seconds)."""
@@ -130,17 +200,30 @@ def bench_spec_decode(torch, bsa, args):
             bsa.bsa_combine(o_part, lse_part, out=out, lse=lse)
 
     timer = Timer(torch)
-    ms = run_steps(torch, step, timer, args.steps, args.warmup)
+    eager_ms = run_steps(torch, step, timer, args.steps, args.warmup)
+    spans = {n: round(timer.mean_ms(n) * 1e3, 2) for n in timer.spans}
+    _log("eager per-launch us (host launch gaps included):", spans)
+
+    def passes():
+        bsa.bsa_speculative_partials(q, k_spec, v_spec, k, v, missed, o_part=o_part, lse_part=lse_part)
+
+    def full_step():
+        passes()
+        bsa.bsa_combine(o_part, lse_part, out=out, lse=lse)
+
+    if args.eager:
+        ms, pass_ms = eager_ms, timer.mean_ms("passes")
+    else:
+        # a decode step replays as one HIP graph (launch overhead off the critical path)
+        ms = run_graph_steps(torch, capture(torch, full_step), args.steps)
+        pass_ms = kernel_mean_ms(torch, passes)
     groups = B * Hkv
     blk_bytes = bs * D * 2 * 2
     kv_bytes = groups * (n_missed + (Sk - s0) // bs) * blk_bytes
     io_bytes = q.numel() * 2 + out.numel() * 2 + lse.numel() * 4 + index.numel() * 4 + count.numel() * 4
     step_bytes = kv_bytes + io_bytes
     pass_bytes = kv_bytes + q.numel() * 2 + index.numel() * 4 + count.numel() * 4
-    pass_ms = timer.mean_ms("passes")
     achieved = pass_bytes / (pass_ms * 1e-3) / 1e9
-    spans = {n: round(timer.mean_ms(n) * 1e3, 2) for n in timer.spans}
-    _log("per-launch us:", spans)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -167,9 +250,11 @@ def bench_spec_decode(torch, bsa, args):
         config={"workload": "speculative+sparse decode", "B": B, "Hq": Hq, "Hkv": Hkv, "D": D, "Sk": Sk,
                 "block": bs, "spec_tokens": Sk - s0, "missed_blocks_per_group": n_missed,
                 "partials": int(o_part.shape[0]), "algorithmic_bytes_per_step": step_bytes,
-                "launch_us": spans},
+                "timing": "eager" if args.eager else "hip graph replay", "eager_ms_per_step": round(eager_ms, 4),
+                "eager_launch_us": spans},
         roofline={"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                  "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                  "frac": round(achieved / HBM_PEAK_GBS, 4),
+                  "traffic": DECODE_TRAFFIC["bytes"] if DECODE_TRAFFIC["sha256"] == sources_digest() else None,
                   "kernel": "decode_kernel<128> (speculative and repair passes, one launch)",
                   "algorithmic_bytes": pass_bytes, "avg_ms": round(pass_ms, 5)},
         cpu_baseline=cpu)
@@ -205,15 +290,29 @@ def bench_tiny(torch, bsa, args):
             bsa.bsa_combine(o_part, lse_part, out=out)
 
     timer = Timer(torch)
-    ms = run_steps(torch, step, timer, args.steps, args.warmup)
+    eager_ms = run_steps(torch, step, timer, args.steps, args.warmup)
     spans = {n: round(timer.mean_ms(n) * 1e3, 2) for n in timer.spans}
+
+    def set_a():
+        bsa.bsa_fwd(q, k, v, pats["set_a"], out=o_part[0], lse=lse_part[0])
+
+    def full_step():
+        set_a()
+        bsa.bsa_fwd(q, k, v, pats["set_b"], out=o_part[1], lse=lse_part[1])
+        bsa.bsa_combine(o_part, lse_part, out=out)
+
+    if args.eager:
+        ms, a_ms = eager_ms, timer.mean_ms("set A")
+    else:
+        ms = run_graph_steps(torch, capture(torch, full_step), args.steps)
+        a_ms = kernel_mean_ms(torch, set_a)
     kv = B * H * 16 * 64 * w["D"] * 2 * 2
-    a_ms = timer.mean_ms("set A")
     a_bytes = B * H * 6 * 64 * w["D"] * 4
     return dict(metric=METRIC, value=round(ms, 4), unit="ms/call", higher_is_better=False, ms_per_step=round(ms, 4),
                 dtype="bf16",
                 config={"workload": "tiny sparse decode (A, B, combine)", "B": B, "H": H, "D": w["D"], "Sk": w["Sk"],
-                        "block": 64, "kv_bytes": kv, "launch_us": spans},
+                        "block": 64, "kv_bytes": kv, "timing": "eager" if args.eager else "hip graph replay",
+                        "eager_ms_per_step": round(eager_ms, 4), "eager_launch_us": spans},
                 roofline={"bound": "hbm", "achieved": round(a_bytes / (a_ms * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS,
                           "unit": "GB/s", "frac": round(a_bytes / (a_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 6),
                           "traffic": None, "kernel": "decode_kernel<64,1> (set A)"},

@@ -219,3 +219,48 @@ def test_fwd_partials_grouping_decode(E):
     o_ref, lse_ref = oracle.block_sparse(q, k, v, cnt, idx, 1, 64)
     check_o(host(o), o_ref, f"partials E={E}")
     check_lse(host(lse), lse_ref, f"partials E={E} lse")
+
+
+def test_graph_replay_matches_eager():
+    """The speculative passes and the combine captured in one HIP graph (as the benchmark
+    replays a decode step): every replay, with eager work and synchronizations in between,
+    equals the eager result bit for bit, and the eager result matches the oracle."""
+    w = _small_spec()
+    say("graph replay of a speculative decode step")
+    q, k, v = dev_bf16(w["q"]), dev_bf16(w["k"]), dev_bf16(w["v"])
+    s0 = w["spec_start"]
+    missed, cnt, idx = _pattern_kv(w["missed"], 64, w["Hkv"])
+    o_part, lse_part = bsa.bsa_speculative_partials(q, k[:, s0:], v[:, s0:], k, v, missed)
+    out = torch.empty((q.shape[0], 1, q.shape[2], q.shape[3]), dtype=torch.float32, device=q.device)
+    lse = torch.empty((q.shape[0], q.shape[2], 1), dtype=torch.float32, device=q.device)
+
+    def step():
+        bsa.bsa_speculative_partials(q, k[:, s0:], v[:, s0:], k, v, missed, o_part=o_part, lse_part=lse_part)
+        bsa.bsa_combine(o_part, lse_part, out=out, lse=lse)
+
+    step()
+    torch.cuda.synchronize()
+    o_eager, l_eager = out.clone(), lse.clone()
+    o_ref, lse_ref = oracle.speculative_sparse(w["q"], w["k"][:, s0:], w["v"][:, s0:], w["k"], w["v"], cnt, idx, 64,
+                                               causal_spec=True)
+    check_o(host(o_eager), o_ref, "eager step")
+    check_lse(host(l_eager), lse_ref, "eager step lse")
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    scratch = torch.zeros(1 << 20, device=q.device)
+    for r in range(4):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        scratch.add_(1.0)  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, o_eager) and torch.equal(lse, l_eager), f"replay {r}"
