@@ -274,6 +274,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 
   // exponentials of the chunk's scores, both normalisers and O^T += V^T P^T
   auto exp_pv = [&](const f32x16* s, const uint16_t* vt) __attribute__((always_inline)) {
+    // V^T operands of the first two 16-key steps are read before the exponentials, so their
+    // LDS latency hides behind the vector work; the rest are read between the MFMAs
+    constexpr int NPRE = NKS < 2 ? NKS : 2;
+    u32x4 vpre[NPRE][D / 32];
+#pragma unroll
+    for (int ks = 0; ks < NPRE; ++ks)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const u32x2 lo = ds_read_tr16(vt + ks * 16 * RS + voff[db]);
+        const u32x2 hi = ds_read_tr16(vt + (ks * 16 + 8) * RS + voff[db]);
+        vpre[ks][db] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      }
     const float m_use = m_run == kNegInf ? 0.f : m_run;
     uint32_t pk[NB][8];
     float psum = 0.f, pesum = 0.f;
@@ -300,9 +312,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       const u32x4 pb = {pk[kb][hb * 4], pk[kb][hb * 4 + 1], pk[kb][hb * 4 + 2], pk[kb][hb * 4 + 3]};
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        const u32x2 lo = ds_read_tr16(vt + ks * 16 * RS + voff[db]);
-        const u32x2 hi = ds_read_tr16(vt + (ks * 16 + 8) * RS + voff[db]);
-        const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
+        u32x4 av;
+        if (ks < NPRE) {
+          av = vpre[ks < NPRE ? ks : 0][db];
+        } else {
+          const u32x2 lo = ds_read_tr16(vt + ks * 16 * RS + voff[db]);
+          const u32x2 hi = ds_read_tr16(vt + (ks * 16 + 8) * RS + voff[db]);
+          av = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        }
         oacc[db] = mfma32x32x16(as_bf16x8(av), as_bf16x8(pb), oacc[db]);
       }
     }
