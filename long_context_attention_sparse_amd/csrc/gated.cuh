@@ -5,26 +5,32 @@
 // shuffle reduce, one LDS exchange between the four waves) and keeps the tile
 // iff j == i or scale * t(i,j) >= T[b, h, i].  Only kept tiles load V_j and
 // run the softmax update and P V product; a skipped tile's scores never enter
-// the softmax.  The next key tile is fetched into registers while the current
-// one is finished.
+// the softmax and its V is never requested.
 //
-// Workgroup: 4 waves x 32 query rows (BM = 128); K and V^T tiles of 128 keys
-// in LDS (70 KB, two workgroups per CU); same MFMA layouts as the prefill
-// kernel (tile.cuh).  Grid remapped XCD-aware, heaviest query blocks first.
+// Workgroup: 4 waves x 32 query rows (BM = 128), 128-key tiles.  K and V go
+// straight from global memory into LDS (global_load_lds_dwordx4, the swizzled
+// row layouts of tile.cuh; 32 KB each, two workgroups per CU); the V^T MFMA
+// operand is read with ds_read_b64_tr_b16.  Per tile:
+//   [K_j resident] S_ij (8 MFMAs per 32-key block), diagonal mask, tile max
+//   -> LDS exchange + barrier (every wave is done with K_j) -> keep decision
+//   -> kept tiles: issue V_j, wait, barrier, issue K_next, softmax + PV;
+//      skipped tiles: issue K_next -> wait for K_next -> barrier,
+// so the next K tile streams in during the PV product (kept tiles) or right
+// after the decision (skipped tiles).  (A workgroup-scope barrier waits for
+// every outstanding load, so K_next is issued after the V barrier, not
+// before it.)  Grid remapped XCD-aware, heaviest query blocks first.
 #pragma once
 #include "tile.cuh"
 
 namespace bsa {
 
-
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void gated_kernel(GatedArgs a) {
   constexpr int D = TD;
   constexpr int BN = 128;
-  constexpr int PIECES = D / 8;
-  constexpr int L = BN * PIECES / 256;  // 8 consecutive keys per thread per tile
-  constexpr int VSTR = BN + 8;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BN * TKS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VSTR];
+  constexpr int RS = D;  // packed 256-byte LDS rows, swizzled
+  constexpr int NB = BN / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t Kt[BN * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[BN * RS];
   __shared__ float red[4];
 
   const int item = xcd_item(wg_x(), a.n_items);
@@ -38,7 +44,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
   const int i = a.nqb - 1 - mrev;
 
   const int t = tid_x();
-  const int w = t >> 6, l = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63;
   const int lq = l & 31, hh = l >> 5;
 
   const uint16_t* qb = reinterpret_cast<const uint16_t*>(a.q.ptr) + (int64_t)b * a.q.sb + (int64_t)h * a.q.sh;
@@ -54,45 +60,70 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
   const float T = a.T[th];
   const int64_t mask_row = th * a.nqb;
 
-  // K: 16 lanes per 256-byte row; V: lanes run over the 32 4-key groups of the tile so
-  // the transposed LDS stores are conflict-free (two head-dim pieces per thread)
-  const int c = t % PIECES, kk = t / PIECES;
-  const int kv = t % 32, cv0 = t / 32;
-  u32x4 kr[L], vr[2][4];
-  auto load_k = [&](int key0) {
+  // Direct loads: wave w fills rows 32w..32w+31 of a tile with eight 1 KB instructions
+  // (rows 32w + 4x + l/16, lane l into slot l%16; R & 15 = 4(x & 3) + l/16).  Key tiles of a
+  // causal self-attention are always complete, so every row address is wave-uniform.
+  const int lrow = l >> 4, lslot = l & 15;
+  const uint32_t kx = (uint32_t)(lslot ^ lrow) << 4;
+  const uint32_t vx = (uint32_t)(lslot ^ (lrow << 2)) << 4;
+  const uint32_t k_lane = (uint32_t)(lrow * a.k.ss) * 2u, v_lane = (uint32_t)(lrow * a.v.ss) * 2u + vx;
+  auto issue_k = [&](int key0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int jj = 0; jj < L; ++jj) kr[jj] = ldg128(kbp + (int64_t)(key0 + kk * L + jj) * a.k.ss + c * 8);
+    for (int x = 0; x < 8; ++x) {
+      const char* p = reinterpret_cast<const char*>(kbp + (int64_t)(key0 + w * 32 + x * 4) * a.k.ss);
+      __builtin_amdgcn_global_load_lds(p + (k_lane + (kx ^ ((x & 3) << 6))), BSA_LDS(Kt + (w * 8 + x) * 4 * RS), 16,
+                                       0, 0);
+    }
   };
-  auto load_v = [&](int key0) {
+  auto issue_v = [&](int key0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-      for (int pp = 0; pp < 2; ++pp)
-        vr[pp][jj] = ldg128(vbp + (int64_t)(key0 + kv * 4 + jj) * a.v.ss + (cv0 + pp * 8) * 8);
+    for (int x = 0; x < 8; ++x) {
+      const char* p = reinterpret_cast<const char*>(vbp + (int64_t)(key0 + w * 32 + x * 4) * a.v.ss);
+      __builtin_amdgcn_global_load_lds(p + v_lane, BSA_LDS(Vt + (w * 8 + x) * 4 * RS), 16, 0, 0);
+    }
   };
-  auto tile_of = [&](int n) { return n == 0 ? i : n - 1; };  // diagonal first
+
+  // per-lane LDS offsets of the MFMA operands
+  int koff[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) koff[ks] = lq * RS + (((ks * 2 + hh) ^ k_swz(lq)) << 3);
+  const int tg = l >> 4, tr = l & 15;
+  const int vrow = (tg >> 1) * 4 + (tr >> 2);
+  int voff[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    const int col = db * 32 + (tg & 1) * 16 + (tr & 3) * 4;
+    voff[db] = vrow * RS + (((col >> 3) ^ v_swz(vrow)) << 3) + (col & 7);
+  }
 
   float m_run = kNegInf, l_run = 0.f, le_run = 0.f;
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int x = 0; x < D / 32; ++x) oacc[x] = f32x16{};
 
-  load_k(tile_of(0) * BN);
+  auto tile_of = [&](int n) { return n == 0 ? i : n - 1; };  // diagonal first
+
+  issue_k(tile_of(0) * BN);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
   for (int n = 0; n <= i; ++n) {
     const int j = tile_of(n);
-    __syncthreads();
+    f32x16 s[NB];
 #pragma unroll
-    for (int jj = 0; jj < L; ++jj) *reinterpret_cast<u32x4*>(Ks + (kk * L + jj) * TKS + c * 8) = kr[jj];
-    __syncthreads();
-
-    f32x16 s[4];
+    for (int kb = 0; kb < NB; ++kb) {
+      f32x16 acc = {};
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) s[kb] = st_block(Ks, kb * 32, qreg, lq, hh);
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const u32x4 av = *reinterpret_cast<const u32x4*>(Kt + kb * 32 * RS + koff[ks]);
+        acc = mfma32x32x16(as_bf16x8(av), qreg[ks], acc);
+      }
+      s[kb] = acc;
+    }
     const bool diag = j == i;
     if (diag) {
       const int rl = w * 32 + lq;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int kl = kb * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
@@ -101,12 +132,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
     }
     float mx = kNegInf;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, shfl_xor_f(mx, off));
     if (l == 0) red[w] = mx;
+    // every wave's maximum is in LDS and every wave is done reading K_j
     __syncthreads();
     const float tile_max = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])) * a.scale;
     const bool keep = diag || tile_max >= T;
@@ -114,16 +146,52 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
       if (a.keep) a.keep[mask_row + j] = keep ? 1 : 0;
       if (a.tmax) a.tmax[mask_row + j] = tile_max;
     }
+    const bool more = n < i;
     if (keep) {
-      load_v(j * BN);
-#pragma unroll
-      for (int pp = 0; pp < 2; ++pp) store_vt_group<VSTR>(Vt, vr[pp], kv * 4, cv0 + pp * 8);
-      if (n < i) load_k(tile_of(n + 1) * BN);
+      issue_v(j * BN);
+      __builtin_amdgcn_s_waitcnt(0);
+      // V_j from every wave is in LDS; K_next streams in during the softmax and PV product
       __syncthreads();
-      softmax_pv64<VSTR>(s[0], s[1], Vt, 0, a.scale_log2, m_run, l_run, le_run, oacc, lq, hh);
-      softmax_pv64<VSTR>(s[2], s[3], Vt, 64, a.scale_log2, m_run, l_run, le_run, oacc, lq, hh);
-    } else {
-      if (n < i) load_k(tile_of(n + 1) * BN);
+      if (more) issue_k(tile_of(n + 1) * BN);
+      softmax_max_n<NB>(s, a.scale_log2, m_run, l_run, le_run, oacc);
+      const float m_use = m_run == kNegInf ? 0.f : m_run;
+      float psum = 0.f, pesum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < NB; ++kb) {
+        uint32_t pk[8];
+#pragma unroll
+        for (int r = 0; r < 16; r += 4) {
+          const float p0 = exp2_fast(fmaf(s[kb][r], a.scale_log2, -m_use));
+          const float p1 = exp2_fast(fmaf(s[kb][r + 1], a.scale_log2, -m_use));
+          const float p2 = exp2_fast(fmaf(s[kb][r + 2], a.scale_log2, -m_use));
+          const float p3 = exp2_fast(fmaf(s[kb][r + 3], a.scale_log2, -m_use));
+          pk[r / 2] = pack_bf16x2(p0, p1);
+          pk[r / 2 + 1] = pack_bf16x2(p2, p3);
+          psum = bf16x2_sum_acc(pk[r / 2], psum);
+          psum = bf16x2_sum_acc(pk[r / 2 + 1], psum);
+          pesum += (p0 + p1) + (p2 + p3);
+        }
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          const int ks = kb * 2 + hb;
+          const u32x4 pb = {pk[hb * 4], pk[hb * 4 + 1], pk[hb * 4 + 2], pk[hb * 4 + 3]};
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            const u32x2 lo = ds_read_tr16(Vt + ks * 16 * RS + voff[db]);
+            const u32x2 hi = ds_read_tr16(Vt + (ks * 16 + 8) * RS + voff[db]);
+            oacc[db] = mfma32x32x16(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), as_bf16x8(pb), oacc[db]);
+          }
+        }
+      }
+      l_run += psum;
+      le_run += pesum;
+    } else if (more) {
+      issue_k(tile_of(n + 1) * BN);
+    }
+    if (more) {
+      // K_next is in LDS and every wave is done reading V_j
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
     }
   }
   const int64_t ob = (int64_t)b * a.o.sb + (int64_t)row * a.o.ss + (int64_t)h * a.o.sh;
