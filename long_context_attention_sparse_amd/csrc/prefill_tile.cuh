@@ -260,16 +260,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     const bool more = c + 1 < n_chunks;
     // V_c streams in while S_c is computed
     issue(Vt, vbp, a.v.ss, false, my_seg(cur), c > 0);
+    // S_c: the NB key blocks advance together through the head dimension, so each K
+    // operand read has the other blocks' MFMAs to hide behind
     f32x16 s[NB];
 #pragma unroll
-    for (int kb = 0; kb < NB; ++kb) {
-      f32x16 acc = {};
+    for (int kb = 0; kb < NB; ++kb) s[kb] = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const u32x4 av = *reinterpret_cast<const u32x4*>(Kt + kb * 32 * RS + koff[ks]);
-        acc = mfma32x32x16(as_bf16x8(av), qreg[ks], acc);
-      }
-      s[kb] = acc;
+    for (int ks = 0; ks < D / 16; ++ks) {
+      u32x4 av[NB];
+#pragma unroll
+      for (int kb = 0; kb < NB; ++kb) av[kb] = *reinterpret_cast<const u32x4*>(Kt + kb * 32 * RS + koff[ks]);
+#pragma unroll
+      for (int kb = 0; kb < NB; ++kb) s[kb] = mfma32x32x16(as_bf16x8(av[kb]), qreg[ks], s[kb]);
     }
 #pragma unroll
     for (int kb = 0; kb < NB; ++kb) mask_block(s[kb], kb, cur[kb >> 1]);
