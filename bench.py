@@ -370,7 +370,7 @@ def bench_block_prefill(torch, bsa, args):
                         "tile": 128, "visited_tiles": tiles, "flops": flops},
                 roofline={"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                           "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None,
-                          "kernel": "prefill_pipe_kernel<1,4>", "avg_ms": round(kms, 4)},
+                          "kernel": "prefill_tile_kernel<1,4>", "avg_ms": round(kms, 4)},
                 cpu_baseline=cpu)
 
 
@@ -474,7 +474,7 @@ def bench_vs(torch, bsa, args):
                         "H": 32, "D": 128, "block": 64, "nnz_v": 1000, "nnz_s": 2000, "flops": flops,
                         "convert_ms": round(cms, 4), "convert_output_bytes": conv_bytes},
                 roofline={"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                          "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None, "kernel": "prefill_pipe_kernel<2,2>",
+                          "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None, "kernel": "prefill_tile_kernel<2,2>",
                           "avg_ms": round(ams, 4)},
                 cpu_baseline=None)
 
