@@ -21,7 +21,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 namespace {
 
-constexpr int kTargetWorkgroups = 2048;  // decode split heuristic: ~8 resident workgroups per CU
 
 bool valid_dtype(int32_t d) { return d == BSA_BF16 || d == BSA_F32; }
 
@@ -151,9 +150,12 @@ int device_cus() {
   return cached[dev];
 }
 
-constexpr int kDecodeWgPerCu = 4;      // resident decode workgroups per CU (120 VGPRs, 36 KB LDS)
-constexpr int kDecodeRounds = 2;       // whole rounds of resident workgroups per launch
-constexpr int kMaxChunksPerSplit = 96; // more rounds when splits would get longer than this
+#ifndef BSA_DECODE_ROUNDS
+#define BSA_DECODE_ROUNDS 4
+#endif
+constexpr int kDecodeWgPerCu = 4;                  // resident decode workgroups per CU (124 VGPRs, 36 KB LDS)
+constexpr int kDecodeRounds = BSA_DECODE_ROUNDS;   // whole rounds of resident workgroups per launch
+constexpr int kMaxChunksPerSplit = 96;             // more rounds when splits would get longer than this
 
 // Split the segments of one decode launch: the splits of a group are a whole number of
 // rounds of resident workgroups (no quarter-full last round), shared between segments in
