@@ -129,8 +129,9 @@ size_t bsa_workspace_size(const bsa_problem* prob, const bsa_pattern* pat);
  *   q, k, v  bf16 inputs (layouts above); k/v may be strided views.
  *   pat      NULL or a pattern; BLOCK needs Sk % block_N == 0 and
  *            block_N in {64, 128}; block_M in {64, 128} (ignored when the
- *            query rows fit one block).  VS needs causal and varlen or
- *            fixed length, block_M <= block_N, both 64.
+ *            query rows fit one block).  VS: block_M <= block_N, each 64
+ *            or 128, fixed length or varlen; with causal == 0 every listed
+ *            key is attended ([SGL] Signature: causal defaults to False).
  *   o        output, bf16 or f32; lse float32 output (may be NULL).
  *   ws       device scratch of at least bsa_workspace_size() bytes (may be
  *            NULL when that is 0).  Overwritten; the caller keeps it alive

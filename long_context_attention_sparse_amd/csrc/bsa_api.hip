@@ -90,7 +90,6 @@ bsa_status check_pattern(const bsa_problem& p, const bsa_pattern* pat) {
     if (!p.cu_seqlens_q && p.Sk % pat->block_N) return BSA_ERR_INVALID_ARG;
   } else {
     if (!pat->col_count || !pat->col_index || pat->col_cap < 0) return BSA_ERR_INVALID_ARG;
-    if (!p.causal) return BSA_ERR_UNSUPPORTED;
     if (pat->block_M > pat->block_N) return BSA_ERR_UNSUPPORTED;
   }
   return BSA_OK;

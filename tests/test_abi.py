@@ -79,8 +79,8 @@ def test_pattern_errors(lib):
     assert _fwd(lib, _prob(), pat=pat) == bd.BSA_ERR_INVALID_ARG                  # list heads
     pat = bd._Pattern(1, 2, 128, 128, 4, 0, addr(cnt), addr(idx), None, None, 0, 0, 0)
     assert _fwd(lib, _prob(Sk=320), pat=pat) == bd.BSA_ERR_INVALID_ARG            # Sk % block_N
-    pat = bd._Pattern(2, 4, 64, 64, 4, 4, addr(cnt), addr(idx), addr(cnt), addr(idx), 0, 0, 0)
-    assert _fwd(lib, _prob(causal=0), pat=pat) == bd.BSA_ERR_UNSUPPORTED          # VS needs causal
+    pat = bd._Pattern(2, 4, 128, 64, 4, 4, addr(cnt), addr(idx), addr(cnt), addr(idx), 0, 0, 0)
+    assert _fwd(lib, _prob(causal=0), pat=pat) == bd.BSA_ERR_UNSUPPORTED          # VS block_M > block_N
     pat = bd._Pattern(9, 2, 64, 64, 4, 0, addr(cnt), addr(idx), None, None, 0, 0, 0)
     assert _fwd(lib, _prob(), pat=pat) == bd.BSA_ERR_INVALID_ARG                  # kind
 

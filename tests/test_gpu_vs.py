@@ -60,6 +60,30 @@ def test_attention_small_varlen(bm, bn):
     check_lse(host(lse), lse_ref, "vs attention lse")
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_attention_fixed_length_gqa(causal):
+    """Fixed-length (batch, seqlen, heads, dim) inputs as the pages' sparse_attn_func takes them,
+    GQA (two query heads per key/value head), with and without the causal mask; the metadata
+    comes from the causal conversion either way."""
+    B, S, H, Hkv = 2, 640, 4, 2
+    w = vs_varlen_prefill(seed=53, seqlens=(S, S), H=H, D=128, nnz_v=30, nnz_s=50, block=64, context_size=S)
+    say("vs attention fixed length, causal =", causal)
+    sl = dev_i32(w["seqlens"])
+    bc, bo, cc, ci = bsa.vs_convert_indexes(sl, sl, dev_i32(w["vertical"]), dev_i32(w["slash"]), S, 64, 64)
+    q4 = w["q"].reshape(B, S, H, 128)
+    k4 = w["k"].reshape(B, S, H, 128)[:, :, :Hkv]
+    v4 = w["v"].reshape(B, S, H, 128)[:, :, :Hkv]
+    o, lse = bsa.bsa_fwd(dev_bf16(q4), dev_bf16(k4), dev_bf16(v4), bsa.VSPattern(bc, bo, cc, ci, 64, 64),
+                         causal=causal, out_dtype=torch.float32)
+    rb, rbo, rcc, rci = oracle.vs_convert(w["seqlens"], w["seqlens"], w["vertical"], w["slash"], S, 64, 64)
+    o_ref, lse_ref = oracle.vs_attention(w["q"], k4.reshape(B * S, Hkv, 128), v4.reshape(B * S, Hkv, 128),
+                                         rb, rbo, rcc, rci, w["cu_seqlens"], w["cu_seqlens"], 64, 64,
+                                         causal=causal)
+    check_o(host(o).reshape(B * S, H, 128), o_ref, "vs fixed length")
+    # varlen LSE is [H, total]; fixed-length LSE is [B, H, S]
+    check_lse(host(lse).transpose(1, 0, 2).reshape(H, B * S), lse_ref, "vs fixed length lse")
+
+
 @pytest.fixture(scope="module")
 def cfg5():
     say("generating vertical-slash varlen workload (seqlens 65536 + 32768, H=32)")
