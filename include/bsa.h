@@ -256,6 +256,22 @@ bsa_status vs_convert_indexes(const int32_t* q_seqlens, const int32_t* kv_seqlen
                               int32_t* block_count, int32_t* block_offset, int32_t* column_count,
                               int32_t* column_index, bsa_stream stream);
 
+/* Vertical-slash conversion with per-head counts of valid indices.
+ * [SGL] Description (the merged-head variant takes per-head variable
+ * sparsity counts) and Signature.  As vs_convert_indexes, except that head h
+ * uses only the first vertical_count[h] entries of each vertical row and the
+ * first slash_count[h] entries of each slash row (counts are clamped to
+ * [0, nnz_v] and [0, nnz_s]; entries past a count are never read).
+ *   vertical_count, slash_count  device int32 [H], shared by every batch entry.
+ * Errors as for vs_convert_indexes; BSA_ERR_INVALID_ARG for NULL counts. */
+bsa_status vs_convert_indexes_mergehead(const int32_t* q_seqlens, const int32_t* kv_seqlens,
+                                        const int32_t* vertical, const int32_t* slash,
+                                        const int32_t* vertical_count, const int32_t* slash_count, int32_t B,
+                                        int32_t H, int32_t nnz_v, int32_t nnz_s, int32_t context_size,
+                                        int32_t block_M, int32_t block_N, int32_t causal, int32_t* block_count,
+                                        int32_t* block_offset, int32_t* column_count, int32_t* column_index,
+                                        bsa_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,7 +24,8 @@ BSA_PAT_DENSE, BSA_PAT_BLOCK, BSA_PAT_VS = 0, 1, 2
 
 EXPORTS = ("bsa_status_string", "bsa_workspace_size", "bsa_fwd", "bsa_fwd_partials", "bsa_num_partials",
            "bsa_speculative_sparse", "bsa_speculative_partials", "bsa_speculative_num_partials",
-           "bsa_speculative_workspace_size", "bsa_combine", "bsa_fwd_gated", "vs_convert_indexes")
+           "bsa_speculative_workspace_size", "bsa_combine", "bsa_fwd_gated", "vs_convert_indexes",
+           "vs_convert_indexes_mergehead")
 
 
 class BSAError(RuntimeError):
@@ -97,6 +98,9 @@ def load(path: str = LIB_PATH):
                                   ctypes.c_void_p, ctypes.c_void_p]
     lib.vs_convert_indexes.restype = ctypes.c_int
     lib.vs_convert_indexes.argtypes = ([ctypes.c_void_p] * 4 + [ctypes.c_int32] * 8 + [ctypes.c_void_p] * 5)
+    lib.vs_convert_indexes_mergehead.restype = ctypes.c_int
+    lib.vs_convert_indexes_mergehead.argtypes = ([ctypes.c_void_p] * 6 + [ctypes.c_int32] * 8 +
+                                                 [ctypes.c_void_p] * 5)
     _lib = lib
     return lib
 
@@ -328,24 +332,53 @@ def bsa_fwd_gated(q, k, v, T: torch.Tensor, *, block_M: int = 128, block_N: int 
     return out, lse, keep, tmax
 
 
+def _vs_outputs(vertical_indexes, slash_indexes, context_size, block_size_M):
+    B, H, nnz_v = vertical_indexes.shape
+    nnz_s = slash_indexes.shape[-1]
+    rows = (context_size + block_size_M - 1) // block_size_M
+    dev = vertical_indexes.device
+    return (torch.empty((B, H, rows), dtype=torch.int32, device=dev),
+            torch.empty((B, H, rows, nnz_s), dtype=torch.int32, device=dev),
+            torch.empty((B, H, rows), dtype=torch.int32, device=dev),
+            torch.empty((B, H, rows, nnz_v), dtype=torch.int32, device=dev))
+
+
 def vs_convert_indexes(q_seqlens, kv_seqlens, vertical_indexes, slash_indexes, context_size: int,
                        block_size_M: int = 64, block_size_N: int = 64, causal: bool = True, stream=None):
     """Vertical-slash conversion.  Returns (block_count, block_offset, column_count, column_index)."""
     lib = load()
     B, H, nnz_v = vertical_indexes.shape
     nnz_s = slash_indexes.shape[-1]
-    rows = (context_size + block_size_M - 1) // block_size_M
-    dev = vertical_indexes.device
-    bc = torch.empty((B, H, rows), dtype=torch.int32, device=dev)
-    bo = torch.empty((B, H, rows, nnz_s), dtype=torch.int32, device=dev)
-    cc = torch.empty((B, H, rows), dtype=torch.int32, device=dev)
-    ci = torch.empty((B, H, rows, nnz_v), dtype=torch.int32, device=dev)
+    bc, bo, cc, ci = _vs_outputs(vertical_indexes, slash_indexes, context_size, block_size_M)
     st = lib.vs_convert_indexes(_ptr(_i32(q_seqlens, "q_seqlens")), _ptr(_i32(kv_seqlens, "kv_seqlens")),
                                 _ptr(_i32(vertical_indexes, "vertical_indexes")),
                                 _ptr(_i32(slash_indexes, "slash_indexes")), B, H, nnz_v, nnz_s, int(context_size),
                                 int(block_size_M), int(block_size_N), int(bool(causal)), _ptr(bc), _ptr(bo),
                                 _ptr(cc), _ptr(ci), _stream(stream))
     _check("vs_convert_indexes", st)
+    return bc, bo, cc, ci
+
+
+def vs_convert_indexes_mergehead(q_seqlens, kv_seqlens, vertical_indexes, slash_indexes, vertical_indices_count,
+                                 slash_indices_count, context_size: int, block_size_M: int = 64,
+                                 block_size_N: int = 64, causal: bool = True, stream=None):
+    """Vertical-slash conversion with per-head counts (int32 [H]) of valid indices.
+    Returns (block_count, block_offset, column_count, column_index)."""
+    lib = load()
+    B, H, nnz_v = vertical_indexes.shape
+    nnz_s = slash_indexes.shape[-1]
+    vc = _i32(vertical_indices_count, "vertical_indices_count")
+    sc = _i32(slash_indices_count, "slash_indices_count")
+    if vc.numel() != H or sc.numel() != H:
+        raise ValueError("vertical_indices_count and slash_indices_count need one entry per head")
+    bc, bo, cc, ci = _vs_outputs(vertical_indexes, slash_indexes, context_size, block_size_M)
+    st = lib.vs_convert_indexes_mergehead(_ptr(_i32(q_seqlens, "q_seqlens")), _ptr(_i32(kv_seqlens, "kv_seqlens")),
+                                          _ptr(_i32(vertical_indexes, "vertical_indexes")),
+                                          _ptr(_i32(slash_indexes, "slash_indexes")), _ptr(vc), _ptr(sc), B, H,
+                                          nnz_v, nnz_s, int(context_size), int(block_size_M), int(block_size_N),
+                                          int(bool(causal)), _ptr(bc), _ptr(bo), _ptr(cc), _ptr(ci),
+                                          _stream(stream))
+    _check("vs_convert_indexes_mergehead", st)
     return bc, bo, cc, ci
 
 

@@ -98,6 +98,8 @@ struct VSConvArgs {
   const int32_t* kv_seqlens;
   const int32_t* vertical;  // [B, H, nnz_v]
   const int32_t* slash;     // [B, H, nnz_s]
+  const int32_t* v_count;   // [H] valid vertical indices per head, or null (all nnz_v)
+  const int32_t* s_count;   // [H] valid slash indices per head, or null (all nnz_s)
   int B, H, nnz_v, nnz_s, rows, BM, BN;
   int32_t* bc;              // [B, H, rows]
   int32_t* bo;              // [B, H, rows, nnz_s]

@@ -525,23 +525,45 @@ bsa_status bsa_fwd_gated(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, bs
   return launch_status();
 }
 
-bsa_status vs_convert_indexes(const int32_t* q_seqlens, const int32_t* kv_seqlens, const int32_t* vertical,
-                              const int32_t* slash, int32_t B, int32_t H, int32_t nnz_v, int32_t nnz_s,
-                              int32_t context_size, int32_t block_M, int32_t block_N, int32_t causal,
-                              int32_t* block_count, int32_t* block_offset, int32_t* column_count,
-                              int32_t* column_index, bsa_stream stream) {
+static bsa_status vs_convert_impl(const int32_t* q_seqlens, const int32_t* kv_seqlens, const int32_t* vertical,
+                                  const int32_t* slash, const int32_t* v_count, const int32_t* s_count, int32_t B,
+                                  int32_t H, int32_t nnz_v, int32_t nnz_s, int32_t context_size, int32_t block_M,
+                                  int32_t block_N, int32_t causal, int32_t* block_count, int32_t* block_offset,
+                                  int32_t* column_count, int32_t* column_index, bsa_stream stream) {
   if (!q_seqlens || !kv_seqlens || !block_count || !column_count) return BSA_ERR_INVALID_ARG;
   if (B <= 0 || H <= 0 || nnz_v < 0 || nnz_s < 0 || context_size <= 0 || block_M <= 0 || block_N <= 0)
     return BSA_ERR_INVALID_ARG;
   if ((nnz_v > 0 && (!vertical || !column_index)) || (nnz_s > 0 && (!slash || !block_offset)))
     return BSA_ERR_INVALID_ARG;
   if (!causal || block_M > block_N) return BSA_ERR_UNSUPPORTED;
-  VSConvArgs a{q_seqlens, kv_seqlens, vertical, slash, B, H, nnz_v, nnz_s, 0, block_M, block_N,
+  VSConvArgs a{q_seqlens, kv_seqlens, vertical, slash, v_count, s_count, B, H, nnz_v, nnz_s, 0, block_M, block_N,
                block_count, block_offset, column_count, column_index};
   a.rows = (context_size + block_M - 1) / block_M;
   const int lds_ints = nnz_s + nnz_v <= kVSConvLdsInts ? nnz_s + nnz_v : 0;
   launch_vs_convert(a, lds_ints * sizeof(int32_t), reinterpret_cast<hipStream_t>(stream));
   return launch_status();
+}
+
+bsa_status vs_convert_indexes(const int32_t* q_seqlens, const int32_t* kv_seqlens, const int32_t* vertical,
+                              const int32_t* slash, int32_t B, int32_t H, int32_t nnz_v, int32_t nnz_s,
+                              int32_t context_size, int32_t block_M, int32_t block_N, int32_t causal,
+                              int32_t* block_count, int32_t* block_offset, int32_t* column_count,
+                              int32_t* column_index, bsa_stream stream) {
+  return vs_convert_impl(q_seqlens, kv_seqlens, vertical, slash, nullptr, nullptr, B, H, nnz_v, nnz_s, context_size,
+                         block_M, block_N, causal, block_count, block_offset, column_count, column_index, stream);
+}
+
+bsa_status vs_convert_indexes_mergehead(const int32_t* q_seqlens, const int32_t* kv_seqlens,
+                                        const int32_t* vertical, const int32_t* slash,
+                                        const int32_t* vertical_count, const int32_t* slash_count, int32_t B,
+                                        int32_t H, int32_t nnz_v, int32_t nnz_s, int32_t context_size,
+                                        int32_t block_M, int32_t block_N, int32_t causal, int32_t* block_count,
+                                        int32_t* block_offset, int32_t* column_count, int32_t* column_index,
+                                        bsa_stream stream) {
+  if (!vertical_count || !slash_count) return BSA_ERR_INVALID_ARG;
+  return vs_convert_impl(q_seqlens, kv_seqlens, vertical, slash, vertical_count, slash_count, B, H, nnz_v, nnz_s,
+                         context_size, block_M, block_N, causal, block_count, block_offset, column_count,
+                         column_index, stream);
 }
 
 }  // extern "C"

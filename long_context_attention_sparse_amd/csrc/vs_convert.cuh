@@ -12,6 +12,10 @@
 // and nothing otherwise.  Vertical indices v <= r1-1+d, ascending, that no
 // window contains become columns.  Rows past the sequence get counts 0.
 //
+// The merged-head variant takes per-head counts of valid vertical and slash
+// indices (same page, Description): head h uses only the first count entries
+// of its rows.
+//
 // One thread per query block; a workgroup takes 64 consecutive query blocks
 // of one (b, h) and stages that head's slash and vertical lists in LDS.  The
 // vertical list is merged with the windows as they are produced (windows are
@@ -26,14 +30,17 @@ namespace bsa {
 __global__ __launch_bounds__(kVSConvThreads) void vs_convert_kernel(VSConvArgs a) {
   extern __shared__ int32_t lists[];
   const int bh = blockIdx.y;
-  const int b = bh / a.H;
+  const int b = bh / a.H, h = bh % a.H;
   const int m = blockIdx.x * kVSConvThreads + threadIdx.x;
   const int32_t* sl_g = a.slash + (int64_t)bh * a.nnz_s;
   const int32_t* vt_g = a.vertical + (int64_t)bh * a.nnz_v;
+  // per-head counts (the merged-head variant): only the first ns / nv entries are indices
+  const int ns = a.s_count ? min(max(a.s_count[h], 0), a.nnz_s) : a.nnz_s;
+  const int nv = a.v_count ? min(max(a.v_count[h], 0), a.nnz_v) : a.nnz_v;
   const bool staged = a.nnz_s + a.nnz_v <= kVSConvLdsInts;
   if (staged) {
-    for (int x = threadIdx.x; x < a.nnz_s; x += kVSConvThreads) lists[x] = sl_g[x];
-    for (int x = threadIdx.x; x < a.nnz_v; x += kVSConvThreads) lists[a.nnz_s + x] = vt_g[x];
+    for (int x = threadIdx.x; x < ns; x += kVSConvThreads) lists[x] = sl_g[x];
+    for (int x = threadIdx.x; x < nv; x += kVSConvThreads) lists[a.nnz_s + x] = vt_g[x];
   }
   __syncthreads();
   if (m >= a.rows) return;
@@ -58,7 +65,7 @@ __global__ __launch_bounds__(kVSConvThreads) void vs_convert_kernel(VSConvArgs a
   int nwin = 0, ncol = 0, vi = 0;
   int frontier = 0;            // valid once nwin > 0
   int prev_end = -0x7fffffff;  // end (exclusive) of the last window
-  for (int si = 0; si < a.nnz_s; ++si) {
+  for (int si = 0; si < ns; ++si) {
     const int s = sl[si];
     const int e = last_visible - s;
     if (e < 0) continue;
@@ -73,7 +80,7 @@ __global__ __launch_bounds__(kVSConvThreads) void vs_convert_kernel(VSConvArgs a
     }
     frontier = wstart + a.BN;
     // verticals left of this window: outside every window unless inside the previous one
-    while (vi < a.nnz_v) {
+    while (vi < nv) {
       const int v = vt[vi];
       if (v >= wstart || v > last_visible) break;
       if (v >= prev_end) co[ncol++] = v;
@@ -82,7 +89,7 @@ __global__ __launch_bounds__(kVSConvThreads) void vs_convert_kernel(VSConvArgs a
     bo[nwin++] = wstart;
     prev_end = frontier;
   }
-  while (vi < a.nnz_v) {
+  while (vi < nv) {
     const int v = vt[vi];
     if (v > last_visible) break;
     if (v >= prev_end) co[ncol++] = v;

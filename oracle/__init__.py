@@ -22,10 +22,10 @@ skipped tiles' softmax mass in the gated variant (excluded).
 from .core import (as_f64, attend_rows, block_mask, block_sparse, block_sparse_partials, causal_mask,
                    combine, dense, default_scale, speculative_sparse)
 from .gate import gated, gated_rows, tile_max_row
-from .vertical_slash import vs_attention, vs_attention_rows, vs_convert, vs_convert_item
+from .vertical_slash import vs_attention, vs_attention_rows, vs_convert, vs_convert_item, vs_convert_mergehead
 
 __all__ = [
     "as_f64", "attend_rows", "block_mask", "block_sparse", "block_sparse_partials", "causal_mask",
     "combine", "dense", "default_scale", "speculative_sparse", "gated", "gated_rows", "tile_max_row",
-    "vs_attention", "vs_attention_rows", "vs_convert", "vs_convert_item",
+    "vs_attention", "vs_attention_rows", "vs_convert", "vs_convert_item", "vs_convert_mergehead",
 ]

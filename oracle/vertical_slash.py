@@ -104,6 +104,36 @@ def vs_convert(q_seqlens, kv_seqlens, vertical, slash, context_size: int, block_
     return bc, bo, cc, ci
 
 
+def vs_convert_mergehead(q_seqlens, kv_seqlens, vertical, slash, vertical_count, slash_count, context_size: int,
+                         block_M: int, block_N: int):
+    """Merged-head conversion ("Implementation: Sgl project Sglang Sparse Flash Attention",
+    Description): per-head counts of valid indices.  Reading: vertical_count and slash_count
+    have shape (H,), are shared by every batch entry, and head h uses the first count entries of
+    its index rows (counts clamped to [0, NNZ]); the rest of the conversion is ``vs_convert``.
+    Output shapes are those of ``vs_convert``."""
+    vertical = np.asarray(vertical)
+    slash = np.asarray(slash)
+    B, H, nnz_v = vertical.shape
+    nnz_s = slash.shape[2]
+    R = (context_size + block_M - 1) // block_M
+    bc = np.zeros((B, H, R), np.int32)
+    bo = np.full((B, H, R, nnz_s), -1, np.int32)
+    cc = np.zeros((B, H, R), np.int32)
+    ci = np.full((B, H, R, nnz_v), -1, np.int32)
+    for h in range(H):
+        nv = min(max(int(vertical_count[h]), 0), nnz_v)
+        ns = min(max(int(slash_count[h]), 0), nnz_s)
+        for b in range(B):
+            for m in range(R):
+                w, c = vs_convert_item(int(q_seqlens[b]), int(kv_seqlens[b]), vertical[b, h, :nv],
+                                       slash[b, h, :ns], m, block_M, block_N)
+                bc[b, h, m] = len(w)
+                bo[b, h, m, :len(w)] = w
+                cc[b, h, m] = len(c)
+                ci[b, h, m, :len(c)] = c
+    return bc, bo, cc, ci
+
+
 def _key_set(kv_len: int, windows, columns, block_N: int) -> np.ndarray:
     keys = set()
     for w in windows:

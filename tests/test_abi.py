@@ -123,3 +123,8 @@ def test_gated_and_vs_convert_errors(lib):
     assert lib.vs_convert_indexes(x, x, x, x, 1, 1, 4, 4, 256, 128, 64, 1, x, x, x, x, None) == bd.BSA_ERR_UNSUPPORTED
     assert lib.vs_convert_indexes(None, x, x, x, 1, 1, 4, 4, 256, 64, 64, 1, x, x, x, x, None) == bd.BSA_ERR_INVALID_ARG
     assert lib.vs_convert_indexes(x, x, x, x, 0, 1, 4, 4, 256, 64, 64, 1, x, x, x, x, None) == bd.BSA_ERR_INVALID_ARG
+    mh = lib.vs_convert_indexes_mergehead
+    assert mh(x, x, x, x, None, x, 1, 1, 4, 4, 256, 64, 64, 1, x, x, x, x, None) == bd.BSA_ERR_INVALID_ARG
+    assert mh(x, x, x, x, x, None, 1, 1, 4, 4, 256, 64, 64, 1, x, x, x, x, None) == bd.BSA_ERR_INVALID_ARG
+    assert mh(x, x, x, x, x, x, 1, 1, 4, 4, 256, 64, 64, 0, x, x, x, x, None) == bd.BSA_ERR_UNSUPPORTED
+    assert mh(x, x, x, x, x, x, 0, 1, 4, 4, 256, 64, 64, 1, x, x, x, x, None) == bd.BSA_ERR_INVALID_ARG

@@ -39,6 +39,27 @@ def test_convert_small_exact(seqlens, ctx):
     _check_items(gpu, w, [(b, h, m) for b in range(len(seqlens)) for h in range(3) for m in range(R)])
 
 
+@pytest.mark.parametrize("bm,bn", [(64, 64), (64, 128)])
+def test_convert_mergehead_exact(bm, bn):
+    """Per-head counts: heads with a full count, an empty count, a count past NNZ (clamped) and
+    partial counts; bit-exact against the oracle on every query block."""
+    say("vs convert mergehead", bm, bn)
+    w = vs_varlen_prefill(seed=54, seqlens=(700, 300, 64), H=5, D=128, nnz_v=40, nnz_s=60, block=64,
+                          context_size=768)
+    vc = np.array([40, 0, 17, 99, 3], np.int32)
+    sc = np.array([0, 60, 25, 1, 70], np.int32)
+    sl = dev_i32(w["seqlens"])
+    gpu = bsa.vs_convert_indexes_mergehead(sl, sl, dev_i32(w["vertical"]), dev_i32(w["slash"]), dev_i32(vc),
+                                           dev_i32(sc), 768, bm, bn)
+    bc, bo, cc, ci = (x.cpu().numpy() for x in gpu)
+    rb, rbo, rcc, rci = oracle.vs_convert_mergehead(w["seqlens"], w["seqlens"], w["vertical"], w["slash"], vc, sc,
+                                                    768, bm, bn)
+    assert np.array_equal(bc, rb) and np.array_equal(cc, rcc)
+    for b, h, m in np.ndindex(*rb.shape):
+        assert np.array_equal(bo[b, h, m, :rb[b, h, m]], rbo[b, h, m, :rb[b, h, m]]), (b, h, m)
+        assert np.array_equal(ci[b, h, m, :rcc[b, h, m]], rci[b, h, m, :rcc[b, h, m]]), (b, h, m)
+
+
 @pytest.mark.parametrize("bm,bn", [(64, 64), (64, 128), (128, 128)])
 def test_attention_small_varlen(bm, bn):
     """Both tile sizes of the prefill kernel (64-row tiles with 32-key chunks, 128-row tiles

@@ -175,3 +175,37 @@ def test_power_law_generator():
     x = power_law_unique(g, 65536, 2000)
     assert x.size == 2000 and np.unique(x).size == 2000 and 0 in x and x.max() < 65536
     assert np.median(x) < 5000                    # heavy head: most mass near 0
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_mergehead_ignores_entries_past_the_counts(seed):
+    """Merged-head conversion: entries past a head's count must not matter.  Fill them with
+    values that would change the result if read (vertical 0..n-1, slash offset 0), and compare
+    with the plain conversion of rows whose tails hold inert values instead (a vertical index past
+    every key, a slash offset past every row: neither can reach a key)."""
+    g = rng(seed, "vs-mergehead")
+    w = vs_varlen_prefill(seed=40 + seed, seqlens=(190, 77), H=3, D=16, nnz_v=14, nnz_s=18, block=16,
+                          context_size=192)
+    B, H = 2, 3
+    vc = g.integers(0, 15, size=H).astype(np.int32)
+    sc = g.integers(0, 19, size=H).astype(np.int32)
+    vc[0], sc[1] = 14, 0  # a full count and an empty one
+    vert, slash = w["vertical"].copy(), w["slash"].copy()
+    inert_v, inert_s = vert.copy(), slash.copy()
+    for h in range(H):
+        vert[:, h, vc[h]:] = np.arange(14 - vc[h])
+        slash[:, h, sc[h]:] = 0
+        inert_v[:, h, vc[h]:] = 10_000
+        inert_s[:, h, sc[h]:] = 10_000
+    got = oracle.vs_convert_mergehead(w["seqlens"], w["seqlens"], vert, slash, vc, sc, 192, 16, 16)
+    want = oracle.vs_convert(w["seqlens"], w["seqlens"], inert_v, inert_s, 192, 16, 16)
+    for x, y in zip(got, want):
+        assert np.array_equal(x, y)
+    # the planted tails do change the plain conversion wherever a count is short
+    planted = oracle.vs_convert(w["seqlens"], w["seqlens"], vert, slash, 192, 16, 16)
+    assert not all(np.array_equal(x, y) for x, y in zip(planted, want))
+    # counts at least NNZ (clamped) give the plain conversion of the full rows
+    full = oracle.vs_convert_mergehead(w["seqlens"], w["seqlens"], w["vertical"], w["slash"],
+                                       np.full(H, 99, np.int32), np.full(H, 18, np.int32), 192, 16, 16)
+    for x, y in zip(full, oracle.vs_convert(w["seqlens"], w["seqlens"], w["vertical"], w["slash"], 192, 16, 16)):
+        assert np.array_equal(x, y)
