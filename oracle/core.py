@@ -14,6 +14,10 @@ Definitions followed:
   O_r = sum exp(s_k - m) v_k / l, LSE_r = m + ln l (natural log).
 * Default scale 1/sqrt(head_dim): "Sglang Sparse Flash Attention",
   I/O Contract (softmax_scale).
+* Softcap: same page, Signature and I/O Contract (softcap, 0.0 switches it
+  off).  The page gives no formula; reading: the usual logit soft-capping,
+  applied to the scaled score before the softmax,
+  s_k = softcap * tanh(scale * <q_r, k_k> / softcap).
 * Grouped-query heads: q has H heads, k/v have Hk heads (same pages, shapes);
   query head h reads key/value head floor(h / (H / Hk)).
 * Causal masking, where asked for, is bottom-right aligned: key c is visible
@@ -78,9 +82,11 @@ def block_mask(count: np.ndarray, index: np.ndarray, block_M: int, block_N: int,
     return mask
 
 
-def _attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, mask: np.ndarray, scale: float):
+def _attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, mask: np.ndarray, scale: float, softcap: float = 0.0):
     """Softmax attention of rows q [R, D] over keys k/v [Sk, D] restricted by mask [R, Sk]."""
     s = scale * (q @ k.T)
+    if softcap > 0.0:
+        s = softcap * np.tanh(s / softcap)
     s = np.where(mask, s, -np.inf)
     m = s.max(axis=1) if s.shape[1] else np.full(s.shape[0], -np.inf)
     empty = np.isneginf(m)
@@ -106,7 +112,7 @@ def _list_head(h: int, Hq: int, Hkv: int, Ht: int) -> int:
     raise ValueError("list heads must equal Hq or Hkv")
 
 
-def dense(q, k, v, causal: bool = False, scale: float | None = None):
+def dense(q, k, v, causal: bool = False, scale: float | None = None, softcap: float = 0.0):
     """Dense attention.  q [B,Sq,Hq,D], k/v [B,Sk,Hkv,D] -> (O [B,Sq,Hq,D], LSE [B,Hq,Sq])."""
     q, k, v = as_f64(q), as_f64(k), as_f64(v)
     B, Sq, Hq, D = q.shape
@@ -118,12 +124,12 @@ def dense(q, k, v, causal: bool = False, scale: float | None = None):
     for b in range(B):
         for h in range(Hq):
             hk = _kv_head(h, Hq, Hkv)
-            o[b, :, h], lse[b, h] = _attend(q[b, :, h], k[b, :, hk], v[b, :, hk], mask, scale)
+            o[b, :, h], lse[b, h] = _attend(q[b, :, h], k[b, :, hk], v[b, :, hk], mask, scale, softcap)
     return o, lse
 
 
 def block_sparse(q, k, v, count, index, block_M: int, block_N: int, causal: bool = False,
-                 scale: float | None = None):
+                 scale: float | None = None, softcap: float = 0.0):
     """Attention over per-(b, list head, query block) block lists.
 
     count [B, Ht, nQB], index [B, Ht, nQB, cap]; Ht is Hq (a list per query
@@ -144,12 +150,12 @@ def block_sparse(q, k, v, count, index, block_M: int, block_N: int, causal: bool
             mask = block_mask(count[b, ht], index[b, ht], block_M, block_N, Sq, Sk)
             if cm is not None:
                 mask &= cm
-            o[b, :, h], lse[b, h] = _attend(q[b, :, h], k[b, :, hk], v[b, :, hk], mask, scale)
+            o[b, :, h], lse[b, h] = _attend(q[b, :, h], k[b, :, hk], v[b, :, hk], mask, scale, softcap)
     return o, lse
 
 
 def block_sparse_partials(q, k, v, count, index, block_M: int, block_N: int, causal: bool = False,
-                          scale: float | None = None):
+                          scale: float | None = None, softcap: float = 0.0):
     """One (o, lse) per list entry.  Returns o_part [cap,B,Sq,Hq,D], lse_part [cap,B,Hq,Sq];
     entry e of a list with fewer than e+1 entries is (0, -inf)."""
     cap = index.shape[-1]
@@ -161,7 +167,8 @@ def block_sparse_partials(q, k, v, count, index, block_M: int, block_N: int, cau
         cnt_e = (count > e).astype(np.int32)
         idx_e = np.zeros(index.shape[:-1] + (1,), np.int32)
         idx_e[..., 0] = np.where(count > e, index[..., e], 0)
-        o_part[e], lse_part[e] = block_sparse(q, k, v, cnt_e, idx_e, block_M, block_N, causal, scale)
+        o_part[e], lse_part[e] = block_sparse(q, k, v, cnt_e, idx_e, block_M, block_N, causal, scale,
+                                                  softcap)
     return o_part, lse_part
 
 
@@ -183,16 +190,16 @@ def combine(o_part, lse_part):
 
 
 def speculative_sparse(q, k_spec, v_spec, k, v, missed_count, missed_index, block_size: int,
-                       causal_spec: bool = True, scale: float | None = None):
+                       causal_spec: bool = True, scale: float | None = None, softcap: float = 0.0):
     """Dense attention over (k_spec, v_spec), sparse attention over the missed blocks of
     (k, v) without a mask, then the combine of the two partials."""
-    o1, l1 = dense(q, k_spec, v_spec, causal=causal_spec, scale=scale)
+    o1, l1 = dense(q, k_spec, v_spec, causal=causal_spec, scale=scale, softcap=softcap)
     Sq = np.asarray(q).shape[1]
-    o2, l2 = block_sparse(q, k, v, missed_count, missed_index, max(Sq, 1), block_size, False, scale)
+    o2, l2 = block_sparse(q, k, v, missed_count, missed_index, max(Sq, 1), block_size, False, scale, softcap)
     return combine(np.stack([o1, o2]), np.stack([l1, l2]))
 
 
-def attend_rows(q_rows, k, v, key_sets, scale: float):
+def attend_rows(q_rows, k, v, key_sets, scale: float, softcap: float = 0.0):
     """Attention for individual rows: q_rows [R, D]; k/v [Sk, D] of the row's kv head;
     key_sets a list of R integer arrays.  For spot checks at full size."""
     q_rows, k, v = as_f64(q_rows), as_f64(k), as_f64(v)
@@ -204,5 +211,5 @@ def attend_rows(q_rows, k, v, key_sets, scale: float):
         if len(np.unique(ks)) != len(ks):
             raise ValueError("duplicate keys in a key set")
         mask = np.ones((1, ks.size), bool)
-        o[r], lse[r] = (x[0] for x in _attend(q_rows[r:r + 1], k[ks], v[ks], mask, scale))
+        o[r], lse[r] = (x[0] for x in _attend(q_rows[r:r + 1], k[ks], v[ks], mask, scale, softcap))
     return o, lse

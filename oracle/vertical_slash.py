@@ -143,7 +143,8 @@ def _key_set(kv_len: int, windows, columns, block_N: int) -> np.ndarray:
 
 
 def vs_attention(q, k, v, block_count, block_offset, column_count, column_index, cu_seqlens_q, cu_seqlens_k,
-                 block_M: int, block_N: int, causal: bool = True, scale: float | None = None):
+                 block_M: int, block_N: int, causal: bool = True, scale: float | None = None,
+                 softcap: float = 0.0):
     """Varlen attention over converted metadata (small inputs).
 
     q [total_q, H, D], k/v [total_k, Hk, D].  Returns O [total_q, H, D] and LSE [H, total_q].
@@ -169,14 +170,15 @@ def vs_attention(q, k, v, block_count, block_offset, column_count, column_index,
                 mask = np.ones((rows.size, keys.size), bool)
                 if causal:
                     mask &= keys[None, :] <= rows[:, None] + d
-                oo, ll = _attend(q64[q0 + rows, h], k64[k0 + keys, hk], v64[k0 + keys, hk], mask, scale)
+                oo, ll = _attend(q64[q0 + rows, h], k64[k0 + keys, hk], v64[k0 + keys, hk], mask, scale,
+                                 softcap)
                 o[q0 + rows, h] = oo
                 lse[h, q0 + rows] = ll
     return o, lse
 
 
 def vs_attention_rows(q, k, v, b: int, h: int, rows, windows, columns, cu_seqlens_q, cu_seqlens_k,
-                      block_N: int, causal: bool = True, scale: float | None = None):
+                      block_N: int, causal: bool = True, scale: float | None = None, softcap: float = 0.0):
     """Attention for selected rows (local positions within sequence b) of one query block
     whose metadata (windows, columns) is given.  For full-size spot checks."""
     q0, q1 = int(cu_seqlens_q[b]), int(cu_seqlens_q[b + 1])
@@ -193,4 +195,4 @@ def vs_attention_rows(q, k, v, b: int, h: int, rows, windows, columns, cu_seqlen
     if causal:
         mask &= keys[None, :] <= rows[:, None] + d
     return _attend(as_f64(np.asarray(q)[q0 + rows, h]), as_f64(np.asarray(k)[k0 + keys, hk]),
-                   as_f64(np.asarray(v)[k0 + keys, hk]), mask, scale)
+                   as_f64(np.asarray(v)[k0 + keys, hk]), mask, scale, softcap)

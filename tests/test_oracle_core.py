@@ -238,3 +238,37 @@ def test_speculative_two_pass_equals_union():
     ou, lu = oracle.block_sparse(q, k, v, np.full((B, Hkv, 1), 9, np.int32), union.astype(np.int32), 1, bs)
     np.testing.assert_allclose(o, ou, atol=1e-12)
     np.testing.assert_allclose(lse, lu, atol=1e-12)
+
+
+def test_softcap_huge_cap_is_plain_attention():
+    """tanh(x / c) * c -> x as c grows: a cap of 1e9 must reproduce plain attention (torch SDPA)."""
+    q, k, v = (bf16_to_f64(normal_bf16(60, t, s)) for t, s in [("q", (2, 33, 4, 64)), ("k", (2, 47, 2, 64)),
+                                                                  ("v", (2, 47, 2, 64))])
+    o, lse = oracle.dense(q, k, v, causal=True, softcap=1e9)
+    np.testing.assert_allclose(o, _sdpa(q, k, v, causal=False, mask=np.tril(np.ones((33, 47), bool), 14)),
+                               atol=1e-12)
+    o0, lse0 = oracle.dense(q, k, v, causal=True)
+    np.testing.assert_allclose(lse, lse0, atol=1e-12)
+
+
+@pytest.mark.parametrize("scale", [0.7, 1.0 / 8.0])
+def test_softcap_closed_form(scale):
+    """Scores chosen through atanh so that the capped scores are known exactly: with cap c, a
+    scaled score of c*atanh(1/2) becomes c/2, a score of 0 stays 0, and a very negative score
+    saturates at -c.  Four keys, causal (bottom-right, Sq = Sk), so row 0 sees only key 0: a
+    mask applied before the cap (tanh(-inf) = -1) would leak the other keys into it."""
+    c = 3.0
+    a = c * math.atanh(0.5) / scale
+    q = np.zeros((1, 4, 1, 2))
+    q[0, :, 0, 0] = a
+    k = np.zeros((1, 4, 1, 2))
+    k[0, :, 0, 0] = [1.0, 0.0, -1000.0, 0.0]
+    v = np.zeros((1, 4, 1, 2))
+    v[0, :, 0] = [[1.0, 0.0], [0.0, 1.0], [2.0, -2.0], [0.5, 0.25]]
+    o, lse = oracle.dense(q, k, v, causal=True, scale=scale, softcap=c)
+    capped = np.array([c / 2, 0.0, -c, 0.0])
+    for r in range(4):
+        w = np.exp(capped[:r + 1])
+        np.testing.assert_allclose(o[0, r, 0], (w[:, None] * v[0, :r + 1, 0]).sum(0) / w.sum(), atol=1e-14)
+        assert abs(lse[0, 0, r] - math.log(w.sum())) < 1e-14
+    assert abs(lse[0, 0, 0] - c / 2) < 1e-14 and np.allclose(o[0, 0, 0], [1.0, 0.0], atol=1e-15)
