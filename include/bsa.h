@@ -70,7 +70,12 @@ typedef struct {
 
 /* Problem shape.  cu_seqlens_q/k are device int32 arrays of B+1 prefix sums
  * (NULL for fixed length); max_seqlen_q/k bound the per-sequence lengths
- * and must be given for varlen.  softmax_scale <= 0 selects 1/sqrt(D). */
+ * and must be given for varlen.  softmax_scale <= 0 selects 1/sqrt(D).
+ * softcap ([SGL] Signature and I/O Contract; 0 = off): when c > 0 every
+ * scaled score x = scale * <q, k> becomes c * tanh(x / c) before masking and
+ * the softmax (the usual logit soft-capping; the page gives no formula).
+ * Negative, NaN or infinite softcap: BSA_ERR_INVALID_ARG; bsa_fwd_gated
+ * rejects softcap > 0 with BSA_ERR_UNSUPPORTED. */
 typedef struct {
   int32_t B, Hq, Hkv, Sq, Sk, D;
   const int32_t* cu_seqlens_q;
@@ -78,6 +83,7 @@ typedef struct {
   int32_t max_seqlen_q, max_seqlen_k;
   float softmax_scale;
   int32_t causal;
+  float softcap;
 } bsa_problem;
 
 typedef enum {

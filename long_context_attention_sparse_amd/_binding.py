@@ -43,7 +43,8 @@ class _Problem(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("Sq", ctypes.c_int32),
                 ("Sk", ctypes.c_int32), ("D", ctypes.c_int32), ("cu_seqlens_q", ctypes.c_void_p),
                 ("cu_seqlens_k", ctypes.c_void_p), ("max_seqlen_q", ctypes.c_int32),
-                ("max_seqlen_k", ctypes.c_int32), ("softmax_scale", ctypes.c_float), ("causal", ctypes.c_int32)]
+                ("max_seqlen_k", ctypes.c_int32), ("softmax_scale", ctypes.c_float), ("causal", ctypes.c_int32),
+                ("softcap", ctypes.c_float)]
 
 
 class _Pattern(ctypes.Structure):
@@ -202,17 +203,20 @@ class VSPattern:
                         self.column_count.data_ptr(), self.column_index.data_ptr(), H * R, R, 1)
 
 
-def _problem(q, k, causal, softmax_scale, cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=0, max_seqlen_k=0):
+def _problem(q, k, causal, softmax_scale, cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=0, max_seqlen_k=0,
+             softcap=0.0):
     if cu_seqlens_q is not None:
         B = cu_seqlens_q.numel() - 1
         _, Hq, D = q.shape
         Hkv = k.shape[1]
         return _Problem(B, Hq, Hkv, int(max_seqlen_q), int(max_seqlen_k), D,
                         _i32(cu_seqlens_q, "cu_seqlens_q").data_ptr(), _i32(cu_seqlens_k, "cu_seqlens_k").data_ptr(),
-                        int(max_seqlen_q), int(max_seqlen_k), float(softmax_scale or 0.0), int(bool(causal)))
+                        int(max_seqlen_q), int(max_seqlen_k), float(softmax_scale or 0.0), int(bool(causal)),
+                        float(softcap or 0.0))
     B, Sq, Hq, D = q.shape
     Sk, Hkv = k.shape[1], k.shape[2]
-    return _Problem(B, Hq, Hkv, Sq, Sk, D, None, None, 0, 0, float(softmax_scale or 0.0), int(bool(causal)))
+    return _Problem(B, Hq, Hkv, Sq, Sk, D, None, None, 0, 0, float(softmax_scale or 0.0), int(bool(causal)),
+                    float(softcap or 0.0))
 
 
 def bsa_workspace_size(q, k, pattern=None, causal=False, **varlen) -> int:
@@ -225,16 +229,17 @@ def bsa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pattern=None, *, 
             softmax_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
             out_dtype: torch.dtype = torch.bfloat16, lse: Optional[torch.Tensor] = None,
             workspace: Optional[torch.Tensor] = None, cu_seqlens_q=None, cu_seqlens_k=None,
-            max_seqlen_q: int = 0, max_seqlen_k: int = 0, stream=None):
+            max_seqlen_q: int = 0, max_seqlen_k: int = 0, softcap: float = 0.0, stream=None):
     """Attention over a key pattern (None = dense).  Returns (out, lse).
 
     q [B, Sq, Hq, D], k/v [B, Sk, Hkv, D] bf16 (or varlen [total, H, D] with
     cu_seqlens).  out defaults to a new ``out_dtype`` tensor shaped like q;
-    lse is float32 [B, Hq, Sq] (varlen: [Hq, total_q]).
+    lse is float32 [B, Hq, Sq] (varlen: [Hq, total_q]).  softcap > 0 caps every scaled score x
+    at softcap * tanh(x / softcap).
     """
     lib = load()
     varlen = cu_seqlens_q is not None
-    prob = _problem(q, k, causal, softmax_scale, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
+    prob = _problem(q, k, causal, softmax_scale, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, softcap)
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
     if lse is None:
@@ -264,13 +269,13 @@ def bsa_num_partials(q, k, pattern=None, entries_per_partial: int = 1, causal: b
 
 def bsa_fwd_partials(q, k, v, pattern=None, entries_per_partial: int = 1, *, causal: bool = False,
                      softmax_scale=None, o_part: Optional[torch.Tensor] = None,
-                     lse_part: Optional[torch.Tensor] = None, stream=None):
+                     lse_part: Optional[torch.Tensor] = None, softcap: float = 0.0, stream=None):
     """(o, lse) partials over groups of ``entries_per_partial`` pattern entries (1 = one per
     list entry; a dense pattern's entries are 64-key blocks).  Returns
     o_part [P, B, Sq, Hq, D] and lse_part [P, B, Hq, Sq] (float32); given buffers (views into a
     larger partial buffer, for instance) are filled in place."""
     lib = load()
-    prob = _problem(q, k, causal, softmax_scale)
+    prob = _problem(q, k, causal, softmax_scale, softcap=softcap)
     pat = pattern.struct(prob.Hq) if pattern is not None else None
     pat_p = ctypes.byref(pat) if pat is not None else None
     P = int(lib.bsa_num_partials(ctypes.byref(prob), pat_p, int(entries_per_partial)))
@@ -384,11 +389,11 @@ def vs_convert_indexes_mergehead(q_seqlens, kv_seqlens, vertical_indexes, slash_
 
 def bsa_speculative_partials(q, k_spec, v_spec, k, v, missed: BlockPattern, *, causal_spec: bool = True,
                              softmax_scale=None, o_part: Optional[torch.Tensor] = None,
-                             lse_part: Optional[torch.Tensor] = None, stream=None):
+                             lse_part: Optional[torch.Tensor] = None, softcap: float = 0.0, stream=None):
     """Partials of both passes of speculative + sparse decoding (one launch on the decode path).
     Returns o_part [P, B, Sq, Hq, D], lse_part [P, B, Hq, Sq] (float32)."""
     lib = load()
-    prob = _problem(q, k, False, softmax_scale)
+    prob = _problem(q, k, False, softmax_scale, softcap=softcap)
     pat = missed.struct(prob.Hq)
     Sk_spec = k_spec.shape[1]
     P = int(lib.bsa_speculative_num_partials(ctypes.byref(prob), Sk_spec, ctypes.byref(pat)))
@@ -410,13 +415,13 @@ def bsa_speculative_partials(q, k_spec, v_spec, k, v, missed: BlockPattern, *, c
 
 def speculative_sparse(q, k_spec, v_spec, k, v, missed: BlockPattern, *, causal_spec: bool = True,
                        softmax_scale=None, out_dtype: torch.dtype = torch.bfloat16, out=None, lse=None,
-                       workspace=None, stream=None):
+                       workspace=None, softcap: float = 0.0, stream=None):
     """Speculative + sparse decoding with exact combine ("Sparse FlashAttention with
     Incremental Repair", Usage 2): attention over (k_spec, v_spec) with the causal flag
     (the speculative pass), attention over the missed blocks of (k, v) without a mask (the
     repair pass), and the log-sum-exp combine.  Returns (out, lse)."""
     lib = load()
-    prob = _problem(q, k, False, softmax_scale)
+    prob = _problem(q, k, False, softmax_scale, softcap=softcap)
     pat = missed.struct(prob.Hq)
     Sk_spec = k_spec.shape[1]
     B, Sq, Hq, D = q.shape

@@ -52,6 +52,7 @@ struct DecodeArgs {
   int B, Hq, Hkv, Sq, G, Gp, R;
   int direct;
   float scale_log2;  // softmax_scale * log2(e)
+  float cap_in, cap_out;  // softcap constants (softcap_score); cap_in == 0: no softcap
 };
 
 struct PrefillArgs {
@@ -66,6 +67,7 @@ struct PrefillArgs {
   int list_by_kv;             // lists indexed by kv head (1) or query head (0)
   int causal;
   float scale_log2;
+  float cap_in, cap_out;      // softcap constants (softcap_score); cap_in == 0: no softcap
   int n_items;
   int partial;                // 1: partials of epp entries each into part_o / part_lse
   int epp, n_part;

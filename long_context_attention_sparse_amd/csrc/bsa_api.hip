@@ -28,6 +28,16 @@ float scale_of(const bsa_problem& p) {
   return p.softmax_scale > 0.f ? p.softmax_scale : 1.0f / std::sqrt((float)p.D);
 }
 
+// softcap_score constants: cap_in = 2 scale log2(e) / c, cap_out = c / scale; (0, 0) when off.
+void cap_consts(const bsa_problem& p, float& cap_in, float& cap_out) {
+  cap_in = cap_out = 0.f;
+  if (p.softcap > 0.f) {
+    const float t = scale_of(p);
+    cap_in = 2.f * t * kLog2e / p.softcap;
+    cap_out = p.softcap / t;
+  }
+}
+
 TensorArg targ(const bsa_tensor& t) { return TensorArg{t.ptr, t.stride_b, t.stride_s, t.stride_h}; }
 OutArg oarg(const bsa_tensor& t) { return OutArg{t.ptr, t.stride_b, t.stride_s, t.stride_h, t.dtype == BSA_F32}; }
 
@@ -69,6 +79,7 @@ bsa_status check_problem(const bsa_problem* prob, const bsa_tensor& q, const bsa
   if (p.Hq % p.Hkv) return BSA_ERR_INVALID_ARG;
   if ((p.cu_seqlens_q == nullptr) != (p.cu_seqlens_k == nullptr)) return BSA_ERR_INVALID_ARG;
   if (p.cu_seqlens_q && (p.max_seqlen_q <= 0 || p.max_seqlen_k <= 0)) return BSA_ERR_INVALID_ARG;
+  if (!(p.softcap >= 0.f) || std::isinf(p.softcap)) return BSA_ERR_INVALID_ARG;
   if (!q.ptr || !k.ptr || !v.ptr || !o.ptr) return BSA_ERR_INVALID_ARG;
   if (q.dtype != BSA_BF16 || k.dtype != BSA_BF16 || v.dtype != BSA_BF16) return BSA_ERR_UNSUPPORTED;
   if (!valid_dtype(o.dtype)) return BSA_ERR_INVALID_ARG;
@@ -223,6 +234,7 @@ bsa_status run_decode(const bsa_problem& p, const DecodePlan& d, const bsa_tenso
   a.Gp = d.Gp;
   a.R = d.R;
   a.scale_log2 = scale_of(p) * kLog2e;
+  cap_consts(p, a.cap_in, a.cap_out);
   if (o) {
     a.direct = 1;
     a.o = oarg(*o);
@@ -273,6 +285,7 @@ bsa_status run_prefill(const bsa_problem& p, const bsa_tensor& q, const bsa_tens
   a.list_by_kv = pat && kind != BSA_PAT_DENSE && pat->Ht == p.Hkv && p.Hkv != p.Hq;
   a.causal = p.causal != 0;
   a.scale_log2 = scale_of(p) * kLog2e;
+  cap_consts(p, a.cap_in, a.cap_out);
   const int64_t items = (int64_t)p.B * p.Hq * a.nqb;
   if (items > INT_MAX) return BSA_ERR_UNSUPPORTED;
   a.n_items = (int)items;
@@ -501,6 +514,7 @@ bsa_status bsa_fwd_gated(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, bs
   if (!T) return BSA_ERR_INVALID_ARG;
   if (block_M != 128 || block_N != 128 || p.D != 128) return BSA_ERR_UNSUPPORTED;
   if (!p.causal || p.cu_seqlens_q || p.Sq != p.Sk || p.Sq % 128) return BSA_ERR_UNSUPPORTED;
+  if (p.softcap > 0.f) return BSA_ERR_UNSUPPORTED;
   GatedArgs a{};
   a.q = targ(q);
   a.k = targ(k);

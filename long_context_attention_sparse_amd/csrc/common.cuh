@@ -33,6 +33,18 @@ constexpr float kNegInf = -__builtin_inff();
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Logit soft-capping ("Implementation: Sgl project Sglang Sparse Flash Attention",
+// Signature: softcap, 0 = off), applied to the raw score s = <q, k> so that the
+// softmax scale still multiplies it afterwards: with cap c and scale t,
+//   s <- (c / t) tanh(t s / c) = cap_out (1 - 2 / (2^(cap_in s) + 1)),
+// cap_in = 2 t log2(e) / c, cap_out = c / t.  2^x overflowing to +inf gives
+// cap_out, underflowing to 0 gives -cap_out; near 0 the absolute error is a few
+// float32 ulps of cap_out.
+__device__ __forceinline__ float softcap_score(float s, float cap_in, float cap_out) {
+  const float e = exp2_fast(s * cap_in);
+  return fmaf(-2.f * cap_out, __builtin_amdgcn_rcpf(e + 1.f), cap_out);
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }

@@ -167,6 +167,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
       const u32x4 kv = *reinterpret_cast<const u32x4*>(Ks + (w * 16 + lr) * KS + ks * 32 + kg * 8);
       s = mfma16x16x32(as_bf16x8(kv), qreg[ks], s);
     }
+    if (a.cap_in != 0.f) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s[r] = softcap_score(s[r], a.cap_in, a.cap_out);
+    }
     float sc[4];
     float cmax = kNegInf;
 #pragma unroll

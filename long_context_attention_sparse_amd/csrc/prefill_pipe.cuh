@@ -397,6 +397,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     s_chunk(K0, sc);
+    softcap_n<NB>(sc, a.cap_in, a.cap_out);
     mask_chunk(kid0, c0, sc);
     softmax_max_n<NB>(sc, a.scale_log2, m_run, l_run, le_run, oacc);
   }
@@ -424,6 +425,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     }
     if (has1) {
       s_chunk(kn, sc);
+      softcap_n<NB>(sc, a.cap_in, a.cap_out);
       mask_chunk(kidn, nxt, sc);
       softmax_max_n<NB>(sc, a.scale_log2, m_run, l_run, le_run, oacc);
     }

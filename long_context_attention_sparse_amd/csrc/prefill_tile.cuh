@@ -273,6 +273,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
       for (int kb = 0; kb < NB; ++kb) s[kb] = mfma32x32x16(as_bf16x8(av[kb]), qreg[ks], s[kb]);
     }
+    softcap_n<NB>(s, a.cap_in, a.cap_out);
 #pragma unroll
     for (int kb = 0; kb < NB; ++kb) mask_block(s[kb], kb, cur[kb >> 1]);
     softmax_max_n<NB>(s, a.scale_log2, m_run, l_run, le_run, oacc);

@@ -61,6 +61,16 @@ __device__ __forceinline__ f32x16 st_block(const uint16_t* Ks, int krow0, const 
 // Step 1: the chunk's row maximum, and the lazy rescale: the reference maximum only
 // moves (rescaling O and the sums) when the new maximum exceeds it by more than 2^8.
 // s holds NB blocks of 32 keys.
+// Soft-caps NB blocks of 32 raw scores in place (softcap_score); a no-op when cap_in == 0.
+template <int NB>
+__device__ __forceinline__ void softcap_n(f32x16* s, float cap_in, float cap_out) {
+  if (cap_in == 0.f) return;
+#pragma unroll
+  for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[kb][r] = softcap_score(s[kb][r], cap_in, cap_out);
+}
+
 template <int NB>
 __device__ __forceinline__ void softmax_max_n(const f32x16* s, float scale_log2, float& m_run, float& l_run,
                                               float& le_run, f32x16* oacc) {

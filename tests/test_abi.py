@@ -39,9 +39,26 @@ def test_status_strings(lib):
     assert lib.bsa_status_string(99) == b"unknown status"
 
 
+def _struct_fields(name):
+    text = open(os.path.join(ROOT, "include", "bsa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    body = re.search(r"typedef struct \{([^}]*)\} " + name + ";", text).group(1)
+    fields = []
+    for decl in filter(None, (d.strip() for d in body.split(";"))):
+        # "[const] type[*] a, b" -> ["a", "b"]
+        names = re.sub(r"^(const\s+)?\w+\s*\*?\s*", "", decl)
+        fields += [x.strip() for x in names.split(",")]
+    return fields
+
+
+def test_struct_layouts_match_header():
+    assert _struct_fields("bsa_problem") == [f for f, _ in bd._Problem._fields_]
+    assert _struct_fields("bsa_tensor") == [f for f, _ in bd._Tensor._fields_]
+
+
 def _prob(**kw):
     base = dict(B=1, Hq=4, Hkv=2, Sq=1, Sk=256, D=128, cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=0,
-                max_seqlen_k=0, softmax_scale=0.0, causal=0)
+                max_seqlen_k=0, softmax_scale=0.0, causal=0, softcap=0.0)
     base.update(kw)
     return bd._Problem(**base)
 
@@ -63,6 +80,9 @@ def test_fwd_argument_errors(lib):
     assert _fwd(lib, _prob(Hq=3, Hkv=2)) == bd.BSA_ERR_INVALID_ARG                # Hq % Hkv
     assert _fwd(lib, _prob(B=0)) == bd.BSA_ERR_INVALID_ARG
     assert _fwd(lib, _prob(D=96)) == bd.BSA_ERR_UNSUPPORTED                       # head dim
+    assert _fwd(lib, _prob(softcap=-1.0)) == bd.BSA_ERR_INVALID_ARG               # softcap < 0
+    assert _fwd(lib, _prob(softcap=float("nan"))) == bd.BSA_ERR_INVALID_ARG
+    assert _fwd(lib, _prob(softcap=float("inf"))) == bd.BSA_ERR_INVALID_ARG
     assert _fwd(lib, _prob(), q=_t(ptr=0)) == bd.BSA_ERR_INVALID_ARG              # null tensor
     assert _fwd(lib, _prob(), k=_t(dtype=1)) == bd.BSA_ERR_UNSUPPORTED            # f32 inputs
     assert _fwd(lib, _prob(), q=_t(ptr=18)) == bd.BSA_ERR_INVALID_ARG             # misaligned rows
@@ -114,6 +134,9 @@ def test_gated_and_vs_convert_errors(lib):
     assert lib.bsa_fwd_gated(ctypes.byref(prob), q, _t(), _t(), None, 128, 128, q, None, None, None, None) \
         == bd.BSA_ERR_INVALID_ARG
     assert lib.bsa_fwd_gated(ctypes.byref(prob), q, _t(), _t(), T, 64, 64, q, None, None, None, None) \
+        == bd.BSA_ERR_UNSUPPORTED
+    sc = _prob(Hq=2, Hkv=2, Sq=256, Sk=256, causal=1, softcap=30.0)
+    assert lib.bsa_fwd_gated(ctypes.byref(sc), q, _t(), _t(), T, 128, 128, q, None, None, None, None) \
         == bd.BSA_ERR_UNSUPPORTED
     nc = _prob(Hq=2, Hkv=2, Sq=256, Sk=256, causal=0)
     assert lib.bsa_fwd_gated(ctypes.byref(nc), q, _t(), _t(), T, 128, 128, q, None, None, None, None) \
