@@ -43,7 +43,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   __shared__ int ents_s[kEnts];
   __shared__ int cols_s[kCols];
 
-  const int item = xcd_item(wg_x(), a.n_items);
+  const int item = KIND == 2 ? head_sync_item(wg_x(), a.nqb, a.n_items) : xcd_item(wg_x(), a.n_items);
   const int mrev = item % a.nqb;
   int rest = item / a.nqb;
   const int g = rest % a.G;

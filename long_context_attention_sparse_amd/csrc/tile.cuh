@@ -193,4 +193,20 @@ __device__ __forceinline__ int xcd_item(int lid, int n_items) {
   return xcd * per + min(xcd, rem) + j8;
 }
 
+// Work order for patterns whose key sets stream through a head's whole K/V (vertical-slash):
+// every XCD works on the same (b, head) at the same time, so that head's K/V stays in the
+// memory-side cache, and each XCD takes runs of kRun consecutive query blocks, so the
+// near-diagonal windows and the columns the blocks of a run share hit in its L2.  Runs are
+// dealt to the XCDs in turn, heaviest (last) query block first.  Returns the item index in
+// the (b, kv head, group member, reversed query block) order of the prefill kernels.
+__device__ __forceinline__ int head_sync_item(int lid, int nqb, int n_items) {
+  constexpr int kRun = 16;
+  if (nqb % (8 * kRun) || n_items % nqb) return xcd_item(lid, n_items);
+  const int xcd = lid & 7, j = lid >> 3;
+  const int share = nqb >> 3;  // query blocks of one head per XCD
+  const int head = j / share, jj = j - head * share;
+  const int c = jj / kRun, r = jj - c * kRun;
+  return head * nqb + (c * 8 + xcd) * kRun + r;
+}
+
 }  // namespace bsa
