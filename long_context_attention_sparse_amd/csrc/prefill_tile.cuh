@@ -44,10 +44,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   __shared__ int cols_s[kCols];
 
   const int item = KIND == 2 ? head_sync_item(wg_x(), a.nqb, a.n_items) : xcd_item(wg_x(), a.n_items);
-  const int mrev = item % a.nqb;
-  int rest = item / a.nqb;
-  const int g = rest % a.G;
-  rest /= a.G;
+  // (b, kv head, query block, group member): the G query heads that share a kv head run
+  // the same query block side by side, so the key blocks they visit meet in L2
+  const int g = item % a.G;
+  int rest = item / a.G;
+  const int mrev = rest % a.nqb;
+  rest /= a.nqb;
   const int hkv = rest % a.Hkv;
   const int b = rest / a.Hkv;
   const int h = hkv * a.G + g;

@@ -198,7 +198,8 @@ __device__ __forceinline__ int xcd_item(int lid, int n_items) {
 // memory-side cache, and each XCD takes runs of kRun consecutive query blocks, so the
 // near-diagonal windows and the columns the blocks of a run share hit in its L2.  Runs are
 // dealt to the XCDs in turn, heaviest (last) query block first.  Returns the item index in
-// the (b, kv head, group member, reversed query block) order of the prefill kernels.
+// the (b, kv head, reversed query block, group member) order of the prefill kernels (with G
+// query heads per kv head a run holds kRun / G query blocks of each of them).
 __device__ __forceinline__ int head_sync_item(int lid, int nqb, int n_items) {
   constexpr int kRun = 16;
   if (nqb % (8 * kRun) || n_items % nqb) return xcd_item(lid, n_items);
