@@ -9,7 +9,7 @@ the HIP kernels or their C interface.
 Modules:
   core            block-sparse softmax attention, per-entry partials, the
                   log-sum-exp combine and the speculative + sparse composition
-  gate            BSFA tile-maximum gating
+  gate            BSFA tile-maximum gating and threshold calibration
   vertical_slash  vertical-slash index conversion and attention over it
 
 Pinning (see the tests marked "not gpu"): every function here is checked
@@ -21,11 +21,12 @@ skipped tiles' softmax mass in the gated variant (excluded).
 """
 from .core import (as_f64, attend_rows, block_mask, block_sparse, block_sparse_partials, causal_mask,
                    combine, dense, default_scale, speculative_sparse)
-from .gate import gated, gated_rows, tile_max_row
+from .gate import calibrate, gated, gated_rows, tile_max_row
+from .gate import density as gated_density
 from .vertical_slash import vs_attention, vs_attention_rows, vs_convert, vs_convert_item, vs_convert_mergehead
 
 __all__ = [
     "as_f64", "attend_rows", "block_mask", "block_sparse", "block_sparse_partials", "causal_mask",
-    "combine", "dense", "default_scale", "speculative_sparse", "gated", "gated_rows", "tile_max_row",
+    "combine", "dense", "default_scale", "speculative_sparse", "gated", "gated_rows", "tile_max_row", "calibrate", "gated_density",
     "vs_attention", "vs_attention_rows", "vs_convert", "vs_convert_item", "vs_convert_mergehead",
 ]

@@ -19,6 +19,17 @@ Readings (the page leaves these open):
 * The scores are the scaled dot products scale*<q, k>; the comparison is taken
   in float32, the precision of the kernel: the exact float64 tile maximum is
   rounded to float32 and compared with the float32 threshold.
+
+Threshold calibration (same page, Abstract: a one-time calibration on a small
+data set learns per-layer and per-head score distributions so that the top-k
+blocks of each query are kept; Figure 2: one threshold T^(k) per query row,
+-inf where fewer than k off-diagonal candidates exist).  The page gives no
+procedure; reading taken here: for each calibration sample b, head h and query
+block i, the k-th largest off-diagonal tile maximum t(i, j), j < i; -inf when
+i < k; T(h, i) is the mean of those values over the samples.  Gating one
+sample with its own threshold then keeps exactly min(k, i) off-diagonal tiles
+of each row (ties aside); the target density of row i is (min(k, i) + 1) /
+(i + 1), the diagonal included.
 """
 from __future__ import annotations
 
@@ -115,3 +126,32 @@ def gated_rows(q, k, v, T: float, b: int, h: int, i: int, rows, BM: int = 128, B
     mask = cols[None, :] <= rows[:, None]
     o, lse = _attend(qr, kv, vv, mask, scale)
     return o, lse, kr, t
+
+
+def calibrate(q, k, k_keep: int, BM: int = 128, BN: int = 128, scale: float | None = None):
+    """Thresholds T [Hq, nQB] (float64; -inf where i < k_keep) from the calibration samples
+    q [B,S,Hq,D], k [B,S,Hkv,D], and the per-sample values [B, Hq, nQB]."""
+    if k_keep < 1:
+        raise ValueError("k_keep must be at least 1")
+    B, S, Hq, _ = np.asarray(q).shape
+    _check(S, np.asarray(k).shape[1], BM, BN)
+    nqb = S // BM
+    per = np.full((B, Hq, nqb), -np.inf)
+    for b in range(B):
+        for h in range(Hq):
+            for i in range(k_keep, nqb):
+                t = tile_max_row(q, k, b, h, i, BM, BN, scale)[:i]   # off-diagonal candidates
+                per[b, h, i] = np.sort(t)[::-1][k_keep - 1]
+    return per.mean(axis=0), per
+
+
+def density(keep, k_keep: int):
+    """(realised, target) fraction of causal tiles kept, over every (b, h, query block) row of a
+    keep mask [B, Hq, nQB, nKB]; the target of row i is (min(k_keep, i) + 1) / (i + 1)."""
+    keep = np.asarray(keep)
+    nqb = keep.shape[-2]
+    lower = np.tril(np.ones((nqb, nqb), bool))
+    realised = float(keep[..., lower].sum()) / (keep[..., 0, 0].size * lower.sum())
+    i = np.arange(nqb)
+    target = float(np.sum(np.minimum(k_keep, i) + 1)) / lower.sum()
+    return realised, target

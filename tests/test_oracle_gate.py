@@ -122,3 +122,53 @@ def test_threshold_generator_margin_and_rate():
             skipped += int(np.sum(t[:i] < T))
             total += i
     assert 0.3 < skipped / total < 0.7
+
+
+# ---- threshold calibration ----
+
+@pytest.mark.parametrize("k_keep", [1, 3, 6])
+def test_calibrated_threshold_keeps_exactly_k_per_row(k_keep):
+    """Gating a calibration sample with its own thresholds keeps min(k, i) off-diagonal tiles
+    of each query block i (the maxima of these inputs are distinct), so the realised density is
+    the target one.  Checked through the gated oracle's own keep rule."""
+    q, k, v, bs = _small(seed=31)
+    T, per = oracle.calibrate(q, k, k_keep, bs, bs)
+    assert np.array_equal(T, per[0])
+    nqb = T.shape[1]
+    assert np.isneginf(T[:, :k_keep]).all() and np.isfinite(T[:, k_keep:]).all()
+    _, _, keep, tmax = oracle.gated(q, k, v, T[None].astype(np.float32), bs, bs)
+    for h in range(T.shape[0]):
+        for i in range(nqb):
+            off = tmax[0, h, i, :i]
+            assert np.unique(off.astype(np.float32)).size == off.size
+            assert keep[0, h, i, :i].sum() == min(k_keep, i), (h, i)
+            assert keep[0, h, i, i] == 1
+    realised, target = oracle.gated_density(keep, k_keep)
+    assert abs(realised - target) < 1e-12
+    assert abs(target - sum(min(k_keep, i) + 1 for i in range(nqb)) / (nqb * (nqb + 1) / 2)) < 1e-12
+
+
+def test_calibration_averages_samples():
+    """Two samples, the second with every query doubled (exact in bf16): its scores, and so its
+    k-th largest tile maximum, double; the calibrated threshold is the mean, 1.5x the first."""
+    from synth import f32_to_bf16_bits
+    q, k, _, bs = _small(seed=32)
+    q2 = f32_to_bf16_bits((2.0 * bf16_to_f64(q)).astype(np.float32))
+    qq = np.concatenate([q, q2])
+    kk = np.concatenate([k, k])
+    T, per = oracle.calibrate(qq, kk, 2, bs, bs)
+    fin = np.isfinite(per[0])
+    np.testing.assert_allclose(per[1][fin], 2.0 * per[0][fin], rtol=1e-12)
+    np.testing.assert_allclose(T[fin], 1.5 * per[0][fin], rtol=1e-12)
+    assert np.isneginf(T[~fin]).all() and (~fin).sum() == 2 * T.shape[0]
+
+
+def test_calibration_with_k_past_every_row_keeps_everything():
+    q, k, v, bs = _small(seed=33, S=128)
+    T, _ = oracle.calibrate(q, k, 4, bs, bs)
+    assert np.isneginf(T).all()
+    _, _, keep, _ = oracle.gated(q, k, v, T[None].astype(np.float32), bs, bs)
+    realised, target = oracle.gated_density(keep, 4)
+    assert realised == 1.0 and target == 1.0
+    with pytest.raises(ValueError):
+        oracle.calibrate(q, k, 0, bs, bs)
