@@ -421,11 +421,36 @@ def bench_gated(torch, bsa, args):
     tf = flops / (kms * 1e-3) / 1e12
     off = lower & ~np.eye(nqb, dtype=bool)
     skip = 1.0 - float(km[..., off].mean())
+
+    # threshold calibration on this input (k = 128 of 512 key blocks), then the gate at it
+    k_cal = 128
+    cal = {}
+
+    def step_cal(timer):
+        with timer.span("calibrate"):
+            cal["T"], _ = bsa.bsfa_calibrate(q, k, k_cal)
+
+    def step_cal_gate(timer):
+        with timer.span("gated at calibrated T"):
+            _, _, cal["keep"], _ = bsa.bsa_fwd_gated(q, k, v, cal["T"], out=out)
+
+    timer3, timer4 = Timer(torch), Timer(torch)
+    run_steps(torch, step_cal, timer3, 3, 1)
+    run_steps(torch, step_cal_gate, timer4, 3, 1)
+    cal_ms, cal_gate_ms = timer3.mean_ms("calibrate"), timer4.mean_ms("gated at calibrated T")
+    ckeep = cal["keep"].cpu().numpy()
+    realised = float(ckeep[..., lower].sum()) / (Hq * int(lower.sum()))
+    target = float(np.sum(np.minimum(k_cal, np.arange(nqb)) + 1)) / int(lower.sum())
+    cal_flops = causal_tiles * 2 * 128 ** 3  # the tile maxima: S on every causal tile
+    calibration = {"k": k_cal, "ms": round(cal_ms, 4), "tflops": round(cal_flops / (cal_ms * 1e-3) / 1e12, 2),
+                   "target_density": round(target, 4), "realised_density": round(realised, 4),
+                   "gated_ms_at_calibrated_T": round(cal_gate_ms, 4)}
     return dict(metric=METRIC, value=round(flops / (ms * 1e-3) / 1e12, 2), unit="TFLOP/s", ms_per_step=round(ms, 4),
                 dtype="bf16",
                 config={"workload": "BSFA gated causal prefill", "B": 1, "Hq": Hq, "Hkv": 8, "S": S, "D": 128,
                         "tile": 128, "skip_fraction_offdiag": round(skip, 4), "flops": flops,
-                        "ungated_ms": round(ms_dense, 4), "gated_speedup": round(ms_dense / ms, 3)},
+                        "ungated_ms": round(ms_dense, 4), "gated_speedup": round(ms_dense / ms, 3),
+                        "calibration": calibration},
                 roofline={"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                           "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None, "kernel": "gated_kernel",
                           "avg_ms": round(kms, 4)},

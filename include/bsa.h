@@ -234,6 +234,29 @@ bsa_status bsa_fwd_gated(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, bs
                          int32_t block_M, int32_t block_N, bsa_tensor o, float* lse, uint8_t* keep_mask,
                          float* tile_max, bsa_stream stream);
 
+/* BSFA threshold calibration (synthetic, one pass over calibration inputs).
+ * [BSFA] Abstract (a one-time calibration learns per-layer, per-head score
+ * distributions so that the top-k blocks of each query are kept) and
+ * Figure 2 (thresholds T^(k), one per query row, -inf where fewer than k
+ * off-diagonal candidates exist).  The page gives no procedure; this one:
+ * for each sample b, head h and 128-row query block i, the tile maxima
+ * t(i, j) (as bsa_fwd_gated computes them) are written to tile_max and the
+ * k_keep-th largest of the off-diagonal ones (j < i) is taken; rows with
+ * i < k_keep get -inf; T[h, i] is the mean over the B samples (float32,
+ * summed in sample order).  Gating a sample with its own thresholds keeps
+ * k_keep off-diagonal tiles per row (ties aside).
+ *   q, k       as bsa_fwd_gated (v is not needed): causal self-attention,
+ *              fixed length, Sq == Sk, Sq % 128 == 0, D == 128, no softcap.
+ *   k_keep     >= 1.
+ *   tile_max   device float32 [B, Hq, nQB, nQB], caller-owned; entries
+ *              j <= i are written (the diagonal over its causal entries).
+ *   T          device float32 [Hq, nQB] output; expand it over the batch
+ *              for bsa_fwd_gated's [B, Hq, nQB].
+ * Errors: BSA_ERR_INVALID_ARG (NULL, k_keep < 1, shapes, alignment);
+ * BSA_ERR_UNSUPPORTED (outside the cases above, nQB > 4096); BSA_ERR_HIP. */
+bsa_status bsfa_calibrate(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, int32_t k_keep, float* tile_max,
+                          float* T, bsa_stream stream);
+
 /* Vertical-slash index conversion.  [SGL] Description and I/O Contract
  * (convert_vertical_slash_indexes); the conversion rule is this library's
  * own, since the page defers it to a paper that is not among the sources:

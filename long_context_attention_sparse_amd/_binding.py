@@ -24,8 +24,8 @@ BSA_PAT_DENSE, BSA_PAT_BLOCK, BSA_PAT_VS = 0, 1, 2
 
 EXPORTS = ("bsa_status_string", "bsa_workspace_size", "bsa_fwd", "bsa_fwd_partials", "bsa_num_partials",
            "bsa_speculative_sparse", "bsa_speculative_partials", "bsa_speculative_num_partials",
-           "bsa_speculative_workspace_size", "bsa_combine", "bsa_fwd_gated", "vs_convert_indexes",
-           "vs_convert_indexes_mergehead")
+           "bsa_speculative_workspace_size", "bsa_combine", "bsa_fwd_gated", "bsfa_calibrate",
+           "vs_convert_indexes", "vs_convert_indexes_mergehead")
 
 
 class BSAError(RuntimeError):
@@ -97,6 +97,9 @@ def load(path: str = LIB_PATH):
     lib.bsa_fwd_gated.argtypes = [ctypes.POINTER(_Problem), _Tensor, _Tensor, _Tensor, ctypes.c_void_p,
                                   ctypes.c_int32, ctypes.c_int32, _Tensor, ctypes.c_void_p, ctypes.c_void_p,
                                   ctypes.c_void_p, ctypes.c_void_p]
+    lib.bsfa_calibrate.restype = ctypes.c_int
+    lib.bsfa_calibrate.argtypes = [ctypes.POINTER(_Problem), _Tensor, _Tensor, ctypes.c_int32, ctypes.c_void_p,
+                                   ctypes.c_void_p, ctypes.c_void_p]
     lib.vs_convert_indexes.restype = ctypes.c_int
     lib.vs_convert_indexes.argtypes = ([ctypes.c_void_p] * 4 + [ctypes.c_int32] * 8 + [ctypes.c_void_p] * 5)
     lib.vs_convert_indexes_mergehead.restype = ctypes.c_int
@@ -329,12 +332,35 @@ def bsa_fwd_gated(q, k, v, T: torch.Tensor, *, block_M: int = 128, block_N: int 
     keep = torch.zeros((B, Hq, nqb, nkb), dtype=torch.uint8, device=q.device) if return_mask else None
     tmax = torch.full((B, Hq, nqb, nkb), float("nan"), dtype=torch.float32, device=q.device) \
         if return_tile_max else None
+    if T.dim() == 2:  # calibrated [Hq, nQB], shared by the batch
+        T = T.unsqueeze(0).expand(B, -1, -1).contiguous()
     if T.dtype != torch.float32 or not T.is_contiguous():
-        raise ValueError("T must be contiguous float32 [B, Hq, nQB]")
+        raise ValueError("T must be contiguous float32 [B, Hq, nQB] (or [Hq, nQB])")
     st = lib.bsa_fwd_gated(ctypes.byref(prob), _tensor(q), _tensor(k), _tensor(v), _ptr(T), block_M, block_N,
                            _tensor(out), _ptr(lse), _ptr(keep), _ptr(tmax), _stream(stream))
     _check("bsa_fwd_gated", st)
     return out, lse, keep, tmax
+
+
+def bsfa_calibrate(q, k, k_keep: int, *, softmax_scale=None, tile_max: Optional[torch.Tensor] = None,
+                   stream=None):
+    """BSFA threshold calibration over calibration samples q [B, S, Hq, D], k [B, S, Hkv, D]:
+    per (b, head, 128-row query block i) the k_keep-th largest off-diagonal tile maximum, -inf
+    for i < k_keep, averaged over the samples.  Returns (T [Hq, nQB], tile_max [B, Hq, nQB, nQB])
+    (float32; tile_max entries above the diagonal are left as given, NaN when allocated here)."""
+    lib = load()
+    prob = _problem(q, k, True, softmax_scale)
+    B, S, Hq, D = q.shape
+    nqb = S // 128
+    if tile_max is None:
+        tile_max = torch.full((B, Hq, nqb, nqb), float("nan"), dtype=torch.float32, device=q.device)
+    if tile_max.dtype != torch.float32 or not tile_max.is_contiguous() or tile_max.numel() != B * Hq * nqb * nqb:
+        raise ValueError("tile_max must be contiguous float32 [B, Hq, nQB, nQB]")
+    T = torch.empty((Hq, nqb), dtype=torch.float32, device=q.device)
+    st = lib.bsfa_calibrate(ctypes.byref(prob), _tensor(q), _tensor(k), int(k_keep), _ptr(tile_max), _ptr(T),
+                            _stream(stream))
+    _check("bsfa_calibrate", st)
+    return T, tile_max
 
 
 def _vs_outputs(vertical_indexes, slash_indexes, context_size, block_size_M):

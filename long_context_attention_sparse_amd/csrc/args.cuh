@@ -29,6 +29,7 @@ struct PatternArg {
 constexpr int kDecodeEntsLds = 256;    // block ids of a decode split staged in LDS (later ones read from global)
 constexpr int kVSConvThreads = 64;     // conversion workgroup size (one query block per thread)
 constexpr int kVSConvLdsInts = 16384;  // slash + vertical entries staged in LDS (longer lists stay in global)
+constexpr int kThreshMaxCand = 4096;   // threshold selection: query blocks per row (LDS candidates)
 
 struct DecodeSeg {
   TensorArg k, v;
@@ -85,6 +86,12 @@ struct GatedArgs {
   int B, Hq, Hkv, G, S, nqb;
   float scale, scale_log2;
   int n_items;
+};
+
+struct ThresholdArgs {
+  const float* tmax;  // [B, Hq, nqb, nqb] scaled tile maxima (j < i read)
+  float* T;           // [Hq, nqb]
+  int B, Hq, nqb, k;
 };
 
 struct CombineArgs {

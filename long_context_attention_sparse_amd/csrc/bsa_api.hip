@@ -535,7 +535,43 @@ bsa_status bsa_fwd_gated(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, bs
   const int64_t items = (int64_t)p.B * p.Hq * a.nqb;
   if (items > INT_MAX) return BSA_ERR_UNSUPPORTED;
   a.n_items = (int)items;
-  launch_gated(a, reinterpret_cast<hipStream_t>(stream));
+  launch_gated(a, false, reinterpret_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+bsa_status bsfa_calibrate(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, int32_t k_keep, float* tile_max,
+                          float* T, bsa_stream stream) {
+  if (!prob || !q.ptr || !k.ptr || !tile_max || !T || k_keep < 1) return BSA_ERR_INVALID_ARG;
+  const bsa_problem& p = *prob;
+  if (p.B <= 0 || p.Hq <= 0 || p.Hkv <= 0 || p.Sq <= 0 || p.Sk <= 0 || p.D <= 0 || p.Hq % p.Hkv)
+    return BSA_ERR_INVALID_ARG;
+  if (!(p.softcap >= 0.f) || std::isinf(p.softcap)) return BSA_ERR_INVALID_ARG;
+  if (q.dtype != BSA_BF16 || k.dtype != BSA_BF16) return BSA_ERR_UNSUPPORTED;
+  if (!aligned_rows(q, 2) || !aligned_rows(k, 2)) return BSA_ERR_INVALID_ARG;
+  if (p.D != 128 || !p.causal || p.cu_seqlens_q || p.Sq != p.Sk || p.Sq % 128 || p.softcap > 0.f)
+    return BSA_ERR_UNSUPPORTED;
+  const int nqb = p.Sq / 128;
+  if (nqb > kThreshMaxCand) return BSA_ERR_UNSUPPORTED;
+  GatedArgs a{};
+  a.q = targ(q);
+  a.k = targ(k);
+  a.v = targ(k);  // not read by the calibration pass
+  a.tmax = tile_max;
+  a.B = p.B;
+  a.Hq = p.Hq;
+  a.Hkv = p.Hkv;
+  a.G = p.Hq / p.Hkv;
+  a.S = p.Sq;
+  a.nqb = nqb;
+  a.scale = scale_of(p);
+  a.scale_log2 = a.scale * kLog2e;
+  const int64_t items = (int64_t)p.B * p.Hq * nqb;
+  if (items > INT_MAX) return BSA_ERR_UNSUPPORTED;
+  a.n_items = (int)items;
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  launch_gated(a, true, st);
+  if (hipPeekAtLastError() != hipSuccess) return launch_status();
+  launch_threshold(ThresholdArgs{tile_max, T, p.B, p.Hq, nqb, k_keep}, st);
   return launch_status();
 }
 

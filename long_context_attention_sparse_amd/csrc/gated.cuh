@@ -24,6 +24,9 @@
 
 namespace bsa {
 
+// CALIB: the threshold-calibration pass — the same S tiles and tile maxima, written to
+// a.tmax, with no tile kept: no V load, no P V product and no output.
+template <bool CALIB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void gated_kernel(GatedArgs a) {
   constexpr int D = TD;
   constexpr int BN = 128;
@@ -57,7 +60,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
   for (int ks = 0; ks < D / 16; ++ks) qreg[ks] = as_bf16x8(ldg128(qb + (int64_t)row * a.q.ss + ks * 16 + hh * 8));
 
   const int64_t th = ((int64_t)b * a.Hq + h) * a.nqb + i;
-  const float T = a.T[th];
+  const float T = CALIB ? 0.f : a.T[th];
   const int64_t mask_row = th * a.nqb;
 
   // Direct loads: wave w fills rows 32w..32w+31 of a tile with eight 1 KB instructions
@@ -141,7 +144,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
     // every wave's maximum is in LDS and every wave is done reading K_j
     __syncthreads();
     const float tile_max = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])) * a.scale;
-    const bool keep = diag || tile_max >= T;
+    const bool keep = !CALIB && (diag || tile_max >= T);
     if (t == 0) {
       if (a.keep) a.keep[mask_row + j] = keep ? 1 : 0;
       if (a.tmax) a.tmax[mask_row + j] = tile_max;
@@ -194,8 +197,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
       __syncthreads();
     }
   }
-  const int64_t ob = (int64_t)b * a.o.sb + (int64_t)row * a.o.ss + (int64_t)h * a.o.sh;
-  write_row(a.o, ob, a.lse ? a.lse + ((int64_t)b * a.Hq + h) * a.S + row : nullptr, oacc, m_run, l_run, le_run, hh);
+  if constexpr (!CALIB) {
+    const int64_t ob = (int64_t)b * a.o.sb + (int64_t)row * a.o.ss + (int64_t)h * a.o.sh;
+    write_row(a.o, ob, a.lse ? a.lse + ((int64_t)b * a.Hq + h) * a.S + row : nullptr, oacc, m_run, l_run, le_run,
+              hh);
+  }
 }
 
 }  // namespace bsa

@@ -1,5 +1,6 @@
-// Memory-streaming kernels (split-KV decode, combine, vertical-slash conversion) and
-// their launch wrappers; compiled with the default IEEE floating-point mode.
+// Memory-streaming kernels (split-KV decode, combine, vertical-slash conversion, threshold
+// selection) and their launch wrappers; compiled with the default IEEE floating-point mode.
+#include "calibrate.cuh"
 #include "combine.cuh"
 #include "decode.cuh"
 #include "launch.h"
@@ -22,6 +23,10 @@ void launch_combine(const CombineArgs& c, hipStream_t st) {
 void launch_vs_convert(const VSConvArgs& a, unsigned lds_bytes, hipStream_t st) {
   dim3 grid((a.rows + kVSConvThreads - 1) / kVSConvThreads, a.B * a.H);
   hipLaunchKernelGGL(vs_convert_kernel, grid, dim3(kVSConvThreads), lds_bytes, st, a);
+}
+
+void launch_threshold(const ThresholdArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(threshold_kernel, dim3(a.nqb, a.Hq), dim3(256), 0, st, a);
 }
 
 }  // namespace bsa

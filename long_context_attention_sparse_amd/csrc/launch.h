@@ -16,7 +16,9 @@ void launch_combine(const CombineArgs& a, hipStream_t st);
 void launch_vs_convert(const VSConvArgs& a, unsigned lds_bytes, hipStream_t st);
 // prefill_pipe_kernel<KIND, NW>: n_items workgroups of NW*64 threads (NW 2 or 4, KIND 0..2).
 void launch_prefill(const PrefillArgs& a, int NW, int KIND, hipStream_t st);
-// gated_kernel: n_items workgroups of 256 threads.
-void launch_gated(const GatedArgs& a, hipStream_t st);
+// gated_kernel<calib>: n_items workgroups of 256 threads.
+void launch_gated(const GatedArgs& a, bool calib, hipStream_t st);
+// threshold_kernel: grid (nqb, Hq), 256 threads; nqb <= kThreshMaxCand.
+void launch_threshold(const ThresholdArgs& a, hipStream_t st);
 
 }  // namespace bsa

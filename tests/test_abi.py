@@ -16,7 +16,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def _header_functions():
     text = open(os.path.join(ROOT, "include", "bsa.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(bsa_\w+|vs_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(bsa_\w+|bsfa_\w+|vs_\w+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -135,6 +135,16 @@ def test_gated_and_vs_convert_errors(lib):
         == bd.BSA_ERR_INVALID_ARG
     assert lib.bsa_fwd_gated(ctypes.byref(prob), q, _t(), _t(), T, 64, 64, q, None, None, None, None) \
         == bd.BSA_ERR_UNSUPPORTED
+    cal = lib.bsfa_calibrate
+    assert cal(ctypes.byref(prob), q, _t(), 0, T, T, None) == bd.BSA_ERR_INVALID_ARG         # k_keep < 1
+    assert cal(ctypes.byref(prob), q, _t(), 2, None, T, None) == bd.BSA_ERR_INVALID_ARG      # no tile_max
+    assert cal(ctypes.byref(prob), q, _t(), 2, T, None, None) == bd.BSA_ERR_INVALID_ARG      # no T
+    assert cal(ctypes.byref(_prob(Hq=2, Hkv=2, Sq=256, Sk=256, causal=0)), q, _t(), 2, T, T, None) \
+        == bd.BSA_ERR_UNSUPPORTED                                                            # not causal
+    assert cal(ctypes.byref(_prob(Hq=2, Hkv=2, Sq=200, Sk=200, causal=1)), q, _t(), 2, T, T, None) \
+        == bd.BSA_ERR_UNSUPPORTED                                                            # S % 128
+    assert cal(ctypes.byref(_prob(Hq=2, Hkv=2, Sq=4097 * 128, Sk=4097 * 128, causal=1)), q, _t(), 2, T, T,
+               None) == bd.BSA_ERR_UNSUPPORTED                                               # rows too long
     sc = _prob(Hq=2, Hkv=2, Sq=256, Sk=256, causal=1, softcap=30.0)
     assert lib.bsa_fwd_gated(ctypes.byref(sc), q, _t(), _t(), T, 128, 128, q, None, None, None, None) \
         == bd.BSA_ERR_UNSUPPORTED

@@ -105,3 +105,63 @@ def test_gated_full_size_sampled(cfg4):
         assert np.abs(tg[0, h, i, :i + 1] - t).max() < 1e-3
         check_o(host(o[0, rows, h]), o_ref, f"gated full h={h} i={i}")
         check_lse(host(lse[0, h, rows]), lse_ref, f"gated full lse h={h} i={i}")
+
+
+# ---- threshold calibration ----
+
+@pytest.mark.parametrize("k_keep", [1, 3, 7])
+def test_calibrate_small(small, k_keep):
+    """Tile maxima (j <= i) and thresholds against the oracle over two calibration samples;
+    k_keep = 7 leaves only the last query block with a finite threshold."""
+    w = small
+    say("calibrate small", k_keep)
+    T, tmax = bsa.bsfa_calibrate(w["dq"], w["dk"], k_keep)
+    T_ref, per_ref = oracle.calibrate(w["q"], w["k"], k_keep, 128, 128)
+    lower = np.tril(np.ones((8, 8), bool))
+    tg = tmax.cpu().numpy().astype(np.float64)
+    for b in range(2):
+        for h in range(4):
+            for i in range(8):
+                t = oracle.tile_max_row(w["q"], w["k"], b, h, i, 128, 128)
+                assert np.abs(tg[b, h, i, :i + 1] - t).max() < 1e-3, (b, h, i)
+    assert np.isnan(tg[..., ~lower]).all(), "entries above the diagonal must stay untouched"
+    Tg = T.cpu().numpy().astype(np.float64)
+    assert np.array_equal(np.isneginf(Tg), np.isneginf(T_ref))
+    fin = np.isfinite(T_ref)
+    assert np.abs(Tg[fin] - T_ref[fin]).max() < 1e-3
+
+
+def test_calibrated_gate_keeps_k_per_row(small):
+    """One calibration sample gated with its own thresholds keeps exactly min(k, i) off-diagonal
+    tiles per query block: the thresholds are that sample's own tile maxima, computed by the
+    same tile loop, so the comparison is exact.  The realised density then equals the target."""
+    w = small
+    k_keep = 3
+    say("calibrated gate keeps k per row")
+    q0, k0, v0 = w["dq"][:1], w["dk"][:1], w["dv"][:1]
+    T, tmax = bsa.bsfa_calibrate(q0, k0, k_keep)
+    _, _, keep, tmax2 = bsa.bsa_fwd_gated(q0, k0, v0, T, out_dtype=torch.float32, return_tile_max=True)
+    kg = keep.cpu().numpy()
+    lower = np.tril(np.ones((8, 8), bool))
+    assert np.array_equal(tmax.cpu().numpy()[..., lower], tmax2.cpu().numpy()[..., lower])
+    for h in range(4):
+        for i in range(8):
+            assert kg[0, h, i, :i].sum() == min(k_keep, i) and kg[0, h, i, i] == 1, (h, i)
+    realised, target = oracle.gated_density(kg, k_keep)
+    assert realised == target
+
+
+def test_calibrate_full_size_sampled(cfg4):
+    """Thresholds at the full 65536-token shape, k = 64, on sampled rows."""
+    w = cfg4
+    say("calibrate full size")
+    T, tmax = bsa.bsfa_calibrate(w["dq"], w["dk"], 64)
+    Tg = T.cpu().numpy().astype(np.float64)
+    tg = tmax.cpu().numpy()
+    assert np.isneginf(Tg[:, :64]).all() and np.isfinite(Tg[:, 64:]).all()
+    for h, i in [(0, 511), (31, 300), (17, 64), (8, 65), (3, 200)]:
+        say("oracle tile maxima", h, i)
+        t = oracle.tile_max_row(w["q"], w["k"], 0, h, i, 128, 128)
+        assert np.abs(tg[0, h, i, :i + 1] - t).max() < 1e-3, (h, i)
+        want = np.sort(t[:i])[::-1][63]
+        assert abs(Tg[h, i] - want) < 1e-3, (h, i, Tg[h, i], want)
