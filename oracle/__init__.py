@@ -11,6 +11,7 @@ Modules:
                   log-sum-exp combine and the speculative + sparse composition
   gate            BSFA tile-maximum gating and threshold calibration
   vertical_slash  vertical-slash index conversion and attention over it
+  selected        selected attention: each query token attends to its top-k key blocks
 
 Pinning (see the tests marked "not gpu"): every function here is checked
 against closed forms, invariants, brute force and an independent library
@@ -23,10 +24,11 @@ from .core import (as_f64, attend_rows, block_mask, block_sparse, block_sparse_p
                    combine, dense, default_scale, speculative_sparse)
 from .gate import calibrate, gated, gated_rows, tile_max_row
 from .gate import density as gated_density
+from .selected import selected, selected_rows
 from .vertical_slash import vs_attention, vs_attention_rows, vs_convert, vs_convert_item, vs_convert_mergehead
 
 __all__ = [
     "as_f64", "attend_rows", "block_mask", "block_sparse", "block_sparse_partials", "causal_mask",
     "combine", "dense", "default_scale", "speculative_sparse", "gated", "gated_rows", "tile_max_row", "calibrate", "gated_density",
-    "vs_attention", "vs_attention_rows", "vs_convert", "vs_convert_item", "vs_convert_mergehead",
+    "selected", "selected_rows", "vs_attention", "vs_attention_rows", "vs_convert", "vs_convert_item", "vs_convert_mergehead",
 ]

@@ -196,3 +196,62 @@ def vs_varlen_prefill(seed: int = 1005, seqlens=(65536, 32768), H: int = 32, D: 
     return dict(q=q, k=k, v=v, cu_seqlens=cu, seqlens=np.array(seqlens, np.int32), vertical=vert,
                 slash=slash, B=B, H=H, D=D, block_M=block, block_N=block,
                 context_size=int(context_size), max_seqlen=max(seqlens))
+
+
+# ---------------------------------------------------------------------------
+# Selected attention (top-k key blocks per query token), the FSA module's example shape
+# ---------------------------------------------------------------------------
+
+def selected_prefill(seed: int = 1006, seqlens=(65536, 32768), Hq: int = 4, Hkv: int = 4, D: int = 128,
+                     block: int = 64, topk: int = 16, init_blocks: int = 1, local_blocks: int = 2) -> dict:
+    """Packed varlen Q/K/V ``[total, H, D]`` ~ N(0, 1) and per (token, kv head) a selection of
+    up to ``topk`` distinct key blocks of its own sequence, ``sel [total, Hkv, topk]`` int32:
+    the first ``init_blocks`` blocks, the ``local_blocks`` blocks ending at the token's own
+    block, and uniformly random other causally reachable blocks to fill ``topk``; -1 pads a
+    token that can reach fewer blocks.  Slot order is random."""
+    seqlens = [int(s) for s in seqlens]
+    total = int(sum(seqlens))
+    cu = np.concatenate([[0], np.cumsum(seqlens)]).astype(np.int32)
+    q = normal_bf16(seed, "q", (total, Hq, D))
+    k = normal_bf16(seed, "k", (total, Hkv, D))
+    v = normal_bf16(seed, "v", (total, Hkv, D))
+    sel = np.full((total, Hkv, topk), -1, np.int32)
+    g = rng(seed, "sel")
+    chunk = 8192
+    for b, L in enumerate(seqlens):
+        for p0 in range(0, L, chunk):
+            pos = np.arange(p0, min(L, p0 + chunk))
+            own = pos // block                                   # the token's own block
+            nb = own + 1                                         # causally reachable blocks
+            R = pos.size
+            for hk in range(Hkv):
+                fixed = np.full((R, init_blocks + local_blocks), -1, np.int64)
+                fixed[:, :init_blocks] = np.arange(init_blocks)[None, :]
+                fixed[:, init_blocks:] = own[:, None] - np.arange(local_blocks)[None, ::-1]
+                fixed = np.where((fixed >= 0) & (fixed < nb[:, None]), fixed, -1)
+                # dedupe: a local block that is also an init block counts once
+                for c in range(init_blocks, init_blocks + local_blocks):
+                    fixed[:, c] = np.where(fixed[:, c] < init_blocks, -1, fixed[:, c])
+                # random others from [init_blocks, own - local_blocks + 1)
+                lo = init_blocks
+                hi = np.maximum(own - local_blocks + 1, lo)               # exclusive
+                n_rand = topk - (fixed >= 0).sum(axis=1)
+                span = hi - lo
+                width = int(span.max()) if R else 0
+                picks = np.full((R, topk), -1, np.int64)
+                if width > 0:
+                    keys = g.random((R, width))
+                    keys[np.arange(width)[None, :] >= span[:, None]] = np.inf
+                    m = min(topk, width)
+                    order = np.argsort(keys, axis=1)[:, :m]
+                    take = np.arange(m)[None, :] < np.minimum(n_rand, span)[:, None]
+                    picks[:, :m] = np.where(take, order + lo, -1)
+                allsel = np.concatenate([fixed, picks], axis=1)
+                # compact the valid entries to the front, then shuffle the slots
+                valid = allsel >= 0
+                idx = np.argsort(~valid, axis=1, kind="stable")[:, :topk]
+                row = np.take_along_axis(allsel, idx, axis=1)
+                perm = np.argsort(g.random((R, topk)), axis=1)
+                sel[cu[b] + pos, hk] = np.take_along_axis(row, perm, axis=1)
+    return dict(q=q, k=k, v=v, sel=sel, cu_seqlens=cu, seqlens=np.array(seqlens, np.int32), Hq=Hq, Hkv=Hkv,
+                D=D, block=block, topk=topk, max_seqlen=max(seqlens))
