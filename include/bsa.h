@@ -17,6 +17,9 @@
  *   [BSFA] "Block Sparse Flash Attention": Abstract; Figure 2 (mechanism).
  *   [SGL]  "Implementation: Sgl project Sglang Sparse Flash Attention":
  *          Description; Signature; I/O Contract.
+ *   [FSA]  "FSA: An Alternative Efficient Implementation of Native Sparse
+ *          Attention Kernel": Abstract; with the Flash-Sparse-Attention
+ *          README page (overview, main features, quick start).
  *
  * Conventions shared by the attention entry points
  * -------------------------------------------------
@@ -233,6 +236,37 @@ bsa_status bsa_combine(int32_t P, int32_t B, int32_t Hq, int32_t Sq, int32_t D, 
 bsa_status bsa_fwd_gated(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, bsa_tensor v, const float* T,
                          int32_t block_M, int32_t block_N, bsa_tensor o, float* lse, uint8_t* keep_mask,
                          float* tile_max, bsa_stream stream);
+
+/* Selected attention: every query token attends to the key blocks it selected.
+ * [FSA] Abstract and the Flash-Sparse-Attention README page (main features:
+ * a batched query-to-KV kernel, a reduction and an online-softmax pass, no
+ * atomics; configuration block_size, topk, varlen cu_seqlens).  Native sparse
+ * attention's selection branch: token t of kv head g selected up to topk
+ * blocks of block_size keys of its own sequence, shared by the group's query
+ * heads; the result is softmax attention over the union of those blocks
+ * (clipped to the sequence and, when prob->causal, to keys <= t + Sk - Sq).
+ * Computed key-block-outer: the selections are inverted into per-block token
+ * lists, each block's K/V tile is loaded once per 128 / G gathered tokens,
+ * every (token, slot, head) gets an (o, lse) partial in the workspace, and
+ * the combine merges a token's topk partials.
+ *   sel        device int32, [B, Sq, Hkv, topk] (fixed length) or
+ *              [total_q, Hkv, topk] (varlen); a block index or -1 (unused).
+ *              A token's blocks must be distinct (a repeated block is
+ *              counted twice).  Blocks past the sequence or with no causally
+ *              visible key contribute nothing.
+ *   total_q    varlen: rows of q (cu_seqlens_q[B] <= total_q); ignored for
+ *              fixed length.
+ *   topk       >= 1.   block_size  64.
+ *   o, lse     as bsa_fwd (lse [B, Hq, Sq] or [Hq, total_q]).
+ *   workspace  bsa_selected_workspace_size bytes, 256-byte aligned: list
+ *              counts and offsets, the inverted lists, and topk float32
+ *              partials of every (token, head).
+ * Needs D == 128 and Hq / Hkv dividing 128, at most 16.
+ * Errors: as bsa_fwd; BSA_ERR_WORKSPACE for a missing or small workspace. */
+size_t bsa_selected_workspace_size(const bsa_problem* prob, int32_t total_q, int32_t topk, int32_t block_size);
+bsa_status bsa_fwd_selected(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, bsa_tensor v, const int32_t* sel,
+                            int32_t total_q, int32_t topk, int32_t block_size, bsa_tensor o, float* lse,
+                            void* workspace, size_t workspace_bytes, bsa_stream stream);
 
 /* BSFA threshold calibration (synthetic, one pass over calibration inputs).
  * [BSFA] Abstract (a one-time calibration learns per-layer, per-head score

@@ -25,7 +25,7 @@ BSA_PAT_DENSE, BSA_PAT_BLOCK, BSA_PAT_VS = 0, 1, 2
 EXPORTS = ("bsa_status_string", "bsa_workspace_size", "bsa_fwd", "bsa_fwd_partials", "bsa_num_partials",
            "bsa_speculative_sparse", "bsa_speculative_partials", "bsa_speculative_num_partials",
            "bsa_speculative_workspace_size", "bsa_combine", "bsa_fwd_gated", "bsfa_calibrate",
-           "vs_convert_indexes", "vs_convert_indexes_mergehead")
+           "bsa_selected_workspace_size", "bsa_fwd_selected", "vs_convert_indexes", "vs_convert_indexes_mergehead")
 
 
 class BSAError(RuntimeError):
@@ -97,6 +97,13 @@ def load(path: str = LIB_PATH):
     lib.bsa_fwd_gated.argtypes = [ctypes.POINTER(_Problem), _Tensor, _Tensor, _Tensor, ctypes.c_void_p,
                                   ctypes.c_int32, ctypes.c_int32, _Tensor, ctypes.c_void_p, ctypes.c_void_p,
                                   ctypes.c_void_p, ctypes.c_void_p]
+    lib.bsa_selected_workspace_size.restype = ctypes.c_size_t
+    lib.bsa_selected_workspace_size.argtypes = [ctypes.POINTER(_Problem), ctypes.c_int32, ctypes.c_int32,
+                                                ctypes.c_int32]
+    lib.bsa_fwd_selected.restype = ctypes.c_int
+    lib.bsa_fwd_selected.argtypes = [ctypes.POINTER(_Problem), _Tensor, _Tensor, _Tensor, ctypes.c_void_p,
+                                     ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _Tensor, ctypes.c_void_p,
+                                     ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.bsfa_calibrate.restype = ctypes.c_int
     lib.bsfa_calibrate.argtypes = [ctypes.POINTER(_Problem), _Tensor, _Tensor, ctypes.c_int32, ctypes.c_void_p,
                                    ctypes.c_void_p, ctypes.c_void_p]
@@ -340,6 +347,42 @@ def bsa_fwd_gated(q, k, v, T: torch.Tensor, *, block_M: int = 128, block_N: int 
                            _tensor(out), _ptr(lse), _ptr(keep), _ptr(tmax), _stream(stream))
     _check("bsa_fwd_gated", st)
     return out, lse, keep, tmax
+
+
+def bsa_fwd_selected(q, k, v, sel: torch.Tensor, *, block_size: int = 64, causal: bool = True,
+                     softmax_scale=None, softcap: float = 0.0, out: Optional[torch.Tensor] = None,
+                     out_dtype: torch.dtype = torch.bfloat16, lse: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None, cu_seqlens_q=None, cu_seqlens_k=None,
+                     max_seqlen_q: int = 0, max_seqlen_k: int = 0, stream=None):
+    """Selected attention: each query token attends to the key blocks it selected.
+    sel int32 [B, Sq, Hkv, topk] (varlen: [total_q, Hkv, topk]), -1 = unused slot.
+    Returns (out, lse) as bsa_fwd."""
+    lib = load()
+    varlen = cu_seqlens_q is not None
+    prob = _problem(q, k, causal, softmax_scale, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, softcap)
+    sel = _i32(sel, "sel")
+    topk = sel.shape[-1]
+    total_q = q.shape[0] if varlen else 0
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    if lse is None:
+        shape = (q.shape[1], q.shape[0]) if varlen else (q.shape[0], q.shape[2], q.shape[1])
+        lse = torch.empty(shape, dtype=torch.float32, device=q.device)
+    need = int(lib.bsa_selected_workspace_size(ctypes.byref(prob), total_q, topk, block_size))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = lib.bsa_fwd_selected(ctypes.byref(prob), _tensor(q, varlen), _tensor(k, varlen), _tensor(v, varlen),
+                              _ptr(sel), total_q, topk, block_size, _tensor(out, varlen), _ptr(lse), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("bsa_fwd_selected", st)
+    return out, lse
+
+
+def bsa_selected_workspace_size(q, k, topk: int, *, block_size: int = 64, cu_seqlens_q=None, cu_seqlens_k=None,
+                                max_seqlen_q: int = 0, max_seqlen_k: int = 0) -> int:
+    prob = _problem(q, k, True, None, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
+    total_q = q.shape[0] if cu_seqlens_q is not None else 0
+    return int(load().bsa_selected_workspace_size(ctypes.byref(prob), total_q, int(topk), int(block_size)))
 
 
 def bsfa_calibrate(q, k, k_keep: int, *, softmax_scale=None, tile_max: Optional[torch.Tensor] = None,

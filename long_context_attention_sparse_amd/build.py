@@ -21,6 +21,7 @@ SOURCES = [
     # the tile kernels never create NaNs (masked scores are -inf, handled explicitly), so
     # max needs no NaN-quieting canonicalisation: plain v_max/v_max3 in the softmax
     ("kernels_tile.hip", ["-fno-honor-nans", "-mno-amdgpu-ieee"]),
+    ("kernels_select.hip", ["-fno-honor-nans", "-mno-amdgpu-ieee"]),
 ]
 
 HIP_FLAGS = [

@@ -88,6 +88,30 @@ struct GatedArgs {
   int n_items;
 };
 
+// Selected attention (top-k key blocks per query token, key-block-outer).  Tokens are
+// numbered t = b * Sq + position (fixed length) or by their packed index (varlen); a
+// selection entry is sel[(t * Hkv + hkv) * topk + slot], a key block of the token's own
+// sequence or -1.
+struct SelArgs {
+  TensorArg q, k, v;
+  const int32_t* sel;
+  const int32_t* cu_q;   // varlen prefix sums or null
+  const int32_t* cu_k;
+  int B, Hq, Hkv, G, Sq, Sk;  // Sq/Sk: lengths (varlen: maxima)
+  int T;                      // query tokens
+  int topk, nkb, tpc;         // key blocks per (b, kv head); tokens per chunk (128 / G)
+  int causal;
+  float scale_log2, cap_in, cap_out;
+  int32_t* counts;       // [B * Hkv * nkb]
+  int32_t* offsets;      // [B * Hkv * nkb + 1]
+  int32_t* cursor;       // [B * Hkv * nkb]
+  int32_t* chunkp;       // [B * Hkv * nkb + 1] prefix sums of chunks
+  int32_t* entries;      // [T * Hkv * topk]: t * topk + slot, grouped by key block
+  float* part_o;         // [topk, Bc, Sc, Hq, D]
+  float* part_lse;       // [topk, Bc, Hq, Sc]
+  int Bc, Sc;            // partial layout: (B, Sq) fixed length, (1, T) varlen
+};
+
 struct ThresholdArgs {
   const float* tmax;  // [B, Hq, nqb, nqb] scaled tile maxima (j < i read)
   float* T;           // [Hq, nqb]

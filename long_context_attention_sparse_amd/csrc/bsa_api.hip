@@ -539,6 +539,112 @@ bsa_status bsa_fwd_gated(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, bs
   return launch_status();
 }
 
+// ---------------------------------------------------------------------------
+// Selected attention (top-k key blocks per query token)
+// ---------------------------------------------------------------------------
+
+namespace {
+
+struct SelLayout {
+  int T = 0, nkb = 0, n_lists = 0, Bc = 0, Sc = 0;
+  size_t counts = 0, offsets = 0, cursor = 0, chunkp = 0, entries = 0, part_o = 0, part_lse = 0, total = 0;
+};
+
+constexpr int kSelD = 128;  // head dim of the selected-attention kernel
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace carve-up; total == 0 for shapes outside the supported set.
+SelLayout sel_layout(const bsa_problem& p, int32_t total_q, int32_t topk) {
+  SelLayout L;
+  if (p.B <= 0 || p.Hq <= 0 || p.Hkv <= 0 || p.Hq % p.Hkv || topk < 1) return L;
+  const bool varlen = p.cu_seqlens_q != nullptr;
+  const int64_t T = varlen ? (int64_t)total_q : (int64_t)p.B * p.Sq;
+  const int kmax = varlen ? p.max_seqlen_k : p.Sk;
+  if (T <= 0 || kmax <= 0) return L;
+  const int64_t nkb = (kmax + 63) / 64;
+  const int64_t n_lists = (int64_t)p.B * p.Hkv * nkb;
+  const int64_t pairs = T * p.Hkv * topk;
+  if (T * topk >= INT_MAX || pairs >= INT_MAX || n_lists >= INT_MAX / 2) return L;
+  L.T = (int)T;
+  L.nkb = (int)nkb;
+  L.n_lists = (int)n_lists;
+  L.Bc = varlen ? 1 : p.B;
+  L.Sc = varlen ? (int)T : p.Sq;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t at = off; off = align256(off + bytes); return at; };
+  L.counts = take(sizeof(int32_t) * n_lists);
+  L.offsets = take(sizeof(int32_t) * (n_lists + 1));
+  L.cursor = take(sizeof(int32_t) * n_lists);
+  L.chunkp = take(sizeof(int32_t) * (n_lists + 1));
+  L.entries = take(sizeof(int32_t) * pairs);
+  L.part_o = take(sizeof(float) * (size_t)topk * T * p.Hq * kSelD);
+  L.part_lse = take(sizeof(float) * (size_t)topk * T * p.Hq);
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+size_t bsa_selected_workspace_size(const bsa_problem* prob, int32_t total_q, int32_t topk, int32_t block_size) {
+  if (!prob || block_size != 64) return 0;
+  return sel_layout(*prob, total_q, topk).total;
+}
+
+bsa_status bsa_fwd_selected(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, bsa_tensor v, const int32_t* sel,
+                            int32_t total_q, int32_t topk, int32_t block_size, bsa_tensor o, float* lse, void* ws,
+                            size_t ws_bytes, bsa_stream stream) {
+  bsa_status st = check_problem(prob, q, k, v, o);
+  if (st != BSA_OK) return st;
+  const bsa_problem& p = *prob;
+  if (!sel || topk < 1) return BSA_ERR_INVALID_ARG;
+  if (p.cu_seqlens_q && total_q <= 0) return BSA_ERR_INVALID_ARG;
+  const int G = p.Hq / p.Hkv;
+  if (p.D != 128 || block_size != 64 || G > 16 || 128 % G) return BSA_ERR_UNSUPPORTED;
+  const SelLayout L = sel_layout(p, total_q, topk);
+  if (L.total == 0) return BSA_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < L.total || (reinterpret_cast<uintptr_t>(ws) & 255)) return BSA_ERR_WORKSPACE;
+  char* base = reinterpret_cast<char*>(ws);
+  SelArgs a{};
+  a.q = targ(q);
+  a.k = targ(k);
+  a.v = targ(v);
+  a.sel = sel;
+  a.cu_q = p.cu_seqlens_q;
+  a.cu_k = p.cu_seqlens_k;
+  a.B = p.B;
+  a.Hq = p.Hq;
+  a.Hkv = p.Hkv;
+  a.G = G;
+  a.Sq = p.cu_seqlens_q ? p.max_seqlen_q : p.Sq;
+  a.Sk = p.cu_seqlens_q ? p.max_seqlen_k : p.Sk;
+  a.T = L.T;
+  a.topk = topk;
+  a.nkb = L.nkb;
+  a.tpc = 128 / G;
+  a.causal = p.causal;
+  a.scale_log2 = scale_of(p) * kLog2e;
+  cap_consts(p, a.cap_in, a.cap_out);
+  a.counts = reinterpret_cast<int32_t*>(base + L.counts);
+  a.offsets = reinterpret_cast<int32_t*>(base + L.offsets);
+  a.cursor = reinterpret_cast<int32_t*>(base + L.cursor);
+  a.chunkp = reinterpret_cast<int32_t*>(base + L.chunkp);
+  a.entries = reinterpret_cast<int32_t*>(base + L.entries);
+  a.part_o = reinterpret_cast<float*>(base + L.part_o);
+  a.part_lse = reinterpret_cast<float*>(base + L.part_lse);
+  a.Bc = L.Bc;
+  a.Sc = L.Sc;
+  // chunks <= sum over lists of (count / tpc + 1) <= pairs / tpc + lists
+  const int64_t grid = ((int64_t)L.T * p.Hkv * topk + a.tpc - 1) / a.tpc + L.n_lists;
+  if (grid > INT_MAX) return BSA_ERR_UNSUPPORTED;
+  const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  launch_selected(a, (int)grid, hs);
+  if (hipPeekAtLastError() != hipSuccess) return launch_status();
+  CombineArgs c{topk, L.Bc, p.Hq, L.Sc, kSelD, a.part_o, a.part_lse, oarg(o), lse};
+  launch_combine(c, hs);
+  return launch_status();
+}
+
 bsa_status bsfa_calibrate(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, int32_t k_keep, float* tile_max,
                           float* T, bsa_stream stream) {
   if (!prob || !q.ptr || !k.ptr || !tile_max || !T || k_keep < 1) return BSA_ERR_INVALID_ARG;

@@ -1,6 +1,6 @@
-// Host-side launch wrappers, one per kernel family, defined in the translation unit
-// that instantiates the kernels (kernels_stream.hip, kernels_tile.hip) so that each
-// family is compiled with its own code-generation flags.
+// Host-side launch wrappers, one per kernel family, defined in the translation unit that
+// instantiates the kernels (kernels_stream.hip, kernels_tile.hip, kernels_select.hip) so
+// that each family is compiled with its own code-generation flags.
 #pragma once
 #include <hip/hip_runtime.h>
 
@@ -20,5 +20,9 @@ void launch_prefill(const PrefillArgs& a, int NW, int KIND, hipStream_t st);
 void launch_gated(const GatedArgs& a, bool calib, hipStream_t st);
 // threshold_kernel: grid (nqb, Hq), 256 threads; nqb <= kThreshMaxCand.
 void launch_threshold(const ThresholdArgs& a, hipStream_t st);
+
+// selected attention: sel_zero, sel_count, sel_scan, sel_fill, then selected_kernel over
+// main_grid workgroups (an upper bound on the chunks; the surplus exits at once).
+void launch_selected(const SelArgs& a, int main_grid, hipStream_t st);
 
 }  // namespace bsa

@@ -145,6 +145,21 @@ def test_gated_and_vs_convert_errors(lib):
         == bd.BSA_ERR_UNSUPPORTED                                                            # S % 128
     assert cal(ctypes.byref(_prob(Hq=2, Hkv=2, Sq=4097 * 128, Sk=4097 * 128, causal=1)), q, _t(), 2, T, T,
                None) == bd.BSA_ERR_UNSUPPORTED                                               # rows too long
+    # selected attention
+    sp = _prob(Hq=4, Hkv=2, Sq=256, Sk=256, causal=1)
+    qs = _t(sb=256 * 4 * 128, ss=4 * 128)
+    ws = lib.bsa_selected_workspace_size(ctypes.byref(sp), 0, 8, 64)
+    assert ws > 8 * 256 * 4 * 128 * 4                                # the float32 partials alone
+    assert lib.bsa_selected_workspace_size(ctypes.byref(sp), 0, 8, 128) == 0
+    fs = lib.bsa_fwd_selected
+    assert fs(ctypes.byref(sp), qs, _t(), _t(), None, 0, 8, 64, qs, None, 256, ws, None) == bd.BSA_ERR_INVALID_ARG
+    assert fs(ctypes.byref(sp), qs, _t(), _t(), 16, 0, 0, 64, qs, None, 256, ws, None) == bd.BSA_ERR_INVALID_ARG
+    assert fs(ctypes.byref(sp), qs, _t(), _t(), 16, 0, 8, 32, qs, None, 256, ws, None) == bd.BSA_ERR_UNSUPPORTED
+    assert fs(ctypes.byref(sp), qs, _t(), _t(), 16, 0, 8, 64, qs, None, 256, ws - 1, None) == bd.BSA_ERR_WORKSPACE
+    assert fs(ctypes.byref(sp), qs, _t(), _t(), 16, 0, 8, 64, qs, None, 16, ws, None) == bd.BSA_ERR_WORKSPACE
+    assert fs(ctypes.byref(_prob(Hq=32, Hkv=1, Sq=256, Sk=256, causal=1)), _t(sb=256 * 32 * 128, ss=32 * 128),
+              _t(), _t(), 16, 0, 8, 64, _t(sb=256 * 32 * 128, ss=32 * 128), None, 256, ws, None) \
+        == bd.BSA_ERR_UNSUPPORTED                                                            # group of 32
     sc = _prob(Hq=2, Hkv=2, Sq=256, Sk=256, causal=1, softcap=30.0)
     assert lib.bsa_fwd_gated(ctypes.byref(sc), q, _t(), _t(), T, 128, 128, q, None, None, None, None) \
         == bd.BSA_ERR_UNSUPPORTED
