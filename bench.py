@@ -32,7 +32,7 @@ def _args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5, 6])
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
@@ -504,6 +504,72 @@ def bench_vs(torch, bsa, args):
                 cpu_baseline=None)
 
 
+# ---------------------------------------------------------------------------
+# Selected attention (top-k key blocks per query token), the FSA module's example shape
+# ---------------------------------------------------------------------------
+
+def bench_selected(torch, bsa, args):
+    from synth import to_torch_bf16
+    from synth.workloads import selected_prefill
+
+    _log("generating selected-attention inputs")
+    w = selected_prefill()
+    dev = torch.device("cuda:0")
+    q, k, v = (to_torch_bf16(w[n]).to(dev) for n in ("q", "k", "v"))
+    sel = torch.from_numpy(w["sel"]).to(dev)
+    cu = torch.from_numpy(w["cu_seqlens"]).to(dev)
+    Hq, Hkv, topk, T = w["Hq"], w["Hkv"], w["topk"], q.shape[0]
+    G = Hq // Hkv
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((Hq, T), dtype=torch.float32, device=dev)
+    ws = torch.empty(bsa.bsa_selected_workspace_size(q, k, topk, cu_seqlens_q=cu, cu_seqlens_k=cu,
+                                                     max_seqlen_q=w["max_seqlen"], max_seqlen_k=w["max_seqlen"]),
+                     dtype=torch.uint8, device=dev)
+
+    def call():
+        bsa.bsa_fwd_selected(q, k, v, sel, out=out, lse=lse, workspace=ws, cu_seqlens_q=cu, cu_seqlens_k=cu,
+                             max_seqlen_q=w["max_seqlen"], max_seqlen_k=w["max_seqlen"])
+
+    def step(timer):
+        with timer.span("selected"):
+            call()
+
+    timer = Timer(torch)
+    ms = run_steps(torch, step, timer, args.steps, args.warmup)
+    call_ms = kernel_mean_ms(torch, call)
+    # work the call must do: every selection here is valid (the generator draws causal blocks)
+    s_np = w["sel"]
+    pairs = int((s_np >= 0).sum())
+    empty = int(s_np.size - pairs)
+    flops = pairs * G * 4 * 64 * 128
+    lists = np.zeros(0, np.int64)
+    nkb = -(-w["max_seqlen"] // 64)
+    for b in range(len(w["seqlens"])):
+        a0, a1 = int(w["cu_seqlens"][b]), int(w["cu_seqlens"][b + 1])
+        for hk in range(Hkv):
+            blk = s_np[a0:a1, hk][s_np[a0:a1, hk] >= 0]
+            lists = np.concatenate([lists, np.bincount(blk, minlength=nkb)])
+    tpc = 128 // G
+    chunks = int(((lists + tpc - 1) // tpc).sum())
+    row = 128 * 4 + 4                                         # a float32 partial (o, lse)
+    alg_bytes = (pairs * (G * 256 + G * row + 2 * 4)          # gathered Q rows, partials, sel + list entry
+                 + empty * (G * row + 4)                      # neutral partials of unused slots
+                 + chunks * 64 * 256 * 2                      # one K and V tile per chunk
+                 + T * Hq * (topk * row + 128 * 2 + 4))       # combine: read partials, write O (bf16), LSE
+    gbs = alg_bytes / (call_ms * 1e-3) / 1e9
+    return dict(metric=METRIC, value=round(flops / (ms * 1e-3) / 1e12, 2), unit="TFLOP/s", ms_per_step=round(ms, 4),
+                dtype="bf16",
+                config={"workload": "selected attention, top-k key blocks per query token (key-block-outer)",
+                        "seqlens": [int(x) for x in w["seqlens"]], "Hq": Hq, "Hkv": Hkv, "D": 128, "block": 64,
+                        "topk": topk, "valid_pairs": pairs, "chunks": chunks, "flops": flops,
+                        "algorithmic_bytes": alg_bytes},
+                roofline={"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                          "kernel": "bsa_fwd_selected (index inversion, selected_kernel, combine)",
+                          "avg_ms": round(call_ms, 4)},
+                cpu_baseline=None)
+
+
 def main():
     args = _args()
     if args.gpus != 1:
@@ -528,7 +594,8 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "copies": 4}), flush=True)
         return
-    fn = {1: bench_tiny, 2: bench_spec_decode, 3: bench_block_prefill, 4: bench_gated, 5: bench_vs}[args.config]
+    fn = {1: bench_tiny, 2: bench_spec_decode, 3: bench_block_prefill, 4: bench_gated, 5: bench_vs,
+          6: bench_selected}[args.config]
     res = fn(torch, bsa, args)
     line = {"metric": res["metric"], "value": res["value"], "unit": res["unit"], "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": res["ms_per_step"],

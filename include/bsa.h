@@ -210,6 +210,8 @@ size_t bsa_speculative_workspace_size(const bsa_problem* prob, int32_t Sk_spec, 
  * identity FA(A u B) == Combine(FA(A), FA(B))) and Usage 2.
  * For each (b, h, s): m = max_p lse_p; if m = -inf the result is (0, -inf);
  * else w_p = exp(lse_p - m), O = sum w_p o_p / sum w_p, LSE = m + ln sum w_p.
+ * A partial with lse -inf has weight 0 and its o_p is not used (it may hold
+ * anything, NaN included).
  *   o_part    float32 [P, B, Sq, Hq, D] contiguous.
  *   lse_part  float32 [P, B, Hq, Sq] contiguous.
  *   o         output view [B, Sq, Hq, D] (bf16 or f32); lse float32
@@ -254,14 +256,15 @@ bsa_status bsa_fwd_gated(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, bs
  *              A token's blocks must be distinct (a repeated block is
  *              counted twice).  Blocks past the sequence or with no causally
  *              visible key contribute nothing.
- *   total_q    varlen: rows of q (cu_seqlens_q[B] <= total_q); ignored for
+ *   total_q    varlen: rows of q, equal to cu_seqlens_q[B]; ignored for
  *              fixed length.
  *   topk       >= 1.   block_size  64.
  *   o, lse     as bsa_fwd (lse [B, Hq, Sq] or [Hq, total_q]).
  *   workspace  bsa_selected_workspace_size bytes, 256-byte aligned: list
  *              counts and offsets, the inverted lists, and topk float32
  *              partials of every (token, head).
- * Needs D == 128 and Hq / Hkv dividing 128, at most 16.
+ * Needs D == 128, Hq / Hkv dividing 128 (at most 16), and sequences of at
+ * most 8192 key blocks (524288 keys).
  * Errors: as bsa_fwd; BSA_ERR_WORKSPACE for a missing or small workspace. */
 size_t bsa_selected_workspace_size(const bsa_problem* prob, int32_t total_q, int32_t topk, int32_t block_size);
 bsa_status bsa_fwd_selected(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, bsa_tensor v, const int32_t* sel,

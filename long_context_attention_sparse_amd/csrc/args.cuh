@@ -30,6 +30,8 @@ constexpr int kDecodeEntsLds = 256;    // block ids of a decode split staged in 
 constexpr int kVSConvThreads = 64;     // conversion workgroup size (one query block per thread)
 constexpr int kVSConvLdsInts = 16384;  // slash + vertical entries staged in LDS (longer lists stay in global)
 constexpr int kThreshMaxCand = 4096;   // threshold selection: query blocks per row (LDS candidates)
+constexpr int kSelTile = 1024;         // selected attention: token positions per index workgroup
+constexpr int kSelMaxBlocks = 8192;    // selected attention: key blocks per sequence (LDS histogram)
 
 struct DecodeSeg {
   TensorArg k, v;

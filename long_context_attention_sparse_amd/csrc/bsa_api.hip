@@ -563,6 +563,7 @@ SelLayout sel_layout(const bsa_problem& p, int32_t total_q, int32_t topk) {
   const int kmax = varlen ? p.max_seqlen_k : p.Sk;
   if (T <= 0 || kmax <= 0) return L;
   const int64_t nkb = (kmax + 63) / 64;
+  if (nkb > kSelMaxBlocks) return L;
   const int64_t n_lists = (int64_t)p.B * p.Hkv * nkb;
   const int64_t pairs = T * p.Hkv * topk;
   if (T * topk >= INT_MAX || pairs >= INT_MAX || n_lists >= INT_MAX / 2) return L;

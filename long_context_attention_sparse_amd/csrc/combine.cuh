@@ -53,7 +53,8 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 #pragma unroll
       for (int j = 0; j < BATCH; ++j) {
         const float wgt = expf(lv[j] - m);
-        // a partial with no keys contributes nothing (its weight is exactly 0)
+        // a partial with no keys contributes nothing (its weight is exactly 0), and its o is
+        // never used (it may hold anything)
         if (wgt != 0.f) {
           acc += wgt * ov[j];
           wsum += wgt;

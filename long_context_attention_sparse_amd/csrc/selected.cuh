@@ -8,13 +8,14 @@
 // for small G), the selections are inverted into per-key-block token lists and one
 // workgroup takes a key block and up to 128 / G of the tokens that selected it:
 //   sel_zero   counts = 0
-//   sel_count  count the valid (token, slot) pairs of every (b, kv head, key block);
-//              invalid slots (-1, past the sequence, no causally visible key) get the
-//              neutral partial (0, -inf) right away
+//   sel_count  count the valid (token, slot) pairs of every (b, kv head, key block),
+//              through a per-tile LDS histogram; invalid slots (-1, past the sequence,
+//              no causally visible key) get an empty partial (LSE -inf) right away
 //   sel_scan   exclusive prefix sums of the counts (list offsets) and of the chunks
 //              per list (ceil(count / (128 / G))), one workgroup
-//   sel_fill   scatter t * topk + slot into the lists (the order inside a list is not
-//              fixed; a row's result does not depend on its place in the MFMA tile)
+//   sel_fill   scatter t * topk + slot into the lists, one reservation per (tile, block)
+//              (the order inside a list is not fixed; a row's result does not depend on
+//              its place in the MFMA tile)
 //   selected   one 64-key block per workgroup: K and V straight into swizzled LDS, the
 //              gathered Q rows as the MFMA B operand, S^T = K Q^T, mask, softmax of the
 //              64 scores, O^T = V^T P^T, one (o, lse) partial per (token, slot, head)
@@ -23,23 +24,6 @@
 #include "tile.cuh"
 
 namespace bsa {
-
-// Sequence and position of query token t.
-__device__ __forceinline__ void sel_token(const SelArgs& a, int t, int& b, int& pos) {
-  if (a.cu_q) {
-    int lo = 0, hi = a.B;  // largest b with cu_q[b] <= t
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (a.cu_q[mid] <= t) lo = mid;
-      else hi = mid;
-    }
-    b = lo;
-    pos = t - a.cu_q[b];
-  } else {
-    b = t / a.Sq;
-    pos = t - b * a.Sq;
-  }
-}
 
 __device__ __forceinline__ void sel_lengths(const SelArgs& a, int b, int& q_len, int& kv_len, int& k_start) {
   if (a.cu_q) {
@@ -63,40 +47,59 @@ __device__ __forceinline__ int64_t sel_part_lse(const SelArgs& a, int slot, int 
   return (((int64_t)slot * a.Bc + bc) * a.Hq + h) * a.Sc + pc;
 }
 
-// Key block j of entry x, or -1 when the slot selects nothing the token can see.
-__device__ __forceinline__ int sel_block(const SelArgs& a, int64_t x, int t, int& b, int& pos) {
-  sel_token(a, t, b, pos);
-  int q_len, kv_len, k_start;
-  sel_lengths(a, b, q_len, kv_len, k_start);
-  const int j = a.sel[x];
-  if (j < 0 || pos >= q_len || (int64_t)j * 64 >= kv_len) return -1;
-  if (a.causal && (int64_t)j * 64 > (int64_t)pos + (kv_len - q_len)) return -1;
-  return j;
-}
-
 __global__ __launch_bounds__(256) void sel_zero_kernel(SelArgs a) {
   const int x = wg_x() * 256 + tid_x();
   if (x < a.B * a.Hkv * a.nkb) a.counts[x] = 0;
 }
 
+// Count and fill work on tiles of kSelTile positions of one (sequence, kv head): the tile's
+// selections are histogrammed over the key blocks in LDS first, so a block every token
+// selects (the first one, the local ones) costs one global atomic per tile, not one per
+// token.  Grid: (tiles per sequence, Hkv, B); tiles past a sequence's end exit.
+__device__ __forceinline__ bool sel_tile(const SelArgs& a, int& b, int& hkv, int& p0, int& p1, int& q_len,
+                                         int& kv_len, int& t0) {
+  const int tile = __builtin_amdgcn_workgroup_id_x();
+  hkv = __builtin_amdgcn_workgroup_id_y();
+  b = __builtin_amdgcn_workgroup_id_z();
+  int k_start;
+  sel_lengths(a, b, q_len, kv_len, k_start);
+  p0 = tile * kSelTile;
+  p1 = min(q_len, p0 + kSelTile);
+  t0 = a.cu_q ? a.cu_q[b] : b * a.Sq;
+  return p0 < q_len;
+}
+
+// Key block of slot `slot` of the token at position pos, or -1 when it selects nothing the
+// token can see.
+__device__ __forceinline__ int sel_valid(const SelArgs& a, int j, int pos, int q_len, int kv_len) {
+  if (j < 0 || (int64_t)j * 64 >= kv_len) return -1;
+  if (a.causal && (int64_t)j * 64 > (int64_t)pos + (kv_len - q_len)) return -1;
+  return j;
+}
+
 __global__ __launch_bounds__(256) void sel_count_kernel(SelArgs a) {
-  const int64_t x = (int64_t)wg_x() * 256 + tid_x();
-  if (x >= (int64_t)a.T * a.Hkv * a.topk) return;
-  const int slot = (int)(x % a.topk);
-  const int64_t th = x / a.topk;
-  const int hkv = (int)(th % a.Hkv), t = (int)(th / a.Hkv);
-  int b, pos;
-  const int j = sel_block(a, x, t, b, pos);
-  if (j >= 0) {
-    atomicAdd(&a.counts[((int64_t)b * a.Hkv + hkv) * a.nkb + j], 1);
-  } else {
-    for (int g = 0; g < a.G; ++g) {
-      const int h = hkv * a.G + g;
-      float4* o = reinterpret_cast<float4*>(a.part_o + sel_part_o(a, slot, b, pos, t, h));
-      for (int d = 0; d < TD / 4; ++d) o[d] = float4{0.f, 0.f, 0.f, 0.f};
-      a.part_lse[sel_part_lse(a, slot, b, pos, t, h)] = kNegInf;
+  __shared__ int hist[kSelMaxBlocks];
+  int b, hkv, p0, p1, q_len, kv_len, t0;
+  if (!sel_tile(a, b, hkv, p0, p1, q_len, kv_len, t0)) return;  // uniform
+  const int tid = tid_x();
+  const int nkb = (kv_len + 63) / 64;
+  for (int x = tid; x < nkb; x += 256) hist[x] = 0;
+  __syncthreads();
+  const int n = (p1 - p0) * a.topk;
+  for (int e = tid; e < n; e += 256) {
+    const int pos = p0 + e / a.topk, slot = e % a.topk, t = t0 + pos;
+    const int j = sel_valid(a, a.sel[((int64_t)t * a.Hkv + hkv) * a.topk + slot], pos, q_len, kv_len);
+    if (j >= 0) {
+      atomicAdd(&hist[j], 1);
+    } else {
+      // an empty partial: LSE -inf (the combine gives it weight 0 and never uses its o)
+      for (int g = 0; g < a.G; ++g) a.part_lse[sel_part_lse(a, slot, b, pos, t, hkv * a.G + g)] = kNegInf;
     }
   }
+  __syncthreads();
+  int* counts = a.counts + ((int64_t)b * a.Hkv + hkv) * a.nkb;
+  for (int x = tid; x < nkb; x += 256)
+    if (hist[x]) atomicAdd(&counts[x], hist[x]);
 }
 
 // One workgroup of 1024 threads, four entries per thread per pass.
@@ -148,17 +151,31 @@ __global__ __launch_bounds__(1024) void sel_scan_kernel(SelArgs a) {
   }
 }
 
+// The tile's histogram again, then one global reservation per block and the entries
+// placed by their LDS rank inside it.
 __global__ __launch_bounds__(256) void sel_fill_kernel(SelArgs a) {
-  const int64_t x = (int64_t)wg_x() * 256 + tid_x();
-  if (x >= (int64_t)a.T * a.Hkv * a.topk) return;
-  const int slot = (int)(x % a.topk);
-  const int64_t th = x / a.topk;
-  const int hkv = (int)(th % a.Hkv), t = (int)(th / a.Hkv);
-  int b, pos;
-  const int j = sel_block(a, x, t, b, pos);
-  if (j >= 0) {
-    const int p = atomicAdd(&a.cursor[((int64_t)b * a.Hkv + hkv) * a.nkb + j], 1);
-    a.entries[p] = t * a.topk + slot;
+  __shared__ int hist[kSelMaxBlocks];
+  int b, hkv, p0, p1, q_len, kv_len, t0;
+  if (!sel_tile(a, b, hkv, p0, p1, q_len, kv_len, t0)) return;  // uniform
+  const int tid = tid_x();
+  const int nkb = (kv_len + 63) / 64;
+  for (int x = tid; x < nkb; x += 256) hist[x] = 0;
+  __syncthreads();
+  const int n = (p1 - p0) * a.topk;
+  for (int e = tid; e < n; e += 256) {
+    const int pos = p0 + e / a.topk, slot = e % a.topk, t = t0 + pos;
+    const int j = sel_valid(a, a.sel[((int64_t)t * a.Hkv + hkv) * a.topk + slot], pos, q_len, kv_len);
+    if (j >= 0) atomicAdd(&hist[j], 1);
+  }
+  __syncthreads();
+  int* cursor = a.cursor + ((int64_t)b * a.Hkv + hkv) * a.nkb;
+  for (int x = tid; x < nkb; x += 256)
+    if (hist[x]) hist[x] = atomicAdd(&cursor[x], hist[x]);  // first list position of this tile's run
+  __syncthreads();
+  for (int e = tid; e < n; e += 256) {
+    const int pos = p0 + e / a.topk, slot = e % a.topk, t = t0 + pos;
+    const int j = sel_valid(a, a.sel[((int64_t)t * a.Hkv + hkv) * a.topk + slot], pos, q_len, kv_len);
+    if (j >= 0) a.entries[atomicAdd(&hist[j], 1)] = t * a.topk + slot;
   }
 }
 

@@ -98,3 +98,18 @@ def test_full_size_sampled(full):
         a = int(w["cu_seqlens"][b])
         check_o(oh[a + rows, h], o_ref, f"selected full b={b} h={h}")
         check_lse(lh[h, a + rows], lse_ref, f"selected full lse b={b} h={h}")
+
+
+def test_combine_ignores_o_of_empty_partials():
+    """An empty partial (lse -inf) may hold anything in its o, NaN included: the selected path
+    writes only the LSE of unused slots and relies on this."""
+    g = rng(7, "combine")
+    P, B, S, H, D = 3, 1, 16, 2, 128
+    o_part = torch.from_numpy(g.standard_normal((P, B, S, H, D)).astype(np.float32)).cuda()
+    lse_part = torch.from_numpy(g.standard_normal((P, B, H, S)).astype(np.float32)).cuda()
+    lse_part[1] = float("-inf")
+    o_part[1] = float("nan")
+    o, lse = bsa.bsa_combine(o_part, lse_part, out_dtype=torch.float32)
+    o_ref, lse_ref = oracle.combine(host(o_part[[0, 2]]), host(lse_part[[0, 2]]))
+    check_o(host(o), o_ref, "combine with an empty NaN partial")
+    check_lse(host(lse), lse_ref, "combine with an empty NaN partial lse")
