@@ -12,6 +12,7 @@ Modules:
   gate            BSFA tile-maximum gating and threshold calibration
   vertical_slash  vertical-slash index conversion and attention over it
   selected        selected attention: each query token attends to its top-k key blocks
+  backward        gradients of block-sparse attention (dQ, dK, dV)
 
 Pinning (see the tests marked "not gpu"): every function here is checked
 against closed forms, invariants, brute force and an independent library
@@ -20,6 +21,7 @@ docstrings: the exact windows chosen by the vertical-slash conversion (own
 greedy rule; only its coverage invariants are pinned), and the treatment of
 skipped tiles' softmax mass in the gated variant (excluded).
 """
+from .backward import block_sparse_bwd
 from .core import (as_f64, attend_rows, block_mask, block_sparse, block_sparse_partials, causal_mask,
                    combine, dense, default_scale, speculative_sparse)
 from .gate import calibrate, gated, gated_rows, tile_max_row
@@ -28,7 +30,7 @@ from .selected import selected, selected_rows
 from .vertical_slash import vs_attention, vs_attention_rows, vs_convert, vs_convert_item, vs_convert_mergehead
 
 __all__ = [
-    "as_f64", "attend_rows", "block_mask", "block_sparse", "block_sparse_partials", "causal_mask",
+    "block_sparse_bwd", "as_f64", "attend_rows", "block_mask", "block_sparse", "block_sparse_partials", "causal_mask",
     "combine", "dense", "default_scale", "speculative_sparse", "gated", "gated_rows", "tile_max_row", "calibrate", "gated_density",
     "selected", "selected_rows", "vs_attention", "vs_attention_rows", "vs_convert", "vs_convert_item", "vs_convert_mergehead",
 ]
