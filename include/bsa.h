@@ -239,6 +239,31 @@ bsa_status bsa_fwd_gated(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, bs
                          int32_t block_M, int32_t block_N, bsa_tensor o, float* lse, uint8_t* keep_mask,
                          float* tile_max, bsa_stream stream);
 
+/* Backward of block-sparse attention: dQ, dK, dV.  The pages name a
+ * backward pass ([IR] keeps FA's backward; [FSA] and FlagAttention list
+ * forward + backward for their sparse kernels) without a formula; this is
+ * the plain derivative of bsa_fwd's result over the same key sets: with
+ * P = exp(scale Q K^T - LSE) on the key set, D = rowsum(dO * O),
+ * dS = P * (dO V^T - D): dV = P^T dO, dQ = scale dS K, dK = scale dS^T Q
+ * (summed over the query heads of a kv head).
+ *   pat        NULL / dense or BSA_PAT_BLOCK (as bsa_fwd; block_M and block_N
+ *              64 or 128); fixed length, D == 128, no softcap.
+ *   o, lse     bsa_fwd's output (bf16 or float32) and LSE for the same call.
+ *   dout       bf16, the layout of q.
+ *   dq         device float32 [B, Sq, Hq, D] contiguous; dk, dv float32
+ *              [B, Sk, Hkv, D] contiguous; every entry is written.
+ *   workspace  bsa_bwd_workspace_size bytes, 256-byte aligned (row dots and,
+ *              for block patterns, the per-key-block lists).
+ * dK and dV come from one workgroup per 64 keys, dQ from one per query
+ * block: no atomics on the gradients; the order in which a key block's
+ * (head, query block) pairs are visited may change from run to run, so dK
+ * and dV may differ in the last float32 bits between runs.
+ * Errors: as bsa_fwd; BSA_ERR_UNSUPPORTED outside the cases above. */
+size_t bsa_bwd_workspace_size(const bsa_problem* prob, const bsa_pattern* pat);
+bsa_status bsa_bwd(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, bsa_tensor v, const bsa_pattern* pat,
+                   bsa_tensor o, const float* lse, bsa_tensor dout, float* dq, float* dk, float* dv,
+                   void* workspace, size_t workspace_bytes, bsa_stream stream);
+
 /* Selected attention: every query token attends to the key blocks it selected.
  * [FSA] Abstract and the Flash-Sparse-Attention README page (main features:
  * a batched query-to-KV kernel, a reduction and an online-softmax pass, no

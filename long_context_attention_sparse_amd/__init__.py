@@ -10,6 +10,7 @@ include/bsa.h and only marshals arguments — the kernels do all the work:
   bsa_fwd_gated       BSFA gated causal attention (tile max vs threshold)
   bsfa_calibrate      BSFA thresholds: k-th largest off-diagonal tile maximum per row
   bsa_fwd_selected    selected attention: each query token over its top-k key blocks
+  bsa_bwd             gradients (dQ, dK, dV) of bsa_fwd over dense or block patterns
   vs_convert_indexes  vertical-slash index conversion
   vs_convert_indexes_mergehead  the same with per-head counts of valid indices
   speculative_sparse  speculative pass + sparse repair pass + combine
@@ -17,13 +18,13 @@ include/bsa.h and only marshals arguments — the kernels do all the work:
                       the combine)
 """
 from ._binding import (EXPORTS, LIB_PATH, BlockPattern, BSAError, VSPattern, bsa_combine, bsa_fwd, bsa_fwd_gated,
-                       bsa_fwd_selected, bsa_selected_workspace_size, bsfa_calibrate,
+                       bsa_bwd, bsa_fwd_selected, bsa_selected_workspace_size, bsfa_calibrate,
                        bsa_fwd_partials, bsa_num_partials, bsa_speculative_partials, bsa_workspace_size, load,
                        speculative_sparse, vs_convert_indexes,
                        vs_convert_indexes_mergehead)
 
 __all__ = ["EXPORTS", "LIB_PATH", "BlockPattern", "BSAError", "VSPattern", "bsa_combine", "bsa_fwd", "bsa_fwd_gated",
-           "bsa_fwd_selected", "bsa_selected_workspace_size", "bsfa_calibrate",
+           "bsa_bwd", "bsa_fwd_selected", "bsa_selected_workspace_size", "bsfa_calibrate",
            "bsa_fwd_partials", "bsa_num_partials", "bsa_speculative_partials", "bsa_workspace_size", "load",
            "speculative_sparse", "vs_convert_indexes",
            "vs_convert_indexes_mergehead"]

@@ -25,7 +25,8 @@ BSA_PAT_DENSE, BSA_PAT_BLOCK, BSA_PAT_VS = 0, 1, 2
 EXPORTS = ("bsa_status_string", "bsa_workspace_size", "bsa_fwd", "bsa_fwd_partials", "bsa_num_partials",
            "bsa_speculative_sparse", "bsa_speculative_partials", "bsa_speculative_num_partials",
            "bsa_speculative_workspace_size", "bsa_combine", "bsa_fwd_gated", "bsfa_calibrate",
-           "bsa_selected_workspace_size", "bsa_fwd_selected", "vs_convert_indexes", "vs_convert_indexes_mergehead")
+           "bsa_selected_workspace_size", "bsa_fwd_selected", "bsa_bwd_workspace_size", "bsa_bwd",
+           "vs_convert_indexes", "vs_convert_indexes_mergehead")
 
 
 class BSAError(RuntimeError):
@@ -104,6 +105,12 @@ def load(path: str = LIB_PATH):
     lib.bsa_fwd_selected.argtypes = [ctypes.POINTER(_Problem), _Tensor, _Tensor, _Tensor, ctypes.c_void_p,
                                      ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _Tensor, ctypes.c_void_p,
                                      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.bsa_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.bsa_bwd_workspace_size.argtypes = [ctypes.POINTER(_Problem), ctypes.POINTER(_Pattern)]
+    lib.bsa_bwd.restype = ctypes.c_int
+    lib.bsa_bwd.argtypes = [ctypes.POINTER(_Problem), _Tensor, _Tensor, _Tensor, ctypes.POINTER(_Pattern), _Tensor,
+                            ctypes.c_void_p, _Tensor, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                            ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.bsfa_calibrate.restype = ctypes.c_int
     lib.bsfa_calibrate.argtypes = [ctypes.POINTER(_Problem), _Tensor, _Tensor, ctypes.c_int32, ctypes.c_void_p,
                                    ctypes.c_void_p, ctypes.c_void_p]
@@ -347,6 +354,29 @@ def bsa_fwd_gated(q, k, v, T: torch.Tensor, *, block_M: int = 128, block_N: int 
                            _tensor(out), _ptr(lse), _ptr(keep), _ptr(tmax), _stream(stream))
     _check("bsa_fwd_gated", st)
     return out, lse, keep, tmax
+
+
+def bsa_bwd(q, k, v, out, lse, dout, pattern=None, *, causal: bool = False, softmax_scale=None,
+            workspace: Optional[torch.Tensor] = None, stream=None):
+    """Gradients of bsa_fwd(q, k, v, pattern, causal=...) given its (out, lse) and the upstream
+    gradient dout.  Returns dq [B, Sq, Hq, D], dk and dv [B, Sk, Hkv, D] (float32)."""
+    lib = load()
+    prob = _problem(q, k, causal, softmax_scale)
+    pat = pattern.struct(prob.Hq) if pattern is not None else None
+    pat_p = ctypes.byref(pat) if pat is not None else None
+    dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
+    dv = torch.empty(v.shape, dtype=torch.float32, device=q.device)
+    if lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B, Hq, Sq]")
+    need = int(lib.bsa_bwd_workspace_size(ctypes.byref(prob), pat_p))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    st = lib.bsa_bwd(ctypes.byref(prob), _tensor(q), _tensor(k), _tensor(v), pat_p, _tensor(out), _ptr(lse),
+                     _tensor(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                     workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("bsa_bwd", st)
+    return dq, dk, dv
 
 
 def bsa_fwd_selected(q, k, v, sel: torch.Tensor, *, block_size: int = 64, causal: bool = True,

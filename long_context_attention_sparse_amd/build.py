@@ -22,6 +22,7 @@ SOURCES = [
     # max needs no NaN-quieting canonicalisation: plain v_max/v_max3 in the softmax
     ("kernels_tile.hip", ["-fno-honor-nans", "-mno-amdgpu-ieee"]),
     ("kernels_select.hip", ["-fno-honor-nans", "-mno-amdgpu-ieee"]),
+    ("kernels_bwd.hip", ["-fno-honor-nans", "-mno-amdgpu-ieee"]),
 ]
 
 HIP_FLAGS = [

@@ -32,6 +32,7 @@ constexpr int kVSConvLdsInts = 16384;  // slash + vertical entries staged in LDS
 constexpr int kThreshMaxCand = 4096;   // threshold selection: query blocks per row (LDS candidates)
 constexpr int kSelTile = 1024;         // selected attention: token positions per index workgroup
 constexpr int kSelMaxBlocks = 8192;    // selected attention: key blocks per sequence (LDS histogram)
+constexpr int kBwdMaxSub = 8192;       // backward: 64-key sub-blocks per sequence (LDS histogram)
 
 struct DecodeSeg {
   TensorArg k, v;
@@ -112,6 +113,29 @@ struct SelArgs {
   float* part_o;         // [topk, Bc, Sc, Hq, D]
   float* part_lse;       // [topk, Bc, Hq, Sc]
   int Bc, Sc;            // partial layout: (B, Sq) fixed length, (1, T) varlen
+};
+
+// Backward of block-sparse attention (fixed length, head dim 128).
+struct BwdArgs {
+  TensorArg q, k, v, o, dout;  // o may be bf16 or float32 (o_f32)
+  int o_f32;
+  const float* lse;            // [B, Hq, Sq] natural log
+  float* dq;                   // [B, Sq, Hq, D] float32, contiguous
+  float* dk;                   // [B, Sk, Hkv, D] float32, contiguous
+  float* dv;
+  float* dsum;                 // [B, Hq, Sq]: sum_d dO * O
+  PatternArg pat;              // kind 0 dense or 1 block lists
+  int B, Hq, Hkv, G, Sq, Sk;
+  int list_by_kv;
+  int causal;
+  float scale, scale_log2;
+  int BM;                      // query block rows of the pattern (64 or 128; dense: 128)
+  int nqb, nks;                // query blocks; 64-key sub-blocks
+  // key-sub-block lists of (query head, query block) pairs (block patterns)
+  int32_t* counts;             // [B * Hkv * nks]
+  int32_t* offsets;            // [B * Hkv * nks + 1]
+  int32_t* cursor;             // [B * Hkv * nks]
+  int32_t* entries;            // h * nqb + i
 };
 
 struct ThresholdArgs {

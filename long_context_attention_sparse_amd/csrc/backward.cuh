@@ -1,0 +1,457 @@
+// Backward of block-sparse attention: dQ, dK, dV of softmax attention restricted to the
+// listed key blocks (the plain derivative of the forward; the "Sparse FlashAttention with
+// Incremental Repair" README keeps FA's backward, the FSA and FlagAttention pages list
+// forward + backward for their sparse kernels).  With S = scale Q K^T on the key set,
+// P = softmax(S), O = P V and the upstream dO:
+//   dV = P^T dO,  dP = dO V^T,  D = rowsum(dO * O),  dS = P * (dP - D),
+//   dQ = scale dS K,  dK = scale dS^T Q.
+// P is rebuilt from the forward's LSE: P = exp(S - LSE).
+//
+//   bwd_dot     D for every (b, h, row)
+//   bwd_count / bwd_scan / bwd_fill (block patterns): for every 64-key sub-block, the list
+//               of (query head, query block) pairs whose key lists name it
+//   bwd_dkdv    one workgroup (two waves, 32 keys each) per 64-key sub-block: K and V stay
+//               in registers, 32-row slabs of Q and dO pass through LDS; S = Q K^T and
+//               dP = dO V^T come out with a key per lane, which makes P and dS directly the
+//               B operands of dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T read with the
+//               transposing LDS read)
+//   bwd_dq      one workgroup per (b, head, query block): the forward's tile loop over the
+//               listed keys, rebuilding P^T and dP^T = V dO^T with a query per lane, then
+//               dQ^T += K^T dS^T
+// No kernel accumulates with atomics: dK/dV belong to one workgroup, dQ to another.
+#pragma once
+#include "tile.cuh"
+
+namespace bsa {
+
+constexpr int kBwdStride = TD + 8;  // LDS row of 136 bf16 (272 bytes): b128 and transposed reads
+
+__device__ __forceinline__ float bf16_lo(uint32_t x) { return bf16_bits_to_f32(x & 0xffffu); }
+__device__ __forceinline__ float bf16_hi(uint32_t x) { return bf16_bits_to_f32(x >> 16); }
+
+// D = sum_d dO * O: 16 threads per row, 16 rows per workgroup.
+__global__ __launch_bounds__(256) void bwd_dot_kernel(BwdArgs a) {
+  const int64_t row = (int64_t)wg_x() * 16 + (tid_x() >> 4);
+  const int part = tid_x() & 15;
+  const int64_t rows = (int64_t)a.B * a.Sq * a.Hq;
+  if (row >= rows) return;  // whole 16-lane groups
+  const int h = (int)(row % a.Hq);
+  const int s = (int)((row / a.Hq) % a.Sq);
+  const int b = (int)(row / ((int64_t)a.Hq * a.Sq));
+  const uint16_t* dp = reinterpret_cast<const uint16_t*>(a.dout.ptr) + (int64_t)b * a.dout.sb +
+                       (int64_t)s * a.dout.ss + (int64_t)h * a.dout.sh + part * 8;
+  const int64_t oo = (int64_t)b * a.o.sb + (int64_t)s * a.o.ss + (int64_t)h * a.o.sh + part * 8;
+  const u32x4 dv = ldg128(dp);
+  float ov[8];
+  if (a.o_f32) {
+    const f32x4 o0 = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(a.o.ptr) + oo);
+    const f32x4 o1 = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(a.o.ptr) + oo + 4);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      ov[x] = o0[x];
+      ov[4 + x] = o1[x];
+    }
+  } else {
+    const u32x4 o = ldg128(reinterpret_cast<const uint16_t*>(a.o.ptr) + oo);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      ov[2 * x] = bf16_lo(o[x]);
+      ov[2 * x + 1] = bf16_hi(o[x]);
+    }
+  }
+  float acc = 0.f;
+#pragma unroll
+  for (int x = 0; x < 4; ++x) acc += bf16_lo(dv[x]) * ov[2 * x] + bf16_hi(dv[x]) * ov[2 * x + 1];
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) acc += shfl_xor_f(acc, off);
+  if (part == 0) a.dsum[((int64_t)b * a.Hq + h) * a.Sq + s] = acc;
+}
+
+// ---- key-sub-block lists (block patterns) ----
+// One workgroup per (b, list head): an LDS histogram of the sub-blocks its lists name
+// (G entries per name when the lists belong to kv heads), then one global add per bin.
+__device__ __forceinline__ void bwd_list_head(const BwdArgs& a, int& b, int& ht, int& Ht, int& hkv) {
+  Ht = a.list_by_kv ? a.Hkv : a.Hq;
+  const int x = wg_x();
+  ht = x % Ht;
+  b = x / Ht;
+  hkv = a.list_by_kv ? ht : ht / a.G;
+}
+
+__global__ __launch_bounds__(256) void bwd_zero_kernel(BwdArgs a) {
+  const int x = wg_x() * 256 + tid_x();
+  if (x < a.B * a.Hkv * a.nks) a.counts[x] = 0;
+}
+
+__global__ __launch_bounds__(256) void bwd_count_kernel(BwdArgs a) {
+  __shared__ int hist[kBwdMaxSub];
+  int b, ht, Ht, hkv;
+  bwd_list_head(a, b, ht, Ht, hkv);
+  const int t = tid_x();
+  for (int x = t; x < a.nks; x += 256) hist[x] = 0;
+  __syncthreads();
+  const int spe = a.pat.block_N / 64, mult = a.list_by_kv ? a.G : 1;
+  const int n = a.nqb * a.pat.cap;
+  for (int e = t; e < n; e += 256) {
+    const int i = e / a.pat.cap, c = e - i * a.pat.cap;
+    const int64_t lb = (int64_t)b * a.pat.s_b + (int64_t)ht * a.pat.s_h + (int64_t)i * a.pat.s_q;
+    if (c >= a.pat.count[lb]) continue;
+    const int jb = a.pat.index[lb * a.pat.cap + c];
+    for (int u = 0; u < spe; ++u) {
+      const int sub = jb * spe + u;
+      if (sub >= 0 && sub < a.nks) atomicAdd(&hist[sub], mult);
+    }
+  }
+  __syncthreads();
+  int* counts = a.counts + ((int64_t)b * a.Hkv + hkv) * a.nks;
+  for (int x = t; x < a.nks; x += 256)
+    if (hist[x]) atomicAdd(&counts[x], hist[x]);
+}
+
+__global__ __launch_bounds__(1024) void bwd_scan_kernel(BwdArgs a) {
+  __shared__ int s_cnt[1024];
+  const int n = a.B * a.Hkv * a.nks;
+  const int t = tid_x();
+  int carry = 0;
+  for (int base = 0; base < n; base += 4096) {
+    int c[4], sc = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int idx = base + t * 4 + u;
+      c[u] = idx < n ? a.counts[idx] : 0;
+      sc += c[u];
+    }
+    s_cnt[t] = sc;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int v = t >= off ? s_cnt[t - off] : 0;
+      __syncthreads();
+      s_cnt[t] += v;
+      __syncthreads();
+    }
+    int ec = carry + s_cnt[t] - sc;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int idx = base + t * 4 + u;
+      if (idx < n) {
+        a.offsets[idx] = ec;
+        a.cursor[idx] = ec;
+      }
+      ec += c[u];
+    }
+    carry += s_cnt[1023];
+    __syncthreads();
+  }
+  if (t == 0) a.offsets[n] = carry;
+}
+
+__global__ __launch_bounds__(256) void bwd_fill_kernel(BwdArgs a) {
+  __shared__ int hist[kBwdMaxSub];
+  int b, ht, Ht, hkv;
+  bwd_list_head(a, b, ht, Ht, hkv);
+  const int t = tid_x();
+  for (int x = t; x < a.nks; x += 256) hist[x] = 0;
+  __syncthreads();
+  const int spe = a.pat.block_N / 64, mult = a.list_by_kv ? a.G : 1;
+  const int n = a.nqb * a.pat.cap;
+  for (int e = t; e < n; e += 256) {
+    const int i = e / a.pat.cap, c = e - i * a.pat.cap;
+    const int64_t lb = (int64_t)b * a.pat.s_b + (int64_t)ht * a.pat.s_h + (int64_t)i * a.pat.s_q;
+    if (c >= a.pat.count[lb]) continue;
+    const int jb = a.pat.index[lb * a.pat.cap + c];
+    for (int u = 0; u < spe; ++u) {
+      const int sub = jb * spe + u;
+      if (sub >= 0 && sub < a.nks) atomicAdd(&hist[sub], mult);
+    }
+  }
+  __syncthreads();
+  int* cursor = a.cursor + ((int64_t)b * a.Hkv + hkv) * a.nks;
+  for (int x = t; x < a.nks; x += 256)
+    if (hist[x]) hist[x] = atomicAdd(&cursor[x], hist[x]);
+  __syncthreads();
+  for (int e = t; e < n; e += 256) {
+    const int i = e / a.pat.cap, c = e - i * a.pat.cap;
+    const int64_t lb = (int64_t)b * a.pat.s_b + (int64_t)ht * a.pat.s_h + (int64_t)i * a.pat.s_q;
+    if (c >= a.pat.count[lb]) continue;
+    const int jb = a.pat.index[lb * a.pat.cap + c];
+    for (int u = 0; u < spe; ++u) {
+      const int sub = jb * spe + u;
+      if (sub < 0 || sub >= a.nks) continue;
+      for (int g = 0; g < mult; ++g) {
+        const int h = a.list_by_kv ? hkv * a.G + g : ht;
+        a.entries[atomicAdd(&hist[sub], 1)] = h * a.nqb + i;
+      }
+    }
+  }
+}
+
+// Per-lane LDS offsets of the transposed A-operand reads (32 rows of d x 16 rows of the
+// tile) from a row-major tile with kBwdStride rows: lane l of 16-lane group tg points at
+// tile row 4(tg / 2) + (l % 16) / 4 and 4 columns 32 db + 16 (tg % 2) + 4 (l % 4).
+__device__ __forceinline__ void bwd_tr_offsets(int l, int* off) {
+  const int tg = l >> 4, tr = l & 15;
+  const int row = (tg >> 1) * 4 + (tr >> 2);
+#pragma unroll
+  for (int db = 0; db < TD / 32; ++db) off[db] = row * kBwdStride + db * 32 + (tg & 1) * 16 + (tr & 3) * 4;
+}
+
+// acc[db] += X^T(32 d x 16 rows) * B for the 16 tile rows r0..r0+15 (rows r0 + 4hh + 0..3
+// and r0 + 8 + 4hh + 0..3 in the 8 k slots, the order of the accumulator registers).
+__device__ __forceinline__ void bwd_tr_mfma(const uint16_t* tile, int r0, const int* off, const u32x4& bop,
+                                            f32x16* acc) {
+#pragma unroll
+  for (int db = 0; db < TD / 32; ++db) {
+    const u32x2 lo = ds_read_tr16(tile + r0 * kBwdStride + off[db]);
+    const u32x2 hi = ds_read_tr16(tile + (r0 + 8) * kBwdStride + off[db]);
+    acc[db] = mfma32x32x16(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), as_bf16x8(bop), acc[db]);
+  }
+}
+
+// 32 rows x 128 bf16 from global rows (row_ptr(r) valid for r < n_valid, zeros past it) into
+// an LDS tile; nt threads.
+template <int NT>
+__device__ __forceinline__ void bwd_stage(uint16_t* tile, const uint16_t* base, int64_t ss, int rows, int n_valid,
+                                          int t) {
+  for (int x = t; x < rows * 16; x += NT) {
+    const int r = x >> 4, piece = x & 15;
+    const u32x4 v = r < n_valid ? ldg128(base + (int64_t)r * ss + piece * 8) : u32x4{0, 0, 0, 0};
+    *reinterpret_cast<u32x4*>(tile + r * kBwdStride + piece * 8) = v;
+  }
+}
+
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int D = TD;
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[32 * kBwdStride];
+  __shared__ __attribute__((aligned(16))) uint16_t Ds[32 * kBwdStride];
+  __shared__ __attribute__((aligned(16))) float ls[32];
+  __shared__ __attribute__((aligned(16))) float dsm[32];
+
+  const int wid = wg_x();
+  const int sub = wid % a.nks;
+  const int bh = wid / a.nks;
+  const int hkv = bh % a.Hkv, b = bh / a.Hkv;
+  const int key0 = sub * 64;
+  const int delta = a.Sk - a.Sq;
+  const int t = tid_x();
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63;
+  const int lq = l & 31, hh = l >> 5;
+  const int key = key0 + w * 32 + lq;  // this lane's key (S, dP, dK, dV columns)
+
+  const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.k.ptr) + (int64_t)b * a.k.sb + (int64_t)hkv * a.k.sh;
+  const uint16_t* vbase = reinterpret_cast<const uint16_t*>(a.v.ptr) + (int64_t)b * a.v.sb + (int64_t)hkv * a.v.sh;
+  bf16x8 kreg[D / 16], vreg[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const bool ok = key < a.Sk;
+    kreg[ks] = as_bf16x8(ok ? ldg128(kbase + (int64_t)key * a.k.ss + ks * 16 + hh * 8) : u32x4{0, 0, 0, 0});
+    vreg[ks] = as_bf16x8(ok ? ldg128(vbase + (int64_t)key * a.v.ss + ks * 16 + hh * 8) : u32x4{0, 0, 0, 0});
+  }
+  int troff[D / 32];
+  bwd_tr_offsets(l, troff);
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int x = 0; x < D / 32; ++x) dk[x] = dv[x] = f32x16{};
+
+  // units: (query head h, first row q0 of a 32-row slab)
+  const int slabs = a.BM / 32;
+  int n_units, list0 = 0, first_slab = 0;
+  const bool dense = a.pat.kind == 0;
+  if (dense) {
+    const int total_slabs = (a.Sq + 31) / 32;
+    // the first slab with a row that sees key0 (causal: row + delta >= key0)
+    first_slab = a.causal ? max(0, (key0 - delta) / 32) : 0;
+    n_units = a.G * max(0, total_slabs - first_slab);
+  } else {
+    const int list = (b * a.Hkv + hkv) * a.nks + sub;
+    list0 = a.offsets[list];
+    n_units = (a.offsets[list + 1] - list0) * slabs;
+  }
+  const int total_slabs = (a.Sq + 31) / 32;
+  for (int u = 0; u < n_units; ++u) {
+    int h, q0;
+    if (dense) {
+      const int per = total_slabs - first_slab;
+      h = hkv * a.G + u / per;
+      q0 = (first_slab + u % per) * 32;
+    } else {
+      const int e = a.entries[list0 + u / slabs];
+      h = e / a.nqb;
+      q0 = (e - h * a.nqb) * a.BM + (u % slabs) * 32;
+    }
+    if (q0 >= a.Sq || (a.causal && q0 + 31 + delta < key0)) continue;  // uniform: nothing visible
+    const int nrow = min(32, a.Sq - q0);
+    __syncthreads();  // the previous slab is consumed
+    bwd_stage<128>(Qs, reinterpret_cast<const uint16_t*>(a.q.ptr) + (int64_t)b * a.q.sb + (int64_t)q0 * a.q.ss +
+                           (int64_t)h * a.q.sh,
+                   a.q.ss, 32, nrow, t);
+    bwd_stage<128>(Ds, reinterpret_cast<const uint16_t*>(a.dout.ptr) + (int64_t)b * a.dout.sb +
+                           (int64_t)q0 * a.dout.ss + (int64_t)h * a.dout.sh,
+                   a.dout.ss, 32, nrow, t);
+    if (t < 32) {
+      const int64_t r = ((int64_t)b * a.Hq + h) * a.Sq + q0 + t;
+      ls[t] = t < nrow ? a.lse[r] * kLog2e : kNegInf;
+      dsm[t] = t < nrow ? a.dsum[r] : 0.f;
+    }
+    __syncthreads();
+    f32x16 s = {}, dp = {};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const u32x4 qa = *reinterpret_cast<const u32x4*>(Qs + lq * kBwdStride + ks * 16 + hh * 8);
+      const u32x4 da = *reinterpret_cast<const u32x4*>(Ds + lq * kBwdStride + ks * 16 + hh * 8);
+      s = mfma32x32x16(as_bf16x8(qa), kreg[ks], s);
+      dp = mfma32x32x16(as_bf16x8(da), vreg[ks], dp);
+    }
+    // lane: key; register r: slab row 8(r/4) + 4hh + r%4
+    uint32_t pp[8], dd[8];
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const f32x4 lv = *reinterpret_cast<const f32x4*>(ls + g4 * 8 + hh * 4);
+      const f32x4 dm = *reinterpret_cast<const f32x4*>(dsm + g4 * 8 + hh * 4);
+      float p[4], d[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = q0 + g4 * 8 + hh * 4 + e;
+        const bool vis = key < a.Sk && lv[e] != kNegInf && (!a.causal || key <= row + delta);
+        p[e] = vis ? exp2_fast(fmaf(s[g4 * 4 + e], a.scale_log2, -lv[e])) : 0.f;
+        d[e] = p[e] * (dp[g4 * 4 + e] - dm[e]);
+      }
+      pp[g4 * 2] = pack_bf16x2(p[0], p[1]);
+      pp[g4 * 2 + 1] = pack_bf16x2(p[2], p[3]);
+      dd[g4 * 2] = pack_bf16x2(d[0], d[1]);
+      dd[g4 * 2 + 1] = pack_bf16x2(d[2], d[3]);
+    }
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      bwd_tr_mfma(Ds, hb * 16, troff, u32x4{pp[hb * 4], pp[hb * 4 + 1], pp[hb * 4 + 2], pp[hb * 4 + 3]}, dv);
+      bwd_tr_mfma(Qs, hb * 16, troff, u32x4{dd[hb * 4], dd[hb * 4 + 1], dd[hb * 4 + 2], dd[hb * 4 + 3]}, dk);
+    }
+  }
+  if (key < a.Sk) {
+    float* dkp = a.dk + (((int64_t)b * a.Sk + key) * a.Hkv + hkv) * D;
+    float* dvp = a.dv + (((int64_t)b * a.Sk + key) * a.Hkv + hkv) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = db * 32 + g4 * 8 + hh * 4;
+        *reinterpret_cast<f32x4*>(dkp + d) =
+            f32x4{dk[db][g4 * 4] * a.scale, dk[db][g4 * 4 + 1] * a.scale, dk[db][g4 * 4 + 2] * a.scale,
+                  dk[db][g4 * 4 + 3] * a.scale};
+        *reinterpret_cast<f32x4*>(dvp + d) =
+            f32x4{dv[db][g4 * 4], dv[db][g4 * 4 + 1], dv[db][g4 * 4 + 2], dv[db][g4 * 4 + 3]};
+      }
+  }
+}
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq_kernel(BwdArgs a) {
+  constexpr int D = TD;
+  constexpr int NT = NW * 64;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[64 * kBwdStride];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[64 * kBwdStride];
+
+  const int item = wg_x();
+  const int i = item % a.nqb;
+  const int bh = item / a.nqb;
+  const int h = bh % a.Hq, b = bh / a.Hq;
+  const int hkv = h / a.G;
+  const int delta = a.Sk - a.Sq;
+  const int t = tid_x();
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63;
+  const int lq = l & 31, hh = l >> 5;
+  const int r0 = i * a.BM;
+  const int row = r0 + w * 32 + lq;  // this lane's query
+  const bool row_ok = row < a.Sq;
+
+  const int64_t qo = (int64_t)b * a.q.sb + (int64_t)row * a.q.ss + (int64_t)h * a.q.sh;
+  const int64_t doo = (int64_t)b * a.dout.sb + (int64_t)row * a.dout.ss + (int64_t)h * a.dout.sh;
+  bf16x8 qreg[D / 16], doreg[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    qreg[ks] = as_bf16x8(row_ok ? ldg128(reinterpret_cast<const uint16_t*>(a.q.ptr) + qo + ks * 16 + hh * 8)
+                                : u32x4{0, 0, 0, 0});
+    doreg[ks] = as_bf16x8(row_ok ? ldg128(reinterpret_cast<const uint16_t*>(a.dout.ptr) + doo + ks * 16 + hh * 8)
+                                 : u32x4{0, 0, 0, 0});
+  }
+  const int64_t rr = ((int64_t)b * a.Hq + h) * a.Sq + row;
+  const float lse2 = row_ok ? a.lse[rr] * kLog2e : kNegInf;
+  const float dsv = row_ok ? a.dsum[rr] : 0.f;
+  const int lim = !row_ok || lse2 == kNegInf ? -1 : (a.causal ? min(row + delta, a.Sk - 1) : a.Sk - 1);
+  int troff[D / 32];
+  bwd_tr_offsets(l, troff);
+  f32x16 dq[D / 32];
+#pragma unroll
+  for (int x = 0; x < D / 32; ++x) dq[x] = f32x16{};
+
+  // the 64-key sub-blocks to visit
+  int n_sub, spe = 1, n_ent = 0;
+  const int32_t* list = nullptr;
+  const int last_row = min(r0 + a.BM, a.Sq) - 1;
+  if (a.pat.kind == 0) {
+    const int kend = a.causal ? min(a.Sk, last_row + delta + 1) : a.Sk;
+    n_sub = kend > 0 ? (kend + 63) / 64 : 0;
+  } else {
+    const int ht = a.list_by_kv ? hkv : h;
+    const int64_t lb = (int64_t)b * a.pat.s_b + (int64_t)ht * a.pat.s_h + (int64_t)i * a.pat.s_q;
+    n_ent = a.pat.count[lb];
+    list = a.pat.index + lb * a.pat.cap;
+    spe = a.pat.block_N / 64;
+    n_sub = n_ent * spe;
+  }
+  for (int x = 0; x < n_sub; ++x) {
+    const int sub = a.pat.kind == 0 ? x : list[x / spe] * spe + x % spe;
+    const int key0 = sub * 64;
+    if (key0 < 0 || key0 >= a.Sk || (a.causal && key0 > last_row + delta)) continue;  // uniform
+    const int nkey = min(64, a.Sk - key0);
+    __syncthreads();
+    bwd_stage<NT>(Ks, reinterpret_cast<const uint16_t*>(a.k.ptr) + (int64_t)b * a.k.sb + (int64_t)key0 * a.k.ss +
+                          (int64_t)hkv * a.k.sh,
+                  a.k.ss, 64, nkey, t);
+    bwd_stage<NT>(Vs, reinterpret_cast<const uint16_t*>(a.v.ptr) + (int64_t)b * a.v.sb + (int64_t)key0 * a.v.ss +
+                          (int64_t)hkv * a.v.sh,
+                  a.v.ss, 64, nkey, t);
+    __syncthreads();
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 st = {}, dpt = {};
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const u32x4 ka = *reinterpret_cast<const u32x4*>(Ks + (kb * 32 + lq) * kBwdStride + ks * 16 + hh * 8);
+        const u32x4 va = *reinterpret_cast<const u32x4*>(Vs + (kb * 32 + lq) * kBwdStride + ks * 16 + hh * 8);
+        st = mfma32x32x16(as_bf16x8(ka), qreg[ks], st);
+        dpt = mfma32x32x16(as_bf16x8(va), doreg[ks], dpt);
+      }
+      // lane: query; register r: key key0 + 32kb + 8(r/4) + 4hh + r%4
+      uint32_t dd[8];
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        float d2[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int kk = key0 + kb * 32 + ((r + e) >> 2) * 8 + hh * 4 + ((r + e) & 3);
+          const float p = kk <= lim ? exp2_fast(fmaf(st[r + e], a.scale_log2, -lse2)) : 0.f;
+          d2[e] = p * (dpt[r + e] - dsv);
+        }
+        dd[r / 2] = pack_bf16x2(d2[0], d2[1]);
+      }
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+        bwd_tr_mfma(Ks, kb * 32 + hb * 16, troff, u32x4{dd[hb * 4], dd[hb * 4 + 1], dd[hb * 4 + 2], dd[hb * 4 + 3]},
+                    dq);
+    }
+  }
+  if (row_ok) {
+    float* dqp = a.dq + (((int64_t)b * a.Sq + row) * a.Hq + h) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = db * 32 + g4 * 8 + hh * 4;
+        *reinterpret_cast<f32x4*>(dqp + d) =
+            f32x4{dq[db][g4 * 4] * a.scale, dq[db][g4 * 4 + 1] * a.scale, dq[db][g4 * 4 + 2] * a.scale,
+                  dq[db][g4 * 4 + 3] * a.scale};
+      }
+  }
+}
+
+}  // namespace bsa

@@ -540,6 +540,108 @@ bsa_status bsa_fwd_gated(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, bs
 }
 
 // ---------------------------------------------------------------------------
+// Backward of block-sparse attention
+// ---------------------------------------------------------------------------
+
+namespace {
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct BwdLayout {
+  int BM = 0, nqb = 0, nks = 0, n_lists = 0;
+  size_t dsum = 0, counts = 0, offsets = 0, cursor = 0, entries = 0, total = 0;
+};
+
+// Shapes the backward kernels take; total == 0 otherwise.
+BwdLayout bwd_layout(const bsa_problem& p, const bsa_pattern* pat) {
+  BwdLayout L;
+  if (p.B <= 0 || p.Hq <= 0 || p.Hkv <= 0 || p.Hq % p.Hkv || p.Sq <= 0 || p.Sk <= 0) return L;
+  if (p.cu_seqlens_q || p.D != 128 || p.softcap > 0.f) return L;
+  const bool block = pat && pat->kind == BSA_PAT_BLOCK;
+  if (pat && pat->kind != BSA_PAT_DENSE && !block) return L;
+  L.BM = block ? pat->block_M : 128;
+  L.nqb = (p.Sq + L.BM - 1) / L.BM;
+  L.nks = (p.Sk + 63) / 64;
+  if (L.nks > kBwdMaxSub) return L;
+  L.n_lists = p.B * p.Hkv * L.nks;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t at = off; off = align256(off + bytes); return at; };
+  L.dsum = take(sizeof(float) * (size_t)p.B * p.Hq * p.Sq);
+  if (block) {
+    const int Ht = pat->Ht;
+    const int mult = Ht == p.Hkv ? p.Hq / p.Hkv : 1;
+    const size_t pairs = (size_t)p.B * Ht * L.nqb * pat->cap * (pat->block_N / 64) * mult;
+    if (pairs >= (size_t)INT_MAX) return BwdLayout{};
+    L.counts = take(sizeof(int32_t) * L.n_lists);
+    L.offsets = take(sizeof(int32_t) * (L.n_lists + 1));
+    L.cursor = take(sizeof(int32_t) * L.n_lists);
+    L.entries = take(sizeof(int32_t) * pairs);
+  }
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+size_t bsa_bwd_workspace_size(const bsa_problem* prob, const bsa_pattern* pat) {
+  if (!prob || check_pattern(*prob, pat) != BSA_OK) return 0;
+  return bwd_layout(*prob, pat).total;
+}
+
+bsa_status bsa_bwd(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, bsa_tensor v, const bsa_pattern* pat,
+                   bsa_tensor o, const float* lse, bsa_tensor dout, float* dq, float* dk, float* dv, void* ws,
+                   size_t ws_bytes, bsa_stream stream) {
+  bsa_status st = check_problem(prob, q, k, v, o);
+  if (st != BSA_OK) return st;
+  const bsa_problem& p = *prob;
+  st = check_pattern(p, pat);
+  if (st != BSA_OK) return st;
+  if (!lse || !dout.ptr || !dq || !dk || !dv) return BSA_ERR_INVALID_ARG;
+  if (dout.dtype != BSA_BF16) return BSA_ERR_UNSUPPORTED;
+  if (!aligned_rows(dout, 2)) return BSA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(dq) | reinterpret_cast<uintptr_t>(dk) | reinterpret_cast<uintptr_t>(dv)) & 15)
+    return BSA_ERR_INVALID_ARG;
+  const BwdLayout L = bwd_layout(p, pat);
+  if (L.total == 0) return BSA_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < L.total || (reinterpret_cast<uintptr_t>(ws) & 255)) return BSA_ERR_WORKSPACE;
+  char* base = reinterpret_cast<char*>(ws);
+  BwdArgs a{};
+  a.q = targ(q);
+  a.k = targ(k);
+  a.v = targ(v);
+  a.o = targ(o);
+  a.o_f32 = o.dtype == BSA_F32;
+  a.dout = targ(dout);
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dsum = reinterpret_cast<float*>(base + L.dsum);
+  a.pat = parg(pat);
+  a.B = p.B;
+  a.Hq = p.Hq;
+  a.Hkv = p.Hkv;
+  a.G = p.Hq / p.Hkv;
+  a.Sq = p.Sq;
+  a.Sk = p.Sk;
+  a.list_by_kv = pat && pat->kind == BSA_PAT_BLOCK && pat->Ht == p.Hkv && p.Hkv != p.Hq;
+  a.causal = p.causal;
+  a.scale = scale_of(p);
+  a.scale_log2 = a.scale * kLog2e;
+  a.BM = L.BM;
+  a.nqb = L.nqb;
+  a.nks = L.nks;
+  if (pat && pat->kind == BSA_PAT_BLOCK) {
+    a.counts = reinterpret_cast<int32_t*>(base + L.counts);
+    a.offsets = reinterpret_cast<int32_t*>(base + L.offsets);
+    a.cursor = reinterpret_cast<int32_t*>(base + L.cursor);
+    a.entries = reinterpret_cast<int32_t*>(base + L.entries);
+  }
+  launch_bwd(a, reinterpret_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+// ---------------------------------------------------------------------------
 // Selected attention (top-k key blocks per query token)
 // ---------------------------------------------------------------------------
 
@@ -551,8 +653,6 @@ struct SelLayout {
 };
 
 constexpr int kSelD = 128;  // head dim of the selected-attention kernel
-
-size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workspace carve-up; total == 0 for shapes outside the supported set.
 SelLayout sel_layout(const bsa_problem& p, int32_t total_q, int32_t topk) {

@@ -1,6 +1,6 @@
 // Host-side launch wrappers, one per kernel family, defined in the translation unit that
-// instantiates the kernels (kernels_stream.hip, kernels_tile.hip, kernels_select.hip) so
-// that each family is compiled with its own code-generation flags.
+// instantiates the kernels (kernels_stream.hip, kernels_tile.hip, kernels_select.hip,
+// kernels_bwd.hip) so that each family is compiled with its own code-generation flags.
 #pragma once
 #include <hip/hip_runtime.h>
 
@@ -21,6 +21,9 @@ void launch_gated(const GatedArgs& a, bool calib, hipStream_t st);
 // threshold_kernel: grid (nqb, Hq), 256 threads; nqb <= kThreshMaxCand.
 void launch_threshold(const ThresholdArgs& a, hipStream_t st);
 
+// backward: bwd_dot, (block patterns) bwd_zero / bwd_count / bwd_scan / bwd_fill, bwd_dkdv,
+// bwd_dq.
+void launch_bwd(const BwdArgs& a, hipStream_t st);
 // selected attention: sel_zero, sel_count, sel_scan, sel_fill, then selected_kernel over
 // main_grid workgroups (an upper bound on the chunks; the surplus exits at once).
 void launch_selected(const SelArgs& a, int main_grid, hipStream_t st);

@@ -160,6 +160,21 @@ def test_gated_and_vs_convert_errors(lib):
     assert fs(ctypes.byref(_prob(Hq=32, Hkv=1, Sq=256, Sk=256, causal=1)), _t(sb=256 * 32 * 128, ss=32 * 128),
               _t(), _t(), 16, 0, 8, 64, _t(sb=256 * 32 * 128, ss=32 * 128), None, 256, ws, None) \
         == bd.BSA_ERR_UNSUPPORTED                                                            # group of 32
+    # backward
+    bp = _prob(Hq=4, Hkv=2, Sq=256, Sk=256, causal=1)
+    wsb = lib.bsa_bwd_workspace_size(ctypes.byref(bp), None)
+    assert wsb >= 4 * 256 * 4                                          # the row dots
+    assert lib.bsa_bwd_workspace_size(ctypes.byref(_prob(Hq=4, Hkv=2, Sq=256, Sk=256, causal=1, softcap=5.0)),
+                                      None) == 0
+    bw = lib.bsa_bwd
+    assert bw(ctypes.byref(bp), qs, _t(), _t(), None, qs, None, qs, 16, 16, 16, 256, wsb, None) \
+        == bd.BSA_ERR_INVALID_ARG                                                            # no lse
+    assert bw(ctypes.byref(bp), qs, _t(), _t(), None, qs, 16, qs, None, 16, 16, 256, wsb, None) \
+        == bd.BSA_ERR_INVALID_ARG                                                            # no dq
+    assert bw(ctypes.byref(bp), qs, _t(), _t(), None, qs, 16, qs, 16, 16, 16, 256, wsb - 1, None) \
+        == bd.BSA_ERR_WORKSPACE
+    assert bw(ctypes.byref(_prob(Hq=4, Hkv=2, Sq=256, Sk=256, causal=1, D=64)), qs, _t(), _t(), None, qs, 16, qs,
+              16, 16, 16, 256, wsb, None) == bd.BSA_ERR_UNSUPPORTED                          # head dim 64
     sc = _prob(Hq=2, Hkv=2, Sq=256, Sk=256, causal=1, softcap=30.0)
     assert lib.bsa_fwd_gated(ctypes.byref(sc), q, _t(), _t(), T, 128, 128, q, None, None, None, None) \
         == bd.BSA_ERR_UNSUPPORTED

@@ -1,0 +1,104 @@
+"""GPU parity for the backward of block-sparse attention (dQ, dK, dV in float32) against the
+float64 oracle: dense causal and not (ragged lengths), block lists per query head and per kv
+head on 128- and 64-row tiles, and empty lists.  The forward's (O, LSE) come from the GPU path
+(float32 O), as a training step would use them.
+
+Tolerance: the kernels round P and dS to bf16 for the MFMA products (relative error <= 2^-9
+per term), so a gradient entry that sums n terms of size up to |t| is off by at most about
+2^-9 * n |t| in the worst case and 2^-9 sqrt(n) |t| typically; the check bounds the error by
+1e-2 of the largest reference entry (floored at 1)."""
+import numpy as np
+import pytest
+import torch
+
+import long_context_attention_sparse_amd as bsa
+import oracle
+from synth import normal_bf16, rng
+from tests.gpu_util import dev_bf16, dev_i32, host, say
+
+pytestmark = [pytest.mark.gpu, pytest.mark.filterwarnings("ignore::RuntimeWarning")]
+
+
+def _check(name, got, ref):
+    scale = max(1.0, float(np.abs(ref).max()))
+    err = float(np.abs(host(got).astype(np.float64) - ref).max())
+    assert np.isfinite(err) and err <= 1e-2 * scale, f"{name}: max error {err:.3g} vs scale {scale:.3g}"
+
+
+def _data(seed, B, Sq, Sk, Hq, Hkv):
+    return (normal_bf16(seed, "q", (B, Sq, Hq, 128)), normal_bf16(seed, "k", (B, Sk, Hkv, 128)),
+            normal_bf16(seed, "v", (B, Sk, Hkv, 128)), normal_bf16(seed, "do", (B, Sq, Hq, 128)))
+
+
+def _grads(q, k, v, do, pattern=None, causal=True, count=None, index=None, bM=128, bN=128):
+    dq_, dk_, dv_ = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    o, lse = bsa.bsa_fwd(dq_, dk_, dv_, pattern, causal=causal, out_dtype=torch.float32)
+    g = bsa.bsa_bwd(dq_, dk_, dv_, o, lse, dev_bf16(do), pattern, causal=causal)
+    ref = oracle.block_sparse_bwd(q, k, v, do, count, index, bM, bN, causal)
+    return g, ref
+
+
+@pytest.mark.parametrize("Sq,Sk,causal", [(384, 384, True), (300, 456, False), (200, 328, True)])
+def test_dense(Sq, Sk, causal):
+    say("backward dense", Sq, Sk, causal)
+    q, k, v, do = _data(91, 2, Sq, Sk, 4, 2)
+    (dq, dk, dv), (rq, rk, rv) = _grads(q, k, v, do, None, causal)
+    _check("dq", dq, rq)
+    _check("dk", dk, rk)
+    _check("dv", dv, rv)
+
+
+def _lists(seed, B, H, nqb, nkb, cap):
+    g = rng(seed, "bwd-lists")
+    count = np.zeros((B, H, nqb), np.int32)
+    index = np.zeros((B, H, nqb, cap), np.int32)
+    for b in range(B):
+        for h in range(H):
+            for i in range(nqb):
+                reach = min(i, nkb - 1)
+                pool = np.arange(reach)
+                n = int(g.integers(0, min(cap - 1, pool.size) + 1)) if pool.size else 0
+                sel = np.concatenate([[reach], g.choice(pool, n, replace=False)]) if n else np.array([reach])
+                sel = g.permutation(sel)
+                count[b, h, i] = sel.size
+                index[b, h, i, :sel.size] = sel
+    return count, index
+
+
+@pytest.mark.parametrize("bM,bN,Ht", [(128, 128, "q"), (128, 128, "kv"), (64, 64, "q"), (64, 128, "kv")])
+def test_block_lists(bM, bN, Ht):
+    B, S, Hq, Hkv = 2, 512, 4, 2
+    say("backward block lists", bM, bN, Ht)
+    q, k, v, do = _data(92, B, S, S, Hq, Hkv)
+    H = Hq if Ht == "q" else Hkv
+    nqb, nkb = S // bM, S // bN
+    # query block i of bM rows reaches key block (i*bM + bM - 1) // bN
+    count, index = _lists(92, B, H, nqb, nkb, 4)
+    for i in range(nqb):
+        index[:, :, i] = np.minimum(index[:, :, i], ((i + 1) * bM - 1) // bN)
+        for b in range(B):
+            for h in range(H):
+                row = index[b, h, i, :count[b, h, i]]
+                u = np.unique(row)
+                count[b, h, i] = u.size
+                index[b, h, i, :u.size] = u
+    pat = bsa.BlockPattern(dev_i32(count), dev_i32(index), bM, bN)
+    (dq, dk, dv), (rq, rk, rv) = _grads(q, k, v, do, pat, True, count, index, bM, bN)
+    _check("dq", dq, rq)
+    _check("dk", dk, rk)
+    _check("dv", dv, rv)
+
+
+def test_empty_lists_give_zero_rows():
+    B, S, Hq, Hkv = 1, 256, 2, 2
+    say("backward empty lists")
+    q, k, v, do = _data(93, B, S, S, Hq, Hkv)
+    count = np.full((B, Hq, 2), 2, np.int32)
+    index = np.broadcast_to(np.array([0, 1], np.int32), (B, Hq, 2, 2)).copy()
+    count[0, 1, 1] = 0
+    pat = bsa.BlockPattern(dev_i32(count), dev_i32(index), 128, 128)
+    (dq, dk, dv), (rq, rk, rv) = _grads(q, k, v, do, pat, True, count, index)
+    assert np.all(host(dq)[0, 128:, 1] == 0)
+    _check("dq", dq, rq)
+    _check("dk", dk, rk)
+    _check("dv", dv, rv)
