@@ -32,7 +32,7 @@ def _args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5, 6])
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7])
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
@@ -505,6 +505,49 @@ def bench_vs(torch, bsa, args):
 
 
 # ---------------------------------------------------------------------------
+# Backward of the block-sparse prefill workload
+# ---------------------------------------------------------------------------
+
+def bench_backward(torch, bsa, args):
+    from synth import normal_bf16, to_torch_bf16
+    from synth.workloads import block_sparse_prefill
+
+    _log("generating block-sparse prefill inputs and an upstream gradient")
+    w = block_sparse_prefill()
+    dev = torch.device("cuda:0")
+    q, k, v = (to_torch_bf16(w[n]).to(dev) for n in ("q", "k", "v"))
+    do = to_torch_bf16(normal_bf16(1007, "do", w["q"].shape)).to(dev)
+    pat = bsa.BlockPattern(torch.from_numpy(w["count"]).to(dev), torch.from_numpy(w["index"]).to(dev), 128, 128)
+    out, lse = bsa.bsa_fwd(q, k, v, pat, causal=True, out_dtype=torch.bfloat16)
+    ws = torch.empty(bsa.bsa_bwd_workspace_size(q, k, pat, causal=True), dtype=torch.uint8, device=dev)
+
+    def call():
+        bsa.bsa_bwd(q, k, v, out, lse, do, pat, causal=True, workspace=ws)
+
+    def step(timer):
+        with timer.span("backward"):
+            call()
+
+    timer = Timer(torch)
+    ms = run_steps(torch, step, timer, args.steps, args.warmup)
+    bms = timer.mean_ms("backward")
+    tiles = int(w["count"].sum())
+    flops = tiles * 5 * 2 * 128 ** 3   # S (rebuilt), dP, dV, dQ, dK: five tile products
+    tf = flops / (bms * 1e-3) / 1e12
+    return dict(metric=METRIC, value=round(flops / (ms * 1e-3) / 1e12, 2), unit="TFLOP/s", ms_per_step=round(ms, 4),
+                dtype="bf16",
+                config={"workload": "block-sparse causal prefill backward (dQ, dK, dV)", "B": 1, "Hq": 32, "Hkv": 8,
+                        "S": 32768, "D": 128, "tile": 128, "visited_tiles": tiles, "flops": flops,
+                        "flops_note": "5 products of 2*128^3 per visited tile (S, dP, dV, dQ, dK); the dQ pass "
+                                      "rebuilds S and dP a second time: 7 executed"},
+                roofline={"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                          "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                          "kernel": "bsa_bwd (bwd_dkdv_kernel + bwd_dq_kernel<4> + list inversion)",
+                          "avg_ms": round(bms, 4)},
+                cpu_baseline=None)
+
+
+# ---------------------------------------------------------------------------
 # Selected attention (top-k key blocks per query token), the FSA module's example shape
 # ---------------------------------------------------------------------------
 
@@ -595,7 +638,7 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n, "copies": 4}), flush=True)
         return
     fn = {1: bench_tiny, 2: bench_spec_decode, 3: bench_block_prefill, 4: bench_gated, 5: bench_vs,
-          6: bench_selected}[args.config]
+          6: bench_selected, 7: bench_backward}[args.config]
     res = fn(torch, bsa, args)
     line = {"metric": res["metric"], "value": res["value"], "unit": res["unit"], "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": res["ms_per_step"],

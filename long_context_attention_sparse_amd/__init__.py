@@ -18,13 +18,13 @@ include/bsa.h and only marshals arguments — the kernels do all the work:
                       the combine)
 """
 from ._binding import (EXPORTS, LIB_PATH, BlockPattern, BSAError, VSPattern, bsa_combine, bsa_fwd, bsa_fwd_gated,
-                       bsa_bwd, bsa_fwd_selected, bsa_selected_workspace_size, bsfa_calibrate,
+                       bsa_bwd, bsa_bwd_workspace_size, bsa_fwd_selected, bsa_selected_workspace_size, bsfa_calibrate,
                        bsa_fwd_partials, bsa_num_partials, bsa_speculative_partials, bsa_workspace_size, load,
                        speculative_sparse, vs_convert_indexes,
                        vs_convert_indexes_mergehead)
 
 __all__ = ["EXPORTS", "LIB_PATH", "BlockPattern", "BSAError", "VSPattern", "bsa_combine", "bsa_fwd", "bsa_fwd_gated",
-           "bsa_bwd", "bsa_fwd_selected", "bsa_selected_workspace_size", "bsfa_calibrate",
+           "bsa_bwd", "bsa_bwd_workspace_size", "bsa_fwd_selected", "bsa_selected_workspace_size", "bsfa_calibrate",
            "bsa_fwd_partials", "bsa_num_partials", "bsa_speculative_partials", "bsa_workspace_size", "load",
            "speculative_sparse", "vs_convert_indexes",
            "vs_convert_indexes_mergehead"]

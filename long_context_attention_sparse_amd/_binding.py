@@ -379,6 +379,12 @@ def bsa_bwd(q, k, v, out, lse, dout, pattern=None, *, causal: bool = False, soft
     return dq, dk, dv
 
 
+def bsa_bwd_workspace_size(q, k, pattern=None, causal: bool = False) -> int:
+    prob = _problem(q, k, causal, None)
+    pat = pattern.struct(prob.Hq) if pattern is not None else None
+    return int(load().bsa_bwd_workspace_size(ctypes.byref(prob), ctypes.byref(pat) if pat is not None else None))
+
+
 def bsa_fwd_selected(q, k, v, sel: torch.Tensor, *, block_size: int = 64, causal: bool = True,
                      softmax_scale=None, softcap: float = 0.0, out: Optional[torch.Tensor] = None,
                      out_dtype: torch.dtype = torch.bfloat16, lse: Optional[torch.Tensor] = None,

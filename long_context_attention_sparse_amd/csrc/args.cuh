@@ -33,6 +33,7 @@ constexpr int kThreshMaxCand = 4096;   // threshold selection: query blocks per 
 constexpr int kSelTile = 1024;         // selected attention: token positions per index workgroup
 constexpr int kSelMaxBlocks = 8192;    // selected attention: key blocks per sequence (LDS histogram)
 constexpr int kBwdMaxSub = 8192;       // backward: 64-key sub-blocks per sequence (LDS histogram)
+constexpr int kBwdChunk = 128;         // backward: 32-row query slabs per dK/dV workgroup
 
 struct DecodeSeg {
   TensorArg k, v;
@@ -131,11 +132,14 @@ struct BwdArgs {
   float scale, scale_log2;
   int BM;                      // query block rows of the pattern (64 or 128; dense: 128)
   int nqb, nks;                // query blocks; 64-key sub-blocks
-  // key-sub-block lists of (query head, query block) pairs (block patterns)
-  int32_t* counts;             // [B * Hkv * nks]
-  int32_t* offsets;            // [B * Hkv * nks + 1]
-  int32_t* cursor;             // [B * Hkv * nks]
+  // per 64-key sub-block ("list"): its (query head, query block) pairs (block patterns), its
+  // units of work (32-row query slabs), and those units cut into chunks of kBwdChunk
+  int32_t* counts;             // [lists]: pairs (block patterns) or units (dense)
+  int32_t* offsets;            // [lists + 1] prefix sums of pairs (block patterns)
+  int32_t* cursor;             // [lists]
   int32_t* entries;            // h * nqb + i
+  int32_t* chunkp;             // [lists + 1] prefix sums of chunks
+  float* part;                 // [chunks, 2, 64, D]: dK^T / dV^T partials of lists cut into chunks
 };
 
 struct ThresholdArgs {

@@ -10,7 +10,11 @@
 //   bwd_dot     D for every (b, h, row)
 //   bwd_count / bwd_scan / bwd_fill (block patterns): for every 64-key sub-block, the list
 //               of (query head, query block) pairs whose key lists name it
-//   bwd_dkdv    one workgroup (two waves, 32 keys each) per 64-key sub-block: K and V stay
+//   bwd_dkdv    one workgroup (two waves, 32 keys each) per chunk of up to kBwdChunk
+//               32-row query slabs of a 64-key sub-block's list (a list every query block
+//               names, like the first block of a causal pattern, is spread over many
+//               workgroups; their float32 partials are summed in chunk order by bwd_reduce,
+//               so the result does not depend on scheduling): K and V stay
 //               in registers, 32-row slabs of Q and dO pass through LDS; S = Q K^T and
 //               dP = dO V^T come out with a key per lane, which makes P and dS directly the
 //               B operands of dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T read with the
@@ -83,6 +87,19 @@ __global__ __launch_bounds__(256) void bwd_zero_kernel(BwdArgs a) {
   if (x < a.B * a.Hkv * a.nks) a.counts[x] = 0;
 }
 
+// First 32-row query slab that sees key0 (causal: some row r with r + Sk - Sq >= key0).
+__device__ __forceinline__ int bwd_first_slab(const BwdArgs& a, int key0) {
+  return a.causal ? max(0, (key0 - (a.Sk - a.Sq)) / 32) : 0;
+}
+
+// Dense patterns: the units of every list are (query head of the group, slab) pairs.
+__global__ __launch_bounds__(256) void bwd_dense_count_kernel(BwdArgs a) {
+  const int x = wg_x() * 256 + tid_x();
+  if (x >= a.B * a.Hkv * a.nks) return;
+  const int total_slabs = (a.Sq + 31) / 32;
+  a.counts[x] = a.G * max(0, total_slabs - bwd_first_slab(a, (x % a.nks) * 64));
+}
+
 __global__ __launch_bounds__(256) void bwd_count_kernel(BwdArgs a) {
   __shared__ int hist[kBwdMaxSub];
   int b, ht, Ht, hkv;
@@ -108,41 +125,58 @@ __global__ __launch_bounds__(256) void bwd_count_kernel(BwdArgs a) {
     if (hist[x]) atomicAdd(&counts[x], hist[x]);
 }
 
+// Exclusive prefix sums of the counts (pair offsets, block patterns) and of the chunks per
+// list, ceil(units / kBwdChunk) with units = counts * slabs (block) or counts (dense).
 __global__ __launch_bounds__(1024) void bwd_scan_kernel(BwdArgs a) {
-  __shared__ int s_cnt[1024];
+  __shared__ int s_cnt[1024], s_chk[1024];
   const int n = a.B * a.Hkv * a.nks;
   const int t = tid_x();
-  int carry = 0;
+  const bool block = a.pat.kind != 0;
+  const int mult = block ? a.BM / 32 : 1;
+  int carry = 0, carry_k = 0;
   for (int base = 0; base < n; base += 4096) {
-    int c[4], sc = 0;
+    int c[4], k[4], sc = 0, sk = 0;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int idx = base + t * 4 + u;
       c[u] = idx < n ? a.counts[idx] : 0;
+      k[u] = (c[u] * mult + kBwdChunk - 1) / kBwdChunk;
       sc += c[u];
+      sk += k[u];
     }
     s_cnt[t] = sc;
+    s_chk[t] = sk;
     __syncthreads();
     for (int off = 1; off < 1024; off <<= 1) {
       const int v = t >= off ? s_cnt[t - off] : 0;
+      const int vk = t >= off ? s_chk[t - off] : 0;
       __syncthreads();
       s_cnt[t] += v;
+      s_chk[t] += vk;
       __syncthreads();
     }
-    int ec = carry + s_cnt[t] - sc;
+    int ec = carry + s_cnt[t] - sc, ek = carry_k + s_chk[t] - sk;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int idx = base + t * 4 + u;
       if (idx < n) {
-        a.offsets[idx] = ec;
-        a.cursor[idx] = ec;
+        if (block) {
+          a.offsets[idx] = ec;
+          a.cursor[idx] = ec;
+        }
+        a.chunkp[idx] = ek;
       }
       ec += c[u];
+      ek += k[u];
     }
     carry += s_cnt[1023];
+    carry_k += s_chk[1023];
     __syncthreads();
   }
-  if (t == 0) a.offsets[n] = carry;
+  if (t == 0) {
+    if (block) a.offsets[n] = carry;
+    a.chunkp[n] = carry_k;
+  }
 }
 
 __global__ __launch_bounds__(256) void bwd_fill_kernel(BwdArgs a) {
@@ -226,11 +260,22 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void b
   __shared__ __attribute__((aligned(16))) float ls[32];
   __shared__ __attribute__((aligned(16))) float dsm[32];
 
+  const int n_lists = a.B * a.Hkv * a.nks;
   const int wid = wg_x();
-  const int sub = wid % a.nks;
-  const int bh = wid / a.nks;
+  if (wid >= a.chunkp[n_lists]) return;  // uniform: the grid is an upper bound
+  int lo = 0, hi = n_lists;              // list with chunkp[lo] <= wid < chunkp[lo + 1]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.chunkp[mid] <= wid) lo = mid;
+    else hi = mid;
+  }
+  const int list = lo;
+  const int sub = list % a.nks;
+  const int bh = list / a.nks;
   const int hkv = bh % a.Hkv, b = bh / a.Hkv;
   const int key0 = sub * 64;
+  const int chunk = wid - a.chunkp[list];
+  const bool split = a.chunkp[list + 1] - a.chunkp[list] > 1;
   const int delta = a.Sk - a.Sq;
   const int t = tid_x();
   const int w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63;
@@ -252,22 +297,16 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void b
 #pragma unroll
   for (int x = 0; x < D / 32; ++x) dk[x] = dv[x] = f32x16{};
 
-  // units: (query head h, first row q0 of a 32-row slab)
+  // units: (query head h, first row q0 of a 32-row slab); this workgroup takes chunk
+  // `chunk` of the list's units
   const int slabs = a.BM / 32;
-  int n_units, list0 = 0, first_slab = 0;
-  const bool dense = a.pat.kind == 0;
-  if (dense) {
-    const int total_slabs = (a.Sq + 31) / 32;
-    // the first slab with a row that sees key0 (causal: row + delta >= key0)
-    first_slab = a.causal ? max(0, (key0 - delta) / 32) : 0;
-    n_units = a.G * max(0, total_slabs - first_slab);
-  } else {
-    const int list = (b * a.Hkv + hkv) * a.nks + sub;
-    list0 = a.offsets[list];
-    n_units = (a.offsets[list + 1] - list0) * slabs;
-  }
   const int total_slabs = (a.Sq + 31) / 32;
-  for (int u = 0; u < n_units; ++u) {
+  const bool dense = a.pat.kind == 0;
+  const int first_slab = dense ? bwd_first_slab(a, key0) : 0;
+  const int list0 = dense ? 0 : a.offsets[list];
+  const int n_units = dense ? a.counts[list] : a.counts[list] * slabs;
+  const int u0 = chunk * kBwdChunk, u1 = min(n_units, u0 + kBwdChunk);
+  for (int u = u0; u < u1; ++u) {
     int h, q0;
     if (dense) {
       const int per = total_slabs - first_slab;
@@ -326,20 +365,54 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void b
       bwd_tr_mfma(Qs, hb * 16, troff, u32x4{dd[hb * 4], dd[hb * 4 + 1], dd[hb * 4 + 2], dd[hb * 4 + 3]}, dk);
     }
   }
-  if (key < a.Sk) {
-    float* dkp = a.dk + (((int64_t)b * a.Sk + key) * a.Hkv + hkv) * D;
-    float* dvp = a.dv + (((int64_t)b * a.Sk + key) * a.Hkv + hkv) * D;
+  // one chunk: the gradients themselves; several: a partial per chunk, summed by bwd_reduce
+  float* dkp;
+  float* dvp;
+  float ks_ = a.scale;
+  if (split) {
+    dkp = a.part + ((int64_t)wid * 2 * 64 + w * 32 + lq) * D;
+    dvp = dkp + 64 * D;
+    ks_ = 1.f;
+  } else {
+    dkp = a.dk + (((int64_t)b * a.Sk + key) * a.Hkv + hkv) * D;
+    dvp = a.dv + (((int64_t)b * a.Sk + key) * a.Hkv + hkv) * D;
+  }
+  if (split || key < a.Sk) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d = db * 32 + g4 * 8 + hh * 4;
         *reinterpret_cast<f32x4*>(dkp + d) =
-            f32x4{dk[db][g4 * 4] * a.scale, dk[db][g4 * 4 + 1] * a.scale, dk[db][g4 * 4 + 2] * a.scale,
-                  dk[db][g4 * 4 + 3] * a.scale};
+            f32x4{dk[db][g4 * 4] * ks_, dk[db][g4 * 4 + 1] * ks_, dk[db][g4 * 4 + 2] * ks_, dk[db][g4 * 4 + 3] * ks_};
         *reinterpret_cast<f32x4*>(dvp + d) =
             f32x4{dv[db][g4 * 4], dv[db][g4 * 4 + 1], dv[db][g4 * 4 + 2], dv[db][g4 * 4 + 3]};
       }
+  }
+}
+
+// Lists not written by a single dK/dV workgroup: none (zeros) or several chunks (their
+// partials summed in chunk order).  One workgroup per list.
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a) {
+  constexpr int D = TD;
+  const int list = wg_x();
+  const int c0 = a.chunkp[list], n = a.chunkp[list + 1] - c0;
+  if (n == 1) return;  // written by its workgroup
+  const int sub = list % a.nks;
+  const int bh = list / a.nks;
+  const int hkv = bh % a.Hkv, b = bh / a.Hkv;
+  for (int x = tid_x(); x < 2 * 64 * (D / 4); x += 256) {
+    const int which = x / (64 * D / 4);  // 0 dK, 1 dV
+    const int rem = x - which * (64 * D / 4);
+    const int kr = rem / (D / 4), d4 = rem - kr * (D / 4);
+    const int key = sub * 64 + kr;
+    if (key >= a.Sk) continue;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < n; ++c)
+      acc += *reinterpret_cast<const f32x4*>(a.part + (((int64_t)(c0 + c) * 2 + which) * 64 + kr) * D + d4 * 4);
+    if (which == 0) acc *= a.scale;
+    float* dst = (which == 0 ? a.dk : a.dv) + (((int64_t)b * a.Sk + key) * a.Hkv + hkv) * D + d4 * 4;
+    *reinterpret_cast<f32x4*>(dst) = acc;
   }
 }
 

@@ -548,8 +548,8 @@ namespace {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct BwdLayout {
-  int BM = 0, nqb = 0, nks = 0, n_lists = 0;
-  size_t dsum = 0, counts = 0, offsets = 0, cursor = 0, entries = 0, total = 0;
+  int BM = 0, nqb = 0, nks = 0, n_lists = 0, chunk_bound = 0;
+  size_t dsum = 0, counts = 0, offsets = 0, cursor = 0, entries = 0, chunkp = 0, part = 0, total = 0;
 };
 
 // Shapes the backward kernels take; total == 0 otherwise.
@@ -567,16 +567,25 @@ BwdLayout bwd_layout(const bsa_problem& p, const bsa_pattern* pat) {
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t at = off; off = align256(off + bytes); return at; };
   L.dsum = take(sizeof(float) * (size_t)p.B * p.Hq * p.Sq);
+  L.counts = take(sizeof(int32_t) * L.n_lists);
+  L.chunkp = take(sizeof(int32_t) * (L.n_lists + 1));
+  size_t units;  // upper bound on the 32-row slabs over all lists
   if (block) {
     const int Ht = pat->Ht;
     const int mult = Ht == p.Hkv ? p.Hq / p.Hkv : 1;
     const size_t pairs = (size_t)p.B * Ht * L.nqb * pat->cap * (pat->block_N / 64) * mult;
     if (pairs >= (size_t)INT_MAX) return BwdLayout{};
-    L.counts = take(sizeof(int32_t) * L.n_lists);
     L.offsets = take(sizeof(int32_t) * (L.n_lists + 1));
     L.cursor = take(sizeof(int32_t) * L.n_lists);
     L.entries = take(sizeof(int32_t) * pairs);
+    units = pairs * (L.BM / 32);
+  } else {
+    units = (size_t)L.n_lists * (p.Hq / p.Hkv) * ((p.Sq + 31) / 32);
   }
+  const size_t chunks = units / kBwdChunk + L.n_lists;  // ceil per list: at most one extra each
+  if (chunks >= (size_t)INT_MAX / 2) return BwdLayout{};
+  L.chunk_bound = (int)chunks;
+  L.part = take(sizeof(float) * chunks * 2 * 64 * 128);
   L.total = off;
   return L;
 }
@@ -631,13 +640,15 @@ bsa_status bsa_bwd(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, bsa_tens
   a.BM = L.BM;
   a.nqb = L.nqb;
   a.nks = L.nks;
+  a.counts = reinterpret_cast<int32_t*>(base + L.counts);
+  a.chunkp = reinterpret_cast<int32_t*>(base + L.chunkp);
+  a.part = reinterpret_cast<float*>(base + L.part);
   if (pat && pat->kind == BSA_PAT_BLOCK) {
-    a.counts = reinterpret_cast<int32_t*>(base + L.counts);
     a.offsets = reinterpret_cast<int32_t*>(base + L.offsets);
     a.cursor = reinterpret_cast<int32_t*>(base + L.cursor);
     a.entries = reinterpret_cast<int32_t*>(base + L.entries);
   }
-  launch_bwd(a, reinterpret_cast<hipStream_t>(stream));
+  launch_bwd(a, L.chunk_bound, reinterpret_cast<hipStream_t>(stream));
   return launch_status();
 }
 

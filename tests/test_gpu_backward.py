@@ -38,10 +38,14 @@ def _grads(q, k, v, do, pattern=None, causal=True, count=None, index=None, bM=12
     return g, ref
 
 
-@pytest.mark.parametrize("Sq,Sk,causal", [(384, 384, True), (300, 456, False), (200, 328, True)])
-def test_dense(Sq, Sk, causal):
+@pytest.mark.parametrize("Sq,Sk,causal,B", [(384, 384, True, 2), (300, 456, False, 2), (200, 328, True, 2),
+                                            (4096, 4096, True, 1), (2560, 2560, False, 1)])
+def test_dense(Sq, Sk, causal, B):
+    """The last two cases give key blocks more than 128 slabs of queries: their lists are split
+    over several dK/dV workgroups and summed by the reduction (non-causal: every list; causal:
+    the early key blocks only)."""
     say("backward dense", Sq, Sk, causal)
-    q, k, v, do = _data(91, 2, Sq, Sk, 4, 2)
+    q, k, v, do = _data(91, B, Sq, Sk, 4, 2)
     (dq, dk, dv), (rq, rk, rv) = _grads(q, k, v, do, None, causal)
     _check("dq", dq, rq)
     _check("dk", dk, rk)
