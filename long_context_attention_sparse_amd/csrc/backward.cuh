@@ -253,12 +253,13 @@ __device__ __forceinline__ void bwd_stage(uint16_t* tile, const uint16_t* base, 
   }
 }
 
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1))) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int D = TD;
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[32 * kBwdStride];
-  __shared__ __attribute__((aligned(16))) uint16_t Ds[32 * kBwdStride];
-  __shared__ __attribute__((aligned(16))) float ls[32];
-  __shared__ __attribute__((aligned(16))) float dsm[32];
+  constexpr int RS = D;  // 256-byte rows; 16-byte pieces swizzled by row (k_swz), as written by the DMA
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][32 * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t Ds[2][32 * RS];
+  __shared__ __attribute__((aligned(16))) float ls[2][32];
+  __shared__ __attribute__((aligned(16))) float dsm[2][32];
 
   const int n_lists = a.B * a.Hkv * a.nks;
   const int wid = wg_x();
@@ -291,14 +292,28 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void b
     kreg[ks] = as_bf16x8(ok ? ldg128(kbase + (int64_t)key * a.k.ss + ks * 16 + hh * 8) : u32x4{0, 0, 0, 0});
     vreg[ks] = as_bf16x8(ok ? ldg128(vbase + (int64_t)key * a.v.ss + ks * 16 + hh * 8) : u32x4{0, 0, 0, 0});
   }
-  int troff[D / 32];
-  bwd_tr_offsets(l, troff);
+  // operand offsets in a slab tile: A rows (lane's row lq, piece 2ks + hh) and the transposed
+  // reads (rows rr and rr + 8 of a 16-row step, 4 columns of d-block db)
+  int aoff[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) aoff[ks] = lq * RS + (((ks * 2 + hh) ^ k_swz(lq)) << 3);
+  int trlo[D / 32], trhi[D / 32];
+  {
+    const int tg = l >> 4, tr = l & 15;
+    const int rr = (tg >> 1) * 4 + (tr >> 2);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int col = db * 32 + (tg & 1) * 16 + (tr & 3) * 4;
+      trlo[db] = rr * RS + (((col >> 3) ^ k_swz(rr)) << 3) + (col & 7);
+      trhi[db] = (rr + 8) * RS + (((col >> 3) ^ k_swz(rr + 8)) << 3) + (col & 7);
+    }
+  }
   f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
   for (int x = 0; x < D / 32; ++x) dk[x] = dv[x] = f32x16{};
 
   // units: (query head h, first row q0 of a 32-row slab); this workgroup takes chunk
-  // `chunk` of the list's units
+  // `chunk` of the list's units and skips slabs no row of which sees the keys
   const int slabs = a.BM / 32;
   const int total_slabs = (a.Sq + 31) / 32;
   const bool dense = a.pat.kind == 0;
@@ -306,37 +321,64 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void b
   const int list0 = dense ? 0 : a.offsets[list];
   const int n_units = dense ? a.counts[list] : a.counts[list] * slabs;
   const int u0 = chunk * kBwdChunk, u1 = min(n_units, u0 + kBwdChunk);
-  for (int u = u0; u < u1; ++u) {
-    int h, q0;
-    if (dense) {
-      const int per = total_slabs - first_slab;
-      h = hkv * a.G + u / per;
-      q0 = (first_slab + u % per) * 32;
-    } else {
-      const int e = a.entries[list0 + u / slabs];
-      h = e / a.nqb;
-      q0 = (e - h * a.nqb) * a.BM + (u % slabs) * 32;
+  auto next_unit = [&](int u, int& h, int& q0) __attribute__((always_inline)) -> int {
+    for (; u < u1; ++u) {
+      if (dense) {
+        const int per = total_slabs - first_slab;
+        h = hkv * a.G + u / per;
+        q0 = (first_slab + u % per) * 32;
+      } else {
+        const int e = a.entries[list0 + u / slabs];
+        h = e / a.nqb;
+        q0 = (e - h * a.nqb) * a.BM + (u % slabs) * 32;
+      }
+      if (q0 < a.Sq && !(a.causal && q0 + 31 + delta < key0)) return u;
     }
-    if (q0 >= a.Sq || (a.causal && q0 + 31 + delta < key0)) continue;  // uniform: nothing visible
-    const int nrow = min(32, a.Sq - q0);
-    __syncthreads();  // the previous slab is consumed
-    bwd_stage<128>(Qs, reinterpret_cast<const uint16_t*>(a.q.ptr) + (int64_t)b * a.q.sb + (int64_t)q0 * a.q.ss +
-                           (int64_t)h * a.q.sh,
-                   a.q.ss, 32, nrow, t);
-    bwd_stage<128>(Ds, reinterpret_cast<const uint16_t*>(a.dout.ptr) + (int64_t)b * a.dout.sb +
-                           (int64_t)q0 * a.dout.ss + (int64_t)h * a.dout.sh,
-                   a.dout.ss, 32, nrow, t);
-    if (t < 32) {
-      const int64_t r = ((int64_t)b * a.Hq + h) * a.Sq + q0 + t;
-      ls[t] = t < nrow ? a.lse[r] * kLog2e : kNegInf;
-      dsm[t] = t < nrow ? a.dsum[r] : 0.f;
+    return u1;
+  };
+  // Q and dO rows q0 + 16w + 4x + l/16 of the slab (clamped to the last row: finite data the
+  // mask then ignores), lane l into slot l%16; LSE and D of the 32 rows by 8 lanes each
+  const int lrow = l >> 4, lslot = l & 15;
+  auto issue = [&](int h, int q0, int bi) __attribute__((always_inline)) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int rl = w * 16 + x * 4 + lrow;
+      const int gr = min(q0 + rl, a.Sq - 1);
+      const uint32_t piece = (uint32_t)((lslot ^ k_swz(rl)) << 4);
+      const char* qp = reinterpret_cast<const char*>(reinterpret_cast<const uint16_t*>(a.q.ptr) + (int64_t)b * a.q.sb +
+                                                     (int64_t)gr * a.q.ss + (int64_t)h * a.q.sh);
+      const char* dp = reinterpret_cast<const char*>(reinterpret_cast<const uint16_t*>(a.dout.ptr) +
+                                                     (int64_t)b * a.dout.sb + (int64_t)gr * a.dout.ss +
+                                                     (int64_t)h * a.dout.sh);
+      __builtin_amdgcn_global_load_lds(qp + piece, BSA_LDS(Qs[bi] + (w * 4 + x) * 4 * RS), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(dp + piece, BSA_LDS(Ds[bi] + (w * 4 + x) * 4 * RS), 16, 0, 0);
     }
+    if (l < 8) {
+      const int r4 = max(0, min(q0 + 4 * l, a.Sq - 4));  // a clamped group of 4 rows
+      const float* src = (w == 0 ? a.lse : a.dsum) + ((int64_t)b * a.Hq + h) * a.Sq + r4;
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(src), BSA_LDS(w == 0 ? ls[bi] : dsm[bi]), 16, 0,
+                                       0);
+    }
+  };
+
+  int h, q0;
+  int u = next_unit(u0, h, q0);
+  int buf = 0;
+  if (u < u1) issue(h, q0, 0);
+  while (u < u1) {
+    int hn = 0, q0n = 0;
+    const int un = next_unit(u + 1, hn, q0n);
+    // this slab's tiles are in LDS from every wave, and every wave is done with the other buffer
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    if (un < u1) issue(hn, q0n, buf ^ 1);  // the next slab streams in during this one
+    const uint16_t* Qb = Qs[buf];
+    const uint16_t* Db = Ds[buf];
     f32x16 s = {}, dp = {};
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      const u32x4 qa = *reinterpret_cast<const u32x4*>(Qs + lq * kBwdStride + ks * 16 + hh * 8);
-      const u32x4 da = *reinterpret_cast<const u32x4*>(Ds + lq * kBwdStride + ks * 16 + hh * 8);
+      const u32x4 qa = *reinterpret_cast<const u32x4*>(Qb + aoff[ks]);
+      const u32x4 da = *reinterpret_cast<const u32x4*>(Db + aoff[ks]);
       s = mfma32x32x16(as_bf16x8(qa), kreg[ks], s);
       dp = mfma32x32x16(as_bf16x8(da), vreg[ks], dp);
     }
@@ -344,14 +386,14 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void b
     uint32_t pp[8], dd[8];
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
-      const f32x4 lv = *reinterpret_cast<const f32x4*>(ls + g4 * 8 + hh * 4);
-      const f32x4 dm = *reinterpret_cast<const f32x4*>(dsm + g4 * 8 + hh * 4);
+      const f32x4 lv = *reinterpret_cast<const f32x4*>(ls[buf] + g4 * 8 + hh * 4);
+      const f32x4 dm = *reinterpret_cast<const f32x4*>(dsm[buf] + g4 * 8 + hh * 4);
       float p[4], d[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int row = q0 + g4 * 8 + hh * 4 + e;
-        const bool vis = key < a.Sk && lv[e] != kNegInf && (!a.causal || key <= row + delta);
-        p[e] = vis ? exp2_fast(fmaf(s[g4 * 4 + e], a.scale_log2, -lv[e])) : 0.f;
+        const bool vis = key < a.Sk && row < a.Sq && lv[e] != kNegInf && (!a.causal || key <= row + delta);
+        p[e] = vis ? exp2_fast(fmaf(s[g4 * 4 + e], a.scale_log2, -lv[e] * kLog2e)) : 0.f;
         d[e] = p[e] * (dp[g4 * 4 + e] - dm[e]);
       }
       pp[g4 * 2] = pack_bf16x2(p[0], p[1]);
@@ -361,10 +403,24 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void b
     }
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
-      bwd_tr_mfma(Ds, hb * 16, troff, u32x4{pp[hb * 4], pp[hb * 4 + 1], pp[hb * 4 + 2], pp[hb * 4 + 3]}, dv);
-      bwd_tr_mfma(Qs, hb * 16, troff, u32x4{dd[hb * 4], dd[hb * 4 + 1], dd[hb * 4 + 2], dd[hb * 4 + 3]}, dk);
+      const u32x4 pb = {pp[hb * 4], pp[hb * 4 + 1], pp[hb * 4 + 2], pp[hb * 4 + 3]};
+      const u32x4 db_ = {dd[hb * 4], dd[hb * 4 + 1], dd[hb * 4 + 2], dd[hb * 4 + 3]};
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const u32x2 dlo = ds_read_tr16(Db + hb * 16 * RS + trlo[db]);
+        const u32x2 dhi = ds_read_tr16(Db + hb * 16 * RS + trhi[db]);
+        dv[db] = mfma32x32x16(as_bf16x8(u32x4{dlo[0], dlo[1], dhi[0], dhi[1]}), as_bf16x8(pb), dv[db]);
+        const u32x2 qlo = ds_read_tr16(Qb + hb * 16 * RS + trlo[db]);
+        const u32x2 qhi = ds_read_tr16(Qb + hb * 16 * RS + trhi[db]);
+        dk[db] = mfma32x32x16(as_bf16x8(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}), as_bf16x8(db_), dk[db]);
+      }
     }
+    u = un;
+    h = hn;
+    q0 = q0n;
+    buf ^= 1;
   }
+
   // one chunk: the gradients themselves; several: a partial per chunk, summed by bwd_reduce
   float* dkp;
   float* dvp;
