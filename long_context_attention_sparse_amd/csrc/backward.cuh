@@ -14,21 +14,19 @@
 //               32-row query slabs of a 64-key sub-block's list (a list every query block
 //               names, like the first block of a causal pattern, is spread over many
 //               workgroups; their float32 partials are summed in chunk order by bwd_reduce,
-//               so the result does not depend on scheduling): K and V stay
-//               in registers, 32-row slabs of Q and dO pass through LDS; S = Q K^T and
+//               so the result does not depend on scheduling): K and V stay in registers,
+//               32-row slabs of Q and dO stream into LDS (double-buffered direct loads); S = Q K^T and
 //               dP = dO V^T come out with a key per lane, which makes P and dS directly the
 //               B operands of dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T read with the
 //               transposing LDS read)
 //   bwd_dq      one workgroup per (b, head, query block): the forward's tile loop over the
-//               listed keys, rebuilding P^T and dP^T = V dO^T with a query per lane, then
-//               dQ^T += K^T dS^T
+//               listed keys (64-key K and V tiles, double-buffered direct loads), rebuilding
+//               P^T and dP^T = V dO^T with a query per lane, then dQ^T += K^T dS^T
 // No kernel accumulates with atomics: dK/dV belong to one workgroup, dQ to another.
 #pragma once
 #include "tile.cuh"
 
 namespace bsa {
-
-constexpr int kBwdStride = TD + 8;  // LDS row of 136 bf16 (272 bytes): b128 and transposed reads
 
 __device__ __forceinline__ float bf16_lo(uint32_t x) { return bf16_bits_to_f32(x & 0xffffu); }
 __device__ __forceinline__ float bf16_hi(uint32_t x) { return bf16_bits_to_f32(x >> 16); }
@@ -216,40 +214,6 @@ __global__ __launch_bounds__(256) void bwd_fill_kernel(BwdArgs a) {
         a.entries[atomicAdd(&hist[sub], 1)] = h * a.nqb + i;
       }
     }
-  }
-}
-
-// Per-lane LDS offsets of the transposed A-operand reads (32 rows of d x 16 rows of the
-// tile) from a row-major tile with kBwdStride rows: lane l of 16-lane group tg points at
-// tile row 4(tg / 2) + (l % 16) / 4 and 4 columns 32 db + 16 (tg % 2) + 4 (l % 4).
-__device__ __forceinline__ void bwd_tr_offsets(int l, int* off) {
-  const int tg = l >> 4, tr = l & 15;
-  const int row = (tg >> 1) * 4 + (tr >> 2);
-#pragma unroll
-  for (int db = 0; db < TD / 32; ++db) off[db] = row * kBwdStride + db * 32 + (tg & 1) * 16 + (tr & 3) * 4;
-}
-
-// acc[db] += X^T(32 d x 16 rows) * B for the 16 tile rows r0..r0+15 (rows r0 + 4hh + 0..3
-// and r0 + 8 + 4hh + 0..3 in the 8 k slots, the order of the accumulator registers).
-__device__ __forceinline__ void bwd_tr_mfma(const uint16_t* tile, int r0, const int* off, const u32x4& bop,
-                                            f32x16* acc) {
-#pragma unroll
-  for (int db = 0; db < TD / 32; ++db) {
-    const u32x2 lo = ds_read_tr16(tile + r0 * kBwdStride + off[db]);
-    const u32x2 hi = ds_read_tr16(tile + (r0 + 8) * kBwdStride + off[db]);
-    acc[db] = mfma32x32x16(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), as_bf16x8(bop), acc[db]);
-  }
-}
-
-// 32 rows x 128 bf16 from global rows (row_ptr(r) valid for r < n_valid, zeros past it) into
-// an LDS tile; nt threads.
-template <int NT>
-__device__ __forceinline__ void bwd_stage(uint16_t* tile, const uint16_t* base, int64_t ss, int rows, int n_valid,
-                                          int t) {
-  for (int x = t; x < rows * 16; x += NT) {
-    const int r = x >> 4, piece = x & 15;
-    const u32x4 v = r < n_valid ? ldg128(base + (int64_t)r * ss + piece * 8) : u32x4{0, 0, 0, 0};
-    *reinterpret_cast<u32x4*>(tile + r * kBwdStride + piece * 8) = v;
   }
 }
 
@@ -473,11 +437,12 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a) {
 }
 
 template <int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4 ? 2 : 1))) void bwd_dq_kernel(BwdArgs a) {
   constexpr int D = TD;
-  constexpr int NT = NW * 64;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[64 * kBwdStride];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[64 * kBwdStride];
+  constexpr int RS = D;  // 256-byte rows, 16-byte pieces swizzled by row (k_swz)
+  constexpr int RPW = 64 / NW;  // tile rows each wave loads
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][64 * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][64 * RS];
 
   const int item = wg_x();
   const int i = item % a.nqb;
@@ -506,14 +471,26 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const float lse2 = row_ok ? a.lse[rr] * kLog2e : kNegInf;
   const float dsv = row_ok ? a.dsum[rr] : 0.f;
   const int lim = !row_ok || lse2 == kNegInf ? -1 : (a.causal ? min(row + delta, a.Sk - 1) : a.Sk - 1);
-  int troff[D / 32];
-  bwd_tr_offsets(l, troff);
+  int koff[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) koff[ks] = lq * RS + (((ks * 2 + hh) ^ k_swz(lq)) << 3);
+  int trlo[D / 32], trhi[D / 32];
+  {
+    const int tg = l >> 4, tr = l & 15;
+    const int r4 = (tg >> 1) * 4 + (tr >> 2);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int col = db * 32 + (tg & 1) * 16 + (tr & 3) * 4;
+      trlo[db] = r4 * RS + (((col >> 3) ^ k_swz(r4)) << 3) + (col & 7);
+      trhi[db] = (r4 + 8) * RS + (((col >> 3) ^ k_swz(r4 + 8)) << 3) + (col & 7);
+    }
+  }
   f32x16 dq[D / 32];
 #pragma unroll
   for (int x = 0; x < D / 32; ++x) dq[x] = f32x16{};
 
   // the 64-key sub-blocks to visit
-  int n_sub, spe = 1, n_ent = 0;
+  int n_sub, spe = 1;
   const int32_t* list = nullptr;
   const int last_row = min(r0 + a.BM, a.Sq) - 1;
   if (a.pat.kind == 0) {
@@ -522,31 +499,55 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   } else {
     const int ht = a.list_by_kv ? hkv : h;
     const int64_t lb = (int64_t)b * a.pat.s_b + (int64_t)ht * a.pat.s_h + (int64_t)i * a.pat.s_q;
-    n_ent = a.pat.count[lb];
     list = a.pat.index + lb * a.pat.cap;
     spe = a.pat.block_N / 64;
-    n_sub = n_ent * spe;
+    n_sub = a.pat.count[lb] * spe;
   }
-  for (int x = 0; x < n_sub; ++x) {
-    const int sub = a.pat.kind == 0 ? x : list[x / spe] * spe + x % spe;
-    const int key0 = sub * 64;
-    if (key0 < 0 || key0 >= a.Sk || (a.causal && key0 > last_row + delta)) continue;  // uniform
-    const int nkey = min(64, a.Sk - key0);
+  auto next_sub = [&](int x, int& key0) __attribute__((always_inline)) -> int {
+    for (; x < n_sub; ++x) {
+      key0 = (a.pat.kind == 0 ? x : list[x / spe] * spe + x % spe) * 64;
+      if (key0 >= 0 && key0 < a.Sk && !(a.causal && key0 > last_row + delta)) return x;
+    }
+    return n_sub;
+  };
+  // K and V rows key0 + RPW w + 4x + l/16 (clamped to the last key: finite, masked), lane l
+  // into slot l%16
+  const int lrow = l >> 4, lslot = l & 15;
+  const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.k.ptr) + (int64_t)b * a.k.sb + (int64_t)hkv * a.k.sh;
+  const uint16_t* vbase = reinterpret_cast<const uint16_t*>(a.v.ptr) + (int64_t)b * a.v.sb + (int64_t)hkv * a.v.sh;
+  auto issue = [&](int key0, int bi) __attribute__((always_inline)) {
+#pragma unroll
+    for (int x = 0; x < RPW / 4; ++x) {
+      const int rl = w * RPW + x * 4 + lrow;
+      const int gk = min(key0 + rl, a.Sk - 1);
+      const uint32_t piece = (uint32_t)((lslot ^ k_swz(rl)) << 4);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(kbase + (int64_t)gk * a.k.ss) + piece,
+                                       BSA_LDS(Ks[bi] + (w * RPW + x * 4) * RS), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(vbase + (int64_t)gk * a.v.ss) + piece,
+                                       BSA_LDS(Vs[bi] + (w * RPW + x * 4) * RS), 16, 0, 0);
+    }
+  };
+
+  int key0 = 0;
+  int x = next_sub(0, key0);
+  int buf = 0;
+  if (x < n_sub) issue(key0, 0);
+  while (x < n_sub) {
+    int key0n = 0;
+    const int xn = next_sub(x + 1, key0n);
+    // this block's K and V are in LDS from every wave; every wave is done with the other buffer
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    bwd_stage<NT>(Ks, reinterpret_cast<const uint16_t*>(a.k.ptr) + (int64_t)b * a.k.sb + (int64_t)key0 * a.k.ss +
-                          (int64_t)hkv * a.k.sh,
-                  a.k.ss, 64, nkey, t);
-    bwd_stage<NT>(Vs, reinterpret_cast<const uint16_t*>(a.v.ptr) + (int64_t)b * a.v.sb + (int64_t)key0 * a.v.ss +
-                          (int64_t)hkv * a.v.sh,
-                  a.v.ss, 64, nkey, t);
-    __syncthreads();
+    if (xn < n_sub) issue(key0n, buf ^ 1);
+    const uint16_t* Kb = Ks[buf];
+    const uint16_t* Vb = Vs[buf];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       f32x16 st = {}, dpt = {};
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
-        const u32x4 ka = *reinterpret_cast<const u32x4*>(Ks + (kb * 32 + lq) * kBwdStride + ks * 16 + hh * 8);
-        const u32x4 va = *reinterpret_cast<const u32x4*>(Vs + (kb * 32 + lq) * kBwdStride + ks * 16 + hh * 8);
+        const u32x4 ka = *reinterpret_cast<const u32x4*>(Kb + kb * 32 * RS + koff[ks]);
+        const u32x4 va = *reinterpret_cast<const u32x4*>(Vb + kb * 32 * RS + koff[ks]);
         st = mfma32x32x16(as_bf16x8(ka), qreg[ks], st);
         dpt = mfma32x32x16(as_bf16x8(va), doreg[ks], dpt);
       }
@@ -564,10 +565,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         dd[r / 2] = pack_bf16x2(d2[0], d2[1]);
       }
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb)
-        bwd_tr_mfma(Ks, kb * 32 + hb * 16, troff, u32x4{dd[hb * 4], dd[hb * 4 + 1], dd[hb * 4 + 2], dd[hb * 4 + 3]},
-                    dq);
+      for (int hb = 0; hb < 2; ++hb) {
+        const u32x4 bop = {dd[hb * 4], dd[hb * 4 + 1], dd[hb * 4 + 2], dd[hb * 4 + 3]};
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const u32x2 lo = ds_read_tr16(Kb + (kb * 32 + hb * 16) * RS + trlo[db]);
+          const u32x2 hi = ds_read_tr16(Kb + (kb * 32 + hb * 16) * RS + trhi[db]);
+          dq[db] = mfma32x32x16(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), as_bf16x8(bop), dq[db]);
+        }
+      }
     }
+    x = xn;
+    key0 = key0n;
+    buf ^= 1;
   }
   if (row_ok) {
     float* dqp = a.dq + (((int64_t)b * a.Sq + row) * a.Hq + h) * D;
