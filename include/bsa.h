@@ -9,6 +9,17 @@
  * reported through the returned status; nothing is launched when
  * validation fails.  No exception crosses this interface.
  *
+ * Host validation covers shapes, strides, pointers and sizes, not the
+ * contents of key patterns (that would need a device round trip).  With the
+ * environment variable BSA_DEBUG_CHECKS set to anything but "" or "0", the
+ * entry points that take a BLOCK or VS pattern (bsa_fwd, bsa_fwd_partials,
+ * bsa_speculative_sparse, bsa_speculative_partials, bsa_bwd) first run the
+ * bsa_check_pattern kernel on the caller's stream, wait for it, and return
+ * BSA_ERR_INVALID_ARG for a pattern that breaks its rules.  That mode
+ * synchronises the stream, cannot be captured in a graph, and keeps its
+ * answer in one library-resident int32 pair per device (concurrent debug
+ * checks on one device share it).  It is meant for development.
+ *
  * Sources of the operations (cited by page title and section):
  *   [IR]   "Sparse FlashAttention with Incremental Repair" (README):
  *          What's in this fork; Usage sections 1 (sparse-only forward),
@@ -126,6 +137,27 @@ typedef struct {
 
 /* Human-readable name of a status code (static storage). */
 const char* bsa_status_string(bsa_status s);
+
+/* Checks the contents of a BLOCK or VS pattern on the device: the rules the
+ * attention kernels rely on without checking them.  BLOCK ([IR] Usage 1):
+ * 0 <= count <= cap; ids j >= 0 with j*block_N below the key length of the
+ * list's sequence; no id twice in a list.  VS ([SGL] I/O Contract): window
+ * starts in [0, key length), ascending, each at least block_N past the one
+ * before (disjoint windows); 0 <= col_count <= col_cap; columns in
+ * [0, key length), strictly ascending, none inside a window.
+ * Lists checked: every (b, h_t, m) with b < B, h_t < Ht and
+ * m < ceil(Sq / block_M) (varlen: the sequence's own query blocks; key
+ * length Sk, or the sequence's own length from cu_seqlens_k).
+ *   result  device int32[2], written on the stream: result[0] = number of
+ *           violating lists, result[1] = the smallest flat list index
+ *           (b*Ht + h_t) * nqb + m among them (INT32_MAX if none), where
+ *           nqb = ceil(Sq / block_M) (varlen: ceil(max_seqlen_q / block_M)).
+ * Asynchronous like the other entry points; the caller reads result after
+ * the stream has passed the call.
+ * Errors: BSA_ERR_INVALID_ARG for NULL arguments, a DENSE or NULL pattern,
+ * or what bsa_fwd rejects in the problem sizes or pattern header;
+ * BSA_ERR_HIP on launch failure. */
+bsa_status bsa_check_pattern(const bsa_problem* prob, const bsa_pattern* pat, int32_t* result, bsa_stream stream);
 
 /* Bytes of workspace bsa_fwd needs for this problem and pattern (0 when the
  * chosen kernel needs none).  Returns 0 on invalid arguments as well; the

@@ -26,7 +26,7 @@ EXPORTS = ("bsa_status_string", "bsa_workspace_size", "bsa_fwd", "bsa_fwd_partia
            "bsa_speculative_sparse", "bsa_speculative_partials", "bsa_speculative_num_partials",
            "bsa_speculative_workspace_size", "bsa_combine", "bsa_fwd_gated", "bsfa_calibrate",
            "bsa_selected_workspace_size", "bsa_fwd_selected", "bsa_bwd_workspace_size", "bsa_bwd",
-           "vs_convert_indexes", "vs_convert_indexes_mergehead")
+           "vs_convert_indexes", "vs_convert_indexes_mergehead", "bsa_check_pattern")
 
 
 class BSAError(RuntimeError):
@@ -119,6 +119,9 @@ def load(path: str = LIB_PATH):
     lib.vs_convert_indexes_mergehead.restype = ctypes.c_int
     lib.vs_convert_indexes_mergehead.argtypes = ([ctypes.c_void_p] * 6 + [ctypes.c_int32] * 8 +
                                                  [ctypes.c_void_p] * 5)
+    lib.bsa_check_pattern.restype = ctypes.c_int
+    lib.bsa_check_pattern.argtypes = [ctypes.POINTER(_Problem), ctypes.POINTER(_Pattern), ctypes.c_void_p,
+                                      ctypes.c_void_p]
     _lib = lib
     return lib
 
@@ -272,6 +275,23 @@ def bsa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pattern=None, *, 
                      _tensor(out, varlen), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream))
     _check("bsa_fwd", st)
     return out, lse
+
+
+def bsa_check_pattern(q, k, pattern, *, causal: bool = False, cu_seqlens_q=None, cu_seqlens_k=None,
+                      max_seqlen_q: int = 0, max_seqlen_k: int = 0, result: Optional[torch.Tensor] = None,
+                      stream=None) -> torch.Tensor:
+    """Checks a BlockPattern or VSPattern on the device against the rules the attention kernels
+    assume (ids in range and distinct; VS windows ascending and disjoint, columns ascending and
+    outside the windows).  Returns int32 [2] on the device: (violating lists, first violating
+    flat list index (b * Ht + h) * nQB + m, or 2**31 - 1 when there is none)."""
+    prob = _problem(q, k, causal, None, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
+    pat = pattern.struct(prob.Hq)
+    if result is None:
+        result = torch.empty(2, dtype=torch.int32, device=q.device)
+    _i32(result, "result")
+    _check("bsa_check_pattern", load().bsa_check_pattern(ctypes.byref(prob), ctypes.byref(pat), _ptr(result),
+                                                         _stream(stream)))
+    return result
 
 
 def bsa_num_partials(q, k, pattern=None, entries_per_partial: int = 1, causal: bool = False) -> int:

@@ -18,6 +18,7 @@ LIB = os.path.join(PKG, "libbsa.so")
 SOURCES = [
     ("bsa_api.hip", []),
     ("kernels_stream.hip", []),
+    ("kernels_check.hip", []),
     # the tile kernels never create NaNs (masked scores are -inf, handled explicitly), so
     # max needs no NaN-quieting canonicalisation: plain v_max/v_max3 in the softmax
     ("kernels_tile.hip", ["-fno-honor-nans", "-mno-amdgpu-ieee"]),

@@ -170,4 +170,13 @@ struct VSConvArgs {
   int32_t* ci;              // [B, H, rows, nnz_v]
 };
 
+// Pattern contents check (check.cuh).
+struct CheckArgs {
+  PatternArg pat;
+  const int32_t* cu_q;  // varlen prefix sums or null
+  const int32_t* cu_k;
+  int B, Ht, nqb, Sk;   // Sk: key length (fixed length)
+  int32_t* result;      // [2]: violations, first violating list
+};
+
 }  // namespace bsa

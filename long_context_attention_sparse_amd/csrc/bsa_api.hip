@@ -9,6 +9,7 @@
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 
 #include "args.cuh"
@@ -104,6 +105,34 @@ bsa_status check_pattern(const bsa_problem& p, const bsa_pattern* pat) {
     if (pat->block_M > pat->block_N) return BSA_ERR_UNSUPPORTED;
   }
   return BSA_OK;
+}
+
+// Pattern validation on the device (bsa_check_pattern; BSA_DEBUG_CHECKS).
+CheckArgs check_args(const bsa_problem& p, const bsa_pattern* pat, int32_t* result) {
+  CheckArgs a{};
+  a.pat = parg(pat);
+  a.cu_q = p.cu_seqlens_q;
+  a.cu_k = p.cu_seqlens_k;
+  a.B = p.B;
+  a.Ht = pat->Ht;
+  const int sq = p.cu_seqlens_q ? p.max_seqlen_q : p.Sq;
+  a.nqb = (sq + pat->block_M - 1) / pat->block_M;
+  a.Sk = p.cu_seqlens_q ? p.max_seqlen_k : p.Sk;
+  a.result = result;
+  return a;
+}
+
+bool debug_checks_on() {
+  const char* e = std::getenv("BSA_DEBUG_CHECKS");
+  return e && *e && std::strcmp(e, "0") != 0;
+}
+
+// With BSA_DEBUG_CHECKS set: check the pattern on the device, wait for the answer and refuse
+// a violating one before anything is launched.
+bsa_status debug_validate(const bsa_problem& p, const bsa_pattern* pat, bsa_stream stream) {
+  if (!pat || pat->kind == BSA_PAT_DENSE || !debug_checks_on()) return BSA_OK;
+  const int r = debug_check(check_args(p, pat, nullptr), reinterpret_cast<hipStream_t>(stream));
+  return r == 0 ? BSA_OK : (r < 0 ? BSA_ERR_HIP : BSA_ERR_INVALID_ARG);
 }
 
 // ---------------------------------------------------------------------------
@@ -341,6 +370,8 @@ bsa_status bsa_fwd(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, bsa_tens
   const bsa_problem& p = *prob;
   st = check_pattern(p, pat);
   if (st != BSA_OK) return st;
+  st = debug_validate(p, pat, stream);
+  if (st != BSA_OK) return st;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   const DecodePlan d = plan_decode(p, pat);
   if (!d.use) return run_prefill(p, q, k, v, pat, &o, lse, 0, 0, nullptr, nullptr, hs);
@@ -392,6 +423,8 @@ bsa_status bsa_fwd_partials(const bsa_problem* prob, bsa_tensor q, bsa_tensor k,
   const bsa_problem& p = *prob;
   if (p.cu_seqlens_q || (pat && pat->kind == BSA_PAT_VS)) return BSA_ERR_UNSUPPORTED;
   st = check_pattern(p, pat);
+  if (st != BSA_OK) return st;
+  st = debug_validate(p, pat, stream);
   if (st != BSA_OK) return st;
   if (reinterpret_cast<uintptr_t>(o_part) & 15) return BSA_ERR_INVALID_ARG;
   const SegPlan sp = partials_plan(p, pat, entries_per_partial);
@@ -449,6 +482,8 @@ bsa_status bsa_speculative_partials(const bsa_problem* prob, bsa_tensor q, bsa_t
   if (!aligned_rows(k_spec, 2) || !aligned_rows(v_spec, 2)) return BSA_ERR_INVALID_ARG;
   if (!missed || missed->kind != BSA_PAT_BLOCK) return BSA_ERR_INVALID_ARG;
   st = check_pattern(p, missed);
+  if (st != BSA_OK) return st;
+  st = debug_validate(p, missed, stream);
   if (st != BSA_OK) return st;
   SegPlan segs[2];
   DecodePlan d;
@@ -543,6 +578,8 @@ bsa_status bsa_fwd_gated(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, bs
 // Backward of block-sparse attention
 // ---------------------------------------------------------------------------
 
+}  // extern "C"
+
 namespace {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -592,6 +629,8 @@ BwdLayout bwd_layout(const bsa_problem& p, const bsa_pattern* pat) {
 
 }  // namespace
 
+extern "C" {
+
 size_t bsa_bwd_workspace_size(const bsa_problem* prob, const bsa_pattern* pat) {
   if (!prob || check_pattern(*prob, pat) != BSA_OK) return 0;
   return bwd_layout(*prob, pat).total;
@@ -604,6 +643,8 @@ bsa_status bsa_bwd(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, bsa_tens
   if (st != BSA_OK) return st;
   const bsa_problem& p = *prob;
   st = check_pattern(p, pat);
+  if (st != BSA_OK) return st;
+  st = debug_validate(p, pat, stream);
   if (st != BSA_OK) return st;
   if (!lse || !dout.ptr || !dq || !dk || !dv) return BSA_ERR_INVALID_ARG;
   if (dout.dtype != BSA_BF16) return BSA_ERR_UNSUPPORTED;
@@ -656,6 +697,8 @@ bsa_status bsa_bwd(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, bsa_tens
 // Selected attention (top-k key blocks per query token)
 // ---------------------------------------------------------------------------
 
+}  // extern "C"
+
 namespace {
 
 struct SelLayout {
@@ -697,6 +740,8 @@ SelLayout sel_layout(const bsa_problem& p, int32_t total_q, int32_t topk) {
 }
 
 }  // namespace
+
+extern "C" {
 
 size_t bsa_selected_workspace_size(const bsa_problem* prob, int32_t total_q, int32_t topk, int32_t block_size) {
   if (!prob || block_size != 64) return 0;
@@ -809,6 +854,19 @@ static bsa_status vs_convert_impl(const int32_t* q_seqlens, const int32_t* kv_se
   a.rows = (context_size + block_M - 1) / block_M;
   const int lds_ints = nnz_s + nnz_v <= kVSConvLdsInts ? nnz_s + nnz_v : 0;
   launch_vs_convert(a, lds_ints * sizeof(int32_t), reinterpret_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+bsa_status bsa_check_pattern(const bsa_problem* prob, const bsa_pattern* pat, int32_t* result, bsa_stream stream) {
+  if (!prob || !pat || !result || (reinterpret_cast<uintptr_t>(result) & 3)) return BSA_ERR_INVALID_ARG;
+  const bsa_problem& p = *prob;
+  if (p.B <= 0 || p.Hq <= 0 || p.Hkv <= 0 || p.Sq <= 0 || p.Sk <= 0 || p.Hq % p.Hkv) return BSA_ERR_INVALID_ARG;
+  if ((p.cu_seqlens_q == nullptr) != (p.cu_seqlens_k == nullptr)) return BSA_ERR_INVALID_ARG;
+  if (p.cu_seqlens_q && (p.max_seqlen_q <= 0 || p.max_seqlen_k <= 0)) return BSA_ERR_INVALID_ARG;
+  const bsa_status st = check_pattern(p, pat);
+  if (st != BSA_OK) return st;
+  if (pat->kind == BSA_PAT_DENSE) return BSA_ERR_INVALID_ARG;
+  launch_check(check_args(p, pat, result), reinterpret_cast<hipStream_t>(stream));
   return launch_status();
 }
 

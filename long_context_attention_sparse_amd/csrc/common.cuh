@@ -57,7 +57,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
-
 // acc + (both bf16 values packed in u), as one v_dot2_f32_bf16 against (1, 1).
 __device__ __forceinline__ float bf16x2_sum_acc(uint32_t u, float acc) {
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};

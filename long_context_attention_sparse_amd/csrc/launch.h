@@ -1,6 +1,7 @@
 // Host-side launch wrappers, one per kernel family, defined in the translation unit that
 // instantiates the kernels (kernels_stream.hip, kernels_tile.hip, kernels_select.hip,
-// kernels_bwd.hip) so that each family is compiled with its own code-generation flags.
+// kernels_bwd.hip, kernels_check.hip) so that each family is compiled with its own
+// code-generation flags.
 #pragma once
 #include <hip/hip_runtime.h>
 
@@ -28,5 +29,10 @@ void launch_bwd(const BwdArgs& a, int chunk_bound, hipStream_t st);
 // selected attention: sel_zero, sel_count, sel_scan, sel_fill, then selected_kernel over
 // main_grid workgroups (an upper bound on the chunks; the surplus exits at once).
 void launch_selected(const SelArgs& a, int main_grid, hipStream_t st);
+
+// pattern check: result[0] = violating lists, result[1] = the first one (flat index).
+void launch_check(const CheckArgs& a, hipStream_t st);
+// The same check into the library's own result words, waited for: violations or -1.
+int debug_check(CheckArgs a, hipStream_t st);
 
 }  // namespace bsa

@@ -191,3 +191,24 @@ def test_gated_and_vs_convert_errors(lib):
     assert mh(x, x, x, x, x, None, 1, 1, 4, 4, 256, 64, 64, 1, x, x, x, x, None) == bd.BSA_ERR_INVALID_ARG
     assert mh(x, x, x, x, x, x, 1, 1, 4, 4, 256, 64, 64, 0, x, x, x, x, None) == bd.BSA_ERR_UNSUPPORTED
     assert mh(x, x, x, x, x, x, 0, 1, 4, 4, 256, 64, 64, 1, x, x, x, x, None) == bd.BSA_ERR_INVALID_ARG
+
+
+def test_check_pattern_errors(lib):
+    cnt = ctypes.c_int32(0)
+    idx = (ctypes.c_int32 * 4)()
+    res = (ctypes.c_int32 * 3)()
+    addr = ctypes.addressof
+    ok = bd._Pattern(1, 2, 128, 64, 4, 0, addr(cnt), addr(idx), None, None, 0, 0, 0)
+    prob = _prob()
+    chk = lib.bsa_check_pattern
+    assert chk(None, ctypes.byref(ok), addr(res), None) == bd.BSA_ERR_INVALID_ARG
+    assert chk(ctypes.byref(prob), None, addr(res), None) == bd.BSA_ERR_INVALID_ARG           # no pattern
+    assert chk(ctypes.byref(prob), ctypes.byref(ok), None, None) == bd.BSA_ERR_INVALID_ARG     # no result
+    assert chk(ctypes.byref(prob), ctypes.byref(ok), addr(res) + 2, None) == bd.BSA_ERR_INVALID_ARG  # misaligned
+    assert chk(ctypes.byref(_prob(Hq=3, Hkv=2)), ctypes.byref(ok), addr(res), None) == bd.BSA_ERR_INVALID_ARG
+    dense = bd._Pattern(0, 2, 128, 64, 4, 0, addr(cnt), addr(idx), None, None, 0, 0, 0)
+    assert chk(ctypes.byref(prob), ctypes.byref(dense), addr(res), None) == bd.BSA_ERR_INVALID_ARG
+    bad_n = bd._Pattern(1, 2, 128, 96, 4, 0, addr(cnt), addr(idx), None, None, 0, 0, 0)
+    assert chk(ctypes.byref(prob), ctypes.byref(bad_n), addr(res), None) == bd.BSA_ERR_UNSUPPORTED
+    vs_nocols = bd._Pattern(2, 2, 64, 64, 4, 4, addr(cnt), addr(idx), None, None, 0, 0, 0)
+    assert chk(ctypes.byref(prob), ctypes.byref(vs_nocols), addr(res), None) == bd.BSA_ERR_INVALID_ARG
