@@ -92,11 +92,11 @@ def run_steps(torch, step, timer, steps, warmup):
 # counter reads for a 1 GiB device copy (FETCH_SIZE reads half the bytes: x2.0; WRITE_SIZE
 # x1.0).  Valid only for the sources the counters were taken on: the digest covers the
 # kernel, its launch planning and the workload generator, and a mismatch reports null.
-DECODE_TRAFFIC = {"bytes": 1_287_914_496, "fetch_kib": 624_964, "write_kib": 7_801,
-                  "sha256": "07e5e15de0e6c9781db566eff26e6be35fba800563507da97f1b3a7bf67e976b"}
-TRAFFIC_SOURCES = ["long_context_attention_sparse_amd/csrc/decode.cuh", "long_context_attention_sparse_amd/csrc/common.cuh",
-                   "long_context_attention_sparse_amd/csrc/args.cuh", "long_context_attention_sparse_amd/csrc/kernels_stream.hip",
-                   "long_context_attention_sparse_amd/csrc/bsa_api.hip", "synth/workloads.py"]
+DECODE_TRAFFIC = {"bytes": 1_287_891_302, "fetch_kib": 624_953, "write_kib": 7_801,
+                  "sha256": "cc845210eed7fe027faf5019c05f26cdeafbd76fc4919ef50cd7867904f5cccb"}
+TRAFFIC_SOURCES = ["long_context_attention_sparse_amd/csrc/" + f for f in
+                   ("decode.cuh", "common.cuh", "args.cuh", "kernels_stream.hip", "decode_plan.h", "host_args.h")] + \
+                  ["synth/workloads.py"]
 
 
 def sources_digest():
@@ -152,6 +152,25 @@ def kernel_mean_ms(torch, fn, per_graph=10, replays=5):
         b.record()
         torch.cuda.synchronize()
         ms.append(a.elapsed_time(b) / per_graph)
+    return float(np.mean(ms))
+
+
+def kernel_mean_ms_flushed(torch, fn, reps=10):
+    """Mean device time of the launch fn makes when neither L2 nor the memory-side cache holds
+    its inputs: a 1 GiB buffer is written before every launch, HIP events around the launch."""
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    ms = []
+    for i in range(reps + 1):
+        scratch.fill_(i & 0xFF)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        if i:
+            ms.append(a.elapsed_time(b))
+    del scratch
     return float(np.mean(ms))
 
 
@@ -217,6 +236,7 @@ def bench_spec_decode(torch, bsa, args):
         # a decode step replays as one HIP graph (launch overhead off the critical path)
         ms = run_graph_steps(torch, capture(torch, full_step), args.steps)
         pass_ms = kernel_mean_ms(torch, passes)
+    flushed_ms = kernel_mean_ms_flushed(torch, passes)
     groups = B * Hkv
     blk_bytes = bs * D * 2 * 2
     kv_bytes = groups * (n_missed + (Sk - s0) // bs) * blk_bytes
@@ -256,7 +276,9 @@ def bench_spec_decode(torch, bsa, args):
                   "frac": round(achieved / HBM_PEAK_GBS, 4),
                   "traffic": DECODE_TRAFFIC["bytes"] if DECODE_TRAFFIC["sha256"] == sources_digest() else None,
                   "kernel": "decode_kernel<128> (speculative and repair passes, one launch)",
-                  "algorithmic_bytes": pass_bytes, "avg_ms": round(pass_ms, 5)},
+                  "algorithmic_bytes": pass_bytes, "avg_ms": round(pass_ms, 5),
+                  "caches_flushed": {"avg_ms": round(flushed_ms, 5),
+                                     "achieved": round(pass_bytes / (flushed_ms * 1e-3) / 1e9, 1)}},
         cpu_baseline=cpu)
 
 

@@ -32,7 +32,6 @@ constexpr int kVSConvLdsInts = 16384;  // slash + vertical entries staged in LDS
 constexpr int kThreshMaxCand = 4096;   // threshold selection: query blocks per row (LDS candidates)
 constexpr int kSelTile = 1024;         // selected attention: token positions per index workgroup
 constexpr int kSelMaxBlocks = 8192;    // selected attention: key blocks per sequence (LDS histogram)
-constexpr int kBwdMaxSub = 8192;       // backward: 64-key sub-blocks per sequence (LDS histogram)
 constexpr int kBwdChunk = 128;         // backward: 32-row query slabs per dK/dV workgroup
 
 struct DecodeSeg {
@@ -131,15 +130,17 @@ struct BwdArgs {
   int causal;
   float scale, scale_log2;
   int BM;                      // query block rows of the pattern (64 or 128; dense: 128)
-  int nqb, nks;                // query blocks; 64-key sub-blocks
-  // per 64-key sub-block ("list"): its (query head, query block) pairs (block patterns), its
-  // units of work (32-row query slabs), and those units cut into chunks of kBwdChunk
+  int SB;                      // keys per sub-block (list): 32 per dK/dV wave, at most the pattern's block_N
+  int nqb, nks;                // query blocks; sub-blocks
+  int nkb, W;                  // pattern key blocks; bitmap words per (list head, key block)
+  // per sub-block ("list"): its (query head, query block) pairs (block patterns), its units of
+  // work (32-row query slabs), and those units cut into chunks of kBwdChunk
   int32_t* counts;             // [lists]: pairs (block patterns) or units (dense)
   int32_t* offsets;            // [lists + 1] prefix sums of pairs (block patterns)
-  int32_t* cursor;             // [lists]
   int32_t* entries;            // h * nqb + i
   int32_t* chunkp;             // [lists + 1] prefix sums of chunks
-  float* part;                 // [chunks, 2, 64, D]: dK^T / dV^T partials of lists cut into chunks
+  uint32_t* bits;              // [B, Ht, nkb, W]: which query blocks name each key block
+  float* part;                 // [chunks, 2, SB, D]: dK / dV partials of lists cut into chunks
 };
 
 struct ThresholdArgs {

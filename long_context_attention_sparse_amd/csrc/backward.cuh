@@ -8,17 +8,18 @@
 // P is rebuilt from the forward's LSE: P = exp(S - LSE).
 //
 //   bwd_dot     D for every (b, h, row)
-//   bwd_count / bwd_scan / bwd_fill (block patterns): for every 64-key sub-block, the list
-//               of (query head, query block) pairs whose key lists name it
+//   bwd_bits_* / bwd_list_count / bwd_scan / bwd_list_fill (block patterns): for every
+//               sub-block of SB = 64 keys, the list of (query head, query block) pairs whose
+//               key lists name it, in a fixed order
 //   bwd_dkdv    one workgroup (two waves, 32 keys each) per chunk of up to kBwdChunk
-//               32-row query slabs of a 64-key sub-block's list (a list every query block
-//               names, like the first block of a causal pattern, is spread over many
-//               workgroups; their float32 partials are summed in chunk order by bwd_reduce,
-//               so the result does not depend on scheduling): K and V stay in registers,
-//               32-row slabs of Q and dO stream into LDS (double-buffered direct loads); S = Q K^T and
-//               dP = dO V^T come out with a key per lane, which makes P and dS directly the
-//               B operands of dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T read with the
-//               transposing LDS read)
+//               32-row query slabs of a sub-block's list (a list every query block names,
+//               like the first block of a causal pattern, is spread over many workgroups;
+//               their float32 partials are summed in chunk order by bwd_reduce, so the
+//               result does not depend on scheduling): K and V stay in registers, 32-row
+//               slabs of Q and dO stream into LDS (double-buffered direct loads) and are
+//               shared by the waves; S = Q K^T and dP = dO V^T come out with a key per lane,
+//               which makes P and dS directly the B operands of dV^T += dO^T P and
+//               dK^T += Q^T dS (dO^T, Q^T read with the transposing LDS read)
 //   bwd_dq      one workgroup per (b, head, query block): the forward's tile loop over the
 //               listed keys (64-key K and V tiles, double-buffered direct loads), rebuilding
 //               P^T and dP^T = V dO^T with a query per lane, then dQ^T += K^T dS^T
@@ -69,20 +70,88 @@ __global__ __launch_bounds__(256) void bwd_dot_kernel(BwdArgs a) {
   if (part == 0) a.dsum[((int64_t)b * a.Hq + h) * a.Sq + s] = acc;
 }
 
-// ---- key-sub-block lists (block patterns) ----
-// One workgroup per (b, list head): an LDS histogram of the sub-blocks its lists name
-// (G entries per name when the lists belong to kv heads), then one global add per bin.
-__device__ __forceinline__ void bwd_list_head(const BwdArgs& a, int& b, int& ht, int& Ht, int& hkv) {
-  Ht = a.list_by_kv ? a.Hkv : a.Hq;
-  const int x = wg_x();
-  ht = x % Ht;
-  b = x / Ht;
-  hkv = a.list_by_kv ? ht : ht / a.G;
+// ---- key-sub-block lists ----
+// A list belongs to a sub-block of SB keys (SB never exceeds the pattern's key block, so
+// every key of a sub-block has the same readers) and holds the (query head, query
+// block) pairs whose key lists name its block.  Block patterns build the lists from a bitmap
+// (bits[((b * Ht + ht) * nkb + j) * W + i / 32], bit i % 32: list (b, ht, i) names key block
+// j) so that a list's order is fixed (by head, then query block) whatever order the bits were
+// set in: dK and dV then sum their slabs in the same order on every run.
+
+__global__ __launch_bounds__(256) void bwd_bits_zero_kernel(BwdArgs a) {
+  const int64_t x = (int64_t)wg_x() * 256 + tid_x();
+  const int Ht = a.list_by_kv ? a.Hkv : a.Hq;
+  if (x < (int64_t)a.B * Ht * a.nkb * a.W) a.bits[x] = 0u;
 }
 
-__global__ __launch_bounds__(256) void bwd_zero_kernel(BwdArgs a) {
+// One thread per list entry slot (b, ht, i, c).
+__global__ __launch_bounds__(256) void bwd_bits_set_kernel(BwdArgs a) {
+  const int64_t x = (int64_t)wg_x() * 256 + tid_x();
+  const int Ht = a.list_by_kv ? a.Hkv : a.Hq;
+  const int cap = a.pat.cap;
+  if (cap <= 0 || x >= (int64_t)a.B * Ht * a.nqb * cap) return;
+  const int c = (int)(x % cap);
+  const int64_t bi = x / cap;
+  const int i = (int)(bi % a.nqb);
+  const int64_t bh = bi / a.nqb;
+  const int ht = (int)(bh % Ht), b = (int)(bh / Ht);
+  const int64_t lb = (int64_t)b * a.pat.s_b + (int64_t)ht * a.pat.s_h + (int64_t)i * a.pat.s_q;
+  if (c >= min(a.pat.count[lb], cap)) return;
+  const int j = a.pat.index[lb * cap + c];
+  if (j < 0 || j >= a.nkb) return;
+  atomicOr(&a.bits[(((int64_t)b * Ht + ht) * a.nkb + j) * a.W + (i >> 5)], 1u << (i & 31));
+}
+
+// Visits the pairs of list (b, hkv, sub) in list order: f(query head, query block).
+template <class F>
+__device__ __forceinline__ void bwd_walk(const BwdArgs& a, int b, int hkv, int sub, F&& f) {
+  const int Ht = a.list_by_kv ? a.Hkv : a.Hq;
+  const int j = sub * a.SB / a.pat.block_N;
+  const int heads = a.list_by_kv ? 1 : a.G;
+  for (int g = 0; g < heads; ++g) {
+    const int ht = a.list_by_kv ? hkv : hkv * a.G + g;
+    const uint32_t* col = a.bits + (((int64_t)b * Ht + ht) * a.nkb + j) * a.W;
+    for (int wd = 0; wd < a.W; ++wd) {
+      uint32_t m = col[wd];
+      while (m) {
+        const int i = wd * 32 + __builtin_ctz(m);
+        m &= m - 1;
+        if (a.list_by_kv) {
+          for (int gg = 0; gg < a.G; ++gg) f(hkv * a.G + gg, i);
+        } else {
+          f(ht, i);
+        }
+      }
+    }
+  }
+}
+
+// One thread per list: its pair count.
+__global__ __launch_bounds__(256) void bwd_list_count_kernel(BwdArgs a) {
   const int x = wg_x() * 256 + tid_x();
-  if (x < a.B * a.Hkv * a.nks) a.counts[x] = 0;
+  if (x >= a.B * a.Hkv * a.nks) return;
+  const int sub = x % a.nks, bh = x / a.nks;
+  const int Ht = a.list_by_kv ? a.Hkv : a.Hq;
+  const int hkv = bh % a.Hkv, b = bh / a.Hkv;
+  const int j = sub * a.SB / a.pat.block_N;
+  const int heads = a.list_by_kv ? 1 : a.G;
+  int n = 0;
+  for (int g = 0; g < heads; ++g) {
+    const int ht = a.list_by_kv ? hkv : hkv * a.G + g;
+    const uint32_t* col = a.bits + (((int64_t)b * Ht + ht) * a.nkb + j) * a.W;
+    for (int wd = 0; wd < a.W; ++wd) n += __builtin_popcount(col[wd]);
+  }
+  a.counts[x] = a.list_by_kv ? n * a.G : n;
+}
+
+// One thread per list: its pairs, h * nqb + i, from offsets[list] on.
+__global__ __launch_bounds__(256) void bwd_list_fill_kernel(BwdArgs a) {
+  const int x = wg_x() * 256 + tid_x();
+  if (x >= a.B * a.Hkv * a.nks) return;
+  const int sub = x % a.nks, bh = x / a.nks;
+  int32_t* out = a.entries + a.offsets[x];
+  int k = 0;
+  bwd_walk(a, bh / a.Hkv, bh % a.Hkv, sub, [&](int h, int i) { out[k++] = h * a.nqb + i; });
 }
 
 // First 32-row query slab that sees key0 (causal: some row r with r + Sk - Sq >= key0).
@@ -95,36 +164,9 @@ __global__ __launch_bounds__(256) void bwd_dense_count_kernel(BwdArgs a) {
   const int x = wg_x() * 256 + tid_x();
   if (x >= a.B * a.Hkv * a.nks) return;
   const int total_slabs = (a.Sq + 31) / 32;
-  a.counts[x] = a.G * max(0, total_slabs - bwd_first_slab(a, (x % a.nks) * 64));
+  a.counts[x] = a.G * max(0, total_slabs - bwd_first_slab(a, (x % a.nks) * a.SB));
 }
 
-__global__ __launch_bounds__(256) void bwd_count_kernel(BwdArgs a) {
-  __shared__ int hist[kBwdMaxSub];
-  int b, ht, Ht, hkv;
-  bwd_list_head(a, b, ht, Ht, hkv);
-  const int t = tid_x();
-  for (int x = t; x < a.nks; x += 256) hist[x] = 0;
-  __syncthreads();
-  const int spe = a.pat.block_N / 64, mult = a.list_by_kv ? a.G : 1;
-  const int n = a.nqb * a.pat.cap;
-  for (int e = t; e < n; e += 256) {
-    const int i = e / a.pat.cap, c = e - i * a.pat.cap;
-    const int64_t lb = (int64_t)b * a.pat.s_b + (int64_t)ht * a.pat.s_h + (int64_t)i * a.pat.s_q;
-    if (c >= a.pat.count[lb]) continue;
-    const int jb = a.pat.index[lb * a.pat.cap + c];
-    for (int u = 0; u < spe; ++u) {
-      const int sub = jb * spe + u;
-      if (sub >= 0 && sub < a.nks) atomicAdd(&hist[sub], mult);
-    }
-  }
-  __syncthreads();
-  int* counts = a.counts + ((int64_t)b * a.Hkv + hkv) * a.nks;
-  for (int x = t; x < a.nks; x += 256)
-    if (hist[x]) atomicAdd(&counts[x], hist[x]);
-}
-
-// Exclusive prefix sums of the counts (pair offsets, block patterns) and of the chunks per
-// list, ceil(units / kBwdChunk) with units = counts * slabs (block) or counts (dense).
 __global__ __launch_bounds__(1024) void bwd_scan_kernel(BwdArgs a) {
   __shared__ int s_cnt[1024], s_chk[1024];
   const int n = a.B * a.Hkv * a.nks;
@@ -158,10 +200,7 @@ __global__ __launch_bounds__(1024) void bwd_scan_kernel(BwdArgs a) {
     for (int u = 0; u < 4; ++u) {
       const int idx = base + t * 4 + u;
       if (idx < n) {
-        if (block) {
-          a.offsets[idx] = ec;
-          a.cursor[idx] = ec;
-        }
+        if (block) a.offsets[idx] = ec;
         a.chunkp[idx] = ek;
       }
       ec += c[u];
@@ -177,48 +216,11 @@ __global__ __launch_bounds__(1024) void bwd_scan_kernel(BwdArgs a) {
   }
 }
 
-__global__ __launch_bounds__(256) void bwd_fill_kernel(BwdArgs a) {
-  __shared__ int hist[kBwdMaxSub];
-  int b, ht, Ht, hkv;
-  bwd_list_head(a, b, ht, Ht, hkv);
-  const int t = tid_x();
-  for (int x = t; x < a.nks; x += 256) hist[x] = 0;
-  __syncthreads();
-  const int spe = a.pat.block_N / 64, mult = a.list_by_kv ? a.G : 1;
-  const int n = a.nqb * a.pat.cap;
-  for (int e = t; e < n; e += 256) {
-    const int i = e / a.pat.cap, c = e - i * a.pat.cap;
-    const int64_t lb = (int64_t)b * a.pat.s_b + (int64_t)ht * a.pat.s_h + (int64_t)i * a.pat.s_q;
-    if (c >= a.pat.count[lb]) continue;
-    const int jb = a.pat.index[lb * a.pat.cap + c];
-    for (int u = 0; u < spe; ++u) {
-      const int sub = jb * spe + u;
-      if (sub >= 0 && sub < a.nks) atomicAdd(&hist[sub], mult);
-    }
-  }
-  __syncthreads();
-  int* cursor = a.cursor + ((int64_t)b * a.Hkv + hkv) * a.nks;
-  for (int x = t; x < a.nks; x += 256)
-    if (hist[x]) hist[x] = atomicAdd(&cursor[x], hist[x]);
-  __syncthreads();
-  for (int e = t; e < n; e += 256) {
-    const int i = e / a.pat.cap, c = e - i * a.pat.cap;
-    const int64_t lb = (int64_t)b * a.pat.s_b + (int64_t)ht * a.pat.s_h + (int64_t)i * a.pat.s_q;
-    if (c >= a.pat.count[lb]) continue;
-    const int jb = a.pat.index[lb * a.pat.cap + c];
-    for (int u = 0; u < spe; ++u) {
-      const int sub = jb * spe + u;
-      if (sub < 0 || sub >= a.nks) continue;
-      for (int g = 0; g < mult; ++g) {
-        const int h = a.list_by_kv ? hkv * a.G + g : ht;
-        a.entries[atomicAdd(&hist[sub], 1)] = h * a.nqb + i;
-      }
-    }
-  }
-}
-
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1))) void bwd_dkdv_kernel(BwdArgs a) {
+template <int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int D = TD;
+  constexpr int SB = NW * 32;   // keys of the sub-block (32 per wave)
+  constexpr int RPW = 32 / NW;  // slab rows each wave loads
   constexpr int RS = D;  // 256-byte rows; 16-byte pieces swizzled by row (k_swz), as written by the DMA
   __shared__ __attribute__((aligned(16))) uint16_t Qs[2][32 * RS];
   __shared__ __attribute__((aligned(16))) uint16_t Ds[2][32 * RS];
@@ -238,7 +240,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1))) void b
   const int sub = list % a.nks;
   const int bh = list / a.nks;
   const int hkv = bh % a.Hkv, b = bh / a.Hkv;
-  const int key0 = sub * 64;
+  const int key0 = sub * SB;
   const int chunk = wid - a.chunkp[list];
   const bool split = a.chunkp[list + 1] - a.chunkp[list] > 1;
   const int delta = a.Sk - a.Sq;
@@ -300,13 +302,13 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1))) void b
     }
     return u1;
   };
-  // Q and dO rows q0 + 16w + 4x + l/16 of the slab (clamped to the last row: finite data the
+  // Q and dO rows q0 + RPW w + 4x + l/16 of the slab (clamped to the last row: finite data the
   // mask then ignores), lane l into slot l%16; LSE and D of the 32 rows by 8 lanes each
   const int lrow = l >> 4, lslot = l & 15;
   auto issue = [&](int h, int q0, int bi) __attribute__((always_inline)) {
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const int rl = w * 16 + x * 4 + lrow;
+    for (int x = 0; x < RPW / 4; ++x) {
+      const int rl = w * RPW + x * 4 + lrow;
       const int gr = min(q0 + rl, a.Sq - 1);
       const uint32_t piece = (uint32_t)((lslot ^ k_swz(rl)) << 4);
       const char* qp = reinterpret_cast<const char*>(reinterpret_cast<const uint16_t*>(a.q.ptr) + (int64_t)b * a.q.sb +
@@ -314,10 +316,10 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1))) void b
       const char* dp = reinterpret_cast<const char*>(reinterpret_cast<const uint16_t*>(a.dout.ptr) +
                                                      (int64_t)b * a.dout.sb + (int64_t)gr * a.dout.ss +
                                                      (int64_t)h * a.dout.sh);
-      __builtin_amdgcn_global_load_lds(qp + piece, BSA_LDS(Qs[bi] + (w * 4 + x) * 4 * RS), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(dp + piece, BSA_LDS(Ds[bi] + (w * 4 + x) * 4 * RS), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(qp + piece, BSA_LDS(Qs[bi] + (w * RPW + x * 4) * RS), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(dp + piece, BSA_LDS(Ds[bi] + (w * RPW + x * 4) * RS), 16, 0, 0);
     }
-    if (l < 8) {
+    if (w < 2 && l < 8) {
       const int r4 = max(0, min(q0 + 4 * l, a.Sq - 4));  // a clamped group of 4 rows
       const float* src = (w == 0 ? a.lse : a.dsum) + ((int64_t)b * a.Hq + h) * a.Sq + r4;
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(src), BSA_LDS(w == 0 ? ls[bi] : dsm[bi]), 16, 0,
@@ -390,8 +392,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1))) void b
   float* dvp;
   float ks_ = a.scale;
   if (split) {
-    dkp = a.part + ((int64_t)wid * 2 * 64 + w * 32 + lq) * D;
-    dvp = dkp + 64 * D;
+    dkp = a.part + ((int64_t)wid * 2 * SB + w * 32 + lq) * D;
+    dvp = dkp + SB * D;
     ks_ = 1.f;
   } else {
     dkp = a.dk + (((int64_t)b * a.Sk + key) * a.Hkv + hkv) * D;
@@ -421,15 +423,16 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a) {
   const int sub = list % a.nks;
   const int bh = list / a.nks;
   const int hkv = bh % a.Hkv, b = bh / a.Hkv;
-  for (int x = tid_x(); x < 2 * 64 * (D / 4); x += 256) {
-    const int which = x / (64 * D / 4);  // 0 dK, 1 dV
-    const int rem = x - which * (64 * D / 4);
+  const int SB = a.SB;
+  for (int x = tid_x(); x < 2 * SB * (D / 4); x += 256) {
+    const int which = x / (SB * D / 4);  // 0 dK, 1 dV
+    const int rem = x - which * (SB * D / 4);
     const int kr = rem / (D / 4), d4 = rem - kr * (D / 4);
-    const int key = sub * 64 + kr;
+    const int key = sub * SB + kr;
     if (key >= a.Sk) continue;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int c = 0; c < n; ++c)
-      acc += *reinterpret_cast<const f32x4*>(a.part + (((int64_t)(c0 + c) * 2 + which) * 64 + kr) * D + d4 * 4);
+      acc += *reinterpret_cast<const f32x4*>(a.part + (((int64_t)(c0 + c) * 2 + which) * SB + kr) * D + d4 * 4);
     if (which == 0) acc *= a.scale;
     float* dst = (which == 0 ? a.dk : a.dv) + (((int64_t)b * a.Sk + key) * a.Hkv + hkv) * D + d4 * 4;
     *reinterpret_cast<f32x4*>(dst) = acc;

@@ -14,63 +14,13 @@
 
 #include "args.cuh"
 #include "bsa.h"
+#include "decode_plan.h"
+#include "host_args.h"
 #include "launch.h"
 
 using namespace bsa;
 
-constexpr float kLog2e = 1.4426950408889634f;
-
 namespace {
-
-
-bool valid_dtype(int32_t d) { return d == BSA_BF16 || d == BSA_F32; }
-
-float scale_of(const bsa_problem& p) {
-  return p.softmax_scale > 0.f ? p.softmax_scale : 1.0f / std::sqrt((float)p.D);
-}
-
-// softcap_score constants: cap_in = 2 scale log2(e) / c, cap_out = c / scale; (0, 0) when off.
-void cap_consts(const bsa_problem& p, float& cap_in, float& cap_out) {
-  cap_in = cap_out = 0.f;
-  if (p.softcap > 0.f) {
-    const float t = scale_of(p);
-    cap_in = 2.f * t * kLog2e / p.softcap;
-    cap_out = p.softcap / t;
-  }
-}
-
-TensorArg targ(const bsa_tensor& t) { return TensorArg{t.ptr, t.stride_b, t.stride_s, t.stride_h}; }
-OutArg oarg(const bsa_tensor& t) { return OutArg{t.ptr, t.stride_b, t.stride_s, t.stride_h, t.dtype == BSA_F32}; }
-
-PatternArg parg(const bsa_pattern* p) {
-  PatternArg a{};
-  if (!p) return a;
-  a.kind = p->kind;
-  a.block_M = p->block_M;
-  a.block_N = p->block_N;
-  a.cap = p->cap;
-  a.col_cap = p->col_cap;
-  a.count = p->count;
-  a.index = p->index;
-  a.col_count = p->col_count;
-  a.col_index = p->col_index;
-  a.s_b = p->s_b;
-  a.s_h = p->s_h;
-  a.s_q = p->s_q;
-  return a;
-}
-
-bsa_status launch_status() {
-  return hipGetLastError() == hipSuccess ? BSA_OK : BSA_ERR_HIP;
-}
-
-// 16-byte alignment of every row start: base pointer and all strides must keep
-// head-dim rows 16-byte aligned for the vector loads.
-bool aligned_rows(const bsa_tensor& t, int elem_bytes) {
-  const uintptr_t p = reinterpret_cast<uintptr_t>(t.ptr);
-  auto ok = [&](int64_t s) { return ((s * elem_bytes) & 15) == 0; };
-  return (p & 15) == 0 && ok(t.stride_b) && ok(t.stride_s) && ok(t.stride_h);
-}
 
 bsa_status check_problem(const bsa_problem* prob, const bsa_tensor& q, const bsa_tensor& k, const bsa_tensor& v,
                          const bsa_tensor& o) {
@@ -133,157 +83,6 @@ bsa_status debug_validate(const bsa_problem& p, const bsa_pattern* pat, bsa_stre
   if (!pat || pat->kind == BSA_PAT_DENSE || !debug_checks_on()) return BSA_OK;
   const int r = debug_check(check_args(p, pat, nullptr), reinterpret_cast<hipStream_t>(stream));
   return r == 0 ? BSA_OK : (r < 0 ? BSA_ERR_HIP : BSA_ERR_INVALID_ARG);
-}
-
-// ---------------------------------------------------------------------------
-// Decode path selection and split heuristic
-// ---------------------------------------------------------------------------
-
-struct SegPlan {
-  int n_entries = 0, cpe = 1, eps = 1, splits = 0;
-};
-
-struct DecodePlan {
-  bool use = false;
-  int Gp = 1, R = 0;
-};
-
-// Packing rule: the G query heads of a kv head share one workgroup when they share
-// its key set; with the query positions they must fit one 16-column MFMA tile.
-DecodePlan plan_decode(const bsa_problem& p, const bsa_pattern* pat) {
-  DecodePlan d;
-  const int kind = pat ? pat->kind : BSA_PAT_DENSE;
-  if (p.cu_seqlens_q || kind == BSA_PAT_VS) return d;
-  const int G = p.Hq / p.Hkv;
-  const bool shared = kind == BSA_PAT_DENSE || pat->Ht == p.Hkv;
-  d.Gp = shared ? G : 1;
-  d.R = d.Gp * p.Sq;
-  if (d.R > 16) return d;
-  if (kind == BSA_PAT_BLOCK && p.Sq > pat->block_M) return d;
-  d.use = true;
-  return d;
-}
-
-SegPlan seg_entries(int Sk, const bsa_pattern* pat) {
-  SegPlan s;
-  if (!pat || pat->kind == BSA_PAT_DENSE) {
-    s.n_entries = (Sk + 63) / 64;
-    s.cpe = 1;
-  } else {
-    s.n_entries = pat->cap;
-    s.cpe = pat->block_N / 64;
-  }
-  return s;
-}
-
-// Compute units of the current device (cached per device).
-int device_cus() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!cached[dev]) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
-
-#ifndef BSA_DECODE_ROUNDS
-#define BSA_DECODE_ROUNDS 4
-#endif
-constexpr int kDecodeWgPerCu = 4;                  // resident decode workgroups per CU (124 VGPRs, 36 KB LDS)
-constexpr int kDecodeRounds = BSA_DECODE_ROUNDS;   // whole rounds of resident workgroups per launch
-constexpr int kMaxChunksPerSplit = 96;             // more rounds when splits would get longer than this
-
-// Split the segments of one decode launch: the splits of a group are a whole number of
-// rounds of resident workgroups (no quarter-full last round), shared between segments in
-// proportion to their chunk counts, so every workgroup streams a similar number of chunks.
-void split_segments(SegPlan* segs, int nseg, int groups) {
-  long total = 0;
-  for (int i = 0; i < nseg; ++i) total += (long)std::max(0, segs[i].n_entries) * segs[i].cpe;
-  const long capacity = (long)device_cus() * kDecodeWgPerCu;
-  long rounds = kDecodeRounds;
-  while (total * groups > rounds * capacity * kMaxChunksPerSplit) ++rounds;
-  long per_group = std::max<long>(1, (rounds * capacity + groups / 2) / groups);
-  per_group = std::max<long>(per_group, nseg);
-  long assigned = 0;
-  for (int i = 0; i < nseg; ++i) {
-    SegPlan& s = segs[i];
-    if (s.n_entries <= 0) {
-      s.eps = 1;
-      s.splits = 1;
-      ++assigned;
-      continue;
-    }
-    const long chunks = (long)s.n_entries * s.cpe;
-    long want = i == nseg - 1 ? per_group - assigned : (per_group * chunks + total / 2) / std::max<long>(total, 1);
-    want = std::max<long>(1, std::min<long>(want, s.n_entries));
-    s.eps = (int)((s.n_entries + want - 1) / want);
-    s.splits = (s.n_entries + s.eps - 1) / s.eps;
-    assigned += s.splits;
-  }
-}
-
-size_t partial_bytes(const bsa_problem& p, int slots) {
-  const size_t rows = (size_t)p.B * p.Sq * p.Hq;
-  return (size_t)slots * rows * (p.D + 1) * sizeof(float) + 256;
-}
-
-DecodeSeg make_seg(const bsa_tensor& k, const bsa_tensor& v, const bsa_pattern* pat, int Sk, int causal,
-                   const SegPlan& sp, int slot0) {
-  DecodeSeg s{};
-  s.k = targ(k);
-  s.v = targ(v);
-  s.pat = parg(pat);
-  s.Sk = Sk;
-  s.causal = causal != 0;
-  s.n_entries = sp.n_entries;
-  s.cpe = sp.cpe;
-  s.eps = sp.eps;
-  s.splits = sp.splits;
-  s.slot0 = slot0;
-  return s;
-}
-
-// One decode launch over one or two segments; writes (O, LSE) directly when o is given
-// (single segment, single split), partial slots otherwise.
-bsa_status run_decode(const bsa_problem& p, const DecodePlan& d, const bsa_tensor& q, const DecodeSeg* segs, int nseg,
-                      float* part_o, float* part_lse, const bsa_tensor* o, float* lse, hipStream_t st) {
-  DecodeArgs a{};
-  a.q = targ(q);
-  a.nseg = nseg;
-  a.seg[0] = segs[0];
-  if (nseg > 1) a.seg[1] = segs[1];
-  a.B = p.B;
-  a.Hq = p.Hq;
-  a.Hkv = p.Hkv;
-  a.Sq = p.Sq;
-  a.G = p.Hq / p.Hkv;
-  a.Gp = d.Gp;
-  a.R = d.R;
-  a.scale_log2 = scale_of(p) * kLog2e;
-  cap_consts(p, a.cap_in, a.cap_out);
-  if (o) {
-    a.direct = 1;
-    a.o = oarg(*o);
-    a.lse = lse;
-  } else {
-    a.direct = 0;
-    a.part_o = part_o;
-    a.part_lse = part_lse;
-  }
-  int gx = 0;
-  for (int i = 0; i < nseg; ++i) gx += segs[i].splits;
-  launch_decode(a, p.D, gx, p.Hq / d.Gp, p.B, st);
-  return launch_status();
-}
-
-// Split plan of bsa_fwd on the decode path (one segment).
-SegPlan fwd_decode_plan(const bsa_problem& p, const bsa_pattern* pat, const DecodePlan& d) {
-  SegPlan sp = seg_entries(p.Sk, pat);
-  split_segments(&sp, 1, p.B * (p.Hq / d.Gp));
-  return sp;
 }
 
 // ---------------------------------------------------------------------------
@@ -438,22 +237,6 @@ bsa_status bsa_fwd_partials(const bsa_problem* prob, bsa_tensor q, bsa_tensor k,
   return run_prefill(p, q, k, v, pat, nullptr, nullptr, sp.eps, sp.splits, o_part, lse_part, hs);
 }
 
-// Partial slots of the fused speculative + repair launch (decode shapes), or 2.
-static void speculative_plan(const bsa_problem& p, int Sk_spec, const bsa_pattern* missed, SegPlan segs[2],
-                             DecodePlan* dp) {
-  *dp = plan_decode(p, missed);
-  segs[0] = seg_entries(Sk_spec, nullptr);
-  segs[1] = seg_entries(p.Sk, missed);
-  if (dp->use) {
-    split_segments(segs, 2, p.B * (p.Hq / dp->Gp));
-  } else {
-    for (int i = 0; i < 2; ++i) {
-      segs[i].eps = std::max(1, segs[i].n_entries);
-      segs[i].splits = 1;
-    }
-  }
-}
-
 int32_t bsa_speculative_num_partials(const bsa_problem* prob, int32_t Sk_spec, const bsa_pattern* missed) {
   if (!prob || prob->B <= 0 || prob->Hkv <= 0 || prob->Hq <= 0 || prob->Hq % prob->Hkv || Sk_spec <= 0) return -1;
   if (!missed || missed->kind != BSA_PAT_BLOCK || check_pattern(*prob, missed) != BSA_OK) return -1;
@@ -585,8 +368,8 @@ namespace {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct BwdLayout {
-  int BM = 0, nqb = 0, nks = 0, n_lists = 0, chunk_bound = 0;
-  size_t dsum = 0, counts = 0, offsets = 0, cursor = 0, entries = 0, chunkp = 0, part = 0, total = 0;
+  int BM = 0, SB = 0, nqb = 0, nks = 0, nkb = 0, W = 0, n_lists = 0, chunk_bound = 0;
+  size_t dsum = 0, counts = 0, offsets = 0, entries = 0, chunkp = 0, bits = 0, part = 0, total = 0;
 };
 
 // Shapes the backward kernels take; total == 0 otherwise.
@@ -597,9 +380,9 @@ BwdLayout bwd_layout(const bsa_problem& p, const bsa_pattern* pat) {
   const bool block = pat && pat->kind == BSA_PAT_BLOCK;
   if (pat && pat->kind != BSA_PAT_DENSE && !block) return L;
   L.BM = block ? pat->block_M : 128;
+  L.SB = 64;  // a sub-block never spans two pattern key blocks (block_N is 64 or 128)
   L.nqb = (p.Sq + L.BM - 1) / L.BM;
-  L.nks = (p.Sk + 63) / 64;
-  if (L.nks > kBwdMaxSub) return L;
+  L.nks = (p.Sk + L.SB - 1) / L.SB;
   L.n_lists = p.B * p.Hkv * L.nks;
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t at = off; off = align256(off + bytes); return at; };
@@ -610,11 +393,15 @@ BwdLayout bwd_layout(const bsa_problem& p, const bsa_pattern* pat) {
   if (block) {
     const int Ht = pat->Ht;
     const int mult = Ht == p.Hkv ? p.Hq / p.Hkv : 1;
-    const size_t pairs = (size_t)p.B * Ht * L.nqb * pat->cap * (pat->block_N / 64) * mult;
+    // each (list head, query block) names a key block at most once in the bitmap
+    const size_t per = (size_t)std::min(pat->cap, (p.Sk + pat->block_N - 1) / pat->block_N);
+    const size_t pairs = (size_t)p.B * Ht * L.nqb * per * (pat->block_N / L.SB) * mult;
     if (pairs >= (size_t)INT_MAX) return BwdLayout{};
+    L.nkb = (p.Sk + pat->block_N - 1) / pat->block_N;
+    L.W = (L.nqb + 31) / 32;
     L.offsets = take(sizeof(int32_t) * (L.n_lists + 1));
-    L.cursor = take(sizeof(int32_t) * L.n_lists);
-    L.entries = take(sizeof(int32_t) * pairs);
+    L.entries = take(sizeof(int32_t) * std::max<size_t>(pairs, 1));
+    L.bits = take(sizeof(uint32_t) * (size_t)p.B * Ht * L.nkb * L.W);
     units = pairs * (L.BM / 32);
   } else {
     units = (size_t)L.n_lists * (p.Hq / p.Hkv) * ((p.Sq + 31) / 32);
@@ -622,7 +409,7 @@ BwdLayout bwd_layout(const bsa_problem& p, const bsa_pattern* pat) {
   const size_t chunks = units / kBwdChunk + L.n_lists;  // ceil per list: at most one extra each
   if (chunks >= (size_t)INT_MAX / 2) return BwdLayout{};
   L.chunk_bound = (int)chunks;
-  L.part = take(sizeof(float) * chunks * 2 * 64 * 128);
+  L.part = take(sizeof(float) * chunks * 2 * L.SB * 128);
   L.total = off;
   return L;
 }
@@ -679,15 +466,18 @@ bsa_status bsa_bwd(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, bsa_tens
   a.scale = scale_of(p);
   a.scale_log2 = a.scale * kLog2e;
   a.BM = L.BM;
+  a.SB = L.SB;
   a.nqb = L.nqb;
   a.nks = L.nks;
+  a.nkb = L.nkb;
+  a.W = L.W;
   a.counts = reinterpret_cast<int32_t*>(base + L.counts);
   a.chunkp = reinterpret_cast<int32_t*>(base + L.chunkp);
   a.part = reinterpret_cast<float*>(base + L.part);
   if (pat && pat->kind == BSA_PAT_BLOCK) {
     a.offsets = reinterpret_cast<int32_t*>(base + L.offsets);
-    a.cursor = reinterpret_cast<int32_t*>(base + L.cursor);
     a.entries = reinterpret_cast<int32_t*>(base + L.entries);
+    a.bits = reinterpret_cast<uint32_t*>(base + L.bits);
   }
   launch_bwd(a, L.chunk_bound, reinterpret_cast<hipStream_t>(stream));
   return launch_status();

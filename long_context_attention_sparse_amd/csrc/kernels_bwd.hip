@@ -11,15 +11,19 @@ void launch_bwd(const BwdArgs& a, int chunk_bound, hipStream_t st) {
   hipLaunchKernelGGL(bwd_dot_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, st, a);
   if (a.pat.kind != 0) {
     const int Ht = a.list_by_kv ? a.Hkv : a.Hq;
-    hipLaunchKernelGGL(bwd_zero_kernel, dim3((n_lists + 255) / 256), dim3(256), 0, st, a);
-    hipLaunchKernelGGL(bwd_count_kernel, dim3(a.B * Ht), dim3(256), 0, st, a);
+    const int64_t words = (int64_t)a.B * Ht * a.nkb * a.W;
+    const int64_t slots = (int64_t)a.B * Ht * a.nqb * a.pat.cap;
+    hipLaunchKernelGGL(bwd_bits_zero_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, st, a);
+    if (slots > 0)
+      hipLaunchKernelGGL(bwd_bits_set_kernel, dim3((unsigned)((slots + 255) / 256)), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(bwd_list_count_kernel, dim3((n_lists + 255) / 256), dim3(256), 0, st, a);
     hipLaunchKernelGGL(bwd_scan_kernel, dim3(1), dim3(1024), 0, st, a);
-    hipLaunchKernelGGL(bwd_fill_kernel, dim3(a.B * Ht), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(bwd_list_fill_kernel, dim3((n_lists + 255) / 256), dim3(256), 0, st, a);
   } else {
     hipLaunchKernelGGL(bwd_dense_count_kernel, dim3((n_lists + 255) / 256), dim3(256), 0, st, a);
     hipLaunchKernelGGL(bwd_scan_kernel, dim3(1), dim3(1024), 0, st, a);
   }
-  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(chunk_bound), dim3(128), 0, st, a);
+  hipLaunchKernelGGL(bwd_dkdv_kernel<2>, dim3(chunk_bound), dim3(128), 0, st, a);
   hipLaunchKernelGGL(bwd_reduce_kernel, dim3(n_lists), dim3(256), 0, st, a);
   const unsigned dq_grid = (unsigned)((int64_t)a.B * a.Hq * a.nqb);
   if (a.BM == 128) hipLaunchKernelGGL(bwd_dq_kernel<4>, dim3(dq_grid), dim3(256), 0, st, a);

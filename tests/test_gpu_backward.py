@@ -106,3 +106,38 @@ def test_empty_lists_give_zero_rows():
     _check("dq", dq, rq)
     _check("dk", dk, rk)
     _check("dv", dv, rv)
+
+
+@pytest.mark.parametrize("Ht", ["q", "kv"])
+def test_long_lists_split_and_repeat_bit_for_bit(Ht):
+    """Key block 0 is named by every query block, so its dK/dV list (G heads x 32 query blocks x
+    4 slabs) is cut into several chunks and reduced; two runs give the same bits (the lists are
+    built in a fixed order)."""
+    B, S, Hq, Hkv, bM = 1, 4096, 8, 2, 128
+    say("backward long lists", Ht)
+    q, k, v, do = _data(94, B, S, S, Hq, Hkv)
+    H = Hq if Ht == "q" else Hkv
+    nqb = S // bM
+    g = rng(94, "long-lists")
+    cap = 6
+    count = np.zeros((B, H, nqb), np.int32)
+    index = np.zeros((B, H, nqb, cap), np.int32)
+    for h in range(H):
+        for i in range(nqb):
+            extra = g.choice(np.arange(1, i), min(cap - 2, max(i - 1, 0)), replace=False) if i > 1 else []
+            sel = np.unique(np.concatenate([[0, i], extra]).astype(np.int32))
+            count[0, h, i] = sel.size
+            index[0, h, i, :sel.size] = g.permutation(sel)
+    pat = bsa.BlockPattern(dev_i32(count), dev_i32(index), bM, 128)
+    (dq, dk, dv), (rq, rk, rv) = _grads(q, k, v, do, pat, True, count, index)
+    _check("dq", dq, rq)
+    _check("dk", dk, rk)
+    _check("dv", dv, rv)
+    dq_, dk_, dv_ = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    o, lse = bsa.bsa_fwd(dq_, dk_, dv_, pat, causal=True, out_dtype=torch.float32)
+    dO = dev_bf16(do)
+    first = bsa.bsa_bwd(dq_, dk_, dv_, o, lse, dO, pat, causal=True)
+    for _ in range(2):
+        again = bsa.bsa_bwd(dq_, dk_, dv_, o, lse, dO, pat, causal=True)
+        for a_, b_ in zip(first, again):
+            assert torch.equal(a_, b_), "backward runs differ"
