@@ -11,12 +11,12 @@
 //   bwd_bits_* / bwd_list_count / bwd_scan / bwd_list_fill (block patterns): for every
 //               sub-block of SB = 64 keys, the list of (query head, query block) pairs whose
 //               key lists name it, in a fixed order
-//   bwd_dkdv    one workgroup (two waves, 32 keys each) per chunk of up to kBwdChunk
-//               32-row query slabs of a sub-block's list (a list every query block names,
-//               like the first block of a causal pattern, is spread over many workgroups;
-//               their float32 partials are summed in chunk order by bwd_reduce, so the
-//               result does not depend on scheduling): K and V stay in registers, 32-row
-//               slabs of Q and dO stream into LDS (double-buffered direct loads) and are
+//   bwd_dkdv    one workgroup (four waves, two per 32-key group) per chunk of up to
+//               kBwdChunk 32-row query slabs of a sub-block's list (a list every query block
+//               names, like the first block of a causal pattern, is spread over many
+//               workgroups; their float32 partials are summed in chunk order by bwd_reduce,
+//               so the result does not depend on scheduling): K or V stays in registers,
+//               32-row slabs of Q and dO stream into LDS (double-buffered direct loads) and are
 //               shared by the waves; S = Q K^T and dP = dO V^T come out with a key per lane,
 //               which makes P and dS directly the B operands of dV^T += dO^T P and
 //               dK^T += Q^T dS (dO^T, Q^T read with the transposing LDS read)
@@ -216,16 +216,22 @@ __global__ __launch_bounds__(1024) void bwd_scan_kernel(BwdArgs a) {
   }
 }
 
-template <int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) void bwd_dkdv_kernel(BwdArgs a) {
+// dK/dV: one workgroup of four waves per chunk of up to kBwdChunk 32-row query slabs of a
+// 64-key sub-block's list.  The work of each 32-key group is split over a pair of waves, so
+// that a wave holds one operand tile and one accumulator set (168 registers: three waves per
+// SIMD): wave 2g (the "P wave") keeps K of its group's keys, builds S^T = K Q^T and
+// P = exp(S - LSE), hands P to its partner through LDS and accumulates dV^T += dO^T P; wave
+// 2g + 1 (the "dS wave") keeps V, builds dP^T = V dO^T, takes P, forms dS = P * (dP - D) and
+// accumulates dK^T += Q^T dS.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int D = TD;
-  constexpr int SB = NW * 32;   // keys of the sub-block (32 per wave)
-  constexpr int RPW = 32 / NW;  // slab rows each wave loads
+  constexpr int SB = 64;
   constexpr int RS = D;  // 256-byte rows; 16-byte pieces swizzled by row (k_swz), as written by the DMA
   __shared__ __attribute__((aligned(16))) uint16_t Qs[2][32 * RS];
   __shared__ __attribute__((aligned(16))) uint16_t Ds[2][32 * RS];
   __shared__ __attribute__((aligned(16))) float ls[2][32];
   __shared__ __attribute__((aligned(16))) float dsm[2][32];
+  __shared__ __attribute__((aligned(16))) uint32_t Ps[2][64 * 8];  // P of each key group, lane layout
 
   const int n_lists = a.B * a.Hkv * a.nks;
   const int wid = wg_x();
@@ -246,20 +252,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
   const int delta = a.Sk - a.Sq;
   const int t = tid_x();
   const int w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63;
+  const int kg = w >> 1;         // key group
+  const bool ds_wave = w & 1;    // role (wave-uniform)
   const int lq = l & 31, hh = l >> 5;
-  const int key = key0 + w * 32 + lq;  // this lane's key (S, dP, dK, dV columns)
+  const int key = key0 + kg * 32 + lq;  // this lane's key
 
-  const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.k.ptr) + (int64_t)b * a.k.sb + (int64_t)hkv * a.k.sh;
-  const uint16_t* vbase = reinterpret_cast<const uint16_t*>(a.v.ptr) + (int64_t)b * a.v.sb + (int64_t)hkv * a.v.sh;
-  bf16x8 kreg[D / 16], vreg[D / 16];
+  // K (P wave) or V (dS wave) rows of the group's keys: the B operand of S^T / dP^T
+  const TensorArg& kv = ds_wave ? a.v : a.k;
+  const uint16_t* kvbase = reinterpret_cast<const uint16_t*>(kv.ptr) + (int64_t)b * kv.sb + (int64_t)hkv * kv.sh;
+  bf16x8 kvreg[D / 16];
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    const bool ok = key < a.Sk;
-    kreg[ks] = as_bf16x8(ok ? ldg128(kbase + (int64_t)key * a.k.ss + ks * 16 + hh * 8) : u32x4{0, 0, 0, 0});
-    vreg[ks] = as_bf16x8(ok ? ldg128(vbase + (int64_t)key * a.v.ss + ks * 16 + hh * 8) : u32x4{0, 0, 0, 0});
-  }
-  // operand offsets in a slab tile: A rows (lane's row lq, piece 2ks + hh) and the transposed
-  // reads (rows rr and rr + 8 of a 16-row step, 4 columns of d-block db)
+  for (int ks = 0; ks < D / 16; ++ks)
+    kvreg[ks] = as_bf16x8(key < a.Sk ? ldg128(kvbase + (int64_t)key * kv.ss + ks * 16 + hh * 8) : u32x4{0, 0, 0, 0});
   int aoff[D / 16];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) aoff[ks] = lq * RS + (((ks * 2 + hh) ^ k_swz(lq)) << 3);
@@ -274,12 +278,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
       trhi[db] = (rr + 8) * RS + (((col >> 3) ^ k_swz(rr + 8)) << 3) + (col & 7);
     }
   }
-  f32x16 dk[D / 32], dv[D / 32];
+  f32x16 acc[D / 32];  // dV^T (P wave) or dK^T (dS wave)
 #pragma unroll
-  for (int x = 0; x < D / 32; ++x) dk[x] = dv[x] = f32x16{};
+  for (int x = 0; x < D / 32; ++x) acc[x] = f32x16{};
 
-  // units: (query head h, first row q0 of a 32-row slab); this workgroup takes chunk
-  // `chunk` of the list's units and skips slabs no row of which sees the keys
   const int slabs = a.BM / 32;
   const int total_slabs = (a.Sq + 31) / 32;
   const bool dense = a.pat.kind == 0;
@@ -302,13 +304,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
     }
     return u1;
   };
-  // Q and dO rows q0 + RPW w + 4x + l/16 of the slab (clamped to the last row: finite data the
-  // mask then ignores), lane l into slot l%16; LSE and D of the 32 rows by 8 lanes each
+  // Q and dO rows q0 + 8w + 4x + l/16 of the slab (clamped to the last row: finite data the
+  // mask then ignores), lane l into slot l%16; LSE (wave 0) and D (wave 1) by 8 lanes each
   const int lrow = l >> 4, lslot = l & 15;
   auto issue = [&](int h, int q0, int bi) __attribute__((always_inline)) {
 #pragma unroll
-    for (int x = 0; x < RPW / 4; ++x) {
-      const int rl = w * RPW + x * 4 + lrow;
+    for (int x = 0; x < 2; ++x) {
+      const int rl = w * 8 + x * 4 + lrow;
       const int gr = min(q0 + rl, a.Sq - 1);
       const uint32_t piece = (uint32_t)((lslot ^ k_swz(rl)) << 4);
       const char* qp = reinterpret_cast<const char*>(reinterpret_cast<const uint16_t*>(a.q.ptr) + (int64_t)b * a.q.sb +
@@ -316,8 +318,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
       const char* dp = reinterpret_cast<const char*>(reinterpret_cast<const uint16_t*>(a.dout.ptr) +
                                                      (int64_t)b * a.dout.sb + (int64_t)gr * a.dout.ss +
                                                      (int64_t)h * a.dout.sh);
-      __builtin_amdgcn_global_load_lds(qp + piece, BSA_LDS(Qs[bi] + (w * RPW + x * 4) * RS), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(dp + piece, BSA_LDS(Ds[bi] + (w * RPW + x * 4) * RS), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(qp + piece, BSA_LDS(Qs[bi] + (w * 8 + x * 4) * RS), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(dp + piece, BSA_LDS(Ds[bi] + (w * 8 + x * 4) * RS), 16, 0, 0);
     }
     if (w < 2 && l < 8) {
       const int r4 = max(0, min(q0 + 4 * l, a.Sq - 4));  // a clamped group of 4 rows
@@ -327,6 +329,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
     }
   };
 
+  uint32_t* pslot = Ps[kg] + l * 8;
   int h, q0;
   int u = next_unit(u0, h, q0);
   int buf = 0;
@@ -334,51 +337,68 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
   while (u < u1) {
     int hn = 0, q0n = 0;
     const int un = next_unit(u + 1, hn, q0n);
-    // this slab's tiles are in LDS from every wave, and every wave is done with the other buffer
+    // this slab's tiles are in LDS from every wave, every wave is done with the other buffer
+    // and the dS waves have read the previous P
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (un < u1) issue(hn, q0n, buf ^ 1);  // the next slab streams in during this one
     const uint16_t* Qb = Qs[buf];
     const uint16_t* Db = Ds[buf];
-    f32x16 s = {}, dp = {};
+    const uint16_t* rows = ds_wave ? Db : Qb;   // A operand of S^T / dP^T
+    const uint16_t* trans = ds_wave ? Qb : Db;  // transposed operand of dK^T / dV^T
+    f32x16 x = {};
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      const u32x4 qa = *reinterpret_cast<const u32x4*>(Qb + aoff[ks]);
-      const u32x4 da = *reinterpret_cast<const u32x4*>(Db + aoff[ks]);
-      s = mfma32x32x16(as_bf16x8(qa), kreg[ks], s);
-      dp = mfma32x32x16(as_bf16x8(da), vreg[ks], dp);
-    }
+    for (int ks = 0; ks < D / 16; ++ks)
+      x = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(rows + aoff[ks])), kvreg[ks], x);
     // lane: key; register r: slab row 8(r/4) + 4hh + r%4
-    uint32_t pp[8], dd[8];
+    uint32_t op[8];
+    if (!ds_wave) {
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const f32x4 lv = *reinterpret_cast<const f32x4*>(ls[buf] + g4 * 8 + hh * 4);
-      const f32x4 dm = *reinterpret_cast<const f32x4*>(dsm[buf] + g4 * 8 + hh * 4);
-      float p[4], d[4];
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 lv = *reinterpret_cast<const f32x4*>(ls[buf] + g4 * 8 + hh * 4);
+        float p[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = q0 + g4 * 8 + hh * 4 + e;
-        const bool vis = key < a.Sk && row < a.Sq && lv[e] != kNegInf && (!a.causal || key <= row + delta);
-        p[e] = vis ? exp2_fast(fmaf(s[g4 * 4 + e], a.scale_log2, -lv[e] * kLog2e)) : 0.f;
-        d[e] = p[e] * (dp[g4 * 4 + e] - dm[e]);
+        for (int e = 0; e < 4; ++e) {
+          const int row = q0 + g4 * 8 + hh * 4 + e;
+          const bool vis = key < a.Sk && row < a.Sq && lv[e] != kNegInf && (!a.causal || key <= row + delta);
+          p[e] = vis ? exp2_fast(fmaf(x[g4 * 4 + e], a.scale_log2, -lv[e] * kLog2e)) : 0.f;
+        }
+        op[g4 * 2] = pack_bf16x2(p[0], p[1]);
+        op[g4 * 2 + 1] = pack_bf16x2(p[2], p[3]);
       }
-      pp[g4 * 2] = pack_bf16x2(p[0], p[1]);
-      pp[g4 * 2 + 1] = pack_bf16x2(p[2], p[3]);
-      dd[g4 * 2] = pack_bf16x2(d[0], d[1]);
-      dd[g4 * 2 + 1] = pack_bf16x2(d[2], d[3]);
+      *reinterpret_cast<u32x4*>(pslot) = u32x4{op[0], op[1], op[2], op[3]};
+      *reinterpret_cast<u32x4*>(pslot + 4) = u32x4{op[4], op[5], op[6], op[7]};
+    }
+    // P is in LDS for the dS waves (an LDS-only barrier: the next slab's loads stay in flight)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    if (ds_wave) {
+      const u32x4 p0 = *reinterpret_cast<const u32x4*>(pslot);
+      const u32x4 p1 = *reinterpret_cast<const u32x4*>(pslot + 4);
+      const uint32_t pw[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 dm = *reinterpret_cast<const f32x4*>(dsm[buf] + g4 * 8 + hh * 4);
+        float d[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t pair = pw[g4 * 2 + (e >> 1)];
+          const float pe = (e & 1) ? bf16_hi(pair) : bf16_lo(pair);
+          d[e] = pe * (x[g4 * 4 + e] - dm[e]);
+        }
+        op[g4 * 2] = pack_bf16x2(d[0], d[1]);
+        op[g4 * 2 + 1] = pack_bf16x2(d[2], d[3]);
+      }
     }
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
-      const u32x4 pb = {pp[hb * 4], pp[hb * 4 + 1], pp[hb * 4 + 2], pp[hb * 4 + 3]};
-      const u32x4 db_ = {dd[hb * 4], dd[hb * 4 + 1], dd[hb * 4 + 2], dd[hb * 4 + 3]};
+      const u32x4 ob = {op[hb * 4], op[hb * 4 + 1], op[hb * 4 + 2], op[hb * 4 + 3]};
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        const u32x2 dlo = ds_read_tr16(Db + hb * 16 * RS + trlo[db]);
-        const u32x2 dhi = ds_read_tr16(Db + hb * 16 * RS + trhi[db]);
-        dv[db] = mfma32x32x16(as_bf16x8(u32x4{dlo[0], dlo[1], dhi[0], dhi[1]}), as_bf16x8(pb), dv[db]);
-        const u32x2 qlo = ds_read_tr16(Qb + hb * 16 * RS + trlo[db]);
-        const u32x2 qhi = ds_read_tr16(Qb + hb * 16 * RS + trhi[db]);
-        dk[db] = mfma32x32x16(as_bf16x8(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}), as_bf16x8(db_), dk[db]);
+        const u32x2 lo2 = ds_read_tr16(trans + hb * 16 * RS + trlo[db]);
+        const u32x2 hi2 = ds_read_tr16(trans + hb * 16 * RS + trhi[db]);
+        acc[db] = mfma32x32x16(as_bf16x8(u32x4{lo2[0], lo2[1], hi2[0], hi2[1]}), as_bf16x8(ob), acc[db]);
       }
     }
     u = un;
@@ -387,17 +407,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
     buf ^= 1;
   }
 
-  // one chunk: the gradients themselves; several: a partial per chunk, summed by bwd_reduce
-  float* dkp;
-  float* dvp;
-  float ks_ = a.scale;
+    // one chunk: the gradient itself; several: a partial per chunk, summed by bwd_reduce
+  const int which = ds_wave ? 0 : 1;  // 0 dK, 1 dV
+  float* dst;
+  float mul = 1.f;
   if (split) {
-    dkp = a.part + ((int64_t)wid * 2 * SB + w * 32 + lq) * D;
-    dvp = dkp + SB * D;
-    ks_ = 1.f;
+    dst = a.part + (((int64_t)wid * 2 + which) * SB + kg * 32 + lq) * D;
   } else {
-    dkp = a.dk + (((int64_t)b * a.Sk + key) * a.Hkv + hkv) * D;
-    dvp = a.dv + (((int64_t)b * a.Sk + key) * a.Hkv + hkv) * D;
+    dst = (ds_wave ? a.dk : a.dv) + (((int64_t)b * a.Sk + key) * a.Hkv + hkv) * D;
+    if (ds_wave) mul = a.scale;
   }
   if (split || key < a.Sk) {
 #pragma unroll
@@ -405,10 +423,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1))) vo
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d = db * 32 + g4 * 8 + hh * 4;
-        *reinterpret_cast<f32x4*>(dkp + d) =
-            f32x4{dk[db][g4 * 4] * ks_, dk[db][g4 * 4 + 1] * ks_, dk[db][g4 * 4 + 2] * ks_, dk[db][g4 * 4 + 3] * ks_};
-        *reinterpret_cast<f32x4*>(dvp + d) =
-            f32x4{dv[db][g4 * 4], dv[db][g4 * 4 + 1], dv[db][g4 * 4 + 2], dv[db][g4 * 4 + 3]};
+        *reinterpret_cast<f32x4*>(dst + d) = f32x4{acc[db][g4 * 4] * mul, acc[db][g4 * 4 + 1] * mul,
+                                                   acc[db][g4 * 4 + 2] * mul, acc[db][g4 * 4 + 3] * mul};
       }
   }
 }

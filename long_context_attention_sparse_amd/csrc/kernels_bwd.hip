@@ -23,7 +23,7 @@ void launch_bwd(const BwdArgs& a, int chunk_bound, hipStream_t st) {
     hipLaunchKernelGGL(bwd_dense_count_kernel, dim3((n_lists + 255) / 256), dim3(256), 0, st, a);
     hipLaunchKernelGGL(bwd_scan_kernel, dim3(1), dim3(1024), 0, st, a);
   }
-  hipLaunchKernelGGL(bwd_dkdv_kernel<2>, dim3(chunk_bound), dim3(128), 0, st, a);
+  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(chunk_bound), dim3(256), 0, st, a);
   hipLaunchKernelGGL(bwd_reduce_kernel, dim3(n_lists), dim3(256), 0, st, a);
   const unsigned dq_grid = (unsigned)((int64_t)a.B * a.Hq * a.nqb);
   if (a.BM == 128) hipLaunchKernelGGL(bwd_dq_kernel<4>, dim3(dq_grid), dim3(256), 0, st, a);

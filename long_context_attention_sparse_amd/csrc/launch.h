@@ -22,9 +22,9 @@ void launch_gated(const GatedArgs& a, bool calib, hipStream_t st);
 // threshold_kernel: grid (nqb, Hq), 256 threads; nqb <= kThreshMaxCand.
 void launch_threshold(const ThresholdArgs& a, hipStream_t st);
 
-// backward: bwd_dot, the lists (block patterns: bwd_zero / bwd_count / bwd_scan / bwd_fill;
-// dense: bwd_dense_count / bwd_scan), bwd_dkdv over chunk_bound workgroups (an upper bound on
-// the chunks), bwd_reduce, bwd_dq.
+// backward: bwd_dot, the lists (block patterns: bwd_bits_zero / bwd_bits_set / bwd_list_count /
+// bwd_scan / bwd_list_fill; dense: bwd_dense_count / bwd_scan), bwd_dkdv (four waves) over
+// chunk_bound workgroups (an upper bound on the chunks), bwd_reduce, bwd_dq.
 void launch_bwd(const BwdArgs& a, int chunk_bound, hipStream_t st);
 // selected attention: sel_zero, sel_count, sel_scan, sel_fill, then selected_kernel over
 // main_grid workgroups (an upper bound on the chunks; the surplus exits at once).
