@@ -236,18 +236,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
   const int n_lists = a.B * a.Hkv * a.nks;
   const int wid = wg_x();
   if (wid >= a.chunkp[n_lists]) return;  // uniform: the grid is an upper bound
-  int lo = 0, hi = n_lists;              // list with chunkp[lo] <= wid < chunkp[lo + 1]
+  // Neighbouring sub-blocks (lists 2p and 2p + 1) read mostly the same query slabs, in the same
+  // order: their chunks are dealt in blocks of eight, list 2p's then list 2p + 1's, so that
+  // chunk c of both lands on one XCD (workgroup ids 8 apart) at about the same time and the
+  // second reads the slabs from that XCD's L2.
+  int lo = 0, hi = (n_lists + 1) >> 1;  // pair with chunkp[2 lo] <= wid < chunkp[2 lo + 2]
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (a.chunkp[mid] <= wid) lo = mid;
+    if (a.chunkp[2 * mid] <= wid) lo = mid;
     else hi = mid;
   }
-  const int list = lo;
+  const int la = 2 * lo;
+  const int n0 = a.chunkp[la + 1] - a.chunkp[la];
+  const int n1 = la + 1 < n_lists ? a.chunkp[la + 2] - a.chunkp[la + 1] : 0;
+  const int full = min(n0, n1) >> 3;
+  int r = wid - a.chunkp[la], list, chunk;
+  if (r < 16 * full) {
+    list = la + ((r >> 3) & 1);
+    chunk = (r >> 4) * 8 + (r & 7);
+  } else {
+    r -= 16 * full;
+    const int ra = n0 - 8 * full;
+    list = r < ra ? la : la + 1;
+    chunk = 8 * full + (r < ra ? r : r - ra);
+  }
   const int sub = list % a.nks;
   const int bh = list / a.nks;
   const int hkv = bh % a.Hkv, b = bh / a.Hkv;
   const int key0 = sub * SB;
-  const int chunk = wid - a.chunkp[list];
+  const int slot = a.chunkp[list] + chunk;  // this chunk's partial (bwd_reduce sums them in order)
   const bool split = a.chunkp[list + 1] - a.chunkp[list] > 1;
   const int delta = a.Sk - a.Sq;
   const int t = tid_x();
@@ -307,7 +324,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
   // Q and dO rows q0 + 8w + 4x + l/16 of the slab (clamped to the last row: finite data the
   // mask then ignores), lane l into slot l%16; LSE (wave 0) and D (wave 1) by 8 lanes each
   const int lrow = l >> 4, lslot = l & 15;
-  auto issue = [&](int h, int q0, int bi) __attribute__((always_inline)) {
+  auto issue = [&](int h, int q0, uint16_t* __restrict__ nq, uint16_t* __restrict__ nd, float* __restrict__ nl,
+                   float* __restrict__ nm) __attribute__((always_inline)) {
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
       const int rl = w * 8 + x * 4 + lrow;
@@ -318,13 +336,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
       const char* dp = reinterpret_cast<const char*>(reinterpret_cast<const uint16_t*>(a.dout.ptr) +
                                                      (int64_t)b * a.dout.sb + (int64_t)gr * a.dout.ss +
                                                      (int64_t)h * a.dout.sh);
-      __builtin_amdgcn_global_load_lds(qp + piece, BSA_LDS(Qs[bi] + (w * 8 + x * 4) * RS), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(dp + piece, BSA_LDS(Ds[bi] + (w * 8 + x * 4) * RS), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(qp + piece, BSA_LDS(nq + (w * 8 + x * 4) * RS), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(dp + piece, BSA_LDS(nd + (w * 8 + x * 4) * RS), 16, 0, 0);
     }
     if (w < 2 && l < 8) {
       const int r4 = max(0, min(q0 + 4 * l, a.Sq - 4));  // a clamped group of 4 rows
       const float* src = (w == 0 ? a.lse : a.dsum) + ((int64_t)b * a.Hq + h) * a.Sq + r4;
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(src), BSA_LDS(w == 0 ? ls[bi] : dsm[bi]), 16, 0,
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(src), BSA_LDS(w == 0 ? nl : nm), 16, 0,
                                        0);
     }
   };
@@ -333,17 +351,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
   int h, q0;
   int u = next_unit(u0, h, q0);
   int buf = 0;
-  if (u < u1) issue(h, q0, 0);
-  while (u < u1) {
+  if (u < u1) issue(h, q0, Qs[0], Ds[0], ls[0], dsm[0]);
+  // One slab from the current buffers while the next slab streams into the other ones.  The
+  // restrict-qualified buffer parameters tell the compiler that those loads cannot alias the
+  // reads of this slab, so it does not make the reads wait for them.
+  auto step = [&](const uint16_t* __restrict__ Qb, const uint16_t* __restrict__ Db, const float* __restrict__ lb,
+                  const float* __restrict__ mb, uint16_t* __restrict__ nq, uint16_t* __restrict__ nd,
+                  float* __restrict__ nl, float* __restrict__ nm) __attribute__((always_inline)) {
     int hn = 0, q0n = 0;
     const int un = next_unit(u + 1, hn, q0n);
     // this slab's tiles are in LDS from every wave, every wave is done with the other buffer
     // and the dS waves have read the previous P
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (un < u1) issue(hn, q0n, buf ^ 1);  // the next slab streams in during this one
-    const uint16_t* Qb = Qs[buf];
-    const uint16_t* Db = Ds[buf];
+    if (un < u1) issue(hn, q0n, nq, nd, nl, nm);  // the next slab streams in during this one
     const uint16_t* rows = ds_wave ? Db : Qb;   // A operand of S^T / dP^T
     const uint16_t* trans = ds_wave ? Qb : Db;  // transposed operand of dK^T / dV^T
     f32x16 x = {};
@@ -355,7 +376,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
     if (!ds_wave) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const f32x4 lv = *reinterpret_cast<const f32x4*>(ls[buf] + g4 * 8 + hh * 4);
+        const f32x4 lv = *reinterpret_cast<const f32x4*>(lb + g4 * 8 + hh * 4);
         float p[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -369,17 +390,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
       *reinterpret_cast<u32x4*>(pslot) = u32x4{op[0], op[1], op[2], op[3]};
       *reinterpret_cast<u32x4*>(pslot + 4) = u32x4{op[4], op[5], op[6], op[7]};
     }
-    // P is in LDS for the dS waves (an LDS-only barrier: the next slab's loads stay in flight)
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    // P is in LDS for the dS waves.  The barrier waits for LDS operations only (a release
+    // fence would also wait for the next slab's loads, which write LDS); the empty asm
+    // statements with memory clobbers keep the compiler from moving LDS accesses across it.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    asm volatile("" ::: "memory");
     if (ds_wave) {
       const u32x4 p0 = *reinterpret_cast<const u32x4*>(pslot);
       const u32x4 p1 = *reinterpret_cast<const u32x4*>(pslot + 4);
       const uint32_t pw[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const f32x4 dm = *reinterpret_cast<const f32x4*>(dsm[buf] + g4 * 8 + hh * 4);
+        const f32x4 dm = *reinterpret_cast<const f32x4*>(mb + g4 * 8 + hh * 4);
         float d[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -404,6 +427,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
     u = un;
     h = hn;
     q0 = q0n;
+  };
+  while (u < u1) {
+    step(Qs[buf], Ds[buf], ls[buf], dsm[buf], Qs[buf ^ 1], Ds[buf ^ 1], ls[buf ^ 1], dsm[buf ^ 1]);
     buf ^= 1;
   }
 
@@ -412,7 +438,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
   float* dst;
   float mul = 1.f;
   if (split) {
-    dst = a.part + (((int64_t)wid * 2 + which) * SB + kg * 32 + lq) * D;
+    dst = a.part + (((int64_t)slot * 2 + which) * SB + kg * 32 + lq) * D;
   } else {
     dst = (ds_wave ? a.dk : a.dv) + (((int64_t)b * a.Sk + key) * a.Hkv + hkv) * D;
     if (ds_wave) mul = a.scale;
@@ -534,32 +560,34 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4
   const int lrow = l >> 4, lslot = l & 15;
   const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.k.ptr) + (int64_t)b * a.k.sb + (int64_t)hkv * a.k.sh;
   const uint16_t* vbase = reinterpret_cast<const uint16_t*>(a.v.ptr) + (int64_t)b * a.v.sb + (int64_t)hkv * a.v.sh;
-  auto issue = [&](int key0, int bi) __attribute__((always_inline)) {
+  auto issue = [&](int key0, uint16_t* __restrict__ nk, uint16_t* __restrict__ nv) __attribute__((always_inline)) {
 #pragma unroll
     for (int x = 0; x < RPW / 4; ++x) {
       const int rl = w * RPW + x * 4 + lrow;
       const int gk = min(key0 + rl, a.Sk - 1);
       const uint32_t piece = (uint32_t)((lslot ^ k_swz(rl)) << 4);
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(kbase + (int64_t)gk * a.k.ss) + piece,
-                                       BSA_LDS(Ks[bi] + (w * RPW + x * 4) * RS), 16, 0, 0);
+                                       BSA_LDS(nk + (w * RPW + x * 4) * RS), 16, 0, 0);
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(vbase + (int64_t)gk * a.v.ss) + piece,
-                                       BSA_LDS(Vs[bi] + (w * RPW + x * 4) * RS), 16, 0, 0);
+                                       BSA_LDS(nv + (w * RPW + x * 4) * RS), 16, 0, 0);
     }
   };
 
   int key0 = 0;
   int x = next_sub(0, key0);
   int buf = 0;
-  if (x < n_sub) issue(key0, 0);
-  while (x < n_sub) {
+  if (x < n_sub) issue(key0, Ks[0], Vs[0]);
+  // One key block from the current buffers while the next streams into the other ones (the
+  // restrict-qualified parameters let the compiler see that the two cannot alias, so the reads
+  // of this block do not wait for those loads).
+  auto step = [&](const uint16_t* __restrict__ Kb, const uint16_t* __restrict__ Vb, uint16_t* __restrict__ nk,
+                  uint16_t* __restrict__ nv) __attribute__((always_inline)) {
     int key0n = 0;
     const int xn = next_sub(x + 1, key0n);
     // this block's K and V are in LDS from every wave; every wave is done with the other buffer
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (xn < n_sub) issue(key0n, buf ^ 1);
-    const uint16_t* Kb = Ks[buf];
-    const uint16_t* Vb = Vs[buf];
+    if (xn < n_sub) issue(key0n, nk, nv);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       f32x16 st = {}, dpt = {};
@@ -596,6 +624,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4
     }
     x = xn;
     key0 = key0n;
+  };
+  while (x < n_sub) {
+    step(Ks[buf], Vs[buf], Ks[buf ^ 1], Vs[buf ^ 1]);
     buf ^= 1;
   }
   if (row_ok) {
