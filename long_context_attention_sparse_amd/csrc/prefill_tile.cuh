@@ -178,12 +178,39 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         __builtin_amdgcn_global_load_lds(p + (is_k ? k_lane + (kx ^ ((x & 3) << 6)) : v_lane),
                                          BSA_LDS(tile + (w * 8 + x) * 4 * RS), 16, 0, 0);
       }
-    } else {
+    } else if constexpr (KIND != 2) {
 #pragma unroll
       for (int x = 0; x < 8; ++x) {
         int key = key_of(srow0 + x * 4 + lrow, r, staged);
         key = key < 0 ? 0 : key;
         const char* p = reinterpret_cast<const char*>(src + (int64_t)key * ss);
+        __builtin_amdgcn_global_load_lds(p + (is_k ? (kx ^ ((x & 3) << 6)) : vx), BSA_LDS(tile + (w * 8 + x) * 4 * RS),
+                                         16, 0, 0);
+      }
+    } else {
+      // all eight keys first, then the loads: a key read from memory is waited for once, not
+      // once per load (each wait would also wait for the loads already in flight)
+      int keys[8];
+      if (!r.gathered) {  // a window that crosses the sequence bounds: arithmetic only
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          const int key = r.key0 + srow0 + x * 4 + lrow;
+          keys[x] = r.valid && (unsigned)key < (unsigned)kv_len ? key : 0;
+        }
+      } else if (staged && r.gbase + 64 <= kCols) {  // gathered, indices staged in LDS
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          const int xi = r.gbase + srow0 + x * 4 + lrow;
+          const int key = xi < ncol ? cols_s[xi] : -1;
+          keys[x] = r.valid && (unsigned)key < (unsigned)kv_len ? key : 0;
+        }
+      } else {
+#pragma unroll
+        for (int x = 0; x < 8; ++x) keys[x] = max(0, key_of(srow0 + x * 4 + lrow, r, staged));
+      }
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        const char* p = reinterpret_cast<const char*>(src + (int64_t)keys[x] * ss);
         __builtin_amdgcn_global_load_lds(p + (is_k ? (kx ^ ((x & 3) << 6)) : vx), BSA_LDS(tile + (w * 8 + x) * 4 * RS),
                                          16, 0, 0);
       }
