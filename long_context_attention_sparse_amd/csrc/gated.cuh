@@ -13,10 +13,10 @@
 // operand is read with ds_read_b64_tr_b16.  Per tile:
 //   [K_j resident] S_ij (8 MFMAs per 32-key block), diagonal mask, tile max
 //   -> LDS exchange + barrier (every wave is done with K_j) -> keep decision
-//   -> kept tiles: issue V_j, wait, barrier, issue K_next, softmax + PV;
+//   -> kept tiles: issue V_j, softmax update and P, wait, barrier, issue K_next, PV;
 //      skipped tiles: issue K_next -> wait for K_next -> barrier,
-// so the next K tile streams in during the PV product (kept tiles) or right
-// after the decision (skipped tiles).  (A workgroup-scope barrier waits for
+// so V_j streams in during the softmax and the next K tile during the PV product (kept
+// tiles) or right after the decision (skipped tiles).  (A workgroup-scope barrier waits for
 // every outstanding load, so K_next is issued after the V barrier, not
 // before it.)  Grid remapped XCD-aware, heaviest query blocks first.
 #pragma once
@@ -152,32 +152,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
     const bool more = n < i;
     if (keep) {
       issue_v(j * BN);
-      __builtin_amdgcn_s_waitcnt(0);
-      // V_j from every wave is in LDS; K_next streams in during the softmax and PV product
-      __syncthreads();
-      if (more) issue_k(tile_of(n + 1) * BN);
+      // the softmax update and P run while V_j streams in
       softmax_max_n<NB>(s, a.scale_log2, m_run, l_run, le_run, oacc);
       const float m_use = m_run == kNegInf ? 0.f : m_run;
       float psum = 0.f, pesum = 0.f;
+      uint32_t pk[NB][8];
 #pragma unroll
-      for (int kb = 0; kb < NB; ++kb) {
-        uint32_t pk[8];
+      for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; r += 4) {
           const float p0 = exp2_fast(fmaf(s[kb][r], a.scale_log2, -m_use));
           const float p1 = exp2_fast(fmaf(s[kb][r + 1], a.scale_log2, -m_use));
           const float p2 = exp2_fast(fmaf(s[kb][r + 2], a.scale_log2, -m_use));
           const float p3 = exp2_fast(fmaf(s[kb][r + 3], a.scale_log2, -m_use));
-          pk[r / 2] = pack_bf16x2(p0, p1);
-          pk[r / 2 + 1] = pack_bf16x2(p2, p3);
-          psum = bf16x2_sum_acc(pk[r / 2], psum);
-          psum = bf16x2_sum_acc(pk[r / 2 + 1], psum);
+          pk[kb][r / 2] = pack_bf16x2(p0, p1);
+          pk[kb][r / 2 + 1] = pack_bf16x2(p2, p3);
+          psum = bf16x2_sum_acc(pk[kb][r / 2], psum);
+          psum = bf16x2_sum_acc(pk[kb][r / 2 + 1], psum);
           pesum += (p0 + p1) + (p2 + p3);
         }
+      __builtin_amdgcn_s_waitcnt(0);
+      // V_j from every wave is in LDS; K_next streams in during the P V product
+      __syncthreads();
+      if (more) issue_k(tile_of(n + 1) * BN);
+#pragma unroll
+      for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb) {
           const int ks = kb * 2 + hb;
-          const u32x4 pb = {pk[hb * 4], pk[hb * 4 + 1], pk[hb * 4 + 2], pk[hb * 4 + 3]};
+          const u32x4 pb = {pk[kb][hb * 4], pk[kb][hb * 4 + 1], pk[kb][hb * 4 + 2], pk[kb][hb * 4 + 3]};
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) {
             const u32x2 lo = ds_read_tr16(Vt + ks * 16 * RS + voff[db]);
@@ -185,7 +188,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
             oacc[db] = mfma32x32x16(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), as_bf16x8(pb), oacc[db]);
           }
         }
-      }
       l_run += psum;
       le_run += pesum;
     } else if (more) {
