@@ -177,6 +177,11 @@ size_t bsa_workspace_size(const bsa_problem* prob, const bsa_pattern* pat);
  *   ws       device scratch of at least bsa_workspace_size() bytes (may be
  *            NULL when that is 0).  Overwritten; the caller keeps it alive
  *            until the stream has passed this call.
+ * Kernels: decode shapes (fixed length, no VS pattern, and the query rows of
+ * a kv head's group, G * Sq for dense or kv-head lists, Sq for query-head
+ * lists, at most 16) run on the split-KV decode kernel with D 64 or 128;
+ * every other shape runs on the tile kernels, which need D == 128
+ * (BSA_ERR_UNSUPPORTED for D == 64 there).
  * Errors: BSA_ERR_INVALID_ARG for NULL tensors, non-positive sizes,
  * Hq % Hkv != 0, pattern heads other than Hq/Hkv, Sk % block_N != 0;
  * BSA_ERR_UNSUPPORTED for D or block sizes outside the list above;
