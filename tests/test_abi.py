@@ -80,6 +80,7 @@ def test_fwd_argument_errors(lib):
     assert _fwd(lib, _prob(Hq=3, Hkv=2)) == bd.BSA_ERR_INVALID_ARG                # Hq % Hkv
     assert _fwd(lib, _prob(B=0)) == bd.BSA_ERR_INVALID_ARG
     assert _fwd(lib, _prob(D=96)) == bd.BSA_ERR_UNSUPPORTED                       # head dim
+    assert _fwd(lib, _prob(D=64, Sq=256)) == bd.BSA_ERR_UNSUPPORTED               # D 64 off the decode path
     assert _fwd(lib, _prob(softcap=-1.0)) == bd.BSA_ERR_INVALID_ARG               # softcap < 0
     assert _fwd(lib, _prob(softcap=float("nan"))) == bd.BSA_ERR_INVALID_ARG
     assert _fwd(lib, _prob(softcap=float("inf"))) == bd.BSA_ERR_INVALID_ARG
