@@ -32,6 +32,13 @@ namespace bsa {
 __device__ __forceinline__ float bf16_lo(uint32_t x) { return bf16_bits_to_f32(x & 0xffffu); }
 __device__ __forceinline__ float bf16_hi(uint32_t x) { return bf16_bits_to_f32(x >> 16); }
 
+// LDS slot of the 16-byte pieces of a tile row that is read both ways: as MFMA row operands
+// (16 consecutive rows, one piece each) and with the transposing read (4 consecutive rows,
+// 4 pieces each).  Piece p of row R sits in slot p ^ bwd_swz(R): the swizzle is a bijection on
+// R & 15 (row reads hit 16 different slots) whose top two bits are R & 3 (the four rows of a
+// transposed read land in four different groups of four slots), so neither read conflicts.
+__device__ __forceinline__ int bwd_swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+
 // D = sum_d dO * O: 16 threads per row, 16 rows per workgroup.
 __global__ __launch_bounds__(256) void bwd_dot_kernel(BwdArgs a) {
   const int64_t row = (int64_t)wg_x() * 16 + (tid_x() >> 4);
@@ -226,7 +233,7 @@ __global__ __launch_bounds__(1024) void bwd_scan_kernel(BwdArgs a) {
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int D = TD;
   constexpr int SB = 64;
-  constexpr int RS = D;  // 256-byte rows; 16-byte pieces swizzled by row (k_swz), as written by the DMA
+  constexpr int RS = D;  // 256-byte rows; 16-byte pieces swizzled by row (bwd_swz), as written by the DMA
   __shared__ __attribute__((aligned(16))) uint16_t Qs[2][32 * RS];
   __shared__ __attribute__((aligned(16))) uint16_t Ds[2][32 * RS];
   __shared__ __attribute__((aligned(16))) float ls[2][32];
@@ -283,7 +290,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
     kvreg[ks] = as_bf16x8(key < a.Sk ? ldg128(kvbase + (int64_t)key * kv.ss + ks * 16 + hh * 8) : u32x4{0, 0, 0, 0});
   int aoff[D / 16];
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) aoff[ks] = lq * RS + (((ks * 2 + hh) ^ k_swz(lq)) << 3);
+  for (int ks = 0; ks < D / 16; ++ks) aoff[ks] = lq * RS + (((ks * 2 + hh) ^ bwd_swz(lq)) << 3);
   int trlo[D / 32], trhi[D / 32];
   {
     const int tg = l >> 4, tr = l & 15;
@@ -291,8 +298,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
       const int col = db * 32 + (tg & 1) * 16 + (tr & 3) * 4;
-      trlo[db] = rr * RS + (((col >> 3) ^ k_swz(rr)) << 3) + (col & 7);
-      trhi[db] = (rr + 8) * RS + (((col >> 3) ^ k_swz(rr + 8)) << 3) + (col & 7);
+      trlo[db] = rr * RS + (((col >> 3) ^ bwd_swz(rr)) << 3) + (col & 7);
+      trhi[db] = (rr + 8) * RS + (((col >> 3) ^ bwd_swz(rr + 8)) << 3) + (col & 7);
     }
   }
   f32x16 acc[D / 32];  // dV^T (P wave) or dK^T (dS wave)
@@ -330,7 +337,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
     for (int x = 0; x < 2; ++x) {
       const int rl = w * 8 + x * 4 + lrow;
       const int gr = min(q0 + rl, a.Sq - 1);
-      const uint32_t piece = (uint32_t)((lslot ^ k_swz(rl)) << 4);
+      const uint32_t piece = (uint32_t)((lslot ^ bwd_swz(rl)) << 4);
       const char* qp = reinterpret_cast<const char*>(reinterpret_cast<const uint16_t*>(a.q.ptr) + (int64_t)b * a.q.sb +
                                                      (int64_t)gr * a.q.ss + (int64_t)h * a.q.sh);
       const char* dp = reinterpret_cast<const char*>(reinterpret_cast<const uint16_t*>(a.dout.ptr) +
@@ -347,7 +354,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
     }
   };
 
-  uint32_t* pslot = Ps[kg] + l * 8;
+  uint32_t* pslot = Ps[kg] + l * 4;  // two 16-byte halves per lane, 1 KB apart (no bank conflicts)
   int h, q0;
   int u = next_unit(u0, h, q0);
   int buf = 0;
@@ -388,7 +395,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
         op[g4 * 2 + 1] = pack_bf16x2(p[2], p[3]);
       }
       *reinterpret_cast<u32x4*>(pslot) = u32x4{op[0], op[1], op[2], op[3]};
-      *reinterpret_cast<u32x4*>(pslot + 4) = u32x4{op[4], op[5], op[6], op[7]};
+      *reinterpret_cast<u32x4*>(pslot + 256) = u32x4{op[4], op[5], op[6], op[7]};
     }
     // P is in LDS for the dS waves.  The barrier waits for LDS operations only (a release
     // fence would also wait for the next slab's loads, which write LDS); the empty asm
@@ -398,7 +405,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
     asm volatile("" ::: "memory");
     if (ds_wave) {
       const u32x4 p0 = *reinterpret_cast<const u32x4*>(pslot);
-      const u32x4 p1 = *reinterpret_cast<const u32x4*>(pslot + 4);
+      const u32x4 p1 = *reinterpret_cast<const u32x4*>(pslot + 256);
       const uint32_t pw[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
@@ -484,7 +491,7 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a) {
 template <int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4 ? 2 : 1))) void bwd_dq_kernel(BwdArgs a) {
   constexpr int D = TD;
-  constexpr int RS = D;  // 256-byte rows, 16-byte pieces swizzled by row (k_swz)
+  constexpr int RS = D;  // 256-byte rows, 16-byte pieces swizzled by row (bwd_swz)
   constexpr int RPW = 64 / NW;  // tile rows each wave loads
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][64 * RS];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][64 * RS];
@@ -518,7 +525,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4
   const int lim = !row_ok || lse2 == kNegInf ? -1 : (a.causal ? min(row + delta, a.Sk - 1) : a.Sk - 1);
   int koff[D / 16];
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) koff[ks] = lq * RS + (((ks * 2 + hh) ^ k_swz(lq)) << 3);
+  for (int ks = 0; ks < D / 16; ++ks) koff[ks] = lq * RS + (((ks * 2 + hh) ^ bwd_swz(lq)) << 3);
   int trlo[D / 32], trhi[D / 32];
   {
     const int tg = l >> 4, tr = l & 15;
@@ -526,8 +533,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
       const int col = db * 32 + (tg & 1) * 16 + (tr & 3) * 4;
-      trlo[db] = r4 * RS + (((col >> 3) ^ k_swz(r4)) << 3) + (col & 7);
-      trhi[db] = (r4 + 8) * RS + (((col >> 3) ^ k_swz(r4 + 8)) << 3) + (col & 7);
+      trlo[db] = r4 * RS + (((col >> 3) ^ bwd_swz(r4)) << 3) + (col & 7);
+      trhi[db] = (r4 + 8) * RS + (((col >> 3) ^ bwd_swz(r4 + 8)) << 3) + (col & 7);
     }
   }
   f32x16 dq[D / 32];
@@ -565,7 +572,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4
     for (int x = 0; x < RPW / 4; ++x) {
       const int rl = w * RPW + x * 4 + lrow;
       const int gk = min(key0 + rl, a.Sk - 1);
-      const uint32_t piece = (uint32_t)((lslot ^ k_swz(rl)) << 4);
+      const uint32_t piece = (uint32_t)((lslot ^ bwd_swz(rl)) << 4);
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(kbase + (int64_t)gk * a.k.ss) + piece,
                                        BSA_LDS(nk + (w * RPW + x * 4) * RS), 16, 0, 0);
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(vbase + (int64_t)gk * a.v.ss) + piece,
