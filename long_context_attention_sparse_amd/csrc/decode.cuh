@@ -39,7 +39,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
   constexpr int KS = D + 8;                    // Ks row stride in bf16 (pad: conflict-free b128 reads)
   constexpr int VSTR = 64 + 8;                 // Vt row stride in bf16
   constexpr int LDS_KV = (64 * KS + D * VSTR) * 2;
-  constexpr int LDS_MERGE = (4 * 16 * D + 3 * 64) * 4;
+  constexpr int MS = D + 4;                    // merge row stride in floats (conflict-free b128 stores)
+  constexpr int LDS_MERGE = (4 * 16 * MS + 3 * 64) * 4;
   constexpr int LDS_BYTES = LDS_KV > LDS_MERGE ? LDS_KV : LDS_MERGE;
   __shared__ __attribute__((aligned(16))) unsigned char smem[LDS_BYTES];
   __shared__ int ents[kDecodeEntsLds];
@@ -209,14 +210,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
   le_run += shfl_xor_f(le_run, 16);
   le_run += shfl_xor_f(le_run, 32);
   __syncthreads();
-  float* mo = reinterpret_cast<float*>(smem);  // [4][16][D]
-  float* mm = mo + 4 * 16 * D;                 // [4][16]
+  float* mo = reinterpret_cast<float*>(smem);  // [4][16][MS]
+  float* mm = mo + 4 * 16 * MS;                // [4][16]
   float* ml = mm + 64;
   float* mle = ml + 64;
 #pragma unroll
-  for (int db = 0; db < D / 16; ++db)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) mo[(w * 16 + lr) * D + db * 16 + kg * 4 + r] = oacc[db][r];
+  for (int db = 0; db < D / 16; ++db) *reinterpret_cast<f32x4*>(mo + (w * 16 + lr) * MS + db * 16 + kg * 4) = oacc[db];
   if (kg == 0) {
     mm[w * 16 + lr] = m_run;
     ml[w * 16 + lr] = l_run;
@@ -224,7 +223,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
   }
   __syncthreads();
 
-  constexpr int DPT = D / 16;  // head-dim values per thread in the merge
+  constexpr int DPT = D / 16;  // head-dim values per thread in the merge (4 per 64-wide half)
   const int row = t >> 4, dp = t & 15;
   if (row >= a.R) return;
   float M = kNegInf;
@@ -240,27 +239,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
   }
   const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
   const float lse_val = Le > 0.f ? (M + log2f(Le)) * kLn2 : kNegInf;
+  // this thread's head-dim values: 4 consecutive ones in each 64-wide half (d = 64j + 4dp + e),
+  // so that the 16 threads of a row read one contiguous 256-byte stretch per instruction
   float out[DPT];
 #pragma unroll
-  for (int i = 0; i < DPT; ++i) {
-    const int d = dp * DPT + i;
-    float acc = 0.f;
+  for (int j = 0; j < D / 64; ++j) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) acc += wt[ww] * mo[(ww * 16 + row) * D + d];
-    out[i] = acc * inv;
+    for (int ww = 0; ww < 4; ++ww) acc += wt[ww] * *reinterpret_cast<const f32x4*>(mo + (ww * 16 + row) * MS + j * 64 + dp * 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[j * 4 + e] = acc[e] * inv;
   }
   const int s_o = row / a.Gp;
   const int hq_o = hg * a.Gp + row % a.Gp;
   if (a.direct) {
-    const int64_t off = b * a.o.sb + (int64_t)s_o * a.o.ss + (int64_t)hq_o * a.o.sh + dp * DPT;
+    const int64_t off = b * a.o.sb + (int64_t)s_o * a.o.ss + (int64_t)hq_o * a.o.sh + dp * 4;
 #pragma unroll
-    for (int i = 0; i < DPT; i += 4) store4(a.o, off + i, out[i], out[i + 1], out[i + 2], out[i + 3]);
+    for (int j = 0; j < D / 64; ++j) store4(a.o, off + j * 64, out[j * 4], out[j * 4 + 1], out[j * 4 + 2], out[j * 4 + 3]);
     if (dp == 0 && a.lse) a.lse[((int64_t)b * a.Hq + hq_o) * a.Sq + s_o] = lse_val;
   } else {
     const int64_t slot = sg.slot0 + sp;
-    float* po = a.part_o + (((slot * a.B + b) * a.Sq + s_o) * a.Hq + hq_o) * D + dp * DPT;
+    float* po = a.part_o + (((slot * a.B + b) * a.Sq + s_o) * a.Hq + hq_o) * D + dp * 4;
 #pragma unroll
-    for (int i = 0; i < DPT; i += 4) *reinterpret_cast<f32x4*>(po + i) = f32x4{out[i], out[i + 1], out[i + 2], out[i + 3]};
+    for (int j = 0; j < D / 64; ++j)
+      *reinterpret_cast<f32x4*>(po + j * 64) = f32x4{out[j * 4], out[j * 4 + 1], out[j * 4 + 2], out[j * 4 + 3]};
     if (dp == 0) a.part_lse[((slot * a.B + b) * a.Hq + hq_o) * a.Sq + s_o] = lse_val;
   }
 }

@@ -66,7 +66,7 @@ inline int device_cus() {
 #ifndef BSA_DECODE_ROUNDS
 #define BSA_DECODE_ROUNDS 4
 #endif
-constexpr int kDecodeWgPerCu = 4;                  // resident decode workgroups per CU (124 VGPRs, 36 KB LDS)
+constexpr int kDecodeWgPerCu = 4;                  // resident decode workgroups per CU (128 VGPRs, 36 KB LDS)
 constexpr int kDecodeRounds = BSA_DECODE_ROUNDS;   // whole rounds of resident workgroups per launch
 constexpr int kMaxChunksPerSplit = 96;             // more rounds when splits would get longer than this
 
