@@ -27,6 +27,37 @@ namespace bsa {
 
 
 
+// A thread's output row, written four entries at a time when the row is 16-byte aligned: each
+// lane writes its own row, so every store is a separate L2 request, and 16-byte stores make a
+// quarter as many of them.
+template <bool VEC>
+struct RowWriter {
+  int32_t* base;
+  int n = 0;
+  int32_t v0 = 0, v1 = 0, v2 = 0, v3 = 0;  // the last four entries
+  __device__ __forceinline__ explicit RowWriter(int32_t* p) : base(p) {}
+  __device__ __forceinline__ void push(int32_t x) {
+    if constexpr (VEC) {
+      v0 = v1;
+      v1 = v2;
+      v2 = v3;
+      v3 = x;
+      if ((++n & 3) == 0)
+        *reinterpret_cast<u32x4*>(base + n - 4) = u32x4{(uint32_t)v0, (uint32_t)v1, (uint32_t)v2, (uint32_t)v3};
+    } else {
+      base[n++] = x;
+    }
+  }
+  __device__ __forceinline__ void flush() {
+    if constexpr (VEC) {
+      const int r = n & 3;  // entries not yet written: the last r
+      if (r >= 3) base[n - 3] = v1;
+      if (r >= 2) base[n - 2] = v2;
+      if (r >= 1) base[n - 1] = v3;
+    }
+  }
+};
+
 __global__ __launch_bounds__(kVSConvThreads) void vs_convert_kernel(VSConvArgs a) {
   extern __shared__ int32_t lists[];
   const int bh = blockIdx.y;
@@ -44,8 +75,6 @@ __global__ __launch_bounds__(kVSConvThreads) void vs_convert_kernel(VSConvArgs a
   }
   __syncthreads();
   if (m >= a.rows) return;
-  const int32_t* sl = staged ? lists : sl_g;
-  const int32_t* vt = staged ? lists + a.nnz_s : vt_g;
 
   const int64_t item = (int64_t)bh * a.rows + m;
   const int q_len = a.q_seqlens[b];
@@ -62,41 +91,73 @@ __global__ __launch_bounds__(kVSConvThreads) void vs_convert_kernel(VSConvArgs a
   int32_t* bo = a.bo + item * a.nnz_s;
   int32_t* co = a.ci + item * a.nnz_v;
 
-  int nwin = 0, ncol = 0, vi = 0;
-  int frontier = 0;            // valid once nwin > 0
-  int prev_end = -0x7fffffff;  // end (exclusive) of the last window
-  for (int si = 0; si < ns; ++si) {
-    const int s = sl[si];
-    const int e = last_visible - s;
-    if (e < 0) continue;
-    const int lo = max(0, r0 + d - s);
-    int wstart;
-    if (nwin == 0 || lo >= frontier) {
-      wstart = lo;
-    } else if (e >= frontier) {
-      wstart = frontier;
-    } else {
-      continue;
+  // the single pass over both lists; called once with the LDS copies and once with the global
+  // lists, so that each call reads through pointers of a known address space (LDS reads, not
+  // generic ones)
+  auto convert = [&](const int32_t* sl, const int32_t* vt, auto wo, auto co_w) __attribute__((always_inline)) {
+    int vi = 0;
+    int frontier = 0;            // valid once a window exists
+    int prev_end = -0x7fffffff;  // end (exclusive) of the last window
+    // the next vertical index, read one step ahead so the LDS latency overlaps the compare
+    int vnext = vi < nv ? vt[vi] : 0x7fffffff;
+    auto slash = [&](int s) __attribute__((always_inline)) {
+      const int e = last_visible - s;
+      if (e < 0) return;
+      const int lo = max(0, r0 + d - s);
+      int wstart;
+      if (wo.n == 0 || lo >= frontier) {
+        wstart = lo;
+      } else if (e >= frontier) {
+        wstart = frontier;
+      } else {
+        return;
+      }
+      frontier = wstart + a.BN;
+      // verticals left of this window: outside every window unless inside the previous one
+      while (vi < nv) {
+        const int v = vnext;
+        if (v >= wstart || v > last_visible) break;
+        ++vi;
+        vnext = vi < nv ? vt[vi] : 0x7fffffff;
+        if (v >= prev_end) co_w.push(v);
+      }
+      wo.push(wstart);
+      prev_end = frontier;
+    };
+    // slash indices four at a time (one 16-byte read) where the list allows it
+    int si = 0;
+    if ((reinterpret_cast<uintptr_t>(sl) & 15) == 0) {
+      for (; si + 4 <= ns; si += 4) {
+        const u32x4 s4 = *reinterpret_cast<const u32x4*>(sl + si);
+        slash((int)s4[0]);
+        slash((int)s4[1]);
+        slash((int)s4[2]);
+        slash((int)s4[3]);
+      }
     }
-    frontier = wstart + a.BN;
-    // verticals left of this window: outside every window unless inside the previous one
+    for (; si < ns; ++si) slash(sl[si]);
     while (vi < nv) {
-      const int v = vt[vi];
-      if (v >= wstart || v > last_visible) break;
-      if (v >= prev_end) co[ncol++] = v;
+      const int v = vnext;
+      if (v > last_visible) break;
       ++vi;
+      vnext = vi < nv ? vt[vi] : 0x7fffffff;
+      if (v >= prev_end) co_w.push(v);
     }
-    bo[nwin++] = wstart;
-    prev_end = frontier;
+    wo.flush();
+    co_w.flush();
+    a.bc[item] = wo.n;
+    a.cc[item] = co_w.n;
+  };
+  // 16-byte stores need 16-byte aligned rows (uniform over the launch)
+  const bool vec = ((a.nnz_s | a.nnz_v) & 3) == 0 && ((reinterpret_cast<uintptr_t>(a.bo) |
+                                                       reinterpret_cast<uintptr_t>(a.ci)) & 15) == 0;
+  if (vec) {
+    if (staged) convert(lists, lists + a.nnz_s, RowWriter<true>(bo), RowWriter<true>(co));
+    else convert(sl_g, vt_g, RowWriter<true>(bo), RowWriter<true>(co));
+  } else {
+    if (staged) convert(lists, lists + a.nnz_s, RowWriter<false>(bo), RowWriter<false>(co));
+    else convert(sl_g, vt_g, RowWriter<false>(bo), RowWriter<false>(co));
   }
-  while (vi < nv) {
-    const int v = vt[vi];
-    if (v > last_visible) break;
-    if (v >= prev_end) co[ncol++] = v;
-    ++vi;
-  }
-  a.bc[item] = nwin;
-  a.cc[item] = ncol;
 }
 
 }  // namespace bsa
