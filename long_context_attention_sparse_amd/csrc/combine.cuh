@@ -28,9 +28,40 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int64_t o_stride = (int64_t)a.B * a.Sq * a.Hq * a.D;
   const int64_t o0 = row * a.D + d;  // row = (b*Sq + s)*Hq + h
 
-  // batches of 8 partials: all loads of a batch are issued before any is used
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f, m = kNegInf;
+  constexpr int ONE = 16;
+  if (a.P <= ONE) {
+    // up to 16 partials: every load in flight at once, one round trip to memory
+    float lv[ONE];
+    f32x4 ov[ONE];
+#pragma unroll
+    for (int j = 0; j < ONE; ++j) {
+      const bool ok = j < a.P;
+      lv[j] = ok ? a.lse_part[lse0 + j * lse_stride] : kNegInf;
+      ov[j] = ok ? *reinterpret_cast<const f32x4*>(a.o_part + o0 + j * o_stride) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int j = 0; j < ONE; ++j) m = fmaxf(m, lv[j]);
+    if (m != kNegInf) {
+#pragma unroll
+      for (int j = 0; j < ONE; ++j) {
+        const float wgt = expf(lv[j] - m);
+        if (wgt != 0.f) {  // an empty partial's o is never used (it may hold anything)
+          acc += wgt * ov[j];
+          wsum += wgt;
+        }
+      }
+    }
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    acc *= inv;
+    const int64_t off = (int64_t)b * a.o.sb + (int64_t)s * a.o.ss + (int64_t)h * a.o.sh + d;
+    store4(a.o, off, acc[0], acc[1], acc[2], acc[3]);
+    if (a.lse && d == 0) a.lse[lse0] = wsum > 0.f ? m + logf(wsum) : kNegInf;
+    return;
+  }
+  // more partials: batches of 8, all loads of a batch issued before any is used
   constexpr int BATCH = 8;
-  float m = kNegInf;
   for (int p0 = 0; p0 < a.P; p0 += BATCH) {
     float lv[BATCH];
 #pragma unroll
@@ -38,8 +69,6 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 #pragma unroll
     for (int j = 0; j < BATCH; ++j) m = fmaxf(m, lv[j]);
   }
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float wsum = 0.f;
   if (m != kNegInf) {
     for (int p0 = 0; p0 < a.P; p0 += BATCH) {
       float lv[BATCH];
