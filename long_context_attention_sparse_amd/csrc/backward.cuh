@@ -493,8 +493,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4
   constexpr int D = TD;
   constexpr int RS = D;  // 256-byte rows, 16-byte pieces swizzled by row (bwd_swz)
   constexpr int RPW = 64 / NW;  // tile rows each wave loads
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][64 * RS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][64 * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t K0[64 * RS], K1[64 * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t V0[64 * RS], V1[64 * RS];
 
   const int item = wg_x();
   const int i = item % a.nqb;
@@ -583,9 +583,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4
   int key0 = 0;
   int x = next_sub(0, key0);
   int buf = 0;
-  if (x < n_sub) issue(key0, Ks[0], Vs[0]);
+  if (x < n_sub) issue(key0, K0, V0);
   // One key block from the current buffers while the next streams into the other ones (the
-  // restrict-qualified parameters let the compiler see that the two cannot alias, so the reads
+  // buffers are separate arrays, so the compiler sees that the two cannot alias and the reads
   // of this block do not wait for those loads).
   auto step = [&](const uint16_t* __restrict__ Kb, const uint16_t* __restrict__ Vb, uint16_t* __restrict__ nk,
                   uint16_t* __restrict__ nv) __attribute__((always_inline)) {
@@ -633,7 +633,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4
     key0 = key0n;
   };
   while (x < n_sub) {
-    step(Ks[buf], Vs[buf], Ks[buf ^ 1], Vs[buf ^ 1]);
+    step(buf ? K1 : K0, buf ? V1 : V0, buf ? K0 : K1, buf ? V0 : V1);
     buf ^= 1;
   }
   if (row_ok) {
