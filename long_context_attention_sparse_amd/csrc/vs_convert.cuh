@@ -25,8 +25,6 @@
 
 namespace bsa {
 
-
-
 // A thread's output row, written four entries at a time when the row is 16-byte aligned: each
 // lane writes its own row, so every store is a separate L2 request, and 16-byte stores make a
 // quarter as many of them.
