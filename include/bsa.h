@@ -290,6 +290,7 @@ bsa_status bsa_fwd_gated(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, bs
  *   dq         device float32 [B, Sq, Hq, D] contiguous; dk, dv float32
  *              [B, Sk, Hkv, D] contiguous; every entry is written.
  *   workspace  bsa_bwd_workspace_size bytes, 256-byte aligned: row dots,
+ *              a bitmap of which query blocks name each key block, the
  *              per-64-key-block lists of (query head, query block) pairs,
  *              and room for float32 dK/dV partials of lists split over
  *              several workgroups (64 KB per 128 query slabs of 32 rows, an
@@ -297,9 +298,9 @@ bsa_status bsa_fwd_gated(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, bs
  *              lists).
  * A 64-key block's dK and dV come from the workgroups that take its list in
  * chunks of 128 slabs (partials summed in chunk order), dQ from one
- * workgroup per query block: no atomics on the gradients; the order in
- * which a block's (head, query block) pairs are listed may change from run
- * to run, so dK and dV may differ in the last float32 bits between runs.
+ * workgroup per query block: no atomics on the gradients, and the lists are
+ * built in a fixed order (by head, then query block), so the gradients are
+ * the same bits on every run.
  * Errors: as bsa_fwd; BSA_ERR_UNSUPPORTED outside the cases above. */
 size_t bsa_bwd_workspace_size(const bsa_problem* prob, const bsa_pattern* pat);
 bsa_status bsa_bwd(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, bsa_tensor v, const bsa_pattern* pat,
