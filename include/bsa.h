@@ -284,11 +284,14 @@ bsa_status bsa_fwd_gated(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, bs
  * dS = P * (dO V^T - D): dV = P^T dO, dQ = scale dS K, dK = scale dS^T Q
  * (summed over the query heads of a kv head).
  *   pat        NULL / dense or BSA_PAT_BLOCK (as bsa_fwd; block_M and block_N
- *              64 or 128); fixed length, D == 128, no softcap.
- *   o, lse     bsa_fwd's output (bf16 or float32) and LSE for the same call.
+ *              64 or 128); fixed length or variable length (cu_seqlens),
+ *              D == 128, no softcap.
+ *   o, lse     bsa_fwd's output (bf16 or float32) and LSE for the same call
+ *              (lse [B, Hq, Sq], or [Hq, total_q] for variable length).
  *   dout       bf16, the layout of q.
  *   dq         device float32 [B, Sq, Hq, D] contiguous; dk, dv float32
- *              [B, Sk, Hkv, D] contiguous; every entry is written.
+ *              [B, Sk, Hkv, D] contiguous (variable length: [total_q, Hq, D]
+ *              and [total_k, Hkv, D]); every entry is written.
  *   workspace  bsa_bwd_workspace_size bytes, 256-byte aligned: row dots,
  *              a bitmap of which query blocks name each key block, the
  *              per-64-key-block lists of (query head, query block) pairs,

@@ -377,24 +377,27 @@ def bsa_fwd_gated(q, k, v, T: torch.Tensor, *, block_M: int = 128, block_N: int 
 
 
 def bsa_bwd(q, k, v, out, lse, dout, pattern=None, *, causal: bool = False, softmax_scale=None,
-            workspace: Optional[torch.Tensor] = None, stream=None):
+            workspace: Optional[torch.Tensor] = None, cu_seqlens_q=None, cu_seqlens_k=None,
+            max_seqlen_q: int = 0, max_seqlen_k: int = 0, stream=None):
     """Gradients of bsa_fwd(q, k, v, pattern, causal=...) given its (out, lse) and the upstream
-    gradient dout.  Returns dq [B, Sq, Hq, D], dk and dv [B, Sk, Hkv, D] (float32)."""
+    gradient dout.  Returns dq shaped like q, dk and dv shaped like k (float32): [B, S, H, D], or
+    packed [total, H, D] with cu_seqlens (lse then [Hq, total_q], as bsa_fwd returns it)."""
     lib = load()
-    prob = _problem(q, k, causal, softmax_scale)
+    varlen = cu_seqlens_q is not None
+    prob = _problem(q, k, causal, softmax_scale, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
     pat = pattern.struct(prob.Hq) if pattern is not None else None
     pat_p = ctypes.byref(pat) if pat is not None else None
     dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
     dv = torch.empty(v.shape, dtype=torch.float32, device=q.device)
     if lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous float32 [B, Hq, Sq]")
+        raise ValueError("lse must be contiguous float32 ([B, Hq, Sq], or [Hq, total_q] with cu_seqlens)")
     need = int(lib.bsa_bwd_workspace_size(ctypes.byref(prob), pat_p))
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    st = lib.bsa_bwd(ctypes.byref(prob), _tensor(q), _tensor(k), _tensor(v), pat_p, _tensor(out), _ptr(lse),
-                     _tensor(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
-                     workspace.numel() * workspace.element_size(), _stream(stream))
+    st = lib.bsa_bwd(ctypes.byref(prob), _tensor(q, varlen), _tensor(k, varlen), _tensor(v, varlen), pat_p,
+                     _tensor(out, varlen), _ptr(lse), _tensor(dout, varlen), _ptr(dq), _ptr(dk), _ptr(dv),
+                     _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     _check("bsa_bwd", st)
     return dq, dk, dv
 

@@ -119,13 +119,15 @@ struct SelArgs {
 struct BwdArgs {
   TensorArg q, k, v, o, dout;  // o may be bf16 or float32 (o_f32)
   int o_f32;
-  const float* lse;            // [B, Hq, Sq] natural log
-  float* dq;                   // [B, Sq, Hq, D] float32, contiguous
-  float* dk;                   // [B, Sk, Hkv, D] float32, contiguous
+  const float* lse;            // [B, Hq, Sq] natural log (variable length: [Hq, total_q])
+  float* dq;                   // [B, Sq, Hq, D] (variable length: [total_q, Hq, D]) float32, contiguous
+  float* dk;                   // [B, Sk, Hkv, D] (variable length: [total_k, Hkv, D]) float32, contiguous
   float* dv;
-  float* dsum;                 // [B, Hq, Sq]: sum_d dO * O
+  float* dsum;                 // sum_d dO * O, laid out as lse
   PatternArg pat;              // kind 0 dense or 1 block lists
-  int B, Hq, Hkv, G, Sq, Sk;
+  const int32_t* cu_q;         // variable length: prefix sums of the query / key lengths, else null
+  const int32_t* cu_k;
+  int B, Hq, Hkv, G, Sq, Sk;   // Sq / Sk: lengths (variable length: maxima)
   int list_by_kv;
   int causal;
   float scale, scale_log2;

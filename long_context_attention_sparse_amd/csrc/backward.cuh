@@ -39,18 +39,50 @@ __device__ __forceinline__ float bf16_hi(uint32_t x) { return bf16_bits_to_f32(x
 // transposed read land in four different groups of four slots), so neither read conflicts.
 __device__ __forceinline__ int bwd_swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 
+// One sequence of the batch: its lengths and its first token (variable length: from the prefix
+// sums; fixed length: b * Sq, b * Sk, the token index in the [B, S, ...] gradients).
+struct BwdSeq {
+  int q_len, k_len, q_tok, k_tok;
+};
+__device__ __forceinline__ BwdSeq bwd_seq(const BwdArgs& a, int b) {
+  BwdSeq s;
+  if (a.cu_q) {
+    s.q_tok = a.cu_q[b];
+    s.q_len = a.cu_q[b + 1] - s.q_tok;
+    s.k_tok = a.cu_k[b];
+    s.k_len = a.cu_k[b + 1] - s.k_tok;
+  } else {
+    s.q_len = a.Sq;
+    s.k_len = a.Sk;
+    s.q_tok = b * a.Sq;
+    s.k_tok = b * a.Sk;
+  }
+  return s;
+}
+// Element offset of token `row` of sequence b in an input view: [B, S, H, D] strides, or the
+// packed [total, H, D] layout (tok0 = the sequence's first token).
+__device__ __forceinline__ int64_t bwd_row(const TensorArg& t, bool packed, int b, int tok0, int row) {
+  return packed ? (int64_t)(tok0 + row) * t.ss : (int64_t)b * t.sb + (int64_t)row * t.ss;
+}
+// Index of (query head h, row) of sequence b in LSE-shaped arrays: [B, Hq, Sq] or [Hq, total_q].
+__device__ __forceinline__ int64_t bwd_lse_idx(const BwdArgs& a, int b, const BwdSeq& s, int h, int row) {
+  return a.cu_q ? (int64_t)h * a.cu_q[a.B] + s.q_tok + row : ((int64_t)b * a.Hq + h) * a.Sq + row;
+}
+
 // D = sum_d dO * O: 16 threads per row, 16 rows per workgroup.
 __global__ __launch_bounds__(256) void bwd_dot_kernel(BwdArgs a) {
-  const int64_t row = (int64_t)wg_x() * 16 + (tid_x() >> 4);
+  const int64_t row = (int64_t)wg_x() * 16 + (tid_x() >> 4);  // (token, head), head fastest
   const int part = tid_x() & 15;
-  const int64_t rows = (int64_t)a.B * a.Sq * a.Hq;
-  if (row >= rows) return;  // whole 16-lane groups
+  const int64_t tokens = a.cu_q ? (int64_t)a.cu_q[a.B] : (int64_t)a.B * a.Sq;
+  if (row >= tokens * a.Hq) return;  // whole 16-lane groups
   const int h = (int)(row % a.Hq);
-  const int s = (int)((row / a.Hq) % a.Sq);
-  const int b = (int)(row / ((int64_t)a.Hq * a.Sq));
-  const uint16_t* dp = reinterpret_cast<const uint16_t*>(a.dout.ptr) + (int64_t)b * a.dout.sb +
-                       (int64_t)s * a.dout.ss + (int64_t)h * a.dout.sh + part * 8;
-  const int64_t oo = (int64_t)b * a.o.sb + (int64_t)s * a.o.ss + (int64_t)h * a.o.sh + part * 8;
+  const int64_t tok = row / a.Hq;
+  const int b = a.cu_q ? 0 : (int)(tok / a.Sq);
+  const int s = a.cu_q ? 0 : (int)(tok % a.Sq);
+  const int64_t dro = a.cu_q ? tok * a.dout.ss : (int64_t)b * a.dout.sb + (int64_t)s * a.dout.ss;
+  const uint16_t* dp = reinterpret_cast<const uint16_t*>(a.dout.ptr) + dro + (int64_t)h * a.dout.sh + part * 8;
+  const int64_t oo = (a.cu_q ? tok * a.o.ss : (int64_t)b * a.o.sb + (int64_t)s * a.o.ss) + (int64_t)h * a.o.sh +
+                     part * 8;
   const u32x4 dv = ldg128(dp);
   float ov[8];
   if (a.o_f32) {
@@ -74,7 +106,7 @@ __global__ __launch_bounds__(256) void bwd_dot_kernel(BwdArgs a) {
   for (int x = 0; x < 4; ++x) acc += bf16_lo(dv[x]) * ov[2 * x] + bf16_hi(dv[x]) * ov[2 * x + 1];
 #pragma unroll
   for (int off = 8; off >= 1; off >>= 1) acc += shfl_xor_f(acc, off);
-  if (part == 0) a.dsum[((int64_t)b * a.Hq + h) * a.Sq + s] = acc;
+  if (part == 0) a.dsum[a.cu_q ? (int64_t)h * tokens + tok : ((int64_t)b * a.Hq + h) * a.Sq + s] = acc;
 }
 
 // ---- key-sub-block lists ----
@@ -102,10 +134,12 @@ __global__ __launch_bounds__(256) void bwd_bits_set_kernel(BwdArgs a) {
   const int i = (int)(bi % a.nqb);
   const int64_t bh = bi / a.nqb;
   const int ht = (int)(bh % Ht), b = (int)(bh / Ht);
+  const BwdSeq sq = bwd_seq(a, b);
+  if ((int64_t)i * a.BM >= sq.q_len) return;  // lists past the sequence are never read
   const int64_t lb = (int64_t)b * a.pat.s_b + (int64_t)ht * a.pat.s_h + (int64_t)i * a.pat.s_q;
   if (c >= min(a.pat.count[lb], cap)) return;
   const int j = a.pat.index[lb * cap + c];
-  if (j < 0 || j >= a.nkb) return;
+  if (j < 0 || j >= a.nkb || (int64_t)j * a.pat.block_N >= sq.k_len) return;
   atomicOr(&a.bits[(((int64_t)b * Ht + ht) * a.nkb + j) * a.W + (i >> 5)], 1u << (i & 31));
 }
 
@@ -161,17 +195,20 @@ __global__ __launch_bounds__(256) void bwd_list_fill_kernel(BwdArgs a) {
   bwd_walk(a, bh / a.Hkv, bh % a.Hkv, sub, [&](int h, int i) { out[k++] = h * a.nqb + i; });
 }
 
-// First 32-row query slab that sees key0 (causal: some row r with r + Sk - Sq >= key0).
-__device__ __forceinline__ int bwd_first_slab(const BwdArgs& a, int key0) {
-  return a.causal ? max(0, (key0 - (a.Sk - a.Sq)) / 32) : 0;
+// First 32-row query slab that sees key0 (causal: some row r with r + delta >= key0, delta =
+// the sequence's key length minus its query length).
+__device__ __forceinline__ int bwd_first_slab(const BwdArgs& a, int key0, int delta) {
+  return a.causal ? max(0, (key0 - delta) / 32) : 0;
 }
 
 // Dense patterns: the units of every list are (query head of the group, slab) pairs.
 __global__ __launch_bounds__(256) void bwd_dense_count_kernel(BwdArgs a) {
   const int x = wg_x() * 256 + tid_x();
   if (x >= a.B * a.Hkv * a.nks) return;
-  const int total_slabs = (a.Sq + 31) / 32;
-  a.counts[x] = a.G * max(0, total_slabs - bwd_first_slab(a, (x % a.nks) * a.SB));
+  const BwdSeq sq = bwd_seq(a, x / (a.Hkv * a.nks));
+  const int key0 = (x % a.nks) * a.SB;
+  const int total_slabs = (sq.q_len + 31) / 32;
+  a.counts[x] = key0 < sq.k_len ? a.G * max(0, total_slabs - bwd_first_slab(a, key0, sq.k_len - sq.q_len)) : 0;
 }
 
 __global__ __launch_bounds__(1024) void bwd_scan_kernel(BwdArgs a) {
@@ -273,7 +310,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
   const int key0 = sub * SB;
   const int slot = a.chunkp[list] + chunk;  // this chunk's partial (bwd_reduce sums them in order)
   const bool split = a.chunkp[list + 1] - a.chunkp[list] > 1;
-  const int delta = a.Sk - a.Sq;
+  const bool packed = a.cu_q != nullptr;
+  const BwdSeq sq = bwd_seq(a, b);
+  const int delta = sq.k_len - sq.q_len;
   const int t = tid_x();
   const int w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63;
   const int kg = w >> 1;         // key group
@@ -283,11 +322,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
 
   // K (P wave) or V (dS wave) rows of the group's keys: the B operand of S^T / dP^T
   const TensorArg& kv = ds_wave ? a.v : a.k;
-  const uint16_t* kvbase = reinterpret_cast<const uint16_t*>(kv.ptr) + (int64_t)b * kv.sb + (int64_t)hkv * kv.sh;
+  const uint16_t* kvbase =
+      reinterpret_cast<const uint16_t*>(kv.ptr) + bwd_row(kv, packed, b, sq.k_tok, 0) + (int64_t)hkv * kv.sh;
   bf16x8 kvreg[D / 16];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks)
-    kvreg[ks] = as_bf16x8(key < a.Sk ? ldg128(kvbase + (int64_t)key * kv.ss + ks * 16 + hh * 8) : u32x4{0, 0, 0, 0});
+    kvreg[ks] =
+        as_bf16x8(key < sq.k_len ? ldg128(kvbase + (int64_t)key * kv.ss + ks * 16 + hh * 8) : u32x4{0, 0, 0, 0});
   int aoff[D / 16];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) aoff[ks] = lq * RS + (((ks * 2 + hh) ^ bwd_swz(lq)) << 3);
@@ -307,9 +348,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
   for (int x = 0; x < D / 32; ++x) acc[x] = f32x16{};
 
   const int slabs = a.BM / 32;
-  const int total_slabs = (a.Sq + 31) / 32;
+  const int total_slabs = (sq.q_len + 31) / 32;
   const bool dense = a.pat.kind == 0;
-  const int first_slab = dense ? bwd_first_slab(a, key0) : 0;
+  const int first_slab = dense ? bwd_first_slab(a, key0, delta) : 0;
   const int list0 = dense ? 0 : a.offsets[list];
   const int n_units = dense ? a.counts[list] : a.counts[list] * slabs;
   const int u0 = chunk * kBwdChunk, u1 = min(n_units, u0 + kBwdChunk);
@@ -324,33 +365,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
         h = e / a.nqb;
         q0 = (e - h * a.nqb) * a.BM + (u % slabs) * 32;
       }
-      if (q0 < a.Sq && !(a.causal && q0 + 31 + delta < key0)) return u;
+      if (q0 < sq.q_len && !(a.causal && q0 + 31 + delta < key0)) return u;
     }
     return u1;
   };
+  // this sequence's first Q / dO row, and its LSE-shaped rows: [B, Hq, Sq] or [Hq, total_q]
+  const uint16_t* qseq = reinterpret_cast<const uint16_t*>(a.q.ptr) + bwd_row(a.q, packed, b, sq.q_tok, 0);
+  const uint16_t* dseq = reinterpret_cast<const uint16_t*>(a.dout.ptr) + bwd_row(a.dout, packed, b, sq.q_tok, 0);
+  const int64_t lse_hs = packed ? (int64_t)a.cu_q[a.B] : a.Sq;
+  const int64_t lse_seq = packed ? (int64_t)sq.q_tok : (int64_t)b * a.Hq * a.Sq;
   // Q and dO rows q0 + 8w + 4x + l/16 of the slab (clamped to the last row: finite data the
-  // mask then ignores), lane l into slot l%16; LSE (wave 0) and D (wave 1) by 8 lanes each
+  // mask then ignores), lane l into slot l%16; LSE (wave 0) and D (wave 1) one row per lane
   const int lrow = l >> 4, lslot = l & 15;
   auto issue = [&](int h, int q0, uint16_t* __restrict__ nq, uint16_t* __restrict__ nd, float* __restrict__ nl,
                    float* __restrict__ nm) __attribute__((always_inline)) {
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
       const int rl = w * 8 + x * 4 + lrow;
-      const int gr = min(q0 + rl, a.Sq - 1);
+      const int gr = min(q0 + rl, sq.q_len - 1);
       const uint32_t piece = (uint32_t)((lslot ^ bwd_swz(rl)) << 4);
-      const char* qp = reinterpret_cast<const char*>(reinterpret_cast<const uint16_t*>(a.q.ptr) + (int64_t)b * a.q.sb +
-                                                     (int64_t)gr * a.q.ss + (int64_t)h * a.q.sh);
-      const char* dp = reinterpret_cast<const char*>(reinterpret_cast<const uint16_t*>(a.dout.ptr) +
-                                                     (int64_t)b * a.dout.sb + (int64_t)gr * a.dout.ss +
-                                                     (int64_t)h * a.dout.sh);
+      const char* qp = reinterpret_cast<const char*>(qseq + (int64_t)gr * a.q.ss + (int64_t)h * a.q.sh);
+      const char* dp = reinterpret_cast<const char*>(dseq + (int64_t)gr * a.dout.ss + (int64_t)h * a.dout.sh);
       __builtin_amdgcn_global_load_lds(qp + piece, BSA_LDS(nq + (w * 8 + x * 4) * RS), 16, 0, 0);
       __builtin_amdgcn_global_load_lds(dp + piece, BSA_LDS(nd + (w * 8 + x * 4) * RS), 16, 0, 0);
     }
-    if (w < 2 && l < 8) {
-      const int r4 = max(0, min(q0 + 4 * l, a.Sq - 4));  // a clamped group of 4 rows
-      const float* src = (w == 0 ? a.lse : a.dsum) + ((int64_t)b * a.Hq + h) * a.Sq + r4;
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(src), BSA_LDS(w == 0 ? nl : nm), 16, 0,
-                                       0);
+    if (w < 2 && l < 32) {  // LSE (wave 0) and D (wave 1) of the 32 rows, one per lane (clamped)
+      const int r = min(q0 + l, sq.q_len - 1);
+      const float* src = (w == 0 ? a.lse : a.dsum) + lse_seq + (int64_t)h * lse_hs + r;
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(src), BSA_LDS(w == 0 ? nl : nm), 4, 0, 0);
     }
   };
 
@@ -388,7 +430,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int row = q0 + g4 * 8 + hh * 4 + e;
-          const bool vis = key < a.Sk && row < a.Sq && lv[e] != kNegInf && (!a.causal || key <= row + delta);
+          const bool vis = key < sq.k_len && row < sq.q_len && lv[e] != kNegInf && (!a.causal || key <= row + delta);
           p[e] = vis ? exp2_fast(fmaf(x[g4 * 4 + e], a.scale_log2, -lv[e] * kLog2e)) : 0.f;
         }
         op[g4 * 2] = pack_bf16x2(p[0], p[1]);
@@ -447,10 +489,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
   if (split) {
     dst = a.part + (((int64_t)slot * 2 + which) * SB + kg * 32 + lq) * D;
   } else {
-    dst = (ds_wave ? a.dk : a.dv) + (((int64_t)b * a.Sk + key) * a.Hkv + hkv) * D;
+    dst = (ds_wave ? a.dk : a.dv) + ((int64_t)(sq.k_tok + key) * a.Hkv + hkv) * D;
     if (ds_wave) mul = a.scale;
   }
-  if (split || key < a.Sk) {
+  if (split || key < sq.k_len) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -472,18 +514,19 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a) {
   const int sub = list % a.nks;
   const int bh = list / a.nks;
   const int hkv = bh % a.Hkv, b = bh / a.Hkv;
+  const BwdSeq sq = bwd_seq(a, b);
   const int SB = a.SB;
   for (int x = tid_x(); x < 2 * SB * (D / 4); x += 256) {
     const int which = x / (SB * D / 4);  // 0 dK, 1 dV
     const int rem = x - which * (SB * D / 4);
     const int kr = rem / (D / 4), d4 = rem - kr * (D / 4);
     const int key = sub * SB + kr;
-    if (key >= a.Sk) continue;
+    if (key >= sq.k_len) continue;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int c = 0; c < n; ++c)
       acc += *reinterpret_cast<const f32x4*>(a.part + (((int64_t)(c0 + c) * 2 + which) * SB + kr) * D + d4 * 4);
     if (which == 0) acc *= a.scale;
-    float* dst = (which == 0 ? a.dk : a.dv) + (((int64_t)b * a.Sk + key) * a.Hkv + hkv) * D + d4 * 4;
+    float* dst = (which == 0 ? a.dk : a.dv) + ((int64_t)(sq.k_tok + key) * a.Hkv + hkv) * D + d4 * 4;
     *reinterpret_cast<f32x4*>(dst) = acc;
   }
 }
@@ -501,16 +544,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4
   const int bh = item / a.nqb;
   const int h = bh % a.Hq, b = bh / a.Hq;
   const int hkv = h / a.G;
-  const int delta = a.Sk - a.Sq;
+  const bool packed = a.cu_q != nullptr;
+  const BwdSeq sq = bwd_seq(a, b);
+  if ((int64_t)i * a.BM >= sq.q_len) return;  // uniform: query blocks past the sequence
+  const int delta = sq.k_len - sq.q_len;
   const int t = tid_x();
   const int w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63;
   const int lq = l & 31, hh = l >> 5;
   const int r0 = i * a.BM;
   const int row = r0 + w * 32 + lq;  // this lane's query
-  const bool row_ok = row < a.Sq;
+  const bool row_ok = row < sq.q_len;
 
-  const int64_t qo = (int64_t)b * a.q.sb + (int64_t)row * a.q.ss + (int64_t)h * a.q.sh;
-  const int64_t doo = (int64_t)b * a.dout.sb + (int64_t)row * a.dout.ss + (int64_t)h * a.dout.sh;
+  const int64_t qo = bwd_row(a.q, packed, b, sq.q_tok, row) + (int64_t)h * a.q.sh;
+  const int64_t doo = bwd_row(a.dout, packed, b, sq.q_tok, row) + (int64_t)h * a.dout.sh;
   bf16x8 qreg[D / 16], doreg[D / 16];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
@@ -519,10 +565,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4
     doreg[ks] = as_bf16x8(row_ok ? ldg128(reinterpret_cast<const uint16_t*>(a.dout.ptr) + doo + ks * 16 + hh * 8)
                                  : u32x4{0, 0, 0, 0});
   }
-  const int64_t rr = ((int64_t)b * a.Hq + h) * a.Sq + row;
+  const int64_t rr = bwd_lse_idx(a, b, sq, h, row);
   const float lse2 = row_ok ? a.lse[rr] * kLog2e : kNegInf;
   const float dsv = row_ok ? a.dsum[rr] : 0.f;
-  const int lim = !row_ok || lse2 == kNegInf ? -1 : (a.causal ? min(row + delta, a.Sk - 1) : a.Sk - 1);
+  const int lim = !row_ok || lse2 == kNegInf ? -1 : (a.causal ? min(row + delta, sq.k_len - 1) : sq.k_len - 1);
   int koff[D / 16];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) koff[ks] = lq * RS + (((ks * 2 + hh) ^ bwd_swz(lq)) << 3);
@@ -544,9 +590,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4
   // the 64-key sub-blocks to visit
   int n_sub, spe = 1;
   const int32_t* list = nullptr;
-  const int last_row = min(r0 + a.BM, a.Sq) - 1;
+  const int last_row = min(r0 + a.BM, sq.q_len) - 1;
   if (a.pat.kind == 0) {
-    const int kend = a.causal ? min(a.Sk, last_row + delta + 1) : a.Sk;
+    const int kend = a.causal ? min(sq.k_len, last_row + delta + 1) : sq.k_len;
     n_sub = kend > 0 ? (kend + 63) / 64 : 0;
   } else {
     const int ht = a.list_by_kv ? hkv : h;
@@ -558,20 +604,22 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4
   auto next_sub = [&](int x, int& key0) __attribute__((always_inline)) -> int {
     for (; x < n_sub; ++x) {
       key0 = (a.pat.kind == 0 ? x : list[x / spe] * spe + x % spe) * 64;
-      if (key0 >= 0 && key0 < a.Sk && !(a.causal && key0 > last_row + delta)) return x;
+      if (key0 >= 0 && key0 < sq.k_len && !(a.causal && key0 > last_row + delta)) return x;
     }
     return n_sub;
   };
   // K and V rows key0 + RPW w + 4x + l/16 (clamped to the last key: finite, masked), lane l
   // into slot l%16
   const int lrow = l >> 4, lslot = l & 15;
-  const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.k.ptr) + (int64_t)b * a.k.sb + (int64_t)hkv * a.k.sh;
-  const uint16_t* vbase = reinterpret_cast<const uint16_t*>(a.v.ptr) + (int64_t)b * a.v.sb + (int64_t)hkv * a.v.sh;
+  const uint16_t* kbase =
+      reinterpret_cast<const uint16_t*>(a.k.ptr) + bwd_row(a.k, packed, b, sq.k_tok, 0) + (int64_t)hkv * a.k.sh;
+  const uint16_t* vbase =
+      reinterpret_cast<const uint16_t*>(a.v.ptr) + bwd_row(a.v, packed, b, sq.k_tok, 0) + (int64_t)hkv * a.v.sh;
   auto issue = [&](int key0, uint16_t* __restrict__ nk, uint16_t* __restrict__ nv) __attribute__((always_inline)) {
 #pragma unroll
     for (int x = 0; x < RPW / 4; ++x) {
       const int rl = w * RPW + x * 4 + lrow;
-      const int gk = min(key0 + rl, a.Sk - 1);
+      const int gk = min(key0 + rl, sq.k_len - 1);
       const uint32_t piece = (uint32_t)((lslot ^ bwd_swz(rl)) << 4);
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(kbase + (int64_t)gk * a.k.ss) + piece,
                                        BSA_LDS(nk + (w * RPW + x * 4) * RS), 16, 0, 0);
@@ -637,7 +685,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4
     buf ^= 1;
   }
   if (row_ok) {
-    float* dqp = a.dq + (((int64_t)b * a.Sq + row) * a.Hq + h) * D;
+    float* dqp = a.dq + ((int64_t)(sq.q_tok + row) * a.Hq + h) * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll

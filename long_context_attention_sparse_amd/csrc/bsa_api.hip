@@ -376,17 +376,19 @@ struct BwdLayout {
 BwdLayout bwd_layout(const bsa_problem& p, const bsa_pattern* pat) {
   BwdLayout L;
   if (p.B <= 0 || p.Hq <= 0 || p.Hkv <= 0 || p.Hq % p.Hkv || p.Sq <= 0 || p.Sk <= 0) return L;
-  if (p.cu_seqlens_q || p.D != 128 || p.softcap > 0.f) return L;
+  if (p.D != 128 || p.softcap > 0.f) return L;
   const bool block = pat && pat->kind == BSA_PAT_BLOCK;
   if (pat && pat->kind != BSA_PAT_DENSE && !block) return L;
+  const int Sq = p.cu_seqlens_q ? p.max_seqlen_q : p.Sq;  // variable length: the longest sequence
+  const int Sk = p.cu_seqlens_q ? p.max_seqlen_k : p.Sk;
   L.BM = block ? pat->block_M : 128;
   L.SB = 64;  // a sub-block never spans two pattern key blocks (block_N is 64 or 128)
-  L.nqb = (p.Sq + L.BM - 1) / L.BM;
-  L.nks = (p.Sk + L.SB - 1) / L.SB;
+  L.nqb = (Sq + L.BM - 1) / L.BM;
+  L.nks = (Sk + L.SB - 1) / L.SB;
   L.n_lists = p.B * p.Hkv * L.nks;
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t at = off; off = align256(off + bytes); return at; };
-  L.dsum = take(sizeof(float) * (size_t)p.B * p.Hq * p.Sq);
+  L.dsum = take(sizeof(float) * (size_t)p.B * p.Hq * Sq);  // at least Hq * total_q
   L.counts = take(sizeof(int32_t) * L.n_lists);
   L.chunkp = take(sizeof(int32_t) * (L.n_lists + 1));
   size_t units;  // upper bound on the 32-row slabs over all lists
@@ -394,17 +396,17 @@ BwdLayout bwd_layout(const bsa_problem& p, const bsa_pattern* pat) {
     const int Ht = pat->Ht;
     const int mult = Ht == p.Hkv ? p.Hq / p.Hkv : 1;
     // each (list head, query block) names a key block at most once in the bitmap
-    const size_t per = (size_t)std::min(pat->cap, (p.Sk + pat->block_N - 1) / pat->block_N);
+    const size_t per = (size_t)std::min(pat->cap, (Sk + pat->block_N - 1) / pat->block_N);
     const size_t pairs = (size_t)p.B * Ht * L.nqb * per * (pat->block_N / L.SB) * mult;
     if (pairs >= (size_t)INT_MAX) return BwdLayout{};
-    L.nkb = (p.Sk + pat->block_N - 1) / pat->block_N;
+    L.nkb = (Sk + pat->block_N - 1) / pat->block_N;
     L.W = (L.nqb + 31) / 32;
     L.offsets = take(sizeof(int32_t) * (L.n_lists + 1));
     L.entries = take(sizeof(int32_t) * std::max<size_t>(pairs, 1));
     L.bits = take(sizeof(uint32_t) * (size_t)p.B * Ht * L.nkb * L.W);
     units = pairs * (L.BM / 32);
   } else {
-    units = (size_t)L.n_lists * (p.Hq / p.Hkv) * ((p.Sq + 31) / 32);
+    units = (size_t)L.n_lists * (p.Hq / p.Hkv) * ((Sq + 31) / 32);
   }
   const size_t chunks = units / kBwdChunk + L.n_lists;  // ceil per list: at most one extra each
   if (chunks >= (size_t)INT_MAX / 2) return BwdLayout{};
@@ -455,12 +457,14 @@ bsa_status bsa_bwd(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, bsa_tens
   a.dv = dv;
   a.dsum = reinterpret_cast<float*>(base + L.dsum);
   a.pat = parg(pat);
+  a.cu_q = p.cu_seqlens_q;
+  a.cu_k = p.cu_seqlens_k;
   a.B = p.B;
   a.Hq = p.Hq;
   a.Hkv = p.Hkv;
   a.G = p.Hq / p.Hkv;
-  a.Sq = p.Sq;
-  a.Sk = p.Sk;
+  a.Sq = p.cu_seqlens_q ? p.max_seqlen_q : p.Sq;
+  a.Sk = p.cu_seqlens_q ? p.max_seqlen_k : p.Sk;
   a.list_by_kv = pat && pat->kind == BSA_PAT_BLOCK && pat->Ht == p.Hkv && p.Hkv != p.Hq;
   a.causal = p.causal;
   a.scale = scale_of(p);

@@ -141,3 +141,50 @@ def test_long_lists_split_and_repeat_bit_for_bit(Ht):
         again = bsa.bsa_bwd(dq_, dk_, dv_, o, lse, dO, pat, causal=True)
         for a_, b_ in zip(first, again):
             assert torch.equal(a_, b_), "backward runs differ"
+
+
+@pytest.mark.parametrize("kind", ["dense", "block"])
+def test_varlen(kind):
+    """Packed variable-length sequences (differing query and key lengths, partial last blocks):
+    each sequence's gradients are those of its own fixed-length problem."""
+    q_lens, k_lens, Hq, Hkv, bM, bN = (300, 129, 512), (420, 129, 512), 4, 2, 128, 64
+    say("backward varlen", kind)
+    cq = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    ck = np.concatenate([[0], np.cumsum(k_lens)]).astype(np.int32)
+    q = normal_bf16(95, "q", (int(cq[-1]), Hq, 128))
+    k = normal_bf16(95, "k", (int(ck[-1]), Hkv, 128))
+    v = normal_bf16(95, "v", (int(ck[-1]), Hkv, 128))
+    do = normal_bf16(95, "do", (int(cq[-1]), Hq, 128))
+    B, nqb = len(q_lens), -(-max(q_lens) // bM)
+    count = index = pat = None
+    if kind == "block":
+        g = rng(95, "varlen-bwd-lists")
+        cap = 5
+        count = np.zeros((B, Hq, nqb), np.int32)
+        index = np.full((B, Hq, nqb, cap), 99, np.int32)  # junk past the counts and the sequences
+        for b in range(B):
+            nkb = -(-k_lens[b] // bN)
+            for h in range(Hq):
+                for i in range(-(-q_lens[b] // bM)):
+                    n = int(g.integers(1, min(cap, nkb) + 1))
+                    count[b, h, i] = n
+                    index[b, h, i, :n] = g.choice(nkb, n, replace=False)
+        pat = bsa.BlockPattern(dev_i32(count), dev_i32(index), bM, bN)
+    varlen = dict(cu_seqlens_q=dev_i32(cq), cu_seqlens_k=dev_i32(ck), max_seqlen_q=max(q_lens),
+                  max_seqlen_k=max(k_lens))
+    dq_, dk_, dv_ = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    for causal in (True, False):
+        o, lse = bsa.bsa_fwd(dq_, dk_, dv_, pat, causal=causal, out_dtype=torch.float32, **varlen)
+        gq, gk, gv = bsa.bsa_bwd(dq_, dk_, dv_, o, lse, dev_bf16(do), pat, causal=causal, **varlen)
+        gq, gk, gv = host(gq), host(gk), host(gv)
+        for b in range(B):
+            qs, ks = slice(int(cq[b]), int(cq[b + 1])), slice(int(ck[b]), int(ck[b + 1]))
+            nq = -(-q_lens[b] // bM)
+            rq, rk, rv = oracle.block_sparse_bwd(
+                q[qs][None], k[ks][None], v[ks][None], do[qs][None],
+                None if count is None else count[b:b + 1, :, :nq], None if index is None else index[b:b + 1, :, :nq],
+                bM, bN, causal)
+            for name, got, ref in (("dq", gq[qs], rq[0]), ("dk", gk[ks], rk[0]), ("dv", gv[ks], rv[0])):
+                scale = max(1.0, float(np.abs(ref).max()))
+                err = float(np.abs(got - ref).max())
+                assert np.isfinite(err) and err <= 1e-2 * scale, f"varlen {kind} causal={causal} seq {b} {name}: {err}"
