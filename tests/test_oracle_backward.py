@@ -101,3 +101,52 @@ def test_empty_rows_and_dense():
     do2[0, 2 * bs:3 * bs, 1] = 0
     for a, b in zip((dk, dv), oracle.block_sparse_bwd(q, k, v, do2, count, index, bs, bs, True)[1:]):
         np.testing.assert_allclose(a, b, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_softcap_matches_torch_autograd(causal):
+    """Softcapped scores c tanh(x / c) before the mask and softmax, differentiated by torch."""
+    B, S, Hq, Hkv, D, bs, cap = 1, 64, 4, 2, 16, 16, 2.5
+    q, k, v, do = _inputs(84, B, S, S, Hq, Hkv, D)
+    count, index = _lists(84, B, Hq, S // bs, S // bs, causal)
+    dq, dk, dv = oracle.block_sparse_bwd(q, k, v, do, count, index, bs, bs, causal, softcap=cap)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    scale = 1.0 / np.sqrt(D)
+    G = Hq // Hkv
+    loss = 0.0
+    for h in range(Hq):
+        mask = oracle.block_mask(count[0, h], index[0, h], bs, bs, S, S)
+        if causal:
+            mask &= np.tril(np.ones((S, S), bool))
+        x = scale * tq[0, :, h] @ tk[0, :, h // G].T
+        x = cap * torch.tanh(x / cap)
+        x = x.masked_fill(~torch.from_numpy(mask), float("-inf"))
+        o = torch.softmax(x, dim=1) @ tv[0, :, h // G]
+        loss = loss + (o * torch.from_numpy(do[0, :, h])).sum()
+    loss.backward()
+    np.testing.assert_allclose(dq, tq.grad.numpy(), atol=1e-11)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), atol=1e-11)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), atol=1e-11)
+
+
+def test_softcap_finite_differences():
+    B, S, Hq, Hkv, D, bs, cap = 1, 32, 2, 1, 8, 8, 1.5
+    q, k, v, do = _inputs(85, B, S, S, Hq, Hkv, D)
+    count, index = _lists(85, B, Hq, S // bs, S // bs, True)
+    dq, dk, dv = oracle.block_sparse_bwd(q, k, v, do, count, index, bs, bs, True, softcap=cap)
+
+    def loss(qq, kk, vv):
+        o, _ = oracle.block_sparse(qq, kk, vv, count, index, bs, bs, causal=True, softcap=cap)
+        return float((o * do).sum())
+
+    g = rng(85, "fd")
+    eps = 1e-5
+    for name, x, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for _ in range(6):
+            idx = tuple(int(g.integers(0, n)) for n in x.shape)
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            lp = loss(*(xp if a is x else a for a in (q, k, v)))
+            lm = loss(*(xm if a is x else a for a in (q, k, v)))
+            assert abs((lp - lm) / (2 * eps) - grad[idx]) < 1e-7, (name, idx)
