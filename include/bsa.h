@@ -285,7 +285,8 @@ bsa_status bsa_fwd_gated(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, bs
  * (summed over the query heads of a kv head).
  *   pat        NULL / dense or BSA_PAT_BLOCK (as bsa_fwd; block_M and block_N
  *              64 or 128); fixed length or variable length (cu_seqlens),
- *              D == 128, no softcap.
+ *              D == 128; with softcap > 0 the gradient goes through the capped
+ *              scores (dS times 1 - tanh^2 of the cap's argument).
  *   o, lse     bsa_fwd's output (bf16 or float32) and LSE for the same call
  *              (lse [B, Hq, Sq], or [Hq, total_q] for variable length).
  *   dout       bf16, the layout of q.

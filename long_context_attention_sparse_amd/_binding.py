@@ -378,13 +378,14 @@ def bsa_fwd_gated(q, k, v, T: torch.Tensor, *, block_M: int = 128, block_N: int 
 
 def bsa_bwd(q, k, v, out, lse, dout, pattern=None, *, causal: bool = False, softmax_scale=None,
             workspace: Optional[torch.Tensor] = None, cu_seqlens_q=None, cu_seqlens_k=None,
-            max_seqlen_q: int = 0, max_seqlen_k: int = 0, stream=None):
+            max_seqlen_q: int = 0, max_seqlen_k: int = 0, softcap: float = 0.0, stream=None):
     """Gradients of bsa_fwd(q, k, v, pattern, causal=...) given its (out, lse) and the upstream
-    gradient dout.  Returns dq shaped like q, dk and dv shaped like k (float32): [B, S, H, D], or
-    packed [total, H, D] with cu_seqlens (lse then [Hq, total_q], as bsa_fwd returns it)."""
+    gradient dout (and the same softcap).  Returns dq shaped like q, dk and dv shaped like k
+    (float32): [B, S, H, D], or packed [total, H, D] with cu_seqlens (lse then [Hq, total_q], as
+    bsa_fwd returns it)."""
     lib = load()
     varlen = cu_seqlens_q is not None
-    prob = _problem(q, k, causal, softmax_scale, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
+    prob = _problem(q, k, causal, softmax_scale, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, softcap)
     pat = pattern.struct(prob.Hq) if pattern is not None else None
     pat_p = ctypes.byref(pat) if pat is not None else None
     dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)

@@ -131,6 +131,7 @@ struct BwdArgs {
   int list_by_kv;
   int causal;
   float scale, scale_log2;
+  float cap_in, cap_out;       // softcap constants (softcap_score); cap_in == 0: no softcap
   int BM;                      // query block rows of the pattern (64 or 128; dense: 128)
   int SB;                      // keys per sub-block (list): 32 per dK/dV wave, at most the pattern's block_N
   int nqb, nks;                // query blocks; sub-blocks

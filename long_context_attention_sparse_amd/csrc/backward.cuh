@@ -267,6 +267,7 @@ __global__ __launch_bounds__(1024) void bwd_scan_kernel(BwdArgs a) {
 // P = exp(S - LSE), hands P to its partner through LDS and accumulates dV^T += dO^T P; wave
 // 2g + 1 (the "dS wave") keeps V, builds dP^T = V dO^T, takes P, forms dS = P * (dP - D) and
 // accumulates dK^T += Q^T dS.
+template <bool CAP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int D = TD;
   constexpr int SB = 64;
@@ -421,23 +422,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
     for (int ks = 0; ks < D / 16; ++ks)
       x = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(rows + aoff[ks])), kvreg[ks], x);
     // lane: key; register r: slab row 8(r/4) + 4hh + r%4
-    uint32_t op[8];
+    uint32_t op[8], xf[CAP ? 4 : 1];
     if (!ds_wave) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const f32x4 lv = *reinterpret_cast<const f32x4*>(lb + g4 * 8 + hh * 4);
         float p[4];
+        float pf[4];  // what the dS wave multiplies by (dP - D): P, times the cap's derivative
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int row = q0 + g4 * 8 + hh * 4 + e;
           const bool vis = key < sq.k_len && row < sq.q_len && lv[e] != kNegInf && (!a.causal || key <= row + delta);
-          p[e] = vis ? exp2_fast(fmaf(x[g4 * 4 + e], a.scale_log2, -lv[e] * kLog2e)) : 0.f;
+          float xs = x[g4 * 4 + e];
+          if constexpr (CAP) xs = softcap_score(xs, a.cap_in, a.cap_out);
+          p[e] = vis ? exp2_fast(fmaf(xs, a.scale_log2, -lv[e] * kLog2e)) : 0.f;
+          if constexpr (CAP) {
+            const float tc = xs / a.cap_out;  // tanh of the capped argument
+            pf[e] = p[e] * (1.f - tc * tc);
+          } else {
+            pf[e] = p[e];
+          }
         }
         op[g4 * 2] = pack_bf16x2(p[0], p[1]);
         op[g4 * 2 + 1] = pack_bf16x2(p[2], p[3]);
+        if constexpr (CAP) {
+          xf[(g4 & 1) * 2] = pack_bf16x2(pf[0], pf[1]);
+          xf[(g4 & 1) * 2 + 1] = pack_bf16x2(pf[2], pf[3]);
+          // stored a half at a time, so that only four of these registers are live
+          if (g4 & 1) *reinterpret_cast<u32x4*>(pslot + (g4 >> 1) * 256) = u32x4{xf[0], xf[1], xf[2], xf[3]};
+        }
       }
-      *reinterpret_cast<u32x4*>(pslot) = u32x4{op[0], op[1], op[2], op[3]};
-      *reinterpret_cast<u32x4*>(pslot + 256) = u32x4{op[4], op[5], op[6], op[7]};
+      if constexpr (!CAP) {
+        *reinterpret_cast<u32x4*>(pslot) = u32x4{op[0], op[1], op[2], op[3]};
+        *reinterpret_cast<u32x4*>(pslot + 256) = u32x4{op[4], op[5], op[6], op[7]};
+      }
     }
     // P is in LDS for the dS waves.  The barrier waits for LDS operations only (a release
     // fence would also wait for the next slab's loads, which write LDS); the empty asm
@@ -531,7 +549,7 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a) {
   }
 }
 
-template <int NW>
+template <int NW, bool CAP>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4 ? 2 : 1))) void bwd_dq_kernel(BwdArgs a) {
   constexpr int D = TD;
   constexpr int RS = D;  // 256-byte rows, 16-byte pieces swizzled by row (bwd_swz)
@@ -661,7 +679,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const int kk = key0 + kb * 32 + ((r + e) >> 2) * 8 + hh * 4 + ((r + e) & 3);
-          const float p = kk <= lim ? exp2_fast(fmaf(st[r + e], a.scale_log2, -lse2)) : 0.f;
+          float xs = st[r + e];
+          if constexpr (CAP) xs = softcap_score(xs, a.cap_in, a.cap_out);
+          float p = kk <= lim ? exp2_fast(fmaf(xs, a.scale_log2, -lse2)) : 0.f;
+          if constexpr (CAP) {
+            const float tc = xs / a.cap_out;  // the cap's derivative: 1 - tanh^2
+            p *= 1.f - tc * tc;
+          }
           d2[e] = p * (dpt[r + e] - dsv);
         }
         dd[r / 2] = pack_bf16x2(d2[0], d2[1]);

@@ -376,7 +376,7 @@ struct BwdLayout {
 BwdLayout bwd_layout(const bsa_problem& p, const bsa_pattern* pat) {
   BwdLayout L;
   if (p.B <= 0 || p.Hq <= 0 || p.Hkv <= 0 || p.Hq % p.Hkv || p.Sq <= 0 || p.Sk <= 0) return L;
-  if (p.D != 128 || p.softcap > 0.f) return L;
+  if (p.D != 128) return L;
   const bool block = pat && pat->kind == BSA_PAT_BLOCK;
   if (pat && pat->kind != BSA_PAT_DENSE && !block) return L;
   const int Sq = p.cu_seqlens_q ? p.max_seqlen_q : p.Sq;  // variable length: the longest sequence
@@ -469,6 +469,7 @@ bsa_status bsa_bwd(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, bsa_tens
   a.causal = p.causal;
   a.scale = scale_of(p);
   a.scale_log2 = a.scale * kLog2e;
+  cap_consts(p, a.cap_in, a.cap_out);
   a.BM = L.BM;
   a.SB = L.SB;
   a.nqb = L.nqb;

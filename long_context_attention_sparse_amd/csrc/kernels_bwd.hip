@@ -23,11 +23,18 @@ void launch_bwd(const BwdArgs& a, int chunk_bound, hipStream_t st) {
     hipLaunchKernelGGL(bwd_dense_count_kernel, dim3((n_lists + 255) / 256), dim3(256), 0, st, a);
     hipLaunchKernelGGL(bwd_scan_kernel, dim3(1), dim3(1024), 0, st, a);
   }
-  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(chunk_bound), dim3(256), 0, st, a);
+  const bool cap = a.cap_in != 0.f;
+  if (cap) hipLaunchKernelGGL(bwd_dkdv_kernel<true>, dim3(chunk_bound), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(bwd_dkdv_kernel<false>, dim3(chunk_bound), dim3(256), 0, st, a);
   hipLaunchKernelGGL(bwd_reduce_kernel, dim3(n_lists), dim3(256), 0, st, a);
   const unsigned dq_grid = (unsigned)((int64_t)a.B * a.Hq * a.nqb);
-  if (a.BM == 128) hipLaunchKernelGGL(bwd_dq_kernel<4>, dim3(dq_grid), dim3(256), 0, st, a);
-  else hipLaunchKernelGGL(bwd_dq_kernel<2>, dim3(dq_grid), dim3(128), 0, st, a);
+  if (a.BM == 128) {
+    if (cap) hipLaunchKernelGGL((bwd_dq_kernel<4, true>), dim3(dq_grid), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((bwd_dq_kernel<4, false>), dim3(dq_grid), dim3(256), 0, st, a);
+  } else {
+    if (cap) hipLaunchKernelGGL((bwd_dq_kernel<2, true>), dim3(dq_grid), dim3(128), 0, st, a);
+    else hipLaunchKernelGGL((bwd_dq_kernel<2, false>), dim3(dq_grid), dim3(128), 0, st, a);
+  }
 }
 
 }  // namespace bsa

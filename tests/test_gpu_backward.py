@@ -30,11 +30,11 @@ def _data(seed, B, Sq, Sk, Hq, Hkv):
             normal_bf16(seed, "v", (B, Sk, Hkv, 128)), normal_bf16(seed, "do", (B, Sq, Hq, 128)))
 
 
-def _grads(q, k, v, do, pattern=None, causal=True, count=None, index=None, bM=128, bN=128):
+def _grads(q, k, v, do, pattern=None, causal=True, count=None, index=None, bM=128, bN=128, softcap=0.0):
     dq_, dk_, dv_ = dev_bf16(q), dev_bf16(k), dev_bf16(v)
-    o, lse = bsa.bsa_fwd(dq_, dk_, dv_, pattern, causal=causal, out_dtype=torch.float32)
-    g = bsa.bsa_bwd(dq_, dk_, dv_, o, lse, dev_bf16(do), pattern, causal=causal)
-    ref = oracle.block_sparse_bwd(q, k, v, do, count, index, bM, bN, causal)
+    o, lse = bsa.bsa_fwd(dq_, dk_, dv_, pattern, causal=causal, out_dtype=torch.float32, softcap=softcap)
+    g = bsa.bsa_bwd(dq_, dk_, dv_, o, lse, dev_bf16(do), pattern, causal=causal, softcap=softcap)
+    ref = oracle.block_sparse_bwd(q, k, v, do, count, index, bM, bN, causal, softcap=softcap)
     return g, ref
 
 
@@ -91,6 +91,26 @@ def test_block_lists(bM, bN, Ht):
     _check("dq", dq, rq)
     _check("dk", dk, rk)
     _check("dv", dv, rv)
+
+
+@pytest.mark.parametrize("kind,causal", [("dense", True), ("dense", False), ("block", True)])
+def test_softcap(kind, causal):
+    """Soft-capped scores (cap 1.5, so that the scaled scores, of size about 1, are far into the
+    nonlinear part of c tanh(x / c)): the gradient carries the factor 1 - tanh^2."""
+    B, Sq, Sk, Hq, Hkv, cap = 2, 384, 456 if not causal else 384, 4, 2, 1.5
+    say("backward softcap", kind, causal)
+    q, k, v, do = _data(96, B, Sq, Sk, Hq, Hkv)
+    count = index = pat = None
+    if kind == "block":
+        count, index = _lists(96, B, Hq, Sq // 128, Sk // 128, 3)
+        pat = bsa.BlockPattern(dev_i32(count), dev_i32(index), 128, 128)
+    (dq, dk, dv), (rq, rk, rv) = _grads(q, k, v, do, pat, causal, count, index, softcap=cap)
+    _check("dq", dq, rq)
+    _check("dk", dk, rk)
+    _check("dv", dv, rv)
+    # the cap matters: the uncapped gradient is far from the capped one
+    r0 = oracle.block_sparse_bwd(q, k, v, do, count, index, 128, 128, causal)[0]
+    assert np.abs(r0 - rq).max() > 0.1 * max(1.0, np.abs(rq).max())
 
 
 def test_empty_lists_give_zero_rows():
