@@ -522,11 +522,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
   }
 }
 
+constexpr int kBwdReduceKeys = 16;  // keys per reduction workgroup
+
 // Lists not written by a single dK/dV workgroup: none (zeros) or several chunks (their
-// partials summed in chunk order).  One workgroup per list.
+// partials summed in chunk order).  One workgroup per kBwdReduceKeys keys of a list (the first
+// block's list has tens of chunks: a workgroup per list would leave its reduction alone at the
+// end); each thread sums four independent outputs, so four partial reads are in flight.
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a) {
   constexpr int D = TD;
-  const int list = wg_x();
+  constexpr int KR = kBwdReduceKeys;
+  static_assert(2 * KR * (D / 4) == 4 * 256, "four outputs per thread");
+  const int groups = a.SB / KR;
+  const int list = wg_x() / groups;
+  const int kg0 = (wg_x() - list * groups) * KR;  // first key of this group within the sub-block
   const int c0 = a.chunkp[list], n = a.chunkp[list + 1] - c0;
   if (n == 1) return;  // written by its workgroup
   const int sub = list % a.nks;
@@ -534,19 +542,31 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a) {
   const int hkv = bh % a.Hkv, b = bh / a.Hkv;
   const BwdSeq sq = bwd_seq(a, b);
   const int SB = a.SB;
-  for (int x = tid_x(); x < 2 * SB * (D / 4); x += 256) {
-    const int which = x / (SB * D / 4);  // 0 dK, 1 dV
-    const int rem = x - which * (SB * D / 4);
-    const int kr = rem / (D / 4), d4 = rem - kr * (D / 4);
+  const int64_t cstride = (int64_t)2 * SB * D;  // floats per chunk partial
+  const float* src[4];
+  float* dst[4];
+  bool ok[4];
+  float mul[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int x = tid_x() + j * 256;
+    const int which = x / (KR * D / 4);  // 0 dK, 1 dV
+    const int rem = x - which * (KR * D / 4);
+    const int kr = kg0 + rem / (D / 4), d4 = rem % (D / 4);
     const int key = sub * SB + kr;
-    if (key >= sq.k_len) continue;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int c = 0; c < n; ++c)
-      acc += *reinterpret_cast<const f32x4*>(a.part + (((int64_t)(c0 + c) * 2 + which) * SB + kr) * D + d4 * 4);
-    if (which == 0) acc *= a.scale;
-    float* dst = (which == 0 ? a.dk : a.dv) + ((int64_t)(sq.k_tok + key) * a.Hkv + hkv) * D + d4 * 4;
-    *reinterpret_cast<f32x4*>(dst) = acc;
+    ok[j] = key < sq.k_len;
+    mul[j] = which == 0 ? a.scale : 1.f;
+    src[j] = a.part + (((int64_t)c0 * 2 + which) * SB + kr) * D + d4 * 4;
+    dst[j] = (which == 0 ? a.dk : a.dv) + ((int64_t)(sq.k_tok + (ok[j] ? key : 0)) * a.Hkv + hkv) * D + d4 * 4;
   }
+  f32x4 acc[4] = {};
+  for (int c = 0; c < n; ++c) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] += *reinterpret_cast<const f32x4*>(src[j] + c * cstride);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (ok[j]) *reinterpret_cast<f32x4*>(dst[j]) = acc[j] * mul[j];
 }
 
 template <int NW, bool CAP>

@@ -26,7 +26,7 @@ void launch_bwd(const BwdArgs& a, int chunk_bound, hipStream_t st) {
   const bool cap = a.cap_in != 0.f;
   if (cap) hipLaunchKernelGGL(bwd_dkdv_kernel<true>, dim3(chunk_bound), dim3(256), 0, st, a);
   else hipLaunchKernelGGL(bwd_dkdv_kernel<false>, dim3(chunk_bound), dim3(256), 0, st, a);
-  hipLaunchKernelGGL(bwd_reduce_kernel, dim3(n_lists), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3(n_lists * (a.SB / kBwdReduceKeys)), dim3(256), 0, st, a);
   const unsigned dq_grid = (unsigned)((int64_t)a.B * a.Hq * a.nqb);
   if (a.BM == 128) {
     if (cap) hipLaunchKernelGGL((bwd_dq_kernel<4, true>), dim3(dq_grid), dim3(256), 0, st, a);
