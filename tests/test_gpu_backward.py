@@ -14,6 +14,7 @@ import torch
 import long_context_attention_sparse_amd as bsa
 import oracle
 from synth import normal_bf16, rng
+from synth.workloads import block_sparse_prefill
 from tests.gpu_util import dev_bf16, dev_i32, host, say
 
 pytestmark = [pytest.mark.gpu, pytest.mark.filterwarnings("ignore::RuntimeWarning")]
@@ -163,12 +164,13 @@ def test_long_lists_split_and_repeat_bit_for_bit(Ht):
             assert torch.equal(a_, b_), "backward runs differ"
 
 
-@pytest.mark.parametrize("kind", ["dense", "block"])
-def test_varlen(kind):
-    """Packed variable-length sequences (differing query and key lengths, partial last blocks):
-    each sequence's gradients are those of its own fixed-length problem."""
+@pytest.mark.parametrize("kind,softcap", [("dense", 0.0), ("block", 0.0), ("block", 2.0)])
+def test_varlen(kind, softcap):
+    """Packed variable-length sequences (differing query and key lengths, partial last blocks),
+    with and without softcap: each sequence's gradients are those of its own fixed-length
+    problem."""
     q_lens, k_lens, Hq, Hkv, bM, bN = (300, 129, 512), (420, 129, 512), 4, 2, 128, 64
-    say("backward varlen", kind)
+    say("backward varlen", kind, softcap)
     cq = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
     ck = np.concatenate([[0], np.cumsum(k_lens)]).astype(np.int32)
     q = normal_bf16(95, "q", (int(cq[-1]), Hq, 128))
@@ -194,8 +196,8 @@ def test_varlen(kind):
                   max_seqlen_k=max(k_lens))
     dq_, dk_, dv_ = dev_bf16(q), dev_bf16(k), dev_bf16(v)
     for causal in (True, False):
-        o, lse = bsa.bsa_fwd(dq_, dk_, dv_, pat, causal=causal, out_dtype=torch.float32, **varlen)
-        gq, gk, gv = bsa.bsa_bwd(dq_, dk_, dv_, o, lse, dev_bf16(do), pat, causal=causal, **varlen)
+        o, lse = bsa.bsa_fwd(dq_, dk_, dv_, pat, causal=causal, out_dtype=torch.float32, softcap=softcap, **varlen)
+        gq, gk, gv = bsa.bsa_bwd(dq_, dk_, dv_, o, lse, dev_bf16(do), pat, causal=causal, softcap=softcap, **varlen)
         gq, gk, gv = host(gq), host(gk), host(gv)
         for b in range(B):
             qs, ks = slice(int(cq[b]), int(cq[b + 1])), slice(int(ck[b]), int(ck[b + 1]))
@@ -203,8 +205,67 @@ def test_varlen(kind):
             rq, rk, rv = oracle.block_sparse_bwd(
                 q[qs][None], k[ks][None], v[ks][None], do[qs][None],
                 None if count is None else count[b:b + 1, :, :nq], None if index is None else index[b:b + 1, :, :nq],
-                bM, bN, causal)
+                bM, bN, causal, softcap=softcap)
             for name, got, ref in (("dq", gq[qs], rq[0]), ("dk", gk[ks], rk[0]), ("dv", gv[ks], rv[0])):
                 scale = max(1.0, float(np.abs(ref).max()))
                 err = float(np.abs(got - ref).max())
-                assert np.isfinite(err) and err <= 1e-2 * scale, f"varlen {kind} causal={causal} seq {b} {name}: {err}"
+                assert np.isfinite(err) and err <= 1e-2 * scale, f"varlen {kind} cap={softcap} causal={causal} seq {b} {name}: {err}"
+
+
+@pytest.fixture(scope="module")
+def bwd_full():
+    say("generating block-sparse causal prefill workload and upstream gradient (S=32768, Hq=32, Hkv=8)")
+    w = block_sparse_prefill()
+    w["do"] = normal_bf16(1007, "do", w["q"].shape)
+    return w
+
+
+def _packed(w, h, i):
+    """Query block i of query head h against the key blocks its list names, packed in ascending
+    order: every listed block but the diagonal one lies wholly before the block's rows, and the
+    diagonal block comes last, so bottom-right causal masking of the packed keys is the original
+    mask.  Returns the sorted block ids and the oracle's (dq, dk, dv) of that small problem."""
+    hk = h // (w["Hq"] // w["Hkv"])
+    ents = np.sort(w["index"][0, h, i, :w["count"][0, h, i]])
+    rows = slice(i * 128, (i + 1) * 128)
+    keys = np.concatenate([np.arange(j * 128, (j + 1) * 128) for j in ents])
+    return ents, oracle.block_sparse_bwd(w["q"][:, rows, h:h + 1], w["k"][:, keys, hk:hk + 1],
+                                         w["v"][:, keys, hk:hk + 1], w["do"][:, rows, h:h + 1], causal=True)
+
+
+def test_full_size_sampled(bwd_full):
+    """The block-sparse causal prefill at full size (S=32768, Hq=32, Hkv=8, 128x128 tiles, bf16 O
+    from the forward), launched as the benchmark launches it.  Sampled: dQ of three query blocks;
+    dK and dV of the last key block (seen by the diagonal tiles only) and of key block 1, which
+    several hundred (head, query block) lists name, so its sums are split over many chunks and
+    go through the reduction.  Each expected block sums the oracle's gradients of the small
+    packed problems of every (head, query block) that names it."""
+    w = bwd_full
+    say("backward full size")
+    q, k, v, do = (dev_bf16(w[n]) for n in ("q", "k", "v", "do"))
+    pat = bsa.BlockPattern(dev_i32(w["count"]), dev_i32(w["index"]), 128, 128)
+    o, lse = bsa.bsa_fwd(q, k, v, pat, causal=True, out_dtype=torch.bfloat16)
+    ws = torch.empty(bsa.bsa_bwd_workspace_size(q, k, pat, causal=True), dtype=torch.uint8, device=q.device)
+    gq, gk, gv = bsa.bsa_bwd(q, k, v, o, lse, do, pat, causal=True, workspace=ws)
+    torch.cuda.synchronize()
+    for h, i in [(0, 255), (31, 0), (12, 200)]:
+        _, (rq, _, _) = _packed(w, h, i)
+        _check(f"full dq h={h} i={i}", gq[0, i * 128:(i + 1) * 128, h], rq[0, :, 0])
+    G = w["Hq"] // w["Hkv"]
+    nqb = w["count"].shape[2]
+    for hk, j in [(3, nqb - 1), (5, 1)]:
+        rk = np.zeros((128, 128))
+        rv = np.zeros((128, 128))
+        named = 0
+        for h in range(hk * G, (hk + 1) * G):
+            for i in range(j, nqb):
+                if j not in w["index"][0, h, i, :w["count"][0, h, i]]:
+                    continue
+                ents, (_, sk, sv) = _packed(w, h, i)
+                p = int(np.searchsorted(ents, j)) * 128
+                rk += sk[0, p:p + 128, 0]
+                rv += sv[0, p:p + 128, 0]
+                named += 1
+        say(f"key block {j} of kv head {hk}: named by {named} lists")
+        _check(f"full dk hk={hk} j={j}", gk[0, j * 128:(j + 1) * 128, hk], rk)
+        _check(f"full dv hk={hk} j={j}", gv[0, j * 128:(j + 1) * 128, hk], rv)
