@@ -577,11 +577,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4
   __shared__ __attribute__((aligned(16))) uint16_t K0[64 * RS], K1[64 * RS];
   __shared__ __attribute__((aligned(16))) uint16_t V0[64 * RS], V1[64 * RS];
 
-  const int item = wg_x();
-  const int i = item % a.nqb;
-  const int bh = item / a.nqb;
-  const int h = bh % a.Hq, b = bh / a.Hq;
-  const int hkv = h / a.G;
+  // (b, kv head, query block, group member), query blocks heaviest (last) first, contiguous
+  // ranges per XCD: the G query heads of a kv head take the same query block side by side, so
+  // the key blocks they share meet in one L2
+  const int item = xcd_item(wg_x(), a.B * a.Hq * a.nqb);
+  const int g = item % a.G;
+  int rest = item / a.G;
+  const int i = a.nqb - 1 - rest % a.nqb;
+  rest /= a.nqb;
+  const int hkv = rest % a.Hkv, b = rest / a.Hkv;
+  const int h = hkv * a.G + g;
   const bool packed = a.cu_q != nullptr;
   const BwdSeq sq = bwd_seq(a, b);
   if ((int64_t)i * a.BM >= sq.q_len) return;  // uniform: query blocks past the sequence
