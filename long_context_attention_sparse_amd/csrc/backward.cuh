@@ -143,30 +143,6 @@ __global__ __launch_bounds__(256) void bwd_bits_set_kernel(BwdArgs a) {
   atomicOr(&a.bits[(((int64_t)b * Ht + ht) * a.nkb + j) * a.W + (i >> 5)], 1u << (i & 31));
 }
 
-// Visits the pairs of list (b, hkv, sub) in list order: f(query head, query block).
-template <class F>
-__device__ __forceinline__ void bwd_walk(const BwdArgs& a, int b, int hkv, int sub, F&& f) {
-  const int Ht = a.list_by_kv ? a.Hkv : a.Hq;
-  const int j = sub * a.SB / a.pat.block_N;
-  const int heads = a.list_by_kv ? 1 : a.G;
-  for (int g = 0; g < heads; ++g) {
-    const int ht = a.list_by_kv ? hkv : hkv * a.G + g;
-    const uint32_t* col = a.bits + (((int64_t)b * Ht + ht) * a.nkb + j) * a.W;
-    for (int wd = 0; wd < a.W; ++wd) {
-      uint32_t m = col[wd];
-      while (m) {
-        const int i = wd * 32 + __builtin_ctz(m);
-        m &= m - 1;
-        if (a.list_by_kv) {
-          for (int gg = 0; gg < a.G; ++gg) f(hkv * a.G + gg, i);
-        } else {
-          f(ht, i);
-        }
-      }
-    }
-  }
-}
-
 // One thread per list: its pair count.
 __global__ __launch_bounds__(256) void bwd_list_count_kernel(BwdArgs a) {
   const int x = wg_x() * 256 + tid_x();
@@ -185,14 +161,48 @@ __global__ __launch_bounds__(256) void bwd_list_count_kernel(BwdArgs a) {
   a.counts[x] = a.list_by_kv ? n * a.G : n;
 }
 
-// One thread per list: its pairs, h * nqb + i, from offsets[list] on.
+// One wave per list: its pairs, h * nqb + i, from offsets[list] on, ordered by query head of
+// the group, then query block (lists per kv head: each query block's G heads in turn).  Lane w
+// takes bitmap word w (64 words at a time); a prefix sum over the wave of the words' entry
+// counts gives each lane where its entries go.
 __global__ __launch_bounds__(256) void bwd_list_fill_kernel(BwdArgs a) {
-  const int x = wg_x() * 256 + tid_x();
-  if (x >= a.B * a.Hkv * a.nks) return;
+  const int x = wg_x() * 4 + (tid_x() >> 6);
+  const int l = tid_x() & 63;
+  if (x >= a.B * a.Hkv * a.nks) return;  // wave-uniform
   const int sub = x % a.nks, bh = x / a.nks;
+  const int hkv = bh % a.Hkv, b = bh / a.Hkv;
+  const int Ht = a.list_by_kv ? a.Hkv : a.Hq;
+  const int j = sub * a.SB / a.pat.block_N;
+  const int heads = a.list_by_kv ? 1 : a.G;
+  const int per = a.list_by_kv ? a.G : 1;  // entries per set bit
   int32_t* out = a.entries + a.offsets[x];
-  int k = 0;
-  bwd_walk(a, bh / a.Hkv, bh % a.Hkv, sub, [&](int h, int i) { out[k++] = h * a.nqb + i; });
+  int base = 0;
+  for (int g = 0; g < heads; ++g) {
+    const int ht = a.list_by_kv ? hkv : hkv * a.G + g;
+    const uint32_t* col = a.bits + (((int64_t)b * Ht + ht) * a.nkb + j) * a.W;
+    for (int w0 = 0; w0 < a.W; w0 += 64) {
+      const int wd = w0 + l;
+      uint32_t m = wd < a.W ? col[wd] : 0u;
+      const int c = __builtin_popcount(m) * per;
+      int incl = c;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(incl, d, 64);
+        if (l >= d) incl += y;
+      }
+      int k = base + incl - c;
+      while (m) {
+        const int i = wd * 32 + __builtin_ctz(m);
+        m &= m - 1;
+        if (a.list_by_kv) {
+          for (int gg = 0; gg < a.G; ++gg) out[k++] = (hkv * a.G + gg) * a.nqb + i;
+        } else {
+          out[k++] = ht * a.nqb + i;
+        }
+      }
+      base += __shfl(incl, 63, 64);
+    }
+  }
 }
 
 // First 32-row query slab that sees key0 (causal: some row r with r + delta >= key0, delta =

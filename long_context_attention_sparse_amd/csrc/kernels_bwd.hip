@@ -18,7 +18,7 @@ void launch_bwd(const BwdArgs& a, int chunk_bound, hipStream_t st) {
       hipLaunchKernelGGL(bwd_bits_set_kernel, dim3((unsigned)((slots + 255) / 256)), dim3(256), 0, st, a);
     hipLaunchKernelGGL(bwd_list_count_kernel, dim3((n_lists + 255) / 256), dim3(256), 0, st, a);
     hipLaunchKernelGGL(bwd_scan_kernel, dim3(1), dim3(1024), 0, st, a);
-    hipLaunchKernelGGL(bwd_list_fill_kernel, dim3((n_lists + 255) / 256), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(bwd_list_fill_kernel, dim3((n_lists + 3) / 4), dim3(256), 0, st, a);
   } else {
     hipLaunchKernelGGL(bwd_dense_count_kernel, dim3((n_lists + 255) / 256), dim3(256), 0, st, a);
     hipLaunchKernelGGL(bwd_scan_kernel, dim3(1), dim3(1024), 0, st, a);
