@@ -228,6 +228,28 @@ bsa_status bsa_speculative_sparse(const bsa_problem* prob, bsa_tensor q, bsa_ten
                                   const bsa_pattern* missed, bsa_tensor o, float* lse, void* ws, size_t ws_bytes,
                                   bsa_stream stream);
 
+/* bsa_speculative_sparse for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, and harnesses that
+ * forbid hipMalloc.  Identical result (the same kernels, the same split
+ * plan), but the float32 partials of the two passes go to a scratch area
+ * that the library keeps in device memory, BSA_NOALLOC_SCRATCH_BYTES per
+ * device, held until the process ends, instead of a caller workspace.  The
+ * call allocates and frees nothing.  The caller still owns every input and
+ * output.  The scratch address is looked up once per device, on the first
+ * call made with that device current.
+ * Every call on one device shares that device's scratch area: calls that
+ * overlap on one GPU (two streams, two threads) race and give undefined
+ * results; calls ordered on one stream are safe.  Nothing needs clearing
+ * between calls, since every partial a call reads was written by that call.
+ * Errors: as bsa_speculative_sparse; BSA_ERR_WORKSPACE when the partials
+ * (bsa_speculative_workspace_size bytes) exceed BSA_NOALLOC_SCRATCH_BYTES;
+ * BSA_ERR_HIP when the scratch address cannot be obtained. */
+#define BSA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+bsa_status bsa_speculative_sparse_noalloc(const bsa_problem* prob, bsa_tensor q, bsa_tensor k_spec,
+                                          bsa_tensor v_spec, int32_t Sk_spec, int32_t causal_spec, bsa_tensor k,
+                                          bsa_tensor v, const bsa_pattern* missed, bsa_tensor o, float* lse,
+                                          bsa_stream stream);
+
 /* The two passes of bsa_speculative_sparse without the combine: P float32
  * partials (o_part [P, B, Sq, Hq, D], lse_part [P, B, Hq, Sq], contiguous),
  * P = bsa_speculative_num_partials().  When the query rows of a kv head fit one

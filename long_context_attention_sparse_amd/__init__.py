@@ -15,18 +15,20 @@ include/bsa.h and only marshals arguments — the kernels do all the work:
   vs_convert_indexes_mergehead  the same with per-head counts of valid indices
   speculative_sparse  speculative pass + sparse repair pass + combine
                       (bsa_speculative_sparse; bsa_speculative_partials without
-                      the combine)
+                      the combine; speculative_sparse_noalloc with the partials
+                      in a library-resident scratch area, for callers that
+                      cannot allocate)
   bsa_check_pattern   device check of a pattern's contents (the same check the
                       entry points run first when BSA_DEBUG_CHECKS is set)
 """
-from ._binding import (EXPORTS, LIB_PATH, BlockPattern, BSAError, VSPattern, bsa_check_pattern, bsa_combine, bsa_fwd,
+from ._binding import (EXPORTS, LIB_PATH, NOALLOC_SCRATCH_BYTES, BlockPattern, BSAError, VSPattern, bsa_check_pattern, bsa_combine, bsa_fwd,
                        bsa_fwd_gated, bsa_bwd, bsa_bwd_workspace_size, bsa_fwd_selected, bsa_selected_workspace_size, bsfa_calibrate,
                        bsa_fwd_partials, bsa_num_partials, bsa_speculative_partials, bsa_workspace_size, load,
-                       speculative_sparse, vs_convert_indexes,
+                       speculative_sparse, speculative_sparse_noalloc, vs_convert_indexes,
                        vs_convert_indexes_mergehead)
 
-__all__ = ["EXPORTS", "LIB_PATH", "BlockPattern", "BSAError", "VSPattern", "bsa_check_pattern", "bsa_combine", "bsa_fwd", "bsa_fwd_gated",
+__all__ = ["EXPORTS", "LIB_PATH", "NOALLOC_SCRATCH_BYTES", "BlockPattern", "BSAError", "VSPattern", "bsa_check_pattern", "bsa_combine", "bsa_fwd", "bsa_fwd_gated",
            "bsa_bwd", "bsa_bwd_workspace_size", "bsa_fwd_selected", "bsa_selected_workspace_size", "bsfa_calibrate",
            "bsa_fwd_partials", "bsa_num_partials", "bsa_speculative_partials", "bsa_workspace_size", "load",
-           "speculative_sparse", "vs_convert_indexes",
+           "speculative_sparse", "speculative_sparse_noalloc", "vs_convert_indexes",
            "vs_convert_indexes_mergehead"]

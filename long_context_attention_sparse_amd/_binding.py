@@ -21,9 +21,10 @@ LIB_PATH = os.path.join(_PKG, "libbsa.so")
 BSA_OK, BSA_ERR_INVALID_ARG, BSA_ERR_UNSUPPORTED, BSA_ERR_WORKSPACE, BSA_ERR_HIP = range(5)
 BSA_BF16, BSA_F32 = 0, 1
 BSA_PAT_DENSE, BSA_PAT_BLOCK, BSA_PAT_VS = 0, 1, 2
+NOALLOC_SCRATCH_BYTES = 16 << 20   # BSA_NOALLOC_SCRATCH_BYTES of include/bsa.h
 
 EXPORTS = ("bsa_status_string", "bsa_workspace_size", "bsa_fwd", "bsa_fwd_partials", "bsa_num_partials",
-           "bsa_speculative_sparse", "bsa_speculative_partials", "bsa_speculative_num_partials",
+           "bsa_speculative_sparse", "bsa_speculative_sparse_noalloc", "bsa_speculative_partials", "bsa_speculative_num_partials",
            "bsa_speculative_workspace_size", "bsa_combine", "bsa_fwd_gated", "bsfa_calibrate",
            "bsa_selected_workspace_size", "bsa_fwd_selected", "bsa_bwd_workspace_size", "bsa_bwd",
            "vs_convert_indexes", "vs_convert_indexes_mergehead", "bsa_check_pattern")
@@ -84,6 +85,8 @@ def load(path: str = LIB_PATH):
     lib.bsa_speculative_sparse.restype = ctypes.c_int
     lib.bsa_speculative_sparse.argtypes = spec_args + [_Tensor, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                                        ctypes.c_void_p]
+    lib.bsa_speculative_sparse_noalloc.restype = ctypes.c_int
+    lib.bsa_speculative_sparse_noalloc.argtypes = spec_args + [_Tensor, ctypes.c_void_p, ctypes.c_void_p]
     lib.bsa_speculative_partials.restype = ctypes.c_int
     lib.bsa_speculative_partials.argtypes = spec_args + [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     lib.bsa_speculative_num_partials.restype = ctypes.c_int32
@@ -566,4 +569,21 @@ def speculative_sparse(q, k_spec, v_spec, k, v, missed: BlockPattern, *, causal_
                                     _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                     _stream(stream))
     _check("bsa_speculative_sparse", st)
+    return out, lse
+
+
+def speculative_sparse_noalloc(q, k_spec, v_spec, k, v, missed: BlockPattern, *, out: torch.Tensor,
+                               lse: Optional[torch.Tensor] = None, causal_spec: bool = True, softmax_scale=None,
+                               softcap: float = 0.0, stream=None):
+    """``speculative_sparse`` without any device allocation: the caller passes the outputs
+    (``out`` like q, bf16 or float32; ``lse`` float32 [B, Hq, Sq] or None) and the partials
+    live in the library's per-device scratch area (NOALLOC_SCRATCH_BYTES).  Calls that
+    overlap on one GPU share that area and race.  Returns (out, lse)."""
+    lib = load()
+    prob = _problem(q, k, False, softmax_scale, softcap=softcap)
+    pat = missed.struct(prob.Hq)
+    st = lib.bsa_speculative_sparse_noalloc(ctypes.byref(prob), _tensor(q), _tensor(k_spec), _tensor(v_spec),
+                                            k_spec.shape[1], int(bool(causal_spec)), _tensor(k), _tensor(v),
+                                            ctypes.byref(pat), _tensor(out), _ptr(lse), _stream(stream))
+    _check("bsa_speculative_sparse_noalloc", st)
     return out, lse

@@ -11,6 +11,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "args.cuh"
 #include "bsa.h"
@@ -129,6 +130,34 @@ bsa_status run_prefill(const bsa_problem& p, const bsa_tensor& q, const bsa_tens
   }
   launch_prefill(a, BM / 32, kind, st);
   return launch_status();
+}
+
+// ---------------------------------------------------------------------------
+// Library-resident scratch of bsa_speculative_sparse_noalloc
+// ---------------------------------------------------------------------------
+
+// One copy per device.  In host code this name is only a handle for the symbol lookup: its
+// device address comes from hipGetSymbolAddress, made once per device with that device
+// current, and only that address is ever handed to a kernel.
+static __device__ __align__(256) unsigned char scratch[BSA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of the current device's scratch area (looked up on first use).
+bsa_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return BSA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return BSA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return BSA_ERR_HIP;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return BSA_OK;
 }
 
 // Entries (list entries, or 64-key chunks for a dense pattern) and the number of
@@ -310,6 +339,22 @@ bsa_status bsa_speculative_sparse(const bsa_problem* prob, bsa_tensor q, bsa_ten
   CombineArgs c{slots, p.B, p.Hq, p.Sq, p.D, part_o, part_lse, oarg(o), lse};
   launch_combine(c, reinterpret_cast<hipStream_t>(stream));
   return launch_status();
+}
+
+bsa_status bsa_speculative_sparse_noalloc(const bsa_problem* prob, bsa_tensor q, bsa_tensor k_spec,
+                                          bsa_tensor v_spec, int32_t Sk_spec, int32_t causal_spec, bsa_tensor k,
+                                          bsa_tensor v, const bsa_pattern* missed, bsa_tensor o, float* lse,
+                                          bsa_stream stream) {
+  bsa_status st = check_problem(prob, q, k, v, o);
+  if (st != BSA_OK) return st;
+  const int32_t slots = bsa_speculative_num_partials(prob, Sk_spec, missed);
+  if (slots <= 0) return BSA_ERR_INVALID_ARG;
+  if (partial_bytes(*prob, slots) > BSA_NOALLOC_SCRATCH_BYTES) return BSA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != BSA_OK) return st;
+  return bsa_speculative_sparse(prob, q, k_spec, v_spec, Sk_spec, causal_spec, k, v, missed, o, lse, ws,
+                                BSA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 bsa_status bsa_combine(int32_t P, int32_t B, int32_t Hq, int32_t Sq, int32_t D, const float* o_part,
