@@ -1,15 +1,23 @@
 """Benchmark of the block-sparse attention hot path on one MI355X.
 
-Default: the speculative + sparse decode workload (B=32, Hq=32, Hkv=8, D=128, Sk=32768;
-speculative pass over the last 2048 keys, repair pass over 25% of the earlier 64-key
-blocks, one combine).  A step is one full pass: both attention passes plus the combine.
-``--config N`` selects another workload (1 tiny decode, 3 block-sparse prefill, 4 gated
-prefill, 5 vertical-slash conversion + varlen prefill).
+Default (no ``--config``): every workload at full size, in one JSON line.
 
-Prints one JSON line: whole-step throughput (HBM GB/s of algorithmic bytes for decode,
-effective TFLOP/s over visited tiles for prefill), the dominant kernel's roofline figures
-measured with HIP events on the stream the kernels run on, and the float64 CPU oracle's
-rate on a bounded sample of the same workload.
+  1 tiny sparse decode             (B=1, H=4, D=64, Sk=1024; sets A, B and their combine)
+  2 speculative + sparse decode    (B=32, Hq=32, Hkv=8, D=128, Sk=32768)      <- headline
+  3 block-sparse causal prefill    (S=32768, Hq=32, Hkv=8, 128x128 tiles, 34-entry lists)
+  4 BSFA gated causal prefill      (S=65536, Hq=32, Hkv=8, ~50% of off-diagonal tiles skipped)
+  5 vertical-slash varlen prefill  (seqlens 65536 + 32768, H=32; conversion + attention)
+  6 selected attention             (seqlens 65536 + 32768, 4 heads, top-16 of 64-key blocks)
+  7 backward of workload 3         (dQ, dK, dV)
+
+The headline ``value`` / ``ms_per_step`` is workload 2, a step being both attention passes and
+the combine; ``config.per_config`` carries every workload's ms per call, rate, dominant kernel,
+algorithmic work, roofline fraction and CPU baseline.  ``--config N`` prints workload N alone.
+
+Phase 1 (CPU only, before anything touches the GPU): generate the seeded inputs and time the
+float64 oracle on a bounded sample of each workload in a process pool (one worker per host
+core, up to 16, each with one BLAS thread).  Phase 2: upload and time each workload on the
+GPU with HIP events on the stream the library launches on.
 """
 import argparse
 import json
@@ -25,6 +33,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 METRIC = "sparse-attn fwd: effective TFLOP/s (prefill), HBM GB/s (decode), ms/call"
+ALL_CONFIGS = (1, 2, 3, 4, 5, 6, 7)
+HEADLINE = 2
 
 
 def _args():
@@ -32,8 +42,9 @@ def _args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7])
-    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU oracle sample")
+    ap.add_argument("--config", type=int, default=None, choices=list(ALL_CONFIGS),
+                    help="one workload only (default: all of them in one line)")
+    ap.add_argument("--cpu-seconds", type=float, default=3.0, help="wall-clock budget of each oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="time decode steps as eager launches instead of HIP graph replays")
@@ -45,6 +56,237 @@ def _args():
 def _log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
+
+# ---------------------------------------------------------------------------
+# Inputs (seeded, synthetic)
+# ---------------------------------------------------------------------------
+
+def generate(cfg):
+    from synth.workloads import (block_sparse_prefill, gated_prefill, selected_prefill, spec_sparse_decode,
+                                 tiny_decode, vs_varlen_prefill)
+    from synth import normal_bf16
+
+    t0 = time.perf_counter()
+    if cfg == 1:
+        w = tiny_decode()
+    elif cfg == 2:
+        w = spec_sparse_decode()
+    elif cfg in (3, 7):
+        w = block_sparse_prefill()
+        if cfg == 7:
+            w["do"] = normal_bf16(1007, "do", w["q"].shape)
+    elif cfg == 4:
+        w = gated_prefill()
+    elif cfg == 5:
+        w = vs_varlen_prefill()
+    else:
+        w = selected_prefill()
+    _log(f"workload {cfg}: inputs generated in {time.perf_counter() - t0:.1f} s")
+    return w
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the float64 oracle on a bounded sample, in a process pool
+# ---------------------------------------------------------------------------
+
+_W = {}  # workloads, read by the forked workers (copy on write)
+
+
+def cpu_cores():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _worker_init():
+    from threadpoolctl import threadpool_limits
+
+    global _LIMIT
+    _LIMIT = threadpool_limits(limits=1)
+
+
+def _unit_tiny(u):
+    import oracle
+
+    w = _W[1]
+    t0 = time.perf_counter()
+    B, H = w["B"], w["Hq"]
+    parts = [oracle.block_sparse(w["q"], w["k"], w["v"], np.full((B, H, 1), w[s].shape[-1], np.int32),
+                                 w[s][:, :, None, :], 1, 64) for s in ("set_a", "set_b")]
+    oracle.combine(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
+    return time.perf_counter() - t0, 1.0
+
+
+def _unit_decode(bh):
+    import oracle
+
+    w = _W[2]
+    b, h = bh
+    G = w["Hq"] // w["Hkv"]
+    hs = slice(h * G, (h + 1) * G)
+    s0, bs, n = w["spec_start"], w["block_size"], w["missed"].shape[-1]
+    t0 = time.perf_counter()
+    oracle.speculative_sparse(w["q"][b:b + 1, :, hs], w["k"][b:b + 1, s0:, h:h + 1], w["v"][b:b + 1, s0:, h:h + 1],
+                              w["k"][b:b + 1, :, h:h + 1], w["v"][b:b + 1, :, h:h + 1],
+                              np.full((1, 1, 1), n, np.int32), w["missed"][b:b + 1, h:h + 1, None, :], bs,
+                              causal_spec=True)
+    dt = time.perf_counter() - t0
+    # algorithmic bytes of one (b, kv head) group: its K/V blocks, Q, O (bf16), LSE, list
+    D = w["D"]
+    byts = (n + (w["Sk"] - s0) // bs) * bs * D * 4 + G * D * 4 + G * 4 + n * 4 + 4
+    return dt, float(byts)
+
+
+def _unit_block(hi):
+    import oracle
+
+    w = _W[3]
+    h, i = hi
+    G = w["Hq"] // w["Hkv"]
+    ents = w["index"][0, h, i, :w["count"][0, h, i]]
+    keys = np.concatenate([np.arange(j * 128, (j + 1) * 128) for j in ents])
+    rows = np.arange(i * 128, (i + 1) * 128)
+    t0 = time.perf_counter()
+    oracle.attend_rows(w["q"][0, rows, h], w["k"][0, :, h // G], w["v"][0, :, h // G],
+                       [keys[keys <= r] for r in rows], 1.0 / np.sqrt(128))
+    return time.perf_counter() - t0, float(len(ents) * 4 * 128 ** 3)
+
+
+def _unit_gated(hi):
+    import oracle
+    from synth.workloads import thresholds_from_tile_max
+
+    w = _W[4]
+    h, i = hi
+    # threshold of this row from the oracle's own tile maxima (the workload's recipe; untimed)
+    t = oracle.tile_max_row(w["q"], w["k"], 0, h, i, 128, 128)
+    T = thresholds_from_tile_max(t, i)
+    t0 = time.perf_counter()
+    _, _, keep, _ = oracle.gated_rows(w["q"], w["k"], w["v"], T, 0, h, i, np.arange(i * 128, (i + 1) * 128))
+    dt = time.perf_counter() - t0
+    return dt, float((i + 1 + int(keep.sum())) * 2 * 128 ** 3)
+
+
+def _unit_vs(bhm):
+    import oracle
+
+    w = _W[5]
+    b, h, m = bhm
+    L = int(w["seqlens"][b])
+    t0 = time.perf_counter()
+    wins, cols = oracle.vs_convert_item(L, L, w["vertical"][b, h], w["slash"][b, h], m, 64, 64)
+    rows = np.arange(m * 64, min(L, m * 64 + 64))
+    oracle.vs_attention_rows(w["q"], w["k"], w["v"], b, h, rows, wins, cols, w["cu_seqlens"], w["cu_seqlens"], 64)
+    dt = time.perf_counter() - t0
+    return dt, float(4 * 64 * 128 * (64 * len(wins) + len(cols)))
+
+
+def _unit_selected(bhr):
+    import oracle
+
+    w = _W[6]
+    b, h, r0 = bhr
+    L = int(w["seqlens"][b])
+    rows = np.arange(r0, min(L, r0 + 16))
+    hk = h // (w["Hq"] // w["Hkv"])
+    sel = w["sel"][int(w["cu_seqlens"][b]) + rows, hk]
+    t0 = time.perf_counter()
+    oracle.selected_rows(w["q"], w["k"], w["v"], w["sel"], 64, w["cu_seqlens"], w["cu_seqlens"], b, h, rows)
+    dt = time.perf_counter() - t0
+    return dt, float((sel >= 0).sum() * 4 * 64 * 128)
+
+
+def _unit_backward(hi):
+    import oracle
+
+    w = _W[7]
+    h, i = hi
+    G = w["Hq"] // w["Hkv"]
+    ents = np.sort(w["index"][0, h, i, :w["count"][0, h, i]])     # the diagonal block last
+    keys = np.concatenate([np.arange(j * 128, (j + 1) * 128) for j in ents])
+    rows = slice(i * 128, (i + 1) * 128)
+    q = w["q"][:, rows, h:h + 1]
+    k = w["k"][:, keys, h // G:h // G + 1]
+    v = w["v"][:, keys, h // G:h // G + 1]
+    do = w["do"][:, rows, h:h + 1]
+    t0 = time.perf_counter()
+    oracle.block_sparse_bwd(q, k, v, do, causal=True)
+    return time.perf_counter() - t0, float(len(ents) * 5 * 2 * 128 ** 3)
+
+
+def _units(cfg, w):
+    g = np.random.default_rng(cfg)
+    if cfg == 1:
+        return _unit_tiny, [None] * 100000
+    if cfg == 2:
+        u = [(b, h) for b in range(w["B"]) for h in range(w["Hkv"])]
+        return _unit_decode, [u[j] for j in g.permutation(len(u))]
+    if cfg in (3, 4, 7):
+        nqb = w["Sq"] // 128
+        u = [(int(h), int(i)) for h, i in zip(g.integers(0, w["Hq"], 8192), g.integers(0, nqb, 8192))]
+        return {3: _unit_block, 4: _unit_gated, 7: _unit_backward}[cfg], u
+    if cfg == 5:
+        u = []
+        for _ in range(8192):
+            b = int(g.integers(0, 2))
+            u.append((b, int(g.integers(0, w["H"])), int(g.integers(0, int(w["seqlens"][b]) // 64))))
+        return _unit_vs, u
+    u = []
+    for _ in range(8192):
+        b = int(g.integers(0, 2))
+        u.append((b, int(g.integers(0, w["Hq"])), int(g.integers(0, int(w["seqlens"][b]) // 16)) * 16))
+    return _unit_selected, u
+
+
+CPU_UNIT = {1: ("ms/call", "calls of the whole workload (set A, set B, combine)"),
+            2: ("GB/s", "(batch, kv head) groups: both passes and the combine"),
+            3: ("TFLOP/s", "(head, 128-row query block) rows over their listed blocks"),
+            4: ("TFLOP/s", "(head, 128-row query block) gated rows: tile maxima, keep rule, attention over kept tiles"
+                           " (each row's threshold is picked from the oracle's tile maxima outside the timing)"),
+            5: ("TFLOP/s", "(sequence, head, 64-row query block) items: conversion and attention"),
+            6: ("TFLOP/s", "16-token runs of one (sequence, head)"),
+            7: ("TFLOP/s", "(head, 128-row query block) rows: dQ and the block's dK/dV contributions")}
+
+
+def cpu_baseline(cfg, w, budget, cores):
+    """Float64 oracle rate on a random sample of the workload's independent units, run in a
+    pool of `cores` forked workers (one BLAS thread each) until `budget` seconds of wall time
+    have passed.  Each unit is timed in its worker; the rate is the work done over the summed
+    unit seconds, times the worker count (the whole host's throughput)."""
+    import multiprocessing as mp
+
+    fn, units = _units(cfg, w)
+    _W.clear()
+    _W[cfg] = w
+    ctx = mp.get_context("fork")
+    secs, work, done = 0.0, 0.0, 0
+    t0 = time.perf_counter()
+    with ctx.Pool(cores, initializer=_worker_init) as pool:
+        for dt, wk in pool.imap_unordered(fn, units):
+            secs += dt
+            work += wk
+            done += 1
+            if time.perf_counter() - t0 > budget:
+                break
+        pool.terminate()
+    wall = time.perf_counter() - t0
+    _W.clear()
+    unit, what = CPU_UNIT[cfg]
+    if cfg == 1:
+        value = round(secs / done * 1e3, 4)  # per call, each call on one core
+    else:
+        rate = work / secs * cores
+        value = round(rate / (1e9 if unit == "GB/s" else 1e12), 6)
+    return {"value": value, "unit": unit, "cores": cores, "kind": "oracle",
+            "sample": f"{done} random {what} of the same workload, float64 NumPy, {cores} worker processes with "
+                      f"one BLAS thread each, {wall:.1f} s wall ({secs:.1f} core-seconds inside the oracle)"}
+
+
+# ---------------------------------------------------------------------------
+# GPU timing helpers
+# ---------------------------------------------------------------------------
 
 class Timer:
     """HIP events around named launches on torch's current stream (where the library enqueues)."""
@@ -103,9 +345,8 @@ def sources_digest():
     import hashlib
 
     h = hashlib.sha256()
-    root = os.path.dirname(os.path.abspath(__file__))
     for f in TRAFFIC_SOURCES:
-        with open(os.path.join(root, f), "rb") as fh:
+        with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
@@ -155,142 +396,47 @@ def kernel_mean_ms(torch, fn, per_graph=10, replays=5):
     return float(np.mean(ms))
 
 
-def kernel_mean_ms_flushed(torch, fn, reps=10):
-    """Mean device time of the launch fn makes when neither L2 nor the memory-side cache holds
-    its inputs: a 1 GiB buffer is written before every launch, HIP events around the launch."""
-    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
+def rotating_mean_ms(torch, fns, reps=12):
+    """Mean device time of one launch when its inputs are in no cache: the launches fns[i]
+    read disjoint copies of the inputs and run in turn, each bracketed by HIP events, so the
+    bytes a launch reads were last touched len(fns) - 1 launches (gigabytes) earlier and
+    nothing is written between the events but the launch's own output."""
     ms = []
-    for i in range(reps + 1):
-        scratch.fill_(i & 0xFF)
+    for i in range(reps + len(fns)):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
         a.record()
-        fn()
+        fns[i % len(fns)]()
         b.record()
         torch.cuda.synchronize()
-        if i:
+        if i >= len(fns):
             ms.append(a.elapsed_time(b))
-    del scratch
     return float(np.mean(ms))
 
 
-def cpu_rate(fn, units, budget_s):
-    """Run fn(unit) over units, BLAS limited to one thread, until the budget is spent;
-    returns (units done, seconds)."""
-    from threadpoolctl import threadpool_limits
+def free(torch):
+    import gc
 
-    done, t0 = 0, time.perf_counter()
-    with threadpool_limits(limits=1):
-        for u in units:
-            fn(u)
-            done += 1
-            if time.perf_counter() - t0 > budget_s:
-                break
-    return done, time.perf_counter() - t0
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
 
 
-# ---------------------------------------------------------------------------
-# Workload 2: speculative + sparse decode (default)
-# ---------------------------------------------------------------------------
-
-def bench_spec_decode(torch, bsa, args):
-    from synth import to_torch_bf16
-    from synth.workloads import spec_sparse_decode
-
-    _log("generating speculative+sparse decode inputs")
-    w = spec_sparse_decode()
-    dev = torch.device("cuda:0")
-    q, k, v = (to_torch_bf16(w[n]).to(dev) for n in ("q", "k", "v"))
-    B, Hq, Hkv, D, Sk, bs = w["B"], w["Hq"], w["Hkv"], w["D"], w["Sk"], w["block_size"]
-    s0 = w["spec_start"]
-    n_missed = w["missed"].shape[-1]
-    count = torch.full((B, Hkv, 1), n_missed, dtype=torch.int32, device=dev)
-    index = torch.from_numpy(np.ascontiguousarray(w["missed"][:, :, None, :])).to(dev)
-    missed = bsa.BlockPattern(count, index, 128, bs)
-    k_spec, v_spec = k[:, s0:], v[:, s0:]
-    o_part, lse_part = bsa.bsa_speculative_partials(q, k_spec, v_spec, k, v, missed)
-    out = torch.empty((B, 1, Hq, D), dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((B, Hq, 1), dtype=torch.float32, device=dev)
-
-    def step(timer):
-        with timer.span("passes"):
-            bsa.bsa_speculative_partials(q, k_spec, v_spec, k, v, missed, o_part=o_part, lse_part=lse_part)
-        with timer.span("combine"):
-            bsa.bsa_combine(o_part, lse_part, out=out, lse=lse)
-
-    timer = Timer(torch)
-    eager_ms = run_steps(torch, step, timer, args.steps, args.warmup)
-    spans = {n: round(timer.mean_ms(n) * 1e3, 2) for n in timer.spans}
-    _log("eager per-launch us (host launch gaps included):", spans)
-
-    def passes():
-        bsa.bsa_speculative_partials(q, k_spec, v_spec, k, v, missed, o_part=o_part, lse_part=lse_part)
-
-    def full_step():
-        passes()
-        bsa.bsa_combine(o_part, lse_part, out=out, lse=lse)
-
-    if args.eager:
-        ms, pass_ms = eager_ms, timer.mean_ms("passes")
-    else:
-        # a decode step replays as one HIP graph (launch overhead off the critical path)
-        ms = run_graph_steps(torch, capture(torch, full_step), args.steps)
-        pass_ms = kernel_mean_ms(torch, passes)
-    flushed_ms = kernel_mean_ms_flushed(torch, passes)
-    groups = B * Hkv
-    blk_bytes = bs * D * 2 * 2
-    kv_bytes = groups * (n_missed + (Sk - s0) // bs) * blk_bytes
-    io_bytes = q.numel() * 2 + out.numel() * 2 + lse.numel() * 4 + index.numel() * 4 + count.numel() * 4
-    step_bytes = kv_bytes + io_bytes
-    pass_bytes = kv_bytes + q.numel() * 2 + index.numel() * 4 + count.numel() * 4
-    achieved = pass_bytes / (pass_ms * 1e-3) / 1e9
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        import oracle
-
-        G = Hq // Hkv
-        order = [(b, h) for b in range(B) for h in range(Hkv)]
-
-        def one(bh):
-            b, h = bh
-            hs = slice(h * G, (h + 1) * G)
-            oracle.speculative_sparse(w["q"][b:b + 1, :, hs], w["k"][b:b + 1, s0:, h:h + 1],
-                                      w["v"][b:b + 1, s0:, h:h + 1], w["k"][b:b + 1, :, h:h + 1],
-                                      w["v"][b:b + 1, :, h:h + 1], np.full((1, 1, 1), n_missed, np.int32),
-                                      w["missed"][b:b + 1, h:h + 1, None, :], bs, causal_spec=True)
-        done, secs = cpu_rate(one, order, args.cpu_seconds)
-        per_group = step_bytes / groups
-        cpu = {"value": round(done * per_group / secs / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-               "sample": f"{done} of {groups} (batch, kv-head) groups of the same workload, float64 NumPy, "
-                         f"{secs:.1f} s, BLAS limited to 1 thread"}
-    value = step_bytes / (ms * 1e-3) / 1e9
-    return dict(
-        metric=METRIC, value=round(value, 2), unit="GB/s", ms_per_step=round(ms, 4), dtype="bf16",
-        config={"workload": "speculative+sparse decode", "B": B, "Hq": Hq, "Hkv": Hkv, "D": D, "Sk": Sk,
-                "block": bs, "spec_tokens": Sk - s0, "missed_blocks_per_group": n_missed,
-                "partials": int(o_part.shape[0]), "algorithmic_bytes_per_step": step_bytes,
-                "timing": "eager" if args.eager else "hip graph replay", "eager_ms_per_step": round(eager_ms, 4),
-                "eager_launch_us": spans},
-        roofline={"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                  "frac": round(achieved / HBM_PEAK_GBS, 4),
-                  "traffic": DECODE_TRAFFIC["bytes"] if DECODE_TRAFFIC["sha256"] == sources_digest() else None,
-                  "kernel": "decode_kernel<128> (speculative and repair passes, one launch)",
-                  "algorithmic_bytes": pass_bytes, "avg_ms": round(pass_ms, 5),
-                  "caches_flushed": {"avg_ms": round(flushed_ms, 5),
-                                     "achieved": round(pass_bytes / (flushed_ms * 1e-3) / 1e9, 1)}},
-        cpu_baseline=cpu)
+def _roof(bound, achieved, kernel, avg_ms, **extra):
+    peak = HBM_PEAK_GBS if bound == "hbm" else BF16_PEAK_TFLOPS
+    d = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": "GB/s" if bound == "hbm" else "TFLOP/s",
+         "frac": round(achieved / peak, 4), "traffic": None, "kernel": kernel, "avg_ms": round(avg_ms, 5)}
+    d.update(extra)
+    return d
 
 
 # ---------------------------------------------------------------------------
 # Workload 1: tiny sparse decode (latency)
 # ---------------------------------------------------------------------------
 
-def bench_tiny(torch, bsa, args):
+def gpu_tiny(torch, bsa, w, args):
     from synth import to_torch_bf16
-    from synth.workloads import tiny_decode
 
-    w = tiny_decode()
     dev = torch.device("cuda:0")
     q, k, v = (to_torch_bf16(w[n]).to(dev) for n in ("q", "k", "v"))
     B, H = w["B"], w["Hq"]
@@ -330,27 +476,111 @@ def bench_tiny(torch, bsa, args):
         a_ms = kernel_mean_ms(torch, set_a)
     kv = B * H * 16 * 64 * w["D"] * 2 * 2
     a_bytes = B * H * 6 * 64 * w["D"] * 4
-    return dict(metric=METRIC, value=round(ms, 4), unit="ms/call", higher_is_better=False, ms_per_step=round(ms, 4),
-                dtype="bf16",
-                config={"workload": "tiny sparse decode (A, B, combine)", "B": B, "H": H, "D": w["D"], "Sk": w["Sk"],
-                        "block": 64, "kv_bytes": kv, "timing": "eager" if args.eager else "hip graph replay",
-                        "eager_ms_per_step": round(eager_ms, 4), "eager_launch_us": spans},
-                roofline={"bound": "hbm", "achieved": round(a_bytes / (a_ms * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS,
-                          "unit": "GB/s", "frac": round(a_bytes / (a_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 6),
-                          "traffic": None, "kernel": "decode_kernel<64,1> (set A)"},
-                cpu_baseline=None)
+    return dict(workload="tiny sparse decode (sets A and B, combine)", value=round(ms, 4), unit="ms/call",
+                higher_is_better=False, ms=ms,
+                config={"B": B, "H": H, "D": w["D"], "Sk": w["Sk"], "block": 64, "kv_bytes": kv,
+                        "timing": "eager" if args.eager else "hip graph replay",
+                        "eager_ms_per_step": round(eager_ms, 4), "eager_launch_us": spans,
+                        "algorithmic_units": "6 + 10 listed 64-key blocks per head (K and V: 16 KB each), 4 heads"},
+                roofline=_roof("hbm", a_bytes / (a_ms * 1e-3) / 1e9, "void bsa::decode_kernel<64>(bsa::DecodeArgs) (set A)",
+                               a_ms, note="latency-bound: 4 workgroups; the launch, not HBM, sets the time"))
+
+
+# ---------------------------------------------------------------------------
+# Workload 2: speculative + sparse decode (headline)
+# ---------------------------------------------------------------------------
+
+def gpu_spec_decode(torch, bsa, w, args):
+    from synth import to_torch_bf16
+
+    dev = torch.device("cuda:0")
+    q, k, v = (to_torch_bf16(w[n]).to(dev) for n in ("q", "k", "v"))
+    B, Hq, Hkv, D, Sk, bs = w["B"], w["Hq"], w["Hkv"], w["D"], w["Sk"], w["block_size"]
+    s0 = w["spec_start"]
+    n_missed = w["missed"].shape[-1]
+    count = torch.full((B, Hkv, 1), n_missed, dtype=torch.int32, device=dev)
+    index = torch.from_numpy(np.ascontiguousarray(w["missed"][:, :, None, :])).to(dev)
+    missed = bsa.BlockPattern(count, index, 128, bs)
+    k_spec, v_spec = k[:, s0:], v[:, s0:]
+    o_part, lse_part = bsa.bsa_speculative_partials(q, k_spec, v_spec, k, v, missed)
+    out = torch.empty((B, 1, Hq, D), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, Hq, 1), dtype=torch.float32, device=dev)
+
+    def step(timer):
+        with timer.span("passes"):
+            bsa.bsa_speculative_partials(q, k_spec, v_spec, k, v, missed, o_part=o_part, lse_part=lse_part)
+        with timer.span("combine"):
+            bsa.bsa_combine(o_part, lse_part, out=out, lse=lse)
+
+    timer = Timer(torch)
+    eager_ms = run_steps(torch, step, timer, args.steps, args.warmup)
+    spans = {n: round(timer.mean_ms(n) * 1e3, 2) for n in timer.spans}
+    _log("decode eager per-launch us (host launch gaps included):", spans)
+
+    def passes():
+        bsa.bsa_speculative_partials(q, k_spec, v_spec, k, v, missed, o_part=o_part, lse_part=lse_part)
+
+    def full_step():
+        passes()
+        bsa.bsa_combine(o_part, lse_part, out=out, lse=lse)
+
+    if args.eager:
+        ms, pass_ms = eager_ms, timer.mean_ms("passes")
+    else:
+        # a decode step replays as one HIP graph (launch overhead off the critical path)
+        ms = run_graph_steps(torch, capture(torch, full_step), args.steps)
+        pass_ms = kernel_mean_ms(torch, passes)
+    groups = B * Hkv
+    blk_bytes = bs * D * 2 * 2
+    kv_bytes = groups * (n_missed + (Sk - s0) // bs) * blk_bytes
+    io_bytes = q.numel() * 2 + out.numel() * 2 + lse.numel() * 4 + index.numel() * 4 + count.numel() * 4
+    step_bytes = kv_bytes + io_bytes
+    pass_bytes = kv_bytes + q.numel() * 2 + index.numel() * 4 + count.numel() * 4
+    achieved = pass_bytes / (pass_ms * 1e-3) / 1e9
+
+    # cold caches: a second copy of K/V, launches alternating between the copies, so every
+    # launch reads bytes last touched 1.3 GB of reads earlier (the memory-side cache holds 256 MB)
+    k2, v2 = k.clone(), v.clone()
+    o_part2, lse_part2 = torch.empty_like(o_part), torch.empty_like(lse_part)
+    cold = [passes, lambda: bsa.bsa_speculative_partials(q, k2[:, s0:], v2[:, s0:], k2, v2, missed, o_part=o_part2,
+                                                         lse_part=lse_part2)]
+    cold_ms = rotating_mean_ms(torch, cold)
+    # a plain device copy moving the same number of bytes (half read, half written), timed
+    # the same way over two rotating source/destination pairs
+    n_el = pass_bytes // 4
+    bufs = [(torch.ones(n_el, dtype=torch.bfloat16, device=dev), torch.empty(n_el, dtype=torch.bfloat16, device=dev))
+            for _ in range(2)]
+    copy_ms = rotating_mean_ms(torch, [lambda p=p: p[1].copy_(p[0]) for p in bufs])
+    del k2, v2, o_part2, lse_part2, bufs
+
+    value = step_bytes / (ms * 1e-3) / 1e9
+    return dict(workload="speculative+sparse decode", value=round(value, 2), unit="GB/s", ms=ms,
+                config={"B": B, "Hq": Hq, "Hkv": Hkv, "D": D, "Sk": Sk, "block": bs, "spec_tokens": Sk - s0,
+                        "missed_blocks_per_group": n_missed, "partials": int(o_part.shape[0]),
+                        "algorithmic_bytes_per_step": step_bytes,
+                        "algorithmic_units": "152 listed 64-key blocks per (batch, kv head) x 256 groups, 32 KB of K "
+                                             "and V each, plus Q, O, LSE and the lists",
+                        "timing": "eager" if args.eager else "hip graph replay", "eager_ms_per_step": round(eager_ms, 4),
+                        "eager_launch_us": spans},
+                roofline=_roof("hbm", achieved, "void bsa::decode_kernel<128>(bsa::DecodeArgs) (both passes, one launch)",
+                               pass_ms,
+                               traffic=DECODE_TRAFFIC["bytes"] if DECODE_TRAFFIC["sha256"] == sources_digest() else None,
+                               algorithmic_bytes=pass_bytes,
+                               caches_cold={"avg_ms": round(cold_ms, 5),
+                                            "achieved": round(pass_bytes / (cold_ms * 1e-3) / 1e9, 1),
+                                            "frac": round(pass_bytes / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                            "method": "two copies of K/V, launches alternating between them",
+                                            "device_copy_same_bytes_ms": round(copy_ms, 5),
+                                            "device_copy_achieved": round(pass_bytes / (copy_ms * 1e-3) / 1e9, 1)}))
 
 
 # ---------------------------------------------------------------------------
 # Workload 3: block-sparse causal prefill
 # ---------------------------------------------------------------------------
 
-def bench_block_prefill(torch, bsa, args):
+def gpu_block_prefill(torch, bsa, w, args):
     from synth import to_torch_bf16
-    from synth.workloads import block_sparse_prefill
 
-    _log("generating block-sparse prefill inputs")
-    w = block_sparse_prefill()
     dev = torch.device("cuda:0")
     q, k, v = (to_torch_bf16(w[n]).to(dev) for n in ("q", "k", "v"))
     pat = bsa.BlockPattern(torch.from_numpy(w["count"]).to(dev), torch.from_numpy(w["index"]).to(dev), 128, 128)
@@ -366,46 +596,23 @@ def bench_block_prefill(torch, bsa, args):
     tiles = int(w["count"].sum())
     flops = tiles * 4 * 128 ** 3
     kms = timer.mean_ms("prefill")
-    tf = flops / (kms * 1e-3) / 1e12
-    cpu = None
-    if not args.no_cpu_baseline:
-        import oracle
-        scale = 1.0 / np.sqrt(128)
-        g = np.random.default_rng(0)
-        units = [(int(h), int(i)) for h, i in zip(g.integers(0, 32, 4096), g.integers(0, 256, 4096))]
-        fl = [0]
-
-        def one(hi):
-            h, i = hi
-            ents = w["index"][0, h, i, :w["count"][0, h, i]]
-            keys = np.concatenate([np.arange(j * 128, (j + 1) * 128) for j in ents])
-            rows = np.arange(i * 128, (i + 1) * 128)
-            oracle.attend_rows(w["q"][0, rows, h], w["k"][0, :, h // 4], w["v"][0, :, h // 4],
-                               [keys[keys <= r] for r in rows], scale)
-            fl[0] += len(ents) * 4 * 128 ** 3
-        done, secs = cpu_rate(one, units, args.cpu_seconds)
-        cpu = {"value": round(fl[0] / secs / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
-               "sample": f"{done} random (head, query block) tiles rows of the same workload, float64, {secs:.1f} s"}
-    return dict(metric=METRIC, value=round(flops / (ms * 1e-3) / 1e12, 2), unit="TFLOP/s", ms_per_step=round(ms, 4),
-                dtype="bf16",
-                config={"workload": "block-sparse causal prefill", "B": 1, "Hq": 32, "Hkv": 8, "S": w["Sq"], "D": 128,
-                        "tile": 128, "visited_tiles": tiles, "flops": flops},
-                roofline={"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                          "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None,
-                          "kernel": "prefill_tile_kernel<1,4>", "avg_ms": round(kms, 4)},
-                cpu_baseline=cpu)
+    return dict(workload="block-sparse causal prefill", value=round(flops / (ms * 1e-3) / 1e12, 2), unit="TFLOP/s",
+                ms=ms,
+                config={"B": 1, "Hq": 32, "Hkv": 8, "S": w["Sq"], "D": 128, "tile": 128, "visited_tiles": tiles,
+                        "flops": flops,
+                        "algorithmic_units": f"{tiles} visited 128x128 tiles x 4*128^3 flop (QK and PV)"},
+                roofline=_roof("mfma", flops / (kms * 1e-3) / 1e12, "void bsa::prefill_tile_kernel<1, 4>(bsa::PrefillArgs)",
+                               kms))
 
 
 # ---------------------------------------------------------------------------
 # Workload 4: gated prefill
 # ---------------------------------------------------------------------------
 
-def bench_gated(torch, bsa, args):
+def gpu_gated(torch, bsa, w, args):
     from synth import to_torch_bf16
-    from synth.workloads import gated_prefill, thresholds_from_tile_max
+    from synth.workloads import thresholds_from_tile_max
 
-    _log("generating gated prefill inputs")
-    w = gated_prefill()
     dev = torch.device("cuda:0")
     q, k, v = (to_torch_bf16(w[n]).to(dev) for n in ("q", "k", "v"))
     Hq, S = w["Hq"], w["Sq"]
@@ -418,6 +625,7 @@ def bench_gated(torch, bsa, args):
     tm = tmax.cpu().numpy()
     T = np.array([[[thresholds_from_tile_max(tm[0, h, i], i) for i in range(nqb)] for h in range(Hq)]], np.float32)
     Td = torch.from_numpy(T).to(dev)
+    del tmax
     out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
     keep = [None]
 
@@ -439,8 +647,8 @@ def bench_gated(torch, bsa, args):
     causal_tiles = Hq * int(lower.sum())
     flops = causal_tiles * 2 * 128 ** 3 + kept * 2 * 128 ** 3
     timer2 = Timer(torch)
-    ms_dense = run_steps(torch, step_dense, timer2, max(3, args.steps // 4), 2)
-    tf = flops / (kms * 1e-3) / 1e12
+    run_steps(torch, step_dense, timer2, max(3, args.steps // 4), 2)
+    ungated_ms = timer2.mean_ms("ungated")
     off = lower & ~np.eye(nqb, dtype=bool)
     skip = 1.0 - float(km[..., off].mean())
 
@@ -467,28 +675,23 @@ def bench_gated(torch, bsa, args):
     calibration = {"k": k_cal, "ms": round(cal_ms, 4), "tflops": round(cal_flops / (cal_ms * 1e-3) / 1e12, 2),
                    "target_density": round(target, 4), "realised_density": round(realised, 4),
                    "gated_ms_at_calibrated_T": round(cal_gate_ms, 4)}
-    return dict(metric=METRIC, value=round(flops / (ms * 1e-3) / 1e12, 2), unit="TFLOP/s", ms_per_step=round(ms, 4),
-                dtype="bf16",
-                config={"workload": "BSFA gated causal prefill", "B": 1, "Hq": Hq, "Hkv": 8, "S": S, "D": 128,
-                        "tile": 128, "skip_fraction_offdiag": round(skip, 4), "flops": flops,
-                        "ungated_ms": round(ms_dense, 4), "gated_speedup": round(ms_dense / ms, 3),
-                        "calibration": calibration},
-                roofline={"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                          "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None, "kernel": "gated_kernel",
-                          "avg_ms": round(kms, 4)},
-                cpu_baseline=None)
+    return dict(workload="BSFA gated causal prefill", value=round(flops / (ms * 1e-3) / 1e12, 2), unit="TFLOP/s", ms=ms,
+                config={"B": 1, "Hq": Hq, "Hkv": 8, "S": S, "D": 128, "tile": 128,
+                        "skip_fraction_offdiag": round(skip, 4), "flops": flops,
+                        "algorithmic_units": f"QK on {causal_tiles} causal 128x128 tiles and PV on {kept} kept tiles, "
+                                             "2*128^3 flop each",
+                        "gated_ms": round(kms, 4), "ungated_ms": round(ungated_ms, 4),
+                        "gated_speedup": round(ungated_ms / kms, 3), "calibration": calibration},
+                roofline=_roof("mfma", flops / (kms * 1e-3) / 1e12, "void bsa::gated_kernel<false>(bsa::GatedArgs)", kms))
 
 
 # ---------------------------------------------------------------------------
 # Workload 5: vertical-slash conversion + varlen prefill
 # ---------------------------------------------------------------------------
 
-def bench_vs(torch, bsa, args):
+def gpu_vs(torch, bsa, w, args):
     from synth import to_torch_bf16
-    from synth.workloads import vs_varlen_prefill
 
-    _log("generating vertical-slash inputs")
-    w = vs_varlen_prefill()
     dev = torch.device("cuda:0")
     q, k, v = (to_torch_bf16(w[n]).to(dev) for n in ("q", "k", "v"))
     sl = torch.from_numpy(w["seqlens"]).to(dev)
@@ -514,71 +717,25 @@ def bench_vs(torch, bsa, args):
     ams = timer.mean_ms("attention")
     cms = timer.mean_ms("convert")
     conv_bytes = int(4 * (bc.sum() + cc.sum() + bc.size + cc.size))
-    tf = flops / (ams * 1e-3) / 1e12
-    return dict(metric=METRIC, value=round(flops / (ms * 1e-3) / 1e12, 2), unit="TFLOP/s", ms_per_step=round(ms, 4),
-                dtype="bf16",
-                config={"workload": "vertical-slash conversion + varlen causal prefill", "seqlens": [65536, 32768],
-                        "H": 32, "D": 128, "block": 64, "nnz_v": 1000, "nnz_s": 2000, "flops": flops,
-                        "convert_ms": round(cms, 4), "convert_output_bytes": conv_bytes},
-                roofline={"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                          "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None, "kernel": "prefill_tile_kernel<2,2>",
-                          "avg_ms": round(ams, 4)},
-                cpu_baseline=None)
-
-
-# ---------------------------------------------------------------------------
-# Backward of the block-sparse prefill workload
-# ---------------------------------------------------------------------------
-
-def bench_backward(torch, bsa, args):
-    from synth import normal_bf16, to_torch_bf16
-    from synth.workloads import block_sparse_prefill
-
-    _log("generating block-sparse prefill inputs and an upstream gradient")
-    w = block_sparse_prefill()
-    dev = torch.device("cuda:0")
-    q, k, v = (to_torch_bf16(w[n]).to(dev) for n in ("q", "k", "v"))
-    do = to_torch_bf16(normal_bf16(1007, "do", w["q"].shape)).to(dev)
-    pat = bsa.BlockPattern(torch.from_numpy(w["count"]).to(dev), torch.from_numpy(w["index"]).to(dev), 128, 128)
-    out, lse = bsa.bsa_fwd(q, k, v, pat, causal=True, out_dtype=torch.bfloat16)
-    ws = torch.empty(bsa.bsa_bwd_workspace_size(q, k, pat, causal=True), dtype=torch.uint8, device=dev)
-
-    def call():
-        bsa.bsa_bwd(q, k, v, out, lse, do, pat, causal=True, workspace=ws)
-
-    def step(timer):
-        with timer.span("backward"):
-            call()
-
-    timer = Timer(torch)
-    ms = run_steps(torch, step, timer, args.steps, args.warmup)
-    bms = timer.mean_ms("backward")
-    tiles = int(w["count"].sum())
-    flops = tiles * 5 * 2 * 128 ** 3   # S (rebuilt), dP, dV, dQ, dK: five tile products
-    tf = flops / (bms * 1e-3) / 1e12
-    return dict(metric=METRIC, value=round(flops / (ms * 1e-3) / 1e12, 2), unit="TFLOP/s", ms_per_step=round(ms, 4),
-                dtype="bf16",
-                config={"workload": "block-sparse causal prefill backward (dQ, dK, dV)", "B": 1, "Hq": 32, "Hkv": 8,
-                        "S": 32768, "D": 128, "tile": 128, "visited_tiles": tiles, "flops": flops,
-                        "flops_note": "5 products of 2*128^3 per visited tile (S, dP, dV, dQ, dK); the dQ pass "
-                                      "rebuilds S and dP a second time: 7 executed"},
-                roofline={"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                          "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None,
-                          "kernel": "bsa_bwd (bwd_dkdv_kernel + bwd_dq_kernel<4> + list inversion)",
-                          "avg_ms": round(bms, 4)},
-                cpu_baseline=None)
+    return dict(workload="vertical-slash conversion + varlen causal prefill",
+                value=round(flops / (ms * 1e-3) / 1e12, 2), unit="TFLOP/s", ms=ms,
+                config={"seqlens": [65536, 32768], "H": 32, "D": 128, "block": 64, "nnz_v": 1000, "nnz_s": 2000,
+                        "flops": flops, "attention_ms": round(ams, 4), "convert_ms": round(cms, 4),
+                        "convert_output_bytes": conv_bytes,
+                        "convert_gbs": round(conv_bytes / (cms * 1e-3) / 1e9, 1),
+                        "algorithmic_units": "per (sequence, head, 64-row query block): 4*64*128*(64*block_count + "
+                                             "column_count) flop over its windows and columns"},
+                roofline=_roof("mfma", flops / (ams * 1e-3) / 1e12, "void bsa::prefill_tile_kernel<2, 2>(bsa::PrefillArgs)",
+                               ams))
 
 
 # ---------------------------------------------------------------------------
 # Selected attention (top-k key blocks per query token), the FSA module's example shape
 # ---------------------------------------------------------------------------
 
-def bench_selected(torch, bsa, args):
+def gpu_selected(torch, bsa, w, args):
     from synth import to_torch_bf16
-    from synth.workloads import selected_prefill
 
-    _log("generating selected-attention inputs")
-    w = selected_prefill()
     dev = torch.device("cuda:0")
     q, k, v = (to_torch_bf16(w[n]).to(dev) for n in ("q", "k", "v"))
     sel = torch.from_numpy(w["sel"]).to(dev)
@@ -622,17 +779,52 @@ def bench_selected(torch, bsa, args):
                  + chunks * 64 * 256 * 2                      # one K and V tile per chunk
                  + T * Hq * (topk * row + 128 * 2 + 4))       # combine: read partials, write O (bf16), LSE
     gbs = alg_bytes / (call_ms * 1e-3) / 1e9
-    return dict(metric=METRIC, value=round(flops / (ms * 1e-3) / 1e12, 2), unit="TFLOP/s", ms_per_step=round(ms, 4),
-                dtype="bf16",
-                config={"workload": "selected attention, top-k key blocks per query token (key-block-outer)",
-                        "seqlens": [int(x) for x in w["seqlens"]], "Hq": Hq, "Hkv": Hkv, "D": 128, "block": 64,
+    return dict(workload="selected attention, top-k key blocks per query token (key-block-outer)",
+                value=round(flops / (ms * 1e-3) / 1e12, 2), unit="TFLOP/s", ms=ms,
+                config={"seqlens": [int(x) for x in w["seqlens"]], "Hq": Hq, "Hkv": Hkv, "D": 128, "block": 64,
                         "topk": topk, "valid_pairs": pairs, "chunks": chunks, "flops": flops,
-                        "algorithmic_bytes": alg_bytes},
-                roofline={"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                          "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                          "kernel": "bsa_fwd_selected (index inversion, selected_kernel, combine)",
-                          "avg_ms": round(call_ms, 4)},
-                cpu_baseline=None)
+                        "algorithmic_bytes": alg_bytes,
+                        "algorithmic_units": "gathered Q rows, one K/V tile per chunk of 128/G tokens, float32 "
+                                             "partials written and read, bf16 O"},
+                roofline=_roof("hbm", gbs, "bsa_fwd_selected (index inversion, selected_kernel, combine_kernel)",
+                               call_ms))
+
+
+# ---------------------------------------------------------------------------
+# Backward of the block-sparse prefill workload
+# ---------------------------------------------------------------------------
+
+def gpu_backward(torch, bsa, w, args):
+    from synth import to_torch_bf16
+
+    dev = torch.device("cuda:0")
+    q, k, v = (to_torch_bf16(w[n]).to(dev) for n in ("q", "k", "v"))
+    do = to_torch_bf16(w["do"]).to(dev)
+    pat = bsa.BlockPattern(torch.from_numpy(w["count"]).to(dev), torch.from_numpy(w["index"]).to(dev), 128, 128)
+    out, lse = bsa.bsa_fwd(q, k, v, pat, causal=True, out_dtype=torch.bfloat16)
+    ws = torch.empty(bsa.bsa_bwd_workspace_size(q, k, pat, causal=True), dtype=torch.uint8, device=dev)
+
+    def step(timer):
+        with timer.span("backward"):
+            bsa.bsa_bwd(q, k, v, out, lse, do, pat, causal=True, workspace=ws)
+
+    timer = Timer(torch)
+    ms = run_steps(torch, step, timer, args.steps, args.warmup)
+    bms = timer.mean_ms("backward")
+    tiles = int(w["count"].sum())
+    flops = tiles * 5 * 2 * 128 ** 3   # S (rebuilt), dP, dV, dQ, dK: five tile products
+    return dict(workload="block-sparse causal prefill backward (dQ, dK, dV)",
+                value=round(flops / (ms * 1e-3) / 1e12, 2), unit="TFLOP/s", ms=ms,
+                config={"B": 1, "Hq": 32, "Hkv": 8, "S": 32768, "D": 128, "tile": 128, "visited_tiles": tiles,
+                        "flops": flops,
+                        "algorithmic_units": "5 products of 2*128^3 per visited tile (S, dP, dV, dQ, dK); the dQ pass "
+                                             "rebuilds S and dP a second time: 7 executed"},
+                roofline=_roof("mfma", flops / (bms * 1e-3) / 1e12,
+                               "bsa_bwd (bwd_dkdv_kernel + bwd_dq_kernel<4> + list inversion)", bms))
+
+
+GPU = {1: gpu_tiny, 2: gpu_spec_decode, 3: gpu_block_prefill, 4: gpu_gated, 5: gpu_vs, 6: gpu_selected,
+       7: gpu_backward}
 
 
 def main():
@@ -645,11 +837,9 @@ def main():
 
     import long_context_attention_sparse_amd as bsa
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    bsa.load()
     if args.copy_calibration:
+        if not torch.cuda.is_available():
+            sys.exit("bench.py needs a GPU")
         n = 1 << 30
         src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
         dst = torch.empty_like(src)
@@ -659,14 +849,54 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "copies": 4}), flush=True)
         return
-    fn = {1: bench_tiny, 2: bench_spec_decode, 3: bench_block_prefill, 4: bench_gated, 5: bench_vs,
-          6: bench_selected, 7: bench_backward}[args.config]
-    res = fn(torch, bsa, args)
-    line = {"metric": res["metric"], "value": res["value"], "unit": res["unit"], "n_gpus": 1, "steps": args.steps,
-            "warmup": args.warmup, "ms_per_step": res["ms_per_step"],
-            "higher_is_better": res.get("higher_is_better", True), "scaling": "weak", "vs_baseline": None,
-            "dtype": res["dtype"], "data": "synthetic", "config": res["config"], "roofline": res["roofline"],
-            "cpu_baseline": res["cpu_baseline"]}
+    configs = [args.config] if args.config else list(ALL_CONFIGS)
+
+    # ---- phase 1: inputs and the oracle's CPU baseline (the GPU is not touched yet) ----
+    work = {}
+    cpu = {}
+    cores = cpu_cores()
+    for c in configs:
+        w = work[3] if c == 7 and 3 in work else None
+        if w is not None:
+            from synth import normal_bf16
+
+            w = dict(w)
+            w["do"] = normal_bf16(1007, "do", w["q"].shape)
+        work[c] = w if w is not None else generate(c)
+        if not args.no_cpu_baseline:
+            t0 = time.perf_counter()
+            cpu[c] = cpu_baseline(c, work[c], args.cpu_seconds, cores)
+            _log(f"workload {c}: oracle sample {cpu[c]['value']} {cpu[c]['unit']} ({time.perf_counter() - t0:.1f} s)")
+
+    # ---- phase 2: the GPU ----
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    bsa.load()
+    res = {}
+    for c in configs:
+        _log(f"workload {c}: timing on the GPU")
+        res[c] = GPU[c](torch, bsa, work[c], args)
+        res[c]["cpu_baseline"] = cpu.get(c)
+        free(torch)
+        _log(f"workload {c}: {res[c]['value']} {res[c]['unit']}, {res[c]['ms']:.4f} ms per call")
+
+    head = HEADLINE if HEADLINE in res else configs[0]
+    r = res[head]
+    cfg = {"workload": r["workload"], **r["config"]}
+    if len(configs) > 1:
+        cfg["headline"] = f"workload {head} ({r['workload']})"
+        cfg["per_config"] = {
+            str(c): {"workload": res[c]["workload"], "ms_per_call": round(res[c]["ms"], 4), "value": res[c]["value"],
+                     "unit": res[c]["unit"], "higher_is_better": res[c].get("higher_is_better", True),
+                     "kernel": res[c]["roofline"]["kernel"], "config": res[c]["config"],
+                     "roofline": res[c]["roofline"], "cpu_baseline": res[c]["cpu_baseline"]}
+            for c in configs}
+    line = {"metric": METRIC, "value": r["value"], "unit": r["unit"], "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(r["ms"], 4),
+            "higher_is_better": r.get("higher_is_better", True), "scaling": "weak", "vs_baseline": None,
+            "dtype": "bf16", "data": "synthetic", "config": cfg, "roofline": r["roofline"],
+            "cpu_baseline": r["cpu_baseline"]}
     print(json.dumps(line), flush=True)
 
 
