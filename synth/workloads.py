@@ -167,17 +167,20 @@ def thresholds_from_tile_max(tmax_row: np.ndarray, i: int, min_gap: float = 2e-2
 
 def vs_varlen_prefill(seed: int = 1005, seqlens=(65536, 32768), H: int = 32, D: int = 128,
                       nnz_v: int = 1000, nnz_s: int = 2000, block: int = 64,
-                      context_size: int | None = None) -> dict:
+                      context_size: int | None = None, with_tensors: bool = True) -> dict:
     """Packed varlen Q/K/V ``[total, H, D]``; per (b, h) ``nnz_v`` vertical key indices
     (ascending) and ``nnz_s`` slash offsets (descending), power-law sampled with 0 forced.
-    A slash offset s marks the diagonal key = query + (kv_len - q_len) - s."""
+    A slash offset s marks the diagonal key = query + (kv_len - q_len) - s.
+    ``with_tensors=False`` leaves Q/K/V out (None); the indices are the same either way."""
     seqlens = [int(s) for s in seqlens]
     B = len(seqlens)
     total = int(sum(seqlens))
     cu = np.concatenate([[0], np.cumsum(seqlens)]).astype(np.int32)
-    q = normal_bf16(seed, "q", (total, H, D))
-    k = normal_bf16(seed, "k", (total, H, D))
-    v = normal_bf16(seed, "v", (total, H, D))
+    q = k = v = None
+    if with_tensors:
+        q = normal_bf16(seed, "q", (total, H, D))
+        k = normal_bf16(seed, "k", (total, H, D))
+        v = normal_bf16(seed, "v", (total, H, D))
     vert = np.zeros((B, H, nnz_v), np.int32)
     slash = np.zeros((B, H, nnz_s), np.int32)
     for b in range(B):

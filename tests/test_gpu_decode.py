@@ -148,27 +148,29 @@ def spec_full():
     return w
 
 
-def test_speculative_full_size_sampled(spec_full):
-    """Full workload in the benchmark's launch configuration; sampled (b, kv head) groups
-    recomputed by the oracle."""
+def test_speculative_full_size_every_group(spec_full):
+    """Full workload in the benchmark's launch configuration; every (b, kv head) group (all
+    1024 query rows) recomputed by the oracle."""
     w = spec_full
     say("speculative+sparse full size")
     s0 = w["spec_start"]
-    missed = bsa.BlockPattern(dev_i32(np.full((32, 8, 1), w["missed"].shape[-1], np.int32)),
-                              dev_i32(w["missed"][:, :, None, :]), 128, 64)
+    n = w["missed"].shape[-1]
+    missed = bsa.BlockPattern(dev_i32(np.full((32, 8, 1), n, np.int32)), dev_i32(w["missed"][:, :, None, :]), 128, 64)
     o, lse = bsa.speculative_sparse(w["dq"], w["dk"][:, s0:], w["dv"][:, s0:], w["dk"], w["dv"], missed,
                                     out_dtype=torch.float32)
     oh, lh = host(o), host(lse)
     G = 4
-    for b, hkv in [(0, 0), (5, 3), (17, 7), (31, 1), (31, 6)]:
-        hs = slice(hkv * G, (hkv + 1) * G)
-        n = w["missed"].shape[-1]
-        o_ref, lse_ref = oracle.speculative_sparse(
-            w["q"][b:b + 1, :, hs], w["k"][b:b + 1, s0:, hkv:hkv + 1], w["v"][b:b + 1, s0:, hkv:hkv + 1],
-            w["k"][b:b + 1, :, hkv:hkv + 1], w["v"][b:b + 1, :, hkv:hkv + 1], np.full((1, 1, 1), n, np.int32),
-            w["missed"][b:b + 1, hkv:hkv + 1, None, :], 64, causal_spec=True)
-        check_o(oh[b:b + 1, :, hs], o_ref, f"full b={b} hkv={hkv}")
-        check_lse(lh[b:b + 1, hs], lse_ref, f"full lse b={b} hkv={hkv}")
+    o_ref = np.zeros_like(oh)
+    lse_ref = np.zeros_like(lh)
+    for b in range(32):
+        for hkv in range(8):
+            hs = slice(hkv * G, (hkv + 1) * G)
+            o_ref[b:b + 1, :, hs], lse_ref[b:b + 1, hs] = oracle.speculative_sparse(
+                w["q"][b:b + 1, :, hs], w["k"][b:b + 1, s0:, hkv:hkv + 1], w["v"][b:b + 1, s0:, hkv:hkv + 1],
+                w["k"][b:b + 1, :, hkv:hkv + 1], w["v"][b:b + 1, :, hkv:hkv + 1], np.full((1, 1, 1), n, np.int32),
+                w["missed"][b:b + 1, hkv:hkv + 1, None, :], 64, causal_spec=True)
+    check_o(oh, o_ref, "full size, all 256 groups")
+    check_lse(lh, lse_ref, "full size lse, all 256 groups")
 
 
 @pytest.mark.parametrize("Sq,causal_spec", [(1, True), (8, True), (3, False)])

@@ -122,22 +122,21 @@ def cfg3():
     return w
 
 
-def test_block_sparse_full_size_sampled(cfg3):
+def test_block_sparse_full_size(cfg3):
+    """Every row of 16 query blocks across the heads, the first and last blocks included."""
     w = cfg3
     say("block-sparse prefill full size")
     pat = bsa.BlockPattern(dev_i32(w["count"]), dev_i32(w["index"]), 128, 128)
     o, lse = bsa.bsa_fwd(w["dq"], w["dk"], w["dv"], pat, causal=True, out_dtype=torch.float32)
-    torch.cuda.synchronize()
+    oh, lh = host(o), host(lse)
     scale = 1.0 / np.sqrt(128)
-    g = rng(3, "sample")
-    for h, i in [(0, 255), (31, 0), (7, 1), (19, 33), (12, 200), (25, 128)]:
-        rows = np.sort(g.choice(np.arange(i * 128, (i + 1) * 128), 6, replace=False))
+    blocks = [(0, 255), (31, 255), (31, 0), (7, 1), (19, 33), (12, 200), (25, 128), (3, 34), (4, 35),
+              (5, 254), (8, 100), (13, 64), (16, 17), (22, 240), (27, 2), (30, 190)]
+    for h, i in blocks:
+        rows = np.arange(i * 128, (i + 1) * 128)
         ents = w["index"][0, h, i, :w["count"][0, h, i]]
-        hk = h // 4
-        keysets = []
-        for r in rows:
-            ks = np.concatenate([np.arange(j * 128, (j + 1) * 128) for j in ents])
-            keysets.append(ks[ks <= r])
-        o_ref, lse_ref = oracle.attend_rows(w["q"][0, rows, h], w["k"][0, :, hk], w["v"][0, :, hk], keysets, scale)
-        check_o(host(o[0, rows, h]), o_ref, f"full h={h} i={i}")
-        check_lse(host(lse[0, h, rows]), lse_ref, f"full lse h={h} i={i}")
+        ks = np.concatenate([np.arange(j * 128, (j + 1) * 128) for j in ents])
+        o_ref, lse_ref = oracle.attend_rows(w["q"][0, rows, h], w["k"][0, :, h // 4], w["v"][0, :, h // 4],
+                                            [ks[ks <= r] for r in rows], scale)
+        check_o(oh[0, rows, h], o_ref, f"full h={h} i={i}")
+        check_lse(lh[0, h, rows], lse_ref, f"full lse h={h} i={i}")

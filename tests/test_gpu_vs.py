@@ -1,15 +1,19 @@
 """GPU parity for vertical-slash conversion (bit-exact counts and valid prefixes) and varlen
-attention over the converted metadata, at small size (everything) and full size (sampled query
-blocks and rows)."""
+attention over the converted metadata, at small size (everything) and full size (every
+conversion item; every row of sampled query blocks)."""
+import os
+
 import numpy as np
 import pytest
 import torch
 
 import long_context_attention_sparse_amd as bsa
 import oracle
-from synth import rng
 from synth.workloads import vs_varlen_prefill
+from tests.golden.make_full_size import vs_digest
 from tests.gpu_util import check_lse, check_o, dev_bf16, dev_i32, host, say
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "full_size.npz")
 
 pytestmark = [pytest.mark.gpu, pytest.mark.filterwarnings("ignore::RuntimeWarning")]
 
@@ -20,8 +24,8 @@ def _convert(w):
                                   w["block_M"], w["block_N"])
 
 
-def _check_items(gpu, w, items):
-    bc, bo, cc, ci = (x.cpu().numpy() for x in gpu)
+def _check_items(gpu, w, items, host_arrays=False):
+    bc, bo, cc, ci = gpu if host_arrays else (x.cpu().numpy() for x in gpu)
     for b, h, m in items:
         L = int(w["seqlens"][b])
         wins, cols = oracle.vs_convert_item(L, L, w["vertical"][b, h], w["slash"][b, h], m, w["block_M"], w["block_N"])
@@ -113,24 +117,41 @@ def cfg5():
     return w
 
 
-def test_full_size_convert_and_attention_sampled(cfg5):
+def test_full_size_convert_every_item(cfg5):
+    """All 65,536 (sequence, head, query block) items of the conversion, bit-exact: each
+    (sequence, head) row's counts and valid prefixes are digested and compared with the oracle's
+    (stored by tests/golden/make_full_size.py); a differing row is then walked item by item."""
     w = cfg5
-    say("vs convert full size")
-    gpu = _convert(w)
-    g = rng(5, "items")
-    items = [(int(g.integers(0, 2)), int(g.integers(0, 32)), int(g.integers(0, 1024))) for _ in range(300)]
-    items += [(0, 0, 1023), (1, 31, 511), (1, 5, 512), (1, 5, 1023), (0, 17, 0)]
-    _check_items(gpu, w, items)
+    gold = np.load(GOLDEN, allow_pickle=False)["vs_sha"]
+    say("vs convert full size, every item")
+    bc, bo, cc, ci = (x.cpu().numpy() for x in _convert(w))
+    assert bc.shape == (2, 32, 1024) and bo.shape == (2, 32, 1024, 2000) and ci.shape == (2, 32, 1024, 1000)
+    bad = [(b, h) for b in range(2) for h in range(32) if vs_digest(bc[b, h], bo[b, h], cc[b, h], ci[b, h]).encode()
+           != gold[b, h]]
+    if bad:
+        b, h = bad[0]
+        _check_items((bc, bo, cc, ci), w, [(b, h, m) for m in range(1024)], host_arrays=True)
+        raise AssertionError(f"conversion digests differ for (sequence, head) rows {bad}")
+    assert (bc[1, :, 512:] == 0).all() and (cc[1, :, 512:] == 0).all()
+    print(f"[parity] vs conversion full size: 65536 items bit-exact, {int(bc.sum())} windows, "
+          f"{int(cc.sum())} columns", flush=True)
+
+
+def test_full_size_attention(cfg5):
+    """Every row of 12 query blocks of the varlen attention over the converted metadata: both
+    sequences, first, middle and last blocks, several heads."""
+    w = cfg5
     say("vs attention full size")
-    bc, bo, cc, ci = gpu
+    bc, bo, cc, ci = _convert(w)
     pat = bsa.VSPattern(bc, bo, cc, ci, 64, 64)
     cu = dev_i32(w["cu_seqlens"])
     o, lse = bsa.bsa_fwd(w["dq"], w["dk"], w["dv"], pat, causal=True, out_dtype=torch.float32, cu_seqlens_q=cu,
                          cu_seqlens_k=cu, max_seqlen_q=65536, max_seqlen_k=65536)
     oh, lh = host(o), host(lse)
-    for b, h, m in [(0, 3, 1023), (1, 30, 511), (0, 11, 400), (1, 0, 0), (0, 20, 7)]:
+    for b, h, m in [(0, 3, 1023), (1, 30, 511), (0, 11, 400), (1, 0, 0), (0, 20, 7), (0, 31, 0), (1, 16, 256),
+                    (0, 0, 1022), (1, 9, 510), (0, 25, 640), (1, 4, 100), (0, 14, 900)]:
         L = int(w["seqlens"][b])
-        rows = np.sort(g.choice(np.arange(m * 64, min(L, m * 64 + 64)), 4, replace=False))
+        rows = np.arange(m * 64, min(L, m * 64 + 64))
         wins, cols = oracle.vs_convert_item(L, L, w["vertical"][b, h], w["slash"][b, h], m, 64, 64)
         o_ref, lse_ref = oracle.vs_attention_rows(w["q"], w["k"], w["v"], b, h, rows, wins, cols, w["cu_seqlens"],
                                                   w["cu_seqlens"], 64)
