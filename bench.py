@@ -646,9 +646,16 @@ def gpu_gated(torch, bsa, w, args):
     kept = int(km[..., lower].sum())
     causal_tiles = Hq * int(lower.sum())
     flops = causal_tiles * 2 * 128 ** 3 + kept * 2 * 128 ** 3
+    def step_count(timer):
+        with timer.span("count"):
+            bsa.bsa_fwd_gated(q, k, v, Td, out=out, return_mask=False, skipped="count")
+
     timer2 = Timer(torch)
     run_steps(torch, step_dense, timer2, max(3, args.steps // 4), 2)
     ungated_ms = timer2.mean_ms("ungated")
+    timer5 = Timer(torch)
+    run_steps(torch, step_count, timer5, max(3, args.steps // 4), 2)
+    count_ms = timer5.mean_ms("count")
     off = lower & ~np.eye(nqb, dtype=bool)
     skip = 1.0 - float(km[..., off].mean())
 
@@ -681,7 +688,11 @@ def gpu_gated(torch, bsa, w, args):
                         "algorithmic_units": f"QK on {causal_tiles} causal 128x128 tiles and PV on {kept} kept tiles, "
                                              "2*128^3 flop each",
                         "gated_ms": round(kms, 4), "ungated_ms": round(ungated_ms, 4),
-                        "gated_speedup": round(ungated_ms / kms, 3), "calibration": calibration},
+                        "gated_speedup": round(ungated_ms / kms, 3),
+                        "skipped_counted_ms": round(count_ms, 4),
+                        "skipped_counted_note": "the other reading of a skipped tile: its scores stay in the "
+                                                "softmax maximum and normaliser (the timed line drops them)",
+                        "calibration": calibration},
                 roofline=_roof("mfma", flops / (kms * 1e-3) / 1e12, "void bsa::gated_kernel<false>(bsa::GatedArgs)", kms))
 
 

@@ -280,23 +280,37 @@ size_t bsa_speculative_workspace_size(const bsa_problem* prob, int32_t Sk_spec, 
 bsa_status bsa_combine(int32_t P, int32_t B, int32_t Hq, int32_t Sq, int32_t D, const float* o_part,
                        const float* lse_part, bsa_tensor o, float* lse, bsa_stream stream);
 
+/* What a skipped tile leaves in the softmax of bsa_fwd_gated.  [BSFA]
+ * Figure 2 names what a skipped block avoids (the V_j load and the P V_j
+ * product) and nothing else, so the tile's scores, computed for its maximum,
+ * may or may not feed the running maximum and normaliser:
+ *   BSA_GATE_DROP_SKIPPED   left out altogether: the result is attention over
+ *                           the kept tiles only (block-sparse attention on the
+ *                           kept set);
+ *   BSA_GATE_COUNT_SKIPPED  kept in the maximum and the normaliser, no value:
+ *                           attention over every causal key with the value
+ *                           rows of skipped tiles taken as zero (LSE is then
+ *                           the dense causal LSE). */
+typedef enum { BSA_GATE_DROP_SKIPPED = 0, BSA_GATE_COUNT_SKIPPED = 1 } bsa_gate_skipped;
+
 /* BSFA gated causal attention.  [BSFA] Abstract and Figure 2: for query
  * block i and key block j < i the exact tile maximum
  * t(i,j) = max over the tile of scale*<q, k> is computed inside the tile loop
  * and the tile is kept iff t(i,j) >= T[b, h, i] (compared in float32);
  * the diagonal tile always runs; a skipped tile loads no V and does no P V
- * product, and its scores are left out of the softmax altogether.
+ * product; its scores enter the softmax or not as `skipped` says.
  *   T          float32 [B, Hq, nQB] thresholds (-inf keeps every tile).
  *   block_M/N  tile sizes; both 128.  Needs Sq == Sk, causal, fixed length,
  *              Sq % 128 == 0.
+ *   skipped    bsa_gate_skipped (anything else: BSA_ERR_INVALID_ARG).
  *   keep_mask  optional uint8 [B, Hq, nQB, nKB]: 1 kept, 0 skipped, for
  *              j <= i (entries j > i are not written).
  *   tile_max   optional float32 [B, Hq, nQB, nKB]: t(i, j) for j <= i
  *              (the diagonal tile's maximum over its causal entries).
  * Errors as for bsa_fwd; BSA_ERR_UNSUPPORTED outside the cases above. */
 bsa_status bsa_fwd_gated(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, bsa_tensor v, const float* T,
-                         int32_t block_M, int32_t block_N, bsa_tensor o, float* lse, uint8_t* keep_mask,
-                         float* tile_max, bsa_stream stream);
+                         int32_t block_M, int32_t block_N, int32_t skipped, bsa_tensor o, float* lse,
+                         uint8_t* keep_mask, float* tile_max, bsa_stream stream);
 
 /* Backward of block-sparse attention: dQ, dK, dV.  The pages name a
  * backward pass ([IR] keeps FA's backward; [FSA] and FlagAttention list

@@ -22,6 +22,7 @@ BSA_OK, BSA_ERR_INVALID_ARG, BSA_ERR_UNSUPPORTED, BSA_ERR_WORKSPACE, BSA_ERR_HIP
 BSA_BF16, BSA_F32 = 0, 1
 BSA_PAT_DENSE, BSA_PAT_BLOCK, BSA_PAT_VS = 0, 1, 2
 NOALLOC_SCRATCH_BYTES = 16 << 20   # BSA_NOALLOC_SCRATCH_BYTES of include/bsa.h
+GATE_SKIPPED = {"drop": 0, "count": 1}   # bsa_gate_skipped
 
 EXPORTS = ("bsa_status_string", "bsa_workspace_size", "bsa_fwd", "bsa_fwd_partials", "bsa_num_partials",
            "bsa_speculative_sparse", "bsa_speculative_sparse_noalloc", "bsa_speculative_partials", "bsa_speculative_num_partials",
@@ -99,8 +100,8 @@ def load(path: str = LIB_PATH):
                                                       ctypes.c_void_p]
     lib.bsa_fwd_gated.restype = ctypes.c_int
     lib.bsa_fwd_gated.argtypes = [ctypes.POINTER(_Problem), _Tensor, _Tensor, _Tensor, ctypes.c_void_p,
-                                  ctypes.c_int32, ctypes.c_int32, _Tensor, ctypes.c_void_p, ctypes.c_void_p,
-                                  ctypes.c_void_p, ctypes.c_void_p]
+                                  ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _Tensor, ctypes.c_void_p,
+                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     lib.bsa_selected_workspace_size.restype = ctypes.c_size_t
     lib.bsa_selected_workspace_size.argtypes = [ctypes.POINTER(_Problem), ctypes.c_int32, ctypes.c_int32,
                                                 ctypes.c_int32]
@@ -355,9 +356,13 @@ def bsa_combine(o_part: torch.Tensor, lse_part: torch.Tensor, *, out: Optional[t
 
 
 def bsa_fwd_gated(q, k, v, T: torch.Tensor, *, block_M: int = 128, block_N: int = 128, softmax_scale=None,
-                  out: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.bfloat16,
+                  skipped: str = "drop", out: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.bfloat16,
                   return_mask: bool = True, return_tile_max: bool = False, stream=None):
-    """BSFA gated causal attention.  Returns (out, lse, keep_mask or None, tile_max or None)."""
+    """BSFA gated causal attention.  ``skipped``: "drop" (a skipped tile's scores are left out of
+    the softmax) or "count" (they stay in the maximum and normaliser; only V and P V are skipped).
+    Returns (out, lse, keep_mask or None, tile_max or None)."""
+    if skipped not in GATE_SKIPPED:
+        raise ValueError(f"skipped must be one of {sorted(GATE_SKIPPED)}")
     lib = load()
     prob = _problem(q, k, True, softmax_scale)
     B, S, Hq, D = q.shape
@@ -374,7 +379,7 @@ def bsa_fwd_gated(q, k, v, T: torch.Tensor, *, block_M: int = 128, block_N: int 
     if T.dtype != torch.float32 or not T.is_contiguous():
         raise ValueError("T must be contiguous float32 [B, Hq, nQB] (or [Hq, nQB])")
     st = lib.bsa_fwd_gated(ctypes.byref(prob), _tensor(q), _tensor(k), _tensor(v), _ptr(T), block_M, block_N,
-                           _tensor(out), _ptr(lse), _ptr(keep), _ptr(tmax), _stream(stream))
+                           GATE_SKIPPED[skipped], _tensor(out), _ptr(lse), _ptr(keep), _ptr(tmax), _stream(stream))
     _check("bsa_fwd_gated", st)
     return out, lse, keep, tmax
 

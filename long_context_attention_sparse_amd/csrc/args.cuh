@@ -89,6 +89,7 @@ struct GatedArgs {
   int B, Hq, Hkv, G, S, nqb;
   float scale, scale_log2;
   int n_items;
+  int count_skipped;   // 1: a skipped tile's scores stay in the running maximum and normalisers
 };
 
 // Selected attention (top-k key blocks per query token, key-block-outer).  Tokens are

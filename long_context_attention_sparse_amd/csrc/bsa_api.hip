@@ -369,12 +369,13 @@ bsa_status bsa_combine(int32_t P, int32_t B, int32_t Hq, int32_t Sq, int32_t D, 
 }
 
 bsa_status bsa_fwd_gated(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, bsa_tensor v, const float* T,
-                         int32_t block_M, int32_t block_N, bsa_tensor o, float* lse, uint8_t* keep_mask,
-                         float* tile_max, bsa_stream stream) {
+                         int32_t block_M, int32_t block_N, int32_t skipped, bsa_tensor o, float* lse,
+                         uint8_t* keep_mask, float* tile_max, bsa_stream stream) {
   bsa_status st = check_problem(prob, q, k, v, o);
   if (st != BSA_OK) return st;
   const bsa_problem& p = *prob;
   if (!T) return BSA_ERR_INVALID_ARG;
+  if (skipped != BSA_GATE_DROP_SKIPPED && skipped != BSA_GATE_COUNT_SKIPPED) return BSA_ERR_INVALID_ARG;
   if (block_M != 128 || block_N != 128 || p.D != 128) return BSA_ERR_UNSUPPORTED;
   if (!p.causal || p.cu_seqlens_q || p.Sq != p.Sk || p.Sq % 128) return BSA_ERR_UNSUPPORTED;
   if (p.softcap > 0.f) return BSA_ERR_UNSUPPORTED;
@@ -395,6 +396,7 @@ bsa_status bsa_fwd_gated(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, bs
   a.nqb = p.Sq / 128;
   a.scale = scale_of(p);
   a.scale_log2 = a.scale * kLog2e;
+  a.count_skipped = skipped == BSA_GATE_COUNT_SKIPPED;
   const int64_t items = (int64_t)p.B * p.Hq * a.nqb;
   if (items > INT_MAX) return BSA_ERR_UNSUPPORTED;
   a.n_items = (int)items;

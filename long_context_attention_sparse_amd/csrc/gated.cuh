@@ -4,8 +4,11 @@
 // score tile S_ij with MFMA, takes its exact maximum t(i,j) (lane max, wave
 // shuffle reduce, one LDS exchange between the four waves) and keeps the tile
 // iff j == i or scale * t(i,j) >= T[b, h, i].  Only kept tiles load V_j and
-// run the softmax update and P V product; a skipped tile's scores never enter
-// the softmax and its V is never requested.
+// run the P V product; V of a skipped tile is never requested.  The figure
+// leaves open what a skipped tile's scores do to the softmax, so both readings
+// run: by default they never enter it (the result is attention over the kept
+// tiles); with count_skipped they still update the running maximum and the
+// normalisers (only the V_j load and the product are skipped).
 //
 // Workgroup: 4 waves x 32 query rows (BM = 128), 128-key tiles.  K and V go
 // straight from global memory into LDS (global_load_lds_dwordx4, the swizzled
@@ -14,7 +17,8 @@
 //   [K_j resident] S_ij (8 MFMAs per 32-key block), diagonal mask, tile max
 //   -> LDS exchange + barrier (every wave is done with K_j) -> keep decision
 //   -> kept tiles: issue V_j, softmax update and P, wait, barrier, issue K_next, PV;
-//      skipped tiles: issue K_next -> wait for K_next -> barrier,
+//      skipped tiles: issue K_next (count_skipped: softmax update) -> wait for K_next
+//      -> barrier,
 // so V_j streams in during the softmax and the next K tile during the PV product (kept
 // tiles) or right after the decision (skipped tiles).  (A workgroup-scope barrier waits for
 // every outstanding load, so K_next is issued after the V barrier, not
@@ -26,7 +30,9 @@ namespace bsa {
 
 // CALIB: the threshold-calibration pass — the same S tiles and tile maxima, written to
 // a.tmax, with no tile kept: no V load, no P V product and no output.
-template <bool CALIB>
+// COUNT: a skipped tile's scores still update the running maximum and the normalisers
+// (a separate instantiation, so the default one keeps its register allocation).
+template <bool CALIB, bool COUNT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void gated_kernel(GatedArgs a) {
   constexpr int D = TD;
   constexpr int BN = 128;
@@ -106,6 +112,46 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
 
   auto tile_of = [&](int n) { return n == 0 ? i : n - 1; };  // diagonal first
 
+  // Online softmax over one tile: the running maximum (lazy rescale), the weights packed to
+  // bf16 as the P^T operand, their rounded sum (normalises O) and exact sum (LSE).
+  auto weights = [&](const f32x16* sc, uint32_t (*pk)[8], float& psum, float& pesum)
+                     __attribute__((always_inline)) {
+    softmax_max_n<NB>(sc, a.scale_log2, m_run, l_run, le_run, oacc);
+    const float m_use = m_run == kNegInf ? 0.f : m_run;
+    psum = 0.f;
+    pesum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 4) {
+        const float p0 = exp2_fast(fmaf(sc[kb][r], a.scale_log2, -m_use));
+        const float p1 = exp2_fast(fmaf(sc[kb][r + 1], a.scale_log2, -m_use));
+        const float p2 = exp2_fast(fmaf(sc[kb][r + 2], a.scale_log2, -m_use));
+        const float p3 = exp2_fast(fmaf(sc[kb][r + 3], a.scale_log2, -m_use));
+        pk[kb][r / 2] = pack_bf16x2(p0, p1);
+        pk[kb][r / 2 + 1] = pack_bf16x2(p2, p3);
+        psum = bf16x2_sum_acc(pk[kb][r / 2], psum);
+        psum = bf16x2_sum_acc(pk[kb][r / 2 + 1], psum);
+        pesum += (p0 + p1) + (p2 + p3);
+      }
+  };
+  // O^T += V_j^T P^T, the V^T operand read with the transposing LDS read
+  auto pv = [&](const uint32_t (*pk)[8]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        const int ks = kb * 2 + hb;
+        const u32x4 pb = {pk[kb][hb * 4], pk[kb][hb * 4 + 1], pk[kb][hb * 4 + 2], pk[kb][hb * 4 + 3]};
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const u32x2 lo = ds_read_tr16(Vt + ks * 16 * RS + voff[db]);
+          const u32x2 hi = ds_read_tr16(Vt + (ks * 16 + 8) * RS + voff[db]);
+          oacc[db] = mfma32x32x16(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), as_bf16x8(pb), oacc[db]);
+        }
+      }
+  };
+
   issue_k(tile_of(0) * BN);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -150,44 +196,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
       if (a.tmax) a.tmax[mask_row + j] = tile_max;
     }
     const bool more = n < i;
-    if (keep) {
+    if constexpr (COUNT && !CALIB) {
+      // every tile's scores enter the maximum and the normalisers; a kept tile's V_j
+      // (or, for a skipped tile, K_next) streams in during the softmax update
+      if (keep) issue_v(j * BN);
+      else if (more) issue_k(tile_of(n + 1) * BN);
+      uint32_t pk[NB][8];
+      float psum, pesum;
+      weights(s, pk, psum, pesum);
+      le_run += pesum;
+      if (keep) {
+        __builtin_amdgcn_s_waitcnt(0);
+        // V_j from every wave is in LDS; K_next streams in during the P V product
+        __syncthreads();
+        if (more) issue_k(tile_of(n + 1) * BN);
+        pv(pk);
+        l_run += psum;
+      } else {
+        l_run += pesum;  // a skipped tile's weights multiply no V row: the exact sum
+      }
+    } else if (keep) {
       issue_v(j * BN);
       // the softmax update and P run while V_j streams in
-      softmax_max_n<NB>(s, a.scale_log2, m_run, l_run, le_run, oacc);
-      const float m_use = m_run == kNegInf ? 0.f : m_run;
-      float psum = 0.f, pesum = 0.f;
       uint32_t pk[NB][8];
-#pragma unroll
-      for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; r += 4) {
-          const float p0 = exp2_fast(fmaf(s[kb][r], a.scale_log2, -m_use));
-          const float p1 = exp2_fast(fmaf(s[kb][r + 1], a.scale_log2, -m_use));
-          const float p2 = exp2_fast(fmaf(s[kb][r + 2], a.scale_log2, -m_use));
-          const float p3 = exp2_fast(fmaf(s[kb][r + 3], a.scale_log2, -m_use));
-          pk[kb][r / 2] = pack_bf16x2(p0, p1);
-          pk[kb][r / 2 + 1] = pack_bf16x2(p2, p3);
-          psum = bf16x2_sum_acc(pk[kb][r / 2], psum);
-          psum = bf16x2_sum_acc(pk[kb][r / 2 + 1], psum);
-          pesum += (p0 + p1) + (p2 + p3);
-        }
+      float psum, pesum;
+      weights(s, pk, psum, pesum);
       __builtin_amdgcn_s_waitcnt(0);
       // V_j from every wave is in LDS; K_next streams in during the P V product
       __syncthreads();
       if (more) issue_k(tile_of(n + 1) * BN);
-#pragma unroll
-      for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
-          const int ks = kb * 2 + hb;
-          const u32x4 pb = {pk[kb][hb * 4], pk[kb][hb * 4 + 1], pk[kb][hb * 4 + 2], pk[kb][hb * 4 + 3]};
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db) {
-            const u32x2 lo = ds_read_tr16(Vt + ks * 16 * RS + voff[db]);
-            const u32x2 hi = ds_read_tr16(Vt + (ks * 16 + 8) * RS + voff[db]);
-            oacc[db] = mfma32x32x16(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), as_bf16x8(pb), oacc[db]);
-          }
-        }
+      pv(pk);
       l_run += psum;
       le_run += pesum;
     } else if (more) {

@@ -36,8 +36,9 @@ void launch_prefill(const PrefillArgs& a, int NW, int KIND, hipStream_t st) {
 }
 
 void launch_gated(const GatedArgs& a, bool calib, hipStream_t st) {
-  if (calib) hipLaunchKernelGGL(gated_kernel<true>, dim3(a.n_items), dim3(256), 0, st, a);
-  else hipLaunchKernelGGL(gated_kernel<false>, dim3(a.n_items), dim3(256), 0, st, a);
+  if (calib) hipLaunchKernelGGL((gated_kernel<true, false>), dim3(a.n_items), dim3(256), 0, st, a);
+  else if (a.count_skipped) hipLaunchKernelGGL((gated_kernel<false, true>), dim3(a.n_items), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((gated_kernel<false, false>), dim3(a.n_items), dim3(256), 0, st, a);
 }
 
 }  // namespace bsa

@@ -18,8 +18,9 @@ Pinning (see the tests marked "not gpu"): every function here is checked
 against closed forms, invariants, brute force and an independent library
 routine.  Two readings have no such pin and say "parity unpinned" in their
 docstrings: the exact windows chosen by the vertical-slash conversion (own
-greedy rule; only its coverage invariants are pinned), and the treatment of
-skipped tiles' softmax mass in the gated variant (excluded).
+greedy rule; only its coverage invariants are pinned), and which of the two
+readings of a skipped tile's scores the gating page's own kernel takes (both
+are implemented, "drop" and "count", each pinned by its own closed forms).
 """
 from .backward import block_sparse_bwd
 from .core import (as_f64, attend_rows, block_mask, block_sparse, block_sparse_partials, causal_mask,

@@ -11,11 +11,22 @@ product.
 Readings (the page leaves these open):
 * Causal self-attention only (Sq == Sk), square tiles; tiles j > i are never
   visited.
-* A skipped tile's scores are excluded from the softmax entirely (from the
-  running maximum, from the normaliser and from P V), so the gated result is
-  exactly block-sparse attention over the kept tiles.  Parity unpinned: the
-  page does not say, and this is the reading under which "skip computation"
-  holds.  Pinned only through that equivalence.
+* What a skipped tile leaves in the softmax.  Figure 2 lists what a skipped
+  block avoids, the V_j load and the P V_j product, and says nothing of the
+  running maximum and normaliser, which the tile's scores (computed anyway for
+  s_max) could still feed.  Both readings are implemented (``skipped``):
+  - "drop" (default): the scores are left out altogether, so the gated result
+    is exactly block-sparse attention over the kept tiles (the top-k "value
+    blocks" of the Abstract are then the only blocks attended);
+  - "count": the literal reading of Figure 2, in which only the V_j load and the
+    product are skipped.  The tile's scores stay in the maximum and in the
+    normaliser, which is then attention over every causal key with the value
+    rows of skipped tiles taken as zero.  LSE is then the dense causal LSE
+    whatever the thresholds.
+  Which one the page's kernel runs is parity unpinned against the pages.  Each
+  is pinned through its own closed forms: "drop" equals block-sparse attention
+  over the kept tiles; "count" has the dense causal LSE, and its numerator
+  O*exp(LSE) equals that of "drop".
 * The scores are the scaled dot products scale*<q, k>; the comparison is taken
   in float32, the precision of the kernel: the exact float64 tile maximum is
   rounded to float32 and compared with the float32 threshold.
@@ -69,13 +80,21 @@ def _keep_row(t: np.ndarray, T: float, i: int) -> np.ndarray:
     return keep
 
 
-def gated(q, k, v, T, BM: int = 128, BN: int = 128, scale: float | None = None):
+def _skip_check(skipped: str) -> None:
+    if skipped not in ("drop", "count"):
+        raise ValueError('skipped must be "drop" or "count"')
+
+
+def gated(q, k, v, T, BM: int = 128, BN: int = 128, scale: float | None = None, skipped: str = "drop"):
     """Gated causal attention for small inputs.
 
     q [B,S,Hq,D], k/v [B,S,Hkv,D], T [B,Hq,nQB] (float32 thresholds).
+    skipped: "drop" (a skipped tile is left out of the softmax) or "count" (its scores stay
+    in the maximum and the normaliser, its values do not enter O).
     Returns O [B,S,Hq,D], LSE [B,Hq,S], keep [B,Hq,nQB,nKB] (uint8, 0 above the
     diagonal) and tmax [B,Hq,nQB,nKB] (float64, NaN above the diagonal).
     """
+    _skip_check(skipped)
     B, S, Hq, D = np.asarray(q).shape
     Hkv = np.asarray(k).shape[2]
     _check(S, np.asarray(k).shape[1], BM, BN)
@@ -97,19 +116,35 @@ def gated(q, k, v, T, BM: int = 128, BN: int = 128, scale: float | None = None):
                 tmax[b, h, i, :i + 1] = t
                 kr = _keep_row(t, T[b, h, i], i)
                 keep[b, h, i, :i + 1] = kr
+                if skipped == "count":
+                    rows = np.arange(i * BM, (i + 1) * BM)
+                    o[b, rows, h], lse[b, h, rows] = _attend_counting_skipped(
+                        qq[b, rows, h], kk[b, :, hk], vv[b, :, hk], rows, kr, BN, scale)
                 for j in np.nonzero(kr)[0]:
                     mask[i * BM:(i + 1) * BM, j * BN:(j + 1) * BN] = True
-            mask &= np.arange(S)[None, :] <= np.arange(S)[:, None]
-            o[b, :, h], lse[b, h] = _attend(qq[b, :, h], kk[b, :, hk], vv[b, :, hk], mask, scale)
+            if skipped == "drop":
+                mask &= np.arange(S)[None, :] <= np.arange(S)[:, None]
+                o[b, :, h], lse[b, h] = _attend(qq[b, :, h], kk[b, :, hk], vv[b, :, hk], mask, scale)
     return o, lse, keep, tmax
 
 
+def _attend_counting_skipped(q_rows, k, v, rows, keep_row, BN: int, scale: float):
+    """Rows of one query block (all of whose keys j <= i tiles are causal candidates) under the
+    "count" reading: softmax over every causal key, values of skipped tiles taken as zero."""
+    nk = keep_row.size * BN
+    kept_key = np.repeat(keep_row.astype(bool), BN)             # [nk]
+    v0 = np.where(kept_key[:, None], v[:nk], 0.0)
+    mask = np.arange(nk)[None, :] <= np.asarray(rows)[:, None]
+    return _attend(q_rows, k[:nk], v0, mask, scale)
+
+
 def gated_rows(q, k, v, T: float, b: int, h: int, i: int, rows, BM: int = 128, BN: int = 128,
-               scale: float | None = None):
+               scale: float | None = None, skipped: str = "drop"):
     """Gated attention for selected rows of query block i of head h (full-size spot checks).
 
     Returns (O [R, D], LSE [R], keep row [i+1], t row [i+1]).
     """
+    _skip_check(skipped)
     q, k = np.asarray(q), np.asarray(k)
     Hq, D = q.shape[2], q.shape[3]
     Hkv = k.shape[2]
@@ -117,6 +152,11 @@ def gated_rows(q, k, v, T: float, b: int, h: int, i: int, rows, BM: int = 128, B
     hk = _kv_head(h, Hq, Hkv)
     t = tile_max_row(q, k, b, h, i, BM, BN, scale)
     kr = _keep_row(t, T, i)
+    if skipped == "count":
+        nk = (i + 1) * BN
+        o, lse = _attend_counting_skipped(as_f64(q[b, np.asarray(rows), h]), as_f64(k[b, :nk, hk]),
+                                          as_f64(v[b, :nk, hk]), rows, kr, BN, scale)
+        return o, lse, kr, t
     kept = np.nonzero(kr)[0]
     cols = np.concatenate([np.arange(j * BN, (j + 1) * BN) for j in kept])
     kv = as_f64(k[b, cols, hk])

@@ -132,10 +132,13 @@ def test_gated_and_vs_convert_errors(lib):
     prob = _prob(Hq=2, Hkv=2, Sq=256, Sk=256, causal=1)
     T = 16
     q = _t(sb=256 * 2 * 128, ss=2 * 128)
-    assert lib.bsa_fwd_gated(ctypes.byref(prob), q, _t(), _t(), None, 128, 128, q, None, None, None, None) \
+    assert lib.bsa_fwd_gated(ctypes.byref(prob), q, _t(), _t(), None, 128, 128, 0, q, None, None, None, None) \
         == bd.BSA_ERR_INVALID_ARG
-    assert lib.bsa_fwd_gated(ctypes.byref(prob), q, _t(), _t(), T, 64, 64, q, None, None, None, None) \
+    assert lib.bsa_fwd_gated(ctypes.byref(prob), q, _t(), _t(), T, 64, 64, 0, q, None, None, None, None) \
         == bd.BSA_ERR_UNSUPPORTED
+    for bad in (2, -1):                                                                 # skipped: 0 or 1
+        assert lib.bsa_fwd_gated(ctypes.byref(prob), q, _t(), _t(), T, 128, 128, bad, q, None, None, None, None) \
+            == bd.BSA_ERR_INVALID_ARG
     cal = lib.bsfa_calibrate
     assert cal(ctypes.byref(prob), q, _t(), 0, T, T, None) == bd.BSA_ERR_INVALID_ARG         # k_keep < 1
     assert cal(ctypes.byref(prob), q, _t(), 2, None, T, None) == bd.BSA_ERR_INVALID_ARG      # no tile_max
@@ -177,10 +180,10 @@ def test_gated_and_vs_convert_errors(lib):
     assert bw(ctypes.byref(_prob(Hq=4, Hkv=2, Sq=256, Sk=256, causal=1, D=64)), qs, _t(), _t(), None, qs, 16, qs,
               16, 16, 16, 256, wsb, None) == bd.BSA_ERR_UNSUPPORTED                          # head dim 64
     sc = _prob(Hq=2, Hkv=2, Sq=256, Sk=256, causal=1, softcap=30.0)
-    assert lib.bsa_fwd_gated(ctypes.byref(sc), q, _t(), _t(), T, 128, 128, q, None, None, None, None) \
+    assert lib.bsa_fwd_gated(ctypes.byref(sc), q, _t(), _t(), T, 128, 128, 0, q, None, None, None, None) \
         == bd.BSA_ERR_UNSUPPORTED
     nc = _prob(Hq=2, Hkv=2, Sq=256, Sk=256, causal=0)
-    assert lib.bsa_fwd_gated(ctypes.byref(nc), q, _t(), _t(), T, 128, 128, q, None, None, None, None) \
+    assert lib.bsa_fwd_gated(ctypes.byref(nc), q, _t(), _t(), T, 128, 128, 0, q, None, None, None, None) \
         == bd.BSA_ERR_UNSUPPORTED
     x = 16
     assert lib.vs_convert_indexes(x, x, x, x, 1, 1, 4, 4, 256, 64, 64, 0, x, x, x, x, None) == bd.BSA_ERR_UNSUPPORTED

@@ -33,21 +33,22 @@ def small():
     return w
 
 
+@pytest.mark.parametrize("skipped", ["drop", "count"])
 @pytest.mark.parametrize("mode", ["median", "-inf", "+inf"])
-def test_gated_small(small, mode):
+def test_gated_small(small, mode, skipped):
     w = small
-    say("gated small", mode)
+    say("gated small", mode, skipped)
     T = {"median": w["T"], "-inf": np.full_like(w["T"], -np.inf), "+inf": np.full_like(w["T"], np.inf)}[mode]
-    o, lse, keep, tmax = bsa.bsa_fwd_gated(w["dq"], w["dk"], w["dv"], torch.from_numpy(T).cuda(),
+    o, lse, keep, tmax = bsa.bsa_fwd_gated(w["dq"], w["dk"], w["dv"], torch.from_numpy(T).cuda(), skipped=skipped,
                                            out_dtype=torch.float32, return_tile_max=True)
-    o_ref, lse_ref, keep_ref, tmax_ref = oracle.gated(w["q"], w["k"], w["v"], T, 128, 128)
+    o_ref, lse_ref, keep_ref, tmax_ref = oracle.gated(w["q"], w["k"], w["v"], T, 128, 128, skipped=skipped)
     lower = np.tril(np.ones((8, 8), bool))
     kg = keep.cpu().numpy()
     assert np.array_equal(kg[..., lower], keep_ref[..., lower]), "keep mask differs"
     tg = tmax.cpu().numpy().astype(np.float64)
     assert np.abs(tg[..., lower] - tmax_ref[..., lower]).max() < 1e-3
-    check_o(host(o), o_ref, f"gated {mode}")
-    check_lse(host(lse), lse_ref, f"gated {mode} lse")
+    check_o(host(o), o_ref, f"gated {mode} {skipped}")
+    check_lse(host(lse), lse_ref, f"gated {mode} {skipped} lse")
     if mode == "median":
         off = lower & ~np.eye(8, dtype=bool)
         frac = 1.0 - kg[..., off].mean()
@@ -113,6 +114,11 @@ def test_gated_full_size_every_keep_decision(cfg4):
     assert abs(skip - float(gold["skip_frac"])) < 1e-12
     print(f"[parity] gated full size: keep masks of 32 heads bit-exact, skip fraction {skip:.4f}", flush=True)
     oh, lh = host(o), host(lse)
+    say("gated full size, skipped tiles counted in the normaliser")
+    oc, lc, kc, _ = bsa.bsa_fwd_gated(w["dq"], w["dk"], w["dv"], torch.from_numpy(T).cuda(), skipped="count",
+                                      out_dtype=torch.float32)
+    assert torch.equal(kc, keep), "the keep decisions do not depend on the skipped-tile reading"
+    och, lch = host(oc), host(lc)
     for h, i in [(0, 511), (31, 300), (9, 1), (17, 64), (5, 0), (22, 450), (12, 127), (28, 2)]:
         rows = np.arange(i * 128, (i + 1) * 128)
         o_ref, lse_ref, kr, t = oracle.gated_rows(w["q"], w["k"], w["v"], T[0, h, i], 0, h, i, rows, 128, 128)
@@ -122,6 +128,10 @@ def test_gated_full_size_every_keep_decision(cfg4):
             assert np.abs(t[:i].astype(np.float32) - T[0, h, i]).min() >= 1e-2 - 1e-6
         check_o(oh[0, rows, h], o_ref, f"gated full h={h} i={i}")
         check_lse(lh[0, h, rows], lse_ref, f"gated full lse h={h} i={i}")
+        o_ref, lse_ref, _, _ = oracle.gated_rows(w["q"], w["k"], w["v"], T[0, h, i], 0, h, i, rows, 128, 128,
+                                                 skipped="count")
+        check_o(och[0, rows, h], o_ref, f"gated full (count) h={h} i={i}")
+        check_lse(lch[0, h, rows], lse_ref, f"gated full (count) lse h={h} i={i}")
 
 
 # ---- threshold calibration ----

@@ -172,3 +172,74 @@ def test_calibration_with_k_past_every_row_keeps_everything():
     assert realised == 1.0 and target == 1.0
     with pytest.raises(ValueError):
         oracle.calibrate(q, k, 0, bs, bs)
+
+
+# ---- the "count" reading of a skipped tile (scores kept in the maximum and normaliser) ----
+
+def _dense_causal_lse(q, k):
+    """log-sum-exp of the scaled causal scores, by torch.logsumexp in float64 (independent of
+    the oracle's softmax)."""
+    qf, kf = bf16_to_f64(q), bf16_to_f64(k)
+    B, S, Hq, D = qf.shape
+    G = Hq // kf.shape[2]
+    out = np.zeros((B, Hq, S))
+    for h in range(Hq):
+        s = torch.from_numpy(qf[0, :, h] @ kf[0, :, h // G].T / math.sqrt(D))
+        s = s.masked_fill(~torch.from_numpy(np.tril(np.ones((S, S), bool))), float("-inf"))
+        out[0, h] = torch.logsumexp(s, dim=-1).numpy()
+    return out
+
+
+def test_count_reading_has_the_dense_causal_lse():
+    """Every causal score stays in the normaliser, whatever the thresholds."""
+    q, k, v, bs = _small(seed=24)
+    want = _dense_causal_lse(q, k)
+    for T in (_median_thresholds(q, k, bs), np.full((1, q.shape[2], q.shape[1] // bs), np.inf, np.float32)):
+        _, lse, _, _ = oracle.gated(q, k, v, T, bs, bs, skipped="count")
+        np.testing.assert_allclose(lse, want, atol=1e-11, rtol=0)
+
+
+def test_count_and_drop_share_the_numerator():
+    """O exp(LSE) is the sum of exp(score) v over the kept keys under both readings; the keep
+    decisions are the same."""
+    q, k, v, bs = _small(seed=25)
+    T = _median_thresholds(q, k, bs)
+    od, ld, kd, _ = oracle.gated(q, k, v, T, bs, bs, skipped="drop")
+    oc, lc, kc, _ = oracle.gated(q, k, v, T, bs, bs, skipped="count")
+    assert np.array_equal(kd, kc)
+    assert (kd[0][:, np.tril(np.ones(kd.shape[-2:], bool), -1)] == 0).any()   # some tiles are skipped
+    np.testing.assert_allclose(oc * np.exp(lc)[..., None].transpose(0, 2, 1, 3),
+                               od * np.exp(ld)[..., None].transpose(0, 2, 1, 3), rtol=1e-10, atol=1e-12)
+    assert np.abs(oc - od).max() > 1e-3          # the readings do differ where tiles are skipped
+
+
+def test_count_reading_with_constant_values_gives_the_kept_mass():
+    """V = c on every key: O = c times the share of the causal mass in kept tiles, i.e.
+    c exp(LSE over kept tiles - dense causal LSE)."""
+    q, k, v, bs = _small(seed=26)
+    c = 0.75
+    v1 = np.full_like(v, np.uint16(0x3F40))      # bf16 bits of 0.75
+    T = _median_thresholds(q, k, bs)
+    oc, _, _, _ = oracle.gated(q, k, v1, T, bs, bs, skipped="count")
+    _, ld, _, _ = oracle.gated(q, k, v1, T, bs, bs, skipped="drop")
+    share = np.exp(ld - _dense_causal_lse(q, k))                  # [B, Hq, S]
+    np.testing.assert_allclose(oc, c * share.transpose(0, 2, 1)[..., None] * np.ones(oc.shape), rtol=1e-10,
+                               atol=1e-13)
+
+
+def test_count_reading_with_minus_inf_threshold_is_dense_causal():
+    q, k, v, bs = _small(seed=27)
+    T = np.full((1, q.shape[2], q.shape[1] // bs), -np.inf, np.float32)
+    o, _, _, _ = oracle.gated(q, k, v, T, bs, bs, skipped="count")
+    np.testing.assert_allclose(o, _sdpa(q, k, v, causal=True), atol=1e-12)
+
+
+def test_gated_rows_count_matches_gated():
+    q, k, v, bs = _small(seed=28)
+    T = _median_thresholds(q, k, bs)
+    o, lse, _, _ = oracle.gated(q, k, v, T, bs, bs, skipped="count")
+    for h, i in [(0, 3), (3, 7), (1, 0)]:
+        rows = np.arange(i * bs, (i + 1) * bs)
+        orr, lr, _, _ = oracle.gated_rows(q, k, v, T[0, h, i], 0, h, i, rows, bs, bs, skipped="count")
+        np.testing.assert_allclose(orr, o[0, rows, h], atol=1e-12)
+        np.testing.assert_allclose(lr, lse[0, h, rows], atol=1e-12)
