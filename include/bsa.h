@@ -135,8 +135,9 @@ typedef struct {
   int64_t s_b, s_h, s_q;
 } bsa_pattern;
 
-/* Human-readable name of a status code (static storage). */
-const char* bsa_status_string(bsa_status s);
+/* Human-readable name of a status code (static storage); any int32 value is
+ * accepted ("unknown status" outside bsa_status). */
+const char* bsa_status_string(int32_t status);
 
 /* Checks the contents of a BLOCK or VS pattern on the device: the rules the
  * attention kernels rely on without checking them.  BLOCK ([IR] Usage 1):

@@ -16,7 +16,8 @@ from typing import Optional
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libbsa.so")
+# BSA_LIBRARY selects another build of the same library (the host-sanitized one)
+LIB_PATH = os.environ.get("BSA_LIBRARY") or os.path.join(_PKG, "libbsa.so")
 
 BSA_OK, BSA_ERR_INVALID_ARG, BSA_ERR_UNSUPPORTED, BSA_ERR_WORKSPACE, BSA_ERR_HIP = range(5)
 BSA_BF16, BSA_F32 = 0, 1

@@ -55,21 +55,42 @@ def _run(cmd, verbose):
         print(out)
 
 
-def build(verbose: bool = False, extra_flags=None) -> str:
-    """Compile every HIP translation unit and link libbsa.so (always recompiles)."""
-    objdir = os.path.join(PKG, "_build")
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer for the C ABI layer (argument
+# validation, plans, launch set-up); the device code is built as usual.  The sanitizer runtime is
+# not linked into the library: a process loading it preloads libclang_rt.asan (sanitizer_runtime()).
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address,undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+SAN_LIB = os.path.join(PKG, "libbsa_sanitized.so")
+
+
+def sanitizer_runtime() -> str:
+    """Path of the AddressSanitizer runtime of the ROCm compiler (for LD_PRELOAD)."""
+    res = subprocess.run([os.path.join(os.path.dirname(hipcc()), "amdclang++"), "-print-file-name=libclang_rt.asan-x86_64.so"],
+                         capture_output=True, text=True)
+    path = res.stdout.strip()
+    if res.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("AddressSanitizer runtime not found")
+    return path
+
+
+def build(verbose: bool = False, extra_flags=None, sanitize: bool = False) -> str:
+    """Compile every HIP translation unit and link libbsa.so (always recompiles).  With
+    sanitize=True the C ABI layer (bsa_api.hip) is built with host ASan/UBSan into
+    libbsa_sanitized.so instead, beside the regular library, which is left alone."""
+    objdir = os.path.join(PKG, "_build_sanitized" if sanitize else "_build")
     os.makedirs(objdir, exist_ok=True)
     objs = []
     for src, flags in SOURCES:
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
-        _run([hipcc(), *HIP_FLAGS, *flags, *(extra_flags or []), "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-              "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        san = SANITIZE_FLAGS if sanitize and src == "bsa_api.hip" else []
+        _run([hipcc(), *HIP_FLAGS, *flags, *san, *(extra_flags or []), "-I", os.path.join(ROOT, "include"), "-I",
+              CSRC, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
         objs.append(obj)
-    tmp = LIB + ".tmp"
+    out = SAN_LIB if sanitize else LIB
+    tmp = out + ".tmp"
     _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, sanitize="--sanitize" in sys.argv))

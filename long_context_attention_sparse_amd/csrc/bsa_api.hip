@@ -171,8 +171,9 @@ int partial_entries(const bsa_problem& p, const bsa_pattern* pat) {
 
 extern "C" {
 
-const char* bsa_status_string(bsa_status s) {
-  switch (s) {
+const char* bsa_status_string(int32_t status) {
+  // an int, not the enum: a value outside bsa_status must not be loaded as one
+  switch (status) {
     case BSA_OK: return "ok";
     case BSA_ERR_INVALID_ARG: return "invalid argument";
     case BSA_ERR_UNSUPPORTED: return "unsupported configuration";
