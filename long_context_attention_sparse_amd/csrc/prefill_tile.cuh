@@ -154,7 +154,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     if (r.gathered) {
       const int x = r.gbase + i;
       if (x >= ncol) return -1;
-      key = (staged && x < kCols) ? cols_s[x] : cols[x];
+      key = (staged && x < kCols) ? lds_int(cols_s, x) : global_int(cols, x);
     } else {
       key = r.key0 + i;
     }
@@ -163,7 +163,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 
   // Direct loads: wave w fills chunk rows 32w..32w+31 (segment w/2, segment rows
   // 32(w%2)..+31) with eight 1 KB instructions, rows 32w + 4x + l/16, lane l into slot l%16
-  // (R & 15 = 4(x & 3) + l/16).  Absent keys load row 0 (finite, masked out later).
+  // (R & 15 = 4(x & 3) + l/16).  Contiguous segments go through a buffer resource based at
+  // the wave's first row, sized to the rows inside [0, kv_len): rows past the sequence, or a
+  // whole absent segment, read zeros (finite, masked out later), with no per-lane test.
+  // Gathered columns keep per-lane global addresses (their keys can lie anywhere).
   const int lrow = l >> 4, lslot = l & 15;
   const int srow0 = (w & 1) * 32;  // first row of this wave within its segment
   const uint32_t kx = (uint32_t)(lslot ^ lrow) << 4;
@@ -171,33 +174,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const uint32_t k_lane = (uint32_t)(lrow * a.k.ss) * 2u, v_lane = (uint32_t)(lrow * a.v.ss) * 2u + vx;
   auto issue = [&](uint16_t* tile, const uint16_t* src, int64_t ss, bool is_k, const Seg& r, bool staged)
                    __attribute__((always_inline)) {
-    if (r.full) {
+    if (!r.gathered) {
+      const int row0 = r.key0 + srow0;
+      const int nrows = (r.valid && row0 >= 0) ? min(kv_len - row0, 32) : 0;
+      const uint32_t row_bytes = (uint32_t)ss * 2u;
+      const __amdgpu_buffer_rsrc_t rs =
+          rows_rsrc(src + (int64_t)max(row0, 0) * ss, nrows > 0 ? (uint32_t)(nrows - 1) * row_bytes + 256u : 0u);
 #pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        const char* p = reinterpret_cast<const char*>(src + (int64_t)(r.key0 + srow0 + x * 4) * ss);
-        __builtin_amdgcn_global_load_lds(p + (is_k ? k_lane + (kx ^ ((x & 3) << 6)) : v_lane),
-                                         BSA_LDS(tile + (w * 8 + x) * 4 * RS), 16, 0, 0);
-      }
-    } else if constexpr (KIND != 2) {
-#pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        int key = key_of(srow0 + x * 4 + lrow, r, staged);
-        key = key < 0 ? 0 : key;
-        const char* p = reinterpret_cast<const char*>(src + (int64_t)key * ss);
-        __builtin_amdgcn_global_load_lds(p + (is_k ? (kx ^ ((x & 3) << 6)) : vx), BSA_LDS(tile + (w * 8 + x) * 4 * RS),
-                                         16, 0, 0);
-      }
-    } else {
+      for (int x = 0; x < 8; ++x)
+        buffer_load_lds16(rs, tile + (w * 8 + x) * 4 * RS,
+                          (uint32_t)(x * 4) * row_bytes + (is_k ? k_lane + (kx ^ ((x & 3) << 6)) : v_lane));
+    } else if constexpr (KIND == 2) {
       // all eight keys first, then the loads: a key read from memory is waited for once, not
       // once per load (each wait would also wait for the loads already in flight)
       int keys[8];
-      if (!r.gathered) {  // a window that crosses the sequence bounds: arithmetic only
-#pragma unroll
-        for (int x = 0; x < 8; ++x) {
-          const int key = r.key0 + srow0 + x * 4 + lrow;
-          keys[x] = r.valid && (unsigned)key < (unsigned)kv_len ? key : 0;
-        }
-      } else if (staged && r.gbase + 64 <= kCols) {  // gathered, indices staged in LDS
+      if (staged && r.gbase + 64 <= kCols) {  // gathered, indices staged in LDS
 #pragma unroll
         for (int x = 0; x < 8; ++x) {
           const int xi = r.gbase + srow0 + x * 4 + lrow;
@@ -294,13 +285,22 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     f32x16 s[NB];
 #pragma unroll
     for (int kb = 0; kb < NB; ++kb) s[kb] = f32x16{};
+    // K operands double-buffered: the reads of step ks + 1 are issued before the products of
+    // step ks, so each read has a whole step of products to land behind
+    u32x4 av[2][NB];
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb) av[0][kb] = *reinterpret_cast<const u32x4*>(Kt + kb * 32 * RS + koff[0]);
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      u32x4 av[NB];
+      if (ks + 1 < D / 16) {
 #pragma unroll
-      for (int kb = 0; kb < NB; ++kb) av[kb] = *reinterpret_cast<const u32x4*>(Kt + kb * 32 * RS + koff[ks]);
+        for (int kb = 0; kb < NB; ++kb)
+          av[(ks + 1) & 1][kb] = *reinterpret_cast<const u32x4*>(Kt + kb * 32 * RS + koff[ks + 1]);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keep the order: reads of step ks + 1, then products of step ks
 #pragma unroll
-      for (int kb = 0; kb < NB; ++kb) s[kb] = mfma32x32x16(as_bf16x8(av[kb]), qreg[ks], s[kb]);
+      for (int kb = 0; kb < NB; ++kb) s[kb] = mfma32x32x16(as_bf16x8(av[ks & 1][kb]), qreg[ks], s[kb]);
+      __builtin_amdgcn_sched_barrier(0);
     }
     softcap_n<NB>(s, a.cap_in, a.cap_out);
 #pragma unroll

@@ -93,6 +93,17 @@ __device__ __forceinline__ int global_int(const int* p, int i) {
   return ((const __attribute__((address_space(1))) int*)p)[i];
 }
 
+// Raw buffer resource over `bytes` bytes from `base`: untyped loads at offsets past `bytes`
+// return zeros (the range check takes the per-lane offset, so every row-dependent part of an
+// address goes into it).  Dword 3 selects 32-bit data, the setting untyped loads need.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+// 16 bytes per lane from a buffer straight into LDS (lane i -> lds + 16 i)
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, BSA_LDS(lds), 16, voff, 0, 0, 0);
+}
+
 __device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t* p) {
   const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
   return __builtin_bit_cast(u32x2, v);
