@@ -45,6 +45,8 @@ def _args():
     ap.add_argument("--config", type=int, default=None, choices=list(ALL_CONFIGS),
                     help="one workload only (default: all of them in one line)")
     ap.add_argument("--cpu-seconds", type=float, default=3.0, help="wall-clock budget of each oracle sample")
+    ap.add_argument("--settle", type=float, default=SETTLE_S,
+                    help="seconds each workload runs untimed before its warm-up (GPU clock ramp)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="time decode steps as eager launches instead of HIP graph replays")
@@ -317,7 +319,18 @@ class Timer:
         self.spans = {}
 
 
+SETTLE_S = 0.2
+
+
 def run_steps(torch, step, timer, steps, warmup):
+    """`warmup` untimed steps, then exactly `steps` timed ones (wall clock, synchronized on both
+    sides).  Before the warm-up the step runs untimed for at least SETTLE_S seconds, so that the
+    GPU clock has ramped up from idle (the first tens of milliseconds of a heavy kernel run
+    slower) and every workload is timed in the same steady state."""
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < SETTLE_S:
+        step(timer)
+        torch.cuda.synchronize()
     for _ in range(warmup):
         step(timer)
     torch.cuda.synchronize()
@@ -334,8 +347,8 @@ def run_steps(torch, step, timer, steps, warmup):
 # counter reads for a 1 GiB device copy (FETCH_SIZE reads half the bytes: x2.0; WRITE_SIZE
 # x1.0).  Valid only for the sources the counters were taken on: the digest covers the
 # kernel, its launch planning and the workload generator, and a mismatch reports null.
-DECODE_TRAFFIC = {"bytes": 1_287_990_552, "fetch_kib": 625_002, "write_kib": 7_800,
-                  "sha256": "b66f93c942e4ac1bf222788cc76c74a1583f9b00bb518d1a18b59f3d54e0d158"}
+DECODE_TRAFFIC = {"bytes": 1_288_036_913, "fetch_kib": 625_024, "write_kib": 7_800,
+                  "sha256": "0197d055bc42db5121b76fbe1ae8abddf4efa9a5ce1305fe89dbaba4d4951779"}
 TRAFFIC_SOURCES = ["long_context_attention_sparse_amd/csrc/" + f for f in
                    ("decode.cuh", "common.cuh", "args.cuh", "kernels_stream.hip", "decode_plan.h", "host_args.h")] + \
                   ["synth/workloads.py"]
@@ -840,6 +853,8 @@ GPU = {1: gpu_tiny, 2: gpu_spec_decode, 3: gpu_block_prefill, 4: gpu_gated, 5: g
 
 def main():
     args = _args()
+    global SETTLE_S
+    SETTLE_S = args.settle
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the kernels are single-GPU and "
               "the multi-GPU sharding is a design note, not part of this build.", file=sys.stderr)
