@@ -45,7 +45,7 @@ def _args():
     ap.add_argument("--config", type=int, default=None, choices=list(ALL_CONFIGS),
                     help="one workload only (default: all of them in one line)")
     ap.add_argument("--cpu-seconds", type=float, default=3.0, help="wall-clock budget of each oracle sample")
-    ap.add_argument("--settle", type=float, default=SETTLE_S,
+    ap.add_argument("--settle", type=float, default=0.2,
                     help="seconds each workload runs untimed before its warm-up (GPU clock ramp)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
@@ -322,24 +322,36 @@ class Timer:
 SETTLE_S = 0.2
 
 
-def run_steps(torch, step, timer, steps, warmup):
-    """`warmup` untimed steps, then exactly `steps` timed ones (wall clock, synchronized on both
-    sides).  Before the warm-up the step runs untimed for at least SETTLE_S seconds, so that the
-    GPU clock has ramped up from idle (the first tens of milliseconds of a heavy kernel run
-    slower) and every workload is timed in the same steady state."""
+MIN_TIMED_S = 0.25
+
+
+def run_steps(torch, step, timer, steps, warmup, min_seconds=0.0):
+    """`warmup` untimed steps, then `steps` timed ones (wall clock, synchronized on both sides);
+    with min_seconds > 0, at least as many more as fill that long (the count is fixed from the
+    settle phase's pace before timing starts).  Before the warm-up the step runs untimed for at least
+    SETTLE_S seconds, so that the GPU clock has ramped up from idle (the first tens of
+    milliseconds of a heavy kernel run slower); the clock then still wanders by up to 30% for
+    tens of milliseconds at a time, which the longer timed window averages out.
+    Returns (ms per step, steps timed)."""
     t0 = time.perf_counter()
+    settled = 0
     while time.perf_counter() - t0 < SETTLE_S:
         step(timer)
         torch.cuda.synchronize()
+        settled += 1
+    per = (time.perf_counter() - t0) / max(settled, 1)
     for _ in range(warmup):
         step(timer)
     torch.cuda.synchronize()
+    n = steps
+    if min_seconds > 0:
+        n = max(steps, int(np.ceil(min_seconds / max(per, 1e-6))))
     timer.reset()
     t0 = time.perf_counter()
-    for _ in range(steps):
+    for _ in range(n):
         step(timer)
     torch.cuda.synchronize()
-    return (time.perf_counter() - t0) * 1e3 / steps
+    return (time.perf_counter() - t0) * 1e3 / n, n
 
 
 # HBM bytes per decode launch on the speculative+sparse workload, from two rocprofv3
@@ -471,7 +483,7 @@ def gpu_tiny(torch, bsa, w, args):
             bsa.bsa_combine(o_part, lse_part, out=out)
 
     timer = Timer(torch)
-    eager_ms = run_steps(torch, step, timer, args.steps, args.warmup)
+    eager_ms, _ = run_steps(torch, step, timer, args.steps, args.warmup)
     spans = {n: round(timer.mean_ms(n) * 1e3, 2) for n in timer.spans}
 
     def set_a():
@@ -526,7 +538,7 @@ def gpu_spec_decode(torch, bsa, w, args):
             bsa.bsa_combine(o_part, lse_part, out=out, lse=lse)
 
     timer = Timer(torch)
-    eager_ms = run_steps(torch, step, timer, args.steps, args.warmup)
+    eager_ms, _ = run_steps(torch, step, timer, args.steps, args.warmup)
     spans = {n: round(timer.mean_ms(n) * 1e3, 2) for n in timer.spans}
     _log("decode eager per-launch us (host launch gaps included):", spans)
 
@@ -605,13 +617,14 @@ def gpu_block_prefill(torch, bsa, w, args):
             bsa.bsa_fwd(q, k, v, pat, causal=True, out=out, lse=lse)
 
     timer = Timer(torch)
-    ms = run_steps(torch, step, timer, args.steps, args.warmup)
+    ms, n_timed = run_steps(torch, step, timer, args.steps, args.warmup, MIN_TIMED_S)
     tiles = int(w["count"].sum())
     flops = tiles * 4 * 128 ** 3
     kms = timer.mean_ms("prefill")
     return dict(workload="block-sparse causal prefill", value=round(flops / (ms * 1e-3) / 1e12, 2), unit="TFLOP/s",
                 ms=ms,
-                config={"B": 1, "Hq": 32, "Hkv": 8, "S": w["Sq"], "D": 128, "tile": 128, "visited_tiles": tiles,
+                config={"timed_steps": n_timed, "B": 1, "Hq": 32, "Hkv": 8, "S": w["Sq"], "D": 128, "tile": 128,
+                        "visited_tiles": tiles,
                         "flops": flops,
                         "algorithmic_units": f"{tiles} visited 128x128 tiles x 4*128^3 flop (QK and PV)"},
                 roofline=_roof("mfma", flops / (kms * 1e-3) / 1e12, "void bsa::prefill_tile_kernel<1, 4>(bsa::PrefillArgs)",
@@ -652,7 +665,7 @@ def gpu_gated(torch, bsa, w, args):
             bsa.bsa_fwd_gated(q, k, v, T_all, out=out, return_mask=False)
 
     timer = Timer(torch)
-    ms = run_steps(torch, step, timer, args.steps, args.warmup)
+    ms, n_timed = run_steps(torch, step, timer, args.steps, args.warmup, MIN_TIMED_S)
     kms = timer.mean_ms("gated")
     km = keep[0].cpu().numpy()
     lower = np.tril(np.ones((nqb, nqb), bool))
@@ -664,10 +677,10 @@ def gpu_gated(torch, bsa, w, args):
             bsa.bsa_fwd_gated(q, k, v, Td, out=out, return_mask=False, skipped="count")
 
     timer2 = Timer(torch)
-    run_steps(torch, step_dense, timer2, max(3, args.steps // 4), 2)
+    run_steps(torch, step_dense, timer2, max(3, args.steps // 4), 2, MIN_TIMED_S)
     ungated_ms = timer2.mean_ms("ungated")
     timer5 = Timer(torch)
-    run_steps(torch, step_count, timer5, max(3, args.steps // 4), 2)
+    run_steps(torch, step_count, timer5, max(3, args.steps // 4), 2, MIN_TIMED_S)
     count_ms = timer5.mean_ms("count")
     off = lower & ~np.eye(nqb, dtype=bool)
     skip = 1.0 - float(km[..., off].mean())
@@ -696,7 +709,7 @@ def gpu_gated(torch, bsa, w, args):
                    "target_density": round(target, 4), "realised_density": round(realised, 4),
                    "gated_ms_at_calibrated_T": round(cal_gate_ms, 4)}
     return dict(workload="BSFA gated causal prefill", value=round(flops / (ms * 1e-3) / 1e12, 2), unit="TFLOP/s", ms=ms,
-                config={"B": 1, "Hq": Hq, "Hkv": 8, "S": S, "D": 128, "tile": 128,
+                config={"timed_steps": n_timed, "B": 1, "Hq": Hq, "Hkv": 8, "S": S, "D": 128, "tile": 128,
                         "skip_fraction_offdiag": round(skip, 4), "flops": flops,
                         "algorithmic_units": f"QK on {causal_tiles} causal 128x128 tiles and PV on {kept} kept tiles, "
                                              "2*128^3 flop each",
@@ -735,7 +748,7 @@ def gpu_vs(torch, bsa, w, args):
         res["m"] = (bc, cc)
 
     timer = Timer(torch)
-    ms = run_steps(torch, step, timer, args.steps, args.warmup)
+    ms, n_timed = run_steps(torch, step, timer, args.steps, args.warmup, MIN_TIMED_S)
     bc, cc = (x.cpu().numpy().astype(np.int64) for x in res["m"])
     flops = int((4 * 64 * 128 * (64 * bc + cc)).sum())
     ams = timer.mean_ms("attention")
@@ -743,7 +756,8 @@ def gpu_vs(torch, bsa, w, args):
     conv_bytes = int(4 * (bc.sum() + cc.sum() + bc.size + cc.size))
     return dict(workload="vertical-slash conversion + varlen causal prefill",
                 value=round(flops / (ms * 1e-3) / 1e12, 2), unit="TFLOP/s", ms=ms,
-                config={"seqlens": [65536, 32768], "H": 32, "D": 128, "block": 64, "nnz_v": 1000, "nnz_s": 2000,
+                config={"timed_steps": n_timed, "seqlens": [65536, 32768], "H": 32, "D": 128, "block": 64,
+                        "nnz_v": 1000, "nnz_s": 2000,
                         "flops": flops, "attention_ms": round(ams, 4), "convert_ms": round(cms, 4),
                         "convert_output_bytes": conv_bytes,
                         "convert_gbs": round(conv_bytes / (cms * 1e-3) / 1e9, 1),
@@ -781,7 +795,7 @@ def gpu_selected(torch, bsa, w, args):
             call()
 
     timer = Timer(torch)
-    ms = run_steps(torch, step, timer, args.steps, args.warmup)
+    ms, n_timed = run_steps(torch, step, timer, args.steps, args.warmup, MIN_TIMED_S)
     call_ms = kernel_mean_ms(torch, call)
     # work the call must do: every selection here is valid (the generator draws causal blocks)
     s_np = w["sel"]
@@ -805,7 +819,8 @@ def gpu_selected(torch, bsa, w, args):
     gbs = alg_bytes / (call_ms * 1e-3) / 1e9
     return dict(workload="selected attention, top-k key blocks per query token (key-block-outer)",
                 value=round(flops / (ms * 1e-3) / 1e12, 2), unit="TFLOP/s", ms=ms,
-                config={"seqlens": [int(x) for x in w["seqlens"]], "Hq": Hq, "Hkv": Hkv, "D": 128, "block": 64,
+                config={"timed_steps": n_timed, "seqlens": [int(x) for x in w["seqlens"]], "Hq": Hq, "Hkv": Hkv,
+                        "D": 128, "block": 64,
                         "topk": topk, "valid_pairs": pairs, "chunks": chunks, "flops": flops,
                         "algorithmic_bytes": alg_bytes,
                         "algorithmic_units": "gathered Q rows, one K/V tile per chunk of 128/G tokens, float32 "
@@ -833,13 +848,14 @@ def gpu_backward(torch, bsa, w, args):
             bsa.bsa_bwd(q, k, v, out, lse, do, pat, causal=True, workspace=ws)
 
     timer = Timer(torch)
-    ms = run_steps(torch, step, timer, args.steps, args.warmup)
+    ms, n_timed = run_steps(torch, step, timer, args.steps, args.warmup, MIN_TIMED_S)
     bms = timer.mean_ms("backward")
     tiles = int(w["count"].sum())
     flops = tiles * 5 * 2 * 128 ** 3   # S (rebuilt), dP, dV, dQ, dK: five tile products
     return dict(workload="block-sparse causal prefill backward (dQ, dK, dV)",
                 value=round(flops / (ms * 1e-3) / 1e12, 2), unit="TFLOP/s", ms=ms,
-                config={"B": 1, "Hq": 32, "Hkv": 8, "S": 32768, "D": 128, "tile": 128, "visited_tiles": tiles,
+                config={"timed_steps": n_timed, "B": 1, "Hq": 32, "Hkv": 8, "S": 32768, "D": 128, "tile": 128,
+                        "visited_tiles": tiles,
                         "flops": flops,
                         "algorithmic_units": "5 products of 2*128^3 per visited tile (S, dP, dV, dQ, dK); the dQ pass "
                                              "rebuilds S and dP a second time: 7 executed"},
