@@ -339,13 +339,13 @@ def run_steps(torch, step, timer, steps, warmup, min_seconds=0.0):
         step(timer)
         torch.cuda.synchronize()
         settled += 1
-    per = (time.perf_counter() - t0) / max(settled, 1)
+    per = (time.perf_counter() - t0) / settled if settled else None
     for _ in range(warmup):
         step(timer)
     torch.cuda.synchronize()
     n = steps
-    if min_seconds > 0:
-        n = max(steps, int(np.ceil(min_seconds / max(per, 1e-6))))
+    if min_seconds > 0 and per is not None:  # without a settle phase there is no pace: K steps
+        n = max(steps, min(int(np.ceil(min_seconds / per)), 100000))
     timer.reset()
     t0 = time.perf_counter()
     for _ in range(n):
