@@ -282,7 +282,8 @@ def cpu_baseline(cfg, w, budget, cores):
         rate = work / secs * cores
         value = round(rate / (1e9 if unit == "GB/s" else 1e12), 6)
     return {"value": value, "unit": unit, "cores": cores, "kind": "oracle",
-            "sample": f"{done} random {what} of the same workload, float64 NumPy, {cores} worker processes with "
+            "sample": f"{'all ' if done == len(units) else ''}{done} {'' if done == len(units) else 'random '}{what} "
+                      f"of the same workload, float64 NumPy, {cores} worker processes with "
                       f"one BLAS thread each, {wall:.1f} s wall ({secs:.1f} core-seconds inside the oracle)"}
 
 
@@ -510,7 +511,7 @@ def gpu_tiny(torch, bsa, w, args):
                         "eager_ms_per_step": round(eager_ms, 4), "eager_launch_us": spans,
                         "algorithmic_units": "6 + 10 listed 64-key blocks per head (K and V: 16 KB each), 4 heads"},
                 roofline=_roof("hbm", a_bytes / (a_ms * 1e-3) / 1e9, "void bsa::decode_kernel<64>(bsa::DecodeArgs) (set A)",
-                               a_ms, note="latency-bound: 4 workgroups; the launch, not HBM, sets the time"))
+                               a_ms, note="latency-bound: a few tens of workgroups; HIP events over graph replays include the gap between dispatches, the kernel itself runs about 6 us in a trace"))
 
 
 # ---------------------------------------------------------------------------
