@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
     voff[db] = vrow * RS + (((col >> 3) ^ v_swz(vrow)) << 3) + (col & 7);
   }
 
-  float m_run = kNegInf, l_run = 0.f, le_run = 0.f;
+  float m_run = kNegInf, l_run = 0.f;
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int x = 0; x < D / 32; ++x) oacc[x] = f32x16{};
@@ -113,13 +113,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
   auto tile_of = [&](int n) { return n == 0 ? i : n - 1; };  // diagonal first
 
   // Online softmax over one tile: the running maximum (lazy rescale), the weights packed to
-  // bf16 as the P^T operand, their rounded sum (normalises O) and exact sum (LSE).
-  auto weights = [&](const f32x16* sc, uint32_t (*pk)[8], float& psum, float& pesum)
-                     __attribute__((always_inline)) {
-    softmax_max_n<NB>(sc, a.scale_log2, m_run, l_run, le_run, oacc);
+  // bf16 as the P^T operand, and the sum of the float32 weights (the normaliser).
+  auto weights = [&](const f32x16* sc, float row_max, uint32_t (*pk)[8], float& psum) __attribute__((always_inline)) {
+    softmax_rescale(row_max * a.scale_log2, m_run, l_run, oacc);
     const float m_use = m_run == kNegInf ? 0.f : m_run;
     psum = 0.f;
-    pesum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
@@ -130,9 +128,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
         const float p3 = exp2_fast(fmaf(sc[kb][r + 3], a.scale_log2, -m_use));
         pk[kb][r / 2] = pack_bf16x2(p0, p1);
         pk[kb][r / 2 + 1] = pack_bf16x2(p2, p3);
-        psum = bf16x2_sum_acc(pk[kb][r / 2], psum);
-        psum = bf16x2_sum_acc(pk[kb][r / 2 + 1], psum);
-        pesum += (p0 + p1) + (p2 + p3);
+        psum += (p0 + p1) + (p2 + p3);
       }
   };
   // O^T += V_j^T P^T, the V^T operand read with the transposing LDS read
@@ -179,13 +175,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
           if (kl > rl) s[kb][r] = kNegInf;
         }
     }
-    float mx = kNegInf;
+    // the row maximum (the softmax's) on the way to the wave's maximum (the tile's)
+    const float row_max = row_max_n<NB>(s);
+    float mx = row_max;
 #pragma unroll
-    for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, shfl_xor_f(mx, off));
+    for (int off = 16; off >= 1; off >>= 1) mx = fmaxf(mx, shfl_xor_f(mx, off));
     if (l == 0) red[w] = mx;
     // every wave's maximum is in LDS and every wave is done reading K_j
     __syncthreads();
@@ -197,37 +191,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
     }
     const bool more = n < i;
     if constexpr (COUNT && !CALIB) {
-      // every tile's scores enter the maximum and the normalisers; a kept tile's V_j
+      // every tile's scores enter the maximum and the normaliser; a kept tile's V_j
       // (or, for a skipped tile, K_next) streams in during the softmax update
       if (keep) issue_v(j * BN);
       else if (more) issue_k(tile_of(n + 1) * BN);
       uint32_t pk[NB][8];
-      float psum, pesum;
-      weights(s, pk, psum, pesum);
-      le_run += pesum;
+      float psum;
+      weights(s, row_max, pk, psum);
+      l_run += psum;
       if (keep) {
         __builtin_amdgcn_s_waitcnt(0);
         // V_j from every wave is in LDS; K_next streams in during the P V product
         __syncthreads();
         if (more) issue_k(tile_of(n + 1) * BN);
         pv(pk);
-        l_run += psum;
-      } else {
-        l_run += pesum;  // a skipped tile's weights multiply no V row: the exact sum
       }
     } else if (keep) {
       issue_v(j * BN);
       // the softmax update and P run while V_j streams in
       uint32_t pk[NB][8];
-      float psum, pesum;
-      weights(s, pk, psum, pesum);
+      float psum;
+      weights(s, row_max, pk, psum);
       __builtin_amdgcn_s_waitcnt(0);
       // V_j from every wave is in LDS; K_next streams in during the P V product
       __syncthreads();
       if (more) issue_k(tile_of(n + 1) * BN);
       pv(pk);
       l_run += psum;
-      le_run += pesum;
     } else if (more) {
       issue_k(tile_of(n + 1) * BN);
     }
@@ -239,8 +229,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
   }
   if constexpr (!CALIB) {
     const int64_t ob = (int64_t)b * a.o.sb + (int64_t)row * a.o.ss + (int64_t)h * a.o.sh;
-    write_row(a.o, ob, a.lse ? a.lse + ((int64_t)b * a.Hq + h) * a.S + row : nullptr, oacc, m_run, l_run, le_run,
-              hh);
+    write_row(a.o, ob, a.lse ? a.lse + ((int64_t)b * a.Hq + h) * a.S + row : nullptr, oacc, m_run, l_run, hh);
   }
 }
 

@@ -269,12 +269,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     }
   };
 
-  float m_run = kNegInf, l_run = 0.f, le_run = 0.f;
+  float m_run = kNegInf, l_run = 0.f;
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
 
-  // exponentials of the chunk's scores, both normalisers and O^T += V^T P^T
+  // exponentials of the chunk's scores, the normaliser and O^T += V^T P^T
   auto exp_pv = [&](const f32x16* s, const uint16_t* vt) __attribute__((always_inline)) {
     // V^T operands of the first two 16-key steps are read before the exponentials, so their
     // LDS latency hides behind the vector work; the rest are read between the MFMAs
@@ -290,7 +290,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       }
     const float m_use = m_run == kNegInf ? 0.f : m_run;
     uint32_t pk[NB][8];
-    float psum = 0.f, pesum = 0.f;
+    float psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < NB; ++kb) {
 #pragma unroll
@@ -301,13 +301,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         const float p3 = exp2_fast(fmaf(s[kb][r + 3], a.scale_log2, -m_use));
         pk[kb][r / 2] = pack_bf16x2(p0, p1);
         pk[kb][r / 2 + 1] = pack_bf16x2(p2, p3);
-        psum = bf16x2_sum_acc(pk[kb][r / 2], psum);
-        psum = bf16x2_sum_acc(pk[kb][r / 2 + 1], psum);
-        pesum += (p0 + p1) + (p2 + p3);
+        psum += (p0 + p1) + (p2 + p3);
       }
     }
     l_run += psum;
-    le_run += pesum;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       const int kb = ks >> 1, hb = ks & 1;
@@ -334,17 +331,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
                            (int64_t)h * a.o.sh;
         float* lp = nullptr;
         if (a.lse) lp = a.lse + (a.cu_q ? (int64_t)h * a.cu_q[a.B] + q_start + row : ((int64_t)b * a.Hq + h) * a.Sq + row);
-        write_row(a.o, ob, lp, oacc, m_run, l_run, le_run, hh);
+        write_row(a.o, ob, lp, oacc, m_run, l_run, hh);
       } else {
         const OutArg po{a.part_o, 0, (int64_t)a.Hq * D, D, 1};
         const int64_t ob = (((int64_t)slot * a.B + b) * a.Sq + row) * a.Hq * D + (int64_t)h * D;
         write_row(po, ob, a.part_lse + (((int64_t)slot * a.B + b) * a.Hq + h) * a.Sq + row, oacc, m_run, l_run,
-                  le_run, hh);
+                  hh);
       }
     }
     m_run = kNegInf;
     l_run = 0.f;
-    le_run = 0.f;
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
   };
@@ -401,7 +397,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     s_chunk(K0, sc);
     softcap_n<NB>(sc, a.cap_in, a.cap_out);
     mask_chunk(kid0, c0, sc);
-    softmax_max_n<NB>(sc, a.scale_log2, m_run, l_run, le_run, oacc);
+    softmax_max_n<NB>(sc, a.scale_log2, m_run, l_run, oacc);
   }
 
   // Chunk ci: S(ci) in sc; K stages kc / kn (this chunk / the next), V stages vc / vn.
@@ -429,7 +425,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       s_chunk(kn, sc);
       softcap_n<NB>(sc, a.cap_in, a.cap_out);
       mask_chunk(kidn, nxt, sc);
-      softmax_max_n<NB>(sc, a.scale_log2, m_run, l_run, le_run, oacc);
+      softmax_max_n<NB>(sc, a.scale_log2, m_run, l_run, oacc);
     }
     nxt = nn;
   };

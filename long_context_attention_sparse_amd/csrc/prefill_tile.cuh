@@ -230,7 +230,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     voff[db] = vrow * RS + (((col >> 3) ^ v_swz(vrow)) << 3) + (col & 7);
   }
 
-  float m_run = kNegInf, l_run = 0.f, le_run = 0.f;
+  float m_run = kNegInf, l_run = 0.f;
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int x = 0; x < D / 32; ++x) oacc[x] = f32x16{};
@@ -305,7 +305,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     softcap_n<NB>(s, a.cap_in, a.cap_out);
 #pragma unroll
     for (int kb = 0; kb < NB; ++kb) mask_block(s[kb], kb, cur[kb >> 1]);
-    softmax_max_n<NB>(s, a.scale_log2, m_run, l_run, le_run, oacc);
+    softmax_max_n<NB>(s, a.scale_log2, m_run, l_run, oacc);
     // V_c is in LDS from every wave, and every wave is done reading K_c (and the indices)
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -328,7 +328,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         vpre[ks][db] = u32x4{lo[0], lo[1], hi[0], hi[1]};
       }
     const float m_use = m_run == kNegInf ? 0.f : m_run;
-    float psum = 0.f, pesum = 0.f;
+    float psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < NB; ++kb) {
       uint32_t pk[8];
@@ -340,9 +340,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         const float p3 = exp2_fast(fmaf(s[kb][r + 3], a.scale_log2, -m_use));
         pk[r / 2] = pack_bf16x2(p0, p1);
         pk[r / 2 + 1] = pack_bf16x2(p2, p3);
-        psum = bf16x2_sum_acc(pk[r / 2], psum);
-        psum = bf16x2_sum_acc(pk[r / 2 + 1], psum);
-        pesum += (p0 + p1) + (p2 + p3);
+        psum += (p0 + p1) + (p2 + p3);
       }
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) {
@@ -363,7 +361,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       }
     }
     l_run += psum;
-    le_run += pesum;
     if (more) {
       // K_{c+1} is in LDS and every wave is done reading V_c
       __builtin_amdgcn_s_waitcnt(0);
@@ -378,7 +375,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
                        (int64_t)h * a.o.sh;
     float* lp = nullptr;
     if (a.lse) lp = a.lse + (a.cu_q ? (int64_t)h * a.cu_q[a.B] + q_start + row : ((int64_t)b * a.Hq + h) * a.Sq + row);
-    write_row(a.o, ob, lp, oacc, m_run, l_run, le_run, hh);
+    write_row(a.o, ob, lp, oacc, m_run, l_run, hh);
   }
 }
 

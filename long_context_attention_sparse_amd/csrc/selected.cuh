@@ -287,13 +287,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
       const int key = j * 64 + kb * 32 + (rg >> 2) * 8 + hh * 4 + (rg & 3);
       if (key > lim) s[kb][rg] = kNegInf;
     }
-  float m_run = kNegInf, l_run = 0.f, le_run = 0.f;
+  float m_run = kNegInf, l_run = 0.f;
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int x = 0; x < D / 32; ++x) oacc[x] = f32x16{};
-  softmax_max_n<NB>(s, a.scale_log2, m_run, l_run, le_run, oacc);
+  softmax_max_n<NB>(s, a.scale_log2, m_run, l_run, oacc);
   const float m_use = m_run == kNegInf ? 0.f : m_run;
-  float psum = 0.f, pesum = 0.f;
+  float psum = 0.f;
 #pragma unroll
   for (int kb = 0; kb < NB; ++kb) {
     uint32_t pk[8];
@@ -305,9 +305,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
       const float p3 = exp2_fast(fmaf(s[kb][rg + 3], a.scale_log2, -m_use));
       pk[rg / 2] = pack_bf16x2(p0, p1);
       pk[rg / 2 + 1] = pack_bf16x2(p2, p3);
-      psum = bf16x2_sum_acc(pk[rg / 2], psum);
-      psum = bf16x2_sum_acc(pk[rg / 2 + 1], psum);
-      pesum += (p0 + p1) + (p2 + p3);
+      psum += (p0 + p1) + (p2 + p3);
     }
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
@@ -322,11 +320,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
     }
   }
   l_run += psum;
-  le_run += pesum;
   if (row_ok) {
     const OutArg po{a.part_o, 0, 0, 0, 1};
     write_row(po, sel_part_o(a, slot, b, pos, tok, h), a.part_lse + sel_part_lse(a, slot, b, pos, tok, h), oacc,
-              m_run, l_run, le_run, hh);
+              m_run, l_run, hh);
   }
 }
 

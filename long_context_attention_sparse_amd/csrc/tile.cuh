@@ -32,37 +32,45 @@ __device__ __forceinline__ void softcap_n(f32x16* s, float cap_in, float cap_out
 // Online softmax, first step of a chunk (the weights and the P V product follow in the
 // kernel): the chunk's row maximum over NB blocks of 32 keys (masked scores -inf; m_run in
 // scaled log2 units) and the lazy rescale — the reference maximum only moves, rescaling O
-// and the sums, when the new maximum exceeds it by more than 2^8.  Two normalisers are
-// kept: l_run sums the bf16-rounded weights the PV product uses (O is then an exact convex
-// combination of V rows, so a dominant key's rounding cancels) and le_run sums the exact
-// weights (for LSE).
-template <int NB>
-__device__ __forceinline__ void softmax_max_n(const f32x16* s, float scale_log2, float& m_run, float& l_run,
-                                              float& le_run, f32x16* oacc) {
-  float mx = kNegInf;
-#pragma unroll
-  for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-  mx = fmaxf(mx, shfl_xor_f(mx, 32)) * scale_log2;
+// and the normaliser, when the new maximum exceeds it by more than 2^8.  One normaliser is
+// kept: l_run sums the float32 weights before their rounding to bf16 for the P V product.
+// It divides O and gives LSE, so O's error is the weights' bf16 rounding alone: at most
+// 2^-9 times the weighted mean of |v| over the attended keys.
+// The lazy rescale for a chunk whose row maximum (scaled log2 units) is mx.
+__device__ __forceinline__ void softmax_rescale(float mx, float& m_run, float& l_run, f32x16* oacc) {
   const float m_new = fmaxf(m_run, mx);
   const bool need = m_new > m_run + kSlack;
   if (__any(need)) {
     const float alpha = need ? exp2_fast(m_run - m_new) : 1.f;
     if (need) m_run = m_new;
     l_run *= alpha;
-    le_run *= alpha;
 #pragma unroll
     for (int db = 0; db < TD / 32; ++db) oacc[db] *= alpha;
   }
 }
 
+// Row maximum of NB blocks of 32 raw scores (the two lanes 32 apart hold one row).
+template <int NB>
+__device__ __forceinline__ float row_max_n(const f32x16* s) {
+  float mx = kNegInf;
+#pragma unroll
+  for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+  return fmaxf(mx, shfl_xor_f(mx, 32));
+}
+
+template <int NB>
+__device__ __forceinline__ void softmax_max_n(const f32x16* s, float scale_log2, float& m_run, float& l_run,
+                                              f32x16* oacc) {
+  softmax_rescale(row_max_n<NB>(s) * scale_log2, m_run, l_run, oacc);
+}
+
 // Normalise and store one query row's O (32 rows per wave, 64 dims per lane) and its LSE.
 // o_off: element offset of the row start (head dim 0) in the output.
 __device__ __forceinline__ void write_row(const OutArg& o, int64_t o_off, float* lse_ptr, const f32x16* oacc,
-                                          float m_run, float l_run, float le_run, int hh) {
+                                          float m_run, float l_run, int hh) {
   const float lt = l_run + shfl_xor_f(l_run, 32);
-  const float le = le_run + shfl_xor_f(le_run, 32);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
 #pragma unroll
   for (int db = 0; db < TD / 32; ++db)
@@ -72,7 +80,7 @@ __device__ __forceinline__ void write_row(const OutArg& o, int64_t o_off, float*
       store4(o, o_off + d, oacc[db][g4 * 4] * inv, oacc[db][g4 * 4 + 1] * inv, oacc[db][g4 * 4 + 2] * inv,
              oacc[db][g4 * 4 + 3] * inv);
     }
-  if (hh == 0 && lse_ptr) *lse_ptr = le > 0.f ? (m_run + log2f(le)) * kLn2 : kNegInf;
+  if (hh == 0 && lse_ptr) *lse_ptr = lt > 0.f ? (m_run + log2f(lt)) * kLn2 : kNegInf;
 }
 
 // ---- direct global->LDS tiles (global_load_lds_dwordx4) and transposed LDS reads ----
