@@ -125,6 +125,7 @@ struct BwdArgs {
   float* dk;                   // [B, Sk, Hkv, D] (variable length: [total_k, Hkv, D]) float32, contiguous
   float* dv;
   float* dsum;                 // sum_d dO * O, laid out as lse
+  float* lse2;                 // lse in log2 units, +inf for a row with no keys (its weights are 0)
   PatternArg pat;              // kind 0 dense or 1 block lists
   const int32_t* cu_q;         // variable length: prefix sums of the query / key lengths, else null
   const int32_t* cu_k;

@@ -69,7 +69,8 @@ __device__ __forceinline__ int64_t bwd_lse_idx(const BwdArgs& a, int b, const Bw
   return a.cu_q ? (int64_t)h * a.cu_q[a.B] + s.q_tok + row : ((int64_t)b * a.Hq + h) * a.Sq + row;
 }
 
-// D = sum_d dO * O: 16 threads per row, 16 rows per workgroup.
+// D = sum_d dO * O, and the LSE in log2 units with +inf for a row that has no keys (so that
+// exp2(s - lse2) is 0 there without a test): 16 threads per row, 16 rows per workgroup.
 __global__ __launch_bounds__(256) void bwd_dot_kernel(BwdArgs a) {
   const int64_t row = (int64_t)wg_x() * 16 + (tid_x() >> 4);  // (token, head), head fastest
   const int part = tid_x() & 15;
@@ -106,7 +107,12 @@ __global__ __launch_bounds__(256) void bwd_dot_kernel(BwdArgs a) {
   for (int x = 0; x < 4; ++x) acc += bf16_lo(dv[x]) * ov[2 * x] + bf16_hi(dv[x]) * ov[2 * x + 1];
 #pragma unroll
   for (int off = 8; off >= 1; off >>= 1) acc += shfl_xor_f(acc, off);
-  if (part == 0) a.dsum[a.cu_q ? (int64_t)h * tokens + tok : ((int64_t)b * a.Hq + h) * a.Sq + s] = acc;
+  if (part == 0) {
+    const int64_t at = a.cu_q ? (int64_t)h * tokens + tok : ((int64_t)b * a.Hq + h) * a.Sq + s;
+    a.dsum[at] = acc;
+    const float lv = a.lse[at];
+    a.lse2[at] = lv == kNegInf ? kPosInf : lv * kLog2e;
+  }
 }
 
 // ---- key-sub-block lists ----
@@ -330,6 +336,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
   const bool ds_wave = w & 1;    // role (wave-uniform)
   const int lq = l & 31, hh = l >> 5;
   const int key = key0 + kg * 32 + lq;  // this lane's key
+  // the rows that see it: [rlo, q_len) (causal: from the row of its diagonal on; none past the keys)
+  const int rlo = key < sq.k_len ? (a.causal ? key - delta : 0) : INT_MAX;
 
   // K (P wave) or V (dS wave) rows of the group's keys: the B operand of S^T / dP^T
   const TensorArg& kv = ds_wave ? a.v : a.k;
@@ -400,9 +408,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
       __builtin_amdgcn_global_load_lds(qp + piece, BSA_LDS(nq + (w * 8 + x * 4) * RS), 16, 0, 0);
       __builtin_amdgcn_global_load_lds(dp + piece, BSA_LDS(nd + (w * 8 + x * 4) * RS), 16, 0, 0);
     }
-    if (w < 2 && l < 32) {  // LSE (wave 0) and D (wave 1) of the 32 rows, one per lane (clamped)
+    if (w < 2 && l < 32) {  // LSE (log2 units, wave 0) and D (wave 1) of the 32 rows, one per lane (clamped)
       const int r = min(q0 + l, sq.q_len - 1);
-      const float* src = (w == 0 ? a.lse : a.dsum) + lse_seq + (int64_t)h * lse_hs + r;
+      const float* src = (w == 0 ? a.lse2 : a.dsum) + lse_seq + (int64_t)h * lse_hs + r;
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(src), BSA_LDS(w == 0 ? nl : nm), 4, 0, 0);
     }
   };
@@ -434,18 +442,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
     // lane: key; register r: slab row 8(r/4) + 4hh + r%4
     uint32_t op[8], xf[CAP ? 4 : 1];
     if (!ds_wave) {
+      // every key of the group sees every row of the slab: no per-element test (wave-uniform)
+      const int klast = key0 + kg * 32 + 31;
+      const bool full = klast < sq.k_len && q0 + 31 < sq.q_len && (!a.causal || klast <= q0 + delta);
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const f32x4 lv = *reinterpret_cast<const f32x4*>(lb + g4 * 8 + hh * 4);
+        const f32x4 lv = *reinterpret_cast<const f32x4*>(lb + g4 * 8 + hh * 4);  // log2 units, +inf: no keys
         float p[4];
         float pf[4];  // what the dS wave multiplies by (dP - D): P, times the cap's derivative
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int row = q0 + g4 * 8 + hh * 4 + e;
-          const bool vis = key < sq.k_len && row < sq.q_len && lv[e] != kNegInf && (!a.causal || key <= row + delta);
           float xs = x[g4 * 4 + e];
           if constexpr (CAP) xs = softcap_score(xs, a.cap_in, a.cap_out);
-          p[e] = vis ? exp2_fast(fmaf(xs, a.scale_log2, -lv[e] * kLog2e)) : 0.f;
+          p[e] = exp2_fast(fmaf(xs, a.scale_log2, -lv[e]));
+          if (!full) {
+            const int row = q0 + g4 * 8 + hh * 4 + e;
+            p[e] = row >= rlo && row < sq.q_len ? p[e] : 0.f;
+          }
           if constexpr (CAP) {
             const float tc = xs / a.cap_out;  // tanh of the capped argument
             pf[e] = p[e] * (1.f - tc * tc);
@@ -619,9 +632,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4
                                  : u32x4{0, 0, 0, 0});
   }
   const int64_t rr = bwd_lse_idx(a, b, sq, h, row);
-  const float lse2 = row_ok ? a.lse[rr] * kLog2e : kNegInf;
+  const float lse2 = row_ok ? a.lse2[rr] : kPosInf;  // +inf: no keys, every weight 0
   const float dsv = row_ok ? a.dsum[rr] : 0.f;
-  const int lim = !row_ok || lse2 == kNegInf ? -1 : (a.causal ? min(row + delta, sq.k_len - 1) : sq.k_len - 1);
+  const int lim = !row_ok ? -1 : (a.causal ? min(row + delta, sq.k_len - 1) : sq.k_len - 1);
+  // the last key every row of this wave sees (wave-uniform; -1 when a row is past the sequence)
+  const int wrow = r0 + w * 32;
+  const int lim_w = wrow + 31 < sq.q_len ? (a.causal ? min(wrow + delta, sq.k_len - 1) : sq.k_len - 1) : -1;
   int koff[D / 16];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) koff[ks] = lq * RS + (((ks * 2 + hh) ^ bwd_swz(lq)) << 3);
@@ -696,6 +712,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (xn < n_sub) issue(key0n, nk, nv);
+    // every row of this wave sees all 64 keys: no per-element test (wave-uniform)
+    const bool full = key0 + 63 <= lim_w;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       f32x16 st = {}, dpt = {};
@@ -713,10 +731,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4
         float d2[2];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          const int kk = key0 + kb * 32 + ((r + e) >> 2) * 8 + hh * 4 + ((r + e) & 3);
           float xs = st[r + e];
           if constexpr (CAP) xs = softcap_score(xs, a.cap_in, a.cap_out);
-          float p = kk <= lim ? exp2_fast(fmaf(xs, a.scale_log2, -lse2)) : 0.f;
+          float p = exp2_fast(fmaf(xs, a.scale_log2, -lse2));
+          if (!full) {
+            const int kk = key0 + kb * 32 + ((r + e) >> 2) * 8 + hh * 4 + ((r + e) & 3);
+            p = kk <= lim ? p : 0.f;
+          }
           if constexpr (CAP) {
             const float tc = xs / a.cap_out;  // the cap's derivative: 1 - tanh^2
             p *= 1.f - tc * tc;

@@ -417,7 +417,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct BwdLayout {
   int BM = 0, SB = 0, nqb = 0, nks = 0, nkb = 0, W = 0, n_lists = 0, chunk_bound = 0;
-  size_t dsum = 0, counts = 0, offsets = 0, entries = 0, chunkp = 0, bits = 0, part = 0, total = 0;
+  size_t dsum = 0, lse2 = 0, counts = 0, offsets = 0, entries = 0, chunkp = 0, bits = 0, part = 0, total = 0;
 };
 
 // Shapes the backward kernels take; total == 0 otherwise.
@@ -437,6 +437,7 @@ BwdLayout bwd_layout(const bsa_problem& p, const bsa_pattern* pat) {
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t at = off; off = align256(off + bytes); return at; };
   L.dsum = take(sizeof(float) * (size_t)p.B * p.Hq * Sq);  // at least Hq * total_q
+  L.lse2 = take(sizeof(float) * (size_t)p.B * p.Hq * Sq);
   L.counts = take(sizeof(int32_t) * L.n_lists);
   L.chunkp = take(sizeof(int32_t) * (L.n_lists + 1));
   size_t units;  // upper bound on the 32-row slabs over all lists
@@ -504,6 +505,7 @@ bsa_status bsa_bwd(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, bsa_tens
   a.dk = dk;
   a.dv = dv;
   a.dsum = reinterpret_cast<float*>(base + L.dsum);
+  a.lse2 = reinterpret_cast<float*>(base + L.lse2);
   a.pat = parg(pat);
   a.cu_q = p.cu_seqlens_q;
   a.cu_k = p.cu_seqlens_k;

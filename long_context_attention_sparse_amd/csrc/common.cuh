@@ -26,6 +26,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kNegInf = -__builtin_inff();
+constexpr float kPosInf = __builtin_inff();
 
 // ---------------------------------------------------------------------------
 // Small helpers
