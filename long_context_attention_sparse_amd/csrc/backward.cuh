@@ -25,6 +25,7 @@
 //               P^T and dP^T = V dO^T with a query per lane, then dQ^T += K^T dS^T
 // No kernel accumulates with atomics: dK/dV belong to one workgroup, dQ to another.
 #pragma once
+#include <type_traits>
 #include "tile.cuh"
 
 namespace bsa {
@@ -396,17 +397,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
   // Q and dO rows q0 + 8w + 4x + l/16 of the slab (clamped to the last row: finite data the
   // mask then ignores), lane l into slot l%16; LSE (wave 0) and D (wave 1) one row per lane
   const int lrow = l >> 4, lslot = l & 15;
+  // Q and dO rows go through buffer resources based at the slab's first row and covering its
+  // rows inside the sequence: a row past the sequence reads zeros (finite, masked), and the
+  // per-lane offsets are the same for every slab
+  const uint32_t qrow = (uint32_t)a.q.ss * 2u, drow = (uint32_t)a.dout.ss * 2u;
   auto issue = [&](int h, int q0, uint16_t* __restrict__ nq, uint16_t* __restrict__ nd, float* __restrict__ nl,
                    float* __restrict__ nm) __attribute__((always_inline)) {
+    const uint32_t last = (uint32_t)min(sq.q_len - 1 - q0, 31);
+    const __amdgpu_buffer_rsrc_t rq = rows_rsrc(qseq + (int64_t)q0 * a.q.ss + (int64_t)h * a.q.sh, last * qrow + 256u);
+    const __amdgpu_buffer_rsrc_t rd =
+        rows_rsrc(dseq + (int64_t)q0 * a.dout.ss + (int64_t)h * a.dout.sh, last * drow + 256u);
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
-      const int rl = w * 8 + x * 4 + lrow;
-      const int gr = min(q0 + rl, sq.q_len - 1);
+      const uint32_t rl = (uint32_t)(w * 8 + x * 4 + lrow);
       const uint32_t piece = (uint32_t)((lslot ^ bwd_swz(rl)) << 4);
-      const char* qp = reinterpret_cast<const char*>(qseq + (int64_t)gr * a.q.ss + (int64_t)h * a.q.sh);
-      const char* dp = reinterpret_cast<const char*>(dseq + (int64_t)gr * a.dout.ss + (int64_t)h * a.dout.sh);
-      __builtin_amdgcn_global_load_lds(qp + piece, BSA_LDS(nq + (w * 8 + x * 4) * RS), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(dp + piece, BSA_LDS(nd + (w * 8 + x * 4) * RS), 16, 0, 0);
+      buffer_load_lds16(rq, nq + (w * 8 + x * 4) * RS, rl * qrow + piece);
+      buffer_load_lds16(rd, nd + (w * 8 + x * 4) * RS, rl * drow + piece);
     }
     if (w < 2 && l < 32) {  // LSE (log2 units, wave 0) and D (wave 1) of the 32 rows, one per lane (clamped)
       const int r = min(q0 + l, sq.q_len - 1);
@@ -442,39 +448,48 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
     // lane: key; register r: slab row 8(r/4) + 4hh + r%4
     uint32_t op[8], xf[CAP ? 4 : 1];
     if (!ds_wave) {
-      // every key of the group sees every row of the slab: no per-element test (wave-uniform)
-      const int klast = key0 + kg * 32 + 31;
-      const bool full = klast < sq.k_len && q0 + 31 < sq.q_len && (!a.causal || klast <= q0 + delta);
+      // P (and, with a softcap, what the dS wave multiplies by dP - D) for the slab; FULL: every
+      // key of the group sees every row of the slab, so no element needs a test.  Two copies of
+      // the code, picked once per slab (wave-uniform), keep the tests out of the common one.
+      auto weights = [&](auto full_c) __attribute__((always_inline)) {
+        constexpr bool FULL = decltype(full_c)::value;
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const f32x4 lv = *reinterpret_cast<const f32x4*>(lb + g4 * 8 + hh * 4);  // log2 units, +inf: no keys
-        float p[4];
-        float pf[4];  // what the dS wave multiplies by (dP - D): P, times the cap's derivative
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x4 lv = *reinterpret_cast<const f32x4*>(lb + g4 * 8 + hh * 4);  // log2 units, +inf: no keys
+          float p[4];
+          float pf[4];  // what the dS wave multiplies by (dP - D): P, times the cap's derivative
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float xs = x[g4 * 4 + e];
-          if constexpr (CAP) xs = softcap_score(xs, a.cap_in, a.cap_out);
-          p[e] = exp2_fast(fmaf(xs, a.scale_log2, -lv[e]));
-          if (!full) {
-            const int row = q0 + g4 * 8 + hh * 4 + e;
-            p[e] = row >= rlo && row < sq.q_len ? p[e] : 0.f;
+          for (int e = 0; e < 4; ++e) {
+            float xs = x[g4 * 4 + e];
+            if constexpr (CAP) xs = softcap_score(xs, a.cap_in, a.cap_out);
+            p[e] = exp2_fast(fmaf(xs, a.scale_log2, -lv[e]));
+            if constexpr (!FULL) {
+              const int row = q0 + g4 * 8 + hh * 4 + e;
+              p[e] = row >= rlo && row < sq.q_len ? p[e] : 0.f;
+            }
+            if constexpr (CAP) {
+              const float tc = xs / a.cap_out;  // tanh of the capped argument
+              pf[e] = p[e] * (1.f - tc * tc);
+            } else {
+              pf[e] = p[e];
+            }
           }
+          op[g4 * 2] = pack_bf16x2(p[0], p[1]);
+          op[g4 * 2 + 1] = pack_bf16x2(p[2], p[3]);
           if constexpr (CAP) {
-            const float tc = xs / a.cap_out;  // tanh of the capped argument
-            pf[e] = p[e] * (1.f - tc * tc);
-          } else {
-            pf[e] = p[e];
+            xf[(g4 & 1) * 2] = pack_bf16x2(pf[0], pf[1]);
+            xf[(g4 & 1) * 2 + 1] = pack_bf16x2(pf[2], pf[3]);
+            // stored a half at a time, so that only four of these registers are live
+            if (g4 & 1) *reinterpret_cast<u32x4*>(pslot + (g4 >> 1) * 256) = u32x4{xf[0], xf[1], xf[2], xf[3]};
           }
         }
-        op[g4 * 2] = pack_bf16x2(p[0], p[1]);
-        op[g4 * 2 + 1] = pack_bf16x2(p[2], p[3]);
-        if constexpr (CAP) {
-          xf[(g4 & 1) * 2] = pack_bf16x2(pf[0], pf[1]);
-          xf[(g4 & 1) * 2 + 1] = pack_bf16x2(pf[2], pf[3]);
-          // stored a half at a time, so that only four of these registers are live
-          if (g4 & 1) *reinterpret_cast<u32x4*>(pslot + (g4 >> 1) * 256) = u32x4{xf[0], xf[1], xf[2], xf[3]};
-        }
-      }
+      };
+      const int klast = key0 + kg * 32 + 31;
+      // (with a softcap one copy, the tested one: two would not fit the registers)
+      if (!CAP && klast < sq.k_len && q0 + 31 < sq.q_len && (!a.causal || klast <= q0 + delta))
+        weights(std::true_type{});
+      else
+        weights(std::false_type{});
       if constexpr (!CAP) {
         *reinterpret_cast<u32x4*>(pslot) = u32x4{op[0], op[1], op[2], op[3]};
         *reinterpret_cast<u32x4*>(pslot + 256) = u32x4{op[4], op[5], op[6], op[7]};
@@ -684,16 +699,20 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4
       reinterpret_cast<const uint16_t*>(a.k.ptr) + bwd_row(a.k, packed, b, sq.k_tok, 0) + (int64_t)hkv * a.k.sh;
   const uint16_t* vbase =
       reinterpret_cast<const uint16_t*>(a.v.ptr) + bwd_row(a.v, packed, b, sq.k_tok, 0) + (int64_t)hkv * a.v.sh;
+  // through buffer resources based at the block's first key and covering its keys inside the
+  // sequence: a key past the sequence reads zeros (finite, masked), and the per-lane offsets
+  // are the same for every block
+  const uint32_t krow = (uint32_t)a.k.ss * 2u, vrow = (uint32_t)a.v.ss * 2u;
   auto issue = [&](int key0, uint16_t* __restrict__ nk, uint16_t* __restrict__ nv) __attribute__((always_inline)) {
+    const uint32_t last = (uint32_t)min(sq.k_len - 1 - key0, 63);
+    const __amdgpu_buffer_rsrc_t rk = rows_rsrc(kbase + (int64_t)key0 * a.k.ss, last * krow + 256u);
+    const __amdgpu_buffer_rsrc_t rv = rows_rsrc(vbase + (int64_t)key0 * a.v.ss, last * vrow + 256u);
 #pragma unroll
     for (int x = 0; x < RPW / 4; ++x) {
-      const int rl = w * RPW + x * 4 + lrow;
-      const int gk = min(key0 + rl, sq.k_len - 1);
+      const uint32_t rl = (uint32_t)(w * RPW + x * 4 + lrow);
       const uint32_t piece = (uint32_t)((lslot ^ bwd_swz(rl)) << 4);
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(kbase + (int64_t)gk * a.k.ss) + piece,
-                                       BSA_LDS(nk + (w * RPW + x * 4) * RS), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(vbase + (int64_t)gk * a.v.ss) + piece,
-                                       BSA_LDS(nv + (w * RPW + x * 4) * RS), 16, 0, 0);
+      buffer_load_lds16(rk, nk + (w * RPW + x * 4) * RS, rl * krow + piece);
+      buffer_load_lds16(rv, nv + (w * RPW + x * 4) * RS, rl * vrow + piece);
     }
   };
 
@@ -724,28 +743,34 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4
         st = mfma32x32x16(as_bf16x8(ka), qreg[ks], st);
         dpt = mfma32x32x16(as_bf16x8(va), doreg[ks], dpt);
       }
-      // lane: query; register r: key key0 + 32kb + 8(r/4) + 4hh + r%4
+      // lane: query; register r: key key0 + 32kb + 8(r/4) + 4hh + r%4.  FULL: every row of the
+      // wave sees all 64 keys (wave-uniform), so no element needs a test
       uint32_t dd[8];
+      auto weights = [&](auto full_c) __attribute__((always_inline)) {
+        constexpr bool FULL = decltype(full_c)::value;
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        float d2[2];
+        for (int r = 0; r < 16; r += 2) {
+          float d2[2];
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          float xs = st[r + e];
-          if constexpr (CAP) xs = softcap_score(xs, a.cap_in, a.cap_out);
-          float p = exp2_fast(fmaf(xs, a.scale_log2, -lse2));
-          if (!full) {
-            const int kk = key0 + kb * 32 + ((r + e) >> 2) * 8 + hh * 4 + ((r + e) & 3);
-            p = kk <= lim ? p : 0.f;
+          for (int e = 0; e < 2; ++e) {
+            float xs = st[r + e];
+            if constexpr (CAP) xs = softcap_score(xs, a.cap_in, a.cap_out);
+            float p = exp2_fast(fmaf(xs, a.scale_log2, -lse2));
+            if constexpr (!FULL) {
+              const int kk = key0 + kb * 32 + ((r + e) >> 2) * 8 + hh * 4 + ((r + e) & 3);
+              p = kk <= lim ? p : 0.f;
+            }
+            if constexpr (CAP) {
+              const float tc = xs / a.cap_out;  // the cap's derivative: 1 - tanh^2
+              p *= 1.f - tc * tc;
+            }
+            d2[e] = p * (dpt[r + e] - dsv);
           }
-          if constexpr (CAP) {
-            const float tc = xs / a.cap_out;  // the cap's derivative: 1 - tanh^2
-            p *= 1.f - tc * tc;
-          }
-          d2[e] = p * (dpt[r + e] - dsv);
+          dd[r / 2] = pack_bf16x2(d2[0], d2[1]);
         }
-        dd[r / 2] = pack_bf16x2(d2[0], d2[1]);
-      }
+      };
+      if (full) weights(std::true_type{});
+      else weights(std::false_type{});
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) {
         const u32x4 bop = {dd[hb * 4], dd[hb * 4 + 1], dd[hb * 4 + 2], dd[hb * 4 + 3]};

@@ -38,6 +38,7 @@ bsa_status check_problem(const bsa_problem* prob, const bsa_tensor& q, const bsa
   if (p.D != 64 && p.D != 128) return BSA_ERR_UNSUPPORTED;
   if (!aligned_rows(q, 2) || !aligned_rows(k, 2) || !aligned_rows(v, 2)) return BSA_ERR_INVALID_ARG;
   if (!aligned_rows(o, o.dtype == BSA_F32 ? 4 : 2)) return BSA_ERR_INVALID_ARG;
+  if (!row_stride_ok(q, 2) || !row_stride_ok(k, 2) || !row_stride_ok(v, 2)) return BSA_ERR_UNSUPPORTED;
   return BSA_OK;
 }
 
@@ -487,6 +488,7 @@ bsa_status bsa_bwd(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, bsa_tens
   if (!lse || !dout.ptr || !dq || !dk || !dv) return BSA_ERR_INVALID_ARG;
   if (dout.dtype != BSA_BF16) return BSA_ERR_UNSUPPORTED;
   if (!aligned_rows(dout, 2)) return BSA_ERR_INVALID_ARG;
+  if (!row_stride_ok(dout, 2)) return BSA_ERR_UNSUPPORTED;
   if ((reinterpret_cast<uintptr_t>(dq) | reinterpret_cast<uintptr_t>(dk) | reinterpret_cast<uintptr_t>(dv)) & 15)
     return BSA_ERR_INVALID_ARG;
   const BwdLayout L = bwd_layout(p, pat);

@@ -56,6 +56,12 @@ inline bsa_status launch_status() {
 
 // 16-byte alignment of every row start: base pointer and all strides must keep
 // head-dim rows 16-byte aligned for the vector loads.
+// Token (row) strides the kernels take: non-negative and at most 32 MB, so that the byte offsets
+// of 64 rows from a block's first row fit the 32-bit offsets of buffer loads.
+inline bool row_stride_ok(const bsa_tensor& t, int elem_bytes) {
+  return t.stride_s >= 0 && t.stride_s * elem_bytes <= ((int64_t)1 << 25);
+}
+
 inline bool aligned_rows(const bsa_tensor& t, int elem_bytes) {
   const uintptr_t p = reinterpret_cast<uintptr_t>(t.ptr);
   auto ok = [&](int64_t s) { return ((s * elem_bytes) & 15) == 0; };
