@@ -75,7 +75,10 @@ typedef enum { BSA_BF16 = 0, BSA_F32 = 1 } bsa_dtype;
 
 /* A strided 4-D (or varlen 3-D) tensor view.  Strides are in elements; the
  * last (head-dim) axis is contiguous.  For varlen tensors stride_b is
- * ignored and the token axis is indexed by cu_seqlens[b] + s. */
+ * ignored and the token axis is indexed by cu_seqlens[b] + s.  The token
+ * stride of q, k, v (and dout) must be non-negative and at most 32 MB in
+ * bytes (the kernels address up to 64 tokens from a block's first one with
+ * 32-bit offsets); larger ones give BSA_ERR_UNSUPPORTED. */
 typedef struct {
   void* ptr;
   int32_t dtype; /* bsa_dtype */

@@ -88,6 +88,11 @@ def test_fwd_argument_errors(lib):
     assert _fwd(lib, _prob(), k=_t(dtype=1)) == bd.BSA_ERR_UNSUPPORTED            # f32 inputs
     assert _fwd(lib, _prob(), q=_t(ptr=18)) == bd.BSA_ERR_INVALID_ARG             # misaligned rows
     assert _fwd(lib, _prob(), o=_t(dtype=7)) == bd.BSA_ERR_INVALID_ARG            # output dtype
+    assert _fwd(lib, _prob(), k=_t(ss=1 << 25)) == bd.BSA_ERR_UNSUPPORTED          # 64 MB token stride
+    assert _fwd(lib, _prob(), v=_t(ss=-128)) == bd.BSA_ERR_UNSUPPORTED             # negative token stride
+    bad_kind = bd._Pattern(9, 2, 64, 64, 4, 0, 16, 16, None, None, 0, 0, 0)
+    assert _fwd(lib, _prob(), q=_t(ss=1 << 24), pat=bad_kind) == bd.BSA_ERR_INVALID_ARG  # 32 MB passes, the
+                                                                                    # pattern check fails
 
 
 def test_pattern_errors(lib):
