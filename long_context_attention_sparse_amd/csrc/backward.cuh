@@ -168,7 +168,11 @@ __global__ __launch_bounds__(256) void bwd_list_count_kernel(BwdArgs a) {
   a.counts[x] = a.list_by_kv ? n * a.G : n;
 }
 
-// One wave per list: its pairs, h * nqb + i, from offsets[list] on, ordered by query head of
+// A list entry: query head h and query block i as (h << kBwdEntryShift) | i, so that reading one
+// back takes a shift and a mask (the host bounds the query blocks and heads to fit).
+constexpr int kBwdEntryShift = 20;
+
+// One wave per list: its pairs (h, i), from offsets[list] on, ordered by query head of
 // the group, then query block (lists per kv head: each query block's G heads in turn).  Lane w
 // takes bitmap word w (64 words at a time); a prefix sum over the wave of the words' entry
 // counts gives each lane where its entries go.
@@ -202,9 +206,9 @@ __global__ __launch_bounds__(256) void bwd_list_fill_kernel(BwdArgs a) {
         const int i = wd * 32 + __builtin_ctz(m);
         m &= m - 1;
         if (a.list_by_kv) {
-          for (int gg = 0; gg < a.G; ++gg) out[k++] = (hkv * a.G + gg) * a.nqb + i;
+          for (int gg = 0; gg < a.G; ++gg) out[k++] = ((hkv * a.G + gg) << kBwdEntryShift) | i;
         } else {
-          out[k++] = ht * a.nqb + i;
+          out[k++] = (ht << kBwdEntryShift) | i;
         }
       }
       base += __shfl(incl, 63, 64);
@@ -293,7 +297,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
   __shared__ __attribute__((aligned(16))) uint16_t Ds[2][32 * RS];
   __shared__ __attribute__((aligned(16))) float ls[2][32];
   __shared__ __attribute__((aligned(16))) float dsm[2][32];
-  __shared__ __attribute__((aligned(16))) uint32_t Ps[2][64 * 8];  // P of each key group, lane layout
+  __shared__ __attribute__((aligned(16))) float Ps[2][64 * 16];  // float32 P of each key group, lane layout
 
   const int n_lists = a.B * a.Hkv * a.nks;
   const int wid = wg_x();
@@ -367,7 +371,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
 #pragma unroll
   for (int x = 0; x < D / 32; ++x) acc[x] = f32x16{};
 
-  const int slabs = a.BM / 32;
+  const int slabs = a.BM / 32;       // 2 or 4
+  const int slabs_log2 = a.BM == 128 ? 2 : 1;
   const int total_slabs = (sq.q_len + 31) / 32;
   const bool dense = a.pat.kind == 0;
   const int first_slab = dense ? bwd_first_slab(a, key0, delta) : 0;
@@ -381,9 +386,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
         h = hkv * a.G + u / per;
         q0 = (first_slab + u % per) * 32;
       } else {
-        const int e = a.entries[list0 + u / slabs];
-        h = e / a.nqb;
-        q0 = (e - h * a.nqb) * a.BM + (u % slabs) * 32;
+        const int e = a.entries[list0 + (u >> slabs_log2)];
+        h = e >> kBwdEntryShift;
+        q0 = (e & ((1 << kBwdEntryShift) - 1)) * a.BM + (u & (slabs - 1)) * 32;
       }
       if (q0 < sq.q_len && !(a.causal && q0 + 31 + delta < key0)) return u;
     }
@@ -421,10 +426,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
     }
   };
 
-  uint32_t* pslot = Ps[kg] + l * 4;  // two 16-byte halves per lane, 1 KB apart (no bank conflicts)
+  float* pslot = Ps[kg] + l * 4;  // four 16-byte quarters per lane, 1 KB apart (no bank conflicts)
   int h, q0;
   int u = next_unit(u0, h, q0);
-  int buf = 0;
   if (u < u1) issue(h, q0, Qs[0], Ds[0], ls[0], dsm[0]);
   // One slab from the current buffers while the next slab streams into the other ones.  The
   // restrict-qualified buffer parameters tell the compiler that those loads cannot alias the
@@ -446,7 +450,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
     for (int ks = 0; ks < D / 16; ++ks)
       x = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(rows + aoff[ks])), kvreg[ks], x);
     // lane: key; register r: slab row 8(r/4) + 4hh + r%4
-    uint32_t op[8], xf[CAP ? 4 : 1];
+    uint32_t op[8];
     if (!ds_wave) {
       // P (and, with a softcap, what the dS wave multiplies by dP - D) for the slab; FULL: every
       // key of the group sees every row of the slab, so no element needs a test.  Two copies of
@@ -476,12 +480,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
           }
           op[g4 * 2] = pack_bf16x2(p[0], p[1]);
           op[g4 * 2 + 1] = pack_bf16x2(p[2], p[3]);
-          if constexpr (CAP) {
-            xf[(g4 & 1) * 2] = pack_bf16x2(pf[0], pf[1]);
-            xf[(g4 & 1) * 2 + 1] = pack_bf16x2(pf[2], pf[3]);
-            // stored a half at a time, so that only four of these registers are live
-            if (g4 & 1) *reinterpret_cast<u32x4*>(pslot + (g4 >> 1) * 256) = u32x4{xf[0], xf[1], xf[2], xf[3]};
-          }
+          // the dS wave's factor, unrounded
+          *reinterpret_cast<f32x4*>(pslot + g4 * 256) = f32x4{pf[0], pf[1], pf[2], pf[3]};
         }
       };
       const int klast = key0 + kg * 32 + 31;
@@ -490,10 +490,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
         weights(std::true_type{});
       else
         weights(std::false_type{});
-      if constexpr (!CAP) {
-        *reinterpret_cast<u32x4*>(pslot) = u32x4{op[0], op[1], op[2], op[3]};
-        *reinterpret_cast<u32x4*>(pslot + 256) = u32x4{op[4], op[5], op[6], op[7]};
-      }
     }
     // P is in LDS for the dS waves.  The barrier waits for LDS operations only (a release
     // fence would also wait for the next slab's loads, which write LDS); the empty asm
@@ -502,19 +498,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if (ds_wave) {
-      const u32x4 p0 = *reinterpret_cast<const u32x4*>(pslot);
-      const u32x4 p1 = *reinterpret_cast<const u32x4*>(pslot + 256);
-      const uint32_t pw[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const f32x4 dm = *reinterpret_cast<const f32x4*>(mb + g4 * 8 + hh * 4);
+        const f32x4 pq = *reinterpret_cast<const f32x4*>(pslot + g4 * 256);
         float d[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t pair = pw[g4 * 2 + (e >> 1)];
-          const float pe = (e & 1) ? bf16_hi(pair) : bf16_lo(pair);
-          d[e] = pe * (x[g4 * 4 + e] - dm[e]);
-        }
+        for (int e = 0; e < 4; ++e) d[e] = pq[e] * (x[g4 * 4 + e] - dm[e]);
         op[g4 * 2] = pack_bf16x2(d[0], d[1]);
         op[g4 * 2 + 1] = pack_bf16x2(d[2], d[3]);
       }
@@ -533,6 +523,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
     h = hn;
     q0 = q0n;
   };
+  int buf = 0;
   while (u < u1) {
     step(Qs[buf], Ds[buf], ls[buf], dsm[buf], Qs[buf ^ 1], Ds[buf ^ 1], ls[buf ^ 1], dsm[buf ^ 1]);
     buf ^= 1;
@@ -718,7 +709,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4
 
   int key0 = 0;
   int x = next_sub(0, key0);
-  int buf = 0;
   if (x < n_sub) issue(key0, K0, V0);
   // One key block from the current buffers while the next streams into the other ones (the
   // buffers are separate arrays, so the compiler sees that the two cannot alias and the reads
@@ -785,6 +775,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4
     x = xn;
     key0 = key0n;
   };
+  int buf = 0;
   while (x < n_sub) {
     step(buf ? K1 : K0, buf ? V1 : V0, buf ? K0 : K1, buf ? V0 : V1);
     buf ^= 1;

@@ -449,6 +449,7 @@ BwdLayout bwd_layout(const bsa_problem& p, const bsa_pattern* pat) {
     const size_t per = (size_t)std::min(pat->cap, (Sk + pat->block_N - 1) / pat->block_N);
     const size_t pairs = (size_t)p.B * Ht * L.nqb * per * (pat->block_N / L.SB) * mult;
     if (pairs >= (size_t)INT_MAX) return BwdLayout{};
+    if (L.nqb > (1 << 20) || p.Hq > (1 << 11)) return BwdLayout{};  // list entries: (head << 20) | block
     L.nkb = (Sk + pat->block_N - 1) / pat->block_N;
     L.W = (L.nqb + 31) / 32;
     L.offsets = take(sizeof(int32_t) * (L.n_lists + 1));
