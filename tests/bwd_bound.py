@@ -15,7 +15,8 @@ sum of n products whose rounding errors add up to at most
   dQ[r, d]: scale * ((2u + n eps) * sum_k A[r, k] |K[k, d]| + dD_r * sum_k |P g|[r, k] |K[k, d]|)
   dK[k, d]: scale * ((2u + n eps) * sum_r A[r, k] |Q[r, d]| + sum_r |P g|[r, k] dD_r |Q[r, d]|)
 with g the softcap factor (1 without one), A = |P| g (|dP - Dr| + D eps |dO| |V|^T) the size of
-dS including the float32 error of dP (u for P's rounding, u for dS's), and dD_r the error of Dr:
+dS including the float32 error of dP (2u: one u for dS's rounding to bf16, one as margin, since
+both kernels now form dS from the float32 P), and dD_r the error of Dr:
 |sum_d dO (O_used - O)| (O_used the O the kernels were given, O the exact one) plus its float32
 rounding.  n is the number of products summed into the entry (keys of the row for dQ, rows that
 see the key for dK and dV), so the bound grows with the worst-case accumulation; the recomputed
