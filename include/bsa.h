@@ -334,6 +334,7 @@ bsa_status bsa_fwd_gated(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, bs
  *              [B, Sk, Hkv, D] contiguous (variable length: [total_q, Hq, D]
  *              and [total_k, Hkv, D]); every entry is written.
  *   workspace  bsa_bwd_workspace_size bytes, 256-byte aligned: row dots,
+ *              each row's LSE in log2 units (+inf for a row with no keys),
  *              a bitmap of which query blocks name each key block, the
  *              per-64-key-block lists of (query head, query block) pairs,
  *              and room for float32 dK/dV partials of lists split over
@@ -345,6 +346,9 @@ bsa_status bsa_fwd_gated(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, bs
  * workgroup per query block: no atomics on the gradients, and the lists are
  * built in a fixed order (by head, then query block), so the gradients are
  * the same bits on every run.
+ * Block patterns take at most 2^20 query blocks and 2^11 query heads (a list
+ * entry packs both in 32 bits); the workspace size is 0 and the call gives
+ * BSA_ERR_UNSUPPORTED beyond them.
  * Errors: as bsa_fwd; BSA_ERR_UNSUPPORTED outside the cases above. */
 size_t bsa_bwd_workspace_size(const bsa_problem* prob, const bsa_pattern* pat);
 bsa_status bsa_bwd(const bsa_problem* prob, bsa_tensor q, bsa_tensor k, bsa_tensor v, const bsa_pattern* pat,

@@ -175,6 +175,11 @@ def test_gated_and_vs_convert_errors(lib):
     assert wsb >= 4 * 256 * 4                                          # the row dots
     assert lib.bsa_bwd_workspace_size(ctypes.byref(_prob(Hq=4, Hkv=2, Sq=256, Sk=256, causal=1, softcap=5.0)),
                                       None) == wsb                                    # softcap: same layout
+    cnt = ctypes.c_int32(0)
+    idx = (ctypes.c_int32 * 4)()
+    many = bd._Pattern(1, 4096, 128, 128, 4, 0, ctypes.addressof(cnt), ctypes.addressof(idx), None, None, 0, 0, 0)
+    assert lib.bsa_bwd_workspace_size(ctypes.byref(_prob(Hq=4096, Hkv=2, Sq=256, Sk=256, causal=1)),
+                                      ctypes.byref(many)) == 0                       # 2^12 query heads
     bw = lib.bsa_bwd
     assert bw(ctypes.byref(bp), qs, _t(), _t(), None, qs, None, qs, 16, 16, 16, 256, wsb, None) \
         == bd.BSA_ERR_INVALID_ARG                                                            # no lse
