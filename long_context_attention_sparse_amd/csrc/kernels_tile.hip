@@ -9,18 +9,13 @@
 namespace bsa {
 
 // Final outputs use the large-chunk kernel; partial outputs (whose group boundaries fall
-// on list entries) and vertical-slash patterns on 128-row tiles (whose instantiation of
-// the large-chunk kernel this compiler rejects) the 2-stage pipelined one.
+// on list entries) the 2-stage pipelined one.
 template <int NW, int KIND>
 static void launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
-  if constexpr (KIND == 2 && NW == 4) {
+  if (a.partial)
     hipLaunchKernelGGL((prefill_pipe_kernel<KIND, NW>), dim3(a.n_items), dim3(NW * 64), 0, st, a);
-  } else {
-    if (a.partial)
-      hipLaunchKernelGGL((prefill_pipe_kernel<KIND, NW>), dim3(a.n_items), dim3(NW * 64), 0, st, a);
-    else
-      hipLaunchKernelGGL((prefill_tile_kernel<KIND, NW>), dim3(a.n_items), dim3(NW * 64), 0, st, a);
-  }
+  else
+    hipLaunchKernelGGL((prefill_tile_kernel<KIND, NW>), dim3(a.n_items), dim3(NW * 64), 0, st, a);
 }
 
 void launch_prefill(const PrefillArgs& a, int NW, int KIND, hipStream_t st) {

@@ -60,24 +60,28 @@ def _vs_inputs(seed, L, H, nnz_v, nnz_s):
     return vert, slash
 
 
-def test_vs_columns_longer_than_staging():
+@pytest.mark.parametrize("blk", [64, 128])
+def test_vs_columns_longer_than_staging(blk):
+    """More gathered columns per query block than the kernels stage in LDS (768): the rest are
+    read from memory.  64-row tiles (64-key windows) and 128-row tiles (128-key windows)."""
     L, H = 4096, 2
-    say("vertical-slash with more than 768 columns per block")
+    say(f"vertical-slash with more than 768 columns per block, {blk}-row blocks")
     vert, slash = _vs_inputs(103, L, H, 1500, 10)
     q, k, v = (normal_bf16(103, n, (L, H, 128)) for n in ("q", "k", "v"))
     sl = dev_i32([L])
-    bc, bo, cc, ci = bsa.vs_convert_indexes(sl, sl, dev_i32(vert), dev_i32(slash), L, 64, 64)
+    bc, bo, cc, ci = bsa.vs_convert_indexes(sl, sl, dev_i32(vert), dev_i32(slash), L, blk, blk)
     assert int(host(cc).max()) > 768
     cu = np.array([0, L], np.int32)
-    pat = bsa.VSPattern(bc, bo, cc, ci, 64, 64)
+    pat = bsa.VSPattern(bc, bo, cc, ci, blk, blk)
     o, lse = bsa.bsa_fwd(dev_bf16(q), dev_bf16(k), dev_bf16(v), pat, causal=True, out_dtype=torch.float32,
                          cu_seqlens_q=dev_i32(cu), cu_seqlens_k=dev_i32(cu), max_seqlen_q=L, max_seqlen_k=L)
     oh, lh = host(o), host(lse)
     g = rng(103, "rows")
-    for h, m in [(0, 63), (1, 63), (0, 40), (1, 20)]:
-        rows = np.sort(g.choice(np.arange(m * 64, m * 64 + 64), 6, replace=False))
-        wins, cols = oracle.vs_convert_item(L, L, vert[0, h], slash[0, h], m, 64, 64)
-        o_ref, lse_ref = oracle.vs_attention_rows(q, k, v, 0, h, rows, wins, cols, cu, cu, 64)
+    last = L // blk - 1
+    for h, m in [(0, last), (1, last), (0, last * 5 // 8), (1, last // 3)]:
+        rows = np.sort(g.choice(np.arange(m * blk, m * blk + blk), 6, replace=False))
+        wins, cols = oracle.vs_convert_item(L, L, vert[0, h], slash[0, h], m, blk, blk)
+        o_ref, lse_ref = oracle.vs_attention_rows(q, k, v, 0, h, rows, wins, cols, cu, cu, blk)
         check_o(oh[rows, h], o_ref, f"vs many columns h={h} m={m}")
         check_lse(lh[h, rows], lse_ref, f"vs many columns lse h={h} m={m}")
 
