@@ -131,13 +131,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
         psum += (p0 + p1) + (p2 + p3);
       }
   };
-  // O^T += V_j^T P^T, the V^T operand read with the transposing LDS read
+  // O^T += V_j^T P^T, the V^T operands read with the transposing LDS read one 16-key step
+  // ahead of their products (read just before, every product waited for its own reads).  The
+  // counting reading keeps the reads next to their products: it has no registers to spare.
   auto pv = [&](const uint32_t (*pk)[8]) __attribute__((always_inline)) {
+    constexpr int NKS = NB * 2;
+    if constexpr (COUNT) {
 #pragma unroll
-    for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        const int ks = kb * 2 + hb;
+      for (int ks = 0; ks < NKS; ++ks) {
+        const int kb = ks >> 1, hb = ks & 1;
         const u32x4 pb = {pk[kb][hb * 4], pk[kb][hb * 4 + 1], pk[kb][hb * 4 + 2], pk[kb][hb * 4 + 3]};
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
@@ -146,6 +148,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
           oacc[db] = mfma32x32x16(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), as_bf16x8(pb), oacc[db]);
         }
       }
+      return;
+    }
+    u32x4 vb[2][D / 32];
+    auto read_v = [&](int ks, u32x4* dst) __attribute__((always_inline)) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const u32x2 lo = ds_read_tr16(Vt + ks * 16 * RS + voff[db]);
+        const u32x2 hi = ds_read_tr16(Vt + (ks * 16 + 8) * RS + voff[db]);
+        dst[db] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      }
+    };
+    read_v(0, vb[0]);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      if (ks + 1 < NKS) read_v(ks + 1, vb[(ks + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      const int kb = ks >> 1, hb = ks & 1;
+      const u32x4 pb = {pk[kb][hb * 4], pk[kb][hb * 4 + 1], pk[kb][hb * 4 + 2], pk[kb][hb * 4 + 3]};
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) oacc[db] = mfma32x32x16(as_bf16x8(vb[ks & 1][db]), as_bf16x8(pb), oacc[db]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
   issue_k(tile_of(0) * BN);
@@ -153,16 +177,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
   __syncthreads();
   for (int n = 0; n <= i; ++n) {
     const int j = tile_of(n);
+    // S_j: the NB key blocks advance together through the head dimension, the K operands of
+    // step ks + 1 read before the products of step ks, so each read has a step of products
+    // to land behind (one block at a time, every product waited for its own read).  The
+    // calibration pass keeps one block at a time: its registers leave room for a fourth wave
+    // per SIMD, which hides the reads instead.
     f32x16 s[NB];
 #pragma unroll
-    for (int kb = 0; kb < NB; ++kb) {
-      f32x16 acc = {};
+    for (int kb = 0; kb < NB; ++kb) s[kb] = f32x16{};
+    if constexpr (CALIB) {
+#pragma unroll
+      for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+          s[kb] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(Kt + kb * 32 * RS + koff[ks])), qreg[ks],
+                               s[kb]);
+    } else {
+      u32x4 av[2][NB];
+#pragma unroll
+      for (int kb = 0; kb < NB; ++kb) av[0][kb] = *reinterpret_cast<const u32x4*>(Kt + kb * 32 * RS + koff[0]);
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
-        const u32x4 av = *reinterpret_cast<const u32x4*>(Kt + kb * 32 * RS + koff[ks]);
-        acc = mfma32x32x16(as_bf16x8(av), qreg[ks], acc);
+        if (ks + 1 < D / 16) {
+#pragma unroll
+          for (int kb = 0; kb < NB; ++kb)
+            av[(ks + 1) & 1][kb] = *reinterpret_cast<const u32x4*>(Kt + kb * 32 * RS + koff[ks + 1]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kb = 0; kb < NB; ++kb) s[kb] = mfma32x32x16(as_bf16x8(av[ks & 1][kb]), qreg[ks], s[kb]);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      s[kb] = acc;
     }
     const bool diag = j == i;
     if (diag) {
