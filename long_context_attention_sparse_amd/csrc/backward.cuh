@@ -494,19 +494,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
     // P is in LDS for the dS waves.  The barrier waits for LDS operations only (a release
     // fence would also wait for the next slab's loads, which write LDS); the empty asm
     // statements with memory clobbers keep the compiler from moving LDS accesses across it.
+    // (the dS wave takes dP - D first, while the P wave is still on P)
+    if (ds_wave) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 dm = *reinterpret_cast<const f32x4*>(mb + g4 * 8 + hh * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[g4 * 4 + e] -= dm[e];
+      }
+    }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if (ds_wave) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const f32x4 dm = *reinterpret_cast<const f32x4*>(mb + g4 * 8 + hh * 4);
         const f32x4 pq = *reinterpret_cast<const f32x4*>(pslot + g4 * 256);
-        float d[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) d[e] = pq[e] * (x[g4 * 4 + e] - dm[e]);
-        op[g4 * 2] = pack_bf16x2(d[0], d[1]);
-        op[g4 * 2 + 1] = pack_bf16x2(d[2], d[3]);
+        op[g4 * 2] = pack_bf16x2(pq[0] * x[g4 * 4], pq[1] * x[g4 * 4 + 1]);
+        op[g4 * 2 + 1] = pack_bf16x2(pq[2] * x[g4 * 4 + 2], pq[3] * x[g4 * 4 + 3]);
       }
     }
 #pragma unroll
