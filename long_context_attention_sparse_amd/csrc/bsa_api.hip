@@ -129,7 +129,13 @@ bsa_status run_prefill(const bsa_problem& p, const bsa_tensor& q, const bsa_tens
     a.part_o = part_o;
     a.part_lse = part_lse;
   }
-  launch_prefill(a, BM / 32, kind, st);
+  if (o && kind == BSA_PAT_VS && BM == 64) {
+    // final outputs of 64-row vertical-slash blocks: pairs of neighbouring query blocks
+    a.n_items = (int)((int64_t)p.B * p.Hq * ((a.nqb + 1) / 2));
+    launch_vs_pair(a, st);
+  } else {
+    launch_prefill(a, BM / 32, kind, st);
+  }
   return launch_status();
 }
 

@@ -5,6 +5,7 @@
 #include "launch.h"
 #include "prefill_pipe.cuh"
 #include "prefill_tile.cuh"
+#include "prefill_vs_pair.cuh"
 
 namespace bsa {
 
@@ -28,6 +29,10 @@ void launch_prefill(const PrefillArgs& a, int NW, int KIND, hipStream_t st) {
     else if (KIND == 1) launch_prefill_t<2, 1>(a, st);
     else launch_prefill_t<2, 2>(a, st);
   }
+}
+
+void launch_vs_pair(const PrefillArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((vs_pair_kernel<4>), dim3(a.n_items), dim3(256), 0, st, a);
 }
 
 void launch_gated(const GatedArgs& a, bool calib, hipStream_t st) {

@@ -17,6 +17,9 @@ void launch_combine(const CombineArgs& a, hipStream_t st);
 void launch_vs_convert(const VSConvArgs& a, unsigned lds_bytes, hipStream_t st);
 // prefill_pipe_kernel<KIND, NW>: n_items workgroups of NW*64 threads (NW 2 or 4, KIND 0..2).
 void launch_prefill(const PrefillArgs& a, int NW, int KIND, hipStream_t st);
+// vs_pair_kernel: vertical-slash patterns on 64-row query blocks, final outputs; n_items =
+// B * Hq * cdiv(nqb, 2) workgroups (pairs of query blocks) of 256 threads.
+void launch_vs_pair(const PrefillArgs& a, hipStream_t st);
 // gated_kernel<calib, count>: n_items workgroups of 256 threads (count: a.count_skipped).
 void launch_gated(const GatedArgs& a, bool calib, hipStream_t st);
 // threshold_kernel: grid (nqb, Hq), 256 threads; nqb <= kThreshMaxCand.

@@ -1,6 +1,7 @@
 """GPU parity where the kernels' LDS staging overflows and the tails are read from global
 memory: block lists of more than 256 entries (prefill and a decode split of more than 256
-entries), vertical-slash blocks with more than 768 gathered columns, and a conversion whose
+entries), vertical-slash blocks with more than 768 gathered columns or more than 256 windows (the
+windows each block of a query-block pair stages), and a conversion whose
 slash + vertical indices exceed the 16,384 ints it stages in LDS.  Expected values come from
 the oracle."""
 import numpy as np
@@ -84,6 +85,34 @@ def test_vs_columns_longer_than_staging(blk):
         o_ref, lse_ref = oracle.vs_attention_rows(q, k, v, 0, h, rows, wins, cols, cu, cu, blk)
         check_o(oh[rows, h], o_ref, f"vs many columns h={h} m={m}")
         check_lse(lh[h, rows], lse_ref, f"vs many columns lse h={h} m={m}")
+
+
+@pytest.mark.parametrize("bn", [64, 128])
+def test_vs_windows_longer_than_staging(bn):
+    """64-row query blocks with more than 256 windows each (slash offsets spread uniformly, so a
+    late block's windows cover almost every earlier key): the pair kernel stages 256 windows
+    of each block and takes the rest as not shared.  Rows of both blocks of a pair are checked,
+    at the end of the sequence (most windows), in the middle and at the start."""
+    L, H = 36864, 2
+    say(f"vertical-slash with more than 256 windows per block, {bn}-key windows")
+    vert, slash = _vs_inputs(105, L, H, 100, 3000)
+    q, k, v = (normal_bf16(105, n, (L, H, 128)) for n in ("q", "k", "v"))
+    sl = dev_i32([L])
+    bc, bo, cc, ci = bsa.vs_convert_indexes(sl, sl, dev_i32(vert), dev_i32(slash), L, 64, bn)
+    assert int(host(bc).max()) > 256
+    cu = np.array([0, L], np.int32)
+    pat = bsa.VSPattern(bc, bo, cc, ci, 64, bn)
+    o, lse = bsa.bsa_fwd(dev_bf16(q), dev_bf16(k), dev_bf16(v), pat, causal=True, out_dtype=torch.float32,
+                         cu_seqlens_q=dev_i32(cu), cu_seqlens_k=dev_i32(cu), max_seqlen_q=L, max_seqlen_k=L)
+    oh, lh = host(o), host(lse)
+    g = rng(105, "rows")
+    last = L // 64 - 1
+    for h, m in [(0, last), (1, last - 1), (0, 300), (1, 301), (0, 1)]:
+        rows = np.sort(g.choice(np.arange(m * 64, m * 64 + 64), 6, replace=False))
+        wins, cols = oracle.vs_convert_item(L, L, vert[0, h], slash[0, h], m, 64, bn)
+        o_ref, lse_ref = oracle.vs_attention_rows(q, k, v, 0, h, rows, wins, cols, cu, cu, bn)
+        check_o(oh[rows, h], o_ref, f"vs many windows h={h} m={m}")
+        check_lse(lh[h, rows], lse_ref, f"vs many windows lse h={h} m={m}")
 
 
 def test_vs_convert_indices_longer_than_staging():
