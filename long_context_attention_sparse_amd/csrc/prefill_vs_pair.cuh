@@ -62,11 +62,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void v
   __shared__ int scan_s[3][4];
 
   // (b, kv head, reversed pair, group member), every XCD on the same head as in the one-block
-  // kernel, in runs of kRunPairs consecutive pairs (runs of 1, 2 and 4 pairs measured alike,
-  // 8 and 16 slower: the last query blocks of a head carry the most windows, and long runs
-  // load the XCDs unevenly)
+  // kernel, in runs of kRunPairs consecutive pairs dealt in mirrored rounds.  The last query
+  // blocks of a head carry the most windows, so what counts is that the XCDs get even shares
+  // of a head: plain rounds of 1, 2 or 4 pairs measured alike and 8 or 16 slower; mirrored
+  // rounds of 4 or 8 pairs 4% faster than plain rounds of 4, of 16 or 32 slower again.
   const int npr = (a.nqb + 1) >> 1;
-  const int item = head_sync_item_n<kRunPairs>(wg_x(), npr, a.n_items);
+  const int item = head_sync_item_n<kRunPairs, true>(wg_x(), npr, a.n_items);
   const int g = item % a.G;
   int rest = item / a.G;
   const int prev = rest % npr;

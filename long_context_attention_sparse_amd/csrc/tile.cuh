@@ -130,17 +130,20 @@ __device__ __forceinline__ int xcd_item(int lid, int n_items) {
 // every XCD works on the same (b, head) at the same time, so that head's K/V stays in the
 // memory-side cache, and each XCD takes runs of kRun consecutive query blocks (or pairs of
 // them), so the near-diagonal windows and the columns the blocks of a run share hit in its
-// L2.  Runs are dealt to the XCDs in turn, heaviest (last) query block first.  Returns the
-// item index in the (b, kv head, reversed query block, group member) order of the prefill
-// kernels (with G query heads per kv head a run holds kRun / G query blocks of each of them).
-template <int kRun>
+// L2.  Runs are dealt to the XCDs in turn, heaviest (last) query block first; with kMirror
+// every second round is dealt in reverse XCD order (x, 15 - x, 16 + x, ...), so that each XCD's
+// runs of a head carry about the same work when the work per block grows along the sequence
+// (otherwise the XCDs drift onto different heads).  Returns the item index in the (b, kv
+// head, reversed query block, group member) order of the prefill kernels (with G query heads
+// per kv head a run holds kRun / G query blocks of each of them).
+template <int kRun, bool kMirror = false>
 __device__ __forceinline__ int head_sync_item_n(int lid, int nqb, int n_items) {
   if (nqb % (8 * kRun) || n_items % nqb) return xcd_item(lid, n_items);
   const int xcd = lid & 7, j = lid >> 3;
   const int share = nqb >> 3;  // query blocks of one head per XCD
   const int head = j / share, jj = j - head * share;
   const int c = jj / kRun, r = jj - c * kRun;
-  return head * nqb + (c * 8 + xcd) * kRun + r;
+  return head * nqb + (c * 8 + (kMirror && (c & 1) ? 7 - xcd : xcd)) * kRun + r;
 }
 // runs of 16 single query blocks (runs of 8, 32 and 64 measured slower)
 __device__ __forceinline__ int head_sync_item(int lid, int nqb, int n_items) {
