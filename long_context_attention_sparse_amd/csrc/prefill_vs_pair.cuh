@@ -191,15 +191,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void v
     r.full = r.key0 >= 0 && r.key0 <= kv_len - 64;
     return r;
   };
-  // segment x (0 or 1) of step c
-  auto seg_of = [&](int c, int x) -> Seg {
-    if (c < n_sh) {
-      const int j = 2 * c + x;
-      if (j >= n_sh_seg) return Seg{};
-      const int e = spe == 2 ? j >> 1 : j;
-      return window_seg(__builtin_amdgcn_readfirstlane(lds_int(wl_s[0], e)), j - e * spe);
-    }
-    const int j = c - n_sh;
+  // segment x (0 or 1) of shared step c (c < n_sh): common windows, in block m's order
+  auto seg_shared = [&](int c, int x) -> Seg {
+    const int j = 2 * c + x;
+    if (j >= n_sh_seg) return Seg{};
+    const int e = spe == 2 ? j >> 1 : j;
+    return window_seg(__builtin_amdgcn_readfirstlane(lds_int(wl_s[0], e)), j - e * spe);
+  };
+  // segment of block m + x (x = 0 or 1) in split step j (step n_sh + j)
+  auto seg_split = [&](int j, int x) -> Seg {
     const int nx = x ? nxb : nxa, nxs = x ? nxb_s : nxa_s;
     if (j < nx * spe) {
       const int e = spe == 2 ? j >> 1 : j;
@@ -233,18 +233,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void v
   const uint32_t kx = (uint32_t)(lslot ^ lrow) << 4;
   const uint32_t vx = (uint32_t)(lslot ^ (lrow << 2)) << 4;
   const uint32_t k_lane = (uint32_t)(lrow * a.k.ss) * 2u, v_lane = (uint32_t)(lrow * a.v.ss) * 2u + vx;
+  // contiguous segment (or an absent one: zeros) through a buffer resource sized to the rows
+  // inside [0, kv_len)
+  auto issue_win = [&](uint16_t* tile, const uint16_t* src, int64_t ss, bool is_k, const Seg& r)
+                       __attribute__((always_inline)) {
+    const int row0 = r.key0 + srow0;
+    const int nrows = (r.valid && row0 >= 0) ? min(kv_len - row0, 32) : 0;
+    const uint32_t row_bytes = (uint32_t)ss * 2u;
+    const __amdgpu_buffer_rsrc_t rs =
+        rows_rsrc(src + (int64_t)max(row0, 0) * ss, nrows > 0 ? (uint32_t)(nrows - 1) * row_bytes + 256u : 0u);
+#pragma unroll
+    for (int x = 0; x < 8; ++x)
+      buffer_load_lds16(rs, tile + (w * 8 + x) * 4 * RS,
+                        (uint32_t)(x * 4) * row_bytes + (is_k ? k_lane + (kx ^ ((x & 3) << 6)) : v_lane));
+  };
   auto issue = [&](uint16_t* tile, const uint16_t* src, int64_t ss, bool is_k, const Seg& r)
                    __attribute__((always_inline)) {
     if (!r.gathered) {
-      const int row0 = r.key0 + srow0;
-      const int nrows = (r.valid && row0 >= 0) ? min(kv_len - row0, 32) : 0;
-      const uint32_t row_bytes = (uint32_t)ss * 2u;
-      const __amdgpu_buffer_rsrc_t rs =
-          rows_rsrc(src + (int64_t)max(row0, 0) * ss, nrows > 0 ? (uint32_t)(nrows - 1) * row_bytes + 256u : 0u);
-#pragma unroll
-      for (int x = 0; x < 8; ++x)
-        buffer_load_lds16(rs, tile + (w * 8 + x) * 4 * RS,
-                          (uint32_t)(x * 4) * row_bytes + (is_k ? k_lane + (kx ^ ((x & 3) << 6)) : v_lane));
+      issue_win(tile, src, ss, is_k, r);
     } else {
       int kk[8];
 #pragma unroll
@@ -387,7 +393,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void v
   };
 
   // ---- step loop ----
-  Seg cur0 = seg_of(0, 0), cur1 = seg_of(0, 1);
+  // a split step only needs this wave's block's segment: both copies hold it
+  Seg cur0, cur1;
+  if (n_sh > 0) {
+    cur0 = seg_shared(0, 0);
+    cur1 = seg_shared(0, 1);
+  } else {
+    cur0 = cur1 = seg_split(0, hb);
+  }
   if (n_steps > 0) {
     const Seg mine = hb ? cur1 : cur0;
     issue(Kt, kbp, a.k.ss, true, mine);
@@ -396,14 +409,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void v
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   // one step: shared (NBW = 4 tile blocks for every wave) or split (NBW = 2, this wave's
-  // block's segment)
-  auto step = [&](auto nbw_c, int c) __attribute__((always_inline)) {
+  // block's segment).  NEXT_SHARED: the next step is a shared one too, so neither this step's
+  // nor the next one's segments are gathered columns (the loop over those steps carries no
+  // gathered-load code).
+  auto step = [&](auto nbw_c, auto next_shared_c, int c) __attribute__((always_inline)) {
     constexpr int NBW = decltype(nbw_c)::value;
-    const bool more = c + 1 < n_steps;
+    constexpr bool NEXT_SHARED = decltype(next_shared_c)::value;
+    const bool more = NEXT_SHARED || c + 1 < n_steps;
     const Seg mine = hb ? cur1 : cur0;
     // a split step whose segment of this wave's block is absent adds nothing to its rows
     const bool work = NBW == 4 || mine.valid;
-    issue(Vt, vbp, a.v.ss, false, mine);
+    if (NBW == 4) issue_win(Vt, vbp, a.v.ss, false, mine);
+    else issue(Vt, vbp, a.v.ss, false, mine);
     f32x16 s[NBW];
     if (work) {
       if (NBW == 4) s_phase(nbw_c, 0, s, cur0, cur1);
@@ -413,12 +430,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void v
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     Seg nxt0, nxt1;
-    if (more) {
-      nxt0 = seg_of(c + 1, 0);
-      nxt1 = seg_of(c + 1, 1);
-      const Seg next_mine = hb ? nxt1 : nxt0;
-      issue(Kt, kbp, a.k.ss, true, next_mine);
-      record_kid(next_mine);
+    if (NEXT_SHARED) {
+      nxt0 = seg_shared(c + 1, 0);
+      nxt1 = seg_shared(c + 1, 1);
+      issue_win(Kt, kbp, a.k.ss, true, hb ? nxt1 : nxt0);
+    } else if (more) {
+      // the next step is a split one (this is the last shared step or a split step)
+      nxt0 = nxt1 = seg_split(c + 1 - n_sh, hb);
+      issue(Kt, kbp, a.k.ss, true, nxt0);
+      record_kid(nxt0);
     }
     if (work) pv_phase(nbw_c, NBW == 4 ? 0 : 2 * hb, s);
     if (more) {
@@ -429,9 +449,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void v
       cur1 = nxt1;
     }
   };
+  using shared_c = std::integral_constant<int, 4>;
+  using split_c = std::integral_constant<int, 2>;
   int c = 0;
-  for (; c < n_sh; ++c) step(std::integral_constant<int, 4>{}, c);
-  for (; c < n_steps; ++c) step(std::integral_constant<int, 2>{}, c);
+  for (; c + 1 < n_sh; ++c) step(shared_c{}, std::true_type{}, c);
+  if (c < n_sh) step(shared_c{}, std::false_type{}, c++);  // the last shared step
+  for (; c < n_steps; ++c) step(split_c{}, std::false_type{}, c);
 
   if (row_ok) {
     const int64_t ob = (a.cu_q ? (int64_t)(q_start + row) * a.o.ss : (int64_t)b * a.o.sb + (int64_t)row * a.o.ss) +

@@ -158,3 +158,34 @@ def test_full_size_attention(cfg5):
         a = int(w["cu_seqlens"][b])
         check_o(oh[a + rows, h], o_ref, f"vs full b={b} h={h} m={m}")
         check_lse(lh[h, a + rows], lse_ref, f"vs full lse b={b} h={h} m={m}")
+
+
+def test_full_size_attention_every_block_of_a_head(cfg5):
+    """Every query block of one head of each sequence (1,536 blocks: both blocks of every pair
+    the kernel takes together), two rows each: a random one and the block's last row, whose
+    causal limit reaches furthest."""
+    w = cfg5
+    say("vs attention full size, every query block of two heads")
+    bc, bo, cc, ci = _convert(w)
+    pat = bsa.VSPattern(bc, bo, cc, ci, 64, 64)
+    cu = dev_i32(w["cu_seqlens"])
+    o, lse = bsa.bsa_fwd(w["dq"], w["dk"], w["dv"], pat, causal=True, out_dtype=torch.float32, cu_seqlens_q=cu,
+                         cu_seqlens_k=cu, max_seqlen_q=65536, max_seqlen_k=65536)
+    oh, lh = host(o), host(lse)
+    g = np.random.default_rng(1005)
+    worst_o = worst_l = 0.0
+    for b, h in [(0, 5), (1, 22)]:
+        L = int(w["seqlens"][b])
+        a = int(w["cu_seqlens"][b])
+        o_ref = np.zeros((L // 64, 2, 128))
+        l_ref = np.zeros((L // 64, 2))
+        rows = np.zeros((L // 64, 2), np.int64)
+        for m in range(L // 64):
+            rows[m] = (m * 64 + int(g.integers(0, 63)), m * 64 + 63)
+            wins, cols = oracle.vs_convert_item(L, L, w["vertical"][b, h], w["slash"][b, h], m, 64, 64)
+            o_ref[m], l_ref[m] = oracle.vs_attention_rows(w["q"], w["k"], w["v"], b, h, rows[m], wins, cols,
+                                                           w["cu_seqlens"], w["cu_seqlens"], 64)
+        worst_o = max(worst_o, check_o(oh[a + rows, h], o_ref, f"vs full b={b} h={h} every block"))
+        worst_l = max(worst_l, check_lse(lh[h, a + rows], l_ref, f"vs full lse b={b} h={h} every block"))
+    print(f"[parity] vs attention, every query block of two heads: max |dO| {worst_o:.3e}, "
+          f"max |dLSE| {worst_l:.3e}", flush=True)
