@@ -289,28 +289,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void v
   // -inf for absent keys and, when causal, keys after the row's diagonal (tile block kb of
   // 32 keys lies in segment kb / 2)
   const int wrow_min = r0 + w * 32;
-  auto mask_block = [&](f32x16& s, int kb, const Seg& r) __attribute__((always_inline)) {
+  // Shared steps hold windows only.  Split steps also hold gathered columns; their mask takes
+  // one path for both kinds, the key of each element being the recorded column index or the
+  // window's key (two alternative paths would make the compiler copy the scores around them).
+  auto mask_block = [&](f32x16& s, int kb, const Seg& r, auto cols_c) __attribute__((always_inline)) {
+    constexpr bool COLS = decltype(cols_c)::value;
     const int lim = a.causal ? row + delta : 0x7ffffffe;
     const int half = (kb & 1) * 32;
-    if (r.gathered) {
+    const bool need = (COLS && r.gathered) || !r.full || (a.causal && r.key0 + half + 31 > wrow_min + delta);
+    if (!need) return;
+    if constexpr (COLS) {
+      // present gathered keys lie in [0, kv_len), absent ones are recorded as INT_MAX
+      const int lim_eff = r.gathered ? lim : (r.valid ? min(lim, kv_len - 1) : -1);
+      const int base = r.key0 + half;
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int4 k4 = *reinterpret_cast<const int4*>(kid_s + kb * 32 + q4 * 8 + hh * 4);
-        if (k4.x > lim) s[q4 * 4 + 0] = kNegInf;
-        if (k4.y > lim) s[q4 * 4 + 1] = kNegInf;
-        if (k4.z > lim) s[q4 * 4 + 2] = kNegInf;
-        if (k4.w > lim) s[q4 * 4 + 3] = kNegInf;
-      }
-      return;
-    }
-    const bool need = !r.full || (a.causal && r.key0 + half + 31 > wrow_min + delta);
-    if (!need) return;
-    const int hi = r.valid ? min(lim, kv_len - 1) - r.key0 - half : -1;
-    const int lo = -r.key0 - half;
+        const int kk[4] = {k4.x, k4.y, k4.z, k4.w};
 #pragma unroll
-    for (int rg = 0; rg < 16; ++rg) {
-      const int kl = (rg >> 2) * 8 + hh * 4 + (rg & 3);
-      if (kl > hi || kl < lo) s[rg] = kNegInf;
+        for (int e = 0; e < 4; ++e) {
+          const int key = r.gathered ? kk[e] : base + q4 * 8 + hh * 4 + e;
+          if (key > lim_eff || key < 0) s[q4 * 4 + e] = kNegInf;
+        }
+      }
+    } else {
+      const int hi = r.valid ? min(lim, kv_len - 1) - r.key0 - half : -1;
+      const int lo = -r.key0 - half;
+#pragma unroll
+      for (int rg = 0; rg < 16; ++rg) {
+        const int kl = (rg >> 2) * 8 + hh * 4 + (rg & 3);
+        if (kl > hi || kl < lo) s[rg] = kNegInf;
+      }
     }
   };
 
@@ -338,8 +347,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void v
     softcap_n<NBW>(s, a.cap_in, a.cap_out);
 #pragma unroll
     for (int kb = 0; kb < NBW; ++kb) {
-      if (NBW == 4) mask_block(s[kb], kb, kb < 2 ? seg0 : seg1);
-      else mask_block(s[kb], kb0 + kb, seg0);  // split step: seg0 is this wave's segment
+      if (NBW == 4) mask_block(s[kb], kb, kb < 2 ? seg0 : seg1, std::false_type{});
+      else mask_block(s[kb], kb0 + kb, seg0, std::true_type{});  // split step: seg0 is this wave's segment
     }
     softmax_max_n<NBW>(s, a.scale_log2, m_run, l_run, oacc);
   };
@@ -417,15 +426,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void v
     constexpr bool NEXT_SHARED = decltype(next_shared_c)::value;
     const bool more = NEXT_SHARED || c + 1 < n_steps;
     const Seg mine = hb ? cur1 : cur0;
-    // a split step whose segment of this wave's block is absent adds nothing to its rows
-    const bool work = NBW == 4 || mine.valid;
+    // (a split step whose segment of this wave's block is absent runs on zeros, all masked:
+    // it adds nothing to the rows, and a test around the products would cost more)
     if (NBW == 4) issue_win(Vt, vbp, a.v.ss, false, mine);
     else issue(Vt, vbp, a.v.ss, false, mine);
     f32x16 s[NBW];
-    if (work) {
-      if (NBW == 4) s_phase(nbw_c, 0, s, cur0, cur1);
-      else s_phase(nbw_c, 2 * hb, s, mine, mine);
-    }
+    if (NBW == 4) s_phase(nbw_c, 0, s, cur0, cur1);
+    else s_phase(nbw_c, 2 * hb, s, mine, mine);
     // V_c is in LDS from every wave, and every wave is done reading K_c and the indices
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -440,7 +447,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void v
       issue(Kt, kbp, a.k.ss, true, nxt0);
       record_kid(nxt0);
     }
-    if (work) pv_phase(nbw_c, NBW == 4 ? 0 : 2 * hb, s);
+    pv_phase(nbw_c, NBW == 4 ? 0 : 2 * hb, s);
     if (more) {
       // K_{c+1} is in LDS and every wave is done reading V_c
       __builtin_amdgcn_s_waitcnt(0);
