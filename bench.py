@@ -767,7 +767,7 @@ def gpu_vs(torch, bsa, w, args):
                         "convert_gbs": round(conv_bytes / (cms * 1e-3) / 1e9, 1),
                         "algorithmic_units": "per (sequence, head, 64-row query block): 4*64*128*(64*block_count + "
                                              "column_count) flop over its windows and columns"},
-                roofline=_roof("mfma", flops / (ams * 1e-3) / 1e12, "void bsa::vs_pair_kernel<4>(bsa::PrefillArgs)",
+                roofline=_roof("mfma", flops / (ams * 1e-3) / 1e12, "void bsa::vs_pair_kernel<8>(bsa::PrefillArgs)",
                                ams))
 
 

@@ -32,7 +32,7 @@ void launch_prefill(const PrefillArgs& a, int NW, int KIND, hipStream_t st) {
 }
 
 void launch_vs_pair(const PrefillArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((vs_pair_kernel<4>), dim3(a.n_items), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((vs_pair_kernel<8>), dim3(a.n_items), dim3(256), 0, st, a);
 }
 
 void launch_gated(const GatedArgs& a, bool calib, hipStream_t st) {

@@ -63,9 +63,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void v
 
   // (b, kv head, reversed pair, group member), every XCD on the same head as in the one-block
   // kernel, in runs of kRunPairs consecutive pairs dealt in mirrored rounds.  The last query
-  // blocks of a head carry the most windows, so what counts is that the XCDs get even shares
-  // of a head: plain rounds of 1, 2 or 4 pairs measured alike and 8 or 16 slower; mirrored
-  // rounds of 4 or 8 pairs 4% faster than plain rounds of 4, of 16 or 32 slower again.
+  // blocks of a head carry the most windows, so the XCDs must get even shares of a head:
+  // plain rounds of 1, 2 or 4 pairs measured alike and 8 or 16 slower; mirrored rounds of 4 or
+  // 8 pairs 4% faster than plain rounds of 4, of 16 or 32 slower again.  With the rotated
+  // shared-step walk below, runs of 8 pairs beat runs of 4 by 2% (more neighbours per XCD
+  // reading the same tiles), runs of 16 are 5% slower.
   const int npr = (a.nqb + 1) >> 1;
   const int item = head_sync_item_n<kRunPairs, true>(wg_x(), npr, a.n_items);
   const int g = item % a.G;
@@ -191,8 +193,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void v
     r.full = r.key0 >= 0 && r.key0 <= kv_len - 64;
     return r;
   };
-  // segment x (0 or 1) of shared step c (c < n_sh): common windows, in block m's order
+  // Segment x (0 or 1) of shared step c (c < n_sh): common windows in block m's order, the
+  // walk rotated by -(pair index) steps.  Near the diagonal the next pair's common windows are
+  // this pair's shifted by 128 keys, one shared step; with the rotation neighbouring pairs
+  // read the same tiles in the same step, while they are still in L2 (an XCD's 64 resident
+  // pairs load about its whole L2 per step).
+  const int rot = n_sh > 0 ? (n_sh - (m >> 1) % n_sh) % n_sh : 0;
   auto seg_shared = [&](int c, int x) -> Seg {
+    c += rot;
+    if (c >= n_sh) c -= n_sh;
     const int j = 2 * c + x;
     if (j >= n_sh_seg) return Seg{};
     const int e = spe == 2 ? j >> 1 : j;
