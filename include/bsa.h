@@ -185,7 +185,10 @@ size_t bsa_workspace_size(const bsa_problem* prob, const bsa_pattern* pat);
  * a kv head's group, G * Sq for dense or kv-head lists, Sq for query-head
  * lists, at most 16) run on the split-KV decode kernel with D 64 or 128;
  * every other shape runs on the tile kernels, which need D == 128
- * (BSA_ERR_UNSUPPORTED for D == 64 there).
+ * (BSA_ERR_UNSUPPORTED for D == 64 there).  VS patterns with 64-row query
+ * blocks take two neighbouring query blocks per workgroup, loading the
+ * windows both name once; the result is the same attention (up to the order
+ * of float32 sums).
  * Errors: BSA_ERR_INVALID_ARG for NULL tensors, non-positive sizes,
  * Hq % Hkv != 0, pattern heads other than Hq/Hkv, Sk % block_N != 0;
  * BSA_ERR_UNSUPPORTED for D or block sizes outside the list above;

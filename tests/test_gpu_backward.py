@@ -243,11 +243,12 @@ def _packed(w, h, i, oh):
 
 def test_full_size_sampled(bwd_full):
     """The block-sparse causal prefill at full size (S=32768, Hq=32, Hkv=8, 128x128 tiles, bf16 O
-    from the forward), launched as the benchmark launches it.  Sampled: dQ of three query blocks;
-    dK and dV of the last key block (seen by the diagonal tiles only) and of key block 1, which
-    several hundred (head, query block) lists name, so its sums are split over many chunks and
-    go through the reduction.  Each expected block sums the oracle's gradients of the small
-    packed problems of every (head, query block) that names it."""
+    from the forward), launched as the benchmark launches it.  Sampled: dQ of 16 query blocks
+    (first and last included, spread over the heads); dK and dV of the last key block (seen by
+    the diagonal tiles only), of key blocks 128 and 200, and of key block 1, which several hundred
+    (head, query block) lists name, so its sums are split over many chunks and go through the
+    reduction.  Each expected block sums the oracle's gradients of the small packed problems of
+    every (head, query block) that names it."""
     w = bwd_full
     say("backward full size")
     q, k, v, do = (dev_bf16(w[n]) for n in ("q", "k", "v", "do"))
@@ -257,12 +258,13 @@ def test_full_size_sampled(bwd_full):
     gq, gk, gv = bsa.bsa_bwd(q, k, v, o, lse, do, pat, causal=True, workspace=ws)
     oh = host(o)
     gq, gk, gv = host(gq), host(gk), host(gv)
-    for h, i in [(0, 255), (31, 0), (12, 200)]:
+    for h, i in [(0, 255), (31, 0), (12, 200), (1, 1), (2, 17), (5, 254), (7, 99), (9, 128), (14, 31), (16, 64),
+                 (19, 177), (21, 240), (24, 3), (26, 150), (28, 211), (30, 90)]:
         _, (rq, _, _), (bq, _, _) = _packed(w, h, i, oh)
         check_within(f"full dq h={h} i={i}", gq[0, i * 128:(i + 1) * 128, h], rq[0, :, 0], bq[0, :, 0])
     G = w["Hq"] // w["Hkv"]
     nqb = w["count"].shape[2]
-    for hk, j in [(3, nqb - 1), (5, 1)]:
+    for hk, j in [(3, nqb - 1), (0, 128), (7, 200), (5, 1)]:
         rk = np.zeros((128, 128))
         rv = np.zeros((128, 128))
         bk = np.zeros((128, 128))
