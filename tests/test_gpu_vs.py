@@ -9,6 +9,7 @@ import torch
 
 import long_context_attention_sparse_amd as bsa
 import oracle
+from synth import normal_bf16
 from synth.workloads import vs_varlen_prefill
 from tests.golden.make_full_size import vs_digest
 from tests.gpu_util import check_lse, check_o, dev_bf16, dev_i32, host, say
@@ -107,6 +108,30 @@ def test_attention_fixed_length_gqa(causal):
     check_o(host(o).reshape(B * S, H, 128), o_ref, "vs fixed length")
     # varlen LSE is [H, total]; fixed-length LSE is [B, H, S]
     check_lse(host(lse).transpose(1, 0, 2).reshape(H, B * S), lse_ref, "vs fixed length lse")
+
+
+@pytest.mark.parametrize("bn", [64, 128])
+def test_attention_varlen_lists_per_kv_head(bn):
+    """GQA with the converted metadata given per kv head (two query heads share each list), on
+    packed sequences whose block counts are odd (a query block without a neighbour to pair
+    with).  The oracle takes the metadata per query head, so each kv head's lists are repeated
+    for its query heads on the host."""
+    Hq, Hkv = 4, 2
+    w = vs_varlen_prefill(seed=54, seqlens=(704, 320, 64), H=Hkv, D=128, nnz_v=40, nnz_s=60, block=64,
+                          context_size=768)
+    say("vs attention varlen, lists per kv head", bn)
+    q = normal_bf16(54, "q gqa", (w["q"].shape[0], Hq, 128))
+    sl = dev_i32(w["seqlens"])
+    bc, bo, cc, ci = bsa.vs_convert_indexes(sl, sl, dev_i32(w["vertical"]), dev_i32(w["slash"]), 768, 64, bn)
+    cu = dev_i32(w["cu_seqlens"])
+    o, lse = bsa.bsa_fwd(dev_bf16(q), dev_bf16(w["k"]), dev_bf16(w["v"]), bsa.VSPattern(bc, bo, cc, ci, 64, bn),
+                         causal=True, out_dtype=torch.float32, cu_seqlens_q=cu, cu_seqlens_k=cu, max_seqlen_q=704,
+                         max_seqlen_k=704)
+    rb, rbo, rcc, rci = oracle.vs_convert(w["seqlens"], w["seqlens"], w["vertical"], w["slash"], 768, 64, bn)
+    rep = [np.repeat(x, Hq // Hkv, axis=1) for x in (rb, rbo, rcc, rci)]
+    o_ref, lse_ref = oracle.vs_attention(q, w["k"], w["v"], *rep, w["cu_seqlens"], w["cu_seqlens"], 64, bn)
+    check_o(host(o), o_ref, "vs attention, lists per kv head")
+    check_lse(host(lse), lse_ref, "vs attention lse, lists per kv head")
 
 
 @pytest.fixture(scope="module")
