@@ -108,13 +108,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
   constexpr bool kVGroups = D == 128;
   const int kv = t % 16, cv = t / 16;
   const uint16_t* vbase2 = reinterpret_cast<const uint16_t*>(sg.v.ptr) + b * sg.v.sb + (int64_t)hkv * sg.v.sh + cv * 8;
+  // K is read once per launch, each 128-byte line by one load instruction: nontemporal loads
+  // (the streaming cache policy) keep it from displacing other lines, 8% faster on the
+  // speculative + sparse workload.  V keeps the default policy: at head dim 128 a wave's load covers half of
+  // each line, and the other half, read by the next wave, must still be in the cache (with
+  // nontemporal V loads 4% of the bytes were fetched twice and the launch ran 3% slower).
+  auto ldg128_nt = [](const uint16_t* p) __attribute__((always_inline)) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  };
   u32x4 kr[L], vr[L];
   auto load_chunk = [&](int key0) {
 #pragma unroll
     for (int j = 0; j < L; ++j) {
       const int key = key0 + kk * L + j;
       const bool ok = (unsigned)key < (unsigned)Sk;
-      kr[j] = ok ? ldg128(kbase + (int64_t)key * sg.k.ss) : u32x4{0, 0, 0, 0};
+      kr[j] = ok ? ldg128_nt(kbase + (int64_t)key * sg.k.ss) : u32x4{0, 0, 0, 0};
       if constexpr (kVGroups) {
         const int vkey = key0 + kv * 4 + j;
         vr[j] = (unsigned)vkey < (unsigned)Sk ? ldg128(vbase2 + (int64_t)vkey * sg.v.ss) : u32x4{0, 0, 0, 0};
