@@ -52,7 +52,60 @@ def _args():
                     help="time decode steps as eager launches instead of HIP graph replays")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 4 device-to-device copies of 1 GiB (reference for HBM byte counters)")
+    ap.add_argument("--markers", action="store_true",
+                    help="wrap each workload's GPU phase in a roctx range (rocprofv3 --marker-trace shows them)")
+    ap.add_argument("--results", default=None,
+                    help="append each workload's result, as it completes, as one JSON line to this file")
+    ap.add_argument("--resume", action="store_true",
+                    help="with --results: reuse the workloads already in the file instead of running them again")
     return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# Results file (JSON lines, one per finished workload) and roctx ranges
+# ---------------------------------------------------------------------------
+
+def load_results(path):
+    """Workload results stored by earlier runs: {workload number: result}; the last line of a
+    workload wins, and lines that do not parse (a run cut off mid-write) are skipped."""
+    out = {}
+    if not path or not os.path.exists(path):
+        return out
+    with open(path) as f:
+        for line in f:
+            try:
+                rec = json.loads(line)
+                out[int(rec["workload_index"])] = rec["result"]
+            except (ValueError, KeyError, TypeError):
+                continue
+    return out
+
+
+def append_result(path, c, r):
+    with open(path, "a") as f:
+        f.write(json.dumps({"workload_index": c, "result": r}) + "\n")
+        f.flush()
+
+
+class _Markers:
+    """roctx ranges through torch's range API (backed by roctx on ROCm); a no-op if unavailable."""
+
+    def __init__(self, torch):
+        self.api = None
+        try:
+            torch.cuda.nvtx.range_push("bench")
+            torch.cuda.nvtx.range_pop()
+            self.api = torch.cuda.nvtx
+        except Exception as e:  # the profiler's marker library may be absent
+            _log(f"markers unavailable ({e}); running without them")
+
+    def push(self, name):
+        if self.api:
+            self.api.range_push(name)
+
+    def pop(self):
+        if self.api:
+            self.api.range_pop()
 
 
 def _log(*a):
@@ -896,12 +949,17 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n, "copies": 4}), flush=True)
         return
     configs = [args.config] if args.config else list(ALL_CONFIGS)
+    done = load_results(args.results) if args.resume else {}
+    if done:
+        _log(f"reusing stored results of workloads {sorted(set(done) & set(configs))} from {args.results}")
 
     # ---- phase 1: inputs and the oracle's CPU baseline (the GPU is not touched yet) ----
     work = {}
     cpu = {}
     cores = cpu_cores()
     for c in configs:
+        if c in done:
+            continue
         w = work[3] if c == 7 and 3 in work else None
         if w is not None:
             from synth import normal_bf16
@@ -920,12 +978,22 @@ def main():
         sys.exit(1)
     bsa.load()
     res = {}
+    markers = _Markers(torch) if args.markers else None
     for c in configs:
+        if c in done:
+            res[c] = done[c]
+            continue
         _log(f"workload {c}: timing on the GPU")
+        if markers:
+            markers.push(f"workload {c}")
         res[c] = GPU[c](torch, bsa, work[c], args)
+        if markers:
+            markers.pop()
         res[c]["cpu_baseline"] = cpu.get(c)
         free(torch)
         _log(f"workload {c}: {res[c]['value']} {res[c]['unit']}, {res[c]['ms']:.4f} ms per call")
+        if args.results:
+            append_result(args.results, c, res[c])
 
     head = HEADLINE if HEADLINE in res else configs[0]
     r = res[head]
