@@ -445,15 +445,30 @@ def capture(torch, fn):
     return g
 
 
-def run_graph_steps(torch, g, steps):
-    """Wall-clock ms per replay of g over exactly `steps` replays, synchronized on both sides."""
+def run_graph_steps(torch, g, steps, min_seconds=0.0):
+    """Wall-clock ms per replay of g, synchronized on both sides, over exactly `steps` replays;
+    with min_seconds > 0, over at least as many more as fill that long.  The count is then fixed
+    from the pace of SETTLE_S of untimed replays, each waited for, which also bring the clock up
+    from idle.  A launch-bound step of tens of microseconds timed over a few replays reads up to
+    twice its steady-state time.  Returns (ms per replay, replays timed)."""
     g.replay()
     torch.cuda.synchronize()
+    n = steps
+    if min_seconds > 0:
+        t0 = time.perf_counter()
+        settled = 0
+        while time.perf_counter() - t0 < SETTLE_S:
+            g.replay()
+            torch.cuda.synchronize()
+            settled += 1
+        per = (time.perf_counter() - t0) / settled
+        n = max(steps, min(int(np.ceil(min_seconds / per)), 100000))
+    steps = n
     t0 = time.perf_counter()
     for _ in range(steps):
         g.replay()
     torch.cuda.synchronize()
-    return (time.perf_counter() - t0) * 1e3 / steps
+    return (time.perf_counter() - t0) * 1e3 / steps, steps
 
 
 def kernel_mean_ms(torch, fn, per_graph=10, replays=5):
@@ -550,17 +565,20 @@ def gpu_tiny(torch, bsa, w, args):
         bsa.bsa_fwd(q, k, v, pats["set_b"], out=o_part[1], lse=lse_part[1])
         bsa.bsa_combine(o_part, lse_part, out=out)
 
+    n_timed = args.steps
     if args.eager:
         ms, a_ms = eager_ms, timer.mean_ms("set A")
     else:
-        ms = run_graph_steps(torch, capture(torch, full_step), args.steps)
+        # a step of tens of microseconds: timed over at least MIN_TIMED_S of replays
+        ms, n_timed = run_graph_steps(torch, capture(torch, full_step), args.steps,
+                                      MIN_TIMED_S if args.settle > 0 else 0.0)
         a_ms = kernel_mean_ms(torch, set_a)
     kv = B * H * 16 * 64 * w["D"] * 2 * 2
     a_bytes = B * H * 6 * 64 * w["D"] * 4
     return dict(workload="tiny sparse decode (sets A and B, combine)", value=round(ms, 4), unit="ms/call",
                 higher_is_better=False, ms=ms,
                 config={"B": B, "H": H, "D": w["D"], "Sk": w["Sk"], "block": 64, "kv_bytes": kv,
-                        "timing": "eager" if args.eager else "hip graph replay",
+                        "timing": "eager" if args.eager else "hip graph replay", "timed_steps": n_timed,
                         "eager_ms_per_step": round(eager_ms, 4), "eager_launch_us": spans,
                         "algorithmic_units": "6 + 10 listed 64-key blocks per head (K and V: 16 KB each), 4 heads"},
                 roofline=_roof("hbm", a_bytes / (a_ms * 1e-3) / 1e9, "void bsa::decode_kernel<64>(bsa::DecodeArgs) (set A)",
@@ -609,7 +627,7 @@ def gpu_spec_decode(torch, bsa, w, args):
         ms, pass_ms = eager_ms, timer.mean_ms("passes")
     else:
         # a decode step replays as one HIP graph (launch overhead off the critical path)
-        ms = run_graph_steps(torch, capture(torch, full_step), args.steps)
+        ms, _ = run_graph_steps(torch, capture(torch, full_step), args.steps)
         pass_ms = kernel_mean_ms(torch, passes)
     groups = B * Hkv
     blk_bytes = bs * D * 2 * 2
