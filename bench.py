@@ -445,13 +445,15 @@ def capture(torch, fn):
     return g
 
 
-def run_graph_steps(torch, g, steps, min_seconds=0.0):
-    """Wall-clock ms per replay of g, synchronized on both sides, over exactly `steps` replays;
+def run_graph_steps(torch, g, steps, min_seconds=0.0, warmup=1):
+    """`warmup` untimed replays of g, then wall-clock ms per replay, synchronized on both sides,
+    over exactly `steps` replays;
     with min_seconds > 0, over at least as many more as fill that long.  The count is then fixed
     from the pace of SETTLE_S of untimed replays, each waited for, which also bring the clock up
     from idle.  A launch-bound step of tens of microseconds timed over a few replays reads up to
     twice its steady-state time.  Returns (ms per replay, replays timed)."""
-    g.replay()
+    for _ in range(max(1, warmup)):
+        g.replay()
     torch.cuda.synchronize()
     n = steps
     if min_seconds > 0:
@@ -571,7 +573,7 @@ def gpu_tiny(torch, bsa, w, args):
     else:
         # a step of tens of microseconds: timed over at least MIN_TIMED_S of replays
         ms, n_timed = run_graph_steps(torch, capture(torch, full_step), args.steps,
-                                      MIN_TIMED_S if args.settle > 0 else 0.0)
+                                      MIN_TIMED_S if args.settle > 0 else 0.0, args.warmup)
         a_ms = kernel_mean_ms(torch, set_a)
     kv = B * H * 16 * 64 * w["D"] * 2 * 2
     a_bytes = B * H * 6 * 64 * w["D"] * 4
@@ -627,7 +629,7 @@ def gpu_spec_decode(torch, bsa, w, args):
         ms, pass_ms = eager_ms, timer.mean_ms("passes")
     else:
         # a decode step replays as one HIP graph (launch overhead off the critical path)
-        ms, _ = run_graph_steps(torch, capture(torch, full_step), args.steps)
+        ms, _ = run_graph_steps(torch, capture(torch, full_step), args.steps, warmup=args.warmup)
         pass_ms = kernel_mean_ms(torch, passes)
     groups = B * Hkv
     blk_bytes = bs * D * 2 * 2
