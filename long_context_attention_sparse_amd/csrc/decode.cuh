@@ -16,9 +16,10 @@
 // threads = 4 waves.  The split's block ids are staged in LDS first, so the
 // address of every chunk is known without a dependent global load.  Per
 // 64-key chunk every thread loads D/32 16-byte pieces of K and of V
-// (coalesced: 16 or 8 lanes per 256/128-byte key row); K goes to LDS
-// row-major, V is transposed in registers and stored key-contiguous per
-// head-dim row.  Wave w owns keys 16w..16w+15 of the chunk and keeps its own
+// (coalesced: K 16 or 8 lanes per 256/128-byte key row, V at head dim 128
+// 8 lanes per 128-byte half row), both with the streaming cache policy; K
+// goes to LDS row-major, V is transposed in registers and stored
+// key-contiguous per head-dim row.  Wave w owns keys 16w..16w+15 of the chunk and keeps its own
 // running (max, sum, O^T); the four waves merge once at the end.
 //   S^T = K Q^T    : v_mfma_f32_16x16x32_bf16, D/32 per chunk (lane = query col)
 //   O^T += V^T P^T : v_mfma_f32_16x16x16_bf16, D/16 per chunk
@@ -37,7 +38,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
   constexpr int KEYS_PER_PASS = 256 / PIECES;  // key rows one pass of 256 threads covers
   constexpr int L = 64 / KEYS_PER_PASS;        // consecutive keys per thread (4 or 2)
   constexpr int KS = D + 8;                    // Ks row stride in bf16 (pad: conflict-free b128 reads)
-  constexpr int VSTR = 64 + 8;                 // Vt row stride in bf16
+  constexpr int VSTR = D == 128 ? 64 + 4 : 64 + 8;  // Vt row stride in bf16 (conflict-free stores and reads)
   constexpr int LDS_KV = (64 * KS + D * VSTR) * 2;
   constexpr int MS = D + 4;                    // merge row stride in floats (conflict-free b128 stores)
   constexpr int LDS_MERGE = (4 * 16 * MS + 3 * 64) * 4;
@@ -102,17 +103,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
     return id * (64 * cpe) + (ci - el * cpe) * 64;
   };
 
-  // V for head dim 128: lanes run over the 16 4-key groups (kv) and each thread owns one
-  // 16-byte head-dim piece (cv), so the transposed LDS stores of a wave write whole
-  // contiguous V^T row segments (no bank conflicts); head dim 64 uses the K mapping
+  // V for head dim 128: each thread owns 4 consecutive keys (4-key group kv) of one 16-byte
+  // head-dim piece (cv) and stores them transposed.  Wave w takes the pieces of one 128-byte
+  // half of each key row (8(w & 1) .. + 7) for the key groups of one half of the chunk
+  // (8(w >> 1) .. + 7), lane l group l % 8 and piece l / 8: every load instruction reads whole
+  // 128-byte lines, and with the 68-element V^T row stride the stores of each 32 lanes and the
+  // P V reads hit distinct banks.  Head dim 64 uses the K mapping.
   constexpr bool kVGroups = D == 128;
-  const int kv = t % 16, cv = t / 16;
+  const int kv = 8 * (w >> 1) + (l & 7), cv = 8 * (w & 1) + (l >> 3);
   const uint16_t* vbase2 = reinterpret_cast<const uint16_t*>(sg.v.ptr) + b * sg.v.sb + (int64_t)hkv * sg.v.sh + cv * 8;
-  // K is read once per launch, each 128-byte line by one load instruction: nontemporal loads
-  // (the streaming cache policy) keep it from displacing other lines, 8% faster on the
-  // speculative + sparse workload.  V keeps the default policy: at head dim 128 a wave's load covers half of
-  // each line, and the other half, read by the next wave, must still be in the cache (with
-  // nontemporal V loads 4% of the bytes were fetched twice and the launch ran 3% slower).
+  // K and V are read once per launch, each 128-byte line by one load instruction, so both go
+  // through nontemporal loads (the streaming cache policy), which keep them from displacing
+  // other lines: K that way made the speculative + sparse launch 8% faster, V another 2% once
+  // its mapping covered whole lines.  (With V lanes over half lines, the other half read by
+  // the next wave, nontemporal V loads fetched 4% of the bytes twice and ran 3% slower.)
   auto ldg128_nt = [](const uint16_t* p) __attribute__((always_inline)) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   };
@@ -125,7 +129,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
       kr[j] = ok ? ldg128_nt(kbase + (int64_t)key * sg.k.ss) : u32x4{0, 0, 0, 0};
       if constexpr (kVGroups) {
         const int vkey = key0 + kv * 4 + j;
-        vr[j] = (unsigned)vkey < (unsigned)Sk ? ldg128(vbase2 + (int64_t)vkey * sg.v.ss) : u32x4{0, 0, 0, 0};
+        vr[j] = (unsigned)vkey < (unsigned)Sk ? ldg128_nt(vbase2 + (int64_t)vkey * sg.v.ss) : u32x4{0, 0, 0, 0};
       } else {
         vr[j] = ok ? ldg128(vbase + (int64_t)key * sg.v.ss) : u32x4{0, 0, 0, 0};
       }
