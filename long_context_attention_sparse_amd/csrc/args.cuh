@@ -28,7 +28,8 @@ struct PatternArg {
 
 constexpr int kDecodeEntsLds = 256;    // block ids of a decode split staged in LDS (later ones read from global)
 constexpr int kVSConvThreads = 64;     // conversion workgroup size (one query block per thread)
-constexpr int kVSConvLdsInts = 16384;  // slash + vertical entries staged in LDS (longer lists stay in global)
+constexpr int kVSConvLdsInts = 16384;  // slash entries staged in LDS for the window walk (longer lists stay in global)
+constexpr int kVSColLdsInts = 4096;    // windows of a query block staged in LDS for the column test
 constexpr int kThreshMaxCand = 4096;   // threshold selection: query blocks per row (LDS candidates)
 constexpr int kSelTile = 1024;         // selected attention: token positions per index workgroup
 constexpr int kSelMaxBlocks = 8192;    // selected attention: key blocks per sequence (LDS histogram)

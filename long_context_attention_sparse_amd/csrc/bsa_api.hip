@@ -706,8 +706,7 @@ static bsa_status vs_convert_impl(const int32_t* q_seqlens, const int32_t* kv_se
   VSConvArgs a{q_seqlens, kv_seqlens, vertical, slash, v_count, s_count, B, H, nnz_v, nnz_s, 0, block_M, block_N,
                block_count, block_offset, column_count, column_index};
   a.rows = (context_size + block_M - 1) / block_M;
-  const int lds_ints = nnz_s + nnz_v <= kVSConvLdsInts ? nnz_s + nnz_v : 0;
-  launch_vs_convert(a, lds_ints * sizeof(int32_t), reinterpret_cast<hipStream_t>(stream));
+  launch_vs_convert(a, reinterpret_cast<hipStream_t>(stream));
   return launch_status();
 }
 

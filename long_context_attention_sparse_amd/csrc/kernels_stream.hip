@@ -20,9 +20,12 @@ void launch_combine(const CombineArgs& c, hipStream_t st) {
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(256), 0, st, c);
 }
 
-void launch_vs_convert(const VSConvArgs& a, unsigned lds_bytes, hipStream_t st) {
+void launch_vs_convert(const VSConvArgs& a, hipStream_t st) {
   dim3 grid((a.rows + kVSConvThreads - 1) / kVSConvThreads, a.B * a.H);
-  hipLaunchKernelGGL(vs_convert_kernel, grid, dim3(kVSConvThreads), lds_bytes, st, a);
+  const unsigned lds_walk = a.nnz_s <= kVSConvLdsInts ? (unsigned)a.nnz_s * sizeof(int32_t) : 0u;
+  hipLaunchKernelGGL(vs_convert_kernel, grid, dim3(kVSConvThreads), lds_walk, st, a);
+  const unsigned lds_cols = (unsigned)(a.nnz_s < kVSColLdsInts ? a.nnz_s : kVSColLdsInts) * sizeof(int32_t);
+  hipLaunchKernelGGL(vs_columns_kernel, dim3(a.rows, a.B * a.H), dim3(64), lds_cols, st, a);
 }
 
 void launch_threshold(const ThresholdArgs& a, hipStream_t st) {

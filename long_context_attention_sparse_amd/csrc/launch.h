@@ -13,8 +13,9 @@ namespace bsa {
 void launch_decode(const DecodeArgs& a, int D, int gx, int groups, int B, hipStream_t st);
 // combine_kernel over B*Sq*Hq rows.
 void launch_combine(const CombineArgs& a, hipStream_t st);
-// vs_convert_kernel: grid (cdiv(rows, kVSConvThreads), B*H), dynamic LDS lds_bytes.
-void launch_vs_convert(const VSConvArgs& a, unsigned lds_bytes, hipStream_t st);
+// vs_convert_kernel (windows): grid (cdiv(rows, kVSConvThreads), B*H), the slash list in dynamic LDS;
+// then vs_columns_kernel (columns): grid (rows, B*H) of one wave, a block's windows in dynamic LDS.
+void launch_vs_convert(const VSConvArgs& a, hipStream_t st);
 // prefill_pipe_kernel<KIND, NW>: n_items workgroups of NW*64 threads (NW 2 or 4, KIND 0..2).
 void launch_prefill(const PrefillArgs& a, int NW, int KIND, hipStream_t st);
 // vs_pair_kernel: vertical-slash patterns on 64-row query blocks, final outputs; n_items =

@@ -16,10 +16,15 @@
 // indices (same page, Description): head h uses only the first count entries
 // of its rows.
 //
-// One thread per query block; a workgroup takes 64 consecutive query blocks
-// of one (b, h) and stages that head's slash and vertical lists in LDS.  The
-// vertical list is merged with the windows as they are produced (windows are
-// disjoint and ascending), so each thread makes a single pass over both lists.
+// Two kernels.  vs_convert_kernel: one thread per query block walks the slash
+// list in order (the window frontier is a sequential dependence); a workgroup
+// takes 64 consecutive query blocks of one (b, h) and stages that head's slash
+// list in LDS.  vs_columns_kernel: one wave per query block tests 64 verticals
+// per round against the block's windows (a vertical is a column iff it is at
+// most the block's last visible key and no window holds it: windows are
+// disjoint and ascending, so a binary search over their starts decides it) and
+// writes the kept ones in order.  The one-thread merge of both lists that this
+// replaces spent three quarters of its time on the verticals.
 #pragma once
 #include "common.cuh"
 
@@ -62,15 +67,11 @@ __global__ __launch_bounds__(kVSConvThreads) void vs_convert_kernel(VSConvArgs a
   const int b = bh / a.H, h = bh % a.H;
   const int m = blockIdx.x * kVSConvThreads + threadIdx.x;
   const int32_t* sl_g = a.slash + (int64_t)bh * a.nnz_s;
-  const int32_t* vt_g = a.vertical + (int64_t)bh * a.nnz_v;
-  // per-head counts (the merged-head variant): only the first ns / nv entries are indices
+  // per-head counts (the merged-head variant): only the first ns entries are indices
   const int ns = a.s_count ? min(max(a.s_count[h], 0), a.nnz_s) : a.nnz_s;
-  const int nv = a.v_count ? min(max(a.v_count[h], 0), a.nnz_v) : a.nnz_v;
-  const bool staged = a.nnz_s + a.nnz_v <= kVSConvLdsInts;
-  if (staged) {
+  const bool staged = a.nnz_s <= kVSConvLdsInts;
+  if (staged)
     for (int x = threadIdx.x; x < ns; x += kVSConvThreads) lists[x] = sl_g[x];
-    for (int x = threadIdx.x; x < nv; x += kVSConvThreads) lists[a.nnz_s + x] = vt_g[x];
-  }
   __syncthreads();
   if (m >= a.rows) return;
 
@@ -80,24 +81,17 @@ __global__ __launch_bounds__(kVSConvThreads) void vs_convert_kernel(VSConvArgs a
   const int r0 = m * a.BM;
   if (r0 >= q_len) {
     a.bc[item] = 0;
-    a.cc[item] = 0;
     return;
   }
   const int r1 = min(r0 + a.BM, q_len);
   const int d = kv_len - q_len;
   const int last_visible = r1 - 1 + d;
   int32_t* bo = a.bo + item * a.nnz_s;
-  int32_t* co = a.ci + item * a.nnz_v;
 
-  // the single pass over both lists; called once with the LDS copies and once with the global
-  // lists, so that each call reads through pointers of a known address space (LDS reads, not
-  // generic ones)
-  auto convert = [&](const int32_t* sl, const int32_t* vt, auto wo, auto co_w) __attribute__((always_inline)) {
-    int vi = 0;
-    int frontier = 0;            // valid once a window exists
-    int prev_end = -0x7fffffff;  // end (exclusive) of the last window
-    // the next vertical index, read one step ahead so the LDS latency overlaps the compare
-    int vnext = vi < nv ? vt[vi] : 0x7fffffff;
+  // the walk; called once with the LDS copy and once with the global list, so that each call
+  // reads through a pointer of a known address space (LDS reads, not generic ones)
+  auto convert = [&](const int32_t* sl, auto wo) __attribute__((always_inline)) {
+    int frontier = 0;  // valid once a window exists
     auto slash = [&](int s) __attribute__((always_inline)) {
       const int e = last_visible - s;
       if (e < 0) return;
@@ -111,16 +105,7 @@ __global__ __launch_bounds__(kVSConvThreads) void vs_convert_kernel(VSConvArgs a
         return;
       }
       frontier = wstart + a.BN;
-      // verticals left of this window: outside every window unless inside the previous one
-      while (vi < nv) {
-        const int v = vnext;
-        if (v >= wstart || v > last_visible) break;
-        ++vi;
-        vnext = vi < nv ? vt[vi] : 0x7fffffff;
-        if (v >= prev_end) co_w.push(v);
-      }
       wo.push(wstart);
-      prev_end = frontier;
     };
     // slash indices four at a time (one 16-byte read) where the list allows it
     int si = 0;
@@ -134,28 +119,71 @@ __global__ __launch_bounds__(kVSConvThreads) void vs_convert_kernel(VSConvArgs a
       }
     }
     for (; si < ns; ++si) slash(sl[si]);
-    while (vi < nv) {
-      const int v = vnext;
-      if (v > last_visible) break;
-      ++vi;
-      vnext = vi < nv ? vt[vi] : 0x7fffffff;
-      if (v >= prev_end) co_w.push(v);
-    }
     wo.flush();
-    co_w.flush();
     a.bc[item] = wo.n;
-    a.cc[item] = co_w.n;
   };
   // 16-byte stores need 16-byte aligned rows (uniform over the launch)
-  const bool vec = ((a.nnz_s | a.nnz_v) & 3) == 0 && ((reinterpret_cast<uintptr_t>(a.bo) |
-                                                       reinterpret_cast<uintptr_t>(a.ci)) & 15) == 0;
+  const bool vec = (a.nnz_s & 3) == 0 && (reinterpret_cast<uintptr_t>(a.bo) & 15) == 0;
   if (vec) {
-    if (staged) convert(lists, lists + a.nnz_s, RowWriter<true>(bo), RowWriter<true>(co));
-    else convert(sl_g, vt_g, RowWriter<true>(bo), RowWriter<true>(co));
+    if (staged) convert(lists, RowWriter<true>(bo));
+    else convert(sl_g, RowWriter<true>(bo));
   } else {
-    if (staged) convert(lists, lists + a.nnz_s, RowWriter<false>(bo), RowWriter<false>(co));
-    else convert(sl_g, vt_g, RowWriter<false>(bo), RowWriter<false>(co));
+    if (staged) convert(lists, RowWriter<false>(bo));
+    else convert(sl_g, RowWriter<false>(bo));
   }
+}
+
+// Columns of query block blockIdx.x of (b, h) = blockIdx.y, after vs_convert_kernel has written
+// its windows: one wave, verticals in rounds of 64 (one per lane, ascending), the kept ones
+// written in order through a ballot and a prefix count.  The block's windows are staged in LDS
+// when they fit (kVSColLdsInts), else searched in global memory.
+__global__ __launch_bounds__(64) void vs_columns_kernel(VSConvArgs a) {
+  extern __shared__ int32_t wins[];
+  const int m = blockIdx.x, bh = blockIdx.y;
+  const int b = bh / a.H, h = bh % a.H;
+  const int64_t item = (int64_t)bh * a.rows + m;
+  const int l = threadIdx.x;
+  const int q_len = a.q_seqlens[b];
+  const int kv_len = a.kv_seqlens[b];
+  const int r0 = m * a.BM;
+  if (r0 >= q_len) {  // uniform: no barrier has run yet
+    if (l == 0) a.cc[item] = 0;
+    return;
+  }
+  const int last_visible = min(r0 + a.BM, q_len) - 1 + (kv_len - q_len);
+  const int nv = a.v_count ? min(max(a.v_count[h], 0), a.nnz_v) : a.nnz_v;
+  const int nw = a.bc[item];
+  const int32_t* bo = a.bo + item * a.nnz_s;  // read only when nw > 0
+  const bool staged = nw <= min(a.nnz_s, kVSColLdsInts);
+  if (staged)
+    for (int x = l; x < nw; x += 64) wins[x] = bo[x];
+  __syncthreads();
+  const int32_t* vt = a.vertical + (int64_t)bh * a.nnz_v;
+  int32_t* co = a.ci + item * a.nnz_v;
+  // v lies in a window iff the last window starting at or before v still holds it
+  auto covered = [&](int v, const int32_t* w) __attribute__((always_inline)) {
+    int lo = 0, hi = nw;  // windows with start <= v: [0, lo)
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (w[mid] <= v) lo = mid + 1;
+      else hi = mid;
+    }
+    return lo > 0 && v < w[lo - 1] + a.BN;
+  };
+  int n = 0;
+  for (int i0 = 0; i0 < nv; i0 += 64) {
+    const int i = i0 + l;
+    const int v = i < nv ? vt[i] : 0x7fffffff;
+    bool keep = v <= last_visible;
+    if (keep) keep = !(staged ? covered(v, wins) : covered(v, bo));
+    const uint64_t bal = __ballot(keep);
+    if (keep)
+      co[n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u))] = v;
+    n += __popcll(bal);
+    // ascending: once a vertical of this round lies past the block, so do all later ones
+    if (__ballot(i < nv && v > last_visible) != 0) break;
+  }
+  if (l == 0) a.cc[item] = n;
 }
 
 }  // namespace bsa
