@@ -261,9 +261,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void v
     if (!r.gathered) {
       issue_win(tile, src, ss, is_k, r);
     } else {
+      // the keys of this wave's 32 tile rows as record_kid stored them (absent ones as INT_MAX,
+      // loaded as key 0 and masked): LDS reads only, so the loads below do not wait for a
+      // column index read from global memory, whose wait would cover every load in flight
       int kk[8];
 #pragma unroll
-      for (int x = 0; x < 8; ++x) kk[x] = max(0, col_key(srow0 + x * 4 + lrow, r));
+      for (int x = 0; x < 8; ++x) {
+        const int kid = kid_s[w * 32 + x * 4 + lrow];
+        kk[x] = kid == 0x7fffffff ? 0 : kid;
+      }
 #pragma unroll
       for (int x = 0; x < 8; ++x) {
         const char* p = reinterpret_cast<const char*>(src + (int64_t)kk[x] * ss);
@@ -272,7 +278,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void v
       }
     }
   };
-  // a gathered segment records its key indices for the masks (tile rows of this wave)
+  // a gathered segment records its key indices for the masks and the loads (tile rows of this
+  // wave); every issue of a gathered segment follows the record of that segment
   auto record_kid = [&](const Seg& r) __attribute__((always_inline)) {
     if (r.gathered && l < 32) {
       const int key = col_key(srow0 + l, r);
@@ -421,8 +428,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void v
   }
   if (n_steps > 0) {
     const Seg mine = hb ? cur1 : cur0;
-    issue(Kt, kbp, a.k.ss, true, mine);
     record_kid(mine);
+    issue(Kt, kbp, a.k.ss, true, mine);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -451,10 +458,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void v
       nxt1 = seg_shared(c + 1, 1);
       issue_win(Kt, kbp, a.k.ss, true, hb ? nxt1 : nxt0);
     } else if (more) {
-      // the next step is a split one (this is the last shared step or a split step)
+      // the next step is a split one (this is the last shared step or a split step).  Its
+      // key indices are recorded before its loads are issued: a column index past the staged
+      // ones is read from global memory, and the wait for that read would also wait for every
+      // load issued before it.
       nxt0 = nxt1 = seg_split(c + 1 - n_sh, hb);
-      issue(Kt, kbp, a.k.ss, true, nxt0);
       record_kid(nxt0);
+      issue(Kt, kbp, a.k.ss, true, nxt0);
     }
     pv_phase(nbw_c, NBW == 4 ? 0 : 2 * hb, s);
     if (more) {
