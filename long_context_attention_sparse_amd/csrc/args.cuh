@@ -34,6 +34,7 @@ constexpr int kThreshMaxCand = 4096;   // threshold selection: query blocks per 
 constexpr int kSelTile = 1024;         // selected attention: token positions per index workgroup
 constexpr int kSelMaxBlocks = 8192;    // selected attention: key blocks per sequence (LDS histogram)
 constexpr int kBwdChunk = 128;         // backward: 32-row query slabs per dK/dV workgroup
+constexpr int kBwdListLds = 256;       // backward dQ: pattern-list entries of a query block staged in LDS
 
 struct DecodeSeg {
   TensorArg k, v;

@@ -298,6 +298,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
   __shared__ __attribute__((aligned(16))) float ls[2][32];
   __shared__ __attribute__((aligned(16))) float dsm[2][32];
   __shared__ __attribute__((aligned(16))) float Ps[2][64 * 16];  // float32 P of each key group, lane layout
+  __shared__ int ents_s[kBwdChunk / 2 + 2];                        // this chunk's list entries
 
   const int n_lists = a.B * a.Hkv * a.nks;
   const int wid = wg_x();
@@ -379,6 +380,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
   const int list0 = dense ? 0 : a.offsets[list];
   const int n_units = dense ? a.counts[list] : a.counts[list] * slabs;
   const int u0 = chunk * kBwdChunk, u1 = min(n_units, u0 + kBwdChunk);
+  // The chunk's list entries (at most kBwdChunk / 2 + 1: an entry covers two or four slabs) are
+  // staged in LDS, so that finding the next slab reads no global memory: the wait before each
+  // slab's barrier would otherwise include that read.
+  const int e0 = u0 >> slabs_log2;
+  if (!dense) {
+    const int ne = u1 > u0 ? ((u1 - 1) >> slabs_log2) - e0 + 1 : 0;
+    for (int x = t; x < ne; x += 256) ents_s[x] = a.entries[list0 + e0 + x];
+  }
+  __syncthreads();
   auto next_unit = [&](int u, int& h, int& q0) __attribute__((always_inline)) -> int {
     for (; u < u1; ++u) {
       if (dense) {
@@ -386,7 +396,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
         h = hkv * a.G + u / per;
         q0 = (first_slab + u % per) * 32;
       } else {
-        const int e = a.entries[list0 + (u >> slabs_log2)];
+        const int e = lds_int(ents_s, (u >> slabs_log2) - e0);
         h = e >> kBwdEntryShift;
         q0 = (e & ((1 << kBwdEntryShift) - 1)) * a.BM + (u & (slabs - 1)) * 32;
       }
@@ -610,6 +620,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4
   constexpr int RPW = 64 / NW;  // tile rows each wave loads
   __shared__ __attribute__((aligned(16))) uint16_t K0[64 * RS], K1[64 * RS];
   __shared__ __attribute__((aligned(16))) uint16_t V0[64 * RS], V1[64 * RS];
+  __shared__ int sub_s[kBwdListLds];  // the first entries of this query block's list
 
   // (b, kv head, query block, group member), query blocks heaviest (last) first, contiguous
   // ranges per XCD: the G query heads of a kv head take the same query block side by side, so
@@ -680,10 +691,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4
     list = a.pat.index + lb * a.pat.cap;
     spe = a.pat.block_N / 64;
     n_sub = a.pat.count[lb] * spe;
+    // staged in LDS (entries past kBwdListLds are read from global memory), so that finding the
+    // next key block reads no global memory before the barrier that waits for every load
+    const int ne = min(a.pat.count[lb], kBwdListLds);
+    for (int e = tid_x(); e < ne; e += NW * 64) sub_s[e] = list[e];
   }
+  __syncthreads();
   auto next_sub = [&](int x, int& key0) __attribute__((always_inline)) -> int {
     for (; x < n_sub; ++x) {
-      key0 = (a.pat.kind == 0 ? x : list[x / spe] * spe + x % spe) * 64;
+      const int e = x / spe;
+      key0 = (a.pat.kind == 0 ? x : (e < kBwdListLds ? lds_int(sub_s, e) : list[e]) * spe + x % spe) * 64;
       if (key0 >= 0 && key0 < sq.k_len && !(a.causal && key0 > last_row + delta)) return x;
     }
     return n_sub;
