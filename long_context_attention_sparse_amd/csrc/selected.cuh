@@ -246,12 +246,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
     __builtin_amdgcn_global_load_lds(vp + ((lslot ^ v_swz(row)) << 4), BSA_LDS(Vt + (w * 4 + x) * 4 * RS), 16, 0, 0);
   }
 
+  // Every lane loads: a lane without a row reads row 0 of its sequence (a valid address,
+  // finite values), and its row is never written (each query row's scores, weights and output
+  // stay in its own lane column).  With a branch around each load, or a select on the loaded
+  // values, the compiler waited for the loads in flight, the K and V tile included, halfway
+  // through issuing them.
   bf16x8 qreg[D / 16];
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    const u32x4 v = row_ok ? ldg128(qrow + ks * 16 + hh * 8) : u32x4{0, 0, 0, 0};
-    qreg[ks] = as_bf16x8(v);
-  }
+  for (int ks = 0; ks < D / 16; ++ks) qreg[ks] = as_bf16x8(ldg128(qrow + ks * 16 + hh * 8));
   int koff[D / 16];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) koff[ks] = lq * RS + (((ks * 2 + hh) ^ k_swz(lq)) << 3);
