@@ -207,19 +207,22 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
                                          0, 0);
       }
     } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        int key = key_of(w * 16 + i * 4 + lrow, r, staged);
-        key = key < 0 ? 0 : key;
-        const char* rowp = reinterpret_cast<const char*>(kbp + (int64_t)key * a.k.ss);
-        __builtin_amdgcn_global_load_lds(rowp + (kx ^ (i << 6)), BSA_LDS(kt + (w * 4 + i) * 4 * RS), 16, 0, 0);
-      }
-      // gathered chunks record their key indices for the mask
+      // the key indices first (a gathered chunk also records them for the mask), then the
+      // loads: an index read from memory is waited for, and that wait would also wait for the
+      // loads already in flight
       if constexpr (KIND == 2) {
         if (r.gathered && t < CK) {
           const int key = key_of(t, r, staged);
           kid[t] = key >= 0 ? key : 0x7fffffff;
         }
+      }
+      int keys[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) keys[i] = max(0, key_of(w * 16 + i * 4 + lrow, r, staged));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const char* rowp = reinterpret_cast<const char*>(kbp + (int64_t)keys[i] * a.k.ss);
+        __builtin_amdgcn_global_load_lds(rowp + (kx ^ (i << 6)), BSA_LDS(kt + (w * 4 + i) * 4 * RS), 16, 0, 0);
       }
     }
   };
@@ -231,11 +234,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         __builtin_amdgcn_global_load_lds(rowp + v_lane, BSA_LDS(vt + (w * 4 + i) * 4 * RS), 16, 0, 0);
       }
     } else {
+      // all four indices before any load (as for K)
+      int keys[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) keys[i] = max(0, key_of(w * 16 + i * 4 + lrow, r, staged));
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        int key = key_of(w * 16 + i * 4 + lrow, r, staged);
-        key = key < 0 ? 0 : key;
-        const char* rowp = reinterpret_cast<const char*>(vbp + (int64_t)key * a.v.ss);
+        const char* rowp = reinterpret_cast<const char*>(vbp + (int64_t)keys[i] * a.v.ss);
         __builtin_amdgcn_global_load_lds(rowp + vx, BSA_LDS(vt + (w * 4 + i) * 4 * RS), 16, 0, 0);
       }
     }

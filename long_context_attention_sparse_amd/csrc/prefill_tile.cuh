@@ -271,8 +271,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   // this wave's segment of the current chunk
   auto my_seg = [&](const Seg* c) -> Seg { return (NS == 1 || w < 2) ? c[0] : c[NS - 1]; };
   if (n_chunks > 0) {
-    issue(Kt, kbp, a.k.ss, true, my_seg(cur), false);
     record_kid(my_seg(cur), false);
+    issue(Kt, kbp, a.k.ss, true, my_seg(cur), false);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -313,8 +313,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     if (more) {
 #pragma unroll
       for (int x = 0; x < NS; ++x) nxt[x] = seg_at((c + 1) * NS + x, true);
-      issue(Kt, kbp, a.k.ss, true, my_seg(nxt), true);
+      // the key indices first: one read past the staged ones is waited for, and that wait
+      // would also wait for loads issued before it
       record_kid(my_seg(nxt), true);
+      issue(Kt, kbp, a.k.ss, true, my_seg(nxt), true);
     }
     // softmax weights and PV; the V^T operands of the first two 16-key steps are read
     // before the exponentials
