@@ -128,3 +128,22 @@ def test_vs_convert_indices_longer_than_staging():
         assert bc[0, 0, m] == len(wins) and cc[0, 0, m] == len(cols), m
         assert np.array_equal(bo[0, 0, m, :len(wins)], wins), m
         assert np.array_equal(ci[0, 0, m, :len(cols)], cols), m
+
+
+def test_vs_convert_past_both_staging_limits():
+    """The conversion's two global-memory paths: more slash indices per head than the window walk
+    stages (16,384) and, on a 280,000-token sequence, late query blocks with more windows than the
+    column test stages (4,096).  Sampled items exactly as the oracle converts them."""
+    L, H, nnz_v, nnz_s = 280000, 1, 100, 17000
+    say("vertical-slash conversion with 17,000 slash indices and more than 4,096 windows per block")
+    vert, slash = _vs_inputs(106, L, H, nnz_v, nnz_s)
+    sl = dev_i32([L])
+    bc, bo, cc, ci = (host(t).astype(np.int64) for t in
+                      bsa.vs_convert_indexes(sl, sl, dev_i32(vert), dev_i32(slash), L, 64, 64))
+    assert bc.max() > 4096
+    last = (L + 63) // 64 - 1
+    for m in (0, 1, 2000, last - 1, last):
+        wins, cols = oracle.vs_convert_item(L, L, vert[0, 0], slash[0, 0], m, 64, 64)
+        assert bc[0, 0, m] == len(wins) and cc[0, 0, m] == len(cols), m
+        assert np.array_equal(bo[0, 0, m, :len(wins)], wins), m
+        assert np.array_equal(ci[0, 0, m, :len(cols)], cols), m
