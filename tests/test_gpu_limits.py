@@ -1,9 +1,9 @@
 """GPU parity where the kernels' LDS staging overflows and the tails are read from global
 memory: block lists of more than 256 entries (prefill and a decode split of more than 256
 entries), vertical-slash blocks with more than 768 gathered columns or more than 256 windows (the
-windows each block of a query-block pair stages), and a conversion whose
-slash + vertical indices exceed the 16,384 ints it stages in LDS.  Expected values come from
-the oracle."""
+windows each block of a query-block pair stages), and conversions with many indices: more slash
+indices per head than the window walk stages in LDS (16,384) and more windows per query block
+than the column test stages (4,096).  Expected values come from the oracle."""
 import numpy as np
 import pytest
 import torch
@@ -116,6 +116,8 @@ def test_vs_windows_longer_than_staging(bn):
 
 
 def test_vs_convert_indices_longer_than_staging():
+    """18,000 indices per head, 12,000 of them verticals: the column test walks them in many
+    rounds of 64 per query block."""
     L, H, nnz_v, nnz_s = 40000, 1, 12000, 6000
     say("vertical-slash conversion of 18,000 indices per head")
     vert, slash = _vs_inputs(104, L, H, nnz_v, nnz_s)
