@@ -12,18 +12,19 @@
 //
 // Workgroup: 4 waves x 32 query rows (BM = 128), 128-key tiles.  K and V go
 // straight from global memory into LDS (global_load_lds_dwordx4, the swizzled
-// row layouts of tile.cuh; 32 KB each, two workgroups per CU); the V^T MFMA
-// operand is read with ds_read_b64_tr_b16.  Per tile:
-//   [K_j resident] S_ij (8 MFMAs per 32-key block), diagonal mask, tile max
-//   -> LDS exchange + barrier (every wave is done with K_j) -> keep decision
-//   -> kept tiles: issue V_j, softmax update and P, wait, barrier, issue K_next, PV;
-//      skipped tiles: issue K_next (count_skipped: softmax update) -> wait for K_next
-//      -> barrier,
-// so V_j streams in during the softmax and the next K tile during the PV product (kept
-// tiles) or right after the decision (skipped tiles).  (A workgroup-scope barrier waits for
-// every outstanding load, so K_next is issued after the V barrier, not
-// before it.)  Grid remapped XCD-aware, heaviest query blocks first.
+// row layouts of tile.cuh); two 32 KB tile buffers, two workgroups per CU; the
+// V^T MFMA operand is read with ds_read_b64_tr_b16.  Per tile, with K_j in
+// buffer X and the other buffer Y free:
+//   issue K_next into Y -> S_ij (8 MFMAs per 32-key block), diagonal mask, tile max
+//   -> LDS exchange + bare barrier (every wave is done with K_j; K_next stays in flight)
+//   -> keep decision -> kept tiles: issue V_j into X, softmax update and P, wait,
+//      barrier, PV; skipped tiles: (count_skipped: softmax update)
+//   -> wait for K_next, barrier; X and Y trade roles,
+// so the next K tile streams in during the whole of tile j, kept or skipped, and V_j
+// during the softmax.  Grid remapped XCD-aware, heaviest query blocks first.
 #pragma once
+#include <type_traits>
+
 #include "tile.cuh"
 
 namespace bsa {
@@ -76,19 +77,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
   const uint32_t kx = (uint32_t)(lslot ^ lrow) << 4;
   const uint32_t vx = (uint32_t)(lslot ^ (lrow << 2)) << 4;
   const uint32_t k_lane = (uint32_t)(lrow * a.k.ss) * 2u, v_lane = (uint32_t)(lrow * a.v.ss) * 2u + vx;
-  auto issue_k = [&](int key0) __attribute__((always_inline)) {
+  auto issue_k = [&](int key0, uint16_t* buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
       const char* p = reinterpret_cast<const char*>(kbp + (int64_t)(key0 + w * 32 + x * 4) * a.k.ss);
-      __builtin_amdgcn_global_load_lds(p + (k_lane + (kx ^ ((x & 3) << 6))), BSA_LDS(Kt + (w * 8 + x) * 4 * RS), 16,
+      __builtin_amdgcn_global_load_lds(p + (k_lane + (kx ^ ((x & 3) << 6))), BSA_LDS(buf + (w * 8 + x) * 4 * RS), 16,
                                        0, 0);
     }
   };
-  auto issue_v = [&](int key0) __attribute__((always_inline)) {
+  auto issue_v = [&](int key0, uint16_t* buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
       const char* p = reinterpret_cast<const char*>(vbp + (int64_t)(key0 + w * 32 + x * 4) * a.v.ss);
-      __builtin_amdgcn_global_load_lds(p + v_lane, BSA_LDS(Vt + (w * 8 + x) * 4 * RS), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(p + v_lane, BSA_LDS(buf + (w * 8 + x) * 4 * RS), 16, 0, 0);
     }
   };
 
@@ -134,7 +135,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
   // O^T += V_j^T P^T, the V^T operands read with the transposing LDS read one 16-key step
   // ahead of their products (read just before, every product waited for its own reads).  The
   // counting reading keeps the reads next to their products: it has no registers to spare.
-  auto pv = [&](const uint32_t (*pk)[8]) __attribute__((always_inline)) {
+  auto pv = [&](const uint32_t (*pk)[8], const uint16_t* Vb) __attribute__((always_inline)) {
     constexpr int NKS = NB * 2;
     if constexpr (COUNT) {
 #pragma unroll
@@ -143,8 +144,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
         const u32x4 pb = {pk[kb][hb * 4], pk[kb][hb * 4 + 1], pk[kb][hb * 4 + 2], pk[kb][hb * 4 + 3]};
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const u32x2 lo = ds_read_tr16(Vt + ks * 16 * RS + voff[db]);
-          const u32x2 hi = ds_read_tr16(Vt + (ks * 16 + 8) * RS + voff[db]);
+          const u32x2 lo = ds_read_tr16(Vb + ks * 16 * RS + voff[db]);
+          const u32x2 hi = ds_read_tr16(Vb + (ks * 16 + 8) * RS + voff[db]);
           oacc[db] = mfma32x32x16(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), as_bf16x8(pb), oacc[db]);
         }
       }
@@ -154,8 +155,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
     auto read_v = [&](int ks, u32x4* dst) __attribute__((always_inline)) {
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        const u32x2 lo = ds_read_tr16(Vt + ks * 16 * RS + voff[db]);
-        const u32x2 hi = ds_read_tr16(Vt + (ks * 16 + 8) * RS + voff[db]);
+        const u32x2 lo = ds_read_tr16(Vb + ks * 16 * RS + voff[db]);
+        const u32x2 hi = ds_read_tr16(Vb + (ks * 16 + 8) * RS + voff[db]);
         dst[db] = u32x4{lo[0], lo[1], hi[0], hi[1]};
       }
     };
@@ -172,11 +173,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
     }
   };
 
-  issue_k(tile_of(0) * BN);
+  issue_k(tile_of(0) * BN, Kt);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int n = 0; n <= i; ++n) {
+  // One tile; the two tile buffers trade roles from tile to tile (P, the parity, is a
+  // compile-time constant so that every LDS access names its array).  K_n sits in X; K_next
+  // goes into Y at once and streams in during S_n, the exchange, the softmax and P V_n.
+  auto step = [&](int n, auto par) __attribute__((always_inline)) {
+    constexpr bool P = decltype(par)::value;
+    uint16_t* const X = P ? Vt : Kt;
+    uint16_t* const Y = P ? Kt : Vt;
     const int j = tile_of(n);
+    const bool more = n < i;
+    if (more) issue_k(tile_of(n + 1) * BN, Y);
     // S_j: the NB key blocks advance together through the head dimension, the K operands of
     // step ks + 1 read before the products of step ks, so each read has a step of products
     // to land behind (one block at a time, every product waited for its own read).  The
@@ -190,18 +199,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
       for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks)
-          s[kb] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(Kt + kb * 32 * RS + koff[ks])), qreg[ks],
+          s[kb] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(X + kb * 32 * RS + koff[ks])), qreg[ks],
                                s[kb]);
     } else {
       u32x4 av[2][NB];
 #pragma unroll
-      for (int kb = 0; kb < NB; ++kb) av[0][kb] = *reinterpret_cast<const u32x4*>(Kt + kb * 32 * RS + koff[0]);
+      for (int kb = 0; kb < NB; ++kb) av[0][kb] = *reinterpret_cast<const u32x4*>(X + kb * 32 * RS + koff[0]);
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
         if (ks + 1 < D / 16) {
 #pragma unroll
           for (int kb = 0; kb < NB; ++kb)
-            av[(ks + 1) & 1][kb] = *reinterpret_cast<const u32x4*>(Kt + kb * 32 * RS + koff[ks + 1]);
+            av[(ks + 1) & 1][kb] = *reinterpret_cast<const u32x4*>(X + kb * 32 * RS + koff[ks + 1]);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -226,51 +235,45 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
 #pragma unroll
     for (int off = 16; off >= 1; off >>= 1) mx = fmaxf(mx, shfl_xor_f(mx, off));
     if (l == 0) red[w] = mx;
-    // every wave's maximum is in LDS and every wave is done reading K_j
-    __syncthreads();
+    // every wave's maximum is in LDS and every wave is done reading K_j.  A bare barrier
+    // after the wait for LDS: the fence of __syncthreads would also wait for K_next.  The
+    // empty asm statements with memory clobbers keep LDS accesses on their side of it.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
     const float tile_max = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])) * a.scale;
     const bool keep = !CALIB && (diag || tile_max >= T);
     if (t == 0) {
       if (a.keep) a.keep[mask_row + j] = keep ? 1 : 0;
       if (a.tmax) a.tmax[mask_row + j] = tile_max;
     }
-    const bool more = n < i;
-    if constexpr (COUNT && !CALIB) {
-      // every tile's scores enter the maximum and the normaliser; a kept tile's V_j
-      // (or, for a skipped tile, K_next) streams in during the softmax update
-      if (keep) issue_v(j * BN);
-      else if (more) issue_k(tile_of(n + 1) * BN);
-      uint32_t pk[NB][8];
-      float psum;
-      weights(s, row_max, pk, psum);
-      l_run += psum;
-      if (keep) {
-        __builtin_amdgcn_s_waitcnt(0);
-        // V_j from every wave is in LDS; K_next streams in during the P V product
-        __syncthreads();
-        if (more) issue_k(tile_of(n + 1) * BN);
-        pv(pk);
+    if constexpr (!CALIB) {
+      // V_j goes where K_j was; it streams in during the softmax update
+      if (keep) issue_v(j * BN, X);
+      if (keep || COUNT) {
+        uint32_t pk[NB][8];
+        float psum;
+        weights(s, row_max, pk, psum);
+        l_run += psum;
+        if (keep) {
+          // V_j from every wave is in LDS
+          __builtin_amdgcn_s_waitcnt(0);
+          __syncthreads();
+          pv(pk, X);
+        }
       }
-    } else if (keep) {
-      issue_v(j * BN);
-      // the softmax update and P run while V_j streams in
-      uint32_t pk[NB][8];
-      float psum;
-      weights(s, row_max, pk, psum);
-      __builtin_amdgcn_s_waitcnt(0);
-      // V_j from every wave is in LDS; K_next streams in during the P V product
-      __syncthreads();
-      if (more) issue_k(tile_of(n + 1) * BN);
-      pv(pk);
-      l_run += psum;
-    } else if (more) {
-      issue_k(tile_of(n + 1) * BN);
     }
     if (more) {
-      // K_next is in LDS and every wave is done reading V_j
+      // K_next is in LDS and every wave is done reading X, which takes K after next
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
+  };
+  for (int n = 0;; n += 2) {
+    step(n, std::integral_constant<bool, false>{});
+    if (n + 1 > i) break;
+    step(n + 1, std::integral_constant<bool, true>{});
+    if (n + 2 > i) break;
   }
   if constexpr (!CALIB) {
     const int64_t ob = (int64_t)b * a.o.sb + (int64_t)row * a.o.ss + (int64_t)h * a.o.sh;
