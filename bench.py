@@ -796,7 +796,7 @@ def gpu_gated(torch, bsa, w, args):
                         "skipped_counted_note": "the other reading of a skipped tile: its scores stay in the "
                                                 "softmax maximum and normaliser (the timed line drops them)",
                         "calibration": calibration},
-                roofline=_roof("mfma", flops / (kms * 1e-3) / 1e12, "void bsa::gated_kernel<false>(bsa::GatedArgs)", kms))
+                roofline=_roof("mfma", flops / (kms * 1e-3) / 1e12, "void bsa::gated_kernel<false, false>(bsa::GatedArgs)", kms))
 
 
 # ---------------------------------------------------------------------------

@@ -21,7 +21,8 @@
 //      barrier, PV; skipped tiles: (count_skipped: softmax update)
 //   -> wait for K_next, barrier; X and Y trade roles,
 // so the next K tile streams in during the whole of tile j, kept or skipped, and V_j
-// during the softmax.  Grid remapped XCD-aware, heaviest query blocks first.
+// during the softmax.  The calibration pass loads no V: it keeps one buffer and requests
+// K_next after the barrier.  Grid remapped XCD-aware, heaviest query blocks first.
 #pragma once
 #include <type_traits>
 
@@ -182,10 +183,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
   auto step = [&](int n, auto par) __attribute__((always_inline)) {
     constexpr bool P = decltype(par)::value;
     uint16_t* const X = P ? Vt : Kt;
-    uint16_t* const Y = P ? Kt : Vt;
+    uint16_t* const Y = CALIB ? Kt : P ? Kt : Vt;
     const int j = tile_of(n);
     const bool more = n < i;
-    if (more) issue_k(tile_of(n + 1) * BN, Y);
+    // (the calibration pass loads no V: it keeps one buffer and requests K_next after the
+    // barrier below, once every wave is done with K_j.  Under 128 registers it runs four waves
+    // per SIMD, which hide the load; the two-buffer loop would cost it that)
+    if (!CALIB && more) issue_k(tile_of(n + 1) * BN, Y);
     // S_j: the NB key blocks advance together through the head dimension, the K operands of
     // step ks + 1 read before the products of step ks, so each read has a step of products
     // to land behind (one block at a time, every product waited for its own read).  The
@@ -241,6 +245,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+    if (CALIB && more) issue_k(tile_of(n + 1) * BN, Y);
     const float tile_max = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])) * a.scale;
     const bool keep = !CALIB && (diag || tile_max >= T);
     if (t == 0) {
@@ -269,11 +274,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
       __syncthreads();
     }
   };
-  for (int n = 0;; n += 2) {
-    step(n, std::integral_constant<bool, false>{});
-    if (n + 1 > i) break;
-    step(n + 1, std::integral_constant<bool, true>{});
-    if (n + 2 > i) break;
+  if constexpr (CALIB) {
+    for (int n = 0; n <= i; ++n) step(n, std::integral_constant<bool, false>{});
+  } else {
+    for (int n = 0;; n += 2) {
+      step(n, std::integral_constant<bool, false>{});
+      if (n + 1 > i) break;
+      step(n + 1, std::integral_constant<bool, true>{});
+      if (n + 2 > i) break;
+    }
   }
   if constexpr (!CALIB) {
     const int64_t ob = (int64_t)b * a.o.sb + (int64_t)row * a.o.ss + (int64_t)h * a.o.sh;
